@@ -1,0 +1,73 @@
+/* Plain CPU oracle for the ExTernD decomposition engine.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This library exists to check the GPU library.  Only the test
+ * suite, the smoke check and the benchmark's CPU-baseline leg may load it; the product path
+ * never does.  It shares no source with the GPU library.
+ *
+ * Method (pages: "ExTernD: Expanded-Rank Ternary Decomposition" review, sections Method and
+ * Key idea; pith.science referee report, "What carries the argument" and minor comment 1 on
+ * Eq. 3; abstract): A (m x n) ~= B diag(D) C with ternary B (m x k), C (k x n), real D,
+ * k = floor(mu * min(m,n)), fitted greedily by alternating least squares with residual
+ * deflation, or in blocks of b components with the decorrelated least-squares target of Eq. 3.
+ *
+ * Numeric conventions (a reading, the pages fix no precision): the residual R is stored in
+ * fp32, every sum is accumulated in fp64 in ascending index order, selection inputs are rounded
+ * to fp32 first, each scale d is computed in fp64 and rounded to fp32, and the deflation
+ * R_ij <- fl32(R_ij - d u_i v_j) is a single fp32 operation.
+ *
+ * Packed ternary vectors: element t sits in bits 2(t%16)..2(t%16)+1 of word t/16;
+ * 00 = 0, 01 = +1, 11 = -1; tail bits zero.
+ */
+#ifndef EXTERND_ORACLE_H
+#define EXTERND_ORACLE_H
+#include <stdint.h>
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct {
+  int threads;              /* OpenMP threads; <= 0 = runtime default */
+  int safeguard;            /* 1 = Prop. 2 best single-entry safeguard on */
+  int64_t k_limit;          /* > 0: stop after this many components (sequential) */
+  double* gaps;             /* nullable, k: smallest selection gap of each component */
+  int64_t* counters;        /* nullable, 4: fallbacks, safeguard activations, ALS passes, zero components */
+  double* energy_explicit;  /* nullable, 1: 1 - ||R||^2_H / ||A||^2_H recomputed from R at the end */
+  int residual_fp64;        /* 1 = keep the residual in fp64 instead of fp32 (precision study only) */
+  int block_engine;         /* 1 = run the block engine even when b == 1 (invariant test) */
+} externd_oracle_opts;
+
+int64_t externd_oracle_rank(int64_t m, int64_t n, float mu);
+int64_t externd_oracle_words(int64_t len);
+
+/* T_tau(x; h): v (int8, L), out[0..2] = P, H, S, *jstar = support size, *gap = selection gap. */
+int externd_oracle_project(const float* x, int64_t L, float tau, const float* h,
+                           int8_t* v, double* out, int64_t* jstar, double* gap);
+
+/* Free-running decomposition.  block <= 1: sequential deflation; block >= 2: block-ALS;
+ * block == -1: b = min(256, min(m,n)/8) (at least 1). */
+int externd_oracle_decompose(const float* A, int64_t m, int64_t n, float mu, float tau,
+                             const float* h, int als_iters, int block,
+                             uint32_t* B, uint32_t* C, float* D, double* energy,
+                             const externd_oracle_opts* opts);
+
+/* Replay: walk the components (or blocks) of a finished decomposition (B, C, D given), applying
+ * each with the oracle's deflation rule.  Before applying component (block) s listed in
+ * `sample` (ascending), fit it afresh from the replayed residual and write the oracle's own
+ * result to Bo/Co/Do/gap_o (one slot per sample; a block slot holds b components).
+ * energy_replay[i] = energy after applying the given component i, from the oracle's own exact
+ * p, q of that component on the replayed residual. */
+int externd_oracle_replay(const float* A, int64_t m, int64_t n, float mu, float tau,
+                          const float* h, int als_iters, int block,
+                          const uint32_t* B, const uint32_t* C, const float* D,
+                          const int64_t* sample, int64_t nsample,
+                          uint32_t* Bo, uint32_t* Co, float* Do, double* gap_o,
+                          double* energy_replay, const externd_oracle_opts* opts);
+
+/* Plain matvecs used by kernel-level parity tests: out = R^T u (transpose = 1) or R (h .* v). */
+int externd_oracle_matvec(const float* R, int64_t m, int64_t n, const int8_t* t, const float* h,
+                          int transpose, double* out, int threads);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,171 @@
+"""Pins of the oracle's ternary projection T_tau(x; h), independent of the oracle's code.
+
+* Brute force over every nonzero ternary vector (3^L - 1 of them, L <= 10): the maximum of
+  (sum_i h_i x_i v_i)^2 / (sum_i h_i v_i^2) over v supported on {|x_i| >= tau max|x|} must equal
+  the oracle's score, and the oracle's v must be a maximiser (the unique one, up to sign, when
+  the maximum is strict).  This is the exact-optimum reading of the adaptive ternarization
+  operator (ExTernD review, Method; pith.science free parameters, tau / Eq. 2) and, with
+  weights, of the corrected V-step (review, Method; pith.science, imatrix assumption).
+* Hand-worked examples in tests/golden/worked_examples.json.
+"""
+
+import itertools
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from expanded_rank_matrix_amd import inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_examples.json")
+_TERNARY = {}
+
+
+def ternary_table(L):
+    if L not in _TERNARY:
+        _TERNARY[L] = np.array(list(itertools.product((-1, 0, 1), repeat=L)), dtype=np.float64)
+    return _TERNARY[L]
+
+
+def brute_force(x, tau, h):
+    """Max over nonzero ternary v with support in the eligible set of (h.x.v)^2/(h.v^2)."""
+    x = np.asarray(x, dtype=np.float64)
+    L = x.shape[0]
+    h = np.ones(L) if h is None else np.asarray(h, dtype=np.float64)
+    a = np.abs(x)
+    M = a.max()
+    V = ternary_table(L)
+    nz = np.any(V != 0, axis=1)
+    elig = (a >= tau * M) & (a > 0)
+    ok = nz & np.all((V == 0) | elig[None, :], axis=1)
+    V = V[ok]
+    if V.shape[0] == 0:
+        return 0.0, None, None
+    num = (V @ (h * x)) ** 2
+    den = (V * V) @ h
+    s = num / den
+    best = s.max()
+    return best, V, s
+
+
+def check_against_brute(x, tau, h):
+    v, P, H, S, j, gap = oracle.project(np.asarray(x, np.float32), tau, h)
+    xf = np.asarray(x, np.float32).astype(np.float64)
+    best, V, s = brute_force(xf, tau, None if h is None else np.asarray(h, np.float32))
+    if V is None:
+        assert j == 0 and S == 0.0 and not v.any()
+        return
+    assert S == pytest.approx(best, rel=1e-12, abs=0.0)
+    hh = np.ones_like(xf) if h is None else np.asarray(h, np.float32).astype(np.float64)
+    vv = v.astype(np.float64)
+    # the oracle's v is itself a maximiser and its score is what it reports
+    own = (vv @ (hh * xf)) ** 2 / ((vv * vv) @ hh)
+    assert own == pytest.approx(best, rel=1e-12)
+    assert (vv @ (hh * xf)) > 0  # signs follow x
+    # unique maximiser up to sign -> identical vector
+    close = s >= best * (1 - 1e-9)
+    if np.count_nonzero(close) == 2:
+        cand = V[close]
+        cand = cand[np.argmax(cand @ (hh * xf))]
+        assert np.array_equal(cand, vv)
+    assert j == np.count_nonzero(v)
+    assert H == pytest.approx(float(np.sum(hh[v != 0])), rel=1e-12)
+    assert P == pytest.approx(float(np.sum(hh[v != 0] * np.abs(xf[v != 0]))), rel=1e-12)
+
+
+@pytest.mark.parametrize("L", list(range(1, 11)))
+@pytest.mark.parametrize("tau", [0.0, 0.1, 0.3, 0.5, 1.0])
+def test_projection_brute_force_random(L, tau):
+    X = inputs.random_vectors(100 + L, 24, L)
+    H = inputs.lognormal_weights(200 + L, L)
+    for x in X:
+        check_against_brute(x, tau, None)
+        check_against_brute(x, tau, H)
+
+
+ADVERSARIAL = [
+    [1, 1, 1, 1],                       # all equal magnitudes
+    [1, -1, 1, -1, 1],                  # equal magnitudes, mixed signs
+    [0, 0, 2, 0, -2],                   # zeros and ties
+    [10, 4, 4, 4, 4, 4, 4, 4, 4, 4],    # non-unimodal score
+    [3, -1, 2, 0.5],
+    [1e-30, 1, -1e-30, 2],              # tiny magnitudes
+    [5, 2.5, 2.5, 2.5, 1],              # tie at the boundary
+    [2, 1, 1, 0.5, 0.5, 0.25],
+    [1.0, 0.5, 0.5000001, 0.4999999],   # near-ties
+    [0.7, 0.7, 0.7, 0.35, 0.35, 0.35, 0.35],
+]
+
+
+@pytest.mark.parametrize("x", ADVERSARIAL)
+@pytest.mark.parametrize("tau", [0.0, 0.25, 0.5, 0.7, 1.0])
+@pytest.mark.parametrize("weighted", [False, True])
+def test_projection_brute_force_adversarial(x, tau, weighted):
+    h = inputs.lognormal_weights(7, len(x)) if weighted else None
+    check_against_brute(x, tau, h)
+
+
+def test_projection_tie_break_smallest_index():
+    # equal magnitudes: the whole tie group is selected (ties are never split)
+    v, P, H, S, j, gap = oracle.project(np.array([2, 1, 1, 0.1], np.float32))
+    assert list(v) == [1, 1, 1, 0]
+    assert j == 3
+
+
+def test_projection_threshold_boundary_inclusive():
+    # |x| == tau * max|x| is eligible
+    x = np.array([4, 2, 2, 2, 2, 2, 2], np.float32)
+    v, *_ = oracle.project(x, 0.5)
+    assert list(v) == [1, 1, 1, 1, 1, 1, 1]
+    v, *_ = oracle.project(x, 0.5000001)
+    assert list(v) == [1, 0, 0, 0, 0, 0, 0]
+
+
+def test_projection_golden():
+    g = json.load(open(GOLDEN))
+    for ex in g["projection"]:
+        x = np.array(ex["x"], np.float32)
+        h = None if ex["h"] is None else np.array(ex["h"], np.float32)
+        v, P, H, S, j, gap = oracle.project(x, ex["tau"], h)
+        assert list(v) == ex["v"], ex
+        assert j == ex["jstar"]
+        assert S == pytest.approx(ex["S"], rel=1e-7)
+        if "S_prefix" in ex:
+            # recompute the prefix scores from the definition to pin the golden values
+            a = np.abs(x.astype(np.float64))
+            order = np.lexsort((np.arange(len(a)), -a))
+            hh = np.ones(len(a)) if h is None else h.astype(np.float64)
+            Pp = np.cumsum(hh[order] * a[order])
+            Hp = np.cumsum(hh[order])
+            assert np.allclose(Pp ** 2 / Hp, ex["S_prefix"], rtol=1e-7)
+
+
+def test_projection_scale_invariance():
+    X = inputs.random_vectors(5, 50, 37)
+    h = inputs.lognormal_weights(6, 37)
+    for x in X:
+        for tau in (0.0, 0.3):
+            v1, *_ = oracle.project(x, tau, h)
+            v2, *_ = oracle.project(x * np.float32(4.0), tau, h)   # exact power-of-two scale
+            v3, *_ = oracle.project(-x, tau, h)
+            assert np.array_equal(v1, v2)
+            assert np.array_equal(v1, -v3)
+
+
+def test_corrected_v_step_never_worse_than_naive():
+    """The corrected weighted V-step's decrease (P^2/H) is >= that of the naive choices:
+    ranking by h|x|, or the unweighted projection, both scored in the weighted objective."""
+    X = inputs.random_vectors(11, 200, 64)
+    h = inputs.lognormal_weights(12, 64).astype(np.float64)
+    for x in X:
+        xd = x.astype(np.float64)
+        v, P, H, S, j, gap = oracle.project(x, 0.0, h.astype(np.float32))
+        order = np.argsort(-(np.abs(xd) * h), kind="stable")       # naive: rank by h|x|
+        Pp = np.cumsum((h * np.abs(xd))[order])
+        Hp = np.cumsum(h[order])
+        naive1 = np.max(Pp ** 2 / Hp)
+        vu, *_ = oracle.project(x, 0.0, None)                       # naive: ignore h
+        naive2 = (vu.astype(np.float64) @ (h * xd)) ** 2 / (np.abs(vu).astype(np.float64) @ h)
+        assert S >= max(naive1, naive2) * (1 - 1e-12)
