@@ -1,0 +1,70 @@
+// Internal declarations shared by the host API and the HIP kernels of libexternd.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace externd {
+
+// ---- sequential persistent kernel (seq.hip)
+struct SeqLaunch {
+  float* R;
+  float* RT;
+  const float* h;
+  const double* rs0;
+  const double* rowE;
+  double* xz;
+  double* xw;
+  double* xf;
+  unsigned* bar;
+  uint32_t* Bp;
+  uint32_t* Cp;
+  float* D;
+  double* energy;
+  u64* stats;
+  double* bytes;
+  int m, n, ldr, ldt, k, T, EHm, grid;
+  float tau;
+  unsigned spin_limit;
+};
+size_t seq_smem_bytes(int m, int n);
+int seq_max_blocks_per_cu(int m, int n);
+hipError_t seq_launch(const SeqLaunch& L, hipStream_t st);
+hipError_t matvec_rows(float* Rp, int rows, int len4, int ld, const float* wt, bool exact, double* out,
+                       hipStream_t st);
+
+// ---- staging and checks (stage.hip)
+// flags[0]: bit0 non-finite A, bit1 non-finite h, bit2 h <= 0; flags[1]: bits of max h
+hipError_t check_inputs(const float* A, int m, int n, const float* h, unsigned* flags, hipStream_t st);
+// R (m x ldr) = A with zero padding; rs = A 1 (fp64); rowE = sum_j h_j A_ij^2 (fp64)
+hipError_t stage_rows(const float* A, int m, int n, const float* h, float* R, int ldr, double* rs,
+                      double* rowE, hipStream_t st);
+// RT (n x ldt) = A^T with zero padding
+hipError_t stage_transpose(const float* A, int m, int n, float* RT, int ldt, hipStream_t st);
+// wt (ld) = t .* h as fp32 with zero padding (signed weights of a ternary vector)
+hipError_t make_weights(const int8_t* t, const float* h, int len, int ld, float* wt, hipStream_t st);
+// rowE = sum_j h_j R_ij^2 (fp64) on an m x ldr residual
+hipError_t row_energy(const float* R, int m, int n, int ldr, const float* h, double* rowE, hipStream_t st);
+// ternary vectors (int8) of a matrix of `count` rows -> scratch for projection tests
+hipError_t project_rows(const float* X, int count, int L, float tau, const float* h, int EHm, int8_t* V,
+                        double* PHC, hipStream_t st);
+
+// ---- block-ALS (block.hip)
+struct BlockLaunch {
+  float* R;            // m x ldr residual
+  int m, n, ldr, k, b, T, EHm;
+  float tau;
+  const float* h;
+  const double* rowE;  // m
+  uint32_t* Bp;
+  uint32_t* Cp;
+  float* D;
+  double* energy;
+  u64* stats;
+  void* ws;            // workspace (block_workspace_bytes)
+};
+size_t block_workspace_bytes(int m, int n, int b);
+hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops);
+
+}  // namespace externd

@@ -1,0 +1,114 @@
+/* externd.h -- C ABI of the MI355X (gfx950) ExTernD decomposition engine.
+ *
+ * The engine factors a real matrix A (m x n) as A ~= B diag(D) C with ternary B (m x k) and
+ * C (k x n), real D and an expanded inner rank k = floor(mu * min(m, n)) (the pages' abstract;
+ * ExTernD review, Method).  Components are fitted greedily by alternating least squares against
+ * the current residual, each with the closed-form scale d = u^T R v / (|u|^2 |v|^2), and the
+ * residual is deflated before the next component (review, Method and Key idea; pith.science
+ * referee report, "What carries the argument").  With block >= 2 the components are fitted b at
+ * a time by block-ALS with the decorrelated least-squares target of Eq. 3 (pith.science, minor
+ * comment 1); with importance weights the residual is measured in the column-weighted norm and
+ * the V-step uses the corrected weighted projection (review, Method; pith.science, imatrix
+ * assumption).
+ *
+ * Conventions for every entry point:
+ *  - Array pointers are HIP device pointers on the current device unless marked (host).
+ *  - Matrices are dense row-major fp32 with leading dimension equal to their column count.
+ *  - The caller owns and allocates every argument buffer; inputs must not alias outputs.
+ *  - Calls are synchronous: they return after all work issued on `stream` has completed.
+ *  - On a nonzero status the output contents are unspecified; externd_last_error() returns a
+ *    thread-local message describing the failure.  No C++ exception crosses the ABI.
+ *  - Packed ternary vectors: element t sits in bits 2(t%16)..2(t%16)+1 of 32-bit word t/16;
+ *    00 = 0, 01 = +1, 11 = -1, 10 never written; tail bits are zero.  This is the mask+sign
+ *    storage model behind the pages' "2 - sparsity bits per element" accounting
+ *    (pith.science free parameters, Eq. 5).
+ */
+#ifndef EXTERND_H
+#define EXTERND_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define EXTERND_OK 0
+#define EXTERND_EINVAL (-1)     /* bad size, mu, tau, iteration count, block, null pointer, weight <= 0 */
+#define EXTERND_ENOMEM (-2)     /* workspace allocation failed */
+#define EXTERND_EDEVICE (-3)    /* HIP runtime error or device-side failure (see externd_last_error) */
+#define EXTERND_ENONFINITE (-4) /* NaN or Inf in A or in the importance weights */
+
+/* (host) optional diagnostics filled by externd_decompose. */
+typedef struct {
+  int64_t k;                    /* components emitted */
+  int64_t passes;               /* residual matvec passes performed (V- and U-steps) */
+  int64_t early_exits;          /* components whose ALS reached an exact fixed point early */
+  int64_t fallback_inits;       /* components started from the largest-entry row */
+  int64_t zero_components;      /* components emitted as zero because the residual was zero */
+  int64_t block;                /* resolved block size (1 = sequential) */
+  double energy_final_explicit; /* 1 - |R|_H^2 / |A|_H^2 recomputed from the final residual */
+  double seconds;               /* host wall time of the call */
+  double kernel_ms;             /* device time of the decomposition kernels (HIP events) */
+  double bytes_algorithmic;     /* residual bytes the method must move (sequential path) */
+  double flops_algorithmic;     /* contraction flops of the block path */
+} externd_stats;
+
+/* k = floor(mu * min(m, n) + 1e-9); -1 if m < 1, n < 1, mu not finite or > 0, or k < 1. */
+int64_t externd_rank(int64_t m, int64_t n, float mu);
+
+/* ceil(len / 16): 32-bit words per packed ternary vector of length len. */
+int64_t externd_packed_words(int64_t len);
+
+/* Decompose A (m x n, device, fp32 row-major) into packed ternary B and C, scales D and the
+ * energy-preserved curve.
+ *   mu                 rank multiplier, finite, > 0, with k = externd_rank(m, n, mu) >= 1
+ *   tau                sparsity threshold in [0, 1]: only |x| >= tau * max|x| may be selected
+ *   importance_weights n per-column weights (> 0, finite), or NULL for uniform weights
+ *   als_iters          >= 1 alternations (V-step then U-step) per component or block
+ *   block              0 or 1: sequential deflation; b >= 2: block-ALS with blocks of b
+ *                      (clamped to k); -1: b = min(256, min(m, n) / 8), at least 1
+ *   B_packed           k x packed_words(m) uint32: row i = column i of B
+ *   C_packed           k x packed_words(n) uint32: row i = row i of C
+ *   D                  k fp32 scales
+ *   energy             k fp64: energy[i] = 1 - |R_i|_H^2 / |A|_H^2 after component i
+ *   stream             hipStream_t, or NULL for the default stream
+ *   stats              (host) nullable diagnostics
+ * Sizes: 1 <= m, n; max(m, n) <= 16384 for the ternary projection; the sequential path keeps
+ * two fp32 copies of the residual (R and its transpose), the block path one.  A = 0 is valid:
+ * every factor is 0, D = 0 and energy = 1.  The library allocates its own workspace on the
+ * call's stream and frees it before returning. */
+int externd_decompose(const float* A, int64_t m, int64_t n, float mu, float tau,
+                      const float* importance_weights, int als_iters, int block,
+                      uint32_t* B_packed, uint32_t* C_packed, float* D, double* energy,
+                      void* stream, externd_stats* stats);
+
+/* Ternary projection T_tau(x; h) of `count` independent vectors, the operator every V- and
+ * U-step applies (reading of the adaptive ternarization operator, review Method; pith.science
+ * free parameters, tau / Eq. 2): among |x_i| >= tau max|x|, the top-j set by |x| maximising
+ * (sum h|x|)^2 / (sum h), smallest j on ties, with the signs of x.
+ *   X   count x L fp32 (device), rows are the vectors
+ *   h   L fp32 weights shared by all rows, or NULL
+ *   V   count x L int8 output in {-1, 0, 1}
+ *   PHC count x 3 fp64 output: P = sum h|x| over the support, H = sum h, support size
+ * 1 <= L <= 16384, count >= 1, 0 <= tau <= 1. */
+int externd_project(const float* X, int64_t count, int64_t L, float tau, const float* h,
+                    int8_t* V, double* PHC, void* stream);
+
+/* The residual matvecs of the V- and U-steps with fp64 accumulation:
+ *   transpose = 1: out (n) = R^T t, t (m) ternary int8
+ *   transpose = 0: out (m) = R (h .* t), t (n) ternary int8, h nullable (uniform)
+ * R is m x n fp32 row-major (device).  Same device routine as the decomposition kernel. */
+int externd_matvec(const float* R, int64_t m, int64_t n, const int8_t* t, const float* h,
+                   int transpose, double* out, void* stream);
+
+/* Human-readable name of a status code (static string). */
+const char* externd_status_string(int status);
+
+/* Thread-local description of the last failure on the calling thread ("" if none). */
+const char* externd_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EXTERND_H */

@@ -178,9 +178,10 @@ def resolve_block(block: int, m: int, n: int, k: int) -> int:
 
 
 def replay(A, mu: float, tau: float, h, als_iters: int, block: int, B, C, D, sample,
-           threads: int = 0):
+           threads: int = 0, upto: int = 0):
     """Replay given factors; fit the sampled components (sequential) or blocks afresh.
 
+    ``upto`` > 0 stops the walk after that many components (energy_replay is NaN beyond).
     Returns dict(Bo, Co, Do, gap_o, energy_replay).  For the block path each sample slot holds
     b components (rows sample_index*b .. +b of the factor arrays)."""
     A = np.ascontiguousarray(A, dtype=np.float32)
@@ -199,8 +200,8 @@ def replay(A, mu: float, tau: float, h, als_iters: int, block: int, B, C, D, sam
     Co = np.zeros((max(slots, 1), words(n)), dtype=np.uint32)
     Do = np.zeros(max(slots, 1), dtype=np.float32)
     go = np.full(max(slots, 1), np.inf)
-    er = np.zeros(k, dtype=np.float64)
-    o = _make_opts(threads, False, 0, None, None, None, False)
+    er = np.full(k, np.nan)
+    o = _make_opts(threads, False, upto, None, None, None, False)
     rc = _load().externd_oracle_replay(_ptr(A), m, n, mu, tau, _ptr(h), als_iters, block,
                                        _ptr(B), _ptr(C), _ptr(D), _ptr(sample), ns, _ptr(Bo),
                                        _ptr(Co), _ptr(Do), _ptr(go), _ptr(er),

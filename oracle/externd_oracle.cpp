@@ -757,9 +757,13 @@ int replay_t(const float* A, int64_t m, int64_t n, float mu, float tau, const fl
   const int64_t b = resolve_block(block, m, n, k);
   const int64_t wm = words_of(m), wn = words_of(n);
   int64_t si = 0;
+  // walk only as far as needed: up to the last sampled component (block), or everything when
+  // the caller asks for the replayed energy curve of all components (opts->k_limit <= 0)
+  int64_t upto = k;
+  if (opts && opts->k_limit > 0) upto = std::min(k, opts->k_limit);
   if (b == 1) {
     std::vector<int8_t> u(m), v(n);
-    for (int64_t i = 0; i < k; ++i) {
+    for (int64_t i = 0; i < upto; ++i) {
       if (si < nsample && sample[si] == i) {
         if (st.E0 > 0.0) {
           Comp c = fit_component(st, false);
@@ -790,7 +794,7 @@ int replay_t(const float* A, int64_t m, int64_t n, float mu, float tau, const fl
     }
   } else {
     const int64_t nblocks = (k + b - 1) / b;
-    for (int64_t s = 0; s < nblocks; ++s) {
+    for (int64_t s = 0; s < nblocks && s * b < upto; ++s) {
       const int64_t bs = std::min(b, k - s * b);
       if (si < nsample && sample[si] == s) {
         if (st.E0 > 0.0) {

@@ -55,7 +55,8 @@ int externd_oracle_decompose(const float* A, int64_t m, int64_t n, float mu, flo
  * `sample` (ascending), fit it afresh from the replayed residual and write the oracle's own
  * result to Bo/Co/Do/gap_o (one slot per sample; a block slot holds b components).
  * energy_replay[i] = energy after applying the given component i, from the oracle's own exact
- * p, q of that component on the replayed residual. */
+ * p, q of that component on the replayed residual.  With opts->k_limit > 0 the walk stops
+ * after that many components (entries beyond it are left untouched). */
 int externd_oracle_replay(const float* A, int64_t m, int64_t n, float mu, float tau,
                           const float* h, int als_iters, int block,
                           const uint32_t* B, const uint32_t* C, const float* D,
