@@ -133,10 +133,16 @@ int externd_decompose(const float* A, int64_t m, int64_t n, float mu, float tau,
     HIP_OR_FAIL(hipGetDevice(&dev));
     int ncu = 0;
     HIP_OR_FAIL(hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev));
-    const int per = seq_max_blocks_per_cu(mi, ni);
+    const int per = seq_max_blocks_per_cu(mi, ni, h != nullptr);
     if (per < 1) return fail(EXTERND_EINVAL, "problem too large for the sequential kernel's on-chip state (%d x %d)", mi, ni);
     const int want = (int)std::max<int64_t>(1, std::min<int64_t>(ncu, (std::max(m, n) + 7) / 8));
     grid = std::min(want, ncu * per);
+    {
+      const long long rows = (std::max(mi, ni) + grid - 1) / grid;
+      const long long upr = (std::max(ldr, ldt) / 4 + 255) / 256;
+      if (rows * upr > kSeqMaxUnits)
+        return fail(EXTERND_EINVAL, "problem too large for the sequential kernel (%d x %d)", mi, ni);
+    }
     o_xf = take((size_t)2 * grid * sizeof(double));
   } else {
     o_blk = take(block_workspace_bytes(mi, ni, bi));
@@ -328,12 +334,15 @@ int externd_matvec(const float* R, int64_t m, int64_t n, const int8_t* t, const 
   if (!R || !t || !out) return fail(EXTERND_EINVAL, "null pointer argument");
   if (m < 1 || n < 1 || m > 16384 || n > 16384) return fail(EXTERND_EINVAL, "need 1 <= m, n <= 16384");
   const int mi = (int)m, ni = (int)n;
-  // stage the operand the way the decomposition kernel holds it: padded rows, fp32 weights
+  // stage the operand the way the decomposition kernel holds it: padded rows (R or R^T), the
+  // ternary vector and the weights padded with zeros
   const int rows = transpose ? ni : mi, len = transpose ? mi : ni;
   const int ld = (len + 3) & ~3;
+  const bool weighted = h && !transpose;
   void* p = nullptr;
-  const size_t bytes = al256((size_t)rows * ld * 4) + al256((size_t)ld * 4) + al256(64) + al256((size_t)m * 16);
-  if (hipMallocAsync(&p, bytes, st) != hipSuccess) {
+  const size_t b_R = al256((size_t)rows * ld * 4), b_t = al256((size_t)ld), b_h = al256((size_t)ld * 4);
+  const size_t b_s = al256((size_t)mi * 16);
+  if (hipMallocAsync(&p, b_R + b_t + b_h + b_s, st) != hipSuccess) {
     (void)hipGetLastError();
     return fail(EXTERND_ENOMEM, "workspace allocation failed");
   }
@@ -342,13 +351,20 @@ int externd_matvec(const float* R, int64_t m, int64_t n, const int8_t* t, const 
     hipStream_t s;
     ~F() { (void)hipFreeAsync(p, s); }
   } fg{p, st};
-  float* Rs = static_cast<float*>(p);
-  float* wt = reinterpret_cast<float*>(static_cast<char*>(p) + al256((size_t)rows * ld * 4));
-  double* scratch = reinterpret_cast<double*>(reinterpret_cast<char*>(wt) + al256((size_t)ld * 4) + al256(64));
+  char* base = static_cast<char*>(p);
+  float* Rs = reinterpret_cast<float*>(base);
+  int8_t* tp = reinterpret_cast<int8_t*>(base + b_R);
+  float* hp = reinterpret_cast<float*>(base + b_R + b_t);
+  double* scratch = reinterpret_cast<double*>(base + b_R + b_t + b_h);
   if (transpose) HIP_OR_FAIL(stage_transpose(R, mi, ni, Rs, ld, st));
   else HIP_OR_FAIL(stage_rows(R, mi, ni, nullptr, Rs, ld, scratch, scratch + mi, st));
-  HIP_OR_FAIL(make_weights(t, transpose ? nullptr : h, len, ld, wt, st));
-  HIP_OR_FAIL(matvec_rows(Rs, rows, ld / 4, ld, wt, transpose || !h, out, st));
+  HIP_OR_FAIL(hipMemsetAsync(tp, 0, (size_t)ld, st));
+  HIP_OR_FAIL(hipMemcpyAsync(tp, t, (size_t)len, hipMemcpyDeviceToDevice, st));
+  if (weighted) {
+    HIP_OR_FAIL(hipMemsetAsync(hp, 0, (size_t)ld * 4, st));
+    HIP_OR_FAIL(hipMemcpyAsync(hp, h, (size_t)len * 4, hipMemcpyDeviceToDevice, st));
+  }
+  HIP_OR_FAIL(matvec_rows(Rs, rows, ld / 4, ld, tp, weighted ? hp : nullptr, out, st));
   HIP_OR_FAIL(hipStreamSynchronize(st));
   return EXTERND_OK;
 }

@@ -28,10 +28,14 @@ struct SeqLaunch {
   float tau;
   unsigned spin_limit;
 };
-size_t seq_smem_bytes(int m, int n);
-int seq_max_blocks_per_cu(int m, int n);
+size_t seq_smem_bytes(int m, int n, bool weighted);
+int seq_max_blocks_per_cu(int m, int n, bool weighted);
+// rows per workgroup times 256-float4 units per row must fit the kernel's partial-sum table
+constexpr int kSeqMaxUnits = 2048;
 hipError_t seq_launch(const SeqLaunch& L, hipStream_t st);
-hipError_t matvec_rows(float* Rp, int rows, int len4, int ld, const float* wt, bool exact, double* out,
+// out[r] = R_r . (t .* h) for rows of a padded row-major matrix; t (and h, nullable) padded to
+// len4 * 4 entries.  Same slab routine as the sequential kernel.
+hipError_t matvec_rows(float* Rp, int rows, int len4, int ld, const int8_t* t, const float* h, double* out,
                        hipStream_t st);
 
 // ---- staging and checks (stage.hip)
@@ -42,8 +46,6 @@ hipError_t stage_rows(const float* A, int m, int n, const float* h, float* R, in
                       double* rowE, hipStream_t st);
 // RT (n x ldt) = A^T with zero padding
 hipError_t stage_transpose(const float* A, int m, int n, float* RT, int ldt, hipStream_t st);
-// wt (ld) = t .* h as fp32 with zero padding (signed weights of a ternary vector)
-hipError_t make_weights(const int8_t* t, const float* h, int len, int ld, float* wt, hipStream_t st);
 // rowE = sum_j h_j R_ij^2 (fp64) on an m x ldr residual
 hipError_t row_energy(const float* R, int m, int n, int ldr, const float* h, double* rowE, hipStream_t st);
 // ternary vectors (int8) of a matrix of `count` rows -> scratch for projection tests

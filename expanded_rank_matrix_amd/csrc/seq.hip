@@ -5,19 +5,21 @@
 // als_iters times v = T_tau(R^T u; h) (V-step, corrected weighted projection) and
 // u = T_tau(R H v) (U-step); the scale d = u^T R H v / (|u|^2 v^T H v) is rounded to fp32,
 // the energy bookkeeping is E <- E - (2 d p - d^2 q), and the residual is deflated,
-// R_ij <- fl32(R_ij - d u_i v_j), before the next component.
+// R_ij <- fl32(R_ij - d u_i v_j), before the next component.  An iteration that reproduces the
+// previous u (or v) has reached an exact fixed point; the remaining iterations would repeat it,
+// so the loop stops there (the result is the same).
 //
 // MI355X layout.  The residual lives in HBM twice: R (m x n) and its transpose RT (n x m), both
 // row-major.  Workgroup g owns a fixed slab of R rows and a fixed slab of RT rows, so both
-// matvecs are reduction-free: a U-step row dot product z_i = R_i . (h v) and a V-step row dot
-// product w_j = RT_j . u are finished inside the owning workgroup.  The only cross-workgroup
-// traffic per half-step is the finished vector (z or w, fp64) plus one grid barrier; every
-// workgroup then runs the same deterministic selection redundantly, so all of them agree on u
-// or v without a broadcast.  Deflation is applied lazily: the pending component is subtracted
-// from RT rows during the next V-step read and from R rows during the next U-step read (one
-// read-modify-write pass fused with a matvec).  The tracked row sums rs (fp64 recurrence
-// rs <- rs - d (sum v) u) are replicated in every workgroup's LDS, so the next u0 is chosen
-// without another exchange.
+// matvecs are reduction-free across workgroups: a U-step row dot product z_i = R_i . (h v) and a
+// V-step row dot product w_j = RT_j . u are finished inside the owning workgroup.  The only
+// cross-workgroup traffic per half-step is the finished vector (z or w, fp64) plus one grid
+// barrier; every workgroup then runs the same deterministic selection redundantly, so all of
+// them agree on u or v without a broadcast.  Deflation is applied lazily: the pending component
+// is subtracted from RT rows during the next V-step read and from R rows during the next U-step
+// read (one read-modify-write pass fused with a matvec).  The tracked row sums rs (fp64
+// recurrence rs <- rs - d (sum v) u) are replicated in every workgroup's LDS, so the next u0 is
+// chosen without another exchange.
 #include "externd_internal.hpp"
 #include "select.hpp"
 
@@ -44,101 +46,187 @@ struct SeqArgs {
   unsigned spin_limit;
 };
 
-
 __device__ __forceinline__ int code_at(const uint32_t* pk, int i) {
   const unsigned c = (pk[i >> 4] >> ((i & 15) * 2)) & 3u;
   return c == 0u ? 0 : (c == 1u ? 1 : -1);
 }
 
-// Row dot product with optional fused pending deflation.
-//   row: fp32 row of length len (padded to a multiple of 4, padding zero)
-//   wt:  LDS weights (len, padded) used as (double)(x * wt) when exact_f32 (ternary weights) or
-//        (double)x * (double)wt otherwise
-//   dfl: if nonzero, subtract sgn * d on columns whose code in pk_other is nonzero, where
-//        sgn = own_code * code(col); the updated row is written back.
-// Returns the fp64 dot product of one wave (lane 0 holds the full sum after reduction).
-__device__ __forceinline__ double row_dot(float* row, int len4, const float* wt, bool exact_f32,
-                                          int own_code, float d, const uint32_t* pk_other,
-                                          int lane) {
-  double acc = 0.0;
-  float4* r4 = reinterpret_cast<float4*>(row);
-  const float4* w4 = reinterpret_cast<const float4*>(wt);
-  for (int q = lane; q < len4; q += 64) {
-    float4 x = r4[q];
-    if (own_code != 0) {
-      const unsigned word = pk_other[q >> 2] >> ((q & 3) * 8);
-      float xs[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const unsigned c = (word >> (2 * t)) & 3u;
-        if (c != 0u) {
-          const int sg = (c == 1u ? 1 : -1) * own_code;
-          xs[t] = sg > 0 ? xs[t] - d : xs[t] + d;
-        }
-      }
-      x = make_float4(xs[0], xs[1], xs[2], xs[3]);
-      r4[q] = x;
-    }
-    const float4 w = w4[q];
-    if (exact_f32) {
-      acc += (double)(x.x * w.x);
-      acc += (double)(x.y * w.y);
-      acc += (double)(x.z * w.z);
-      acc += (double)(x.w * w.w);
-    } else {
-      acc += (double)x.x * (double)w.x;
-      acc += (double)x.y * (double)w.y;
-      acc += (double)x.z * (double)w.z;
-      acc += (double)x.w * (double)w.w;
-    }
-  }
-  return wave_sum_f64(acc);
-}
-
 // Dynamic LDS of the sequential kernel; every region starts on a 16-byte boundary.
 struct SeqLds {
-  size_t rs, hv, uf, tmp, pk, total;
+  size_t rs, dl, hl, tmp, pk, part, total;
 };
 __host__ __device__ inline size_t al16(size_t x) { return (x + 15) & ~(size_t)15; }
-__host__ __device__ inline SeqLds seq_lds_layout(int m, int n) {
-  const size_t m4 = (size_t)((m + 3) & ~3), n4 = (size_t)((n + 3) & ~3);
+constexpr int kMaxUnits = 2048;  // row units per workgroup per matvec (checked on the host)
+__host__ __device__ inline SeqLds seq_lds_layout(int m, int n, bool weighted) {
+  const size_t L = (size_t)(m > n ? m : n);
+  const size_t L4 = (L + 3) & ~(size_t)3, n4 = (size_t)((n + 3) & ~3);
   const size_t wm = (size_t)((m + 15) / 16), wn = (size_t)((n + 15) / 16);
-  SeqLds L;
-  L.rs = al16(sizeof(SelScratch));
-  L.hv = al16(L.rs + 8 * (size_t)m);
-  L.uf = al16(L.hv + 4 * n4);
-  L.tmp = al16(L.uf + 4 * m4);
-  L.pk = al16(L.tmp + (m4 > n4 ? m4 : n4));
-  L.total = al16(L.pk + 4 * (4 * wm + 3 * wn));
-  return L;
+  SeqLds s;
+  s.rs = al16(sizeof(SelScratch));
+  s.dl = al16(s.rs + 8 * (size_t)m);
+  s.hl = al16(s.dl + 8 * L);
+  s.tmp = al16(s.hl + (weighted ? 4 * n4 : 0));
+  s.pk = al16(s.tmp + L4);
+  s.part = al16(s.pk + 4 * (4 * wm + 3 * wn + 4));
+  s.total = al16(s.part + 8 * (size_t)kMaxUnits);
+  return s;
 }
 
 struct SeqShared {
-  int flag;
   int ivals[8];
-  double dvals[8];
 };
 
-template <int NT, int NE>
+// Weights of one float4 (elements 4q .. 4q+3) of a packed ternary vector, optionally times the
+// LDS column weights hl: (double) products with fp32 data are exact either way.
+__device__ __forceinline__ float4 code_weights(const uint32_t* pk, int q, const float* hl) {
+  const unsigned word = pk[q >> 2] >> ((q & 3) * 8);
+  float c[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const unsigned cd = (word >> (2 * t)) & 3u;
+    c[t] = cd == 0u ? 0.0f : (cd == 1u ? 1.0f : -1.0f);
+  }
+  float4 w = make_float4(c[0], c[1], c[2], c[3]);
+  if (hl) {
+    const float4 h = reinterpret_cast<const float4*>(hl)[q];
+    w = make_float4(w.x * h.x, w.y * h.y, w.z * h.z, w.w * h.w);
+  }
+  return w;
+}
+
+// Rows [r0, r1) of a row-major matrix (leading dimension ld floats, len4 float4 per row) dotted
+// with a packed ternary vector pk_w (times the LDS weights hl when given); the results go to
+// out[row] (exchange buffer, device-coherent stores).  Each row is cut into units of 64 * kQ
+// float4; every wave takes kUPW units per round and issues all their loads before consuming any,
+// so one memory latency covers the round.  The per-unit partial sums are combined in a fixed
+// order (deterministic).  Pending deflation of rows whose own code in pk_own is nonzero is fused
+// in: x <- fl32(x - own * other * d) on the columns where pk_other is nonzero, written back.
+constexpr int kQ = 4;
+constexpr int kUPW = 4;
+template <int NT>
+__device__ void slab_matvec(float* base, int ld, int len4, int r0, int r1, const uint32_t* pk_w,
+                            const float* hl, bool apply, const uint32_t* pk_own,
+                            const uint32_t* pk_other, float d, double* part, double* out) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int rows = r1 > r0 ? r1 - r0 : 0;
+  const int upr = (len4 + 64 * kQ - 1) / (64 * kQ);
+  const int units = rows * upr;
+  for (int ub = 0; ub < units; ub += NW * kUPW) {
+    float4 buf[kUPW][kQ];
+#pragma unroll
+    for (int j = 0; j < kUPW; ++j) {
+      const int u = ub + wid * kUPW + j;
+      const int r = u / upr, sgi = u - (u / upr) * upr;
+      const float4* r4 = reinterpret_cast<const float4*>(base + (size_t)(r0 + r) * ld);
+#pragma unroll
+      for (int t = 0; t < kQ; ++t) {
+        const int q = sgi * 64 * kQ + t * 64 + lane;
+        buf[j][t] = (u < units && q < len4) ? r4[q] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kUPW; ++j) {
+      const int u = ub + wid * kUPW + j;
+      if (u >= units) break;
+      const int r = u / upr, sgi = u - r * upr;
+      const int row = r0 + r;
+      const int oc = apply ? code_at(pk_own, row) : 0;
+      float4* r4 = reinterpret_cast<float4*>(base + (size_t)row * ld);
+      double acc0 = 0.0, acc1 = 0.0;
+#pragma unroll
+      for (int t = 0; t < kQ; ++t) {
+        const int q = sgi * 64 * kQ + t * 64 + lane;
+        if (q >= len4) continue;
+        float4 x = buf[j][t];
+        if (oc != 0) {
+          const unsigned word = pk_other[q >> 2] >> ((q & 3) * 8);
+          if (word & 0xFFu) {
+            float xv[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              const unsigned cd = (word >> (2 * c)) & 3u;
+              if (cd != 0u) {
+                const int sg = (cd == 1u ? 1 : -1) * oc;
+                xv[c] = sg > 0 ? xv[c] - d : xv[c] + d;
+              }
+            }
+            x = make_float4(xv[0], xv[1], xv[2], xv[3]);
+            r4[q] = x;
+          }
+        }
+        const float4 w = code_weights(pk_w, q, hl);
+        if (!hl) {
+          acc0 += (double)(x.x * w.x);
+          acc1 += (double)(x.y * w.y);
+          acc0 += (double)(x.z * w.z);
+          acc1 += (double)(x.w * w.w);
+        } else {
+          acc0 += (double)x.x * (double)w.x;
+          acc1 += (double)x.y * (double)w.y;
+          acc0 += (double)x.z * (double)w.z;
+          acc1 += (double)x.w * (double)w.w;
+        }
+      }
+      const double v = wave_sum_f64(acc0 + acc1);
+      if (lane == 0) part[u] = v;
+    }
+  }
+  __syncthreads();
+  for (int r = threadIdx.x; r < rows; r += NT) {
+    double acc = 0.0;
+    for (int q = 0; q < upr; ++q) acc += part[r * upr + q];
+    st_dev(out + r0 + r, acc);
+  }
+  __syncthreads();
+}
+
+// Apply the pending deflation to rows [r0, r1) (used where no matvec pass is due).
+template <int NT>
+__device__ void slab_deflate(float* base, int ld, int len4, int r0, int r1, const uint32_t* pk_own,
+                             const uint32_t* pk_other, float d) {
+  for (int r = r0; r < r1; ++r) {
+    const int oc = code_at(pk_own, r);
+    if (oc == 0) continue;
+    float4* r4 = reinterpret_cast<float4*>(base + (size_t)r * ld);
+    for (int q = threadIdx.x; q < len4; q += NT) {
+      const unsigned word = pk_other[q >> 2] >> ((q & 3) * 8);
+      if (!(word & 0xFFu)) continue;
+      float4 x = r4[q];
+      float xv[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const unsigned cd = (word >> (2 * c)) & 3u;
+        if (cd != 0u) {
+          const int sg = (cd == 1u ? 1 : -1) * oc;
+          xv[c] = sg > 0 ? xv[c] - d : xv[c] + d;
+        }
+      }
+      r4[q] = make_float4(xv[0], xv[1], xv[2], xv[3]);
+    }
+  }
+  __syncthreads();
+}
+
+template <int NT, bool WV>
 __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
-  constexpr int kNT = NT;
-  constexpr int kNW = NT / 64;
+  constexpr int NW = NT / 64;
   extern __shared__ __align__(16) char smem[];
   SelScratch& s = *reinterpret_cast<SelScratch*>(smem);
   const int m = a.m, n = a.n;
   const int m4 = (m + 3) & ~3, n4 = (n + 3) & ~3;
-  const SeqLds lay = seq_lds_layout(m, n);
-  double* rs = reinterpret_cast<double*>(smem + lay.rs);  // m: replicated row sums
-  float* hv = reinterpret_cast<float*>(smem + lay.hv);    // n4: signed weights of v
-  float* uf = reinterpret_cast<float*>(smem + lay.uf);    // m4: u as fp32 {-1,0,1}
-  int8_t* tmp = reinterpret_cast<int8_t*>(smem + lay.tmp);  // max(m4, n4) staging for packing
+  const SeqLds lay = seq_lds_layout(m, n, WV);
+  double* rs = reinterpret_cast<double*>(smem + lay.rs);    // m: replicated row sums
+  double* dl = reinterpret_cast<double*>(smem + lay.dl);    // exchanged vector (z or w)
+  float* hl = reinterpret_cast<float*>(smem + lay.hl);      // n4 column weights (weighted)
+  int8_t* tmp = reinterpret_cast<int8_t*>(smem + lay.tmp);  // staging for packing
   uint32_t* pk = reinterpret_cast<uint32_t*>(smem + lay.pk);
+  double* part = reinterpret_cast<double*>(smem + lay.part);
   const int wm = a.wm, wn = a.wn;
   uint32_t* pu = pk;            // current u
   uint32_t* pv = pu + wm;       // current v
   uint32_t* pu_prev = pv + wn;  // u that produced the current v
-  uint32_t* pv_prev = pu_prev + wm;
-  uint32_t* du = pv_prev + wn;  // pending deflation component
+  uint32_t* du = pu_prev + wm;  // pending deflation component
   uint32_t* dv = du + wm;
   uint32_t* pu0 = dv + wn;      // u0 of this component (for the byte count)
   __shared__ SeqShared sh;
@@ -148,192 +236,181 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
   const int G = gridDim.x, g = blockIdx.x;
   const int r0 = (int)((long long)g * m / G), r1 = (int)((long long)(g + 1) * m / G);
   const int c0 = (int)((long long)g * n / G), c1 = (int)((long long)(g + 1) * n / G);
-  const bool weighted = a.h != nullptr;
+  const float* hw = WV ? hl : nullptr;
   unsigned epoch = 0;
 
-  // ---- set-up: replicated row sums, E0 in a fixed order, padding cleared
-  for (int i = tid; i < m; i += kNT) rs[i] = a.rs0[i];
-  for (int i = tid; i < m4; i += kNT) uf[i] = 0.0f;
-  for (int i = tid; i < n4; i += kNT) hv[i] = 0.0f;
-  for (int i = tid; i < 4 * wm + 3 * wn; i += kNT) pk[i] = 0u;
+  for (int i = tid; i < m; i += NT) rs[i] = a.rs0[i];
+  if (WV)
+    for (int j = tid; j < n4; j += NT) hl[j] = j < n ? a.h[j] : 0.0f;
+  for (int i = tid; i < 4 * wm + 3 * wn; i += NT) pk[i] = 0u;
   double e0 = 0.0;
-  for (int i = tid; i < m; i += kNT) e0 += a.rowE[i];
+  for (int i = tid; i < m; i += NT) e0 += a.rowE[i];
   e0 = wave_sum_f64(e0);
   if (lane == 0) s.red_d[wid] = e0;
   __syncthreads();
   double E0 = 0.0;
-  for (int w = 0; w < kNW; ++w) E0 += s.red_d[w];
+  for (int w = 0; w < NW; ++w) E0 += s.red_d[w];
   double E = E0;
   bool dead = !(E0 > 0.0);
   bool have_pending = false, r_applied = true, rt_applied = true;
   float pd = 0.0f;
   __syncthreads();
 
-  // element slots of this thread for selections: index = tid + e * kNT
-  float av[NE], hw[NE];
-  double zd[NE];
-  int sg[NE];
+  // pack the +-1/0 staging array into words; returns whether any word changed
+  auto pack_into = [&](uint32_t* dst, int len, int words) -> int {
+    int changed = 0;
+    for (int w = tid; w < words; w += NT) {
+      unsigned word = 0u;
+      for (int q = 0; q < 16; ++q) {
+        const int i = w * 16 + q;
+        if (i < len) word |= tcode(tmp[i]) << (2 * q);
+      }
+      if (word != dst[w]) changed = 1;
+      dst[w] = word;
+    }
+    return changed;
+  };
+  // staging from a selection over vals (fp32 rounding decides membership and sign)
+  auto stage_from = [&](const double* vals, int len, const SelResult& r) -> int {
+    int sum = 0;
+    for (int i = tid; i < len; i += NT) {
+      const float x = (float)vals[i];
+      const int v = selected(x, r) ? (x > 0.0f ? 1 : -1) : 0;
+      tmp[i] = (int8_t)v;
+      sum += v;
+    }
+    __syncthreads();
+    return sum;
+  };
+  // Largest |R_ij| over the residual (smallest row-major index on ties), after the pending
+  // deflation.  Returns the row, -1 if R == 0, -2 on a barrier failure.
+  auto fallback_row = [&]() -> int {
+    if (have_pending && !r_applied) {
+      slab_deflate<NT>(a.R, a.ldr, n4 / 4, r0, r1, du, dv, pd);
+      r_applied = true;
+    }
+    double best = 0.0, bidx = -1.0;
+    for (int i = r0 + wid; i < r1; i += NW) {
+      const float* row = a.R + (size_t)i * a.ldr;
+      for (int j = lane; j < n; j += 64) {
+        const double v = fabs((double)row[j]);
+        const double idx = (double)i * (double)n + (double)j;
+        if (v > best || (v == best && v > 0.0 && idx < bidx)) {
+          best = v;
+          bidx = idx;
+        }
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const double b2 = __shfl_xor(best, o), i2 = __shfl_xor(bidx, o);
+      if (b2 > best || (b2 == best && b2 > 0.0 && i2 < bidx)) {
+        best = b2;
+        bidx = i2;
+      }
+    }
+    if (lane == 0) {
+      part[2 * wid] = best;
+      part[2 * wid + 1] = bidx;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      double bb = 0.0, bi = -1.0;
+      for (int w = 0; w < NW; ++w) {
+        const double v = part[2 * w], ix = part[2 * w + 1];
+        if (v > bb || (v == bb && v > 0.0 && ix < bi)) {
+          bb = v;
+          bi = ix;
+        }
+      }
+      st_dev(a.xf + 2 * g, bb);
+      st_dev(a.xf + 2 * g + 1, bi);
+    }
+    ++epoch;
+    if (grid_barrier(a.bar, epoch, a.spin_limit, &bar_flag)) return -2;
+    if (tid == 0) {
+      double bb = 0.0, bi = -1.0;
+      for (int q = 0; q < G; ++q) {
+        const double v = ld_dev(a.xf + 2 * q), ix = ld_dev(a.xf + 2 * q + 1);
+        if (v > bb || (v == bb && v > 0.0 && ix < bi)) {
+          bb = v;
+          bi = ix;
+        }
+      }
+      sh.ivals[0] = bb > 0.0 ? (int)(bi / (double)n) : -1;
+    }
+    __syncthreads();
+    return sh.ivals[0];
+  };
+  auto set_unit_u = [&](int r) {
+    for (int w = tid; w < wm; w += NT) pu[w] = (w == (r >> 4)) ? (1u << (2 * (r & 15))) : 0u;
+    __syncthreads();
+  };
+  auto emit_zero = [&](int comp) {
+    if (g == 0) {
+      for (int w = tid; w < wm; w += NT) a.Bp[(size_t)comp * wm + w] = 0u;
+      for (int w = tid; w < wn; w += NT) a.Cp[(size_t)comp * wn + w] = 0u;
+      if (tid == 0) {
+        a.D[comp] = 0.0f;
+        a.energy[comp] = 1.0;
+        a.stats[3] += 1ull;
+      }
+    }
+  };
+  auto block_sum_int = [&](int v) -> int {
+    if (tid == 0) sh.ivals[1] = 0;
+    __syncthreads();
+    if (v != 0) atomicAdd(&sh.ivals[1], v);
+    __syncthreads();
+    const int r = sh.ivals[1];
+    __syncthreads();
+    return r;
+  };
 
   for (int comp = 0; comp < a.k; ++comp) {
     if (dead) {
-      if (g == 0) {
-        for (int w = tid; w < wm; w += kNT) a.Bp[(size_t)comp * wm + w] = 0u;
-        for (int w = tid; w < wn; w += kNT) a.Cp[(size_t)comp * wn + w] = 0u;
-        if (tid == 0) {
-          a.D[comp] = 0.0f;
-          a.energy[comp] = 1.0;
-          a.stats[3] += 1ull;
-        }
-      }
+      emit_zero(comp);
       continue;
     }
     // ---------------- initial u: ternarized fp32 row sums
-#pragma unroll
-    for (int e = 0; e < NE; ++e) {
-      const int i = tid + e * kNT;
-      const float x = i < m ? (float)rs[i] : 0.0f;
-      av[e] = fabsf(x);
-      sg[e] = x > 0.0f ? 1 : (x < 0.0f ? -1 : 0);
-      hw[e] = 1.0f;
-    }
-    SelResult su = ternary_select<kNT, NE, false>(av, hw, a.tau, 0, s);
+    const SelResult su = ternary_select<NT, false>(rs, nullptr, m, a.tau, 0, s);
     bool fallback = false;
-    auto write_u_from_slots = [&](const SelResult& r) {
-#pragma unroll
-      for (int e = 0; e < NE; ++e) {
-        const int i = tid + e * kNT;
-        if (i < m) {
-          const unsigned k = __float_as_uint(av[e]);
-          const bool on = r.count > 0u && k != 0u && k >= r.ekey && k >= r.tkey;
-          tmp[i] = on ? (int8_t)sg[e] : (int8_t)0;
-          uf[i] = on ? (float)sg[e] : 0.0f;
-        }
-      }
-      __syncthreads();
-      for (int w = tid; w < wm; w += kNT) {
-        unsigned word = 0u;
-        for (int t = 0; t < 16; ++t) {
-          const int i = w * 16 + t;
-          if (i < m) word |= tcode(tmp[i]) << (2 * t);
-        }
-        pu[w] = word;
-      }
-      __syncthreads();
-    };
-    // Largest |R_ij| over the whole residual (smallest row-major index on ties); applies the
-    // pending deflation to R rows first.  Returns the row, or -1 if R == 0 (or on error).
-    auto fallback_row = [&]() -> int {
-      double best = 0.0, bidx = -1.0;
-      for (int i = r0 + wid; i < r1; i += kNW) {
-        float* row = a.R + (size_t)i * a.ldr;
-        const int oc = (have_pending && !r_applied) ? code_at(du, i) : 0;
-        if (oc != 0) row_dot(row, n4 / 4, hv, true, oc, pd, dv, lane);  // writes the deflated row
-        for (int j = lane; j < n; j += 64) {
-          const double v = fabs((double)row[j]);
-          const double idx = (double)i * (double)n + (double)j;
-          if (v > best || (v == best && v > 0.0 && idx < bidx)) {
-            best = v;
-            bidx = idx;
-          }
-        }
-      }
-      // block argmax (value desc, index asc)
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        const double b2 = __shfl_xor(best, o), i2 = __shfl_xor(bidx, o);
-        if (b2 > best || (b2 == best && b2 > 0.0 && i2 < bidx)) {
-          best = b2;
-          bidx = i2;
-        }
-      }
-      __syncthreads();
-      if (lane == 0) {
-        s.red_d[wid] = best;
-        sh.dvals[0] = 0.0;
-      }
-      if (lane == 0) s.c_plo[wid] = (u64)__double_as_longlong(bidx);
-      __syncthreads();
-      if (tid == 0) {
-        double bb = 0.0, bi = -1.0;
-        for (int w = 0; w < kNW; ++w) {
-          const double v = s.red_d[w], ix = __longlong_as_double((long long)s.c_plo[w]);
-          if (v > bb || (v == bb && v > 0.0 && ix < bi)) {
-            bb = v;
-            bi = ix;
-          }
-        }
-        st_dev(a.xf + 2 * g, bb);
-        st_dev(a.xf + 2 * g + 1, bi);
-      }
-      r_applied = true;
-      ++epoch;
-      if (grid_barrier(a.bar, epoch, a.spin_limit, &bar_flag)) return -2;
-      if (tid == 0) {
-        double bb = 0.0, bi = -1.0;
-        for (int q = 0; q < G; ++q) {
-          const double v = ld_dev(a.xf + 2 * q), ix = ld_dev(a.xf + 2 * q + 1);
-          if (v > bb || (v == bb && v > 0.0 && ix < bi)) {
-            bb = v;
-            bi = ix;
-          }
-        }
-        sh.ivals[0] = bb > 0.0 ? (int)(bi / (double)n) : -1;
-      }
-      __syncthreads();
-      return sh.ivals[0];
-    };
-    auto set_unit_u = [&](int r) {
-      for (int i = tid; i < m; i += kNT) uf[i] = i == r ? 1.0f : 0.0f;
-      for (int w = tid; w < wm; w += kNT) pu[w] = (w == (r >> 4)) ? (1u << (2 * (r & 15))) : 0u;
-      __syncthreads();
-    };
     if (su.count == 0u) {
       const int r = fallback_row();
       if (r == -2) return;
       if (r < 0) {
         dead = true;
-        E = 0.0;
-        --comp;
+        emit_zero(comp);
         continue;
       }
       set_unit_u(r);
       fallback = true;
     } else {
-      write_u_from_slots(su);
+      stage_from(rs, m, su);
+      pack_into(pu, m, wm);
+      __syncthreads();
     }
-    for (int w = tid; w < wm; w += kNT) pu0[w] = pu[w];
+    for (int w = tid; w < wm; w += NT) pu0[w] = pu[w];
     __syncthreads();
 
     // ---------------- ALS
     double p = 0.0, Hv = 0.0;
-    unsigned cnt_u = 0, cnt_v = 0;
-    int sumv = 0;
-    int passes = 0, usteps = 0;
+    unsigned cnt_u = 0;
+    int sumv = 0, passes = 0, usteps = 0;
     bool early = false;
     double vbytes = 0.0;
     int t = 0;
     while (t < a.T) {
       // ---- V-step: w_j = RT_j . u on owned RT rows (pending deflation fused)
-      for (int j = c0 + wid; j < c1; j += kNW) {
-        float* row = a.RT + (size_t)j * a.ldt;
-        const int oc = (have_pending && !rt_applied) ? code_at(dv, j) : 0;
-        const double wj = row_dot(row, m4 / 4, uf, true, oc, pd, du, lane);
-        if (lane == 0) st_dev(a.xw + j, wj);
-      }
+      slab_matvec<NT>(a.RT, a.ldt, m4 / 4, c0, c1, pu, nullptr, have_pending && !rt_applied, dv, du, pd,
+                      part, a.xw);
       rt_applied = true;
       ++passes;
       ++epoch;
       if (grid_barrier(a.bar, epoch, a.spin_limit, &bar_flag)) return;
-#pragma unroll
-      for (int e = 0; e < NE; ++e) {
-        const int j = tid + e * kNT;
-        const double w = j < n ? ld_dev(a.xw + j) : 0.0;
-        const float x = (float)w;
-        av[e] = fabsf(x);
-        sg[e] = x > 0.0f ? 1 : (x < 0.0f ? -1 : 0);
-        hw[e] = (weighted && j < n) ? a.h[j] : 1.0f;
-      }
-      SelResult sv = (weighted ? ternary_select<kNT, NE, true>(av, hw, a.tau, a.EHm, s) : ternary_select<kNT, NE, false>(av, hw, a.tau, 0, s));
+      for (int j = tid; j < n; j += NT) dl[j] = ld_dev(a.xw + j);
+      __syncthreads();
+      const SelResult sv = ternary_select<NT, WV>(dl, hw, n, a.tau, a.EHm, s);
       if (sv.count == 0u) {
         // R^T u == 0: only possible for the initial u; restart from the largest-entry row
         if (fallback) {
@@ -347,95 +424,43 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
           break;
         }
         set_unit_u(r);
-        for (int w = tid; w < wm; w += kNT) pu0[w] = pu[w];
+        for (int w = tid; w < wm; w += NT) pu0[w] = pu[w];
         fallback = true;
         __syncthreads();
         continue;
       }
-      // build v: signed weights for the U-step and the packed form
-      if (tid == 0) sh.ivals[1] = 0;
-      __syncthreads();
-      int lsum = 0;
-#pragma unroll
-      for (int e = 0; e < NE; ++e) {
-        const int j = tid + e * kNT;
-        if (j < n) {
-          const unsigned k = __float_as_uint(av[e]);
-          const bool on = k != 0u && k >= sv.ekey && k >= sv.tkey;
-          const int vj = on ? sg[e] : 0;
-          tmp[j] = (int8_t)vj;
-          hv[j] = vj == 0 ? 0.0f : (vj > 0 ? hw[e] : -hw[e]);
-          lsum += vj;
-        }
-      }
-      if (lsum != 0) atomicAdd(&sh.ivals[1], lsum);
-      __syncthreads();
-      int changed = 0;
-      for (int w = tid; w < wn; w += kNT) {
-        unsigned word = 0u;
-        for (int q = 0; q < 16; ++q) {
-          const int j = w * 16 + q;
-          if (j < n) word |= tcode(tmp[j]) << (2 * q);
-        }
-        if (word != pv[w]) changed = 1;
-        pv[w] = word;
-      }
-      sumv = sh.ivals[1];
-      const int vchanged = __syncthreads_or(changed);
+      sumv = block_sum_int(stage_from(dl, n, sv));
+      const int vchanged = __syncthreads_or(pack_into(pv, n, wn));
       Hv = sv.H;
-      cnt_v = sv.count;
-      if (t >= 1) {
-        // a V-step beyond the first reads the rows of the u that produced it
-        vbytes += 4.0 * (double)n * (double)cnt_u;
-      }
+      if (t >= 1) vbytes += 4.0 * (double)n * (double)cnt_u;  // rows of the u behind this V-step
       if (t >= 1 && !vchanged) {
         early = true;
         break;
       }
       // ---- U-step: z_i = R_i . (h v) on owned R rows (pending deflation fused)
-      for (int i = r0 + wid; i < r1; i += kNW) {
-        float* row = a.R + (size_t)i * a.ldr;
-        const int oc = (have_pending && !r_applied) ? code_at(du, i) : 0;
-        const double zi = row_dot(row, n4 / 4, hv, !weighted, oc, pd, dv, lane);
-        if (lane == 0) st_dev(a.xz + i, zi);
-      }
+      slab_matvec<NT>(a.R, a.ldr, n4 / 4, r0, r1, pv, hw, have_pending && !r_applied, du, dv, pd, part,
+                      a.xz);
       r_applied = true;
       ++passes;
       ++usteps;
       ++epoch;
       if (grid_barrier(a.bar, epoch, a.spin_limit, &bar_flag)) return;
-#pragma unroll
-      for (int e = 0; e < NE; ++e) {
-        const int i = tid + e * kNT;
-        const double z = i < m ? ld_dev(a.xz + i) : 0.0;
-        zd[e] = z;
-        const float x = (float)z;
-        av[e] = fabsf(x);
-        sg[e] = x > 0.0f ? 1 : (x < 0.0f ? -1 : 0);
-        hw[e] = 1.0f;
-      }
-      SelResult s2 = ternary_select<kNT, NE, false>(av, hw, a.tau, 0, s);
-      // p = sum over supp(u) of u_i z_i (fp64 z), fixed reduction order
+      for (int i = tid; i < m; i += NT) dl[i] = ld_dev(a.xz + i);
+      __syncthreads();
+      const SelResult s2 = ternary_select<NT, false>(dl, nullptr, m, a.tau, 0, s);
+      // p = sum over supp(u) of u_i z_i with the fp64 z, fixed reduction order
       double lp = 0.0;
-#pragma unroll
-      for (int e = 0; e < NE; ++e) {
-        const unsigned k = __float_as_uint(av[e]);
-        if (s2.count > 0u && k != 0u && k >= s2.ekey && k >= s2.tkey) lp += fabs(zd[e]);
-      }
+      for (int i = tid; i < m; i += NT)
+        if (selected((float)dl[i], s2)) lp += fabs(dl[i]);
       lp = wave_sum_f64(lp);
-      if (lane == 0) s.red_d[wid] = lp;
+      if (lane == 0) part[wid] = lp;
+      for (int w = tid; w < wm; w += NT) pu_prev[w] = pu[w];
       __syncthreads();
       p = 0.0;
-      for (int w = 0; w < kNW; ++w) p += s.red_d[w];
+      for (int w = 0; w < NW; ++w) p += part[w];
       cnt_u = s2.count;
-      // new u; compare with the u that produced v
-      for (int w = tid; w < wm; w += kNT) pu_prev[w] = pu[w];
-      __syncthreads();
-      write_u_from_slots(s2);
-      int uchanged = 0;
-      for (int w = tid; w < wm; w += kNT)
-        if (pu[w] != pu_prev[w]) uchanged = 1;
-      uchanged = __syncthreads_or(uchanged);
+      stage_from(dl, m, s2);
+      const int uchanged = __syncthreads_or(pack_into(pu, m, wm));
       ++t;
       if (!uchanged && t < a.T) {
         early = true;
@@ -443,8 +468,7 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
       }
     }
     if (dead) {
-      E = 0.0;
-      --comp;
+      emit_zero(comp);
       continue;
     }
     // ---------------- scale, energy, outputs
@@ -453,43 +477,36 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
     const double dd = (double)d;
     E = E - (2.0 * dd * p - dd * dd * q);
     if (g == 0) {
-      for (int w = tid; w < wm; w += kNT) a.Bp[(size_t)comp * wm + w] = pu[w];
-      for (int w = tid; w < wn; w += kNT) a.Cp[(size_t)comp * wn + w] = pv[w];
-      // |supp u0 U supp u_prev| for the fused deflate + first V-step read
-      if (tid == 0) sh.ivals[2] = 0;
-      __syncthreads();
-      int un = 0;
-      for (int w = tid; w < wm; w += kNT) {
-        const unsigned x = pu0[w] | (have_pending ? du[w] : 0u);
+      for (int w = tid; w < wm; w += NT) a.Bp[(size_t)comp * wm + w] = pu[w];
+      for (int w = tid; w < wn; w += NT) a.Cp[(size_t)comp * wn + w] = pv[w];
+      // |supp u0 U supp u_prev| (fused deflate + first V-step rows) and |supp u_prev| (writes)
+      int un = 0, pn = 0;
+      for (int w = tid; w < wm; w += NT) {
+        const unsigned dw = have_pending ? du[w] : 0u;
+        const unsigned x = pu0[w] | dw;
         un += __popc((x | (x >> 1)) & 0x55555555u);
+        pn += __popc((dw | (dw >> 1)) & 0x55555555u);
       }
-      if (un) atomicAdd(&sh.ivals[2], un);
-      if (tid == 0) sh.ivals[3] = 0;
-      __syncthreads();
-      int pn = 0;
-      if (have_pending)
-        for (int w = tid; w < wm; w += kNT) pn += __popc((du[w] | (du[w] >> 1)) & 0x55555555u);
-      if (pn) atomicAdd(&sh.ivals[3], pn);
-      __syncthreads();
+      un = block_sum_int(un);
+      pn = block_sum_int(pn);
       if (tid == 0) {
         a.D[comp] = d;
         a.energy[comp] = 1.0 - E / E0;
         a.stats[0] += (u64)passes;
         if (early) a.stats[1] += 1ull;
         if (fallback) a.stats[2] += 1ull;
-        const double nU = (double)usteps;
-        a.bytes[0] += 4.0 * (double)n * (double)sh.ivals[2] + 4.0 * (double)n * (double)sh.ivals[3] +
-                      nU * 4.0 * (double)m * (double)n + vbytes;
+        a.bytes[0] += 4.0 * (double)n * (double)un + 4.0 * (double)n * (double)pn +
+                      (double)usteps * 4.0 * (double)m * (double)n + vbytes;
       }
     }
     // row-sum recurrence and pending deflation
     const double dsv = dd * (double)sumv;
-    for (int i = tid; i < m; i += kNT) {
-      const float ui = uf[i];
-      if (ui != 0.0f) rs[i] = rs[i] - (double)ui * dsv;
+    for (int i = tid; i < m; i += NT) {
+      const int ui = code_at(pu, i);
+      if (ui != 0) rs[i] = rs[i] - (double)ui * dsv;
     }
-    for (int w = tid; w < wm; w += kNT) du[w] = pu[w];
-    for (int w = tid; w < wn; w += kNT) dv[w] = pv[w];
+    for (int w = tid; w < wm; w += NT) du[w] = pu[w];
+    for (int w = tid; w < wn; w += NT) dv[w] = pv[w];
     pd = d;
     have_pending = true;
     r_applied = false;
@@ -497,58 +514,35 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
     __syncthreads();
   }
   // apply the last pending deflation to R (the transpose copy is no longer needed)
-  if (have_pending && !r_applied) {
-    for (int i = r0 + wid; i < r1; i += kNW) {
-      const int oc = code_at(du, i);
-      if (oc != 0) row_dot(a.R + (size_t)i * a.ldr, n4 / 4, hv, true, oc, pd, dv, lane);
-    }
-  }
+  if (have_pending && !r_applied) slab_deflate<NT>(a.R, a.ldr, n4 / 4, r0, r1, du, dv, pd);
 }
 
-size_t seq_smem_bytes(int m, int n) { return seq_lds_layout(m, n).total; }
+size_t seq_smem_bytes(int m, int n, bool weighted) { return seq_lds_layout(m, n, weighted).total; }
 
-// Threads per workgroup: 512 (up to 256 VGPRs per lane) when the longer side fits 16 slots per
-// thread, else 1024.
-static int seq_threads(int m, int n) { return (m > n ? m : n) <= 512 * 16 ? 512 : 1024; }
-
-int seq_elems_per_thread(int m, int n) {
-  const int L = m > n ? m : n;
-  const int nt = seq_threads(m, n);
-  return (L + nt - 1) / nt;
-}
-
-template <int NT, int E>
-static hipError_t launch_e(const SeqArgs& a, int G, size_t smem, hipStream_t st) {
-  auto kern = seq_kernel<NT, E>;
+template <bool WV>
+static hipError_t launch_one(const SeqArgs& a, int G, size_t smem, hipStream_t st) {
+  auto kern = seq_kernel<512, WV>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (e != hipSuccess) return e;
   SeqArgs copy = a;
   void* args[] = {&copy};
-  return hipLaunchCooperativeKernel((const void*)kern, dim3(G), dim3(NT), args, (unsigned)smem, st);
+  return hipLaunchCooperativeKernel((const void*)kern, dim3(G), dim3(512), args, (unsigned)smem, st);
 }
 
-template <int NT, int E>
-static int max_coresident(size_t smem) {
+template <bool WV>
+static int coresident_one(size_t smem) {
   int nb = 0;
-  auto kern = seq_kernel<NT, E>;
+  auto kern = seq_kernel<512, WV>;
   if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem) != hipSuccess)
     return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, NT, smem) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, 512, smem) != hipSuccess) return 0;
   return nb;
 }
 
-int seq_max_blocks_per_cu(int m, int n) {
-  const size_t smem = seq_smem_bytes(m, n);
+int seq_max_blocks_per_cu(int m, int n, bool weighted) {
+  const size_t smem = seq_smem_bytes(m, n, weighted);
   if (smem > 160 * 1024) return 0;
-  const int E = seq_elems_per_thread(m, n);
-  if (seq_threads(m, n) == 1024) return E <= 16 ? max_coresident<1024, 16>(smem) : 0;
-  if (E <= 1) return max_coresident<512, 1>(smem);
-  if (E <= 2) return max_coresident<512, 2>(smem);
-  if (E <= 4) return max_coresident<512, 4>(smem);
-  if (E <= 6) return max_coresident<512, 6>(smem);
-  if (E <= 8) return max_coresident<512, 8>(smem);
-  if (E <= 12) return max_coresident<512, 12>(smem);
-  return max_coresident<512, 16>(smem);
+  return weighted ? coresident_one<true>(smem) : coresident_one<false>(smem);
 }
 
 hipError_t seq_launch(const SeqLaunch& L, hipStream_t st) {
@@ -579,35 +573,46 @@ hipError_t seq_launch(const SeqLaunch& L, hipStream_t st) {
   a.EHm = L.EHm;
   a.tau = L.tau;
   a.spin_limit = L.spin_limit;
-  const size_t smem = seq_smem_bytes(L.m, L.n);
-  const int E = seq_elems_per_thread(L.m, L.n);
-  if (seq_threads(L.m, L.n) == 1024) {
-    if (E <= 16) return launch_e<1024, 16>(a, L.grid, smem, st);
-    return hipErrorInvalidValue;
+  const size_t smem = seq_smem_bytes(L.m, L.n, L.h != nullptr);
+  return L.h ? launch_one<true>(a, L.grid, smem, st) : launch_one<false>(a, L.grid, smem, st);
+}
+
+// ---- standalone matvec with the same slab routine (kernel-level parity tests) ----------
+// Each workgroup packs the ternary vector into LDS and runs slab_matvec over its rows.
+__global__ void __launch_bounds__(512) matvec_rows_kernel(float* Rp, int rows, int len4, int ld, const int8_t* t,
+                                                           const float* h, double* out) {
+  extern __shared__ __align__(16) char smem[];
+  const int words = (len4 * 4 + 15) / 16;
+  uint32_t* pk = reinterpret_cast<uint32_t*>(smem);
+  float* hl = reinterpret_cast<float*>(smem + al16(4 * (size_t)words));
+  double* part = reinterpret_cast<double*>(smem + al16(4 * (size_t)words) + al16(h ? 16 * (size_t)len4 : 0));
+  const int len = len4 * 4;  // t and h are padded to len4 * 4 by the caller
+  for (int w = threadIdx.x; w < words; w += 512) {
+    unsigned word = 0u;
+    for (int q = 0; q < 16; ++q) {
+      const int i = w * 16 + q;
+      if (i < len) word |= tcode(t[i]) << (2 * q);
+    }
+    pk[w] = word;
   }
-  if (E <= 1) return launch_e<512, 1>(a, L.grid, smem, st);
-  if (E <= 2) return launch_e<512, 2>(a, L.grid, smem, st);
-  if (E <= 4) return launch_e<512, 4>(a, L.grid, smem, st);
-  if (E <= 6) return launch_e<512, 6>(a, L.grid, smem, st);
-  if (E <= 8) return launch_e<512, 8>(a, L.grid, smem, st);
-  if (E <= 12) return launch_e<512, 12>(a, L.grid, smem, st);
-  return launch_e<512, 16>(a, L.grid, smem, st);
+  if (h)
+    for (int j = threadIdx.x; j < len; j += 512) hl[j] = h[j];
+  __syncthreads();
+  const int G = gridDim.x, g = blockIdx.x;
+  const int r0 = (int)((long long)g * rows / G), r1 = (int)((long long)(g + 1) * rows / G);
+  slab_matvec<512>(Rp, ld, len4, r0, r1, pk, h ? hl : nullptr, false, nullptr, nullptr, 0.0f, part, out);
 }
 
-// ---- standalone matvec with the same row routine (kernel-level parity tests) -----------
-__global__ void __launch_bounds__(256) matvec_rows_kernel(float* Rp, int rows, int len4, int ld,
-                                                           const float* wt, bool exact, double* out) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
-  const double v = row_dot(Rp + (size_t)row * ld, len4, wt, exact, 0, 0.0f, nullptr, lane);
-  if (lane == 0) out[row] = v;
-}
-
-hipError_t matvec_rows(float* Rp, int rows, int len4, int ld, const float* wt, bool exact, double* out,
+hipError_t matvec_rows(float* Rp, int rows, int len4, int ld, const int8_t* t, const float* h, double* out,
                        hipStream_t st) {
-  hipLaunchKernelGGL(matvec_rows_kernel, dim3((rows + 3) / 4), dim3(256), 0, st, Rp, rows, len4, ld, wt,
-                     exact, out);
+  const int words = (len4 * 4 + 15) / 16;
+  const int G = rows < 256 ? rows : 256;
+  const int upr = (len4 + 64 * kQ - 1) / (64 * kQ);
+  if ((long long)((rows + G - 1) / G) * upr > kMaxUnits) return hipErrorInvalidValue;
+  const size_t smem = al16(4 * (size_t)words) + al16(h ? 16 * (size_t)len4 : 0) + 8 * (size_t)kMaxUnits;
+  hipError_t e = hipFuncSetAttribute((const void*)matvec_rows_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(matvec_rows_kernel, dim3(G), dim3(512), smem, st, Rp, rows, len4, ld, t, h, out);
   return hipGetLastError();
 }
 

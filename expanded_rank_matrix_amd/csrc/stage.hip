@@ -111,19 +111,3 @@ hipError_t row_energy(const float* R, int m, int n, int ldr, const float* h, dou
 
 }  // namespace externd
 
-namespace externd {
-
-__global__ void __launch_bounds__(256) make_weights_kernel(const int8_t* t, const float* h, int len, int ld, float* wt) {
-  const int j = blockIdx.x * blockDim.x + threadIdx.x;
-  if (j >= ld) return;
-  float w = 0.0f;
-  if (j < len && t[j] != 0) w = (h ? h[j] : 1.0f) * (t[j] > 0 ? 1.0f : -1.0f);
-  wt[j] = w;
-}
-
-hipError_t make_weights(const int8_t* t, const float* h, int len, int ld, float* wt, hipStream_t st) {
-  hipLaunchKernelGGL(make_weights_kernel, dim3((ld + 255) / 256), dim3(256), 0, st, t, h, len, ld, wt);
-  return hipGetLastError();
-}
-
-}  // namespace externd
