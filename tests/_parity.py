@@ -37,15 +37,19 @@ def first_divergence(g, o):
     return int(bad[0]) if len(bad) else k
 
 
-def check_free_run(g, o, label=""):
+def check_free_run(g, o, label="", b=1):
     """Identical factors up to the first divergence, which must sit at a near-tie; D and the
-    energy curve agree on the common prefix.  Returns the divergence index."""
+    energy curve agree on the common prefix.  Returns the divergence index (for the block path,
+    the first component of the first block that differs: the components of a block are fitted
+    jointly, so a tie anywhere in the block may change all of them)."""
     k = min(g["B"].shape[0], o["B"].shape[0])
     f = first_divergence(g, o)
     if f < k:
-        assert o["gaps"][f] <= GAP_TOL, (
+        f = (f // b) * b
+        gap = float(np.min(o["gaps"][f:f + b]))
+        assert gap <= GAP_TOL, (
             f"{label}: factors diverge at component {f} whose oracle selection gap "
-            f"{o['gaps'][f]:.3e} exceeds {GAP_TOL}")
+            f"{gap:.3e} exceeds {GAP_TOL}")
     np.testing.assert_allclose(g["D"][:f], o["D"][:f], rtol=D_RTOL, atol=0, err_msg=label)
     assert np.max(np.abs(g["energy"][:f] - o["energy"][:f]), initial=0.0) <= E_ATOL, label
     return f
@@ -58,17 +62,20 @@ def check_replay(A, mu, tau, h, T, block, g, sample, label="", upto=0):
     b = r["b"]
     mism = 0
     for si, s in enumerate(r["sample"]):
-        rows = range(s * b, min(s * b + b, g["B"].shape[0])) if b > 1 else [s]
-        for c, i in enumerate(rows):
-            slot = si * b + c
-            same = (np.array_equal(r["Bo"][slot], g["B"][i]) and np.array_equal(r["Co"][slot], g["C"][i]))
-            if not same:
-                mism += 1
-                assert r["gap_o"][slot] <= GAP_TOL, (
-                    f"{label}: component {i} differs from the oracle refit; gap {r['gap_o'][slot]:.3e}")
-            else:
-                np.testing.assert_allclose(g["D"][i], r["Do"][slot], rtol=D_RTOL, atol=0,
-                                           err_msg=f"{label}: D[{i}]")
+        rows = list(range(s * b, min(s * b + b, g["B"].shape[0]))) if b > 1 else [s]
+        slots = [si * b + c for c in range(len(rows))]
+        same = [np.array_equal(r["Bo"][sl], g["B"][i]) and np.array_equal(r["Co"][sl], g["C"][i])
+                for sl, i in zip(slots, rows)]
+        if not all(same):
+            # a block is fitted jointly: one near-tie anywhere in it may change every member
+            mism += 1
+            gap = float(np.min(r["gap_o"][slots]))
+            assert gap <= GAP_TOL, (
+                f"{label}: component(s) {[i for i, ok in zip(rows, same) if not ok][:8]} differ "
+                f"from the oracle refit; smallest gap in the block {gap:.3e}")
+            continue
+        np.testing.assert_allclose(g["D"][rows], r["Do"][slots], rtol=D_RTOL, atol=0,
+                                   err_msg=f"{label}: D[{rows[0]}..]")
     er = r["energy_replay"]
     ok = ~np.isnan(er)
     assert np.max(np.abs(g["energy"][ok] - er[ok]), initial=0.0) <= E_ATOL, label

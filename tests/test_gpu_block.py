@@ -1,0 +1,140 @@
+"""GPU parity of the block-ALS path (block size b >= 2) against the oracle (through the C ABI).
+
+The components of a block are fitted jointly (Eq. 3 target with the Gram solves), so parity is
+judged per block: a block either matches the oracle exactly or holds a selection near-tie.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from expanded_rank_matrix_amd import inputs
+from tests import _parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+def run_both(A, mu, tau, h, T, block, k_limit=0):
+    g = P.gpu_decompose(A, mu, tau, h, T, block)
+    o = oracle.decompose(A, mu, tau, h, T, block, k_limit=k_limit)
+    return g, o
+
+
+def blocks_of(g, A, block):
+    m, n = A.shape
+    b = oracle.resolve_block(block, m, n, g["k"])
+    return b, -(-g["k"] // b)
+
+
+@pytest.mark.parametrize("block", [2, 4, 16, 48])
+def test_tiny_blocks_every_component(block):
+    c = inputs.CONFIGS["tiny64x48"]
+    A, h = inputs.make_input("tiny64x48")
+    g, o = run_both(A, c["mu"], c["tau"], h, 2, block)
+    b, nb = blocks_of(g, A, block)
+    f = P.check_free_run(g, o, f"tiny b={block}", b)
+    P.check_replay(A, c["mu"], c["tau"], h, 2, block, g, np.arange(nb), f"tiny b={block}")
+    assert f >= b
+    assert P.monotone(g["energy"])
+    if f == g["k"]:
+        assert g["stats"]["passes"] == o["counters"][2]
+        assert g["stats"]["fallback_inits"] == o["counters"][0]
+        assert g["stats"]["block"] == b
+
+
+@pytest.mark.parametrize("name,m,n,mu,block", [
+    ("mlp9728x2560", 389, 103, 2.0, 16),     # ragged last block (206 = 12 x 16 + 14)
+    ("down2560x9728", 103, 389, 3.0, 32),    # weighted, 309 = 9 x 32 + 21
+    ("attn2560", 700, 650, 0.5, 64),         # several 64-tiles with ragged tails, split-K
+    ("lowrank1024", 300, 260, 1.0, -1),      # default block size min(256, min(m, n) / 8)
+    ("attn2560", 300, 280, 1.0, 256),        # largest block
+    ("attn2560", 333, 257, 1.0, 100),        # block not a multiple of the MFMA tile
+    ("attn2560", 1, 37, 2.0, 2),
+    ("attn2560", 41, 1, 2.0, 2),
+    ("attn2560", 17, 1100, 1.0, 8),
+])
+def test_scaled_blocks_free_run_and_replay(name, m, n, mu, block):
+    c = inputs.CONFIGS[name]
+    A, h = inputs.make_input(name, m=m, n=n)
+    tau = c["tau"]
+    g, o = run_both(A, mu, tau, h, 3, block)
+    b, nb = blocks_of(g, A, block)
+    label = f"{name} {m}x{n} b={b}"
+    P.check_free_run(g, o, label, b)
+    P.check_replay(A, mu, tau, h, 3, block, g, sorted({0, 1 % nb, nb // 2, nb - 1}), label)
+    assert P.monotone(g["energy"]), label
+
+
+def test_mlp_full_size_sampled():
+    """9728 x 2560 MLP projection, b = 64: oracle free run over the first two blocks and
+    refits of sampled blocks from the GPU's own residual history."""
+    name = "mlp9728x2560"
+    c = inputs.CONFIGS[name]
+    A, h = inputs.make_input(name)
+    g = P.gpu_decompose(A, c["mu"], c["tau"], h, c["als_iters"], c["block"])
+    o = oracle.decompose(A, c["mu"], c["tau"], h, c["als_iters"], c["block"], k_limit=2 * c["block"])
+    P.check_free_run(g, o, name, c["block"])
+    P.check_replay(A, c["mu"], c["tau"], h, c["als_iters"], c["block"], g, [0, 1, 12], name,
+                   upto=13 * c["block"])
+    assert P.monotone(g["energy"])
+    assert abs(g["energy"][-1] - g["stats"]["energy_final_explicit"]) <= 1e-4
+
+
+def test_down_weighted_full_size_sampled():
+    """2560 x 9728 down projection with importance weights, b = 128."""
+    name = "down2560x9728"
+    c = inputs.CONFIGS[name]
+    A, h = inputs.make_input(name)
+    g = P.gpu_decompose(A, c["mu"], c["tau"], h, c["als_iters"], c["block"])
+    o = oracle.decompose(A, c["mu"], c["tau"], h, c["als_iters"], c["block"], k_limit=c["block"])
+    P.check_free_run(g, o, name, c["block"])
+    P.check_replay(A, c["mu"], c["tau"], h, c["als_iters"], c["block"], g, [0, 7], name,
+                   upto=8 * c["block"])
+    assert P.monotone(g["energy"])
+    assert abs(g["energy"][-1] - g["stats"]["energy_final_explicit"]) <= 1e-4
+
+
+def test_block_determinism():
+    A, h = inputs.make_input("down2560x9728", m=512, n=700)
+    g1 = P.gpu_decompose(A, 1.0, 0.2, h, 3, 32)
+    g2 = P.gpu_decompose(A, 1.0, 0.2, h, 3, 32)
+    for key in ("B", "C", "D", "energy"):
+        assert np.array_equal(g1[key], g2[key]), key
+
+
+def test_block_integer_inputs_exact():
+    """Small integer matrices: every fp64 sum is exact in any order, so the GPU must reproduce
+    the oracle bit for bit, ties included."""
+    rng = np.random.default_rng(11)
+    for (m, n, mu, block) in [(2, 2, 3.0, 2), (6, 5, 2.0, 3), (12, 9, 1.0, 4), (9, 12, 2.0, 5)]:
+        A = rng.integers(-3, 4, size=(m, n)).astype(np.float32)
+        g, o = run_both(A, mu, 0.0, None, 3, block)
+        assert np.array_equal(g["B"], o["B"]) and np.array_equal(g["C"], o["C"]), (m, n, block)
+        assert np.array_equal(g["D"], o["D"]), (m, n, block)
+        np.testing.assert_allclose(g["energy"], o["energy"], rtol=0, atol=1e-12)
+
+
+def test_block_special_cases():
+    # zero matrix
+    g = P.gpu_decompose(np.zeros((19, 23), np.float32), 2.0, 0.0, None, 3, 4)
+    assert np.all(g["B"] == 0) and np.all(g["C"] == 0) and np.all(g["D"] == 0)
+    assert np.all(g["energy"] == 1.0)
+    # identity: compare with the oracle exactly (integer data)
+    n = 40
+    A = np.eye(n, dtype=np.float32)
+    g, o = run_both(A, 1.0, 0.0, None, 4, 8)
+    assert np.array_equal(g["B"], o["B"]) and np.array_equal(g["C"], o["C"])
+    assert np.array_equal(g["D"], o["D"])
+    # rank-one ternary matrix: the first component recovers it and the rest are zero
+    rng = np.random.default_rng(3)
+    u = rng.choice([-1, 0, 1], size=30).astype(np.float32)
+    v = rng.choice([-1, 0, 1], size=20).astype(np.float32)
+    u[0] = v[0] = 1
+    A = 0.75 * np.outer(u, v)
+    g, o = run_both(A, 1.0, 0.0, None, 3, 4)
+    assert np.array_equal(g["B"], o["B"]) and np.array_equal(g["D"], o["D"])
+    assert g["energy"][-1] == pytest.approx(1.0, abs=1e-12)
+    # block larger than k is clamped to k
+    A, _ = inputs.make_input("attn2560", m=20, n=30)
+    g = P.gpu_decompose(A, 0.5, 0.0, None, 2, 64)
+    assert g["stats"]["block"] == g["k"] == 10
