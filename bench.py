@@ -11,6 +11,8 @@ iterations, sequential deflation.  Prints one JSON line.
 from __future__ import annotations
 
 import argparse
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -24,6 +26,46 @@ FP64_MFMA_PEAK_TFLOPS = 78.6  # MI355X dense fp64 matrix
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def source_digest():
+    """sha256 over the library's kernel sources: HBM counter figures are only valid for them."""
+    here = os.path.dirname(os.path.abspath(__file__))
+    files = sorted(glob.glob(os.path.join(here, "expanded_rank_matrix_amd", "csrc", "*")))
+    h = hashlib.sha256()
+    for f in files:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3 counter runs
+    (FETCH_SIZE and WRITE_SIZE, scaled by a plain copy's reading), or None when they were taken
+    on other kernel sources."""
+    here = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(here, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        t = json.load(fh)
+    if t.get("source_digest") != source_digest():
+        return None
+    return float(t["traffic_bytes_per_launch"])
+
+
+def copy_probe(megabytes):
+    """A plain device copy of known size, timed by the counter runs to scale FETCH_SIZE/WRITE_SIZE."""
+    import torch
+
+    n = megabytes * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copy probe: {megabytes} MiB read + {megabytes} MiB written")
 
 
 def cpu_baseline(A, c, seconds_target=15.0):
@@ -56,6 +98,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="attn2560")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="run a plain copy of this many MiB first (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build runs the "
@@ -67,6 +111,8 @@ def main():
     import expanded_rank_matrix_amd as erm
     from expanded_rank_matrix_amd import inputs
 
+    if args.copy_mb > 0:
+        copy_probe(args.copy_mb)
     c = inputs.CONFIGS[args.workload]
     A_np, h_np = inputs.make_input(args.workload)
     m, n = A_np.shape
@@ -93,20 +139,22 @@ def main():
     value = k * args.steps / wall
     kms = float(np.mean(kernel_ms))
     energy = out["energy"].cpu().numpy()
+    traffic = measured_traffic(args.workload)
     if c["block"] in (0, 1):
         achieved = stats["bytes_algorithmic"] / (kms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
                 "kernel": "seq_kernel (persistent)", "kernel_ms": kms,
                 "bytes_per_launch": stats["bytes_algorithmic"]}
     else:
         achieved = stats["flops_algorithmic"] / (kms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": FP64_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / FP64_MFMA_PEAK_TFLOPS, "traffic": None,
+                "frac": achieved / FP64_MFMA_PEAK_TFLOPS, "traffic": traffic,
                 "kernel": "block-ALS contractions", "kernel_ms": kms,
                 "flops_per_launch": stats["flops_algorithmic"]}
     res = {
         "metric": "ExTernD components fitted/sec + achieved GB/s at 2560x2560, mu=3",
+        "source_digest": source_digest(),
         "value": value,
         "unit": "components/s",
         "n_gpus": 1,

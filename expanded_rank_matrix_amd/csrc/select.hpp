@@ -10,25 +10,28 @@
 // the weight added, so it never beats both ends of the group: the optimum is a threshold t,
 // support = {eligible i : |x_i| >= t}, t one of the distinct eligible values, and "smallest j"
 // means "largest t".  The search needs no sort:
-//   1. histogram the eligible values by their fp32 bit pattern into 1024 bins (64 per octave
-//      below the maximum, the last bin catches the rest), with counts and fp64 sums of h|x|
-//      and h (LDS atomics; used for pruning only);
+//   1. histogram the eligible values by their fp32 bit pattern ("key") into 1024 bins (64 per
+//      octave below the maximum, the last bin catches the rest), with counts and fp64 sums of
+//      h|x| and h (LDS atomics; used for pruning only);
 //   2. every bin boundary is a threshold whose score follows from the prefix sums; a bin's
 //      interior can only win if (P_above + top_of_bin * H_bin)^2 / (H_above + H_bin) reaches the
 //      best boundary score (each added element adds at most top_of_bin per unit weight, and the
 //      score is quasi-convex in the added weight).  The bins that can hold the optimum form a
-//      narrow window (typically three bins);
-//   3. the window's elements are scored exactly: P(t) = P_above + sum over window elements
-//      >= t, every sum an exact 128-bit fixed-point integer (order independent), so the decision
-//      is canonical: it depends neither on the launch shape nor on atomic ordering.
+//      narrow window (typically three bins, a few dozen elements).  A window with too many
+//      elements is histogrammed again over its own key range at a finer bin width;
+//   3. the window's elements are scored exactly: P(t) = P_above + sum over window elements with
+//      key >= t, every sum an exact 128-bit fixed-point integer (order independent), so the
+//      decision is canonical: it depends neither on the launch shape nor on atomic ordering.
+//      Each wave scores 64 window elements against the whole window (LDS broadcast reads).
 #pragma once
 #include "common.hpp"
 
 namespace externd {
 
-constexpr int kSelBins = 1024;     // 64 per octave
-constexpr int kSelShift = 23 - 6;  // fp32 mantissa bits dropped per bin
-constexpr int kWinMax = 256;       // window elements scored in one pass
+constexpr int kSelBins = 1024;      // bins per histogram level
+constexpr int kSelShift0 = 23 - 6;  // first level: fp32 mantissa bits dropped per bin (64/octave)
+constexpr int kWinMax = 512;        // window elements scored in one pass (8 waves x 64)
+constexpr int kSelLevels = 4;       // histogram levels before the distinct-key walk
 
 struct SelScratch {
   unsigned cnt[kSelBins];
@@ -36,15 +39,21 @@ struct SelScratch {
   double hsum[kSelBins];
   unsigned w_key[kWinMax];
   u64 w_plo[kWinMax], w_phi[kWinMax], w_hlo[kWinMax], w_hhi[kWinMax];
-  u64 a_plo[16], a_phi[16], a_hlo[16], a_hhi[16];
+  u64 a_plo[16], a_phi[16], a_hlo[16], a_hhi[16];  // per-wave exact partial sums
   unsigned a_cnt[16];
+  u64 f_plo[16], f_phi[16], f_hlo[16], f_hhi[16];  // per-wave best threshold
+  unsigned f_cnt[16];
+  double f_s[16];
+  unsigned f_k[16];
+  double d_p[16], d_h[16];  // per-wave fp64 sums above a refined histogram's range
   unsigned red_u[16];
-  double red_d[16];
-  unsigned red_k[16];
-  unsigned wk_hi, wk_lo;  // window keys in (wk_lo, wk_hi]
+  double w_sp[16], w_sh[16];  // per-wave scan totals
+  unsigned w_sc[16];
+  double w_bn[16], w_bd[16];  // per-wave best boundary
+  int w_lo[16], w_hi[16];     // per-wave candidate bin range
+  unsigned w_clo[16], w_chi[16];
+  double bn, bd;              // best boundary score so far, as a fraction
   unsigned slot;
-  unsigned walk;
-  int mode;  // 1: window scored in one pass, 2: window scored by exact block reductions
 };
 
 struct SelResult {
@@ -60,6 +69,12 @@ __device__ __forceinline__ bool better(double S1, unsigned k1, double S2, unsign
 
 __device__ __forceinline__ u128 shfl_xor128(u128 v, int o) {
   return mk128(__shfl_xor(v.lo, o), __shfl_xor(v.hi, o));
+}
+
+__device__ __forceinline__ u64 readlane64(u64 v, int l) {
+  const unsigned lo = __builtin_amdgcn_readlane((unsigned)v, l);
+  const unsigned hi = __builtin_amdgcn_readlane((unsigned)(v >> 32), l);
+  return ((u64)hi << 32) | lo;
 }
 
 // Whether a slot holding x is in the support of r.
@@ -82,7 +97,7 @@ __device__ SelResult ternary_select(const T* vals, const float* hl, int L, float
   out.P = 0.0;
   out.H = 0.0;
   out.count = 0u;
-  // ---- max |x|; clear the histogram meanwhile
+  // ---- max |x|; clear the first histogram meanwhile
   unsigned km = 0;
   for (int i = tid; i < L; i += NT) {
     const unsigned k = __float_as_uint((float)vals[i]) & 0x7FFFFFFFu;
@@ -95,7 +110,11 @@ __device__ SelResult ternary_select(const T* vals, const float* hl, int L, float
     s.psum[b] = 0.0;
     if (W) s.hsum[b] = 0.0;
   }
-  if (tid == 0) s.slot = 0u;
+  if (tid == 0) {
+    s.slot = 0u;
+    s.bn = 0.0;
+    s.bd = 1.0;
+  }
   __syncthreads();
   km = 0;
 #pragma unroll
@@ -118,49 +137,115 @@ __device__ SelResult ternary_select(const T* vals, const float* hl, int L, float
     const unsigned k = __float_as_uint((float)vals[i]) & 0x7FFFFFFFu;
     return k >= ekey ? k : 0u;
   };
-  // ---- approximate histogram.  Bin b is stored at (b % 16) * 64 + b / 16 so that the scan
-  // below (lane l owns bins 16 l .. 16 l + 15) reads consecutive addresses across lanes.
-  for (int i = tid; i < L; i += NT) {
-    const unsigned k = keyof(i);
-    if (k != 0u) {
-      unsigned b = (km - k) >> kSelShift;
-      b = b > (unsigned)(kSelBins - 1) ? (unsigned)(kSelBins - 1) : b;
-      const unsigned hb = (b & 15u) * 64u + (b >> 4);
-      const double av = (double)__uint_as_float(k);
-      atomicAdd(&s.cnt[hb], 1u);
-      atomicAdd(&s.psum[hb], W ? (double)hl[i] * av : av);
-      if (W) atomicAdd(&s.hsum[hb], (double)hl[i]);
+
+  // ---- histogram levels.  Level 0 covers keys <= km with bins of 2^17 keys (the last bin
+  // catches the rest); a later level covers the previous window (wk_lo, wk_hi] at a finer shift.
+  unsigned kt = km, klo = 0u, wk_hi = 0u, wk_lo = 0u;
+  int sh = kSelShift0;
+  int mode = 0;
+  for (int level = 0; level < kSelLevels; ++level) {
+    if (level > 0) {
+      for (int b = tid; b < kSelBins; b += NT) {
+        s.cnt[b] = 0u;
+        s.psum[b] = 0.0;
+        if (W) s.hsum[b] = 0.0;
+      }
+      __syncthreads();
     }
-  }
-  __syncthreads();
-  // ---- wave 0: prefix sums, boundary scores, interior bounds -> window of bins.  Scores are
-  // compared as fractions (num * den' vs num' * den) to avoid fp64 divisions.
-  if (wid == 0) {
-    constexpr int BPL = kSelBins / 64;  // contiguous bins per lane
-    auto binp = [&](int q) -> double { return s.psum[q * 64 + lane]; };
-    auto binh = [&](int q) -> double { return W ? s.hsum[q * 64 + lane] : (double)s.cnt[q * 64 + lane]; };
+    // Bin b is stored at (b % BPL) * NT + b / BPL so that thread t, which owns bins
+    // BPL t .. BPL t + BPL - 1 in the scan below, reads consecutive addresses across lanes.
+    constexpr int BPL = kSelBins / NT;
+    double dp = 0.0, dh = 0.0;  // fp64 sums above the range (level > 0)
+    for (int i = tid; i < L; i += NT) {
+      const unsigned k = keyof(i);
+      if (k == 0u || k <= klo) continue;
+      const double av = (double)__uint_as_float(k);
+      const double hw = W ? (double)hl[i] : 1.0;
+      if (k > kt) {
+        dp += hw * av;
+        dh += hw;
+        continue;
+      }
+      unsigned b = (kt - k) >> sh;
+      b = b > (unsigned)(kSelBins - 1) ? (unsigned)(kSelBins - 1) : b;
+      const unsigned hb = (b % BPL) * NT + b / BPL;
+      atomicAdd(&s.cnt[hb], 1u);
+      atomicAdd(&s.psum[hb], hw * av);
+      if (W) atomicAdd(&s.hsum[hb], hw);
+    }
+    if (level > 0) {
+      dp = wave_sum_f64(dp);
+      dh = wave_sum_f64(dh);
+      if (lane == 0) {
+        s.d_p[wid] = dp;
+        s.d_h[wid] = dh;
+      }
+    }
+    __syncthreads();
+    // ---- all threads: prefix sums, boundary scores, interior bounds -> window of bins.  Scores
+    // are compared as fractions (num * den' vs num' * den) to avoid fp64 divisions.  Every thread
+    // ends with the same window (the cross-wave steps read the same LDS values in the same order).
+    double bp[BPL], bh[BPL];
+    unsigned bc[BPL];
+#pragma unroll
+    for (int q = 0; q < BPL; ++q) {
+      bc[q] = s.cnt[q * NT + tid];
+      bp[q] = s.psum[q * NT + tid];
+      bh[q] = W ? s.hsum[q * NT + tid] : (double)bc[q];
+    }
+    double P0 = 0.0, H0 = 0.0;
+    if (level > 0) {
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        P0 += s.d_p[w];
+        H0 += s.d_h[w];
+      }
+    }
     double tp = 0.0, th = 0.0;
-    _Pragma("unroll 2") for (int q = 0; q < BPL; ++q) {
-      tp += binp(q);
-      th += binh(q);
+    unsigned tc = 0u;
+#pragma unroll
+    for (int q = 0; q < BPL; ++q) {
+      tp += bp[q];
+      th += bh[q];
+      tc += bc[q];
     }
     double ip = tp, ih = th;
+    unsigned ic = tc;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const double a0 = __shfl_up(ip, o), a1 = __shfl_up(ih, o);
+      const unsigned a2 = __shfl_up(ic, o);
       if (lane >= o) {
         ip += a0;
         ih += a1;
+        ic += a2;
       }
     }
-    // best boundary score as a fraction bn / bd
-    double bn = 0.0, bd = 1.0;
+    if (lane == 63) {
+      s.w_sp[wid] = ip;
+      s.w_sh[wid] = ih;
+      s.w_sc[wid] = ic;
+    }
+    __syncthreads();
+    double rp0 = P0, rh0 = H0;  // prefix before this thread's first bin
+    unsigned rc0 = 0u;
+    for (int w = 0; w < wid; ++w) {
+      rp0 += s.w_sp[w];
+      rh0 += s.w_sh[w];
+      rc0 += s.w_sc[w];
+    }
+    rp0 += ip - tp;
+    rh0 += ih - th;
+    rc0 += ic - tc;
+    // best boundary score as a fraction bn / bd (carried over from earlier levels)
+    double bn = s.bn, bd = s.bd;
     {
-      double rp = ip - tp, rh = ih - th;
-      _Pragma("unroll 2") for (int q = 0; q < BPL; ++q) {
-        rp += binp(q);
-        rh += binh(q);
-        if (s.cnt[q * 64 + lane] != 0u && rp * rp * bd > bn * rh) {
+      double rp = rp0, rh = rh0;
+#pragma unroll
+      for (int q = 0; q < BPL; ++q) {
+        rp += bp[q];
+        rh += bh[q];
+        if (bc[q] != 0u && rp * rp * bd > bn * rh) {
           bn = rp * rp;
           bd = rh;
         }
@@ -174,52 +259,118 @@ __device__ SelResult ternary_select(const T* vals, const float* hl, int L, float
         bd = d2;
       }
     }
+    if (lane == 0) {
+      s.w_bn[wid] = bn;
+      s.w_bd[wid] = bd;
+    }
+    __syncthreads();
+    bn = s.w_bn[0];
+    bd = s.w_bd[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w)
+      if (s.w_bn[w] * bd > bn * s.w_bd[w]) {
+        bn = s.w_bn[w];
+        bd = s.w_bd[w];
+      }
     const double cutn = bn * (1.0 - 1e-9);  // candidate if score * bd >= cutn
     int lo = kSelBins, hi = -1;
+    unsigned clo = 0u, chi = 0u;  // element counts before bin lo / through bin hi
     {
-      double rp = ip - tp, rh = ih - th;
-      _Pragma("unroll 2") for (int q = 0; q < BPL; ++q) {
-        const int b = lane * BPL + q;
-        const unsigned c = s.cnt[q * 64 + lane];
-        const double hbq = binh(q);
-        const double Pi = rp + binp(q), Hi = rh + hbq;
+      double rp = rp0, rh = rh0;
+      unsigned rc = rc0;
+#pragma unroll
+      for (int q = 0; q < BPL; ++q) {
+        const int b = tid * BPL + q;
+        const unsigned c = bc[q];
+        const double Pi = rp + bp[q], Hi = rh + bh[q];
         bool cand = c != 0u && Pi * Pi * bd >= cutn * Hi;
         if (!cand && c >= 2u) {
-          const unsigned top = km - ((unsigned)b << kSelShift);  // largest key the bin can hold
-          const double t1 = rp + (double)__uint_as_float(top) * hbq;
+          const unsigned off = (unsigned)b << sh;
+          const unsigned top = kt > off ? kt - off : 0u;  // largest key the bin can hold
+          const double t1 = rp + (double)__uint_as_float(top) * bh[q];
           cand = t1 * t1 * bd >= cutn * Hi || (rh > 0.0 && rp * rp * bd >= cutn * rh);
         }
         if (cand) {
-          lo = b < lo ? b : lo;
-          hi = b > hi ? b : hi;
+          if (b < lo) {
+            lo = b;
+            clo = rc;
+          }
+          if (b > hi) {
+            hi = b;
+            chi = rc + c;
+          }
         }
         rp = Pi;
         rh = Hi;
+        rc += c;
       }
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
       const int l2 = __shfl_xor(lo, o), h2 = __shfl_xor(hi, o);
-      lo = l2 < lo ? l2 : lo;
-      hi = h2 > hi ? h2 : hi;
+      const unsigned cl2 = __shfl_xor(clo, o), ch2 = __shfl_xor(chi, o);
+      if (l2 < lo) {
+        lo = l2;
+        clo = cl2;
+      }
+      if (h2 > hi) {
+        hi = h2;
+        chi = ch2;
+      }
     }
-    unsigned nw = 0u;
-    _Pragma("unroll 2") for (int q = 0; q < BPL; ++q) {
-      const int b = lane * BPL + q;
-      if (b >= lo && b <= hi) nw += s.cnt[q * 64 + lane];
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) nw += __shfl_xor(nw, o);
     if (lane == 0) {
-      s.wk_hi = km - ((unsigned)lo << kSelShift);
-      const long long klo = (long long)km - ((long long)(hi + 1) << kSelShift);
-      s.wk_lo = (hi == kSelBins - 1 || klo < 0) ? 0u : (unsigned)klo;
-      s.mode = nw <= (unsigned)kWinMax ? 1 : 2;
+      s.w_lo[wid] = lo;
+      s.w_hi[wid] = hi;
+      s.w_clo[wid] = clo;
+      s.w_chi[wid] = chi;
+    }
+    __syncthreads();
+    lo = kSelBins;
+    hi = -1;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      if (s.w_lo[w] < lo) {
+        lo = s.w_lo[w];
+        clo = s.w_clo[w];
+      }
+      if (s.w_hi[w] > hi) {
+        hi = s.w_hi[w];
+        chi = s.w_chi[w];
+      }
+    }
+    const unsigned nw = chi - clo;
+    {
+      const unsigned offlo = (unsigned)lo << sh;
+      const unsigned whi = kt > offlo ? kt - offlo : 0u;
+      const long long wlo = (long long)kt - ((long long)(hi + 1) << sh);
+      // the last bin of the first level also holds every smaller key
+      const bool tail = level == 0 && hi == kSelBins - 1;
+      const unsigned wlo_u = (tail || wlo < (long long)klo) ? klo : (unsigned)wlo;
+      int md = 1, nsh = 0;
+      if (nw > (unsigned)kWinMax) {
+        md = 2;
+        const unsigned range = whi - wlo_u;  // keys in (wlo_u, whi]
+        if (sh > 0 && range > 1u) {
+          while (((range - 1u) >> nsh) > (unsigned)(kSelBins - 1)) ++nsh;
+          if (nsh < sh || tail) md = 3;  // a finer (or tail-resolving) level exists
+        }
+      }
+      wk_hi = whi;
+      wk_lo = wlo_u;
+      mode = md;
+      if (tid == 0) {
+        s.bn = bn;
+        s.bd = bd;
+      }
+      if (mode != 3 || level == kSelLevels - 1) {
+        if (mode == 3) mode = 2;
+        break;
+      }
+      kt = whi;
+      klo = wlo_u;
+      sh = nsh;
     }
   }
-  __syncthreads();
-  const unsigned wk_hi = s.wk_hi, wk_lo = s.wk_lo;
-  const int mode = s.mode;
   const int EM = exp_bound(M);
   const int scP = W ? (100 - EM - EHm) : (100 - EM);
   const int scH = W ? (100 - EHm) : 0;
@@ -228,18 +379,8 @@ __device__ SelResult ternary_select(const T* vals, const float* hl, int L, float
     return W ? fixp((double)hl[i] * av, scP) : fixp(av, scP);
   };
   auto hterm = [&](int i) -> u128 { return W ? fixp((double)hl[i], scH) : mk128(1ull, 0ull); };
-  // Exact block sum over eligible slots with key >= kmin (and key <= kmax); all threads call.
-  auto exact_sum = [&](unsigned kmin, unsigned kmax, u128& P, u128& H, unsigned& C) {
-    u128 p = mk128(0, 0), h = mk128(0, 0);
-    unsigned c = 0u;
-    for (int i = tid; i < L; i += NT) {
-      const unsigned k = keyof(i);
-      if (k != 0u && k >= kmin && k <= kmax) {
-        p = add128(p, pterm(i, k));
-        if (W) h = add128(h, hterm(i));
-        ++c;
-      }
-    }
+  // per-wave exact partials -> LDS -> every thread sums them in wave order
+  auto block_sum128 = [&](u128 p, u128 h, unsigned c, u128& P, u128& H, unsigned& C) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
       p = add128(p, shfl_xor128(p, o));
@@ -265,54 +406,74 @@ __device__ SelResult ternary_select(const T* vals, const float* hl, int L, float
       C += s.a_cnt[w];
     }
   };
-  // ---- gather the window (one-pass mode)
-  if (mode == 1) {
+  // ---- one pass: exact sums above the window and, to be scored, the window's elements
+  u128 AP, AH;
+  unsigned AC;
+  {
+    u128 p = mk128(0, 0), h = mk128(0, 0);
+    unsigned c = 0u;
     for (int i = tid; i < L; i += NT) {
       const unsigned k = keyof(i);
-      if (k != 0u && k > wk_lo && k <= wk_hi) {
+      if (k == 0u || k <= wk_lo) continue;
+      if (k > wk_hi) {
+        p = add128(p, pterm(i, k));
+        if (W) h = add128(h, hterm(i));
+        ++c;
+      } else if (mode == 1) {
         const unsigned slot = atomicAdd(&s.slot, 1u);
-        const u128 pe = pterm(i, k);
-        s.w_key[slot] = k;
-        s.w_plo[slot] = pe.lo;
-        s.w_phi[slot] = pe.hi;
-        if (W) {
-          const u128 he = hterm(i);
-          s.w_hlo[slot] = he.lo;
-          s.w_hhi[slot] = he.hi;
+        if (slot < (unsigned)kWinMax) {
+          const u128 pe = pterm(i, k);
+          s.w_key[slot] = k;
+          s.w_plo[slot] = pe.lo;
+          s.w_phi[slot] = pe.hi;
+          if (W) {
+            const u128 he = hterm(i);
+            s.w_hlo[slot] = he.lo;
+            s.w_hhi[slot] = he.hi;
+          }
         }
       }
     }
+    block_sum128(p, h, c, AP, AH, AC);  // its barriers also publish the window
   }
-  // exact sums of the elements above the window
-  u128 AP, AH;
-  unsigned AC;
-  exact_sum(wk_hi + 1u, 0xFFFFFFFFu, AP, AH, AC);
   double myS = -1.0;
   unsigned myK = 0u;
+  u128 myP = mk128(0, 0), myH = mk128(0, 0);
+  unsigned myC = 0u;
   if (mode == 1) {
-    const unsigned nwin = s.slot;
-    for (unsigned t = tid; t < nwin; t += NT) {
-      const unsigned kt = s.w_key[t];
+    // wave w scores window elements 64 w .. 64 w + 63 against every window element
+    const unsigned ns = s.slot;
+    const int nwin = ns < (unsigned)kWinMax ? (int)ns : kWinMax;
+    const int e = wid * 64 + lane;
+    if (wid * 64 < nwin) {
+      const unsigned ke = e < nwin ? s.w_key[e] : 0xFFFFFFFFu;
       u128 P = AP, H = AH;
       unsigned C = AC;
-      _Pragma("unroll 2") for (unsigned j = 0; j < nwin; ++j) {
-        if (s.w_key[j] >= kt) {
-          P = add128(P, mk128(s.w_plo[j], s.w_phi[j]));
-          if (W) H = add128(H, mk128(s.w_hlo[j], s.w_hhi[j]));
-          ++C;
+#pragma unroll 4
+      for (int j = 0; j < nwin; ++j) {
+        const unsigned kj = s.w_key[j];
+        const u64 plo = s.w_plo[j], phi = s.w_phi[j];
+        const bool in = kj >= ke;
+        P = add128(P, mk128(in ? plo : 0ull, in ? phi : 0ull));
+        if (W) {
+          const u64 hlo = s.w_hlo[j], hhi = s.w_hhi[j];
+          H = add128(H, mk128(in ? hlo : 0ull, in ? hhi : 0ull));
         }
+        C += in ? 1u : 0u;
       }
-      const double Pd = to_double(P);
-      const double Hd = W ? to_double(H) : (double)C;
-      const double St = Pd * Pd / Hd;
-      if (better(St, kt, myS, myK)) {
-        myS = St;
-        myK = kt;
+      if (e < nwin) {
+        const double Pd = to_double(P);
+        const double Hd = W ? to_double(H) : (double)C;
+        myS = Pd * Pd / Hd;
+        myK = ke;
+        myP = P;
+        myH = H;
+        myC = C;
       }
     }
   } else {
-    // Large window (heavy ties or an unusually flat score): walk its distinct keys downwards
-    // and score each with an exact block reduction.  Slow, and only reached by unusual inputs.
+    // Many window elements with few distinct keys (heavy ties): walk the distinct keys
+    // downwards and score each with an exact block reduction.
     unsigned prev = wk_hi + 1u;
     for (;;) {
       unsigned best = 0u;
@@ -328,54 +489,78 @@ __device__ SelResult ternary_select(const T* vals, const float* hl, int L, float
 #pragma unroll
       for (int w = 0; w < NW; ++w) best = s.red_u[w] > best ? s.red_u[w] : best;
       if (best == 0u) break;
+      u128 p = mk128(0, 0), h = mk128(0, 0);
+      unsigned c = 0u;
+      for (int i = tid; i < L; i += NT) {
+        const unsigned k = keyof(i);
+        if (k >= best && k <= wk_hi) {
+          p = add128(p, pterm(i, k));
+          if (W) h = add128(h, hterm(i));
+          ++c;
+        }
+      }
       u128 P, H;
       unsigned C;
-      exact_sum(best, wk_hi, P, H, C);
+      block_sum128(p, h, c, P, H, C);
       P = add128(P, AP);
       if (W) H = add128(H, AH);
       C += AC;
       const double Pd = to_double(P);
       const double Hd = W ? to_double(H) : (double)C;
       const double St = Pd * Pd / Hd;
-      if (better(St, best, myS, myK)) {
+      if (tid == 0 && better(St, best, myS, myK)) {  // tracked by thread 0 only
         myS = St;
         myK = best;
+        myP = P;
+        myH = H;
+        myC = C;
       }
       prev = best;
     }
   }
-  // ---- block argmax over (score desc, key desc)
+  // ---- argmax over (score desc, key desc): within the wave, then across waves.  Lanes with
+  // equal (score, key) hold equal sums; the lowest such lane is taken.
+  int src = lane;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     const double S2 = __shfl_xor(myS, o);
     const unsigned k2 = __shfl_xor(myK, o);
-    if (better(S2, k2, myS, myK)) {
+    const int s2 = __shfl_xor(src, o);
+    if (better(S2, k2, myS, myK) || (S2 == myS && k2 == myK && s2 < src)) {
       myS = S2;
       myK = k2;
+      src = s2;
     }
   }
-  __syncthreads();
-  if (lane == 0) {
-    s.red_d[wid] = myS;
-    s.red_k[wid] = myK;
+  {
+    const u64 plo = readlane64(myP.lo, src), phi = readlane64(myP.hi, src);
+    const u64 hlo = readlane64(myH.lo, src), hhi = readlane64(myH.hi, src);
+    const unsigned cc = __builtin_amdgcn_readlane(myC, src);
+    if (lane == 0) {
+      s.f_s[wid] = myS;
+      s.f_k[wid] = myK;
+      s.f_plo[wid] = plo;
+      s.f_phi[wid] = phi;
+      s.f_hlo[wid] = hlo;
+      s.f_hhi[wid] = hhi;
+      s.f_cnt[wid] = cc;
+    }
   }
   __syncthreads();
   double S = -1.0;
   unsigned K = 0u;
+  int bw = 0;
 #pragma unroll
   for (int w = 0; w < NW; ++w)
-    if (better(s.red_d[w], s.red_k[w], S, K)) {
-      S = s.red_d[w];
-      K = s.red_k[w];
+    if (better(s.f_s[w], s.f_k[w], S, K)) {
+      S = s.f_s[w];
+      K = s.f_k[w];
+      bw = w;
     }
-  // ---- exact support sums at the chosen threshold
-  u128 P, H;
-  unsigned C;
-  exact_sum(K, 0xFFFFFFFFu, P, H, C);
   out.tkey = K;
-  out.count = C;
-  out.P = ldexp(to_double(P), -scP);
-  out.H = W ? ldexp(to_double(H), -scH) : (double)C;
+  out.count = s.f_cnt[bw];
+  out.P = ldexp(to_double(mk128(s.f_plo[bw], s.f_phi[bw])), -scP);
+  out.H = W ? ldexp(to_double(mk128(s.f_hlo[bw], s.f_hhi[bw])), -scH) : (double)out.count;
   __syncthreads();
   return out;
 }

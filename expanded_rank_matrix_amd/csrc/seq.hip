@@ -53,20 +53,19 @@ __device__ __forceinline__ int code_at(const uint32_t* pk, int i) {
 
 // Dynamic LDS of the sequential kernel; every region starts on a 16-byte boundary.
 struct SeqLds {
-  size_t rs, dl, hl, tmp, pk, part, total;
+  size_t rs, dl, hl, pk, part, total;
 };
 __host__ __device__ inline size_t al16(size_t x) { return (x + 15) & ~(size_t)15; }
 constexpr int kMaxUnits = 2048;  // row units per workgroup per matvec (checked on the host)
 __host__ __device__ inline SeqLds seq_lds_layout(int m, int n, bool weighted) {
   const size_t L = (size_t)(m > n ? m : n);
-  const size_t L4 = (L + 3) & ~(size_t)3, n4 = (size_t)((n + 3) & ~3);
+  const size_t n4 = (size_t)((n + 3) & ~3);
   const size_t wm = (size_t)((m + 15) / 16), wn = (size_t)((n + 15) / 16);
   SeqLds s;
   s.rs = al16(sizeof(SelScratch));
   s.dl = al16(s.rs + 8 * (size_t)m);
   s.hl = al16(s.dl + 8 * L);
-  s.tmp = al16(s.hl + (weighted ? 4 * n4 : 0));
-  s.pk = al16(s.tmp + L4);
+  s.pk = al16(s.hl + (weighted ? 4 * n4 : 0));
   s.part = al16(s.pk + 4 * (4 * wm + 3 * wn + 4));
   s.total = al16(s.part + 8 * (size_t)kMaxUnits);
   return s;
@@ -74,6 +73,24 @@ __host__ __device__ inline SeqLds seq_lds_layout(int m, int n, bool weighted) {
 
 struct SeqShared {
   int ivals[8];
+  int pk_changed[16];
+  int pk_sum[16];
+  double pk_p[16];
+};
+
+// 16 bits spread to the even bit positions of a 32-bit word.
+__device__ __forceinline__ unsigned spread16(unsigned x) {
+  x = (x | (x << 8)) & 0x00FF00FFu;
+  x = (x | (x << 4)) & 0x0F0F0F0Fu;
+  x = (x | (x << 2)) & 0x33333333u;
+  x = (x | (x << 1)) & 0x55555555u;
+  return x;
+}
+
+struct PackOut {
+  int changed;  // some word differs from the previous contents
+  int sum;      // signed sum of the codes
+  double p;     // sum of |vals| over the support (when asked for)
 };
 
 // Weights of one float4 (elements 4q .. 4q+3) of a packed ternary vector, optionally times the
@@ -219,7 +236,6 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
   double* rs = reinterpret_cast<double*>(smem + lay.rs);    // m: replicated row sums
   double* dl = reinterpret_cast<double*>(smem + lay.dl);    // exchanged vector (z or w)
   float* hl = reinterpret_cast<float*>(smem + lay.hl);      // n4 column weights (weighted)
-  int8_t* tmp = reinterpret_cast<int8_t*>(smem + lay.tmp);  // staging for packing
   uint32_t* pk = reinterpret_cast<uint32_t*>(smem + lay.pk);
   double* part = reinterpret_cast<double*>(smem + lay.part);
   const int wm = a.wm, wn = a.wn;
@@ -246,41 +262,64 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
   double e0 = 0.0;
   for (int i = tid; i < m; i += NT) e0 += a.rowE[i];
   e0 = wave_sum_f64(e0);
-  if (lane == 0) s.red_d[wid] = e0;
+  if (lane == 0) s.f_s[wid] = e0;
   __syncthreads();
   double E0 = 0.0;
-  for (int w = 0; w < NW; ++w) E0 += s.red_d[w];
+  for (int w = 0; w < NW; ++w) E0 += s.f_s[w];
   double E = E0;
   bool dead = !(E0 > 0.0);
   bool have_pending = false, r_applied = true, rt_applied = true;
   float pd = 0.0f;
   __syncthreads();
 
-  // pack the +-1/0 staging array into words; returns whether any word changed
-  auto pack_into = [&](uint32_t* dst, int len, int words) -> int {
-    int changed = 0;
-    for (int w = tid; w < words; w += NT) {
-      unsigned word = 0u;
-      for (int q = 0; q < 16; ++q) {
-        const int i = w * 16 + q;
-        if (i < len) word |= tcode(tmp[i]) << (2 * q);
+  // Pack the selection r of vals[0..len) into dst (2-bit codes) with wave ballots: wave w takes
+  // the 64-element chunks w, w + NW, ...; lanes 0..3 write the chunk's four words.  prev, when
+  // given, receives the old words.  Block totals are combined in wave order (deterministic).
+  auto pack_sel = [&](const double* vals, int len, const SelResult& r, uint32_t* dst, uint32_t* prev,
+                      bool want_p) -> PackOut {
+    const int words = (len + 15) >> 4;
+    const int nch = (len + 63) >> 6;
+    int changed = 0, sum = 0;
+    double pacc = 0.0;
+    for (int c = wid; c < nch; c += NW) {
+      const int i = c * 64 + lane;
+      const double xv = i < len ? vals[i] : 0.0;
+      const float x = (float)xv;
+      const bool sel = i < len && selected(x, r);
+      const bool neg = sel && x < 0.0f;
+      const u64 mnz = __ballot(sel), mneg = __ballot(neg);
+      if (want_p && sel) pacc += fabs(xv);
+      sum += (int)__popcll(mnz) - 2 * (int)__popcll(mneg);
+      const int w = c * 4 + lane;
+      if (lane < 4 && w < words) {
+        const unsigned bnz = (unsigned)(mnz >> (16 * lane)) & 0xFFFFu;
+        const unsigned bng = (unsigned)(mneg >> (16 * lane)) & 0xFFFFu;
+        const unsigned word = spread16(bnz) | (spread16(bng) << 1);
+        const unsigned old = dst[w];
+        if (prev) prev[w] = old;
+        changed |= word != old ? 1 : 0;
+        dst[w] = word;
       }
-      if (word != dst[w]) changed = 1;
-      dst[w] = word;
     }
-    return changed;
-  };
-  // staging from a selection over vals (fp32 rounding decides membership and sign)
-  auto stage_from = [&](const double* vals, int len, const SelResult& r) -> int {
-    int sum = 0;
-    for (int i = tid; i < len; i += NT) {
-      const float x = (float)vals[i];
-      const int v = selected(x, r) ? (x > 0.0f ? 1 : -1) : 0;
-      tmp[i] = (int8_t)v;
-      sum += v;
+    const int wch = __ballot(changed != 0) != 0ull ? 1 : 0;
+    if (want_p) pacc = wave_sum_f64(pacc);
+    if (lane == 0) {
+      sh.pk_changed[wid] = wch;
+      sh.pk_sum[wid] = sum;
+      sh.pk_p[wid] = pacc;
     }
     __syncthreads();
-    return sum;
+    PackOut o;
+    o.changed = 0;
+    o.sum = 0;
+    o.p = 0.0;
+#pragma unroll
+    for (int w2 = 0; w2 < NW; ++w2) {
+      o.changed |= sh.pk_changed[w2];
+      o.sum += sh.pk_sum[w2];
+      o.p += sh.pk_p[w2];
+    }
+    return o;
   };
   // Largest |R_ij| over the residual (smallest row-major index on ties), after the pending
   // deflation.  Returns the row, -1 if R == 0, -2 on a barrier failure.
@@ -386,9 +425,7 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
       set_unit_u(r);
       fallback = true;
     } else {
-      stage_from(rs, m, su);
-      pack_into(pu, m, wm);
-      __syncthreads();
+      pack_sel(rs, m, su, pu, nullptr, false);
     }
     for (int w = tid; w < wm; w += NT) pu0[w] = pu[w];
     __syncthreads();
@@ -429,8 +466,9 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
         __syncthreads();
         continue;
       }
-      sumv = block_sum_int(stage_from(dl, n, sv));
-      const int vchanged = __syncthreads_or(pack_into(pv, n, wn));
+      const PackOut pvo = pack_sel(dl, n, sv, pv, nullptr, false);
+      sumv = pvo.sum;
+      const int vchanged = pvo.changed;
       Hv = sv.H;
       if (t >= 1) vbytes += 4.0 * (double)n * (double)cnt_u;  // rows of the u behind this V-step
       if (t >= 1 && !vchanged) {
@@ -448,19 +486,12 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
       for (int i = tid; i < m; i += NT) dl[i] = ld_dev(a.xz + i);
       __syncthreads();
       const SelResult s2 = ternary_select<NT, false>(dl, nullptr, m, a.tau, 0, s);
-      // p = sum over supp(u) of u_i z_i with the fp64 z, fixed reduction order
-      double lp = 0.0;
-      for (int i = tid; i < m; i += NT)
-        if (selected((float)dl[i], s2)) lp += fabs(dl[i]);
-      lp = wave_sum_f64(lp);
-      if (lane == 0) part[wid] = lp;
-      for (int w = tid; w < wm; w += NT) pu_prev[w] = pu[w];
-      __syncthreads();
-      p = 0.0;
-      for (int w = 0; w < NW; ++w) p += part[w];
+      // new u, the previous one kept in pu_prev, and p = sum over supp(u) of u_i z_i with the
+      // fp64 z (fixed reduction order)
+      const PackOut puo = pack_sel(dl, m, s2, pu, pu_prev, true);
+      p = puo.p;
       cnt_u = s2.count;
-      stage_from(dl, m, s2);
-      const int uchanged = __syncthreads_or(pack_into(pu, m, wm));
+      const int uchanged = puo.changed;
       ++t;
       if (!uchanged && t < a.T) {
         early = true;
