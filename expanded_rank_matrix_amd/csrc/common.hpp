@@ -127,18 +127,76 @@ __device__ __forceinline__ int exp_bound(float x) {
 }
 
 // ---- wave / block reductions --------------------------------------------------------
-__device__ __forceinline__ unsigned wave_max_u32(unsigned v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    unsigned t = __shfl_xor(v, o);
-    v = t > v ? t : v;
-  }
+// Wave-wide scans and reductions move data with DPP (no LDS round trip).  Encodings (gfx9):
+// row_shr:n = 0x110 + n, row_bcast:15 = 0x142, row_bcast:31 = 0x143.  The six steps
+//   row_shr 1, 2, 4, 8 (inclusive scan inside each row of 16 lanes; lanes that would read
+//   outside their row read zero), row_bcast:15 into rows 1 and 3, row_bcast:31 into rows 2 and 3
+// leave the inclusive scan of the wave in every lane, so lane 63 holds the total.  Every op
+// below must therefore treat a zero operand as neutral.  Reductions broadcast lane 63's value
+// with readlane, so all lanes receive bitwise the same result.
+template <int CTRL, int RM>
+__device__ __forceinline__ unsigned dpp32(unsigned v) {
+  return (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, RM, 0xF, true);
+}
+template <int CTRL, int RM>
+__device__ __forceinline__ u64 dpp64(u64 v) {
+  const unsigned lo = dpp32<CTRL, RM>((unsigned)v);
+  const unsigned hi = dpp32<CTRL, RM>((unsigned)(v >> 32));
+  return ((u64)hi << 32) | lo;
+}
+template <int CTRL, int RM>
+__device__ __forceinline__ double dppf64(double v) {
+  return __longlong_as_double((long long)dpp64<CTRL, RM>((u64)__double_as_longlong(v)));
+}
+__device__ __forceinline__ unsigned readlane32(unsigned v, int l) { return __builtin_amdgcn_readlane(v, l); }
+__device__ __forceinline__ u64 readlane64(u64 v, int l) {
+  const unsigned lo = __builtin_amdgcn_readlane((unsigned)v, l);
+  const unsigned hi = __builtin_amdgcn_readlane((unsigned)(v >> 32), l);
+  return ((u64)hi << 32) | lo;
+}
+__device__ __forceinline__ double readlane_f64(double v, int l) {
+  return __longlong_as_double((long long)readlane64((u64)__double_as_longlong(v), l));
+}
+
+#define EXTERND_WAVE_STEPS(STEP) \
+  STEP(0x111, 0xF)               \
+  STEP(0x112, 0xF)               \
+  STEP(0x114, 0xF)               \
+  STEP(0x118, 0xF)               \
+  STEP(0x142, 0xA)               \
+  STEP(0x143, 0xC)
+
+__device__ __forceinline__ double wave_scan_f64(double v) {
+#define EXTERND_STEP(C, R) v += dppf64<C, R>(v);
+  EXTERND_WAVE_STEPS(EXTERND_STEP)
+#undef EXTERND_STEP
   return v;
 }
-__device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+__device__ __forceinline__ unsigned wave_scan_u32(unsigned v) {
+#define EXTERND_STEP(C, R) v += dpp32<C, R>(v);
+  EXTERND_WAVE_STEPS(EXTERND_STEP)
+#undef EXTERND_STEP
   return v;
+}
+__device__ __forceinline__ double wave_sum_f64(double v) { return readlane_f64(wave_scan_f64(v), 63); }
+__device__ __forceinline__ unsigned wave_sum_u32(unsigned v) { return readlane32(wave_scan_u32(v), 63); }
+__device__ __forceinline__ unsigned wave_max_u32(unsigned v) {
+#define EXTERND_STEP(C, R)              \
+  {                                     \
+    const unsigned t = dpp32<C, R>(v);  \
+    v = t > v ? t : v;                  \
+  }
+  EXTERND_WAVE_STEPS(EXTERND_STEP)
+#undef EXTERND_STEP
+  return readlane32(v, 63);
+}
+
+// Wave sum of 128-bit values (exact, any order), same result in every lane.
+__device__ __forceinline__ u128 wave_sum128(u128 v) {
+#define EXTERND_STEP(C, R) v = add128(v, mk128(dpp64<C, R>(v.lo), dpp64<C, R>(v.hi)));
+  EXTERND_WAVE_STEPS(EXTERND_STEP)
+#undef EXTERND_STEP
+  return mk128(readlane64(v.lo, 63), readlane64(v.hi, 63));
 }
 
 // Ternary packing: element t in bits 2(t%16)..2(t%16)+1 of word t/16; 00 = 0, 01 = +1, 11 = -1.

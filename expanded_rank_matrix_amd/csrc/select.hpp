@@ -67,16 +67,6 @@ __device__ __forceinline__ bool better(double S1, unsigned k1, double S2, unsign
   return S1 > S2 || (S1 == S2 && k1 > k2);
 }
 
-__device__ __forceinline__ u128 shfl_xor128(u128 v, int o) {
-  return mk128(__shfl_xor(v.lo, o), __shfl_xor(v.hi, o));
-}
-
-__device__ __forceinline__ u64 readlane64(u64 v, int l) {
-  const unsigned lo = __builtin_amdgcn_readlane((unsigned)v, l);
-  const unsigned hi = __builtin_amdgcn_readlane((unsigned)(v >> 32), l);
-  return ((u64)hi << 32) | lo;
-}
-
 // Whether a slot holding x is in the support of r.
 __device__ __forceinline__ bool selected(float x, const SelResult& r) {
   const unsigned k = __float_as_uint(x) & 0x7FFFFFFFu;
@@ -209,21 +199,11 @@ __device__ SelResult ternary_select(const T* vals, const float* hl, int L, float
       th += bh[q];
       tc += bc[q];
     }
-    double ip = tp, ih = th;
-    unsigned ic = tc;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const double a0 = __shfl_up(ip, o), a1 = __shfl_up(ih, o);
-      const unsigned a2 = __shfl_up(ic, o);
-      if (lane >= o) {
-        ip += a0;
-        ih += a1;
-        ic += a2;
-      }
-    }
+    const double ip = wave_scan_f64(tp), ih = W ? wave_scan_f64(th) : 0.0;
+    const unsigned ic = wave_scan_u32(tc);
     if (lane == 63) {
       s.w_sp[wid] = ip;
-      s.w_sh[wid] = ih;
+      s.w_sh[wid] = W ? ih : (double)ic;
       s.w_sc[wid] = ic;
     }
     __syncthreads();
@@ -235,7 +215,7 @@ __device__ SelResult ternary_select(const T* vals, const float* hl, int L, float
       rc0 += s.w_sc[w];
     }
     rp0 += ip - tp;
-    rh0 += ih - th;
+    rh0 += W ? ih - th : (double)(ic - tc);
     rc0 += ic - tc;
     // best boundary score as a fraction bn / bd (carried over from earlier levels)
     double bn = s.bn, bd = s.bd;
@@ -251,15 +231,18 @@ __device__ SelResult ternary_select(const T* vals, const float* hl, int L, float
         }
       }
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const double n2 = __shfl_xor(bn, o), d2 = __shfl_xor(bd, o);
-      if (n2 * bd > bn * d2) {
-        bn = n2;
-        bd = d2;
-      }
-    }
-    if (lane == 0) {
+    // wave maximum (lane 63); a zero-filled operand (0, 0) never wins
+#define EXTERND_STEP(C, R)                                  \
+  {                                                         \
+    const double n2 = dppf64<C, R>(bn), d2 = dppf64<C, R>(bd); \
+    if (n2 * bd > bn * d2) {                                \
+      bn = n2;                                              \
+      bd = d2;                                              \
+    }                                                       \
+  }
+    EXTERND_WAVE_STEPS(EXTERND_STEP)
+#undef EXTERND_STEP
+    if (lane == 63) {
       s.w_bn[wid] = bn;
       s.w_bd[wid] = bd;
     }
@@ -305,24 +288,31 @@ __device__ SelResult ternary_select(const T* vals, const float* hl, int L, float
         rc += c;
       }
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const int l2 = __shfl_xor(lo, o), h2 = __shfl_xor(hi, o);
-      const unsigned cl2 = __shfl_xor(clo, o), ch2 = __shfl_xor(chi, o);
-      if (l2 < lo) {
-        lo = l2;
-        clo = cl2;
+    // wave minimum of lo and maximum of hi (lane 63), with their counts; encoded so that a
+    // zero-filled operand is neutral: xlo = kSelBins - lo, xhi = hi + 1
+    {
+      unsigned xlo = (unsigned)(kSelBins - lo), xhi = (unsigned)(hi + 1);
+#define EXTERND_STEP(C, R)                                                  \
+  {                                                                         \
+    const unsigned l2 = dpp32<C, R>(xlo), c2 = dpp32<C, R>(clo);              \
+    const unsigned h2 = dpp32<C, R>(xhi), d2 = dpp32<C, R>(chi);              \
+    if (l2 > xlo) {                                                         \
+      xlo = l2;                                                             \
+      clo = c2;                                                             \
+    }                                                                       \
+    if (h2 > xhi) {                                                         \
+      xhi = h2;                                                             \
+      chi = d2;                                                             \
+    }                                                                       \
+  }
+      EXTERND_WAVE_STEPS(EXTERND_STEP)
+#undef EXTERND_STEP
+      if (lane == 63) {
+        s.w_lo[wid] = kSelBins - (int)xlo;
+        s.w_hi[wid] = (int)xhi - 1;
+        s.w_clo[wid] = clo;
+        s.w_chi[wid] = chi;
       }
-      if (h2 > hi) {
-        hi = h2;
-        chi = ch2;
-      }
-    }
-    if (lane == 0) {
-      s.w_lo[wid] = lo;
-      s.w_hi[wid] = hi;
-      s.w_clo[wid] = clo;
-      s.w_chi[wid] = chi;
     }
     __syncthreads();
     lo = kSelBins;
@@ -381,12 +371,9 @@ __device__ SelResult ternary_select(const T* vals, const float* hl, int L, float
   auto hterm = [&](int i) -> u128 { return W ? fixp((double)hl[i], scH) : mk128(1ull, 0ull); };
   // per-wave exact partials -> LDS -> every thread sums them in wave order
   auto block_sum128 = [&](u128 p, u128 h, unsigned c, u128& P, u128& H, unsigned& C) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      p = add128(p, shfl_xor128(p, o));
-      if (W) h = add128(h, shfl_xor128(h, o));
-      c += __shfl_xor(c, o);
-    }
+    p = wave_sum128(p);
+    if (W) h = wave_sum128(h);
+    c = wave_sum_u32(c);
     __syncthreads();
     if (lane == 0) {
       s.a_plo[wid] = p.lo;
@@ -518,20 +505,25 @@ __device__ SelResult ternary_select(const T* vals, const float* hl, int L, float
       prev = best;
     }
   }
-  // ---- argmax over (score desc, key desc): within the wave, then across waves.  Lanes with
-  // equal (score, key) hold equal sums; the lowest such lane is taken.
+  // ---- argmax over (score desc, key desc): within the wave (toward lane 63; a zero-filled
+  // operand, score 0, loses to every real threshold), then across waves.  Lanes with equal
+  // (score, key) hold equal sums.
   int src = lane;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const double S2 = __shfl_xor(myS, o);
-    const unsigned k2 = __shfl_xor(myK, o);
-    const int s2 = __shfl_xor(src, o);
-    if (better(S2, k2, myS, myK) || (S2 == myS && k2 == myK && s2 < src)) {
-      myS = S2;
-      myK = k2;
-      src = s2;
-    }
+#define EXTERND_STEP(C, R)                                                               \
+  {                                                                                      \
+    const double S2 = dppf64<C, R>(myS);                                                 \
+    const unsigned k2 = dpp32<C, R>(myK), s2 = dpp32<C, R>((unsigned)src);                \
+    if (better(S2, k2, myS, myK)) {                                                      \
+      myS = S2;                                                                          \
+      myK = k2;                                                                          \
+      src = (int)s2;                                                                     \
+    }                                                                                    \
   }
+  EXTERND_WAVE_STEPS(EXTERND_STEP)
+#undef EXTERND_STEP
+  myS = readlane_f64(myS, 63);
+  myK = readlane32(myK, 63);
+  src = (int)readlane32((unsigned)src, 63);
   {
     const u64 plo = readlane64(myP.lo, src), phi = readlane64(myP.hi, src);
     const u64 hlo = readlane64(myH.lo, src), hhi = readlane64(myH.hi, src);
