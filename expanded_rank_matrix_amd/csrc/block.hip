@@ -37,7 +37,9 @@ struct BlockWs {
   double* part;    // split-K partials
   double* GU;      // b x b
   double* GV;      // b x b
-  double* Lc;      // b x b Cholesky factor
+  double* Lc;      // b x b Cholesky factor (lower triangle)
+  double* LT;      // its transpose
+  double* Md;      // b: u_c^T Q_c (diagonal of U^T R H V)
   double* PHC;     // b x 3 selection results
   float* d;        // b
   double* st;      // [0] E, [1] E0
@@ -67,6 +69,8 @@ static BlockWs carve(void* base, int m, int n, int b) {
   w.GU = reinterpret_cast<double*>(take((size_t)b * b * 8));
   w.GV = reinterpret_cast<double*>(take((size_t)b * b * 8));
   w.Lc = reinterpret_cast<double*>(take((size_t)b * b * 8));
+  w.LT = reinterpret_cast<double*>(take((size_t)b * b * 8));
+  w.Md = reinterpret_cast<double*>(take((size_t)b * 8));
   w.PHC = reinterpret_cast<double*>(take((size_t)b * 3 * 8));
   w.d = reinterpret_cast<float*>(take((size_t)b * 4));
   w.st = reinterpret_cast<double*>(take(64));
@@ -87,6 +91,8 @@ size_t block_workspace_bytes(int m, int n, int b) {
   take((size_t)b * b * 8);
   take((size_t)b * b * 8);
   take((size_t)b * b * 8);
+  take((size_t)b * b * 8);
+  take((size_t)b * 8);
   take((size_t)b * 3 * 8);
   take((size_t)b * 4);
   take(64);
@@ -125,8 +131,8 @@ __global__ void __launch_bounds__(256) omega_kernel(int8_t* Vt, int bs, int n, l
 // D(i, j) in lane j + 16 (i % 4), register i / 4 (rows interleaved, unlike the fp32 forms).
 // Tile: 64 rows of R (one 16-row strip per wave) x all components (NCT tiles of 16); K chunks
 // of 32 columns staged in LDS.
-template <int NCT>
-__global__ void __launch_bounds__(256) contract_rw_kernel(const float* R, int ldr, int m, int n, const int8_t* T,
+template <int NCT, typename TR>
+__global__ void __launch_bounds__(256) contract_rw_kernel(const TR* R, int ldr, int m, int n, const int8_t* T,
                                                           const float* h, int bs, int kspan, double* part) {
   constexpr int KC = 32;
   __shared__ float Rs[64][KC + 1];
@@ -144,7 +150,7 @@ __global__ void __launch_bounds__(256) contract_rw_kernel(const float* R, int ld
     for (int x = tid; x < 64 * KC; x += 256) {
       const int r = x / KC, c = x % KC;
       const int i = i0 + r, j = k0 + c;
-      Rs[r][c] = (i < m && j < ke) ? R[(size_t)i * ldr + j] : 0.0f;
+      Rs[r][c] = (i < m && j < ke) ? (float)R[(size_t)i * ldr + j] : 0.0f;
     }
     for (int x = tid; x < 16 * NCT * KC; x += 256) {
       const int cc = x / KC, c = x % KC;
@@ -243,88 +249,134 @@ __global__ void __launch_bounds__(256) reduce_splits_kernel(const double* part, 
   }
 }
 
-// ---- Gram of ternary component rows: G[c][c2] = sum_i w_i T[c][i] T[c2][i] ---------------
-__global__ void __launch_bounds__(256) gram_kernel(const int8_t* T, int len, int bs, const float* w, double* G) {
-  __shared__ double red[4][16];
-  const int c = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  for (int c2b = 0; c2b < bs; c2b += 16) {
-    double acc[16];
-#pragma unroll
-    for (int q = 0; q < 16; ++q) acc[q] = 0.0;
-    for (int i = tid; i < len; i += 256) {
-      const int tc = T[(size_t)c * len + i];
-      if (tc == 0) continue;
-      const double wt = w ? (double)w[i] : 1.0;
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int c2 = c2b + q;
-        if (c2 < bs) {
-          const int p = tc * (int)T[(size_t)c2 * len + i];
-          if (p) acc[q] += wt * (double)p;
-        }
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const double v = wave_sum_f64(acc[q]);
-      if (lane == 0) red[wid][q] = v;
-    }
-    __syncthreads();
-    if (tid < 16 && c2b + tid < bs) {
-      const double v = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
-      G[(size_t)c * bs + c2b + tid] = v;
-    }
-    __syncthreads();
-  }
-}
-
-// ---- Cholesky of G + eps I, eps = 1e-6 trace(G) / bs (one workgroup; textbook order) --------
-__global__ void __launch_bounds__(256) chol_kernel(const double* G, int bs, double* L) {
+// ---- Cholesky of G + eps I, eps = 1e-6 trace(G) / bs, by one workgroup of NT threads.  The
+// lower triangle (packed, element e = i (i + 1) / 2 + k) is held in registers: slot q of thread t
+// holds element q * NT + t.  Right-looking order: after step j every entry (i, k), k > j, has had
+// L_ij L_kj subtracted, so each entry sees its subtractions in ascending t, as in the textbook
+// left-looking formula.  Writes L (row-major) and its transpose.
+constexpr int kCholSlots = 33;  // ceil(128 * 129 / 2 / 256) = ceil(256 * 257 / 2 / 1024) = 33
+template <int NT>
+__global__ void __launch_bounds__(NT) chol_kernel(const double* G, int bs, double* L, double* LT) {
 #pragma clang fp contract(off)
+  __shared__ double colb[2][256];  // column j in buffer j % 2 (no barrier needed between steps)
   __shared__ double eps_s;
-  if (threadIdx.x == 0) {
+  const int tid = threadIdx.x;
+  const int ne = bs * (bs + 1) / 2;
+  if (tid == 0) {
     double tr = 0.0;
     for (int c = 0; c < bs; ++c) tr += G[(size_t)c * bs + c];
     eps_s = 1e-6 * tr / (double)bs;
   }
-  for (int x = threadIdx.x; x < bs * bs; x += 256) L[x] = 0.0;
   __syncthreads();
   const double eps = eps_s;
-  for (int j = 0; j < bs; ++j) {
-    if (threadIdx.x == 0) {
-      double s = G[(size_t)j * bs + j] + eps;
-      for (int t = 0; t < j; ++t) s -= L[(size_t)j * bs + t] * L[(size_t)j * bs + t];
-      L[(size_t)j * bs + j] = s > 0.0 ? sqrt(s) : 0.0;
+  double a[kCholSlots];
+  int ik[kCholSlots];  // (i << 16) | k, or -1 for an unused slot
+#pragma unroll
+  for (int q = 0; q < kCholSlots; ++q) {
+    const int e = q * NT + tid;
+    if (e < ne) {
+      int i = (int)((sqrt(8.0 * (double)e + 1.0) - 1.0) * 0.5);
+      while ((i + 1) * (i + 2) / 2 <= e) ++i;
+      while (i * (i + 1) / 2 > e) --i;
+      const int k = e - i * (i + 1) / 2;
+      ik[q] = (i << 16) | k;
+      a[q] = G[(size_t)i * bs + k] + (i == k ? eps : 0.0);
+    } else {
+      ik[q] = -1;
+      a[q] = 0.0;
     }
-    __syncthreads();
-    const double ljj = L[(size_t)j * bs + j];
-    for (int i = j + 1 + threadIdx.x; i < bs; i += 256) {
-      double s = G[(size_t)i * bs + j];
-      for (int t = 0; t < j; ++t) s -= L[(size_t)i * bs + t] * L[(size_t)j * bs + t];
-      L[(size_t)i * bs + j] = ljj > 0.0 ? s / ljj : 0.0;
-    }
-    __syncthreads();
   }
+  for (int j = 0; j < bs; ++j) {
+    double* col = colb[j & 1];
+#pragma unroll
+    for (int q = 0; q < kCholSlots; ++q)
+      if (ik[q] == ((j << 16) | j)) {
+        a[q] = a[q] > 0.0 ? sqrt(a[q]) : 0.0;
+        col[j] = a[q];
+      }
+    __syncthreads();
+    const double ljj = col[j];
+#pragma unroll
+    for (int q = 0; q < kCholSlots; ++q) {
+      const int i = ik[q] >> 16, k = ik[q] & 0xFFFF;
+      if (ik[q] >= 0 && k == j && i > j) {
+        a[q] = ljj > 0.0 ? a[q] / ljj : 0.0;
+        col[i] = a[q];
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < kCholSlots; ++q) {
+      const int i = ik[q] >> 16, k = ik[q] & 0xFFFF;
+      if (ik[q] >= 0 && k > j) a[q] -= col[i] * col[k];
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < kCholSlots; ++q)
+    if (ik[q] >= 0) {
+      const int i = ik[q] >> 16, k = ik[q] & 0xFFFF;
+      L[(size_t)i * bs + k] = a[q];
+      LT[(size_t)k * bs + i] = a[q];
+    }
 }
 
-// ---- out[:, col] = (L L^T)^-1 in[:, col] for every column (b x ncols, column-major access) ----
-__global__ void __launch_bounds__(256) solve_kernel(const double* L, int bs, const double* in, double* out,
-                                                    long long ncols) {
-#pragma clang fp contract(off)
-  const long long col = blockIdx.x * 256ll + threadIdx.x;
-  if (col >= ncols) return;
+// ---- out[:, col] = (L L^T)^-1 in[:, col]: one column per lane, 64 columns per workgroup, the
+// column in LDS (bs x 64 doubles); L and L^T are read at workgroup-uniform addresses.  The inner
+// sums run in four interleaved partial sums.  in and out may alias.
+__global__ void __launch_bounds__(64) solve_kernel(const double* __restrict__ L, const double* __restrict__ LT,
+                                                   int bs, const double* in, double* out, int ncols) {
+  extern __shared__ double xs[];
+  const int lane = threadIdx.x;
+  const int col = blockIdx.x * 64 + lane;
+  const bool ok = col < ncols;
+  for (int i = 0; i < bs; ++i) xs[i * 64 + lane] = ok ? in[(size_t)i * ncols + col] : 0.0;
   for (int i = 0; i < bs; ++i) {
-    double s = in[(size_t)i * ncols + col];
-    for (int t = 0; t < i; ++t) s -= L[(size_t)i * bs + t] * out[(size_t)t * ncols + col];
-    const double lii = L[(size_t)i * bs + i];
-    out[(size_t)i * ncols + col] = lii > 0.0 ? s / lii : 0.0;
+    const double* Li = L + (size_t)i * bs;
+    double p0 = 0.0, p1 = 0.0, p2 = 0.0, p3 = 0.0;
+    int t = 0;
+    for (; t + 4 <= i; t += 4) {
+      p0 += Li[t] * xs[t * 64 + lane];
+      p1 += Li[t + 1] * xs[(t + 1) * 64 + lane];
+      p2 += Li[t + 2] * xs[(t + 2) * 64 + lane];
+      p3 += Li[t + 3] * xs[(t + 3) * 64 + lane];
+    }
+    for (; t < i; ++t) p0 += Li[t] * xs[t * 64 + lane];
+    const double s = xs[i * 64 + lane] - ((p0 + p1) + (p2 + p3));
+    const double lii = Li[i];
+    xs[i * 64 + lane] = lii > 0.0 ? s / lii : 0.0;
   }
   for (int i = bs - 1; i >= 0; --i) {
-    double s = out[(size_t)i * ncols + col];
-    for (int t = i + 1; t < bs; ++t) s -= L[(size_t)t * bs + i] * out[(size_t)t * ncols + col];
-    const double lii = L[(size_t)i * bs + i];
-    out[(size_t)i * ncols + col] = lii > 0.0 ? s / lii : 0.0;
+    const double* Ci = LT + (size_t)i * bs;  // column i of L
+    double p0 = 0.0, p1 = 0.0, p2 = 0.0, p3 = 0.0;
+    int t = i + 1;
+    for (; t + 4 <= bs; t += 4) {
+      p0 += Ci[t] * xs[t * 64 + lane];
+      p1 += Ci[t + 1] * xs[(t + 1) * 64 + lane];
+      p2 += Ci[t + 2] * xs[(t + 2) * 64 + lane];
+      p3 += Ci[t + 3] * xs[(t + 3) * 64 + lane];
+    }
+    for (; t < bs; ++t) p0 += Ci[t] * xs[t * 64 + lane];
+    const double s = xs[i * 64 + lane] - ((p0 + p1) + (p2 + p3));
+    const double lii = Ci[i];
+    xs[i * 64 + lane] = lii > 0.0 ? s / lii : 0.0;
   }
+  if (ok)
+    for (int i = 0; i < bs; ++i) out[(size_t)i * ncols + col] = xs[i * 64 + lane];
+}
+
+// ---- Md[c] = sum_i U[c][i] Y[c][i] (one workgroup per component, fixed reduction order)
+__global__ void __launch_bounds__(256) rowdot_kernel(const int8_t* Ut, const double* Yt, int m, double* Md) {
+  __shared__ double red[4];
+  const int c = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  double acc = 0.0;
+  for (int i = tid; i < m; i += 256) {
+    const int u = Ut[(size_t)c * m + i];
+    if (u) acc += (double)u * Yt[(size_t)c * m + i];
+  }
+  acc = wave_sum_f64(acc);
+  if (lane == 0) red[wid] = acc;
+  __syncthreads();
+  if (tid == 0) Md[c] = (red[0] + red[1]) + (red[2] + red[3]);
 }
 
 // ---- one workgroup per component row: T[c] = T_tau(fp32(X[c]); h) -----------------------------
@@ -410,20 +462,24 @@ __global__ void __launch_bounds__(512) fallback_kernel(const float* R, int ldr, 
   }
 }
 
-// ---- scales and energy: one workgroup, the sequential scale per component in order ----------
-__global__ void __launch_bounds__(256) scales_kernel(const int8_t* Ut, const double* Yt, const double* GU,
-                                                     const double* GV, int m, int bs, int k0, int T, float* dvec,
-                                                     float* D, double* energy, double* st, int* flags,
-                                                     u64* stats) {
+// ---- scales and energy: one workgroup, thread t owns component t.  The sequential scale of each
+// component against the residual left by the earlier ones of the block:
+//   p_t = Md_t - sum_{c < t} d_c (u_t . u_c) (v_c^T H v_t),   d_t = fp32(p_t / q_t),
+// the subtractions applied in ascending c (as the textbook loop does); the Gram of U is exactly
+// symmetric (integer entries), so row c is read for column c.
+__global__ void __launch_bounds__(256) scales_kernel(const double* Md, const double* GU, const double* GV, int bs,
+                                                     int k0, int T, float* dvec, float* D, double* energy,
+                                                     double* st, int* flags, u64* stats) {
 #pragma clang fp contract(off)
-  __shared__ double Mdiag[256];
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  __shared__ float ds[256];
+  __shared__ double ps[256], qs[256];
+  const int tid = threadIdx.x;
   if (tid == 0) {
     if (flags[0]) {
       if (st[1] > 0.0) stats[3] += (u64)bs;  // zero components (none counted when A = 0)
     } else {
-      stats[0] += (u64)(2 * T);      // ALS half-steps
-      stats[2] += (u64)flags[2];     // sketch columns started from the largest entry
+      stats[0] += (u64)(2 * T);   // ALS half-steps
+      stats[2] += (u64)flags[2];  // sketch columns started from the largest entry
     }
   }
   if (flags[0]) {
@@ -434,28 +490,39 @@ __global__ void __launch_bounds__(256) scales_kernel(const int8_t* Ut, const dou
     }
     return;
   }
-  for (int c = wid; c < bs; c += 4) {
-    double acc = 0.0;
-    for (int i = lane; i < m; i += 64) {
-      const int u = Ut[(size_t)c * m + i];
-      if (u) acc += (double)u * Yt[(size_t)c * m + i];
+  const bool own = tid < bs;
+  double acc = own ? Md[tid] : 0.0;
+  const double q = own ? GU[(size_t)tid * bs + tid] * GV[(size_t)tid * bs + tid] : 0.0;
+  double gu = own ? GU[tid] : 0.0, gv = own ? GV[tid] : 0.0;  // row 0
+  for (int c = 0; c < bs; ++c) {
+    if (tid == c) {
+      const float d = q > 0.0 ? (float)(acc / q) : 0.0f;
+      ds[c] = d;
+      ps[c] = acc;
+      qs[c] = q;
     }
-    acc = wave_sum_f64(acc);
-    if (lane == 0) Mdiag[c] = acc;
+    // prefetch row c + 1 before waiting
+    double gu2 = 0.0, gv2 = 0.0;
+    if (own && c + 1 < bs) {
+      gu2 = GU[(size_t)(c + 1) * bs + tid];
+      gv2 = GV[(size_t)(c + 1) * bs + tid];
+    }
+    __syncthreads();
+    if (own && tid > c) acc -= (double)ds[c] * gu * gv;
+    gu = gu2;
+    gv = gv2;
   }
   __syncthreads();
+  if (own) {
+    dvec[tid] = ds[tid];
+    D[k0 + tid] = ds[tid];
+  }
   if (tid == 0) {
     double E = st[0];
     const double E0 = st[1];
     for (int c = 0; c < bs; ++c) {
-      double p = Mdiag[c];
-      for (int c2 = 0; c2 < c; ++c2) p -= (double)dvec[c2] * GU[(size_t)c * bs + c2] * GV[(size_t)c2 * bs + c];
-      const double q = GU[(size_t)c * bs + c] * GV[(size_t)c * bs + c];
-      const float d = q > 0.0 ? (float)(p / q) : 0.0f;
-      const double dd = (double)d;
-      E = E - (2.0 * dd * p - dd * dd * q);
-      dvec[c] = d;
-      D[k0 + c] = d;
+      const double dd = (double)ds[c];
+      E = E - (2.0 * dd * ps[c] - dd * dd * qs[c]);
       energy[k0 + c] = 1.0 - E / E0;
     }
     st[0] = E;
@@ -569,12 +636,12 @@ __global__ void __launch_bounds__(256) zero_check_kernel(const float* R, int ldr
   }
 }
 
-template <int NCT>
-static void launch_rw(const float* R, int ldr, int m, int n, const int8_t* T, const float* h, int bs, int nsplit,
+template <int NCT, typename TR>
+static void launch_rw(const TR* R, int ldr, int m, int n, const int8_t* T, const float* h, int bs, int nsplit,
                       double* part, hipStream_t st) {
   const int kspan = ((n + nsplit - 1) / nsplit + 31) / 32 * 32;
-  hipLaunchKernelGGL(contract_rw_kernel<NCT>, dim3((m + 63) / 64, nsplit), dim3(256), 0, st, R, ldr, m, n, T, h,
-                     bs, kspan, part);
+  hipLaunchKernelGGL((contract_rw_kernel<NCT, TR>), dim3((m + 63) / 64, nsplit), dim3(256), 0, st, R, ldr, m, n,
+                     T, h, bs, kspan, part);
 }
 
 template <int NCT>
@@ -585,45 +652,74 @@ static void launch_utr(const float* R, int ldr, int m, int n, const int8_t* U, i
                      kspan, part);
 }
 
-static int splits_for(int tiles, int K) {
+// split-K factor: about 512 workgroups, at least 256 of K per split, at most cap splits
+static int splits_for(int tiles, int K, int cap) {
   int s = (512 + tiles - 1) / tiles;
   const int maxs = (K + 255) / 256;
   s = s > maxs ? maxs : s;
-  s = s > kMaxSplit ? kMaxSplit : s;
+  s = s > cap ? cap : s;
   return s < 1 ? 1 : s;
 }
 
-// Y^T (bs x m) = (R W)^T with W = diag(h) T^T
-static hipError_t rw_product(const BlockLaunch& L, const BlockWs& w, const int8_t* T, const float* h, int bs,
-                             double* outT, hipStream_t st) {
-  const int tiles = (L.m + 63) / 64;
-  const int ns = splits_for(tiles, L.n);
+static void reduce_splits(const double* part, int ns, long long cnt, double* out, hipStream_t st) {
+  const long long nb = (cnt + 255) / 256;
+  hipLaunchKernelGGL(reduce_splits_kernel, dim3((unsigned)(nb < 4096 ? nb : 4096)), dim3(256), 0, st, part, ns, cnt,
+                     out);
+}
+
+// part[s][c][i] = sum over split s of R[i][j] h_j T[c][j], R rows x K (ld ldr), then out = sum over s
+template <typename TR>
+static void rw_contract(const TR* R, int ldr, int rows, int K, const int8_t* T, const float* h, int bs, int cap,
+                        double* part, double* out, hipStream_t st) {
+  const int ns = splits_for((rows + 63) / 64, K, cap);
   const int nct = (bs + 15) / 16;
-  if (nct <= 1) launch_rw<1>(L.R, L.ldr, L.m, L.n, T, h, bs, ns, w.part, st);
-  else if (nct <= 2) launch_rw<2>(L.R, L.ldr, L.m, L.n, T, h, bs, ns, w.part, st);
-  else if (nct <= 4) launch_rw<4>(L.R, L.ldr, L.m, L.n, T, h, bs, ns, w.part, st);
-  else if (nct <= 8) launch_rw<8>(L.R, L.ldr, L.m, L.n, T, h, bs, ns, w.part, st);
-  else launch_rw<16>(L.R, L.ldr, L.m, L.n, T, h, bs, ns, w.part, st);
-  const long long cnt = (long long)bs * L.m;
-  hipLaunchKernelGGL(reduce_splits_kernel, dim3((unsigned)((cnt + 255) / 256 < 4096 ? (cnt + 255) / 256 : 4096)),
-                     dim3(256), 0, st, w.part, ns, cnt, outT);
-  return hipGetLastError();
+  if (nct <= 1) launch_rw<1, TR>(R, ldr, rows, K, T, h, bs, ns, part, st);
+  else if (nct <= 2) launch_rw<2, TR>(R, ldr, rows, K, T, h, bs, ns, part, st);
+  else if (nct <= 4) launch_rw<4, TR>(R, ldr, rows, K, T, h, bs, ns, part, st);
+  else if (nct <= 8) launch_rw<8, TR>(R, ldr, rows, K, T, h, bs, ns, part, st);
+  else launch_rw<16, TR>(R, ldr, rows, K, T, h, bs, ns, part, st);
+  reduce_splits(part, ns, (long long)bs * rows, out, st);
+}
+
+// Y^T (bs x m) = (R diag(h) T^T)^T
+static void rw_product(const BlockLaunch& L, const BlockWs& w, const int8_t* T, const float* h, int bs,
+                       double* outT, hipStream_t st) {
+  rw_contract<float>(L.R, L.ldr, L.m, L.n, T, h, bs, kMaxSplit, w.part, outT, st);
+}
+
+// G (bs x bs) = T diag(w) T^T for ternary rows T (bs x len); integer-exact without weights
+static void gram_product(const BlockLaunch& L, const BlockWs& w, const int8_t* T, int len, const float* wt, int bs,
+                         double* G, hipStream_t st) {
+  const int mx = L.m > L.n ? L.m : L.n;
+  long long cap = (long long)kMaxSplit * mx / bs;  // partials must fit the split buffer
+  cap = cap > 64 ? 64 : cap;
+  rw_contract<int8_t>(T, len, bs, len, T, wt, bs, (int)cap, w.part, G, st);
 }
 
 // X (bs x n) = U^T R
-static hipError_t utr_product(const BlockLaunch& L, const BlockWs& w, int bs, hipStream_t st) {
-  const int tiles = (L.n + 63) / 64;
-  const int ns = splits_for(tiles, L.m);
+static void utr_product(const BlockLaunch& L, const BlockWs& w, int bs, hipStream_t st) {
+  const int ns = splits_for((L.n + 63) / 64, L.m, kMaxSplit);
   const int nct = (bs + 15) / 16;
   if (nct <= 1) launch_utr<1>(L.R, L.ldr, L.m, L.n, w.Ut, bs, ns, w.part, st);
   else if (nct <= 2) launch_utr<2>(L.R, L.ldr, L.m, L.n, w.Ut, bs, ns, w.part, st);
   else if (nct <= 4) launch_utr<4>(L.R, L.ldr, L.m, L.n, w.Ut, bs, ns, w.part, st);
   else if (nct <= 8) launch_utr<8>(L.R, L.ldr, L.m, L.n, w.Ut, bs, ns, w.part, st);
   else launch_utr<16>(L.R, L.ldr, L.m, L.n, w.Ut, bs, ns, w.part, st);
-  const long long cnt = (long long)bs * L.n;
-  hipLaunchKernelGGL(reduce_splits_kernel, dim3((unsigned)((cnt + 255) / 256 < 4096 ? (cnt + 255) / 256 : 4096)),
-                     dim3(256), 0, st, w.part, ns, cnt, w.X);
-  return hipGetLastError();
+  reduce_splits(w.part, ns, (long long)bs * L.n, w.X, st);
+}
+
+// Cholesky of G + eps I into w.Lc / w.LT
+static void cholesky(const BlockWs& w, const double* G, int bs, hipStream_t st) {
+  if (bs <= 128)
+    hipLaunchKernelGGL(chol_kernel<256>, dim3(1), dim3(256), 0, st, G, bs, w.Lc, w.LT);
+  else
+    hipLaunchKernelGGL(chol_kernel<1024>, dim3(1), dim3(1024), 0, st, G, bs, w.Lc, w.LT);
+}
+
+// out (bs x ncols) = (L L^T)^-1 in
+static void solve(const BlockWs& w, int bs, const double* in, double* out, int ncols, hipStream_t st) {
+  const size_t smem = (size_t)bs * 64 * sizeof(double);
+  hipLaunchKernelGGL(solve_kernel, dim3((ncols + 63) / 64), dim3(64), smem, st, w.Lc, w.LT, bs, in, out, ncols);
 }
 
 static void select_rows(const double* X, int L, int bs, float tau, const float* h, int EHm, int8_t* T, double* PHC,
@@ -640,6 +736,11 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops) {
   if (L.b > 256) return hipErrorInvalidValue;
   const BlockWs w = carve(L.ws, L.m, L.n, L.b);
   const int m = L.m, n = L.n;
+  {
+    const hipError_t e = hipFuncSetAttribute((const void*)solve_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             (int)((size_t)L.b * 64 * sizeof(double)));
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(block_init_kernel, dim3(1), dim3(256), 0, st, L.rowE, m, w.st, w.flags);
   const int nblocks = (L.k + L.b - 1) / L.b;
   double fl = 0.0;
@@ -656,23 +757,24 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops) {
     fl += 2.0 * m * n * bs;
     for (int t = 0; t < L.T; ++t) {
       // V-step: G = (U^T U + eps I)^-1 U^T R, rows ternarized with weights h
-      hipLaunchKernelGGL(gram_kernel, dim3(bs), dim3(256), 0, st, w.Ut, m, bs, nullptr, w.GU);
-      hipLaunchKernelGGL(chol_kernel, dim3(1), dim3(256), 0, st, w.GU, bs, w.Lc);
+      gram_product(L, w, w.Ut, m, nullptr, bs, w.GU, st);
+      cholesky(w, w.GU, bs, st);
       utr_product(L, w, bs, st);
-      hipLaunchKernelGGL(solve_kernel, dim3((n + 255) / 256), dim3(256), 0, st, w.Lc, bs, w.X, w.X, (long long)n);
+      solve(w, bs, w.X, w.X, n, st);
       select_rows(w.X, n, bs, L.tau, L.h, L.EHm, w.Vt, w.PHC, w.flags, 0, st);
       // U-step: F^T = (V^T H V + eps I)^-1 (R H V)^T, columns ternarized without weights
-      hipLaunchKernelGGL(gram_kernel, dim3(bs), dim3(256), 0, st, w.Vt, n, bs, L.h, w.GV);
-      hipLaunchKernelGGL(chol_kernel, dim3(1), dim3(256), 0, st, w.GV, bs, w.Lc);
+      gram_product(L, w, w.Vt, n, L.h, bs, w.GV, st);
+      cholesky(w, w.GV, bs, st);
       rw_product(L, w, w.Vt, L.h, bs, w.Yt, st);
-      hipLaunchKernelGGL(solve_kernel, dim3((m + 255) / 256), dim3(256), 0, st, w.Lc, bs, w.Yt, w.Ft, (long long)m);
+      solve(w, bs, w.Yt, w.Ft, m, st);
       select_rows(w.Ft, m, bs, L.tau, nullptr, 0, w.Ut, w.PHC, w.flags, 0, st);
       fl += 4.0 * m * n * bs;
     }
     // scales against Q = R H V of the last U-step, then the update and the outputs
-    hipLaunchKernelGGL(gram_kernel, dim3(bs), dim3(256), 0, st, w.Ut, m, bs, nullptr, w.GU);
-    hipLaunchKernelGGL(scales_kernel, dim3(1), dim3(256), 0, st, w.Ut, w.Yt, w.GU, w.GV, m, bs, k0, L.T, w.d,
-                       L.D, L.energy, w.st, w.flags, L.stats);
+    gram_product(L, w, w.Ut, m, nullptr, bs, w.GU, st);
+    hipLaunchKernelGGL(rowdot_kernel, dim3(bs), dim3(256), 0, st, w.Ut, w.Yt, m, w.Md);
+    hipLaunchKernelGGL(scales_kernel, dim3(1), dim3(256), 0, st, w.Md, w.GU, w.GV, bs, k0, L.T, w.d, L.D, L.energy,
+                       w.st, w.flags, L.stats);
     hipLaunchKernelGGL(update_kernel, dim3((n + 63) / 64, (m + 63) / 64), dim3(256), 0, st, L.R, L.ldr, m, n, w.Ut,
                        w.Vt, w.d, bs, w.flags);
     hipLaunchKernelGGL(emit_kernel, dim3(256), dim3(256), 0, st, w.Ut, w.Vt, m, n, bs, k0, L.Bp, L.Cp, w.flags);
