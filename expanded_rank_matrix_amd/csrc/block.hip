@@ -33,12 +33,14 @@ struct BlockWs {
   int8_t* Vt;      // b x n (also holds Omega for the sketch)
   double* Yt;      // b x m: sketch / (R H V)^T
   double* Ft;      // b x m: F^T
-  double* X;       // b x n: U^T R, then G
-  double* part;    // split-K partials
+  double* X;       // b x n: U^T R
+  double* Z;       // b x max(m, n): G (V-step target)
+  double* Tmp;     // b x max(m, n): L^-1 times the right-hand sides
+  double* part;    // split-K partials of the residual contractions
+  double* gpart;   // split-K partials of the Grams (side stream)
   double* GU;      // b x b
   double* GV;      // b x b
-  double* Lc;      // b x b Cholesky factor (lower triangle)
-  double* LT;      // its transpose
+  double* Li;      // b x b inverse Cholesky factor (lower triangular, zeros above)
   double* Md;      // b: u_c^T Q_c (diagonal of U^T R H V)
   double* PHC;     // b x 3 selection results
   float* d;        // b
@@ -47,57 +49,70 @@ struct BlockWs {
   int* used;       // m: rows used by sketch fallbacks within the block
 };
 
-constexpr int kMaxSplit = 8;
+constexpr int kMaxSplit = 8;       // split-K factor cap of the residual contractions
+constexpr int kMaxGramSplit = 64;  // ... and of the Grams
 
 static size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// One layout for both sizing and carving.
+template <typename F>
+static void ws_layout(int m, int n, int b, F&& take) {
+  const size_t mx = (size_t)(m > n ? m : n), bb = (size_t)b;
+  take((void**)nullptr, bb * m);  // Ut
+  take((void**)nullptr, bb * n);  // Vt
+  take((void**)nullptr, bb * m * 8);
+  take((void**)nullptr, bb * m * 8);
+  take((void**)nullptr, bb * n * 8);
+  take((void**)nullptr, bb * mx * 8);
+  take((void**)nullptr, bb * mx * 8);
+  take((void**)nullptr, (size_t)kMaxSplit * bb * mx * 8);
+  take((void**)nullptr, (size_t)kMaxGramSplit * bb * bb * 8);
+  take((void**)nullptr, bb * bb * 8);
+  take((void**)nullptr, bb * bb * 8);
+  take((void**)nullptr, bb * bb * 8);
+  take((void**)nullptr, bb * 8);
+  take((void**)nullptr, bb * 3 * 8);
+  take((void**)nullptr, bb * 4);
+  take((void**)nullptr, 64);
+  take((void**)nullptr, 64);
+  take((void**)nullptr, (size_t)m * 4);
+}
 
 static BlockWs carve(void* base, int m, int n, int b) {
   char* p = static_cast<char*>(base);
   size_t o = 0;
-  auto take = [&](size_t bytes) {
-    char* r = p + o;
+  void* ptrs[32];
+  int np = 0;
+  ws_layout(m, n, b, [&](void**, size_t bytes) {
+    ptrs[np++] = p + o;
     o = al(o + bytes);
-    return r;
-  };
+  });
   BlockWs w;
-  w.Ut = reinterpret_cast<int8_t*>(take((size_t)b * m));
-  w.Vt = reinterpret_cast<int8_t*>(take((size_t)b * n));
-  w.Yt = reinterpret_cast<double*>(take((size_t)b * m * 8));
-  w.Ft = reinterpret_cast<double*>(take((size_t)b * m * 8));
-  w.X = reinterpret_cast<double*>(take((size_t)b * n * 8));
-  w.part = reinterpret_cast<double*>(take((size_t)kMaxSplit * b * (m > n ? m : n) * 8));
-  w.GU = reinterpret_cast<double*>(take((size_t)b * b * 8));
-  w.GV = reinterpret_cast<double*>(take((size_t)b * b * 8));
-  w.Lc = reinterpret_cast<double*>(take((size_t)b * b * 8));
-  w.LT = reinterpret_cast<double*>(take((size_t)b * b * 8));
-  w.Md = reinterpret_cast<double*>(take((size_t)b * 8));
-  w.PHC = reinterpret_cast<double*>(take((size_t)b * 3 * 8));
-  w.d = reinterpret_cast<float*>(take((size_t)b * 4));
-  w.st = reinterpret_cast<double*>(take(64));
-  w.flags = reinterpret_cast<int*>(take(64));
-  w.used = reinterpret_cast<int*>(take((size_t)m * 4));
+  int q = 0;
+  w.Ut = static_cast<int8_t*>(ptrs[q++]);
+  w.Vt = static_cast<int8_t*>(ptrs[q++]);
+  w.Yt = static_cast<double*>(ptrs[q++]);
+  w.Ft = static_cast<double*>(ptrs[q++]);
+  w.X = static_cast<double*>(ptrs[q++]);
+  w.Z = static_cast<double*>(ptrs[q++]);
+  w.Tmp = static_cast<double*>(ptrs[q++]);
+  w.part = static_cast<double*>(ptrs[q++]);
+  w.gpart = static_cast<double*>(ptrs[q++]);
+  w.GU = static_cast<double*>(ptrs[q++]);
+  w.GV = static_cast<double*>(ptrs[q++]);
+  w.Li = static_cast<double*>(ptrs[q++]);
+  w.Md = static_cast<double*>(ptrs[q++]);
+  w.PHC = static_cast<double*>(ptrs[q++]);
+  w.d = static_cast<float*>(ptrs[q++]);
+  w.st = static_cast<double*>(ptrs[q++]);
+  w.flags = static_cast<int*>(ptrs[q++]);
+  w.used = static_cast<int*>(ptrs[q++]);
   return w;
 }
 
 size_t block_workspace_bytes(int m, int n, int b) {
   size_t o = 0;
-  auto take = [&](size_t bytes) { o = al(o + bytes); };
-  take((size_t)b * m);
-  take((size_t)b * n);
-  take((size_t)b * m * 8);
-  take((size_t)b * m * 8);
-  take((size_t)b * n * 8);
-  take((size_t)kMaxSplit * b * (m > n ? m : n) * 8);
-  take((size_t)b * b * 8);
-  take((size_t)b * b * 8);
-  take((size_t)b * b * 8);
-  take((size_t)b * b * 8);
-  take((size_t)b * 8);
-  take((size_t)b * 3 * 8);
-  take((size_t)b * 4);
-  take(64);
-  take(64);
-  take((size_t)m * 4);
+  ws_layout(m, n, b, [&](void**, size_t bytes) { o = al(o + bytes); });
   return o;
 }
 
@@ -249,16 +264,21 @@ __global__ void __launch_bounds__(256) reduce_splits_kernel(const double* part, 
   }
 }
 
-// ---- Cholesky of G + eps I, eps = 1e-6 trace(G) / bs, by one workgroup of NT threads.  The
-// lower triangle (packed, element e = i (i + 1) / 2 + k) is held in registers: slot q of thread t
-// holds element q * NT + t.  Right-looking order: after step j every entry (i, k), k > j, has had
-// L_ij L_kj subtracted, so each entry sees its subtractions in ascending t, as in the textbook
-// left-looking formula.  Writes L (row-major) and its transpose.
-constexpr int kCholSlots = 33;  // ceil(128 * 129 / 2 / 256) = ceil(256 * 257 / 2 / 1024) = 33
-template <int NT>
-__global__ void __launch_bounds__(NT) chol_kernel(const double* G, int bs, double* L, double* LT) {
+// ---- inverse Cholesky factor of G + eps I, eps = 1e-6 trace(G) / bs, by one workgroup of NT
+// threads.  The packed lower triangle (element e = i (i + 1) / 2 + k) lives in registers: slot q
+// of thread t holds element q * NT + t.
+//   1. Cholesky, right-looking: after step j every entry (i, k), k > j, has had L_ij L_kj
+//      subtracted, so each entry sees its subtractions in ascending order;
+//   2. X = L^-1 in place, right-looking: at step t row t of X is finished (divided by L_tt) and
+//      every later row i takes X_ik -= L_it X_tk for k <= t; entry (i, t) turns from L_it into
+//      X_it = -L_it X_tt at that step, just after its last use as an L entry.
+// Columns / rows broadcast through LDS are double-buffered by step parity, so two barriers per
+// step suffice.  Writes Li = L^-1 (row-major, zeros above the diagonal).
+template <int NT, int SLOTS>
+__global__ void __launch_bounds__(NT) chol_inv_kernel(const double* G, int bs, double* Li) {
 #pragma clang fp contract(off)
-  __shared__ double colb[2][256];  // column j in buffer j % 2 (no barrier needed between steps)
+  __shared__ double colb[2][256];
+  __shared__ double rowb[2][256];
   __shared__ double eps_s;
   const int tid = threadIdx.x;
   const int ne = bs * (bs + 1) / 2;
@@ -267,12 +287,16 @@ __global__ void __launch_bounds__(NT) chol_kernel(const double* G, int bs, doubl
     for (int c = 0; c < bs; ++c) tr += G[(size_t)c * bs + c];
     eps_s = 1e-6 * tr / (double)bs;
   }
+  for (int x = tid; x < bs * bs; x += NT) {
+    const int i = x / bs, k = x - i * bs;
+    if (k > i) Li[x] = 0.0;
+  }
   __syncthreads();
   const double eps = eps_s;
-  double a[kCholSlots];
-  int ik[kCholSlots];  // (i << 16) | k, or -1 for an unused slot
+  double a[SLOTS];
+  int ik[SLOTS];  // (i << 16) | k, or -1 for an unused slot
 #pragma unroll
-  for (int q = 0; q < kCholSlots; ++q) {
+  for (int q = 0; q < SLOTS; ++q) {
     const int e = q * NT + tid;
     if (e < ne) {
       int i = (int)((sqrt(8.0 * (double)e + 1.0) - 1.0) * 0.5);
@@ -286,10 +310,11 @@ __global__ void __launch_bounds__(NT) chol_kernel(const double* G, int bs, doubl
       a[q] = 0.0;
     }
   }
+  // 1. Cholesky
   for (int j = 0; j < bs; ++j) {
     double* col = colb[j & 1];
 #pragma unroll
-    for (int q = 0; q < kCholSlots; ++q)
+    for (int q = 0; q < SLOTS; ++q)
       if (ik[q] == ((j << 16) | j)) {
         a[q] = a[q] > 0.0 ? sqrt(a[q]) : 0.0;
         col[j] = a[q];
@@ -297,7 +322,7 @@ __global__ void __launch_bounds__(NT) chol_kernel(const double* G, int bs, doubl
     __syncthreads();
     const double ljj = col[j];
 #pragma unroll
-    for (int q = 0; q < kCholSlots; ++q) {
+    for (int q = 0; q < SLOTS; ++q) {
       const int i = ik[q] >> 16, k = ik[q] & 0xFFFF;
       if (ik[q] >= 0 && k == j && i > j) {
         a[q] = ljj > 0.0 ? a[q] / ljj : 0.0;
@@ -306,62 +331,80 @@ __global__ void __launch_bounds__(NT) chol_kernel(const double* G, int bs, doubl
     }
     __syncthreads();
 #pragma unroll
-    for (int q = 0; q < kCholSlots; ++q) {
+    for (int q = 0; q < SLOTS; ++q) {
       const int i = ik[q] >> 16, k = ik[q] & 0xFFFF;
       if (ik[q] >= 0 && k > j) a[q] -= col[i] * col[k];
     }
   }
+  __syncthreads();
+  // 2. X = L^-1
+  for (int t = 0; t < bs; ++t) {
+    double* lc = colb[t & 1];
+    double* xr = rowb[t & 1];
 #pragma unroll
-  for (int q = 0; q < kCholSlots; ++q)
+    for (int q = 0; q < SLOTS; ++q)
+      if (ik[q] == ((t << 16) | t)) lc[t] = a[q];  // L_tt
+    __syncthreads();
+    const double ltt = lc[t];
+#pragma unroll
+    for (int q = 0; q < SLOTS; ++q) {
+      if (ik[q] < 0) continue;
+      const int i = ik[q] >> 16, k = ik[q] & 0xFFFF;
+      if (i == t) {  // row t of X: finished
+        a[q] = ltt > 0.0 ? (k == t ? 1.0 : a[q]) / ltt : 0.0;
+        xr[k] = a[q];
+      } else if (k == t && i > t) {
+        lc[i] = a[q];  // L_it
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < SLOTS; ++q) {
+      if (ik[q] < 0) continue;
+      const int i = ik[q] >> 16, k = ik[q] & 0xFFFF;
+      if (i > t && k < t) a[q] -= lc[i] * xr[k];
+      else if (i > t && k == t) a[q] = 0.0 - lc[i] * xr[t];
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < SLOTS; ++q)
     if (ik[q] >= 0) {
       const int i = ik[q] >> 16, k = ik[q] & 0xFFFF;
-      L[(size_t)i * bs + k] = a[q];
-      LT[(size_t)k * bs + i] = a[q];
+      Li[(size_t)i * bs + k] = a[q];
     }
 }
 
-// ---- out[:, col] = (L L^T)^-1 in[:, col]: one column per lane, 64 columns per workgroup, the
-// column in LDS (bs x 64 doubles); L and L^T are read at workgroup-uniform addresses.  The inner
-// sums run in four interleaved partial sums.  in and out may alias.
-__global__ void __launch_bounds__(64) solve_kernel(const double* __restrict__ L, const double* __restrict__ LT,
-                                                   int bs, const double* in, double* out, int ncols) {
-  extern __shared__ double xs[];
-  const int lane = threadIdx.x;
-  const int col = blockIdx.x * 64 + lane;
-  const bool ok = col < ncols;
-  for (int i = 0; i < bs; ++i) xs[i * 64 + lane] = ok ? in[(size_t)i * ncols + col] : 0.0;
-  for (int i = 0; i < bs; ++i) {
-    const double* Li = L + (size_t)i * bs;
-    double p0 = 0.0, p1 = 0.0, p2 = 0.0, p3 = 0.0;
-    int t = 0;
-    for (; t + 4 <= i; t += 4) {
-      p0 += Li[t] * xs[t * 64 + lane];
-      p1 += Li[t + 1] * xs[(t + 1) * 64 + lane];
-      p2 += Li[t + 2] * xs[(t + 2) * 64 + lane];
-      p3 += Li[t + 3] * xs[(t + 3) * 64 + lane];
+// ---- out (bs x ncols) = op(A) B with A bs x bs (op: A or A^T), B bs x ncols, fp64 MFMA, K = bs.
+// Workgroup: 64 columns; wave w: columns 16 w .. 16 w + 15, all bs rows (NRT tiles of 16).
+template <int NRT, bool TA>
+__global__ void __launch_bounds__(256) apply_kernel(const double* __restrict__ A, int bs, const double* Bm,
+                                                    double* out, int ncols) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int col = blockIdx.x * 64 + wid * 16 + (lane & 15);
+  const bool okc = col < ncols;
+  dbl4 acc[NRT];
+#pragma unroll
+  for (int t = 0; t < NRT; ++t) acc[t] = (dbl4){0.0, 0.0, 0.0, 0.0};
+  for (int k0 = 0; k0 < bs; k0 += 4) {
+    const int k = k0 + (lane >> 4);
+    const double bv = (k < bs && okc) ? Bm[(size_t)k * ncols + col] : 0.0;
+#pragma unroll
+    for (int t = 0; t < NRT; ++t) {
+      const int r = t * 16 + (lane & 15);
+      double av = 0.0;
+      if (r < bs && k < bs) av = TA ? A[(size_t)k * bs + r] : A[(size_t)r * bs + k];
+      acc[t] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc[t], 0, 0, 0);
     }
-    for (; t < i; ++t) p0 += Li[t] * xs[t * 64 + lane];
-    const double s = xs[i * 64 + lane] - ((p0 + p1) + (p2 + p3));
-    const double lii = Li[i];
-    xs[i * 64 + lane] = lii > 0.0 ? s / lii : 0.0;
   }
-  for (int i = bs - 1; i >= 0; --i) {
-    const double* Ci = LT + (size_t)i * bs;  // column i of L
-    double p0 = 0.0, p1 = 0.0, p2 = 0.0, p3 = 0.0;
-    int t = i + 1;
-    for (; t + 4 <= bs; t += 4) {
-      p0 += Ci[t] * xs[t * 64 + lane];
-      p1 += Ci[t + 1] * xs[(t + 1) * 64 + lane];
-      p2 += Ci[t + 2] * xs[(t + 2) * 64 + lane];
-      p3 += Ci[t + 3] * xs[(t + 3) * 64 + lane];
-    }
-    for (; t < bs; ++t) p0 += Ci[t] * xs[t * 64 + lane];
-    const double s = xs[i * 64 + lane] - ((p0 + p1) + (p2 + p3));
-    const double lii = Ci[i];
-    xs[i * 64 + lane] = lii > 0.0 ? s / lii : 0.0;
+  if (okc) {
+#pragma unroll
+    for (int t = 0; t < NRT; ++t)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = t * 16 + (lane >> 4) + 4 * q;
+        if (r < bs) out[(size_t)r * ncols + col] = acc[t][q];
+      }
   }
-  if (ok)
-    for (int i = 0; i < bs; ++i) out[(size_t)i * ncols + col] = xs[i * 64 + lane];
 }
 
 // ---- Md[c] = sum_i U[c][i] Y[c][i] (one workgroup per component, fixed reduction order)
@@ -688,12 +731,9 @@ static void rw_product(const BlockLaunch& L, const BlockWs& w, const int8_t* T, 
 }
 
 // G (bs x bs) = T diag(w) T^T for ternary rows T (bs x len); integer-exact without weights
-static void gram_product(const BlockLaunch& L, const BlockWs& w, const int8_t* T, int len, const float* wt, int bs,
-                         double* G, hipStream_t st) {
-  const int mx = L.m > L.n ? L.m : L.n;
-  long long cap = (long long)kMaxSplit * mx / bs;  // partials must fit the split buffer
-  cap = cap > 64 ? 64 : cap;
-  rw_contract<int8_t>(T, len, bs, len, T, wt, bs, (int)cap, w.part, G, st);
+static void gram_product(const BlockWs& w, const int8_t* T, int len, const float* wt, int bs, double* G,
+                         hipStream_t st) {
+  rw_contract<int8_t>(T, len, bs, len, T, wt, bs, kMaxGramSplit, w.gpart, G, st);
 }
 
 // X (bs x n) = U^T R
@@ -708,18 +748,40 @@ static void utr_product(const BlockLaunch& L, const BlockWs& w, int bs, hipStrea
   reduce_splits(w.part, ns, (long long)bs * L.n, w.X, st);
 }
 
-// Cholesky of G + eps I into w.Lc / w.LT
-static void cholesky(const BlockWs& w, const double* G, int bs, hipStream_t st) {
-  if (bs <= 128)
-    hipLaunchKernelGGL(chol_kernel<256>, dim3(1), dim3(256), 0, st, G, bs, w.Lc, w.LT);
+// Li = L^-1 for L L^T = G + eps I
+static void chol_inverse(const BlockWs& w, const double* G, int bs, hipStream_t st) {
+  const int ne = bs * (bs + 1) / 2;
+  if (ne <= 256 * 2)
+    hipLaunchKernelGGL((chol_inv_kernel<256, 2>), dim3(1), dim3(256), 0, st, G, bs, w.Li);
+  else if (ne <= 256 * 5)
+    hipLaunchKernelGGL((chol_inv_kernel<256, 5>), dim3(1), dim3(256), 0, st, G, bs, w.Li);
+  else if (ne <= 256 * 9)
+    hipLaunchKernelGGL((chol_inv_kernel<256, 9>), dim3(1), dim3(256), 0, st, G, bs, w.Li);
+  else if (ne <= 1024 * 5)
+    hipLaunchKernelGGL((chol_inv_kernel<1024, 5>), dim3(1), dim3(1024), 0, st, G, bs, w.Li);
+  else if (ne <= 1024 * 9)
+    hipLaunchKernelGGL((chol_inv_kernel<1024, 9>), dim3(1), dim3(1024), 0, st, G, bs, w.Li);
+  else if (ne <= 1024 * 17)
+    hipLaunchKernelGGL((chol_inv_kernel<1024, 17>), dim3(1), dim3(1024), 0, st, G, bs, w.Li);
   else
-    hipLaunchKernelGGL(chol_kernel<1024>, dim3(1), dim3(1024), 0, st, G, bs, w.Lc, w.LT);
+    hipLaunchKernelGGL((chol_inv_kernel<1024, 33>), dim3(1), dim3(1024), 0, st, G, bs, w.Li);
 }
 
-// out (bs x ncols) = (L L^T)^-1 in
+template <bool TA>
+static void apply(const double* A, int bs, const double* Bm, double* out, int ncols, hipStream_t st) {
+  const dim3 grid((ncols + 63) / 64);
+  const int nrt = (bs + 15) / 16;
+  if (nrt <= 1) hipLaunchKernelGGL((apply_kernel<1, TA>), grid, dim3(256), 0, st, A, bs, Bm, out, ncols);
+  else if (nrt <= 2) hipLaunchKernelGGL((apply_kernel<2, TA>), grid, dim3(256), 0, st, A, bs, Bm, out, ncols);
+  else if (nrt <= 4) hipLaunchKernelGGL((apply_kernel<4, TA>), grid, dim3(256), 0, st, A, bs, Bm, out, ncols);
+  else if (nrt <= 8) hipLaunchKernelGGL((apply_kernel<8, TA>), grid, dim3(256), 0, st, A, bs, Bm, out, ncols);
+  else hipLaunchKernelGGL((apply_kernel<16, TA>), grid, dim3(256), 0, st, A, bs, Bm, out, ncols);
+}
+
+// out (bs x ncols) = (G + eps I)^-1 in = L^-T (L^-1 in); in and out may not alias
 static void solve(const BlockWs& w, int bs, const double* in, double* out, int ncols, hipStream_t st) {
-  const size_t smem = (size_t)bs * 64 * sizeof(double);
-  hipLaunchKernelGGL(solve_kernel, dim3((ncols + 63) / 64), dim3(64), smem, st, w.Lc, w.LT, bs, in, out, ncols);
+  apply<false>(w.Li, bs, in, w.Tmp, ncols, st);
+  apply<true>(w.Li, bs, w.Tmp, out, ncols, st);
 }
 
 static void select_rows(const double* X, int L, int bs, float tau, const float* h, int EHm, int8_t* T, double* PHC,
@@ -732,15 +794,47 @@ static void select_rows(const double* X, int L, int bs, float tau, const float* 
                        flag_empty);
 }
 
+// Side stream for the Gram and inverse-factor work, which overlaps the residual contraction of
+// the same half-step (both depend only on the ternary factor just selected).  Created once per
+// device at the default priority.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+
+static hipError_t side_stream(SideStream** out) {
+  static SideStream per_dev[64];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  SideStream& ss = per_dev[dev];
+  if (!ss.s) {
+    if ((e = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming)) != hipSuccess) return e;
+    if ((e = hipEventCreateWithFlags(&ss.join, hipEventDisableTiming)) != hipSuccess) return e;
+  }
+  *out = &ss;
+  return hipSuccess;
+}
+
 hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops) {
   if (L.b > 256) return hipErrorInvalidValue;
   const BlockWs w = carve(L.ws, L.m, L.n, L.b);
   const int m = L.m, n = L.n;
-  {
-    const hipError_t e = hipFuncSetAttribute((const void*)solve_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             (int)((size_t)L.b * 64 * sizeof(double)));
-    if (e != hipSuccess) return e;
-  }
+  SideStream* ss = nullptr;
+  hipError_t e = side_stream(&ss);
+  if (e != hipSuccess) return e;
+  // G and its inverse factor on the side stream, after everything queued so far on st
+  auto gram_inverse = [&](const int8_t* T, int len, const float* wt, int bs, double* G) -> hipError_t {
+    hipError_t r;
+    if ((r = hipEventRecord(ss->fork, st)) != hipSuccess) return r;
+    if ((r = hipStreamWaitEvent(ss->s, ss->fork, 0)) != hipSuccess) return r;
+    gram_product(w, T, len, wt, bs, G, ss->s);
+    chol_inverse(w, G, bs, ss->s);
+    return hipEventRecord(ss->join, ss->s);
+  };
+  auto join = [&]() -> hipError_t { return hipStreamWaitEvent(st, ss->join, 0); };
   hipLaunchKernelGGL(block_init_kernel, dim3(1), dim3(256), 0, st, L.rowE, m, w.st, w.flags);
   const int nblocks = (L.k + L.b - 1) / L.b;
   double fl = 0.0;
@@ -757,21 +851,21 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops) {
     fl += 2.0 * m * n * bs;
     for (int t = 0; t < L.T; ++t) {
       // V-step: G = (U^T U + eps I)^-1 U^T R, rows ternarized with weights h
-      gram_product(L, w, w.Ut, m, nullptr, bs, w.GU, st);
-      cholesky(w, w.GU, bs, st);
+      if ((e = gram_inverse(w.Ut, m, nullptr, bs, w.GU)) != hipSuccess) return e;
       utr_product(L, w, bs, st);
-      solve(w, bs, w.X, w.X, n, st);
-      select_rows(w.X, n, bs, L.tau, L.h, L.EHm, w.Vt, w.PHC, w.flags, 0, st);
+      if ((e = join()) != hipSuccess) return e;
+      solve(w, bs, w.X, w.Z, n, st);
+      select_rows(w.Z, n, bs, L.tau, L.h, L.EHm, w.Vt, w.PHC, w.flags, 0, st);
       // U-step: F^T = (V^T H V + eps I)^-1 (R H V)^T, columns ternarized without weights
-      gram_product(L, w, w.Vt, n, L.h, bs, w.GV, st);
-      cholesky(w, w.GV, bs, st);
+      if ((e = gram_inverse(w.Vt, n, L.h, bs, w.GV)) != hipSuccess) return e;
       rw_product(L, w, w.Vt, L.h, bs, w.Yt, st);
+      if ((e = join()) != hipSuccess) return e;
       solve(w, bs, w.Yt, w.Ft, m, st);
       select_rows(w.Ft, m, bs, L.tau, nullptr, 0, w.Ut, w.PHC, w.flags, 0, st);
       fl += 4.0 * m * n * bs;
     }
     // scales against Q = R H V of the last U-step, then the update and the outputs
-    gram_product(L, w, w.Ut, m, nullptr, bs, w.GU, st);
+    gram_product(w, w.Ut, m, nullptr, bs, w.GU, st);
     hipLaunchKernelGGL(rowdot_kernel, dim3(bs), dim3(256), 0, st, w.Ut, w.Yt, m, w.Md);
     hipLaunchKernelGGL(scales_kernel, dim3(1), dim3(256), 0, st, w.Md, w.GU, w.GV, bs, k0, L.T, w.d, L.D, L.energy,
                        w.st, w.flags, L.stats);
@@ -779,8 +873,7 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops) {
                        w.Vt, w.d, bs, w.flags);
     hipLaunchKernelGGL(emit_kernel, dim3(256), dim3(256), 0, st, w.Ut, w.Vt, m, n, bs, k0, L.Bp, L.Cp, w.flags);
     fl += 2.0 * m * n * bs;
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   *flops = fl;
   return hipGetLastError();
