@@ -29,8 +29,9 @@ namespace externd {
 typedef double dbl4 __attribute__((ext_vector_type(4)));
 
 struct BlockWs {
-  int8_t* Ut;      // b x m, component-major
-  int8_t* Vt;      // b x n (also holds Omega for the sketch)
+  int ldu, ldv;    // row lengths of Ut / Vt: m and n rounded up to 16 (zero padding)
+  int8_t* Ut;      // b x ldu, component-major
+  int8_t* Vt;      // b x ldv (also holds Omega for the sketch)
   double* Yt;      // b x m: sketch / (R H V)^T
   double* Ft;      // b x m: F^T
   double* X;       // b x n: U^T R
@@ -58,8 +59,8 @@ static size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
 template <typename F>
 static void ws_layout(int m, int n, int b, F&& take) {
   const size_t mx = (size_t)(m > n ? m : n), bb = (size_t)b;
-  take((void**)nullptr, bb * m);  // Ut
-  take((void**)nullptr, bb * n);  // Vt
+  take((void**)nullptr, bb * (size_t)((m + 15) & ~15));  // Ut
+  take((void**)nullptr, bb * (size_t)((n + 15) & ~15));  // Vt
   take((void**)nullptr, bb * m * 8);
   take((void**)nullptr, bb * m * 8);
   take((void**)nullptr, bb * n * 8);
@@ -88,6 +89,8 @@ static BlockWs carve(void* base, int m, int n, int b) {
     o = al(o + bytes);
   });
   BlockWs w;
+  w.ldu = (m + 15) & ~15;
+  w.ldv = (n + 15) & ~15;
   int q = 0;
   w.Ut = static_cast<int8_t*>(ptrs[q++]);
   w.Vt = static_cast<int8_t*>(ptrs[q++]);
@@ -124,16 +127,16 @@ __device__ __forceinline__ u64 splitmix64(u64 key) {
   return z ^ (z >> 31);
 }
 
-__global__ void __launch_bounds__(256) omega_kernel(int8_t* Vt, int bs, int n, long long s, int* flags) {
+__global__ void __launch_bounds__(256) omega_kernel(int8_t* Vt, int ldv, int bs, int n, long long s, int* flags) {
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     flags[1] = 0;  // empty sketch columns of this block
     flags[2] = 0;  // fallback starts of this block
   }
-  const long long total = (long long)bs * n;
+  const long long total = (long long)bs * ldv;
   for (long long x = blockIdx.x * 256ll + threadIdx.x; x < total; x += (long long)gridDim.x * 256) {
-    const int c = (int)(x / n), j = (int)(x - (long long)c * n);
-    int8_t v = 1;
-    if (c > 0) {
+    const int c = (int)(x / ldv), j = (int)(x - (long long)c * ldv);
+    int8_t v = j < n ? (int8_t)1 : (int8_t)0;
+    if (c > 0 && j < n) {
       const u64 key = (((u64)s << 16) + (u64)c) * (1ull << 32) + (u64)j;
       v = (splitmix64(key) >> 63) ? (int8_t)-1 : (int8_t)1;
     }
@@ -141,115 +144,171 @@ __global__ void __launch_bounds__(256) omega_kernel(int8_t* Vt, int bs, int n, l
   }
 }
 
-// ---- contraction 1: part[split][c][i] = sum_{j in split} R[i][j] * h_j * T[c][j] ------------
-// MFMA f64 16x16x4: D(16x16) += A(16x4) B(4x16).  Lane l: A[l%16][l/16], B[l/16][l%16];
-// D(i, j) in lane j + 16 (i % 4), register i / 4 (rows interleaved, unlike the fp32 forms).
-// Tile: 64 rows of R (one 16-row strip per wave) x all components (NCT tiles of 16); K chunks
-// of 32 columns staged in LDS.
+// ---- residual contractions on v_mfma_f64_16x16x4f64: D(16x16) += A(16x4) B(4x16).
+// Lane l supplies A[l % 16][l / 16] and B[l / 16][l % 16]; D(i, j) lands in lane j + 16 (i % 4),
+// register i / 4.  The k order inside a group of 16 is permuted so that lane (r, kq) covers
+// k = g + 4 kq + s at step s = 0..3: one 16-byte load then feeds four MFMA steps.  Operands are
+// loaded straight into registers (no LDS), one group ahead.
+
+// part[split][c][i] = sum_{k in split} R[i][k] * h_k * T[c][k]   (rows of R x components)
+// Workgroup: 64 rows of R (16 per wave) x all components (NCT tiles of 16).
 template <int NCT, typename TR>
-__global__ void __launch_bounds__(256) contract_rw_kernel(const TR* R, int ldr, int m, int n, const int8_t* T,
-                                                          const float* h, int bs, int kspan, double* part) {
-  constexpr int KC = 32;
-  __shared__ float Rs[64][KC + 1];
-  __shared__ int8_t Ts[16 * NCT][KC + 4];
-  __shared__ float hs[KC];
+__global__ void __launch_bounds__(256) contract_rw_kernel(const TR* R, int ldr, int rows, int K, const int8_t* T,
+                                                          int ldt, const float* h, int bs, int kspan,
+                                                          double* part) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int i0 = blockIdx.x * 64;
-  const int split = blockIdx.y;
-  const int kb = split * kspan, ke = (kb + kspan < n) ? kb + kspan : n;
+  const int row = blockIdx.x * 64 + wid * 16 + (lane & 15);
+  const int kq = lane >> 4;
+  const int kb = blockIdx.y * kspan, ke = (kb + kspan < K) ? kb + kspan : K;
+  const bool rok = row < rows;
+  const TR* rp = R + (size_t)(rok ? row : 0) * ldr;
+  const int8_t* tp[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    const int c = ct * 16 + (lane & 15);
+    tp[ct] = T + (size_t)(c < bs ? c : 0) * ldt;
+  }
   dbl4 acc[NCT];
 #pragma unroll
-  for (int c = 0; c < NCT; ++c) acc[c] = (dbl4){0.0, 0.0, 0.0, 0.0};
-  for (int k0 = kb; k0 < ke; k0 += KC) {
-    // stage R[i0 .. i0+63][k0 .. k0+31] (zero outside)
-    for (int x = tid; x < 64 * KC; x += 256) {
-      const int r = x / KC, c = x % KC;
-      const int i = i0 + r, j = k0 + c;
-      Rs[r][c] = (i < m && j < ke) ? (float)R[(size_t)i * ldr + j] : 0.0f;
-    }
-    for (int x = tid; x < 16 * NCT * KC; x += 256) {
-      const int cc = x / KC, c = x % KC;
-      const int j = k0 + c;
-      Ts[cc][c] = (cc < bs && j < ke) ? T[(size_t)cc * n + j] : (int8_t)0;
-    }
-    if (tid < KC) {
-      const int j = k0 + tid;
-      hs[tid] = (j < ke) ? (h ? h[j] : 1.0f) : 0.0f;
-    }
-    __syncthreads();
+  for (int ct = 0; ct < NCT; ++ct) acc[ct] = (dbl4){0.0, 0.0, 0.0, 0.0};
+  auto load = [&](int g, float (&av)[4], unsigned (&tv)[NCT], float (&hv)[4]) {
+    const int k = g + 4 * kq;
+    const bool full = k + 4 <= ke;
 #pragma unroll
-    for (int kk = 0; kk < KC; kk += 4) {
-      const int kq = kk + (lane >> 4);
-      const double a = (double)Rs[wid * 16 + (lane & 15)][kq];
-      const float hw = hs[kq];
+    for (int q = 0; q < 4; ++q) av[q] = 0.0f;
+    if (rok) {
+      if (sizeof(TR) == 4 && full) {
+        const float4 v = *reinterpret_cast<const float4*>(rp + k);
+        av[0] = v.x;
+        av[1] = v.y;
+        av[2] = v.z;
+        av[3] = v.w;
+      } else if (sizeof(TR) == 1 && full) {
+        const unsigned v = *reinterpret_cast<const unsigned*>(rp + k);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) av[q] = (float)(int8_t)(v >> (8 * q));
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) av[q] = k + q < ke ? (float)rp[k + q] : 0.0f;
+      }
+    }
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const int c = ct * 16 + (lane & 15);
+      unsigned v = 0u;
+      if (c < bs && k < ke) {
+        v = *reinterpret_cast<const unsigned*>(tp[ct] + k);  // rows are zero-padded to 16
+        if (!full) v &= 0xFFFFFFFFu >> (8 * (k + 4 - ke));
+      }
+      tv[ct] = v;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) hv[q] = h ? (k + q < ke ? h[k + q] : 0.0f) : 1.0f;
+  };
+  float av[4], hv[4];
+  unsigned tv[NCT];
+  if (kb < ke) load(kb, av, tv, hv);
+  for (int g = kb; g < ke; g += 16) {
+    float av2[4], hv2[4];
+    unsigned tv2[NCT];
+    const bool more = g + 16 < ke;
+    if (more) load(g + 16, av2, tv2, hv2);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const double a = (double)av[q];
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
-        const double bv = (double)(hw * (float)Ts[ct * 16 + (lane & 15)][kq]);
+        const double bv = (double)(hv[q] * (float)(int8_t)(tv[ct] >> (8 * q)));
         acc[ct] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, bv, acc[ct], 0, 0, 0);
       }
     }
-    __syncthreads();
+    if (more) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        av[q] = av2[q];
+        hv[q] = hv2[q];
+      }
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) tv[ct] = tv2[ct];
+    }
   }
-  double* out = part + (size_t)split * bs * m;
+  double* out = part + (size_t)blockIdx.y * bs * rows;
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) {
     const int c = ct * 16 + (lane & 15);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int i = i0 + wid * 16 + (lane >> 4) + 4 * r;
-      if (c < bs && i < m) out[(size_t)c * m + i] = acc[ct][r];
+      const int i = blockIdx.x * 64 + wid * 16 + (lane >> 4) + 4 * r;
+      if (c < bs && i < rows) out[(size_t)c * rows + i] = acc[ct][r];
     }
   }
 }
 
-// ---- contraction 2: part[split][c][j] = sum_{i in split} U[c][i] * R[i][j] ----------------
-// D rows = components (16 per tile), columns = j.  A[c][k] = U[c][i0+k], B[k][j] = R[i0+k][j].
-// Tile: all components x 64 columns (one 16-column strip per wave); K chunks of 32 rows.
+// part[split][c][j] = sum_{i in split} U[c][i] * R[i][j]   (components x columns of R)
+// Workgroup: all components (NCT tiles of 16) x 64 columns (16 per wave).
 template <int NCT>
 __global__ void __launch_bounds__(256) contract_utr_kernel(const float* R, int ldr, int m, int n, const int8_t* U,
-                                                           int bs, int kspan, double* part) {
-  constexpr int KC = 32;
-  __shared__ float Rs[KC][64 + 1];
-  __shared__ int8_t Us[16 * NCT][KC + 4];
+                                                           int ldu, int bs, int kspan, double* part) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int j0 = blockIdx.x * 64;
-  const int split = blockIdx.y;
-  const int kb = split * kspan, ke = (kb + kspan < m) ? kb + kspan : m;
-  dbl4 acc[NCT];
-#pragma unroll
-  for (int c = 0; c < NCT; ++c) acc[c] = (dbl4){0.0, 0.0, 0.0, 0.0};
-  for (int k0 = kb; k0 < ke; k0 += KC) {
-    for (int x = tid; x < KC * 64; x += 256) {
-      const int r = x / 64, c = x % 64;
-      const int i = k0 + r, j = j0 + c;
-      Rs[r][c] = (i < ke && j < n) ? R[(size_t)i * ldr + j] : 0.0f;
-    }
-    for (int x = tid; x < 16 * NCT * KC; x += 256) {
-      const int cc = x / KC, r = x % KC;
-      const int i = k0 + r;
-      Us[cc][r] = (cc < bs && i < ke) ? U[(size_t)cc * m + i] : (int8_t)0;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < KC; kk += 4) {
-      const int kq = kk + (lane >> 4);
-      const double bv = (double)Rs[kq][wid * 16 + (lane & 15)];
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        const double a = (double)Us[ct * 16 + (lane & 15)][kq];
-        acc[ct] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, bv, acc[ct], 0, 0, 0);
-      }
-    }
-    __syncthreads();
-  }
-  double* out = part + (size_t)split * bs * n;
+  const int j = blockIdx.x * 64 + wid * 16 + (lane & 15);
+  const int kq = lane >> 4;
+  const int kb = blockIdx.y * kspan, ke = (kb + kspan < m) ? kb + kspan : m;
+  const bool jok = j < n;
+  const int8_t* up[NCT];
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) {
-    const int j = j0 + wid * 16 + (lane & 15);
+    const int c = ct * 16 + (lane & 15);
+    up[ct] = U + (size_t)(c < bs ? c : 0) * ldu;
+  }
+  dbl4 acc[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) acc[ct] = (dbl4){0.0, 0.0, 0.0, 0.0};
+  auto load = [&](int g, float (&bv)[4], unsigned (&uv)[NCT]) {
+    const int i = g + 4 * kq;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) bv[q] = (jok && i + q < ke) ? R[(size_t)(i + q) * ldr + j] : 0.0f;
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const int c = ct * 16 + (lane & 15);
+      unsigned v = 0u;
+      if (c < bs && i < ke) {
+        v = *reinterpret_cast<const unsigned*>(up[ct] + i);
+        if (i + 4 > ke) v &= 0xFFFFFFFFu >> (8 * (i + 4 - ke));
+      }
+      uv[ct] = v;
+    }
+  };
+  float bv[4];
+  unsigned uv[NCT];
+  if (kb < ke) load(kb, bv, uv);
+  for (int g = kb; g < ke; g += 16) {
+    float bv2[4];
+    unsigned uv2[NCT];
+    const bool more = g + 16 < ke;
+    if (more) load(g + 16, bv2, uv2);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const double b = (double)bv[q];
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        const double a = (double)(int8_t)(uv[ct] >> (8 * q));
+        acc[ct] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, acc[ct], 0, 0, 0);
+      }
+    }
+    if (more) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) bv[q] = bv2[q];
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) uv[ct] = uv2[ct];
+    }
+  }
+  double* out = part + (size_t)blockIdx.y * bs * n;
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int c = ct * 16 + (lane >> 4) + 4 * r;
-      if (c < bs && j < n) out[(size_t)c * n + j] = acc[ct][r];
+      if (c < bs && jok) out[(size_t)c * n + j] = acc[ct][r];
     }
   }
 }
@@ -268,7 +327,8 @@ __global__ void __launch_bounds__(256) reduce_splits_kernel(const double* part, 
 // threads.  The packed lower triangle (element e = i (i + 1) / 2 + k) lives in registers: slot q
 // of thread t holds element q * NT + t.
 //   1. Cholesky, right-looking: after step j every entry (i, k), k > j, has had L_ij L_kj
-//      subtracted, so each entry sees its subtractions in ascending order;
+//      subtracted, so each entry sees its subtractions in ascending order (the column is scaled
+//      by the reciprocal of the pivot: one division per step);
 //   2. X = L^-1 in place, right-looking: at step t row t of X is finished (divided by L_tt) and
 //      every later row i takes X_ik -= L_it X_tk for k <= t; entry (i, t) turns from L_it into
 //      X_it = -L_it X_tt at that step, just after its last use as an L entry.
@@ -321,11 +381,12 @@ __global__ void __launch_bounds__(NT) chol_inv_kernel(const double* G, int bs, d
       }
     __syncthreads();
     const double ljj = col[j];
+    const double rj = ljj > 0.0 ? 1.0 / ljj : 0.0;  // one division per step, then products
 #pragma unroll
     for (int q = 0; q < SLOTS; ++q) {
       const int i = ik[q] >> 16, k = ik[q] & 0xFFFF;
       if (ik[q] >= 0 && k == j && i > j) {
-        a[q] = ljj > 0.0 ? a[q] / ljj : 0.0;
+        a[q] = a[q] * rj;
         col[i] = a[q];
       }
     }
@@ -346,12 +407,13 @@ __global__ void __launch_bounds__(NT) chol_inv_kernel(const double* G, int bs, d
       if (ik[q] == ((t << 16) | t)) lc[t] = a[q];  // L_tt
     __syncthreads();
     const double ltt = lc[t];
+    const double rt = ltt > 0.0 ? 1.0 / ltt : 0.0;
 #pragma unroll
     for (int q = 0; q < SLOTS; ++q) {
       if (ik[q] < 0) continue;
       const int i = ik[q] >> 16, k = ik[q] & 0xFFFF;
       if (i == t) {  // row t of X: finished
-        a[q] = ltt > 0.0 ? (k == t ? 1.0 : a[q]) / ltt : 0.0;
+        a[q] = k == t ? rt : a[q] * rt;
         xr[k] = a[q];
       } else if (k == t && i > t) {
         lc[i] = a[q];  // L_it
@@ -408,12 +470,12 @@ __global__ void __launch_bounds__(256) apply_kernel(const double* __restrict__ A
 }
 
 // ---- Md[c] = sum_i U[c][i] Y[c][i] (one workgroup per component, fixed reduction order)
-__global__ void __launch_bounds__(256) rowdot_kernel(const int8_t* Ut, const double* Yt, int m, double* Md) {
+__global__ void __launch_bounds__(256) rowdot_kernel(const int8_t* Ut, int ldu, const double* Yt, int m, double* Md) {
   __shared__ double red[4];
   const int c = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   double acc = 0.0;
   for (int i = tid; i < m; i += 256) {
-    const int u = Ut[(size_t)c * m + i];
+    const int u = Ut[(size_t)c * ldu + i];
     if (u) acc += (double)u * Yt[(size_t)c * m + i];
   }
   acc = wave_sum_f64(acc);
@@ -424,20 +486,20 @@ __global__ void __launch_bounds__(256) rowdot_kernel(const int8_t* Ut, const dou
 
 // ---- one workgroup per component row: T[c] = T_tau(fp32(X[c]); h) -----------------------------
 template <bool W>
-__global__ void __launch_bounds__(512) select_rows_kernel(const double* X, int L, float tau, const float* h,
-                                                          int EHm, int8_t* T, double* PHC, int* flags,
-                                                          int flag_empty) {
+__global__ void __launch_bounds__(512) select_rows_kernel(const double* X, int L, int ldT, float tau,
+                                                          const float* h, int EHm, int8_t* T, double* PHC,
+                                                          int* flags, int flag_empty) {
   __shared__ SelScratch s;
   const int c = blockIdx.x;
   const double* x = X + (size_t)c * L;
   if (flags[0]) {  // residual is zero: nothing to select
-    for (int j = threadIdx.x; j < L; j += 512) T[(size_t)c * L + j] = 0;
+    for (int j = threadIdx.x; j < ldT; j += 512) T[(size_t)c * ldT + j] = 0;
     return;
   }
   const SelResult r = ternary_select<512, W>(x, h, L, tau, EHm, s);
-  for (int j = threadIdx.x; j < L; j += 512) {
-    const float xv = (float)x[j];
-    T[(size_t)c * L + j] = selected(xv, r) ? (xv > 0.0f ? (int8_t)1 : (int8_t)-1) : (int8_t)0;
+  for (int j = threadIdx.x; j < ldT; j += 512) {  // the padding [L, ldT) stays zero
+    const float xv = j < L ? (float)x[j] : 0.0f;
+    T[(size_t)c * ldT + j] = selected(xv, r) ? (xv > 0.0f ? (int8_t)1 : (int8_t)-1) : (int8_t)0;
   }
   if (threadIdx.x == 0) {
     PHC[3 * c + 0] = r.P;
@@ -451,7 +513,7 @@ __global__ void __launch_bounds__(512) select_rows_kernel(const double* X, int L
 // on ties) in a row not used yet by this block; one workgroup, and it only does work when such a
 // column exists (the sketch of a nonzero residual is almost never empty) ----
 __global__ void __launch_bounds__(512) fallback_kernel(const float* R, int ldr, int m, int n, int bs, int8_t* Ut,
-                                                       const double* PHC, int* flags, int* used) {
+                                                       int ldu, const double* PHC, int* flags, int* used) {
   __shared__ float bv[8];
   __shared__ long long bi[8];
   if (flags[1] == 0 || flags[0]) return;
@@ -495,7 +557,7 @@ __global__ void __launch_bounds__(512) fallback_kernel(const float* R, int ldr, 
       }
     if (bb > 0.0f) {  // else every row holding a nonzero entry is taken: the column stays empty
       const int r = (int)(bix / n);
-      for (int i = tid; i < m; i += 512) Ut[(size_t)c * m + i] = (i == r) ? (int8_t)1 : (int8_t)0;
+      for (int i = tid; i < m; i += 512) Ut[(size_t)c * ldu + i] = (i == r) ? (int8_t)1 : (int8_t)0;
       if (tid == 0) {
         used[r] = 1;
         flags[2] += 1;
@@ -575,8 +637,9 @@ __global__ void __launch_bounds__(256) scales_kernel(const double* Md, const dou
 // ---- update: R <- fl32(R - U diag(d) V^T), fp64 MFMA with K = bs ----------------------------
 // Tile 64 x 64 of R; wave w owns rows 16w..16w+15 and four 16-column strips.
 // A[i][k] = d_k U[k][i], B[k][j] = V[k][j].
-__global__ void __launch_bounds__(256) update_kernel(float* R, int ldr, int m, int n, const int8_t* Ut,
-                                                     const int8_t* Vt, const float* dvec, int bs, const int* flags) {
+__global__ void __launch_bounds__(256) update_kernel(float* R, int ldr, int m, int n, const int8_t* Ut, int ldu,
+                                                     const int8_t* Vt, int ldv, const float* dvec, int bs,
+                                                     const int* flags) {
   if (flags[0]) return;
   __shared__ int8_t Us[256][64 + 4];
   __shared__ int8_t Vs[256][64 + 4];
@@ -586,8 +649,8 @@ __global__ void __launch_bounds__(256) update_kernel(float* R, int ldr, int m, i
   const int bs4 = (bs + 3) & ~3;
   for (int x = tid; x < bs4 * 64; x += 256) {
     const int c = x / 64, r = x % 64;
-    Us[c][r] = (c < bs && i0 + r < m) ? Ut[(size_t)c * m + i0 + r] : (int8_t)0;
-    Vs[c][r] = (c < bs && j0 + r < n) ? Vt[(size_t)c * n + j0 + r] : (int8_t)0;
+    Us[c][r] = (c < bs && i0 + r < m) ? Ut[(size_t)c * ldu + i0 + r] : (int8_t)0;
+    Vs[c][r] = (c < bs && j0 + r < n) ? Vt[(size_t)c * ldv + j0 + r] : (int8_t)0;
   }
   for (int c = tid; c < bs4; c += 256) ds[c] = c < bs ? dvec[c] : 0.0f;
   __syncthreads();
@@ -619,8 +682,8 @@ __global__ void __launch_bounds__(256) update_kernel(float* R, int ldr, int m, i
 }
 
 // ---- emit: pack the block's components into B and C rows ----------------------------------
-__global__ void __launch_bounds__(256) emit_kernel(const int8_t* Ut, const int8_t* Vt, int m, int n, int bs, int k0,
-                                                   uint32_t* Bp, uint32_t* Cp, const int* flags) {
+__global__ void __launch_bounds__(256) emit_kernel(const int8_t* Ut, int ldu, const int8_t* Vt, int ldv, int m, int n,
+                                                   int bs, int k0, uint32_t* Bp, uint32_t* Cp, const int* flags) {
   const int wm = (m + 15) / 16, wn = (n + 15) / 16;
   const bool dead = flags[0] != 0;
   const long long totB = (long long)bs * wm, totC = (long long)bs * wn;
@@ -629,7 +692,7 @@ __global__ void __launch_bounds__(256) emit_kernel(const int8_t* Ut, const int8_
     const long long y = isB ? x : x - totB;
     const int words = isB ? wm : wn, len = isB ? m : n;
     const int c = (int)(y / words), w = (int)(y - (long long)c * words);
-    const int8_t* src = isB ? Ut + (size_t)c * m : Vt + (size_t)c * n;
+    const int8_t* src = isB ? Ut + (size_t)c * ldu : Vt + (size_t)c * ldv;
     unsigned word = 0u;
     if (!dead)
       for (int q = 0; q < 16; ++q) {
@@ -680,19 +743,19 @@ __global__ void __launch_bounds__(256) zero_check_kernel(const float* R, int ldr
 }
 
 template <int NCT, typename TR>
-static void launch_rw(const TR* R, int ldr, int m, int n, const int8_t* T, const float* h, int bs, int nsplit,
-                      double* part, hipStream_t st) {
-  const int kspan = ((n + nsplit - 1) / nsplit + 31) / 32 * 32;
-  hipLaunchKernelGGL((contract_rw_kernel<NCT, TR>), dim3((m + 63) / 64, nsplit), dim3(256), 0, st, R, ldr, m, n,
-                     T, h, bs, kspan, part);
+static void launch_rw(const TR* R, int ldr, int rows, int K, const int8_t* T, int ldt, const float* h, int bs,
+                      int nsplit, double* part, hipStream_t st) {
+  const int kspan = ((K + nsplit - 1) / nsplit + 31) / 32 * 32;
+  hipLaunchKernelGGL((contract_rw_kernel<NCT, TR>), dim3((rows + 63) / 64, nsplit), dim3(256), 0, st, R, ldr, rows,
+                     K, T, ldt, h, bs, kspan, part);
 }
 
 template <int NCT>
-static void launch_utr(const float* R, int ldr, int m, int n, const int8_t* U, int bs, int nsplit, double* part,
-                       hipStream_t st) {
+static void launch_utr(const float* R, int ldr, int m, int n, const int8_t* U, int ldu, int bs, int nsplit,
+                       double* part, hipStream_t st) {
   const int kspan = ((m + nsplit - 1) / nsplit + 31) / 32 * 32;
-  hipLaunchKernelGGL(contract_utr_kernel<NCT>, dim3((n + 63) / 64, nsplit), dim3(256), 0, st, R, ldr, m, n, U, bs,
-                     kspan, part);
+  hipLaunchKernelGGL(contract_utr_kernel<NCT>, dim3((n + 63) / 64, nsplit), dim3(256), 0, st, R, ldr, m, n, U, ldu,
+                     bs, kspan, part);
 }
 
 // split-K factor: about 512 workgroups, at least 256 of K per split, at most cap splits
@@ -710,41 +773,41 @@ static void reduce_splits(const double* part, int ns, long long cnt, double* out
                      out);
 }
 
-// part[s][c][i] = sum over split s of R[i][j] h_j T[c][j], R rows x K (ld ldr), then out = sum over s
+// out[c][i] = sum_k R[i][k] h_k T[c][k] for R rows x K (ld ldr), T bs x K (ld ldt), split over K
 template <typename TR>
-static void rw_contract(const TR* R, int ldr, int rows, int K, const int8_t* T, const float* h, int bs, int cap,
-                        double* part, double* out, hipStream_t st) {
+static void rw_contract(const TR* R, int ldr, int rows, int K, const int8_t* T, int ldt, const float* h, int bs,
+                        int cap, double* part, double* out, hipStream_t st) {
   const int ns = splits_for((rows + 63) / 64, K, cap);
   const int nct = (bs + 15) / 16;
-  if (nct <= 1) launch_rw<1, TR>(R, ldr, rows, K, T, h, bs, ns, part, st);
-  else if (nct <= 2) launch_rw<2, TR>(R, ldr, rows, K, T, h, bs, ns, part, st);
-  else if (nct <= 4) launch_rw<4, TR>(R, ldr, rows, K, T, h, bs, ns, part, st);
-  else if (nct <= 8) launch_rw<8, TR>(R, ldr, rows, K, T, h, bs, ns, part, st);
-  else launch_rw<16, TR>(R, ldr, rows, K, T, h, bs, ns, part, st);
+  if (nct <= 1) launch_rw<1, TR>(R, ldr, rows, K, T, ldt, h, bs, ns, part, st);
+  else if (nct <= 2) launch_rw<2, TR>(R, ldr, rows, K, T, ldt, h, bs, ns, part, st);
+  else if (nct <= 4) launch_rw<4, TR>(R, ldr, rows, K, T, ldt, h, bs, ns, part, st);
+  else if (nct <= 8) launch_rw<8, TR>(R, ldr, rows, K, T, ldt, h, bs, ns, part, st);
+  else launch_rw<16, TR>(R, ldr, rows, K, T, ldt, h, bs, ns, part, st);
   reduce_splits(part, ns, (long long)bs * rows, out, st);
 }
 
-// Y^T (bs x m) = (R diag(h) T^T)^T
-static void rw_product(const BlockLaunch& L, const BlockWs& w, const int8_t* T, const float* h, int bs,
-                       double* outT, hipStream_t st) {
-  rw_contract<float>(L.R, L.ldr, L.m, L.n, T, h, bs, kMaxSplit, w.part, outT, st);
+// Y^T (bs x m) = (R diag(h) V^T)^T for V = Vt rows
+static void rw_product(const BlockLaunch& L, const BlockWs& w, const float* h, int bs, double* outT,
+                       hipStream_t st) {
+  rw_contract<float>(L.R, L.ldr, L.m, L.n, w.Vt, w.ldv, h, bs, kMaxSplit, w.part, outT, st);
 }
 
-// G (bs x bs) = T diag(w) T^T for ternary rows T (bs x len); integer-exact without weights
-static void gram_product(const BlockWs& w, const int8_t* T, int len, const float* wt, int bs, double* G,
+// G (bs x bs) = T diag(w) T^T for ternary rows T (bs x len, ld ldt); integer-exact without weights
+static void gram_product(const BlockWs& w, const int8_t* T, int len, int ldt, const float* wt, int bs, double* G,
                          hipStream_t st) {
-  rw_contract<int8_t>(T, len, bs, len, T, wt, bs, kMaxGramSplit, w.gpart, G, st);
+  rw_contract<int8_t>(T, ldt, bs, len, T, ldt, wt, bs, kMaxGramSplit, w.gpart, G, st);
 }
 
 // X (bs x n) = U^T R
 static void utr_product(const BlockLaunch& L, const BlockWs& w, int bs, hipStream_t st) {
   const int ns = splits_for((L.n + 63) / 64, L.m, kMaxSplit);
   const int nct = (bs + 15) / 16;
-  if (nct <= 1) launch_utr<1>(L.R, L.ldr, L.m, L.n, w.Ut, bs, ns, w.part, st);
-  else if (nct <= 2) launch_utr<2>(L.R, L.ldr, L.m, L.n, w.Ut, bs, ns, w.part, st);
-  else if (nct <= 4) launch_utr<4>(L.R, L.ldr, L.m, L.n, w.Ut, bs, ns, w.part, st);
-  else if (nct <= 8) launch_utr<8>(L.R, L.ldr, L.m, L.n, w.Ut, bs, ns, w.part, st);
-  else launch_utr<16>(L.R, L.ldr, L.m, L.n, w.Ut, bs, ns, w.part, st);
+  if (nct <= 1) launch_utr<1>(L.R, L.ldr, L.m, L.n, w.Ut, w.ldu, bs, ns, w.part, st);
+  else if (nct <= 2) launch_utr<2>(L.R, L.ldr, L.m, L.n, w.Ut, w.ldu, bs, ns, w.part, st);
+  else if (nct <= 4) launch_utr<4>(L.R, L.ldr, L.m, L.n, w.Ut, w.ldu, bs, ns, w.part, st);
+  else if (nct <= 8) launch_utr<8>(L.R, L.ldr, L.m, L.n, w.Ut, w.ldu, bs, ns, w.part, st);
+  else launch_utr<16>(L.R, L.ldr, L.m, L.n, w.Ut, w.ldu, bs, ns, w.part, st);
   reduce_splits(w.part, ns, (long long)bs * L.n, w.X, st);
 }
 
@@ -784,13 +847,13 @@ static void solve(const BlockWs& w, int bs, const double* in, double* out, int n
   apply<true>(w.Li, bs, w.Tmp, out, ncols, st);
 }
 
-static void select_rows(const double* X, int L, int bs, float tau, const float* h, int EHm, int8_t* T, double* PHC,
-                        int* flags, int flag_empty, hipStream_t st) {
+static void select_rows(const double* X, int L, int ldT, int bs, float tau, const float* h, int EHm, int8_t* T,
+                        double* PHC, int* flags, int flag_empty, hipStream_t st) {
   if (h)
-    hipLaunchKernelGGL(select_rows_kernel<true>, dim3(bs), dim3(512), 0, st, X, L, tau, h, EHm, T, PHC, flags,
+    hipLaunchKernelGGL(select_rows_kernel<true>, dim3(bs), dim3(512), 0, st, X, L, ldT, tau, h, EHm, T, PHC, flags,
                        flag_empty);
   else
-    hipLaunchKernelGGL(select_rows_kernel<false>, dim3(bs), dim3(512), 0, st, X, L, tau, h, EHm, T, PHC, flags,
+    hipLaunchKernelGGL(select_rows_kernel<false>, dim3(bs), dim3(512), 0, st, X, L, ldT, tau, h, EHm, T, PHC, flags,
                        flag_empty);
 }
 
@@ -826,11 +889,11 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops) {
   hipError_t e = side_stream(&ss);
   if (e != hipSuccess) return e;
   // G and its inverse factor on the side stream, after everything queued so far on st
-  auto gram_inverse = [&](const int8_t* T, int len, const float* wt, int bs, double* G) -> hipError_t {
+  auto gram_inverse = [&](const int8_t* T, int len, int ldt, const float* wt, int bs, double* G) -> hipError_t {
     hipError_t r;
     if ((r = hipEventRecord(ss->fork, st)) != hipSuccess) return r;
     if ((r = hipStreamWaitEvent(ss->s, ss->fork, 0)) != hipSuccess) return r;
-    gram_product(w, T, len, wt, bs, G, ss->s);
+    gram_product(w, T, len, ldt, wt, bs, G, ss->s);
     chol_inverse(w, G, bs, ss->s);
     return hipEventRecord(ss->join, ss->s);
   };
@@ -842,36 +905,37 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops) {
     const int bs = (L.k - s * L.b) < L.b ? (L.k - s * L.b) : L.b;
     const int k0 = s * L.b;
     // sketch
-    hipLaunchKernelGGL(omega_kernel, dim3(256), dim3(256), 0, st, w.Vt, bs, n, (long long)s, w.flags);
-    rw_product(L, w, w.Vt, nullptr, bs, w.Yt, st);
-    select_rows(w.Yt, m, bs, L.tau, nullptr, 0, w.Ut, w.PHC, w.flags, 1, st);
+    hipLaunchKernelGGL(omega_kernel, dim3(256), dim3(256), 0, st, w.Vt, w.ldv, bs, n, (long long)s, w.flags);
+    rw_product(L, w, nullptr, bs, w.Yt, st);
+    select_rows(w.Yt, m, w.ldu, bs, L.tau, nullptr, 0, w.Ut, w.PHC, w.flags, 1, st);
     hipLaunchKernelGGL(zero_check_kernel, dim3(1), dim3(256), 0, st, L.R, L.ldr, m, n, w.flags, w.st);
-    hipLaunchKernelGGL(fallback_kernel, dim3(1), dim3(512), 0, st, L.R, L.ldr, m, n, bs, w.Ut, w.PHC, w.flags,
-                       w.used);
+    hipLaunchKernelGGL(fallback_kernel, dim3(1), dim3(512), 0, st, L.R, L.ldr, m, n, bs, w.Ut, w.ldu, w.PHC,
+                       w.flags, w.used);
     fl += 2.0 * m * n * bs;
     for (int t = 0; t < L.T; ++t) {
       // V-step: G = (U^T U + eps I)^-1 U^T R, rows ternarized with weights h
-      if ((e = gram_inverse(w.Ut, m, nullptr, bs, w.GU)) != hipSuccess) return e;
+      if ((e = gram_inverse(w.Ut, m, w.ldu, nullptr, bs, w.GU)) != hipSuccess) return e;
       utr_product(L, w, bs, st);
       if ((e = join()) != hipSuccess) return e;
       solve(w, bs, w.X, w.Z, n, st);
-      select_rows(w.Z, n, bs, L.tau, L.h, L.EHm, w.Vt, w.PHC, w.flags, 0, st);
+      select_rows(w.Z, n, w.ldv, bs, L.tau, L.h, L.EHm, w.Vt, w.PHC, w.flags, 0, st);
       // U-step: F^T = (V^T H V + eps I)^-1 (R H V)^T, columns ternarized without weights
-      if ((e = gram_inverse(w.Vt, n, L.h, bs, w.GV)) != hipSuccess) return e;
-      rw_product(L, w, w.Vt, L.h, bs, w.Yt, st);
+      if ((e = gram_inverse(w.Vt, n, w.ldv, L.h, bs, w.GV)) != hipSuccess) return e;
+      rw_product(L, w, L.h, bs, w.Yt, st);
       if ((e = join()) != hipSuccess) return e;
       solve(w, bs, w.Yt, w.Ft, m, st);
-      select_rows(w.Ft, m, bs, L.tau, nullptr, 0, w.Ut, w.PHC, w.flags, 0, st);
+      select_rows(w.Ft, m, w.ldu, bs, L.tau, nullptr, 0, w.Ut, w.PHC, w.flags, 0, st);
       fl += 4.0 * m * n * bs;
     }
     // scales against Q = R H V of the last U-step, then the update and the outputs
-    gram_product(w, w.Ut, m, nullptr, bs, w.GU, st);
-    hipLaunchKernelGGL(rowdot_kernel, dim3(bs), dim3(256), 0, st, w.Ut, w.Yt, m, w.Md);
+    gram_product(w, w.Ut, m, w.ldu, nullptr, bs, w.GU, st);
+    hipLaunchKernelGGL(rowdot_kernel, dim3(bs), dim3(256), 0, st, w.Ut, w.ldu, w.Yt, m, w.Md);
     hipLaunchKernelGGL(scales_kernel, dim3(1), dim3(256), 0, st, w.Md, w.GU, w.GV, bs, k0, L.T, w.d, L.D, L.energy,
                        w.st, w.flags, L.stats);
     hipLaunchKernelGGL(update_kernel, dim3((n + 63) / 64, (m + 63) / 64), dim3(256), 0, st, L.R, L.ldr, m, n, w.Ut,
-                       w.Vt, w.d, bs, w.flags);
-    hipLaunchKernelGGL(emit_kernel, dim3(256), dim3(256), 0, st, w.Ut, w.Vt, m, n, bs, k0, L.Bp, L.Cp, w.flags);
+                       w.ldu, w.Vt, w.ldv, w.d, bs, w.flags);
+    hipLaunchKernelGGL(emit_kernel, dim3(256), dim3(256), 0, st, w.Ut, w.ldu, w.Vt, w.ldv, m, n, bs, k0, L.Bp, L.Cp,
+                       w.flags);
     fl += 2.0 * m * n * bs;
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
