@@ -123,8 +123,9 @@ int externd_decompose(const float* A, int64_t m, int64_t n, float mu, float tau,
   const size_t o_R = take((size_t)mi * ldr * sizeof(float));
   const size_t o_rs = take((size_t)mi * sizeof(double));
   const size_t o_rowE = take((size_t)mi * sizeof(double));
-  size_t o_RT = 0, o_xz = 0, o_xw = 0, o_xf = 0, o_blk = 0;
+  size_t o_RT = 0, o_xz = 0, o_xw = 0, o_xf = 0, o_rsg = 0, o_blk = 0;
   int grid = 0;
+  bool rl = false;
   if (b == 1) {
     o_RT = take((size_t)ni * ldt * sizeof(float));
     o_xz = take((size_t)mi * sizeof(double));
@@ -133,17 +134,10 @@ int externd_decompose(const float* A, int64_t m, int64_t n, float mu, float tau,
     HIP_OR_FAIL(hipGetDevice(&dev));
     int ncu = 0;
     HIP_OR_FAIL(hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev));
-    const int per = seq_max_blocks_per_cu(mi, ni, h != nullptr);
-    if (per < 1) return fail(EXTERND_EINVAL, "problem too large for the sequential kernel's on-chip state (%d x %d)", mi, ni);
-    const int want = (int)std::max<int64_t>(1, std::min<int64_t>(ncu, (std::max(m, n) + 7) / 8));
-    grid = std::min(want, ncu * per);
-    {
-      const long long rows = (std::max(mi, ni) + grid - 1) / grid;
-      const long long upr = (std::max(ldr, ldt) / 4 + 255) / 256;
-      if (rows * upr > kSeqMaxUnits)
-        return fail(EXTERND_EINVAL, "problem too large for the sequential kernel (%d x %d)", mi, ni);
-    }
+    if (!seq_plan(mi, ni, h != nullptr, ncu, &grid, &rl))
+      return fail(EXTERND_EINVAL, "problem too large for the sequential kernel's on-chip state (%d x %d)", mi, ni);
     o_xf = take((size_t)2 * grid * sizeof(double));
+    o_rsg = take((size_t)grid * mi * sizeof(double));
   } else {
     o_blk = take(block_workspace_bytes(mi, ni, bi));
   }
@@ -202,6 +196,8 @@ int externd_decompose(const float* A, int64_t m, int64_t n, float mu, float tau,
     L.xz = reinterpret_cast<double*>(base + o_xz);
     L.xw = reinterpret_cast<double*>(base + o_xw);
     L.xf = reinterpret_cast<double*>(base + o_xf);
+    L.rsg = reinterpret_cast<double*>(base + o_rsg);
+    L.rl = rl;
     L.bar = bar;
     L.Bp = B_packed;
     L.Cp = C_packed;

@@ -489,7 +489,7 @@ template <bool W>
 __global__ void __launch_bounds__(512) select_rows_kernel(const double* X, int L, int ldT, float tau,
                                                           const float* h, int EHm, int8_t* T, double* PHC,
                                                           int* flags, int flag_empty) {
-  __shared__ SelScratch s;
+  __shared__ SelScratchT<W> s;
   const int c = blockIdx.x;
   const double* x = X + (size_t)c * L;
   if (flags[0]) {  // residual is zero: nothing to select

@@ -17,6 +17,7 @@ struct SeqLaunch {
   double* xz;
   double* xw;
   double* xf;
+  double* rsg;  // grid x m private row-sum copies
   unsigned* bar;
   uint32_t* Bp;
   uint32_t* Cp;
@@ -25,13 +26,14 @@ struct SeqLaunch {
   u64* stats;
   double* bytes;
   int m, n, ldr, ldt, k, T, EHm, grid;
+  bool rl;  // R slab resident in LDS
   float tau;
   unsigned spin_limit;
 };
-size_t seq_smem_bytes(int m, int n, bool weighted);
-int seq_max_blocks_per_cu(int m, int n, bool weighted);
-// rows per workgroup times 256-float4 units per row must fit the kernel's partial-sum table
-constexpr int kSeqMaxUnits = 2048;
+size_t seq_smem_bytes(int m, int n, bool weighted, int G, bool rl);
+// Grid size (one workgroup per CU at most) and whether the R slab fits in LDS; 0 if the problem
+// does not fit the kernel's on-chip state.
+int seq_plan(int m, int n, bool weighted, int ncu, int* grid, bool* rl);
 hipError_t seq_launch(const SeqLaunch& L, hipStream_t st);
 // out[r] = R_r . (t .* h) for rows of a padded row-major matrix; t (and h, nullable) padded to
 // len4 * 4 entries.  Same slab routine as the sequential kernel.

@@ -8,7 +8,7 @@ namespace externd {
 template <bool W>
 __global__ void __launch_bounds__(512) project_kernel(const float* X, int L, float tau, const float* h, int EHm,
                                                       int8_t* V, double* PHC) {
-  __shared__ SelScratch s;
+  __shared__ SelScratchT<W> s;
   const int row = blockIdx.x, tid = threadIdx.x;
   const float* x = X + (size_t)row * L;
   const SelResult r = ternary_select<512, W>(x, h, L, tau, EHm, s);

@@ -30,15 +30,18 @@ namespace externd {
 
 constexpr int kSelBins = 1024;      // bins per histogram level
 constexpr int kSelShift0 = 23 - 6;  // first level: fp32 mantissa bits dropped per bin (64/octave)
-constexpr int kWinMax = 512;        // window elements scored in one pass (8 waves x 64)
+constexpr int kWinMax = 256;        // window elements scored in one pass (4 waves x 64)
 constexpr int kSelLevels = 4;       // histogram levels before the distinct-key walk
 
-struct SelScratch {
+// LDS scratch of one selection; the weight sums exist only where weighted selections run.
+template <bool HW>
+struct SelScratchT {
   unsigned cnt[kSelBins];
   double psum[kSelBins];
-  double hsum[kSelBins];
+  double hsum[HW ? kSelBins : 1];
   unsigned w_key[kWinMax];
-  u64 w_plo[kWinMax], w_phi[kWinMax], w_hlo[kWinMax], w_hhi[kWinMax];
+  u64 w_plo[kWinMax], w_phi[kWinMax];
+  u64 w_hlo[HW ? kWinMax : 1], w_hhi[HW ? kWinMax : 1];
   u64 a_plo[16], a_phi[16], a_hlo[16], a_hhi[16];  // per-wave exact partial sums
   unsigned a_cnt[16];
   u64 f_plo[16], f_phi[16], f_hlo[16], f_hhi[16];  // per-wave best threshold
@@ -73,12 +76,35 @@ __device__ __forceinline__ bool selected(float x, const SelResult& r) {
   return r.count > 0u && k != 0u && k >= r.ekey && k >= r.tkey;
 }
 
+// Clears the first histogram and publishes each wave's largest key (kx: this thread's largest
+// |x| bit pattern) for a following ternary_select<..., PRE = true>; ends with a barrier.  Lets a
+// caller that already touches every element fold this pass into its own loop.
+template <int NT, bool HW>
+__device__ __forceinline__ void select_prepare(SelScratchT<HW>& s, unsigned kx) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  kx = wave_max_u32(kx);
+  if (lane == 0) s.red_u[wid] = kx;
+  for (int b = tid; b < kSelBins; b += NT) {
+    s.cnt[b] = 0u;
+    s.psum[b] = 0.0;
+    if (HW) s.hsum[b] = 0.0;
+  }
+  if (tid == 0) {
+    s.slot = 0u;
+    s.bn = 0.0;
+    s.bd = 1.0;
+  }
+  __syncthreads();
+}
+
 // All NT threads of the workgroup call this.  vals[0..L) (LDS or global, fp32 or fp64) holds the
 // vector; its fp32 rounding is what is projected.  hl[0..L) holds the weights (read only when W).
-// EHm: exponent with max(h) < 2^EHm (W only).  Every thread receives the same result.
-template <int NT, bool W, typename T>
-__device__ SelResult ternary_select(const T* vals, const float* hl, int L, float tau, int EHm,
-                                    SelScratch& s) {
+// EHm: exponent with max(h) < 2^EHm (W only).  Every thread receives the same result.  PRE: the
+// caller already ran select_prepare with the vector's largest key.
+template <int NT, bool W, typename T, bool HW, bool PRE = false>
+__device__ __forceinline__ SelResult ternary_select(const T* vals, const float* hl, int L, float tau, int EHm,
+                                    SelScratchT<HW>& s) {
+  static_assert(HW || !W, "a weighted selection needs the weighted scratch");
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   constexpr int NW = NT / 64;
   SelResult out;
@@ -87,26 +113,15 @@ __device__ SelResult ternary_select(const T* vals, const float* hl, int L, float
   out.P = 0.0;
   out.H = 0.0;
   out.count = 0u;
-  // ---- max |x|; clear the first histogram meanwhile
+  if (!PRE) {  // max |x| and the cleared histogram
+    unsigned kx = 0;
+    for (int i = tid; i < L; i += NT) {
+      const unsigned k = __float_as_uint((float)vals[i]) & 0x7FFFFFFFu;
+      kx = k > kx ? k : kx;
+    }
+    select_prepare<NT>(s, kx);
+  }
   unsigned km = 0;
-  for (int i = tid; i < L; i += NT) {
-    const unsigned k = __float_as_uint((float)vals[i]) & 0x7FFFFFFFu;
-    km = k > km ? k : km;
-  }
-  km = wave_max_u32(km);
-  if (lane == 0) s.red_u[wid] = km;
-  for (int b = tid; b < kSelBins; b += NT) {
-    s.cnt[b] = 0u;
-    s.psum[b] = 0.0;
-    if (W) s.hsum[b] = 0.0;
-  }
-  if (tid == 0) {
-    s.slot = 0u;
-    s.bn = 0.0;
-    s.bd = 1.0;
-  }
-  __syncthreads();
-  km = 0;
 #pragma unroll
   for (int w = 0; w < NW; ++w) km = s.red_u[w] > km ? s.red_u[w] : km;
   if (km == 0u) {

@@ -9,17 +9,22 @@
 // previous u (or v) has reached an exact fixed point; the remaining iterations would repeat it,
 // so the loop stops there (the result is the same).
 //
-// MI355X layout.  The residual lives in HBM twice: R (m x n) and its transpose RT (n x m), both
+// MI355X layout.  The residual is kept twice: R (m x n) and its transpose RT (n x m), both
 // row-major.  Workgroup g owns a fixed slab of R rows and a fixed slab of RT rows, so both
 // matvecs are reduction-free across workgroups: a U-step row dot product z_i = R_i . (h v) and a
-// V-step row dot product w_j = RT_j . u are finished inside the owning workgroup.  The only
+// V-step row dot product w_j = RT_j . u are finished inside the owning workgroup.  When it fits,
+// the R slab lives in the workgroup's LDS for the whole run (the U-steps and the R half of the
+// deflation never touch HBM) and only the RT slab is streamed; one XCD's RT slabs (m n / 8 floats)
+// then fit its L2.  The only
 // cross-workgroup traffic per half-step is the finished vector (z or w, fp64) plus one grid
 // barrier; every workgroup then runs the same deterministic selection redundantly, so all of
 // them agree on u or v without a broadcast.  Deflation is applied lazily: the pending component
 // is subtracted from RT rows during the next V-step read and from R rows during the next U-step
 // read (one read-modify-write pass fused with a matvec).  The tracked row sums rs (fp64
-// recurrence rs <- rs - d (sum v) u) are replicated in every workgroup's LDS, so the next u0 is
-// chosen without another exchange.
+// recurrence rs <- rs - d (sum v) u) are replicated: every workgroup keeps a private copy in
+// global memory (it stays in its XCD's L2), so the next u0 is chosen without another exchange.
+#include <algorithm>
+
 #include "externd_internal.hpp"
 #include "select.hpp"
 
@@ -34,6 +39,7 @@ struct SeqArgs {
   double* xz;          // m
   double* xw;          // n
   double* xf;          // 2 * gridDim.x
+  double* rsg;         // gridDim.x x m: private row-sum copies
   unsigned* bar;
   uint32_t* Bp;
   uint32_t* Cp;
@@ -53,21 +59,21 @@ __device__ __forceinline__ int code_at(const uint32_t* pk, int i) {
 
 // Dynamic LDS of the sequential kernel; every region starts on a 16-byte boundary.
 struct SeqLds {
-  size_t rs, dl, hl, pk, part, total;
+  size_t dl, hl, pk, part, slab, total;
 };
 __host__ __device__ inline size_t al16(size_t x) { return (x + 15) & ~(size_t)15; }
-constexpr int kMaxUnits = 2048;  // row units per workgroup per matvec (checked on the host)
-__host__ __device__ inline SeqLds seq_lds_layout(int m, int n, bool weighted) {
+__host__ __device__ inline SeqLds seq_lds_layout(int m, int n, bool weighted, int G, bool rl) {
   const size_t L = (size_t)(m > n ? m : n);
-  const size_t n4 = (size_t)((n + 3) & ~3);
+  const size_t n4 = (size_t)((n + 3) & ~3), m4 = (size_t)((m + 3) & ~3);
   const size_t wm = (size_t)((m + 15) / 16), wn = (size_t)((n + 15) / 16);
+  const size_t parts = 8 * 16;  // per-wave row sums of the matvec (waves x rows reduced together)
   SeqLds s;
-  s.rs = al16(sizeof(SelScratch));
-  s.dl = al16(s.rs + 8 * (size_t)m);
+  s.dl = al16(weighted ? sizeof(SelScratchT<true>) : sizeof(SelScratchT<false>));
   s.hl = al16(s.dl + 8 * L);
   s.pk = al16(s.hl + (weighted ? 4 * n4 : 0));
   s.part = al16(s.pk + 4 * (4 * wm + 3 * wn + 4));
-  s.total = al16(s.part + 8 * (size_t)kMaxUnits);
+  s.slab = al16(s.part + 8 * parts);
+  s.total = al16(s.slab + (rl ? 4 * n4 * (((size_t)m + G - 1) / G) : 0));
   return s;
 }
 
@@ -93,119 +99,130 @@ struct PackOut {
   double p;     // sum of |vals| over the support (when asked for)
 };
 
-// Weights of one float4 (elements 4q .. 4q+3) of a packed ternary vector, optionally times the
-// LDS column weights hl: (double) products with fp32 data are exact either way.
-__device__ __forceinline__ float4 code_weights(const uint32_t* pk, int q, const float* hl) {
-  const unsigned word = pk[q >> 2] >> ((q & 3) * 8);
+// Rows [r0, r1) of a row-major matrix (leading dimension ld floats, len4 float4 per row) dotted
+// with a packed ternary vector pk_w (times the LDS weights hl when given); the results go to
+// out[row] (exchange buffer, device-coherent stores).  Column-stationary: thread t owns the
+// float4 columns t, t + NT, ... of every row, so it decodes its ternary weights (and the pending
+// component's codes) once and reuses them for all rows; loads of kRC rows are issued together.
+// A row's sum is the thread partials (fixed order), a DPP wave sum, then the wave sums in wave
+// order: deterministic.  Pending deflation of rows whose own code in pk_own is nonzero is fused
+// in: x <- fl32(x - own * other * d) where pk_other is nonzero, written back.
+constexpr int kQMax = 8;   // float4 columns per thread: len4 <= kQMax * NT (n <= 16384 at 512 threads)
+constexpr int kQC = 2;     // float4 columns per thread handled per pass over the rows
+constexpr int kRC = 4;     // rows whose loads are issued together
+constexpr int kRS = 16;    // rows reduced together
+__device__ __forceinline__ float4 decode4(const uint32_t* pk, int q) {
+  const unsigned b = (pk[q >> 2] >> ((q & 3) * 8)) & 0xFFu;
   float c[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    const unsigned cd = (word >> (2 * t)) & 3u;
+    const unsigned cd = (b >> (2 * t)) & 3u;
     c[t] = cd == 0u ? 0.0f : (cd == 1u ? 1.0f : -1.0f);
   }
-  float4 w = make_float4(c[0], c[1], c[2], c[3]);
-  if (hl) {
-    const float4 h = reinterpret_cast<const float4*>(hl)[q];
-    w = make_float4(w.x * h.x, w.y * h.y, w.z * h.z, w.w * h.w);
-  }
-  return w;
+  return make_float4(c[0], c[1], c[2], c[3]);
 }
-
-// Rows [r0, r1) of a row-major matrix (leading dimension ld floats, len4 float4 per row) dotted
-// with a packed ternary vector pk_w (times the LDS weights hl when given); the results go to
-// out[row] (exchange buffer, device-coherent stores).  Each row is cut into units of 64 * kQ
-// float4; every wave takes kUPW units per round and issues all their loads before consuming any,
-// so one memory latency covers the round.  The per-unit partial sums are combined in a fixed
-// order (deterministic).  Pending deflation of rows whose own code in pk_own is nonzero is fused
-// in: x <- fl32(x - own * other * d) on the columns where pk_other is nonzero, written back.
-constexpr int kQ = 4;
-constexpr int kUPW = 4;
 template <int NT>
-__device__ void slab_matvec(float* base, int ld, int len4, int r0, int r1, const uint32_t* pk_w,
-                            const float* hl, bool apply, const uint32_t* pk_own,
-                            const uint32_t* pk_other, float d, double* part, double* out) {
+__device__ __forceinline__ void slab_matvec(float* base, int row_base, int ld, int len4, int r0, int r1,
+                                            const uint32_t* pk_w, const float* hl, bool apply,
+                                            const uint32_t* pk_own, const uint32_t* pk_other, float d,
+                                            double* part, double* out) {
   constexpr int NW = NT / 64;
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int rows = r1 > r0 ? r1 - r0 : 0;
-  const int upr = (len4 + 64 * kQ - 1) / (64 * kQ);
-  const int units = rows * upr;
-  for (int ub = 0; ub < units; ub += NW * kUPW) {
-    float4 buf[kUPW][kQ];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int nqc = (len4 + kQC * NT - 1) / (kQC * NT);  // column passes
+  for (int rs = r0; rs < r1; rs += kRS) {
+    double acc[kRS];
 #pragma unroll
-    for (int j = 0; j < kUPW; ++j) {
-      const int u = ub + wid * kUPW + j;
-      const int r = u / upr, sgi = u - (u / upr) * upr;
-      const float4* r4 = reinterpret_cast<const float4*>(base + (size_t)(r0 + r) * ld);
+    for (int k = 0; k < kRS; ++k) acc[k] = 0.0;
+    for (int qc = 0; qc < nqc; ++qc) {
+      double w[kQC][4];  // code (times h): exact in fp64, so fma(x, w, acc) = acc + x w rounded once
+      float4 od[kQC];
 #pragma unroll
-      for (int t = 0; t < kQ; ++t) {
-        const int q = sgi * 64 * kQ + t * 64 + lane;
-        buf[j][t] = (u < units && q < len4) ? r4[q] : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < kUPW; ++j) {
-      const int u = ub + wid * kUPW + j;
-      if (u >= units) break;
-      const int r = u / upr, sgi = u - r * upr;
-      const int row = r0 + r;
-      const int oc = apply ? code_at(pk_own, row) : 0;
-      float4* r4 = reinterpret_cast<float4*>(base + (size_t)row * ld);
-      double acc0 = 0.0, acc1 = 0.0;
-#pragma unroll
-      for (int t = 0; t < kQ; ++t) {
-        const int q = sgi * 64 * kQ + t * 64 + lane;
-        if (q >= len4) continue;
-        float4 x = buf[j][t];
-        if (oc != 0) {
-          const unsigned word = pk_other[q >> 2] >> ((q & 3) * 8);
-          if (word & 0xFFu) {
-            float xv[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              const unsigned cd = (word >> (2 * c)) & 3u;
-              if (cd != 0u) {
-                const int sg = (cd == 1u ? 1 : -1) * oc;
-                xv[c] = sg > 0 ? xv[c] - d : xv[c] + d;
-              }
-            }
-            x = make_float4(xv[0], xv[1], xv[2], xv[3]);
-            r4[q] = x;
+      for (int qi = 0; qi < kQC; ++qi) {
+        const int q = tid + (qc * kQC + qi) * NT;
+        float4 wf = make_float4(0.f, 0.f, 0.f, 0.f);
+        od[qi] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (q < len4) {
+          wf = decode4(pk_w, q);
+          if (hl) {
+            const float4 h = reinterpret_cast<const float4*>(hl)[q];
+            wf = make_float4(wf.x * h.x, wf.y * h.y, wf.z * h.z, wf.w * h.w);
+          }
+          if (apply) {
+            const float4 o = decode4(pk_other, q);
+            od[qi] = make_float4(d * o.x, d * o.y, d * o.z, d * o.w);
           }
         }
-        const float4 w = code_weights(pk_w, q, hl);
-        if (!hl) {
-          acc0 += (double)(x.x * w.x);
-          acc1 += (double)(x.y * w.y);
-          acc0 += (double)(x.z * w.z);
-          acc1 += (double)(x.w * w.w);
-        } else {
-          acc0 += (double)x.x * (double)w.x;
-          acc1 += (double)x.y * (double)w.y;
-          acc0 += (double)x.z * (double)w.z;
-          acc1 += (double)x.w * (double)w.w;
+        w[qi][0] = (double)wf.x;
+        w[qi][1] = (double)wf.y;
+        w[qi][2] = (double)wf.z;
+        w[qi][3] = (double)wf.w;
+      }
+#pragma unroll
+      for (int rc = 0; rc < kRS; rc += kRC) {
+        if (rs + rc >= r1) break;  // uniform
+        float4 x[kRC][kQC];
+#pragma unroll
+        for (int k = 0; k < kRC; ++k) {
+          const int row = rs + rc + k;
+          const float4* r4 = reinterpret_cast<const float4*>(base + (size_t)(row - row_base) * ld);
+#pragma unroll
+          for (int qi = 0; qi < kQC; ++qi) {
+            const int q = tid + (qc * kQC + qi) * NT;
+            x[k][qi] = (row < r1 && q < len4) ? r4[q] : make_float4(0.f, 0.f, 0.f, 0.f);
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < kRC; ++k) {
+          const int row = rs + rc + k;
+          if (row >= r1) break;  // uniform
+          const int oc = apply ? code_at(pk_own, row) : 0;
+          float4* r4 = reinterpret_cast<float4*>(base + (size_t)(row - row_base) * ld);
+          double a0 = 0.0, a1 = 0.0;
+#pragma unroll
+          for (int qi = 0; qi < kQC; ++qi) {
+            const int q = tid + (qc * kQC + qi) * NT;
+            float4 v = x[k][qi];
+            if (oc != 0) {  // uniform across the workgroup
+              const float sg = oc > 0 ? -1.0f : 1.0f;
+              const float4 o = od[qi];
+              v = make_float4(fmaf(sg, o.x, v.x), fmaf(sg, o.y, v.y), fmaf(sg, o.z, v.z), fmaf(sg, o.w, v.w));
+              if (q < len4 && (o.x != 0.0f || o.y != 0.0f || o.z != 0.0f || o.w != 0.0f)) r4[q] = v;
+            }
+            a0 = fma((double)v.x, w[qi][0], a0);
+            a1 = fma((double)v.y, w[qi][1], a1);
+            a0 = fma((double)v.z, w[qi][2], a0);
+            a1 = fma((double)v.w, w[qi][3], a1);
+          }
+          acc[rc + k] += a0 + a1;
         }
       }
-      const double v = wave_sum_f64(acc0 + acc1);
-      if (lane == 0) part[u] = v;
     }
+    // per-row block sums: DPP wave sums, then the waves in order
+#pragma unroll
+    for (int k = 0; k < kRS; ++k) {
+      if (rs + k >= r1) break;
+      const double v = wave_sum_f64(acc[k]);
+      if (lane == 0) part[wid * kRS + k] = v;
+    }
+    __syncthreads();
+    if (tid < kRS && rs + tid < r1) {
+      double t = 0.0;
+#pragma unroll
+      for (int w2 = 0; w2 < NW; ++w2) t += part[w2 * kRS + tid];
+      st_dev(out + rs + tid, t);
+    }
+    __syncthreads();
   }
-  __syncthreads();
-  for (int r = threadIdx.x; r < rows; r += NT) {
-    double acc = 0.0;
-    for (int q = 0; q < upr; ++q) acc += part[r * upr + q];
-    st_dev(out + r0 + r, acc);
-  }
-  __syncthreads();
 }
 
 // Apply the pending deflation to rows [r0, r1) (used where no matvec pass is due).
 template <int NT>
-__device__ void slab_deflate(float* base, int ld, int len4, int r0, int r1, const uint32_t* pk_own,
+__device__ __forceinline__ void slab_deflate(float* base, int row_base, int ld, int len4, int r0, int r1, const uint32_t* pk_own,
                              const uint32_t* pk_other, float d) {
   for (int r = r0; r < r1; ++r) {
     const int oc = code_at(pk_own, r);
     if (oc == 0) continue;
-    float4* r4 = reinterpret_cast<float4*>(base + (size_t)r * ld);
+    float4* r4 = reinterpret_cast<float4*>(base + (size_t)(r - row_base) * ld);
     for (int q = threadIdx.x; q < len4; q += NT) {
       const unsigned word = pk_other[q >> 2] >> ((q & 3) * 8);
       if (!(word & 0xFFu)) continue;
@@ -225,15 +242,14 @@ __device__ void slab_deflate(float* base, int ld, int len4, int r0, int r1, cons
   __syncthreads();
 }
 
-template <int NT, bool WV>
+template <int NT, bool WV, bool RL>
 __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
   constexpr int NW = NT / 64;
   extern __shared__ __align__(16) char smem[];
-  SelScratch& s = *reinterpret_cast<SelScratch*>(smem);
+  SelScratchT<WV>& s = *reinterpret_cast<SelScratchT<WV>*>(smem);
   const int m = a.m, n = a.n;
   const int m4 = (m + 3) & ~3, n4 = (n + 3) & ~3;
-  const SeqLds lay = seq_lds_layout(m, n, WV);
-  double* rs = reinterpret_cast<double*>(smem + lay.rs);    // m: replicated row sums
+  const SeqLds lay = seq_lds_layout(m, n, WV, (int)gridDim.x, RL);
   double* dl = reinterpret_cast<double*>(smem + lay.dl);    // exchanged vector (z or w)
   float* hl = reinterpret_cast<float*>(smem + lay.hl);      // n4 column weights (weighted)
   uint32_t* pk = reinterpret_cast<uint32_t*>(smem + lay.pk);
@@ -254,8 +270,20 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
   const int c0 = (int)((long long)g * n / G), c1 = (int)((long long)(g + 1) * n / G);
   const float* hw = WV ? hl : nullptr;
   unsigned epoch = 0;
+  double* rs = a.rsg + (size_t)g * m;  // this workgroup's copy of the row sums
+  // the residual rows this workgroup owns: LDS-resident (RL) or in HBM
+  float* Rb = RL ? reinterpret_cast<float*>(smem + lay.slab) : a.R;
+  const int Rld = RL ? n4 : a.ldr, Rrow0 = RL ? r0 : 0;
 
   for (int i = tid; i < m; i += NT) rs[i] = a.rs0[i];
+  if (RL) {
+    const int q4 = n4 / 4;
+    for (int x = tid; x < (r1 - r0) * q4; x += NT) {
+      const int r = x / q4, q = x - r * q4;
+      reinterpret_cast<float4*>(Rb + (size_t)r * n4)[q] =
+          reinterpret_cast<const float4*>(a.R + (size_t)(r0 + r) * a.ldr)[q];
+    }
+  }
   if (WV)
     for (int j = tid; j < n4; j += NT) hl[j] = j < n ? a.h[j] : 0.0f;
   for (int i = tid; i < 4 * wm + 3 * wn; i += NT) pk[i] = 0u;
@@ -272,6 +300,18 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
   float pd = 0.0f;
   __syncthreads();
 
+  // Read the exchanged vector (device-coherent loads) into LDS; its largest key and the cleared
+  // histogram are prepared for the selection on the way (one barrier).
+  auto load_exchange = [&](const double* src, int len) {
+    unsigned kx = 0u;
+    for (int j = tid; j < len; j += NT) {
+      const double v = ld_dev(src + j);
+      dl[j] = v;
+      const unsigned k = __float_as_uint((float)v) & 0x7FFFFFFFu;
+      kx = k > kx ? k : kx;
+    }
+    select_prepare<NT>(s, kx);
+  };
   // Pack the selection r of vals[0..len) into dst (2-bit codes) with wave ballots: wave w takes
   // the 64-element chunks w, w + NW, ...; lanes 0..3 write the chunk's four words.  prev, when
   // given, receives the old words.  Block totals are combined in wave order (deterministic).
@@ -325,12 +365,12 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
   // deflation.  Returns the row, -1 if R == 0, -2 on a barrier failure.
   auto fallback_row = [&]() -> int {
     if (have_pending && !r_applied) {
-      slab_deflate<NT>(a.R, a.ldr, n4 / 4, r0, r1, du, dv, pd);
+      slab_deflate<NT>(Rb, Rrow0, Rld, n4 / 4, r0, r1, du, dv, pd);
       r_applied = true;
     }
     double best = 0.0, bidx = -1.0;
     for (int i = r0 + wid; i < r1; i += NW) {
-      const float* row = a.R + (size_t)i * a.ldr;
+      const float* row = Rb + (size_t)(i - Rrow0) * Rld;
       for (int j = lane; j < n; j += 64) {
         const double v = fabs((double)row[j]);
         const double idx = (double)i * (double)n + (double)j;
@@ -412,7 +452,17 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
       continue;
     }
     // ---------------- initial u: ternarized fp32 row sums
-    const SelResult su = ternary_select<NT, false>(rs, nullptr, m, a.tau, 0, s);
+    {
+      unsigned kx = 0u;
+      for (int i = tid; i < m; i += NT) {
+        const double v = rs[i];
+        dl[i] = v;
+        const unsigned k = __float_as_uint((float)v) & 0x7FFFFFFFu;
+        kx = k > kx ? k : kx;
+      }
+      select_prepare<NT>(s, kx);
+    }
+    const SelResult su = ternary_select<NT, false, double, WV, true>(dl, nullptr, m, a.tau, 0, s);
     bool fallback = false;
     if (su.count == 0u) {
       const int r = fallback_row();
@@ -425,7 +475,7 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
       set_unit_u(r);
       fallback = true;
     } else {
-      pack_sel(rs, m, su, pu, nullptr, false);
+      pack_sel(dl, m, su, pu, nullptr, false);
     }
     for (int w = tid; w < wm; w += NT) pu0[w] = pu[w];
     __syncthreads();
@@ -439,15 +489,14 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
     int t = 0;
     while (t < a.T) {
       // ---- V-step: w_j = RT_j . u on owned RT rows (pending deflation fused)
-      slab_matvec<NT>(a.RT, a.ldt, m4 / 4, c0, c1, pu, nullptr, have_pending && !rt_applied, dv, du, pd,
+      slab_matvec<NT>(a.RT, 0, a.ldt, m4 / 4, c0, c1, pu, nullptr, have_pending && !rt_applied, dv, du, pd,
                       part, a.xw);
       rt_applied = true;
       ++passes;
       ++epoch;
       if (grid_barrier(a.bar, epoch, a.spin_limit, &bar_flag)) return;
-      for (int j = tid; j < n; j += NT) dl[j] = ld_dev(a.xw + j);
-      __syncthreads();
-      const SelResult sv = ternary_select<NT, WV>(dl, hw, n, a.tau, a.EHm, s);
+      load_exchange(a.xw, n);
+      const SelResult sv = ternary_select<NT, WV, double, WV, true>(dl, hw, n, a.tau, a.EHm, s);
       if (sv.count == 0u) {
         // R^T u == 0: only possible for the initial u; restart from the largest-entry row
         if (fallback) {
@@ -476,16 +525,15 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
         break;
       }
       // ---- U-step: z_i = R_i . (h v) on owned R rows (pending deflation fused)
-      slab_matvec<NT>(a.R, a.ldr, n4 / 4, r0, r1, pv, hw, have_pending && !r_applied, du, dv, pd, part,
+      slab_matvec<NT>(Rb, Rrow0, Rld, n4 / 4, r0, r1, pv, hw, have_pending && !r_applied, du, dv, pd, part,
                       a.xz);
       r_applied = true;
       ++passes;
       ++usteps;
       ++epoch;
       if (grid_barrier(a.bar, epoch, a.spin_limit, &bar_flag)) return;
-      for (int i = tid; i < m; i += NT) dl[i] = ld_dev(a.xz + i);
-      __syncthreads();
-      const SelResult s2 = ternary_select<NT, false>(dl, nullptr, m, a.tau, 0, s);
+      load_exchange(a.xz, m);
+      const SelResult s2 = ternary_select<NT, false, double, WV, true>(dl, nullptr, m, a.tau, 0, s);
       // new u, the previous one kept in pu_prev, and p = sum over supp(u) of u_i z_i with the
       // fp64 z (fixed reduction order)
       const PackOut puo = pack_sel(dl, m, s2, pu, pu_prev, true);
@@ -545,14 +593,24 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
     __syncthreads();
   }
   // apply the last pending deflation to R (the transpose copy is no longer needed)
-  if (have_pending && !r_applied) slab_deflate<NT>(a.R, a.ldr, n4 / 4, r0, r1, du, dv, pd);
+  if (have_pending && !r_applied) slab_deflate<NT>(Rb, Rrow0, Rld, n4 / 4, r0, r1, du, dv, pd);
+  if (RL) {  // the final residual back to HBM
+    const int q4 = n4 / 4;
+    for (int x = tid; x < (r1 - r0) * q4; x += NT) {
+      const int r = x / q4, q = x - r * q4;
+      reinterpret_cast<float4*>(a.R + (size_t)(r0 + r) * a.ldr)[q] =
+          reinterpret_cast<const float4*>(Rb + (size_t)r * n4)[q];
+    }
+  }
 }
 
-size_t seq_smem_bytes(int m, int n, bool weighted) { return seq_lds_layout(m, n, weighted).total; }
+size_t seq_smem_bytes(int m, int n, bool weighted, int G, bool rl) {
+  return seq_lds_layout(m, n, weighted, G, rl).total;
+}
 
-template <bool WV>
+template <bool WV, bool RL>
 static hipError_t launch_one(const SeqArgs& a, int G, size_t smem, hipStream_t st) {
-  auto kern = seq_kernel<512, WV>;
+  auto kern = seq_kernel<512, WV, RL>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (e != hipSuccess) return e;
   SeqArgs copy = a;
@@ -560,20 +618,31 @@ static hipError_t launch_one(const SeqArgs& a, int G, size_t smem, hipStream_t s
   return hipLaunchCooperativeKernel((const void*)kern, dim3(G), dim3(512), args, (unsigned)smem, st);
 }
 
-template <bool WV>
+template <bool WV, bool RL>
 static int coresident_one(size_t smem) {
   int nb = 0;
-  auto kern = seq_kernel<512, WV>;
+  auto kern = seq_kernel<512, WV, RL>;
   if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem) != hipSuccess)
     return 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, 512, smem) != hipSuccess) return 0;
   return nb;
 }
 
-int seq_max_blocks_per_cu(int m, int n, bool weighted) {
-  const size_t smem = seq_smem_bytes(m, n, weighted);
-  if (smem > 160 * 1024) return 0;
-  return weighted ? coresident_one<true>(smem) : coresident_one<false>(smem);
+constexpr size_t kLdsBytes = 160 * 1024;
+
+int seq_plan(int m, int n, bool weighted, int ncu, int* grid, bool* rl) {
+  const int want = (int)std::max<long long>(1, std::min<long long>(ncu, ((long long)std::max(m, n) + 7) / 8));
+  // the R slab in LDS when it fits (one workgroup per CU)
+  const bool try_rl = !weighted && seq_smem_bytes(m, n, weighted, want, true) <= kLdsBytes;
+  const size_t smem = seq_smem_bytes(m, n, weighted, want, try_rl);
+  if (smem > kLdsBytes) return 0;
+  int per = 0;
+  if (weighted) per = try_rl ? coresident_one<true, true>(smem) : coresident_one<true, false>(smem);
+  else per = try_rl ? coresident_one<false, true>(smem) : coresident_one<false, false>(smem);
+  if (per < 1 || want > ncu * per) return 0;
+  *grid = want;
+  *rl = try_rl;
+  return 1;
 }
 
 hipError_t seq_launch(const SeqLaunch& L, hipStream_t st) {
@@ -586,6 +655,7 @@ hipError_t seq_launch(const SeqLaunch& L, hipStream_t st) {
   a.xz = L.xz;
   a.xw = L.xw;
   a.xf = L.xf;
+  a.rsg = L.rsg;
   a.bar = L.bar;
   a.Bp = L.Bp;
   a.Cp = L.Cp;
@@ -604,8 +674,9 @@ hipError_t seq_launch(const SeqLaunch& L, hipStream_t st) {
   a.EHm = L.EHm;
   a.tau = L.tau;
   a.spin_limit = L.spin_limit;
-  const size_t smem = seq_smem_bytes(L.m, L.n, L.h != nullptr);
-  return L.h ? launch_one<true>(a, L.grid, smem, st) : launch_one<false>(a, L.grid, smem, st);
+  const size_t smem = seq_smem_bytes(L.m, L.n, L.h != nullptr, L.grid, L.rl);
+  if (L.h) return L.rl ? launch_one<true, true>(a, L.grid, smem, st) : launch_one<true, false>(a, L.grid, smem, st);
+  return L.rl ? launch_one<false, true>(a, L.grid, smem, st) : launch_one<false, false>(a, L.grid, smem, st);
 }
 
 // ---- standalone matvec with the same slab routine (kernel-level parity tests) ----------
@@ -631,16 +702,16 @@ __global__ void __launch_bounds__(512) matvec_rows_kernel(float* Rp, int rows, i
   __syncthreads();
   const int G = gridDim.x, g = blockIdx.x;
   const int r0 = (int)((long long)g * rows / G), r1 = (int)((long long)(g + 1) * rows / G);
-  slab_matvec<512>(Rp, ld, len4, r0, r1, pk, h ? hl : nullptr, false, nullptr, nullptr, 0.0f, part, out);
+  slab_matvec<512>(Rp, 0, ld, len4, r0, r1, pk, h ? hl : nullptr, false, nullptr, nullptr, 0.0f, part, out);
 }
 
 hipError_t matvec_rows(float* Rp, int rows, int len4, int ld, const int8_t* t, const float* h, double* out,
                        hipStream_t st) {
   const int words = (len4 * 4 + 15) / 16;
   const int G = rows < 256 ? rows : 256;
-  const int upr = (len4 + 64 * kQ - 1) / (64 * kQ);
-  if ((long long)((rows + G - 1) / G) * upr > kMaxUnits) return hipErrorInvalidValue;
-  const size_t smem = al16(4 * (size_t)words) + al16(h ? 16 * (size_t)len4 : 0) + 8 * (size_t)kMaxUnits;
+  if (len4 > kQMax * 512) return hipErrorInvalidValue;
+  const size_t smem = al16(4 * (size_t)words) + al16(h ? 16 * (size_t)len4 : 0) + 8 * (size_t)(8 * kRS);
+  if (smem > 160 * 1024) return hipErrorInvalidValue;
   hipError_t e = hipFuncSetAttribute((const void*)matvec_rows_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(matvec_rows_kernel, dim3(G), dim3(512), smem, st, Rp, rows, len4, ld, t, h, out);
