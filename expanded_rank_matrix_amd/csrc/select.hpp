@@ -1,4 +1,4 @@
-// Exact ternary projection T_tau(x; h) computed by one workgroup.
+// Ternary projection T_tau(x; h) computed by one workgroup.
 //
 // Definition (reading of the adaptive ternarization operator, ExTernD review, Method;
 // pith.science free parameters, tau / Eq. 2): among the elements with |x_i| >= tau * max|x|
@@ -11,18 +11,22 @@
 // support = {eligible i : |x_i| >= t}, t one of the distinct eligible values, and "smallest j"
 // means "largest t".  The search needs no sort:
 //   1. histogram the eligible values by their fp32 bit pattern ("key") into 1024 bins (64 per
-//      octave below the maximum, the last bin catches the rest), with counts and fp64 sums of
-//      h|x| and h (LDS atomics; used for pruning only);
+//      octave below the maximum, the last bin catches the rest): counts and sums of h|x| and h as
+//      64-bit fixed-point integers (LDS integer atomics: exact, so the sums do not depend on the
+//      order in which threads add them);
 //   2. every bin boundary is a threshold whose score follows from the prefix sums; a bin's
 //      interior can only win if (P_above + top_of_bin * H_bin)^2 / (H_above + H_bin) reaches the
 //      best boundary score (each added element adds at most top_of_bin per unit weight, and the
 //      score is quasi-convex in the added weight).  The bins that can hold the optimum form a
-//      narrow window (typically three bins, a few dozen elements).  A window with too many
-//      elements is histogrammed again over its own key range at a finer bin width;
-//   3. the window's elements are scored exactly: P(t) = P_above + sum over window elements with
-//      key >= t, every sum an exact 128-bit fixed-point integer (order independent), so the
-//      decision is canonical: it depends neither on the launch shape nor on atomic ordering.
-//      Each wave scores 64 window elements against the whole window (LDS broadcast reads).
+//      narrow window (typically three bins, a few dozen elements); the prefix sums also give the
+//      sums over everything above it.  A window with too many elements is histogrammed again over
+//      its own key range at a finer bin width;
+//   3. the window's elements are scored: P(t) = P_above + sum over window elements with key >= t,
+//      all in the same fixed point, so every workgroup that runs the selection on the same vector
+//      reaches the same decision whatever its thread count or atomic ordering.
+// Fixed-point scales: one unit of P is 2^-sP with sP = 62 - EM - EHm - LB (|x| < 2^EM, h < 2^EHm,
+// L < 2^LB), so no sum can overflow, and each element is truncated by less than 2^-47 of the
+// largest |x|.
 #pragma once
 #include "common.hpp"
 
@@ -37,38 +41,56 @@ constexpr int kSelLevels = 4;       // histogram levels before the distinct-key 
 template <bool HW>
 struct SelScratchT {
   unsigned cnt[kSelBins];
-  double psum[kSelBins];
-  double hsum[HW ? kSelBins : 1];
+  u64 psum[kSelBins];
+  u64 hsum[HW ? kSelBins : 1];
   unsigned w_key[kWinMax];
-  u64 w_plo[kWinMax], w_phi[kWinMax];
-  u64 w_hlo[HW ? kWinMax : 1], w_hhi[HW ? kWinMax : 1];
-  u64 a_plo[16], a_phi[16], a_hlo[16], a_hhi[16];  // per-wave exact partial sums
-  unsigned a_cnt[16];
-  u64 f_plo[16], f_phi[16], f_hlo[16], f_hhi[16];  // per-wave best threshold
-  unsigned f_cnt[16];
-  double f_s[16];
-  unsigned f_k[16];
-  double d_p[16], d_h[16];  // per-wave fp64 sums above a refined histogram's range
-  unsigned red_u[16];
-  double w_sp[16], w_sh[16];  // per-wave scan totals
+  u64 w_p[kWinMax];
+  u64 w_h[HW ? kWinMax : 1];
+  u64 a_p[16], a_h[16];  // per-wave sums (above a refined range; the distinct-key walk)
+  unsigned a_c[16];
+  u64 w_sp[16], w_sh[16];  // per-wave scan totals
   unsigned w_sc[16];
   double w_bn[16], w_bd[16];  // per-wave best boundary
   int w_lo[16], w_hi[16];     // per-wave candidate bin range
   unsigned w_clo[16], w_chi[16];
-  double bn, bd;              // best boundary score so far, as a fraction
+  u64 w_plo[16], w_hlo[16];   // sums over everything above bin lo
+  double f_s[16];             // per-wave best threshold
+  unsigned f_k[16], f_c[16];
+  u64 f_p[16], f_h[16];
+  unsigned red_u[16];
+  double bn, bd;  // best boundary score so far, as a fraction
   unsigned slot;
 };
 
 struct SelResult {
   unsigned tkey;   // support = eligible elements with key >= tkey
   unsigned ekey;   // eligibility: key >= ekey
-  double P, H;     // sum h|x| and sum h over the support (real units)
+  double P, H;     // sum h|x| and sum h over the support (real units, from the fixed point)
   unsigned count;  // support size (0: empty)
 };
 
 __device__ __forceinline__ bool better(double S1, unsigned k1, double S2, unsigned k2) {
   return S1 > S2 || (S1 == S2 && k1 > k2);
 }
+
+// floor(x * 2^sc) for finite x >= 0 whose result is below 2^63.
+__device__ __forceinline__ u64 fix64(double x, int sc) {
+  const u64 bits = (u64)__double_as_longlong(x);
+  const int ef = (int)((bits >> 52) & 0x7FF);
+  if (ef == 0) return 0ull;  // zero or subnormal: far below one unit
+  const u64 mant = (bits & 0xFFFFFFFFFFFFFull) | (1ull << 52);
+  const int sh = ef - 1075 + sc;
+  if (sh >= 0) return mant << sh;
+  return sh > -64 ? mant >> (-sh) : 0ull;
+}
+
+__device__ __forceinline__ u64 wave_scan_u64(u64 v) {
+#define EXTERND_STEP(C, R) v += dpp64<C, R>(v);
+  EXTERND_WAVE_STEPS(EXTERND_STEP)
+#undef EXTERND_STEP
+  return v;
+}
+__device__ __forceinline__ u64 wave_sum_u64(u64 v) { return readlane64(wave_scan_u64(v), 63); }
 
 // Whether a slot holding x is in the support of r.
 __device__ __forceinline__ bool selected(float x, const SelResult& r) {
@@ -86,8 +108,8 @@ __device__ __forceinline__ void select_prepare(SelScratchT<HW>& s, unsigned kx) 
   if (lane == 0) s.red_u[wid] = kx;
   for (int b = tid; b < kSelBins; b += NT) {
     s.cnt[b] = 0u;
-    s.psum[b] = 0.0;
-    if (HW) s.hsum[b] = 0.0;
+    s.psum[b] = 0ull;
+    if (HW) s.hsum[b] = 0ull;
   }
   if (tid == 0) {
     s.slot = 0u;
@@ -103,7 +125,7 @@ __device__ __forceinline__ void select_prepare(SelScratchT<HW>& s, unsigned kx) 
 // caller already ran select_prepare with the vector's largest key.
 template <int NT, bool W, typename T, bool HW, bool PRE = false>
 __device__ __forceinline__ SelResult ternary_select(const T* vals, const float* hl, int L, float tau, int EHm,
-                                    SelScratchT<HW>& s) {
+                                                    SelScratchT<HW>& s) {
   static_assert(HW || !W, "a weighted selection needs the weighted scratch");
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   constexpr int NW = NT / 64;
@@ -142,71 +164,91 @@ __device__ __forceinline__ SelResult ternary_select(const T* vals, const float* 
     const unsigned k = __float_as_uint((float)vals[i]) & 0x7FFFFFFFu;
     return k >= ekey ? k : 0u;
   };
+  // fixed-point scales (see the header)
+  const int LB = 32 - __clz((unsigned)L);
+  const int EM = exp_bound(M);
+  const int sP = 62 - EM - (W ? EHm : 0) - LB;
+  const int sH = 62 - EHm - LB;
+  auto pterm = [&](int i, unsigned k) -> u64 {
+    const double av = (double)__uint_as_float(k);
+    return fix64(W ? (double)hl[i] * av : av, sP);
+  };
+  auto hterm = [&](int i) -> u64 { return W ? fix64((double)hl[i], sH) : 1ull; };
+  // a key's value per unit of H, in P units: converts top * H_bin into P units
+  const double tconv = W ? ldexp(1.0, sP - sH) : ldexp(1.0, sP);
 
   // ---- histogram levels.  Level 0 covers keys <= km with bins of 2^17 keys (the last bin
   // catches the rest); a later level covers the previous window (wk_lo, wk_hi] at a finer shift.
   unsigned kt = km, klo = 0u, wk_hi = 0u, wk_lo = 0u;
   int sh = kSelShift0;
   int mode = 0;
+  u64 AP = 0ull, AH = 0ull;  // sums over everything above the window
+  unsigned AC = 0u;
   for (int level = 0; level < kSelLevels; ++level) {
     if (level > 0) {
       for (int b = tid; b < kSelBins; b += NT) {
         s.cnt[b] = 0u;
-        s.psum[b] = 0.0;
-        if (W) s.hsum[b] = 0.0;
+        s.psum[b] = 0ull;
+        if (W) s.hsum[b] = 0ull;
       }
       __syncthreads();
     }
     // Bin b is stored at (b % BPL) * NT + b / BPL so that thread t, which owns bins
     // BPL t .. BPL t + BPL - 1 in the scan below, reads consecutive addresses across lanes.
     constexpr int BPL = kSelBins / NT;
-    double dp = 0.0, dh = 0.0;  // fp64 sums above the range (level > 0)
+    u64 dp = 0ull, dh = 0ull;  // sums above the range (level > 0)
+    unsigned dc = 0u;
     for (int i = tid; i < L; i += NT) {
       const unsigned k = keyof(i);
       if (k == 0u || k <= klo) continue;
-      const double av = (double)__uint_as_float(k);
-      const double hw = W ? (double)hl[i] : 1.0;
+      const u64 pt = pterm(i, k), ht = hterm(i);
       if (k > kt) {
-        dp += hw * av;
-        dh += hw;
+        dp += pt;
+        dh += ht;
+        ++dc;
         continue;
       }
       unsigned b = (kt - k) >> sh;
       b = b > (unsigned)(kSelBins - 1) ? (unsigned)(kSelBins - 1) : b;
       const unsigned hb = (b % BPL) * NT + b / BPL;
       atomicAdd(&s.cnt[hb], 1u);
-      atomicAdd(&s.psum[hb], hw * av);
-      if (W) atomicAdd(&s.hsum[hb], hw);
+      atomicAdd(&s.psum[hb], pt);
+      if (W) atomicAdd(&s.hsum[hb], ht);
     }
     if (level > 0) {
-      dp = wave_sum_f64(dp);
-      dh = wave_sum_f64(dh);
+      dp = wave_sum_u64(dp);
+      dh = W ? wave_sum_u64(dh) : 0ull;
+      dc = wave_sum_u32(dc);
       if (lane == 0) {
-        s.d_p[wid] = dp;
-        s.d_h[wid] = dh;
+        s.a_p[wid] = dp;
+        s.a_h[wid] = dh;
+        s.a_c[wid] = dc;
       }
     }
     __syncthreads();
     // ---- all threads: prefix sums, boundary scores, interior bounds -> window of bins.  Scores
-    // are compared as fractions (num * den' vs num' * den) to avoid fp64 divisions.  Every thread
-    // ends with the same window (the cross-wave steps read the same LDS values in the same order).
-    double bp[BPL], bh[BPL];
+    // are compared as fractions (num * den' vs num' * den) to avoid divisions.  Every thread ends
+    // with the same window (the cross-wave steps read the same LDS values in the same order).
+    u64 bp[BPL], bh[BPL];
     unsigned bc[BPL];
 #pragma unroll
     for (int q = 0; q < BPL; ++q) {
       bc[q] = s.cnt[q * NT + tid];
       bp[q] = s.psum[q * NT + tid];
-      bh[q] = W ? s.hsum[q * NT + tid] : (double)bc[q];
+      bh[q] = W ? s.hsum[q * NT + tid] : (u64)bc[q];
     }
-    double P0 = 0.0, H0 = 0.0;
+    u64 P0 = 0ull, H0 = 0ull;
+    unsigned C0 = 0u;
     if (level > 0) {
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
-        P0 += s.d_p[w];
-        H0 += s.d_h[w];
+        P0 += s.a_p[w];
+        H0 += s.a_h[w];
+        C0 += s.a_c[w];
       }
+      if (!W) H0 = C0;
     }
-    double tp = 0.0, th = 0.0;
+    u64 tp = 0ull, th = 0ull;
     unsigned tc = 0u;
 #pragma unroll
     for (int q = 0; q < BPL; ++q) {
@@ -214,46 +256,48 @@ __device__ __forceinline__ SelResult ternary_select(const T* vals, const float* 
       th += bh[q];
       tc += bc[q];
     }
-    const double ip = wave_scan_f64(tp), ih = W ? wave_scan_f64(th) : 0.0;
+    const u64 ip = wave_scan_u64(tp);
     const unsigned ic = wave_scan_u32(tc);
+    const u64 ih = W ? wave_scan_u64(th) : (u64)ic;
     if (lane == 63) {
       s.w_sp[wid] = ip;
-      s.w_sh[wid] = W ? ih : (double)ic;
+      s.w_sh[wid] = ih;
       s.w_sc[wid] = ic;
     }
     __syncthreads();
-    double rp0 = P0, rh0 = H0;  // prefix before this thread's first bin
-    unsigned rc0 = 0u;
+    u64 rp0 = P0, rh0 = H0;  // sums before this thread's first bin
+    unsigned rc0 = C0;
     for (int w = 0; w < wid; ++w) {
       rp0 += s.w_sp[w];
       rh0 += s.w_sh[w];
       rc0 += s.w_sc[w];
     }
     rp0 += ip - tp;
-    rh0 += W ? ih - th : (double)(ic - tc);
+    rh0 += ih - th;
     rc0 += ic - tc;
     // best boundary score as a fraction bn / bd (carried over from earlier levels)
     double bn = s.bn, bd = s.bd;
     {
-      double rp = rp0, rh = rh0;
+      u64 rp = rp0, rh = rh0;
 #pragma unroll
       for (int q = 0; q < BPL; ++q) {
         rp += bp[q];
         rh += bh[q];
-        if (bc[q] != 0u && rp * rp * bd > bn * rh) {
-          bn = rp * rp;
-          bd = rh;
+        const double pd = (double)rp, hd = (double)rh;
+        if (bc[q] != 0u && pd * pd * bd > bn * hd) {
+          bn = pd * pd;
+          bd = hd;
         }
       }
     }
     // wave maximum (lane 63); a zero-filled operand (0, 0) never wins
-#define EXTERND_STEP(C, R)                                  \
-  {                                                         \
+#define EXTERND_STEP(C, R)                                     \
+  {                                                            \
     const double n2 = dppf64<C, R>(bn), d2 = dppf64<C, R>(bd); \
-    if (n2 * bd > bn * d2) {                                \
-      bn = n2;                                              \
-      bd = d2;                                              \
-    }                                                       \
+    if (n2 * bd > bn * d2) {                                   \
+      bn = n2;                                                 \
+      bd = d2;                                                 \
+    }                                                          \
   }
     EXTERND_WAVE_STEPS(EXTERND_STEP)
 #undef EXTERND_STEP
@@ -272,26 +316,30 @@ __device__ __forceinline__ SelResult ternary_select(const T* vals, const float* 
       }
     const double cutn = bn * (1.0 - 1e-9);  // candidate if score * bd >= cutn
     int lo = kSelBins, hi = -1;
-    unsigned clo = 0u, chi = 0u;  // element counts before bin lo / through bin hi
+    unsigned clo = 0u, chi = 0u;  // element counts above bin lo / through bin hi
+    u64 plo = 0ull, hlo = 0ull;   // sums above bin lo
     {
-      double rp = rp0, rh = rh0;
+      u64 rp = rp0, rh = rh0;
       unsigned rc = rc0;
 #pragma unroll
       for (int q = 0; q < BPL; ++q) {
         const int b = tid * BPL + q;
         const unsigned c = bc[q];
-        const double Pi = rp + bp[q], Hi = rh + bh[q];
-        bool cand = c != 0u && Pi * Pi * bd >= cutn * Hi;
+        const u64 Pi = rp + bp[q], Hi = rh + bh[q];
+        const double pid = (double)Pi, hid = (double)Hi, rpd = (double)rp, rhd = (double)rh;
+        bool cand = c != 0u && pid * pid * bd >= cutn * hid;
         if (!cand && c >= 2u) {
           const unsigned off = (unsigned)b << sh;
           const unsigned top = kt > off ? kt - off : 0u;  // largest key the bin can hold
-          const double t1 = rp + (double)__uint_as_float(top) * bh[q];
-          cand = t1 * t1 * bd >= cutn * Hi || (rh > 0.0 && rp * rp * bd >= cutn * rh);
+          const double t1 = rpd + (double)__uint_as_float(top) * tconv * (double)bh[q];
+          cand = t1 * t1 * bd >= cutn * hid || (rh > 0ull && rpd * rpd * bd >= cutn * rhd);
         }
         if (cand) {
           if (b < lo) {
             lo = b;
             clo = rc;
+            plo = rp;
+            hlo = rh;
           }
           if (b > hi) {
             hi = b;
@@ -303,22 +351,25 @@ __device__ __forceinline__ SelResult ternary_select(const T* vals, const float* 
         rc += c;
       }
     }
-    // wave minimum of lo and maximum of hi (lane 63), with their counts; encoded so that a
+    // wave minimum of lo and maximum of hi (lane 63), with their prefix sums; encoded so that a
     // zero-filled operand is neutral: xlo = kSelBins - lo, xhi = hi + 1
     {
       unsigned xlo = (unsigned)(kSelBins - lo), xhi = (unsigned)(hi + 1);
-#define EXTERND_STEP(C, R)                                                  \
-  {                                                                         \
-    const unsigned l2 = dpp32<C, R>(xlo), c2 = dpp32<C, R>(clo);              \
-    const unsigned h2 = dpp32<C, R>(xhi), d2 = dpp32<C, R>(chi);              \
-    if (l2 > xlo) {                                                         \
-      xlo = l2;                                                             \
-      clo = c2;                                                             \
-    }                                                                       \
-    if (h2 > xhi) {                                                         \
-      xhi = h2;                                                             \
-      chi = d2;                                                             \
-    }                                                                       \
+#define EXTERND_STEP(C, R)                                       \
+  {                                                              \
+    const unsigned l2 = dpp32<C, R>(xlo), c2 = dpp32<C, R>(clo); \
+    const u64 p2 = dpp64<C, R>(plo), q2 = dpp64<C, R>(hlo);      \
+    const unsigned h2 = dpp32<C, R>(xhi), d2 = dpp32<C, R>(chi); \
+    if (l2 > xlo) {                                              \
+      xlo = l2;                                                  \
+      clo = c2;                                                  \
+      plo = p2;                                                  \
+      hlo = q2;                                                  \
+    }                                                            \
+    if (h2 > xhi) {                                              \
+      xhi = h2;                                                  \
+      chi = d2;                                                  \
+    }                                                            \
   }
       EXTERND_WAVE_STEPS(EXTERND_STEP)
 #undef EXTERND_STEP
@@ -327,6 +378,8 @@ __device__ __forceinline__ SelResult ternary_select(const T* vals, const float* 
         s.w_hi[wid] = (int)xhi - 1;
         s.w_clo[wid] = clo;
         s.w_chi[wid] = chi;
+        s.w_plo[wid] = plo;
+        s.w_hlo[wid] = hlo;
       }
     }
     __syncthreads();
@@ -337,6 +390,8 @@ __device__ __forceinline__ SelResult ternary_select(const T* vals, const float* 
       if (s.w_lo[w] < lo) {
         lo = s.w_lo[w];
         clo = s.w_clo[w];
+        plo = s.w_plo[w];
+        hlo = s.w_hlo[w];
       }
       if (s.w_hi[w] > hi) {
         hi = s.w_hi[w];
@@ -344,6 +399,9 @@ __device__ __forceinline__ SelResult ternary_select(const T* vals, const float* 
       }
     }
     const unsigned nw = chi - clo;
+    AP = plo;
+    AH = hlo;
+    AC = clo;
     {
       const unsigned offlo = (unsigned)lo << sh;
       const unsigned whi = kt > offlo ? kt - offlo : 0u;
@@ -376,72 +434,24 @@ __device__ __forceinline__ SelResult ternary_select(const T* vals, const float* 
       sh = nsh;
     }
   }
-  const int EM = exp_bound(M);
-  const int scP = W ? (100 - EM - EHm) : (100 - EM);
-  const int scH = W ? (100 - EHm) : 0;
-  auto pterm = [&](int i, unsigned k) -> u128 {
-    const double av = (double)__uint_as_float(k);
-    return W ? fixp((double)hl[i] * av, scP) : fixp(av, scP);
-  };
-  auto hterm = [&](int i) -> u128 { return W ? fixp((double)hl[i], scH) : mk128(1ull, 0ull); };
-  // per-wave exact partials -> LDS -> every thread sums them in wave order
-  auto block_sum128 = [&](u128 p, u128 h, unsigned c, u128& P, u128& H, unsigned& C) {
-    p = wave_sum128(p);
-    if (W) h = wave_sum128(h);
-    c = wave_sum_u32(c);
-    __syncthreads();
-    if (lane == 0) {
-      s.a_plo[wid] = p.lo;
-      s.a_phi[wid] = p.hi;
-      s.a_hlo[wid] = h.lo;
-      s.a_hhi[wid] = h.hi;
-      s.a_cnt[wid] = c;
-    }
-    __syncthreads();
-    P = mk128(0, 0);
-    H = mk128(0, 0);
-    C = 0u;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      P = add128(P, mk128(s.a_plo[w], s.a_phi[w]));
-      if (W) H = add128(H, mk128(s.a_hlo[w], s.a_hhi[w]));
-      C += s.a_cnt[w];
-    }
-  };
-  // ---- one pass: exact sums above the window and, to be scored, the window's elements
-  u128 AP, AH;
-  unsigned AC;
-  {
-    u128 p = mk128(0, 0), h = mk128(0, 0);
-    unsigned c = 0u;
+  // ---- the window's elements into LDS
+  if (mode == 1) {
     for (int i = tid; i < L; i += NT) {
       const unsigned k = keyof(i);
-      if (k == 0u || k <= wk_lo) continue;
-      if (k > wk_hi) {
-        p = add128(p, pterm(i, k));
-        if (W) h = add128(h, hterm(i));
-        ++c;
-      } else if (mode == 1) {
+      if (k != 0u && k > wk_lo && k <= wk_hi) {
         const unsigned slot = atomicAdd(&s.slot, 1u);
         if (slot < (unsigned)kWinMax) {
-          const u128 pe = pterm(i, k);
           s.w_key[slot] = k;
-          s.w_plo[slot] = pe.lo;
-          s.w_phi[slot] = pe.hi;
-          if (W) {
-            const u128 he = hterm(i);
-            s.w_hlo[slot] = he.lo;
-            s.w_hhi[slot] = he.hi;
-          }
+          s.w_p[slot] = pterm(i, k);
+          if (W) s.w_h[slot] = hterm(i);
         }
       }
     }
-    block_sum128(p, h, c, AP, AH, AC);  // its barriers also publish the window
+    __syncthreads();
   }
   double myS = -1.0;
-  unsigned myK = 0u;
-  u128 myP = mk128(0, 0), myH = mk128(0, 0);
-  unsigned myC = 0u;
+  unsigned myK = 0u, myC = 0u;
+  u64 myP = 0ull, myH = 0ull;
   if (mode == 1) {
     // wave w scores window elements 64 w .. 64 w + 63 against every window element
     const unsigned ns = s.slot;
@@ -449,33 +459,29 @@ __device__ __forceinline__ SelResult ternary_select(const T* vals, const float* 
     const int e = wid * 64 + lane;
     if (wid * 64 < nwin) {
       const unsigned ke = e < nwin ? s.w_key[e] : 0xFFFFFFFFu;
-      u128 P = AP, H = AH;
+      u64 P = AP, H = AH;
       unsigned C = AC;
 #pragma unroll 4
       for (int j = 0; j < nwin; ++j) {
         const unsigned kj = s.w_key[j];
-        const u64 plo = s.w_plo[j], phi = s.w_phi[j];
         const bool in = kj >= ke;
-        P = add128(P, mk128(in ? plo : 0ull, in ? phi : 0ull));
-        if (W) {
-          const u64 hlo = s.w_hlo[j], hhi = s.w_hhi[j];
-          H = add128(H, mk128(in ? hlo : 0ull, in ? hhi : 0ull));
-        }
+        P += in ? s.w_p[j] : 0ull;
+        if (W) H += in ? s.w_h[j] : 0ull;
         C += in ? 1u : 0u;
       }
       if (e < nwin) {
-        const double Pd = to_double(P);
-        const double Hd = W ? to_double(H) : (double)C;
+        const double Pd = (double)P;
+        const double Hd = W ? (double)H : (double)C;
         myS = Pd * Pd / Hd;
         myK = ke;
         myP = P;
-        myH = H;
+        myH = W ? H : (u64)C;
         myC = C;
       }
     }
   } else {
     // Many window elements with few distinct keys (heavy ties): walk the distinct keys
-    // downwards and score each with an exact block reduction.
+    // downwards and score each with a block reduction.
     unsigned prev = wk_hi + 1u;
     for (;;) {
       unsigned best = 0u;
@@ -491,25 +497,37 @@ __device__ __forceinline__ SelResult ternary_select(const T* vals, const float* 
 #pragma unroll
       for (int w = 0; w < NW; ++w) best = s.red_u[w] > best ? s.red_u[w] : best;
       if (best == 0u) break;
-      u128 p = mk128(0, 0), h = mk128(0, 0);
+      u64 p = 0ull, h = 0ull;
       unsigned c = 0u;
       for (int i = tid; i < L; i += NT) {
         const unsigned k = keyof(i);
         if (k >= best && k <= wk_hi) {
-          p = add128(p, pterm(i, k));
-          if (W) h = add128(h, hterm(i));
+          p += pterm(i, k);
+          if (W) h += hterm(i);
           ++c;
         }
       }
-      u128 P, H;
-      unsigned C;
-      block_sum128(p, h, c, P, H, C);
-      P = add128(P, AP);
-      if (W) H = add128(H, AH);
-      C += AC;
-      const double Pd = to_double(P);
-      const double Hd = W ? to_double(H) : (double)C;
-      const double St = Pd * Pd / Hd;
+      p = wave_sum_u64(p);
+      h = W ? wave_sum_u64(h) : 0ull;
+      c = wave_sum_u32(c);
+      __syncthreads();
+      if (lane == 0) {
+        s.a_p[wid] = p;
+        s.a_h[wid] = h;
+        s.a_c[wid] = c;
+      }
+      __syncthreads();
+      u64 P = AP, H = AH;
+      unsigned C = AC;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        P += s.a_p[w];
+        H += s.a_h[w];
+        C += s.a_c[w];
+      }
+      if (!W) H = C;
+      const double Pd = (double)P;
+      const double St = Pd * Pd / (double)H;
       if (tid == 0 && better(St, best, myS, myK)) {  // tracked by thread 0 only
         myS = St;
         myK = best;
@@ -524,15 +542,15 @@ __device__ __forceinline__ SelResult ternary_select(const T* vals, const float* 
   // operand, score 0, loses to every real threshold), then across waves.  Lanes with equal
   // (score, key) hold equal sums.
   int src = lane;
-#define EXTERND_STEP(C, R)                                                               \
-  {                                                                                      \
-    const double S2 = dppf64<C, R>(myS);                                                 \
-    const unsigned k2 = dpp32<C, R>(myK), s2 = dpp32<C, R>((unsigned)src);                \
-    if (better(S2, k2, myS, myK)) {                                                      \
-      myS = S2;                                                                          \
-      myK = k2;                                                                          \
-      src = (int)s2;                                                                     \
-    }                                                                                    \
+#define EXTERND_STEP(C, R)                                                 \
+  {                                                                        \
+    const double S2 = dppf64<C, R>(myS);                                   \
+    const unsigned k2 = dpp32<C, R>(myK), s2 = dpp32<C, R>((unsigned)src); \
+    if (better(S2, k2, myS, myK)) {                                        \
+      myS = S2;                                                            \
+      myK = k2;                                                            \
+      src = (int)s2;                                                       \
+    }                                                                      \
   }
   EXTERND_WAVE_STEPS(EXTERND_STEP)
 #undef EXTERND_STEP
@@ -540,17 +558,14 @@ __device__ __forceinline__ SelResult ternary_select(const T* vals, const float* 
   myK = readlane32(myK, 63);
   src = (int)readlane32((unsigned)src, 63);
   {
-    const u64 plo = readlane64(myP.lo, src), phi = readlane64(myP.hi, src);
-    const u64 hlo = readlane64(myH.lo, src), hhi = readlane64(myH.hi, src);
-    const unsigned cc = __builtin_amdgcn_readlane(myC, src);
+    const u64 pp = readlane64(myP, src), hh = readlane64(myH, src);
+    const unsigned cc = readlane32(myC, src);
     if (lane == 0) {
       s.f_s[wid] = myS;
       s.f_k[wid] = myK;
-      s.f_plo[wid] = plo;
-      s.f_phi[wid] = phi;
-      s.f_hlo[wid] = hlo;
-      s.f_hhi[wid] = hhi;
-      s.f_cnt[wid] = cc;
+      s.f_p[wid] = pp;
+      s.f_h[wid] = hh;
+      s.f_c[wid] = cc;
     }
   }
   __syncthreads();
@@ -565,9 +580,9 @@ __device__ __forceinline__ SelResult ternary_select(const T* vals, const float* 
       bw = w;
     }
   out.tkey = K;
-  out.count = s.f_cnt[bw];
-  out.P = ldexp(to_double(mk128(s.f_plo[bw], s.f_phi[bw])), -scP);
-  out.H = W ? ldexp(to_double(mk128(s.f_hlo[bw], s.f_hhi[bw])), -scH) : (double)out.count;
+  out.count = s.f_c[bw];
+  out.P = ldexp((double)s.f_p[bw], -sP);
+  out.H = W ? ldexp((double)s.f_h[bw], -sH) : (double)out.count;
   __syncthreads();
   return out;
 }

@@ -175,8 +175,10 @@ def test_projection_matches_oracle():
                     if gap > 1e-12:
                         assert np.array_equal(V[r], v), (L, tau, hh is None, r)
                         assert PHC[r, 2] == jo
-                        assert PHC[r, 0] == pytest.approx(Po, rel=1e-12)
-                        assert PHC[r, 1] == pytest.approx(Ho, rel=1e-12)
+                        # the reported sums come from the selection's 64-bit fixed point:
+                        # each element is truncated by < 2^-47 of max h|x|
+                        assert PHC[r, 0] == pytest.approx(Po, rel=1e-9)
+                        assert PHC[r, 1] == pytest.approx(Ho, rel=1e-9)
 
 
 def test_projection_adversarial():
