@@ -351,35 +351,22 @@ __device__ __forceinline__ SelResult ternary_select(const T* vals, const float* 
         rc += c;
       }
     }
-    // wave minimum of lo and maximum of hi (lane 63), with their prefix sums; encoded so that a
-    // zero-filled operand is neutral: xlo = kSelBins - lo, xhi = hi + 1
+    // wave minimum of lo and maximum of hi, then their prefix sums from the lanes that hold them
+    // (thread t holds bins BPL t .. BPL t + BPL - 1)
     {
-      unsigned xlo = (unsigned)(kSelBins - lo), xhi = (unsigned)(hi + 1);
-#define EXTERND_STEP(C, R)                                       \
-  {                                                              \
-    const unsigned l2 = dpp32<C, R>(xlo), c2 = dpp32<C, R>(clo); \
-    const u64 p2 = dpp64<C, R>(plo), q2 = dpp64<C, R>(hlo);      \
-    const unsigned h2 = dpp32<C, R>(xhi), d2 = dpp32<C, R>(chi); \
-    if (l2 > xlo) {                                              \
-      xlo = l2;                                                  \
-      clo = c2;                                                  \
-      plo = p2;                                                  \
-      hlo = q2;                                                  \
-    }                                                            \
-    if (h2 > xhi) {                                              \
-      xhi = h2;                                                  \
-      chi = d2;                                                  \
-    }                                                            \
-  }
-      EXTERND_WAVE_STEPS(EXTERND_STEP)
-#undef EXTERND_STEP
-      if (lane == 63) {
-        s.w_lo[wid] = kSelBins - (int)xlo;
-        s.w_hi[wid] = (int)xhi - 1;
-        s.w_clo[wid] = clo;
-        s.w_chi[wid] = chi;
-        s.w_plo[wid] = plo;
-        s.w_hlo[wid] = hlo;
+      const int wlo = kSelBins - (int)wave_max_u32((unsigned)(kSelBins - lo));
+      const int whi = (int)wave_max_u32((unsigned)(hi + 1)) - 1;
+      const int llo = wlo < kSelBins ? wlo / BPL - wid * 64 : 0;
+      const int lhi = whi >= 0 ? whi / BPL - wid * 64 : 0;
+      const unsigned c_lo = readlane32(clo, llo), c_hi = readlane32(chi, lhi);
+      const u64 p_lo = readlane64(plo, llo), h_lo = readlane64(hlo, llo);
+      if (lane == 0) {
+        s.w_lo[wid] = wlo;
+        s.w_hi[wid] = whi;
+        s.w_clo[wid] = c_lo;
+        s.w_chi[wid] = c_hi;
+        s.w_plo[wid] = p_lo;
+        s.w_hlo[wid] = h_lo;
       }
     }
     __syncthreads();
@@ -453,31 +440,51 @@ __device__ __forceinline__ SelResult ternary_select(const T* vals, const float* 
   unsigned myK = 0u, myC = 0u;
   u64 myP = 0ull, myH = 0ull;
   if (mode == 1) {
-    // wave w scores window elements 64 w .. 64 w + 63 against every window element
+    // Element e's threshold sums P_e = AP + sum of w_p[j] over window elements j with
+    // w_key[j] >= w_key[e].  The window's elements come in nch chunks of 64 (one per lane); each
+    // chunk's j range is split into NW / nch parts, one wave per (chunk, part), whose partial sums
+    // go to the (now free) bin arrays.  The waves of the first nch then add the parts in order.
     const unsigned ns = s.slot;
     const int nwin = ns < (unsigned)kWinMax ? (int)ns : kWinMax;
-    const int e = wid * 64 + lane;
-    if (wid * 64 < nwin) {
+    const int nch = nwin > 64 ? (nwin + 63) >> 6 : 1;
+    const int parts = NW / nch;
+    const int span = (nwin + parts - 1) / parts;
+    const int ch = wid % nch, part = wid / nch;
+    const int e = ch * 64 + lane;
+    if (part < parts) {
       const unsigned ke = e < nwin ? s.w_key[e] : 0xFFFFFFFFu;
-      u64 P = AP, H = AH;
-      unsigned C = AC;
+      const int j0 = part * span, j1 = j0 + span < nwin ? j0 + span : nwin;
+      u64 P = 0ull, H = 0ull;
+      unsigned C = 0u;
 #pragma unroll 4
-      for (int j = 0; j < nwin; ++j) {
-        const unsigned kj = s.w_key[j];
-        const bool in = kj >= ke;
+      for (int j = j0; j < j1; ++j) {
+        const bool in = s.w_key[j] >= ke;
         P += in ? s.w_p[j] : 0ull;
         if (W) H += in ? s.w_h[j] : 0ull;
         C += in ? 1u : 0u;
       }
-      if (e < nwin) {
-        const double Pd = (double)P;
-        const double Hd = W ? (double)H : (double)C;
-        myS = Pd * Pd / Hd;
-        myK = ke;
-        myP = P;
-        myH = W ? H : (u64)C;
-        myC = C;
+      const int slot = part * (nch * 64) + e;
+      s.psum[slot] = P;
+      if (W) s.hsum[slot] = H;
+      s.cnt[slot] = C;
+    }
+    __syncthreads();
+    if (wid < nch && e < nwin) {
+      u64 P = AP, H = AH;
+      unsigned C = AC;
+      for (int q = 0; q < parts; ++q) {
+        const int slot = q * (nch * 64) + e;
+        P += s.psum[slot];
+        if (W) H += s.hsum[slot];
+        C += s.cnt[slot];
       }
+      const double Pd = (double)P;
+      const double Hd = W ? (double)H : (double)C;
+      myS = Pd * Pd / Hd;
+      myK = s.w_key[e];
+      myP = P;
+      myH = W ? H : (u64)C;
+      myC = C;
     }
   } else {
     // Many window elements with few distinct keys (heavy ties): walk the distinct keys
