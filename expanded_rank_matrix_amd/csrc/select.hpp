@@ -84,6 +84,16 @@ __device__ __forceinline__ u64 fix64(double x, int sc) {
   return sh > -64 ? mant >> (-sh) : 0ull;
 }
 
+// floor(value * 2^sc) for the positive finite fp32 bit pattern k, whose result is below 2^63
+// (the same value as fix64 of its exact double).
+__device__ __forceinline__ u64 fixkey(unsigned k, int sc) {
+  const unsigned ex = k >> 23;
+  const u64 mant = (u64)((k & 0x7FFFFFu) | (ex != 0u ? 0x800000u : 0u));
+  const int sh = (int)(ex != 0u ? ex : 1u) - 150 + sc;
+  const u64 up = mant << (sh & 63), dn = mant >> ((-sh) & 63);
+  return sh >= 0 ? up : (sh > -64 ? dn : 0ull);
+}
+
 __device__ __forceinline__ u64 wave_scan_u64(u64 v) {
 #define EXTERND_STEP(C, R) v += dpp64<C, R>(v);
   EXTERND_WAVE_STEPS(EXTERND_STEP)
@@ -170,10 +180,13 @@ __device__ __forceinline__ SelResult ternary_select(const T* vals, const float* 
   const int sP = 62 - EM - (W ? EHm : 0) - LB;
   const int sH = 62 - EHm - LB;
   auto pterm = [&](int i, unsigned k) -> u64 {
-    const double av = (double)__uint_as_float(k);
-    return fix64(W ? (double)hl[i] * av : av, sP);
+    if (!W) return fixkey(k, sP);
+    return fix64((double)hl[i] * (double)__uint_as_float(k), sP);
   };
   auto hterm = [&](int i) -> u64 { return W ? fix64((double)hl[i], sH) : 1ull; };
+  // Passes over the vector take kGrp elements per thread at a time, loading them all first so
+  // that their latencies overlap.
+  constexpr int kGrp = 4;
   // a key's value per unit of H, in P units: converts top * H_bin into P units
   const double tconv = W ? ldexp(1.0, sP - sH) : ldexp(1.0, sP);
 
@@ -198,22 +211,29 @@ __device__ __forceinline__ SelResult ternary_select(const T* vals, const float* 
     constexpr int BPL = kSelBins / NT;
     u64 dp = 0ull, dh = 0ull;  // sums above the range (level > 0)
     unsigned dc = 0u;
-    for (int i = tid; i < L; i += NT) {
-      const unsigned k = keyof(i);
-      if (k == 0u || k <= klo) continue;
-      const u64 pt = pterm(i, k), ht = hterm(i);
-      if (k > kt) {
-        dp += pt;
-        dh += ht;
-        ++dc;
-        continue;
+    for (int i0 = tid; i0 < L; i0 += kGrp * NT) {
+      unsigned kk[kGrp];
+#pragma unroll
+      for (int u = 0; u < kGrp; ++u) kk[u] = i0 + u * NT < L ? keyof(i0 + u * NT) : 0u;
+#pragma unroll
+      for (int u = 0; u < kGrp; ++u) {
+        const unsigned k = kk[u];
+        const int i = i0 + u * NT;
+        if (k == 0u || k <= klo) continue;
+        const u64 pt = pterm(i, k), ht = hterm(i);
+        if (k > kt) {
+          dp += pt;
+          dh += ht;
+          ++dc;
+          continue;
+        }
+        unsigned b = (kt - k) >> sh;
+        b = b > (unsigned)(kSelBins - 1) ? (unsigned)(kSelBins - 1) : b;
+        const unsigned hb = (b % BPL) * NT + b / BPL;
+        atomicAdd(&s.cnt[hb], 1u);
+        atomicAdd(&s.psum[hb], pt);
+        if (W) atomicAdd(&s.hsum[hb], ht);
       }
-      unsigned b = (kt - k) >> sh;
-      b = b > (unsigned)(kSelBins - 1) ? (unsigned)(kSelBins - 1) : b;
-      const unsigned hb = (b % BPL) * NT + b / BPL;
-      atomicAdd(&s.cnt[hb], 1u);
-      atomicAdd(&s.psum[hb], pt);
-      if (W) atomicAdd(&s.hsum[hb], ht);
     }
     if (level > 0) {
       dp = wave_sum_u64(dp);
@@ -267,10 +287,13 @@ __device__ __forceinline__ SelResult ternary_select(const T* vals, const float* 
     __syncthreads();
     u64 rp0 = P0, rh0 = H0;  // sums before this thread's first bin
     unsigned rc0 = C0;
-    for (int w = 0; w < wid; ++w) {
-      rp0 += s.w_sp[w];
-      rh0 += s.w_sh[w];
-      rc0 += s.w_sc[w];
+#pragma unroll
+    for (int w = 0; w < NW - 1; ++w) {  // all loads issued together, then masked
+      const u64 p = s.w_sp[w], h = s.w_sh[w];
+      const unsigned c = s.w_sc[w];
+      rp0 += w < wid ? p : 0ull;
+      rh0 += w < wid ? h : 0ull;
+      rc0 += w < wid ? c : 0u;
     }
     rp0 += ip - tp;
     rh0 += ih - th;
@@ -372,19 +395,19 @@ __device__ __forceinline__ SelResult ternary_select(const T* vals, const float* 
     __syncthreads();
     lo = kSelBins;
     hi = -1;
+    int low = 0, hiw = 0;
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
-      if (s.w_lo[w] < lo) {
-        lo = s.w_lo[w];
-        clo = s.w_clo[w];
-        plo = s.w_plo[w];
-        hlo = s.w_hlo[w];
-      }
-      if (s.w_hi[w] > hi) {
-        hi = s.w_hi[w];
-        chi = s.w_chi[w];
-      }
+      const int l = s.w_lo[w], h = s.w_hi[w];
+      low = l < lo ? w : low;
+      lo = l < lo ? l : lo;
+      hiw = h > hi ? w : hiw;
+      hi = h > hi ? h : hi;
     }
+    clo = s.w_clo[low];
+    plo = s.w_plo[low];
+    hlo = s.w_hlo[low];
+    chi = s.w_chi[hiw];
     const unsigned nw = chi - clo;
     AP = plo;
     AH = hlo;
@@ -423,14 +446,21 @@ __device__ __forceinline__ SelResult ternary_select(const T* vals, const float* 
   }
   // ---- the window's elements into LDS
   if (mode == 1) {
-    for (int i = tid; i < L; i += NT) {
-      const unsigned k = keyof(i);
-      if (k != 0u && k > wk_lo && k <= wk_hi) {
-        const unsigned slot = atomicAdd(&s.slot, 1u);
-        if (slot < (unsigned)kWinMax) {
-          s.w_key[slot] = k;
-          s.w_p[slot] = pterm(i, k);
-          if (W) s.w_h[slot] = hterm(i);
+    for (int i0 = tid; i0 < L; i0 += kGrp * NT) {
+      unsigned kk[kGrp];
+#pragma unroll
+      for (int u = 0; u < kGrp; ++u) kk[u] = i0 + u * NT < L ? keyof(i0 + u * NT) : 0u;
+#pragma unroll
+      for (int u = 0; u < kGrp; ++u) {
+        const unsigned k = kk[u];
+        if (k != 0u && k > wk_lo && k <= wk_hi) {
+          const int i = i0 + u * NT;
+          const unsigned slot = atomicAdd(&s.slot, 1u);
+          if (slot < (unsigned)kWinMax) {
+            s.w_key[slot] = k;
+            s.w_p[slot] = pterm(i, k);
+            if (W) s.w_h[slot] = hterm(i);
+          }
         }
       }
     }
@@ -472,11 +502,14 @@ __device__ __forceinline__ SelResult ternary_select(const T* vals, const float* 
     if (wid < nch && e < nwin) {
       u64 P = AP, H = AH;
       unsigned C = AC;
-      for (int q = 0; q < parts; ++q) {
-        const int slot = q * (nch * 64) + e;
-        P += s.psum[slot];
-        if (W) H += s.hsum[slot];
-        C += s.cnt[slot];
+#pragma unroll
+      for (int q = 0; q < NW; ++q) {  // all loads issued together, then masked
+        const int slot = (q < parts ? q : 0) * (nch * 64) + e;
+        const u64 pq = s.psum[slot], hq = W ? s.hsum[slot] : 0ull;
+        const unsigned cq = s.cnt[slot];
+        P += q < parts ? pq : 0ull;
+        if (W) H += q < parts ? hq : 0ull;
+        C += q < parts ? cq : 0u;
       }
       const double Pd = (double)P;
       const double Hd = W ? (double)H : (double)C;

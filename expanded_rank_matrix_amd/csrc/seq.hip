@@ -66,7 +66,7 @@ __host__ __device__ inline SeqLds seq_lds_layout(int m, int n, bool weighted, in
   const size_t L = (size_t)(m > n ? m : n);
   const size_t n4 = (size_t)((n + 3) & ~3), m4 = (size_t)((m + 3) & ~3);
   const size_t wm = (size_t)((m + 15) / 16), wn = (size_t)((n + 15) / 16);
-  const size_t parts = 8 * 16;  // per-wave row sums of the matvec (waves x rows reduced together)
+  const size_t parts = 8 * 16;  // matvec segment sums (at least kMvPart)
   SeqLds s;
   s.dl = al16(weighted ? sizeof(SelScratchT<true>) : sizeof(SelScratchT<false>));
   s.hl = al16(s.dl + 8 * L);
@@ -101,117 +101,120 @@ struct PackOut {
 
 // Rows [r0, r1) of a row-major matrix (leading dimension ld floats, len4 float4 per row) dotted
 // with a packed ternary vector pk_w (times the LDS weights hl when given); the results go to
-// out[row] (exchange buffer, device-coherent stores).  Column-stationary: thread t owns the
-// float4 columns t, t + NT, ... of every row, so it decodes its ternary weights (and the pending
-// component's codes) once and reuses them for all rows; loads of kRC rows are issued together.
-// A row's sum is the thread partials (fixed order), a DPP wave sum, then the wave sums in wave
-// order: deterministic.  Pending deflation of rows whose own code in pk_own is nonzero is fused
-// in: x <- fl32(x - own * other * d) where pk_other is nonzero, written back.
-constexpr int kQMax = 8;   // float4 columns per thread: len4 <= kQMax * NT (n <= 16384 at 512 threads)
-constexpr int kQC = 2;     // float4 columns per thread handled per pass over the rows
-constexpr int kRC = 4;     // rows whose loads are issued together
-constexpr int kRS = 16;    // rows reduced together
-__device__ __forceinline__ float4 decode4(const uint32_t* pk, int q) {
-  const unsigned b = (pk[q >> 2] >> ((q & 3) * 8)) & 0xFFu;
-  float c[4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const unsigned cd = (b >> (2 * t)) & 3u;
-    c[t] = cd == 0u ? 0.0f : (cd == 1u ? 1.0f : -1.0f);
-  }
-  return make_float4(c[0], c[1], c[2], c[3]);
-}
+// out[row] (exchange buffer, device-coherent stores).  Each row is split into S column segments
+// (S a power of two, chosen so that the R x S (row, segment) items spread evenly over the waves);
+// wave w owns segment w % S of rows w / S, w / S + waves / S, ...  A lane covers float4 columns
+// lane, lane + 64, ... of its segment, decodes their weights once per chunk of kQL columns and
+// reuses them for up to kRW rows.  A row's sum is fixed-order: lane partials, a DPP wave sum,
+// then the segments in order: deterministic, with one barrier only when S > 1.  Pending deflation
+// of rows whose own code in pk_own is nonzero is fused in: x <- fl32(x - own * other * d) where
+// pk_other is nonzero, written back by the wave that owns the (row, segment).
+constexpr int kQMax = 8;    // longest row accepted: len4 <= kQMax * 512 float4 (n <= 16384)
+constexpr int kQL = 5;     // float4 columns per lane per chunk
+constexpr int kRW = 4;     // rows of one wave handled together
+constexpr int kMvPart = 8 * 16;  // LDS doubles for the segment sums (needs R * S <= 3 * waves)
+// The 2-bit code at bit offset off of word (0, 1 or 3 = -1) as -1, 0, 1: a signed bit-field
+// extract.
+__device__ __forceinline__ int code2(unsigned word, int off) { return __builtin_amdgcn_sbfe(word, off, 2); }
 template <int NT>
 __device__ __forceinline__ void slab_matvec(float* base, int row_base, int ld, int len4, int r0, int r1,
                                             const uint32_t* pk_w, const float* hl, bool apply,
                                             const uint32_t* pk_own, const uint32_t* pk_other, float d,
                                             double* part, double* out) {
   constexpr int NW = NT / 64;
+  static_assert(kMvPart >= 3 * NW, "segment sums need 3 x waves doubles");
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int nqc = (len4 + kQC * NT - 1) / (kQC * NT);  // column passes
-  for (int rs = r0; rs < r1; rs += kRS) {
-    double acc[kRS];
+  const int R = r1 - r0;
+  if (R <= 0) return;
+  int S = 1;
+  while (S < NW && R * (2 * S) <= 3 * NW) S *= 2;
+  const int seg = wid % S, rw0 = wid / S, rstep = NW / S;
+  const int segq = (len4 + S - 1) / S;
+  const int qb = seg * segq, qe = min(len4, qb + segq);
+  const int mine = R > rw0 ? (R - rw0 + rstep - 1) / rstep : 0;  // rows r0 + rw0 + rstep * j
+  for (int j0 = 0; j0 < mine; j0 += kRW) {
+    const int nr = min(kRW, mine - j0);
+    int oc[kRW];
 #pragma unroll
-    for (int k = 0; k < kRS; ++k) acc[k] = 0.0;
-    for (int qc = 0; qc < nqc; ++qc) {
-      double w[kQC][4];  // code (times h): exact in fp64, so fma(x, w, acc) = acc + x w rounded once
-      float4 od[kQC];
+    for (int k = 0; k < kRW; ++k) oc[k] = (apply && k < nr) ? code_at(pk_own, r0 + rw0 + rstep * (j0 + k)) : 0;
+    double acc[kRW];
 #pragma unroll
-      for (int qi = 0; qi < kQC; ++qi) {
-        const int q = tid + (qc * kQC + qi) * NT;
-        float4 wf = make_float4(0.f, 0.f, 0.f, 0.f);
-        od[qi] = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (q < len4) {
-          wf = decode4(pk_w, q);
-          if (hl) {
-            const float4 h = reinterpret_cast<const float4*>(hl)[q];
-            wf = make_float4(wf.x * h.x, wf.y * h.y, wf.z * h.z, wf.w * h.w);
-          }
-          if (apply) {
-            const float4 o = decode4(pk_other, q);
-            od[qi] = make_float4(d * o.x, d * o.y, d * o.z, d * o.w);
-          }
+    for (int k = 0; k < kRW; ++k) acc[k] = 0.0;
+    for (int q0 = qb; q0 < qe; q0 += 64 * kQL) {
+      double w[kQL][4];
+      float od[kQL][4];
+#pragma unroll
+      for (int qi = 0; qi < kQL; ++qi) {
+        const int q = q0 + lane + 64 * qi;
+        const bool ok = q < qe;
+        const unsigned word = ok ? pk_w[q >> 2] : 0u;
+        const int off = (q & 3) * 8;
+        float4 h = make_float4(1.f, 1.f, 1.f, 1.f);
+        if (hl && ok) h = reinterpret_cast<const float4*>(hl)[q];
+        const float hh[4] = {h.x, h.y, h.z, h.w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const double c = (double)code2(word, off + 2 * t);
+          w[qi][t] = hl ? c * (double)hh[t] : c;
         }
-        w[qi][0] = (double)wf.x;
-        w[qi][1] = (double)wf.y;
-        w[qi][2] = (double)wf.z;
-        w[qi][3] = (double)wf.w;
+        if (apply) {
+          const unsigned ow = ok ? pk_other[q >> 2] : 0u;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) od[qi][t] = d * (float)code2(ow, off + 2 * t);
+        }
       }
 #pragma unroll
-      for (int rc = 0; rc < kRS; rc += kRC) {
-        if (rs + rc >= r1) break;  // uniform
-        float4 x[kRC][kQC];
+      for (int k = 0; k < kRW; ++k) {
+        if (k >= nr) break;  // uniform within the wave
+        const int row = r0 + rw0 + rstep * (j0 + k);
+        float4* r4 = reinterpret_cast<float4*>(base + (size_t)(row - row_base) * ld);
+        float4 x[kQL];
 #pragma unroll
-        for (int k = 0; k < kRC; ++k) {
-          const int row = rs + rc + k;
-          const float4* r4 = reinterpret_cast<const float4*>(base + (size_t)(row - row_base) * ld);
-#pragma unroll
-          for (int qi = 0; qi < kQC; ++qi) {
-            const int q = tid + (qc * kQC + qi) * NT;
-            x[k][qi] = (row < r1 && q < len4) ? r4[q] : make_float4(0.f, 0.f, 0.f, 0.f);
-          }
+        for (int qi = 0; qi < kQL; ++qi) {
+          const int q = q0 + lane + 64 * qi;
+          x[qi] = q < qe ? r4[q] : make_float4(0.f, 0.f, 0.f, 0.f);
         }
+        double a0 = 0.0, a1 = 0.0;
 #pragma unroll
-        for (int k = 0; k < kRC; ++k) {
-          const int row = rs + rc + k;
-          if (row >= r1) break;  // uniform
-          const int oc = apply ? code_at(pk_own, row) : 0;
-          float4* r4 = reinterpret_cast<float4*>(base + (size_t)(row - row_base) * ld);
-          double a0 = 0.0, a1 = 0.0;
+        for (int qi = 0; qi < kQL; ++qi) {
+          float v[4] = {x[qi].x, x[qi].y, x[qi].z, x[qi].w};
+          if (oc[k] != 0) {  // uniform within the wave
+            const float sg = oc[k] > 0 ? -1.0f : 1.0f;
+            bool any = false;
 #pragma unroll
-          for (int qi = 0; qi < kQC; ++qi) {
-            const int q = tid + (qc * kQC + qi) * NT;
-            float4 v = x[k][qi];
-            if (oc != 0) {  // uniform across the workgroup
-              const float sg = oc > 0 ? -1.0f : 1.0f;
-              const float4 o = od[qi];
-              v = make_float4(fmaf(sg, o.x, v.x), fmaf(sg, o.y, v.y), fmaf(sg, o.z, v.z), fmaf(sg, o.w, v.w));
-              if (q < len4 && (o.x != 0.0f || o.y != 0.0f || o.z != 0.0f || o.w != 0.0f)) r4[q] = v;
+            for (int t = 0; t < 4; ++t) {
+              v[t] = fmaf(sg, od[qi][t], v[t]);
+              any = any || od[qi][t] != 0.0f;
             }
-            a0 = fma((double)v.x, w[qi][0], a0);
-            a1 = fma((double)v.y, w[qi][1], a1);
-            a0 = fma((double)v.z, w[qi][2], a0);
-            a1 = fma((double)v.w, w[qi][3], a1);
+            const int q = q0 + lane + 64 * qi;
+            if (q < qe && any) r4[q] = make_float4(v[0], v[1], v[2], v[3]);
           }
-          acc[rc + k] += a0 + a1;
+          a0 = fma((double)v[0], w[qi][0], a0);
+          a1 = fma((double)v[1], w[qi][1], a1);
+          a0 = fma((double)v[2], w[qi][2], a0);
+          a1 = fma((double)v[3], w[qi][3], a1);
         }
+        acc[k] += a0 + a1;
       }
     }
-    // per-row block sums: DPP wave sums, then the waves in order
 #pragma unroll
-    for (int k = 0; k < kRS; ++k) {
-      if (rs + k >= r1) break;
+    for (int k = 0; k < kRW; ++k) {
+      if (k >= nr) break;
+      const int rl = rw0 + rstep * (j0 + k);
       const double v = wave_sum_f64(acc[k]);
-      if (lane == 0) part[wid * kRS + k] = v;
+      if (lane == 0) {
+        if (S == 1) st_dev(out + r0 + rl, v);
+        else part[rl * S + seg] = v;
+      }
     }
+  }
+  if (S > 1) {
     __syncthreads();
-    if (tid < kRS && rs + tid < r1) {
+    if (tid < R) {
       double t = 0.0;
-#pragma unroll
-      for (int w2 = 0; w2 < NW; ++w2) t += part[w2 * kRS + tid];
-      st_dev(out + rs + tid, t);
+      for (int s2 = 0; s2 < S; ++s2) t += part[tid * S + s2];
+      st_dev(out + r0 + tid, t);
     }
-    __syncthreads();
   }
 }
 
@@ -710,7 +713,7 @@ hipError_t matvec_rows(float* Rp, int rows, int len4, int ld, const int8_t* t, c
   const int words = (len4 * 4 + 15) / 16;
   const int G = rows < 256 ? rows : 256;
   if (len4 > kQMax * 512) return hipErrorInvalidValue;
-  const size_t smem = al16(4 * (size_t)words) + al16(h ? 16 * (size_t)len4 : 0) + 8 * (size_t)(8 * kRS);
+  const size_t smem = al16(4 * (size_t)words) + al16(h ? 16 * (size_t)len4 : 0) + 8 * (size_t)kMvPart;
   if (smem > 160 * 1024) return hipErrorInvalidValue;
   hipError_t e = hipFuncSetAttribute((const void*)matvec_rows_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (e != hipSuccess) return e;
