@@ -305,13 +305,20 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
 
   // Read the exchanged vector (device-coherent loads) into LDS; its largest key and the cleared
   // histogram are prepared for the selection on the way (one barrier).
+  // Loads are issued in groups of kXg per thread before any is used, so their latencies overlap.
+  constexpr int kXg = 8;
   auto load_exchange = [&](const double* src, int len) {
     unsigned kx = 0u;
-    for (int j = tid; j < len; j += NT) {
-      const double v = ld_dev(src + j);
-      dl[j] = v;
-      const unsigned k = __float_as_uint((float)v) & 0x7FFFFFFFu;
-      kx = k > kx ? k : kx;
+    for (int j0 = tid; j0 < len; j0 += kXg * NT) {
+      double v[kXg];
+#pragma unroll
+      for (int u = 0; u < kXg; ++u) v[u] = j0 + u * NT < len ? ld_dev(src + j0 + u * NT) : 0.0;
+#pragma unroll
+      for (int u = 0; u < kXg; ++u) {
+        if (j0 + u * NT < len) dl[j0 + u * NT] = v[u];
+        const unsigned k = __float_as_uint((float)v[u]) & 0x7FFFFFFFu;
+        kx = k > kx ? k : kx;
+      }
     }
     select_prepare<NT>(s, kx);
   };
@@ -457,11 +464,16 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
     // ---------------- initial u: ternarized fp32 row sums
     {
       unsigned kx = 0u;
-      for (int i = tid; i < m; i += NT) {
-        const double v = rs[i];
-        dl[i] = v;
-        const unsigned k = __float_as_uint((float)v) & 0x7FFFFFFFu;
-        kx = k > kx ? k : kx;
+      for (int i0 = tid; i0 < m; i0 += kXg * NT) {
+        double v[kXg];
+#pragma unroll
+        for (int u = 0; u < kXg; ++u) v[u] = i0 + u * NT < m ? rs[i0 + u * NT] : 0.0;
+#pragma unroll
+        for (int u = 0; u < kXg; ++u) {
+          if (i0 + u * NT < m) dl[i0 + u * NT] = v[u];
+          const unsigned k = __float_as_uint((float)v[u]) & 0x7FFFFFFFu;
+          kx = k > kx ? k : kx;
+        }
       }
       select_prepare<NT>(s, kx);
     }
