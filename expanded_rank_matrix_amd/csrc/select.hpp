@@ -469,6 +469,7 @@ __device__ __forceinline__ SelResult ternary_select(const T* vals, const float* 
   double myS = -1.0;
   unsigned myK = 0u, myC = 0u;
   u64 myP = 0ull, myH = 0ull;
+  int nact = 1;  // waves that hold candidate thresholds (uniform)
   if (mode == 1) {
     // Element e's threshold sums P_e = AP + sum of w_p[j] over window elements j with
     // w_key[j] >= w_key[e].  The window's elements come in nch chunks of 64 (one per lane); each
@@ -477,6 +478,7 @@ __device__ __forceinline__ SelResult ternary_select(const T* vals, const float* 
     const unsigned ns = s.slot;
     const int nwin = ns < (unsigned)kWinMax ? (int)ns : kWinMax;
     const int nch = nwin > 64 ? (nwin + 63) >> 6 : 1;
+    nact = nch;
     const int parts = NW / nch;
     const int span = (nwin + parts - 1) / parts;
     const int ch = wid % nch, part = wid / nch;
@@ -578,10 +580,11 @@ __device__ __forceinline__ SelResult ternary_select(const T* vals, const float* 
       prev = best;
     }
   }
-  // ---- argmax over (score desc, key desc): within the wave (toward lane 63; a zero-filled
-  // operand, score 0, loses to every real threshold), then across waves.  Lanes with equal
-  // (score, key) hold equal sums.
-  int src = lane;
+  // ---- argmax over (score desc, key desc) among the candidate waves: within the wave (toward
+  // lane 63; a zero-filled operand, score 0, loses to every real threshold), then across them.
+  // Lanes with equal (score, key) hold equal sums.
+  if (wid < nact) {
+    int src = lane;
 #define EXTERND_STEP(C, R)                                                 \
   {                                                                        \
     const double S2 = dppf64<C, R>(myS);                                   \
@@ -592,12 +595,11 @@ __device__ __forceinline__ SelResult ternary_select(const T* vals, const float* 
       src = (int)s2;                                                       \
     }                                                                      \
   }
-  EXTERND_WAVE_STEPS(EXTERND_STEP)
+    EXTERND_WAVE_STEPS(EXTERND_STEP)
 #undef EXTERND_STEP
-  myS = readlane_f64(myS, 63);
-  myK = readlane32(myK, 63);
-  src = (int)readlane32((unsigned)src, 63);
-  {
+    myS = readlane_f64(myS, 63);
+    myK = readlane32(myK, 63);
+    src = (int)readlane32((unsigned)src, 63);
     const u64 pp = readlane64(myP, src), hh = readlane64(myH, src);
     const unsigned cc = readlane32(myC, src);
     if (lane == 0) {
@@ -612,8 +614,7 @@ __device__ __forceinline__ SelResult ternary_select(const T* vals, const float* 
   double S = -1.0;
   unsigned K = 0u;
   int bw = 0;
-#pragma unroll
-  for (int w = 0; w < NW; ++w)
+  for (int w = 0; w < nact; ++w)
     if (better(s.f_s[w], s.f_k[w], S, K)) {
       S = s.f_s[w];
       K = s.f_k[w];

@@ -111,7 +111,7 @@ struct PackOut {
 // pk_other is nonzero, written back by the wave that owns the (row, segment).
 constexpr int kQMax = 8;    // longest row accepted: len4 <= kQMax * 512 float4 (n <= 16384)
 constexpr int kQL = 5;     // float4 columns per lane per chunk
-constexpr int kRW = 4;     // rows of one wave handled together
+constexpr int kRW = 2;     // rows of one wave handled together (more spills registers)
 constexpr int kMvPart = 8 * 16;  // LDS doubles for the segment sums (needs R * S <= 3 * waves)
 // The 2-bit code at bit offset off of word (0, 1 or 3 = -1) as -1, 0, 1: a signed bit-field
 // extract.
@@ -163,6 +163,17 @@ __device__ __forceinline__ void slab_matvec(float* base, int row_base, int ld, i
           for (int t = 0; t < 4; ++t) od[qi][t] = d * (float)code2(ow, off + 2 * t);
         }
       }
+      // the next row's columns are loaded while the current one is summed
+      float4 xn[kQL];
+      auto load_row = [&](int k) {
+        const float4* r4 = reinterpret_cast<const float4*>(base + (size_t)(r0 + rw0 + rstep * (j0 + k) - row_base) * ld);
+#pragma unroll
+        for (int qi = 0; qi < kQL; ++qi) {
+          const int q = q0 + lane + 64 * qi;
+          xn[qi] = q < qe ? r4[q] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+      };
+      load_row(0);
 #pragma unroll
       for (int k = 0; k < kRW; ++k) {
         if (k >= nr) break;  // uniform within the wave
@@ -170,10 +181,8 @@ __device__ __forceinline__ void slab_matvec(float* base, int row_base, int ld, i
         float4* r4 = reinterpret_cast<float4*>(base + (size_t)(row - row_base) * ld);
         float4 x[kQL];
 #pragma unroll
-        for (int qi = 0; qi < kQL; ++qi) {
-          const int q = q0 + lane + 64 * qi;
-          x[qi] = q < qe ? r4[q] : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
+        for (int qi = 0; qi < kQL; ++qi) x[qi] = xn[qi];
+        if (k + 1 < nr) load_row(k + 1);
         double a0 = 0.0, a1 = 0.0;
 #pragma unroll
         for (int qi = 0; qi < kQL; ++qi) {
@@ -331,24 +340,38 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
     const int nch = (len + 63) >> 6;
     int changed = 0, sum = 0;
     double pacc = 0.0;
-    for (int c = wid; c < nch; c += NW) {
-      const int i = c * 64 + lane;
-      const double xv = i < len ? vals[i] : 0.0;
-      const float x = (float)xv;
-      const bool sel = i < len && selected(x, r);
-      const bool neg = sel && x < 0.0f;
-      const u64 mnz = __ballot(sel), mneg = __ballot(neg);
-      if (want_p && sel) pacc += fabs(xv);
-      sum += (int)__popcll(mnz) - 2 * (int)__popcll(mneg);
-      const int w = c * 4 + lane;
-      if (lane < 4 && w < words) {
-        const unsigned bnz = (unsigned)(mnz >> (16 * lane)) & 0xFFFFu;
-        const unsigned bng = (unsigned)(mneg >> (16 * lane)) & 0xFFFFu;
-        const unsigned word = spread16(bnz) | (spread16(bng) << 1);
-        const unsigned old = dst[w];
-        if (prev) prev[w] = old;
-        changed |= word != old ? 1 : 0;
-        dst[w] = word;
+    constexpr int kPg = 8;  // chunks per wave whose loads are issued together
+    for (int c0 = wid; c0 < nch; c0 += kPg * NW) {
+      double xs[kPg];
+      unsigned olds[kPg];
+#pragma unroll
+      for (int u = 0; u < kPg; ++u) {
+        const int c = c0 + u * NW, i = c * 64 + lane, w = c * 4 + lane;
+        xs[u] = (c < nch && i < len) ? vals[i] : 0.0;
+        olds[u] = (c < nch && lane < 4 && w < words) ? dst[w] : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < kPg; ++u) {
+        const int c = c0 + u * NW;
+        if (c >= nch) break;  // uniform within the wave
+        const int i = c * 64 + lane;
+        const double xv = xs[u];
+        const float x = (float)xv;
+        const bool sel = i < len && selected(x, r);
+        const bool neg = sel && x < 0.0f;
+        const u64 mnz = __ballot(sel), mneg = __ballot(neg);
+        if (want_p && sel) pacc += fabs(xv);
+        sum += (int)__popcll(mnz) - 2 * (int)__popcll(mneg);
+        const int w = c * 4 + lane;
+        if (lane < 4 && w < words) {
+          const unsigned bnz = (unsigned)(mnz >> (16 * lane)) & 0xFFFFu;
+          const unsigned bng = (unsigned)(mneg >> (16 * lane)) & 0xFFFFu;
+          const unsigned word = spread16(bnz) | (spread16(bng) << 1);
+          const unsigned old = olds[u];
+          if (prev) prev[w] = old;
+          changed |= word != old ? 1 : 0;
+          dst[w] = word;
+        }
       }
     }
     const int wch = __ballot(changed != 0) != 0ull ? 1 : 0;
