@@ -41,7 +41,7 @@ struct BlockWs {
   double* gpart;   // split-K partials of the Grams (side stream)
   double* GU;      // b x b
   double* GV;      // b x b
-  double* Li;      // b x b inverse Cholesky factor (lower triangular, zeros above)
+  double* Li;      // b x b: (G + eps I)^-1 for b <= kSpdMax, else the inverse Cholesky factor
   double* Md;      // b: u_c^T Q_c (diagonal of U^T R H V)
   double* PHC;     // b x 3 selection results
   float* d;        // b
@@ -436,6 +436,175 @@ __global__ void __launch_bounds__(NT) chol_inv_kernel(const double* G, int bs, d
     }
 }
 
+// ---- Gi = (G + eps I)^-1 for bs <= 128, eps = 1e-6 trace(G) / bs (the regularised Gram of the
+// pages' Eq. 3), by a blocked Cholesky factorisation on 16 x 16 tiles, the block inverse of the
+// factor and the product X^T X (X = L^-1), all in LDS.  The tile products run on fp64 MFMA; the
+// 16 x 16 diagonal blocks are factored and inverted by one wave with a row per lane.  Pivots that
+// are not positive give zero rows, as in a plain Cholesky solve.  The matrix is padded to a
+// multiple of 16 with an identity block, which keeps it block diagonal and leaves the real part of
+// the inverse unchanged.  One workgroup of 256 threads; about 4 (nb - 1) + 2 barriers for nb tiles
+// per side.
+constexpr int kSpdMax = 128;
+__host__ __device__ inline size_t spd_lds_bytes(int bs) {
+  const int bp = (bs + 15) & ~15, ld = bp + 1;
+  return 8 * ((size_t)bp * ld + (size_t)(bp / 16) * 256 + 16);
+}
+__global__ void __launch_bounds__(256) spd_inv_kernel(const double* G, int bs, double* Gi) {
+  extern __shared__ __align__(16) char smem[];
+  const int bp = (bs + 15) & ~15, nb = bp / 16, ld = bp + 1;
+  double* A = reinterpret_cast<double*>(smem);  // bp x ld
+  double* Dg = A + (size_t)bp * ld;             // nb diagonal-block inverses, 16 x 16 row-major
+  double* misc = Dg + (size_t)nb * 256;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int lr = lane & 15, lk = lane >> 4;  // MFMA operand coordinates: row / column lr, k 4 s + lk
+  if (wid == 0) {
+    double tr = 0.0;
+    for (int c = lane; c < bs; c += 64) tr += G[(size_t)c * bs + c];
+    tr = wave_sum_f64(tr);
+    if (lane == 0) misc[0] = 1e-6 * tr / (double)bs;
+  }
+  __syncthreads();
+  const double eps = misc[0];
+  for (int x = tid; x < bp * bp; x += 256) {
+    const int i = x / bp, j = x - i * bp;
+    double v;
+    if (i < bs && j < bs) v = G[(size_t)i * bs + j] + (i == j ? eps : 0.0);
+    else v = i == j ? 1.0 : 0.0;
+    A[(size_t)i * ld + j] = v;
+  }
+  __syncthreads();
+  auto at = [&](int bi, int bj) -> double* { return A + (size_t)(16 * bi) * ld + 16 * bj; };
+  // operand "row lr, column 4 s + lk" of a row-major 16 x 16 tile (P of P Q^T, or Q^T's Q)
+  auto opr = [&](const double* t, int tld, int sl) -> double { return t[(size_t)lr * tld + 4 * sl + lk]; };
+  // operand "row 4 s + lk, column lr" (B of P Q with Q row-major)
+  auto opc = [&](const double* t, int tld, int sl) -> double { return t[(size_t)(4 * sl + lk) * tld + lr]; };
+  // ---------------- Cholesky, one 16-column panel at a time
+  for (int p = 0; p < nb; ++p) {
+    if (wid == 0) {
+      // factor and invert the diagonal block: lane r (mod 16) holds row r
+      const int r = lr;
+      double* T = at(p, p);
+      double a[16], x[16], rk[16];
+#pragma unroll
+      for (int c = 0; c < 16; ++c) a[c] = T[(size_t)r * ld + c];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const double piv = readlane_f64(a[k], k);
+        const double lkk = piv > 0.0 ? sqrt(piv) : 0.0;
+        const double rr = lkk > 0.0 ? 1.0 / lkk : 0.0;
+        rk[k] = rr;
+        a[k] = r > k ? a[k] * rr : (r == k ? lkk : a[k]);
+#pragma unroll
+        for (int j = k + 1; j < 16; ++j) {
+          const double ljk = readlane_f64(a[k], j);
+          a[j] = fma(-a[k], ljk, a[j]);  // meaningful for rows r >= j
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < 16; ++c) x[c] = 0.0;
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        // row t of X = L^-1 is finished: x[c] held -sum_{j<t} L_tj X_jc
+#pragma unroll
+        for (int c = 0; c < t; ++c) x[c] = r == t ? x[c] * rk[t] : x[c];
+        x[t] = r == t ? rk[t] : x[t];
+#pragma unroll
+        for (int c = 0; c <= t; ++c) {
+          const double xtc = readlane_f64(x[c], t);
+          x[c] = r > t ? fma(-a[t], xtc, x[c]) : x[c];
+        }
+      }
+      if (lane < 16) {
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+          T[(size_t)r * ld + c] = c <= r ? a[c] : 0.0;
+          Dg[p * 256 + r * 16 + c] = c <= r ? x[c] : 0.0;
+        }
+      }
+    }
+    __syncthreads();
+    // panel below: L_ip = A_ip D_p^T (in place)
+    for (int i = p + 1 + wid; i < nb; i += 4) {
+      double* T = at(i, p);
+      dbl4 acc = (dbl4){0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl)
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(opr(T, ld, sl), opr(Dg + p * 256, 16, sl), acc, 0, 0, 0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) T[(size_t)(4 * q + lk) * ld + lr] = acc[q];
+    }
+    __syncthreads();
+    // trailing update: A_ij -= L_ip L_jp^T for p < j <= i (tiles numbered row by row)
+    const int rem = nb - 1 - p;
+    for (int t = wid; t < rem * (rem + 1) / 2; t += 4) {
+      int ii = 0;
+      while ((ii + 1) * (ii + 2) / 2 <= t) ++ii;
+      const int jj = t - ii * (ii + 1) / 2;
+      const int i = p + 1 + ii, j = p + 1 + jj;
+      double* T = at(i, j);
+      const double* Li_ = at(i, p);
+      const double* Lj_ = at(j, p);
+      dbl4 acc;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q] = T[(size_t)(4 * q + lk) * ld + lr];
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl)
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(-opr(Li_, ld, sl), opr(Lj_, ld, sl), acc, 0, 0, 0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) T[(size_t)(4 * q + lk) * ld + lr] = acc[q];
+    }
+    __syncthreads();
+  }
+  // ---------------- X = L^-1 by block rows: X_ii = D_i, X_ij = -D_i sum_{k=j}^{i-1} L_ik X_kj.
+  // X_ij (i > j) is stored transposed in the free upper block (j, i) of A.
+  for (int i = 1; i < nb; ++i) {
+    for (int j = wid; j < i; j += 4) {
+      dbl4 sacc = (dbl4){0.0, 0.0, 0.0, 0.0};
+      for (int k = j; k < i; ++k) {
+        const double* P = at(i, k);
+#pragma unroll
+        for (int sl = 0; sl < 4; ++sl) {
+          // X_kj[4 s + lk][lr]: D_j for k == j, else transposed storage in block (j, k)
+          const double bq = k == j ? opc(Dg + j * 256, 16, sl) : opr(at(j, k), ld, sl);
+          sacc = __builtin_amdgcn_mfma_f64_16x16x4f64(opr(P, ld, sl), bq, sacc, 0, 0, 0);
+        }
+      }
+      dbl4 xacc = (dbl4){0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl)  // an MFMA result in lane l, register s is operand B[4 s + lk][lr]
+        xacc = __builtin_amdgcn_mfma_f64_16x16x4f64(-opr(Dg + i * 256, 16, sl), sacc[sl], xacc, 0, 0, 0);
+      double* T = at(j, i);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) T[(size_t)lr * ld + 4 * q + lk] = xacc[q];
+    }
+    __syncthreads();
+  }
+  // ---------------- Gi = X^T X: tile (i, j), i >= j, is sum_{k >= i} X_ki^T X_kj
+  for (int t = wid; t < nb * (nb + 1) / 2; t += 4) {
+    int i = 0;
+    while ((i + 1) * (i + 2) / 2 <= t) ++i;
+    const int j = t - i * (i + 1) / 2;
+    dbl4 acc = (dbl4){0.0, 0.0, 0.0, 0.0};
+    for (int k = i; k < nb; ++k) {
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl) {
+        // X_ki[4 s + lk][lr] and X_kj[4 s + lk][lr]
+        const double av = k == i ? opc(Dg + i * 256, 16, sl) : opr(at(i, k), ld, sl);
+        const double bv = k == j ? opc(Dg + j * 256, 16, sl) : opr(at(j, k), ld, sl);
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int r = 16 * i + 4 * q + lk, c = 16 * j + lr;
+      if (r < bs && c < bs) {
+        Gi[(size_t)r * bs + c] = acc[q];
+        if (i != j) Gi[(size_t)c * bs + r] = acc[q];
+      }
+    }
+  }
+}
+
 // ---- out (bs x ncols) = op(A) B with A bs x bs (op: A or A^T), B bs x ncols, fp64 MFMA, K = bs.
 // Workgroup: 64 columns; wave w: columns 16 w .. 16 w + 15, all bs rows (NRT tiles of 16).
 template <int NRT, bool TA>
@@ -811,8 +980,20 @@ static void utr_product(const BlockLaunch& L, const BlockWs& w, int bs, hipStrea
   reduce_splits(w.part, ns, (long long)bs * L.n, w.X, st);
 }
 
-// Li = L^-1 for L L^T = G + eps I
+// Li = (G + eps I)^-1 for bs <= kSpdMax, else Li = L^-1 for L L^T = G + eps I
 static void chol_inverse(const BlockWs& w, const double* G, int bs, hipStream_t st) {
+  if (bs <= kSpdMax) {
+    static bool attr_set[64] = {};  // once per device: dynamic LDS above 64 KB
+    int dev = 0;
+    hipGetDevice(&dev);
+    if (dev >= 0 && dev < 64 && !attr_set[dev]) {
+      hipFuncSetAttribute((const void*)spd_inv_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          (int)spd_lds_bytes(kSpdMax));
+      attr_set[dev] = true;
+    }
+    hipLaunchKernelGGL(spd_inv_kernel, dim3(1), dim3(256), spd_lds_bytes(bs), st, G, bs, w.Li);
+    return;
+  }
   const int ne = bs * (bs + 1) / 2;
   if (ne <= 256 * 2)
     hipLaunchKernelGGL((chol_inv_kernel<256, 2>), dim3(1), dim3(256), 0, st, G, bs, w.Li);
@@ -841,8 +1022,13 @@ static void apply(const double* A, int bs, const double* Bm, double* out, int nc
   else hipLaunchKernelGGL((apply_kernel<16, TA>), grid, dim3(256), 0, st, A, bs, Bm, out, ncols);
 }
 
-// out (bs x ncols) = (G + eps I)^-1 in = L^-T (L^-1 in); in and out may not alias
+// out (bs x ncols) = (G + eps I)^-1 in: one product with the inverse, or L^-T (L^-1 in) for
+// bs > kSpdMax; in and out may not alias
 static void solve(const BlockWs& w, int bs, const double* in, double* out, int ncols, hipStream_t st) {
+  if (bs <= kSpdMax) {
+    apply<false>(w.Li, bs, in, out, ncols, st);
+    return;
+  }
   apply<false>(w.Li, bs, in, w.Tmp, ncols, st);
   apply<true>(w.Li, bs, w.Tmp, out, ncols, st);
 }
