@@ -48,8 +48,11 @@ struct BlockWs {
   double* st;      // [0] E, [1] E0
   int* flags;      // [0] dead, [1] empty sketch columns, [2] fallbacks
   int* used;       // m: rows used by sketch fallbacks within the block
+  unsigned* rmax;  // [64 (s & 1) + w]: max |R| (fp32 bits) at the start of block s, spread over 64
+                   // words w to keep the atomics of one update uncontended
 };
 
+constexpr int kMaxWords = 64;      // words per residual-max slot (one per lane of a wave)
 constexpr int kMaxSplit = 8;       // split-K factor cap of the residual contractions
 constexpr int kMaxGramSplit = 64;  // ... and of the Grams
 
@@ -77,6 +80,7 @@ static void ws_layout(int m, int n, int b, F&& take) {
   take((void**)nullptr, 64);
   take((void**)nullptr, 64);
   take((void**)nullptr, (size_t)m * 4);
+  take((void**)nullptr, 2 * kMaxWords * 4);
 }
 
 static BlockWs carve(void* base, int m, int n, int b) {
@@ -110,6 +114,7 @@ static BlockWs carve(void* base, int m, int n, int b) {
   w.st = static_cast<double*>(ptrs[q++]);
   w.flags = static_cast<int*>(ptrs[q++]);
   w.used = static_cast<int*>(ptrs[q++]);
+  w.rmax = static_cast<unsigned*>(ptrs[q++]);
   return w;
 }
 
@@ -127,11 +132,13 @@ __device__ __forceinline__ u64 splitmix64(u64 key) {
   return z ^ (z >> 31);
 }
 
-__global__ void __launch_bounds__(256) omega_kernel(int8_t* Vt, int ldv, int bs, int n, long long s, int* flags) {
+__global__ void __launch_bounds__(256) omega_kernel(int8_t* Vt, int ldv, int bs, int n, long long s, int* flags,
+                                                    unsigned* rmax) {
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     flags[1] = 0;  // empty sketch columns of this block
     flags[2] = 0;  // fallback starts of this block
   }
+  if (blockIdx.x == 0 && threadIdx.x < kMaxWords) rmax[kMaxWords * ((s + 1) & 1) + threadIdx.x] = 0u;
   const long long total = (long long)bs * ldv;
   for (long long x = blockIdx.x * 256ll + threadIdx.x; x < total; x += (long long)gridDim.x * 256) {
     const int c = (int)(x / ldv), j = (int)(x - (long long)c * ldv);
@@ -144,11 +151,11 @@ __global__ void __launch_bounds__(256) omega_kernel(int8_t* Vt, int ldv, int bs,
   }
 }
 
-// ---- residual contractions on v_mfma_f64_16x16x4f64: D(16x16) += A(16x4) B(4x16).
-// Lane l supplies A[l % 16][l / 16] and B[l / 16][l % 16]; D(i, j) lands in lane j + 16 (i % 4),
-// register i / 4.  The k order inside a group of 16 is permuted so that lane (r, kq) covers
-// k = g + 4 kq + s at step s = 0..3: one 16-byte load then feeds four MFMA steps.  Operands are
-// loaded straight into registers (no LDS), one group ahead.
+// ---- weighted Gram T diag(h) T^T on v_mfma_f64_16x16x4f64 (the weights are not integers):
+// D(16x16) += A(16x4) B(4x16).  Lane l supplies A[l % 16][l / 16] and B[l / 16][l % 16];
+// D(i, j) lands in lane j + 16 (i % 4), register i / 4.  The k order inside a group of 16 is
+// permuted so that lane (r, kq) covers k = g + 4 kq + s at step s = 0..3: one 4-byte load then
+// feeds four MFMA steps.  Operands are loaded straight into registers, one group ahead.
 
 // part[split][c][i] = sum_{k in split} R[i][k] * h_k * T[c][k]   (rows of R x components)
 // Workgroup: 64 rows of R (16 per wave) x all components (NCT tiles of 16).
@@ -244,72 +251,256 @@ __global__ void __launch_bounds__(256) contract_rw_kernel(const TR* R, int ldr, 
   }
 }
 
-// part[split][c][j] = sum_{i in split} U[c][i] * R[i][j]   (components x columns of R)
-// Workgroup: all components (NCT tiles of 16) x 64 columns (16 per wave).
-template <int NCT>
-__global__ void __launch_bounds__(256) contract_utr_kernel(const float* R, int ldr, int m, int n, const int8_t* U,
-                                                           int ldu, int bs, int kspan, double* part) {
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int j = blockIdx.x * 64 + wid * 16 + (lane & 15);
-  const int kq = lane >> 4;
-  const int kb = blockIdx.y * kspan, ke = (kb + kspan < m) ? kb + kspan : m;
-  const bool jok = j < n;
-  const int8_t* up[NCT];
+// ---- residual contractions on v_mfma_i32_16x16x64_i8 with R in fixed point ------------------
+// D(16x16) += A(16x64) B(64x16) in int32: lane l supplies 16 bytes of row l % 16 of A and 16 bytes
+// of column l % 16 of B, paired on the same k; D(i, j) lands in lane j + 16 (i / 4), register i % 4.
+// Lane group g = l / 16 takes k = k0 + 16 g .. k0 + 16 g + 15 of each 64-wide k chunk.
+//
+// R enters as N = rint(x 2^f), x = R_ij (times h_j where weighted), with one power-of-two scale per
+// block chosen from max |R| so that |N| <= 2^30, split into four signed 8-bit digits
+// N = sum_s 2^(8 s) d_s.  The ternary operand is exact in int8, each digit product sums exactly
+// in int32 (|sum| <= 2^7 K), the digits recombine exactly in fp64 and splits of K add exactly
+// (every partial is an integer times 2^-f below 2^53).  The result is therefore the exact
+// contraction of the fixed-point image of R, whatever the launch shape or the order of the
+// atomic adds: its only error is the rounding of each x to the grid 2^-f, at most 2^-31 of the
+// largest |x|.
+typedef int v4i __attribute__((ext_vector_type(4)));
+
+// exponent E of the fixed-point range: |x| < 2^E for every x entering a contraction (each wave
+// reduces the 64 words of block s's slot itself)
+__device__ __forceinline__ int fx_exponent(const unsigned* rmax, int s, int ehm) {
+  const unsigned bits = wave_max_u32(rmax[kMaxWords * (s & 1) + (threadIdx.x & 63)]);
+  if (bits == 0u) return 0;
+  return exp_bound(__uint_as_float(bits)) + ehm;
+}
+
+// Digits of four fixed-point values: word t holds digit t of n[0..3] in bytes 0..3.  With
+// B = n + 0x808080, digits 0..2 are B's bytes minus 128 (byte ^ 0x80) and digit 3 is B >> 24.
+__device__ __forceinline__ void fx_digits4(int n0, int n1, int n2, int n3, unsigned (&w)[4]) {
+  const unsigned b0 = (unsigned)(n0 + 0x808080), b1 = (unsigned)(n1 + 0x808080);
+  const unsigned b2 = (unsigned)(n2 + 0x808080), b3 = (unsigned)(n3 + 0x808080);
+  // v_perm_b32: selector bytes 0..3 pick bytes of the second source, 4..7 of the first
+  const unsigned x01lo = __builtin_amdgcn_perm(b1, b0, 0x05010400u);  // b0.0 b1.0 b0.1 b1.1
+  const unsigned x01hi = __builtin_amdgcn_perm(b1, b0, 0x07030602u);  // b0.2 b1.2 b0.3 b1.3
+  const unsigned x23lo = __builtin_amdgcn_perm(b3, b2, 0x05010400u);
+  const unsigned x23hi = __builtin_amdgcn_perm(b3, b2, 0x07030602u);
+  w[0] = __builtin_amdgcn_perm(x23lo, x01lo, 0x05040100u) ^ 0x80808080u;
+  w[1] = __builtin_amdgcn_perm(x23lo, x01lo, 0x07060302u) ^ 0x80808080u;
+  w[2] = __builtin_amdgcn_perm(x23hi, x01hi, 0x05040100u) ^ 0x80808080u;
+  w[3] = __builtin_amdgcn_perm(x23hi, x01hi, 0x07060302u);
+}
+
+// 16 fixed-point values -> the four digit operands (operand t = digit t of values 0..15)
+__device__ __forceinline__ void fx_operands(const int (&nv)[16], v4i (&op)[4]) {
 #pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) {
-    const int c = ct * 16 + (lane & 15);
-    up[ct] = U + (size_t)(c < bs ? c : 0) * ldu;
+  for (int q = 0; q < 4; ++q) {
+    unsigned w[4];
+    fx_digits4(nv[4 * q], nv[4 * q + 1], nv[4 * q + 2], nv[4 * q + 3], w);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) op[t][q] = (int)w[t];
   }
-  dbl4 acc[NCT];
+}
+
+__device__ __forceinline__ v4i load16(const int8_t* p) { return *reinterpret_cast<const v4i*>(p); }
+
+// out[c][i] (+)= sum_{k in this split} x_ik T[c][k], x_ik = R[i][k] (h_k): rows of R x components.
+// Workgroup: 64 rows (16 per wave) x 16 NCT components (blockIdx.y), K range blockIdx.z.
+template <int NCT>
+__global__ void __launch_bounds__(256) rv_i8_kernel(const float* R, int ldr, int rows, int K, const int8_t* T,
+                                                    int ldt, const float* h, int ehm, int bs, const unsigned* rmax,
+                                                    int sblk, int kspan, double* out) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int lr = lane & 15, g = lane >> 4;
+  const int i = blockIdx.x * 64 + wid * 16 + lr;  // row supplied by this lane
+  const int c0 = blockIdx.y * 16 * NCT;
+  const int kb = blockIdx.z * kspan, ke = kb + kspan < K ? kb + kspan : K;
+  const int E = fx_exponent(rmax, sblk, h ? ehm : 0);
+  const int sc = 30 - E < 126 ? (30 - E > -126 ? 30 - E : -126) : 126;  // scale 2^sc, a normal float
+  const float fscale = ldexpf(1.0f, sc);
+  const double dscale = ldexp(1.0, sc);
+  const bool rok = i < rows;
+  const float* rp = R + (size_t)(rok ? i : 0) * ldr;
+  v4i acc[NCT][4];
 #pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) acc[ct] = (dbl4){0.0, 0.0, 0.0, 0.0};
-  auto load = [&](int g, float (&bv)[4], unsigned (&uv)[NCT]) {
-    const int i = g + 4 * kq;
+  for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) bv[q] = (jok && i + q < ke) ? R[(size_t)(i + q) * ldr + j] : 0.0f;
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      const int c = ct * 16 + (lane & 15);
-      unsigned v = 0u;
-      if (c < bs && i < ke) {
-        v = *reinterpret_cast<const unsigned*>(up[ct] + i);
-        if (i + 4 > ke) v &= 0xFFFFFFFFu >> (8 * (i + 4 - ke));
-      }
-      uv[ct] = v;
-    }
-  };
-  float bv[4];
-  unsigned uv[NCT];
-  if (kb < ke) load(kb, bv, uv);
-  for (int g = kb; g < ke; g += 16) {
-    float bv2[4];
-    unsigned uv2[NCT];
-    const bool more = g + 16 < ke;
-    if (more) load(g + 16, bv2, uv2);
+    for (int t = 0; t < 4; ++t) acc[ct][t] = (v4i){0, 0, 0, 0};
+  for (int k0 = kb; k0 < ke; k0 += 64) {
+    const int k = k0 + 16 * g;
+    float xv[16];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const double b = (double)bv[q];
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        const double a = (double)(int8_t)(uv[ct] >> (8 * q));
-        acc[ct] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, acc[ct], 0, 0, 0);
-      }
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (rok && k + 4 * q < ke) v = *reinterpret_cast<const float4*>(rp + k + 4 * q);
+      xv[4 * q] = v.x;
+      xv[4 * q + 1] = v.y;
+      xv[4 * q + 2] = v.z;
+      xv[4 * q + 3] = v.w;
     }
-    if (more) {
+    v4i tb[NCT];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) bv[q] = bv2[q];
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) uv[ct] = uv2[ct];
+    for (int ct = 0; ct < NCT; ++ct) {
+      const int c = c0 + ct * 16 + lr;
+      tb[ct] = (c < bs && k < ke) ? load16(T + (size_t)c * ldt + k) : (v4i){0, 0, 0, 0};
     }
+    int nv[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const bool in = k + t < ke;
+      if (h) nv[t] = in ? __double2int_rn((double)xv[t] * (double)h[k + t] * dscale) : 0;
+      else nv[t] = in ? __float2int_rn(xv[t] * fscale) : 0;
+    }
+    v4i da[4];
+    fx_operands(nv, da);
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc[ct][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(tb[ct], da[t], acc[ct][t], 0, 0, 0);
   }
-  double* out = part + (size_t)blockIdx.y * bs * n;
+  // D = T x^T: lane l, register q holds component 4 g + q of the tile for row lr, so each store
+  // instruction covers four components x 16 consecutive rows
+  const double unit = ldexp(1.0, -sc);
+  const bool split = gridDim.z > 1;
+  const int r = blockIdx.x * 64 + wid * 16 + lr;
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int c = ct * 16 + (lane >> 4) + 4 * r;
-      if (c < bs && jok) out[(size_t)c * n + j] = acc[ct][r];
+    for (int q = 0; q < 4; ++q) {
+      const int c = c0 + ct * 16 + 4 * g + q;
+      if (c < bs && r < rows) {
+        const double v = ((double)acc[ct][0][q] + 256.0 * (double)acc[ct][1][q] + 65536.0 * (double)acc[ct][2][q] +
+                          16777216.0 * (double)acc[ct][3][q]) * unit;
+        double* o = out + (size_t)c * rows + r;
+        if (split) atomicAdd(o, v);
+        else *o = v;
+      }
     }
+  }
+}
+
+// out[c][j] (+)= sum_{i in this split} U[c][i] R[i][j]: components x columns of R.
+// Workgroup: 64 columns (16 per wave) x 16 NCT components (blockIdx.y), K = m range blockIdx.z.
+template <int NCT>
+__global__ void __launch_bounds__(256) utr_i8_kernel(const float* R, int ldr, int m, int n, const int8_t* U, int ldu,
+                                                     int bs, const unsigned* rmax, int sblk, int kspan, double* out) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int lr = lane & 15, g = lane >> 4;
+  const int j = blockIdx.x * 64 + wid * 16 + lr;  // column supplied by this lane
+  const int c0 = blockIdx.y * 16 * NCT;
+  const int kb = blockIdx.z * kspan, ke = kb + kspan < m ? kb + kspan : m;
+  const int E = fx_exponent(rmax, sblk, 0);
+  const int sc = 30 - E < 126 ? (30 - E > -126 ? 30 - E : -126) : 126;  // scale 2^sc, a normal float
+  const float fscale = ldexpf(1.0f, sc);
+  const bool jok = j < n;
+  v4i acc[NCT][4];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[ct][t] = (v4i){0, 0, 0, 0};
+  for (int k0 = kb; k0 < ke; k0 += 64) {
+    const int k = k0 + 16 * g;
+    float xv[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) xv[t] = (jok && k + t < ke) ? R[(size_t)(k + t) * ldr + j] : 0.0f;
+    v4i ua[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const int c = c0 + ct * 16 + lr;
+      ua[ct] = (c < bs && k < ke) ? load16(U + (size_t)c * ldu + k) : (v4i){0, 0, 0, 0};
+    }
+    int nv[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) nv[t] = __float2int_rn(xv[t] * fscale);
+    v4i db[4];
+    fx_operands(nv, db);
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc[ct][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ua[ct], db[t], acc[ct][t], 0, 0, 0);
+  }
+  const double unit = ldexp(1.0, -sc);
+  const bool split = gridDim.z > 1;
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int c = c0 + ct * 16 + 4 * g + q;
+      if (c < bs && jok) {
+        const double v = ((double)acc[ct][0][q] + 256.0 * (double)acc[ct][1][q] + 65536.0 * (double)acc[ct][2][q] +
+                          16777216.0 * (double)acc[ct][3][q]) * unit;
+        double* o = out + (size_t)c * n + j;
+        if (split) atomicAdd(o, v);
+        else *o = v;
+      }
+    }
+  }
+}
+
+// G = T T^T for ternary rows T (bs x K, ld ldt, zero-padded to ldt): integer-exact.  One
+// workgroup of 16 waves per lower 16 x 16 tile; the waves split K (four 64-wide chunks in flight
+// per wave) and add their int32 sums in LDS in wave order.
+__global__ void __launch_bounds__(1024) gram_i8_kernel(const int8_t* T, int ldt, int K, int bs, double* G) {
+  __shared__ int red[16][256];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int lr = lane & 15, g = lane >> 4;
+  int ti = 0;
+  while ((ti + 1) * (ti + 2) / 2 <= (int)blockIdx.x) ++ti;
+  const int tj = (int)blockIdx.x - ti * (ti + 1) / 2;
+  const int ra = ti * 16 + lr, rb = tj * 16 + lr;
+  const int nch = (K + 63) / 64;
+  v4i acc = (v4i){0, 0, 0, 0};
+  for (int c0 = wid; c0 < nch; c0 += 4 * 16) {
+    v4i a[4], b[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int k = (c0 + 16 * u) * 64 + 16 * g;
+      const bool ok = c0 + 16 * u < nch && k < ldt;
+      a[u] = (ok && ra < bs) ? load16(T + (size_t)ra * ldt + k) : (v4i){0, 0, 0, 0};
+      b[u] = (ok && rb < bs) ? load16(T + (size_t)rb * ldt + k) : (v4i){0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[u], b[u], acc, 0, 0, 0);
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) red[wid][q * 64 + lane] = acc[q];
+  __syncthreads();
+  if (wid == 0) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      int v = 0;
+#pragma unroll
+      for (int w2 = 0; w2 < 16; ++w2) v += red[w2][q * 64 + lane];
+      const int r = ti * 16 + 4 * g + q, c = tj * 16 + lr;
+      if (r < bs && c < bs) {
+        G[(size_t)r * bs + c] = (double)v;
+        G[(size_t)c * bs + r] = (double)v;
+      }
+    }
+  }
+}
+
+__global__ void __launch_bounds__(256) zero_kernel(double* p, long long count) {
+  for (long long x = blockIdx.x * 256ll + threadIdx.x; x < count; x += (long long)gridDim.x * 256) p[x] = 0.0;
+}
+
+// max |R| over the m x n residual into words[0..kMaxWords) (fp32 bits; the words start at zero)
+__global__ void __launch_bounds__(256) rmax_kernel(const float* R, int ldr, int m, int n, unsigned* words) {
+  __shared__ unsigned wm[4];
+  unsigned mx = 0u;
+  const long long total = (long long)m * n;
+  for (long long x = blockIdx.x * 256ll + threadIdx.x; x < total; x += (long long)gridDim.x * 256) {
+    const int i = (int)(x / n), j = (int)(x - (long long)i * n);
+    const unsigned b = __float_as_uint(R[(size_t)i * ldr + j]) & 0x7FFFFFFFu;
+    mx = b > mx ? b : mx;
+  }
+  mx = wave_max_u32(mx);
+  if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = mx;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    mx = wm[0] > wm[1] ? wm[0] : wm[1];
+    mx = wm[2] > mx ? wm[2] : mx;
+    mx = wm[3] > mx ? wm[3] : mx;
+    if (mx != 0u) atomicMax(words + blockIdx.x % kMaxWords, mx);
   }
 }
 
@@ -808,7 +999,7 @@ __global__ void __launch_bounds__(256) scales_kernel(const double* Md, const dou
 // A[i][k] = d_k U[k][i], B[k][j] = V[k][j].
 __global__ void __launch_bounds__(256) update_kernel(float* R, int ldr, int m, int n, const int8_t* Ut, int ldu,
                                                      const int8_t* Vt, int ldv, const float* dvec, int bs,
-                                                     const int* flags) {
+                                                     const int* flags, unsigned* rmax_next) {
   if (flags[0]) return;
   __shared__ int8_t Us[256][64 + 4];
   __shared__ int8_t Vs[256][64 + 4];
@@ -835,6 +1026,7 @@ __global__ void __launch_bounds__(256) update_kernel(float* R, int ldr, int m, i
       acc[t] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, bv, acc[t], 0, 0, 0);
     }
   }
+  unsigned mx = 0u;  // largest |R| of the tile after the update (fp32 bits)
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int j = j0 + t * 16 + (lane & 15);
@@ -844,9 +1036,25 @@ __global__ void __launch_bounds__(256) update_kernel(float* R, int ldr, int m, i
       if (i < m && j < n) {
         float* p = R + (size_t)i * ldr + j;
         const double s = acc[t][r];
-        if (s != 0.0) *p = (float)((double)*p - s);
+        float x = *p;
+        if (s != 0.0) {
+          x = (float)((double)x - s);
+          *p = x;
+        }
+        const unsigned b = __float_as_uint(x) & 0x7FFFFFFFu;
+        mx = b > mx ? b : mx;
       }
     }
+  }
+  __shared__ unsigned wm[4];
+  mx = wave_max_u32(mx);
+  if (lane == 0) wm[wid] = mx;
+  __syncthreads();
+  if (tid == 0) {
+    mx = wm[0] > wm[1] ? wm[0] : wm[1];
+    mx = wm[2] > mx ? wm[2] : mx;
+    mx = wm[3] > mx ? wm[3] : mx;
+    if (mx != 0u) atomicMax(rmax_next + (blockIdx.x + blockIdx.y) % kMaxWords, mx);
   }
 }
 
@@ -873,7 +1081,7 @@ __global__ void __launch_bounds__(256) emit_kernel(const int8_t* Ut, int ldu, co
 }
 
 // E0 from the per-row energies (fixed order), dead flag for A = 0
-__global__ void block_init_kernel(const double* rowE, int m, double* st, int* flags) {
+__global__ void block_init_kernel(const double* rowE, int m, double* st, int* flags, unsigned* rmax) {
   __shared__ double red[4];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   double e = 0.0;
@@ -888,6 +1096,7 @@ __global__ void block_init_kernel(const double* rowE, int m, double* st, int* fl
     flags[0] = E0 > 0.0 ? 0 : 1;
     flags[1] = 0;
     flags[2] = 0;
+    for (int x = 0; x < 2 * kMaxWords; ++x) rmax[x] = 0u;
   }
 }
 
@@ -919,14 +1128,6 @@ static void launch_rw(const TR* R, int ldr, int rows, int K, const int8_t* T, in
                      K, T, ldt, h, bs, kspan, part);
 }
 
-template <int NCT>
-static void launch_utr(const float* R, int ldr, int m, int n, const int8_t* U, int ldu, int bs, int nsplit,
-                       double* part, hipStream_t st) {
-  const int kspan = ((m + nsplit - 1) / nsplit + 31) / 32 * 32;
-  hipLaunchKernelGGL(contract_utr_kernel<NCT>, dim3((n + 63) / 64, nsplit), dim3(256), 0, st, R, ldr, m, n, U, ldu,
-                     bs, kspan, part);
-}
-
 // split-K factor: about 512 workgroups, at least 256 of K per split, at most cap splits
 static int splits_for(int tiles, int K, int cap) {
   int s = (512 + tiles - 1) / tiles;
@@ -956,28 +1157,71 @@ static void rw_contract(const TR* R, int ldr, int rows, int K, const int8_t* T, 
   reduce_splits(part, ns, (long long)bs * rows, out, st);
 }
 
-// Y^T (bs x m) = (R diag(h) V^T)^T for V = Vt rows
-static void rw_product(const BlockLaunch& L, const BlockWs& w, const float* h, int bs, double* outT,
+// K splits of an int8 contraction with `tiles` workgroups per split: about 512 workgroups, at
+// least 256 of K per split, at most 16 splits; kspan is a multiple of the 64-wide k chunk.
+static int i8_splits(int tiles, int K, int* kspan) {
+  int z = (512 + tiles - 1) / tiles;
+  const int maxz = (K + 255) / 256;
+  z = z > maxz ? maxz : z;
+  z = z > 16 ? 16 : z;
+  z = z < 1 ? 1 : z;
+  *kspan = ((K + z - 1) / z + 63) / 64 * 64;
+  return (K + *kspan - 1) / *kspan;
+}
+
+static void zero_fill(double* p, long long count, hipStream_t st) {
+  const long long nb = (count + 255) / 256;
+  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)(nb < 2048 ? nb : 2048)), dim3(256), 0, st, p, count);
+}
+
+// Y^T (bs x m) = (R diag(h) V^T)^T for V = Vt rows, on int8 MFMA with R in fixed point
+static void rw_product(const BlockLaunch& L, const BlockWs& w, const float* h, int bs, int sblk, double* outT,
                        hipStream_t st) {
-  rw_contract<float>(L.R, L.ldr, L.m, L.n, w.Vt, w.ldv, h, bs, kMaxSplit, w.part, outT, st);
+  const int nct = bs <= 16 ? 1 : (bs <= 32 ? 2 : 4);
+  const int gx = (L.m + 63) / 64, gy = (bs + 16 * nct - 1) / (16 * nct);
+  int kspan = 0;
+  const int gz = i8_splits(gx * gy, L.n, &kspan);
+  if (gz > 1) zero_fill(outT, (long long)bs * L.m, st);
+  const dim3 grid(gx, gy, gz);
+  if (nct == 1)
+    hipLaunchKernelGGL(rv_i8_kernel<1>, grid, dim3(256), 0, st, L.R, L.ldr, L.m, L.n, w.Vt, w.ldv, h, L.EHm, bs,
+                       w.rmax, sblk, kspan, outT);
+  else if (nct == 2)
+    hipLaunchKernelGGL(rv_i8_kernel<2>, grid, dim3(256), 0, st, L.R, L.ldr, L.m, L.n, w.Vt, w.ldv, h, L.EHm, bs,
+                       w.rmax, sblk, kspan, outT);
+  else
+    hipLaunchKernelGGL(rv_i8_kernel<4>, grid, dim3(256), 0, st, L.R, L.ldr, L.m, L.n, w.Vt, w.ldv, h, L.EHm, bs,
+                       w.rmax, sblk, kspan, outT);
 }
 
 // G (bs x bs) = T diag(w) T^T for ternary rows T (bs x len, ld ldt); integer-exact without weights
 static void gram_product(const BlockWs& w, const int8_t* T, int len, int ldt, const float* wt, int bs, double* G,
                          hipStream_t st) {
+  if (!wt) {
+    const int nt = (bs + 15) / 16;
+    hipLaunchKernelGGL(gram_i8_kernel, dim3(nt * (nt + 1) / 2), dim3(1024), 0, st, T, ldt, len, bs, G);
+    return;
+  }
   rw_contract<int8_t>(T, ldt, bs, len, T, ldt, wt, bs, kMaxGramSplit, w.gpart, G, st);
 }
 
-// X (bs x n) = U^T R
-static void utr_product(const BlockLaunch& L, const BlockWs& w, int bs, hipStream_t st) {
-  const int ns = splits_for((L.n + 63) / 64, L.m, kMaxSplit);
-  const int nct = (bs + 15) / 16;
-  if (nct <= 1) launch_utr<1>(L.R, L.ldr, L.m, L.n, w.Ut, w.ldu, bs, ns, w.part, st);
-  else if (nct <= 2) launch_utr<2>(L.R, L.ldr, L.m, L.n, w.Ut, w.ldu, bs, ns, w.part, st);
-  else if (nct <= 4) launch_utr<4>(L.R, L.ldr, L.m, L.n, w.Ut, w.ldu, bs, ns, w.part, st);
-  else if (nct <= 8) launch_utr<8>(L.R, L.ldr, L.m, L.n, w.Ut, w.ldu, bs, ns, w.part, st);
-  else launch_utr<16>(L.R, L.ldr, L.m, L.n, w.Ut, w.ldu, bs, ns, w.part, st);
-  reduce_splits(w.part, ns, (long long)bs * L.n, w.X, st);
+// X (bs x n) = U^T R, on int8 MFMA with R in fixed point
+static void utr_product(const BlockLaunch& L, const BlockWs& w, int bs, int sblk, hipStream_t st) {
+  const int nct = bs <= 16 ? 1 : (bs <= 32 ? 2 : 4);
+  const int gx = (L.n + 63) / 64, gy = (bs + 16 * nct - 1) / (16 * nct);
+  int kspan = 0;
+  const int gz = i8_splits(gx * gy, L.m, &kspan);
+  if (gz > 1) zero_fill(w.X, (long long)bs * L.n, st);
+  const dim3 grid(gx, gy, gz);
+  if (nct == 1)
+    hipLaunchKernelGGL(utr_i8_kernel<1>, grid, dim3(256), 0, st, L.R, L.ldr, L.m, L.n, w.Ut, w.ldu, bs, w.rmax,
+                       sblk, kspan, w.X);
+  else if (nct == 2)
+    hipLaunchKernelGGL(utr_i8_kernel<2>, grid, dim3(256), 0, st, L.R, L.ldr, L.m, L.n, w.Ut, w.ldu, bs, w.rmax,
+                       sblk, kspan, w.X);
+  else
+    hipLaunchKernelGGL(utr_i8_kernel<4>, grid, dim3(256), 0, st, L.R, L.ldr, L.m, L.n, w.Ut, w.ldu, bs, w.rmax,
+                       sblk, kspan, w.X);
 }
 
 // Li = (G + eps I)^-1 for bs <= kSpdMax, else Li = L^-1 for L L^T = G + eps I
@@ -1084,15 +1328,21 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops) {
     return hipEventRecord(ss->join, ss->s);
   };
   auto join = [&]() -> hipError_t { return hipStreamWaitEvent(st, ss->join, 0); };
-  hipLaunchKernelGGL(block_init_kernel, dim3(1), dim3(256), 0, st, L.rowE, m, w.st, w.flags);
+  hipLaunchKernelGGL(block_init_kernel, dim3(1), dim3(256), 0, st, L.rowE, m, w.st, w.flags, w.rmax);
+  {
+    const long long nb = ((long long)m * n + 255) / 256;
+    hipLaunchKernelGGL(rmax_kernel, dim3((unsigned)(nb < 2048 ? nb : 2048)), dim3(256), 0, st, L.R, L.ldr, m, n,
+                       w.rmax);
+  }
   const int nblocks = (L.k + L.b - 1) / L.b;
   double fl = 0.0;
   for (int s = 0; s < nblocks; ++s) {
     const int bs = (L.k - s * L.b) < L.b ? (L.k - s * L.b) : L.b;
     const int k0 = s * L.b;
     // sketch
-    hipLaunchKernelGGL(omega_kernel, dim3(256), dim3(256), 0, st, w.Vt, w.ldv, bs, n, (long long)s, w.flags);
-    rw_product(L, w, nullptr, bs, w.Yt, st);
+    hipLaunchKernelGGL(omega_kernel, dim3(256), dim3(256), 0, st, w.Vt, w.ldv, bs, n, (long long)s, w.flags,
+                       w.rmax);
+    rw_product(L, w, nullptr, bs, s, w.Yt, st);
     select_rows(w.Yt, m, w.ldu, bs, L.tau, nullptr, 0, w.Ut, w.PHC, w.flags, 1, st);
     hipLaunchKernelGGL(zero_check_kernel, dim3(1), dim3(256), 0, st, L.R, L.ldr, m, n, w.flags, w.st);
     hipLaunchKernelGGL(fallback_kernel, dim3(1), dim3(512), 0, st, L.R, L.ldr, m, n, bs, w.Ut, w.ldu, w.PHC,
@@ -1101,13 +1351,13 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops) {
     for (int t = 0; t < L.T; ++t) {
       // V-step: G = (U^T U + eps I)^-1 U^T R, rows ternarized with weights h
       if ((e = gram_inverse(w.Ut, m, w.ldu, nullptr, bs, w.GU)) != hipSuccess) return e;
-      utr_product(L, w, bs, st);
+      utr_product(L, w, bs, s, st);
       if ((e = join()) != hipSuccess) return e;
       solve(w, bs, w.X, w.Z, n, st);
       select_rows(w.Z, n, w.ldv, bs, L.tau, L.h, L.EHm, w.Vt, w.PHC, w.flags, 0, st);
       // U-step: F^T = (V^T H V + eps I)^-1 (R H V)^T, columns ternarized without weights
       if ((e = gram_inverse(w.Vt, n, w.ldv, L.h, bs, w.GV)) != hipSuccess) return e;
-      rw_product(L, w, L.h, bs, w.Yt, st);
+      rw_product(L, w, L.h, bs, s, w.Yt, st);
       if ((e = join()) != hipSuccess) return e;
       solve(w, bs, w.Yt, w.Ft, m, st);
       select_rows(w.Ft, m, w.ldu, bs, L.tau, nullptr, 0, w.Ut, w.PHC, w.flags, 0, st);
@@ -1119,7 +1369,7 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops) {
     hipLaunchKernelGGL(scales_kernel, dim3(1), dim3(256), 0, st, w.Md, w.GU, w.GV, bs, k0, L.T, w.d, L.D, L.energy,
                        w.st, w.flags, L.stats);
     hipLaunchKernelGGL(update_kernel, dim3((n + 63) / 64, (m + 63) / 64), dim3(256), 0, st, L.R, L.ldr, m, n, w.Ut,
-                       w.ldu, w.Vt, w.ldv, w.d, bs, w.flags);
+                       w.ldu, w.Vt, w.ldv, w.d, bs, w.flags, w.rmax + kMaxWords * ((s + 1) & 1));
     hipLaunchKernelGGL(emit_kernel, dim3(256), dim3(256), 0, st, w.Ut, w.ldu, w.Vt, w.ldv, m, n, bs, k0, L.Bp, L.Cp,
                        w.flags);
     fl += 2.0 * m * n * bs;
