@@ -829,6 +829,63 @@ __global__ void __launch_bounds__(256) apply_kernel(const double* __restrict__ A
   }
 }
 
+// ---- out (bs x ncols) = A B for bs <= kSpdMax (A bs x bs, B bs x ncols), fp64 MFMA, K = bs.
+// Workgroup: one 16-column strip of B (staged in LDS) x all bs rows; wave w takes the row tiles
+// w, w + 4, ...  Loads of A run 8 k-steps ahead of the MFMAs.
+template <int NRW>
+__global__ void __launch_bounds__(256) apply_strip_kernel(const double* __restrict__ A, int bs, const double* Bm,
+                                                          double* out, int ncols) {
+  __shared__ double Bs[kSpdMax][16];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int lr = lane & 15, lk = lane >> 4;
+  const int col0 = blockIdx.x * 16;
+  for (int x = tid; x < bs * 16; x += 256) {
+    const int k = x >> 4, c = x & 15;
+    Bs[k][c] = col0 + c < ncols ? Bm[(size_t)k * ncols + col0 + c] : 0.0;
+  }
+  __syncthreads();
+  const int ntiles = (bs + 15) / 16;
+  dbl4 acc[NRW];
+  const double* ap[NRW];
+  bool rok[NRW];
+#pragma unroll
+  for (int u = 0; u < NRW; ++u) {
+    acc[u] = (dbl4){0.0, 0.0, 0.0, 0.0};
+    const int r = (wid + 4 * u) * 16 + lr;
+    rok[u] = wid + 4 * u < ntiles && r < bs;
+    ap[u] = A + (size_t)(rok[u] ? r : 0) * bs;
+  }
+  constexpr int kAhead = 8;  // k-steps of 4 whose A operands are loaded together
+  for (int k0 = 0; k0 < bs; k0 += 4 * kAhead) {
+    double av[kAhead][NRW];
+#pragma unroll
+    for (int st = 0; st < kAhead; ++st) {
+      const int k = k0 + 4 * st + lk;
+#pragma unroll
+      for (int u = 0; u < NRW; ++u) av[st][u] = (rok[u] && k < bs) ? ap[u][k] : 0.0;
+    }
+#pragma unroll
+    for (int st = 0; st < kAhead; ++st) {
+      const int k = k0 + 4 * st + lk;
+      const double bv = k < bs ? Bs[k][lr] : 0.0;
+#pragma unroll
+      for (int u = 0; u < NRW; ++u) acc[u] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[st][u], bv, acc[u], 0, 0, 0);
+    }
+  }
+  const int col = col0 + lr;
+  if (col < ncols) {
+#pragma unroll
+    for (int u = 0; u < NRW; ++u) {
+      if (wid + 4 * u >= ntiles) continue;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = (wid + 4 * u) * 16 + lk + 4 * q;
+        if (r < bs) out[(size_t)r * ncols + col] = acc[u][q];
+      }
+    }
+  }
+}
+
 // ---- Md[c] = sum_i U[c][i] Y[c][i] (one workgroup per component, fixed reduction order)
 __global__ void __launch_bounds__(256) rowdot_kernel(const int8_t* Ut, int ldu, const double* Yt, int m, double* Md) {
   __shared__ double red[4];
@@ -1001,16 +1058,21 @@ __global__ void __launch_bounds__(256) update_kernel(float* R, int ldr, int m, i
                                                      const int8_t* Vt, int ldv, const float* dvec, int bs,
                                                      const int* flags, unsigned* rmax_next) {
   if (flags[0]) return;
-  __shared__ int8_t Us[256][64 + 4];
-  __shared__ int8_t Vs[256][64 + 4];
+  __shared__ __align__(16) int8_t Us[256][64 + 16];
+  __shared__ __align__(16) int8_t Vs[256][64 + 16];
   __shared__ float ds[256];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
   const int bs4 = (bs + 3) & ~3;
-  for (int x = tid; x < bs4 * 64; x += 256) {
-    const int c = x / 64, r = x % 64;
-    Us[c][r] = (c < bs && i0 + r < m) ? Ut[(size_t)c * ldu + i0 + r] : (int8_t)0;
-    Vs[c][r] = (c < bs && j0 + r < n) ? Vt[(size_t)c * ldv + j0 + r] : (int8_t)0;
+  // 16-byte pieces: rows of Ut / Vt are zero-padded to a multiple of 16, and i0, j0 are multiples
+  // of 64, so a piece is either inside the padded row or past it
+  for (int x = tid; x < bs4 * 4; x += 256) {
+    const int c = x >> 2, q = (x & 3) * 16;
+    const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+    *reinterpret_cast<uint4*>(&Us[c][q]) =
+        (c < bs && i0 + q < ldu) ? *reinterpret_cast<const uint4*>(Ut + (size_t)c * ldu + i0 + q) : z;
+    *reinterpret_cast<uint4*>(&Vs[c][q]) =
+        (c < bs && j0 + q < ldv) ? *reinterpret_cast<const uint4*>(Vt + (size_t)c * ldv + j0 + q) : z;
   }
   for (int c = tid; c < bs4; c += 256) ds[c] = c < bs ? dvec[c] : 0.0f;
   __syncthreads();
@@ -1270,7 +1332,11 @@ static void apply(const double* A, int bs, const double* Bm, double* out, int nc
 // bs > kSpdMax; in and out may not alias
 static void solve(const BlockWs& w, int bs, const double* in, double* out, int ncols, hipStream_t st) {
   if (bs <= kSpdMax) {
-    apply<false>(w.Li, bs, in, out, ncols, st);
+    const dim3 grid((ncols + 15) / 16);
+    if (bs <= 64)
+      hipLaunchKernelGGL(apply_strip_kernel<1>, grid, dim3(256), 0, st, w.Li, bs, in, out, ncols);
+    else
+      hipLaunchKernelGGL(apply_strip_kernel<2>, grid, dim3(256), 0, st, w.Li, bs, in, out, ncols);
     return;
   }
   apply<false>(w.Li, bs, in, w.Tmp, ncols, st);
