@@ -1384,12 +1384,13 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops) {
   SideStream* ss = nullptr;
   hipError_t e = side_stream(&ss);
   if (e != hipSuccess) return e;
-  // G and its inverse factor on the side stream, after everything queued so far on st
+  // G (on st: a short kernel that would otherwise wait for CUs behind the contraction), then its
+  // inverse on the side stream, concurrently with the residual contraction queued next on st
   auto gram_inverse = [&](const int8_t* T, int len, int ldt, const float* wt, int bs, double* G) -> hipError_t {
     hipError_t r;
+    gram_product(w, T, len, ldt, wt, bs, G, st);
     if ((r = hipEventRecord(ss->fork, st)) != hipSuccess) return r;
     if ((r = hipStreamWaitEvent(ss->s, ss->fork, 0)) != hipSuccess) return r;
-    gram_product(w, T, len, ldt, wt, bs, G, ss->s);
     chol_inverse(w, G, bs, ss->s);
     return hipEventRecord(ss->join, ss->s);
   };
