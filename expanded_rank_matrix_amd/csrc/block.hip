@@ -37,8 +37,6 @@ struct BlockWs {
   double* X;       // b x n: U^T R
   double* Z;       // b x max(m, n): G (V-step target)
   double* Tmp;     // b x max(m, n): L^-1 times the right-hand sides
-  double* part;    // split-K partials of the residual contractions
-  double* gpart;   // split-K partials of the Grams (side stream)
   double* GU;      // b x b
   double* GV;      // b x b
   double* Li;      // b x b: (G + eps I)^-1 for b <= kSpdMax, else the inverse Cholesky factor
@@ -50,11 +48,11 @@ struct BlockWs {
   int* used;       // m: rows used by sketch fallbacks within the block
   unsigned* rmax;  // [64 (s & 1) + w]: max |R| (fp32 bits) at the start of block s, spread over 64
                    // words w to keep the atomics of one update uncontended
+  uint8_t* hdig;   // kHDig x ldv: 7-bit digits of the fixed-point column weights (weighted only)
 };
 
 constexpr int kMaxWords = 64;      // words per residual-max slot (one per lane of a wave)
-constexpr int kMaxSplit = 8;       // split-K factor cap of the residual contractions
-constexpr int kMaxGramSplit = 64;  // ... and of the Grams
+constexpr int kHDig = 5;           // 7-bit digits of the fixed-point weights (35 bits)
 
 static size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -69,8 +67,6 @@ static void ws_layout(int m, int n, int b, F&& take) {
   take((void**)nullptr, bb * n * 8);
   take((void**)nullptr, bb * mx * 8);
   take((void**)nullptr, bb * mx * 8);
-  take((void**)nullptr, (size_t)kMaxSplit * bb * mx * 8);
-  take((void**)nullptr, (size_t)kMaxGramSplit * bb * bb * 8);
   take((void**)nullptr, bb * bb * 8);
   take((void**)nullptr, bb * bb * 8);
   take((void**)nullptr, bb * bb * 8);
@@ -81,6 +77,7 @@ static void ws_layout(int m, int n, int b, F&& take) {
   take((void**)nullptr, 64);
   take((void**)nullptr, (size_t)m * 4);
   take((void**)nullptr, 2 * kMaxWords * 4);
+  take((void**)nullptr, (size_t)kHDig * (size_t)((n + 15) & ~15));
 }
 
 static BlockWs carve(void* base, int m, int n, int b) {
@@ -103,8 +100,6 @@ static BlockWs carve(void* base, int m, int n, int b) {
   w.X = static_cast<double*>(ptrs[q++]);
   w.Z = static_cast<double*>(ptrs[q++]);
   w.Tmp = static_cast<double*>(ptrs[q++]);
-  w.part = static_cast<double*>(ptrs[q++]);
-  w.gpart = static_cast<double*>(ptrs[q++]);
   w.GU = static_cast<double*>(ptrs[q++]);
   w.GV = static_cast<double*>(ptrs[q++]);
   w.Li = static_cast<double*>(ptrs[q++]);
@@ -115,6 +110,7 @@ static BlockWs carve(void* base, int m, int n, int b) {
   w.flags = static_cast<int*>(ptrs[q++]);
   w.used = static_cast<int*>(ptrs[q++]);
   w.rmax = static_cast<unsigned*>(ptrs[q++]);
+  w.hdig = static_cast<uint8_t*>(ptrs[q++]);
   return w;
 }
 
@@ -148,106 +144,6 @@ __global__ void __launch_bounds__(256) omega_kernel(int8_t* Vt, int ldv, int bs,
       v = (splitmix64(key) >> 63) ? (int8_t)-1 : (int8_t)1;
     }
     Vt[x] = v;
-  }
-}
-
-// ---- weighted Gram T diag(h) T^T on v_mfma_f64_16x16x4f64 (the weights are not integers):
-// D(16x16) += A(16x4) B(4x16).  Lane l supplies A[l % 16][l / 16] and B[l / 16][l % 16];
-// D(i, j) lands in lane j + 16 (i % 4), register i / 4.  The k order inside a group of 16 is
-// permuted so that lane (r, kq) covers k = g + 4 kq + s at step s = 0..3: one 4-byte load then
-// feeds four MFMA steps.  Operands are loaded straight into registers, one group ahead.
-
-// part[split][c][i] = sum_{k in split} R[i][k] * h_k * T[c][k]   (rows of R x components)
-// Workgroup: 64 rows of R (16 per wave) x all components (NCT tiles of 16).
-template <int NCT, typename TR>
-__global__ void __launch_bounds__(256) contract_rw_kernel(const TR* R, int ldr, int rows, int K, const int8_t* T,
-                                                          int ldt, const float* h, int bs, int kspan,
-                                                          double* part) {
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int row = blockIdx.x * 64 + wid * 16 + (lane & 15);
-  const int kq = lane >> 4;
-  const int kb = blockIdx.y * kspan, ke = (kb + kspan < K) ? kb + kspan : K;
-  const bool rok = row < rows;
-  const TR* rp = R + (size_t)(rok ? row : 0) * ldr;
-  const int8_t* tp[NCT];
-#pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) {
-    const int c = ct * 16 + (lane & 15);
-    tp[ct] = T + (size_t)(c < bs ? c : 0) * ldt;
-  }
-  dbl4 acc[NCT];
-#pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) acc[ct] = (dbl4){0.0, 0.0, 0.0, 0.0};
-  auto load = [&](int g, float (&av)[4], unsigned (&tv)[NCT], float (&hv)[4]) {
-    const int k = g + 4 * kq;
-    const bool full = k + 4 <= ke;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) av[q] = 0.0f;
-    if (rok) {
-      if (sizeof(TR) == 4 && full) {
-        const float4 v = *reinterpret_cast<const float4*>(rp + k);
-        av[0] = v.x;
-        av[1] = v.y;
-        av[2] = v.z;
-        av[3] = v.w;
-      } else if (sizeof(TR) == 1 && full) {
-        const unsigned v = *reinterpret_cast<const unsigned*>(rp + k);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) av[q] = (float)(int8_t)(v >> (8 * q));
-      } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) av[q] = k + q < ke ? (float)rp[k + q] : 0.0f;
-      }
-    }
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      const int c = ct * 16 + (lane & 15);
-      unsigned v = 0u;
-      if (c < bs && k < ke) {
-        v = *reinterpret_cast<const unsigned*>(tp[ct] + k);  // rows are zero-padded to 16
-        if (!full) v &= 0xFFFFFFFFu >> (8 * (k + 4 - ke));
-      }
-      tv[ct] = v;
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) hv[q] = h ? (k + q < ke ? h[k + q] : 0.0f) : 1.0f;
-  };
-  float av[4], hv[4];
-  unsigned tv[NCT];
-  if (kb < ke) load(kb, av, tv, hv);
-  for (int g = kb; g < ke; g += 16) {
-    float av2[4], hv2[4];
-    unsigned tv2[NCT];
-    const bool more = g + 16 < ke;
-    if (more) load(g + 16, av2, tv2, hv2);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const double a = (double)av[q];
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        const double bv = (double)(hv[q] * (float)(int8_t)(tv[ct] >> (8 * q)));
-        acc[ct] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, bv, acc[ct], 0, 0, 0);
-      }
-    }
-    if (more) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        av[q] = av2[q];
-        hv[q] = hv2[q];
-      }
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) tv[ct] = tv2[ct];
-    }
-  }
-  double* out = part + (size_t)blockIdx.y * bs * rows;
-#pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) {
-    const int c = ct * 16 + (lane & 15);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = blockIdx.x * 64 + wid * 16 + (lane >> 4) + 4 * r;
-      if (c < bs && i < rows) out[(size_t)c * rows + i] = acc[ct][r];
-    }
   }
 }
 
@@ -479,6 +375,80 @@ __global__ void __launch_bounds__(1024) gram_i8_kernel(const int8_t* T, int ldt,
   }
 }
 
+// Column weights in fixed point: H_j = rint(h_j 2^(35 - EHm)) < 2^35 (h < 2^EHm), stored as five
+// unsigned 7-bit digits hdig[t][j] (zero past n, up to the padded length ldv).
+__global__ void __launch_bounds__(256) hdig_kernel(const float* h, int n, int ldv, int ehm, uint8_t* hdig) {
+  for (int j = blockIdx.x * 256 + threadIdx.x; j < ldv; j += gridDim.x * 256) {
+    const u64 H = j < n ? (u64)llrint(ldexp((double)h[j], kHDig * 7 - ehm)) : 0ull;
+#pragma unroll
+    for (int t = 0; t < kHDig; ++t) hdig[(size_t)t * ldv + j] = (uint8_t)((H >> (7 * t)) & 0x7Fu);
+  }
+}
+
+// bytes of t (each 0, 1 or -1) times bytes of d (each 0..127), as signed bytes
+__device__ __forceinline__ unsigned tmul_bytes(unsigned t, unsigned d) {
+  const unsigned nz = (t & 0x01010101u) * 0xFFu;         // 0xFF where t != 0
+  const unsigned ng = ((t >> 7) & 0x01010101u) * 0xFFu;  // 0xFF where t == -1
+  const unsigned nd = (0x80808080u - d) ^ 0x80808080u;   // per-byte -d (no borrows: d <= 0x7F)
+  return (d & nz & ~ng) | (nd & ng);
+}
+
+// G = T diag(h) T^T for ternary rows T with h in fixed point (hdig): sum_t 2^(7 t) T (T o dig_t)^T,
+// each digit product exact in int32, recombined exactly in fp64, times 2^-(35 - EHm).  The only
+// difference from the fp64 sum is the rounding of each h_j to the grid.  One workgroup of 16
+// waves per lower 16 x 16 tile; the waves split K and add in LDS in wave order.
+__global__ void __launch_bounds__(1024) gram_w_i8_kernel(const int8_t* T, int ldt, int K, int bs, const uint8_t* hdig,
+                                                         int ehm, double* G) {
+  __shared__ double red[16][256];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int lr = lane & 15, g = lane >> 4;
+  int ti = 0;
+  while ((ti + 1) * (ti + 2) / 2 <= (int)blockIdx.x) ++ti;
+  const int tj = (int)blockIdx.x - ti * (ti + 1) / 2;
+  const int ra = ti * 16 + lr, rb = tj * 16 + lr;
+  const int nch = (K + 63) / 64;
+  v4i acc[kHDig];
+#pragma unroll
+  for (int t = 0; t < kHDig; ++t) acc[t] = (v4i){0, 0, 0, 0};
+  for (int ch = wid; ch < nch; ch += 16) {
+    const int k = ch * 64 + 16 * g;
+    const bool ok = k < ldt;
+    const v4i a = (ok && ra < bs) ? load16(T + (size_t)ra * ldt + k) : (v4i){0, 0, 0, 0};
+    const v4i b = (ok && rb < bs) ? load16(T + (size_t)rb * ldt + k) : (v4i){0, 0, 0, 0};
+#pragma unroll
+    for (int t = 0; t < kHDig; ++t) {
+      const v4i d = ok ? load16(reinterpret_cast<const int8_t*>(hdig) + (size_t)t * ldt + k) : (v4i){0, 0, 0, 0};
+      v4i bd;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) bd[q] = (int)tmul_bytes((unsigned)b[q], (unsigned)d[q]);
+      acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bd, acc[t], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    double v = 0.0;
+#pragma unroll
+    for (int t = kHDig - 1; t >= 0; --t) v = v * 128.0 + (double)acc[t][q];
+    red[wid][q * 64 + lane] = v;
+  }
+  __syncthreads();
+  if (wid == 0) {
+    const double unit = ldexp(1.0, ehm - kHDig * 7);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      double v = 0.0;
+#pragma unroll
+      for (int w2 = 0; w2 < 16; ++w2) v += red[w2][q * 64 + lane];
+      v *= unit;
+      const int r = ti * 16 + 4 * g + q, c = tj * 16 + lr;
+      if (r < bs && c < bs) {
+        G[(size_t)r * bs + c] = v;
+        G[(size_t)c * bs + r] = v;
+      }
+    }
+  }
+}
+
 __global__ void __launch_bounds__(256) zero_kernel(double* p, long long count) {
   for (long long x = blockIdx.x * 256ll + threadIdx.x; x < count; x += (long long)gridDim.x * 256) p[x] = 0.0;
 }
@@ -501,16 +471,6 @@ __global__ void __launch_bounds__(256) rmax_kernel(const float* R, int ldr, int 
     mx = wm[2] > mx ? wm[2] : mx;
     mx = wm[3] > mx ? wm[3] : mx;
     if (mx != 0u) atomicMax(words + blockIdx.x % kMaxWords, mx);
-  }
-}
-
-// out[x] = sum over splits (ascending) of part[s][x]
-__global__ void __launch_bounds__(256) reduce_splits_kernel(const double* part, int nsplit, long long count,
-                                                            double* out) {
-  for (long long x = blockIdx.x * 256ll + threadIdx.x; x < count; x += (long long)gridDim.x * 256) {
-    double acc = 0.0;
-    for (int s = 0; s < nsplit; ++s) acc += part[(size_t)s * count + x];
-    out[x] = acc;
   }
 }
 
@@ -1182,43 +1142,6 @@ __global__ void __launch_bounds__(256) zero_check_kernel(const float* R, int ldr
   }
 }
 
-template <int NCT, typename TR>
-static void launch_rw(const TR* R, int ldr, int rows, int K, const int8_t* T, int ldt, const float* h, int bs,
-                      int nsplit, double* part, hipStream_t st) {
-  const int kspan = ((K + nsplit - 1) / nsplit + 31) / 32 * 32;
-  hipLaunchKernelGGL((contract_rw_kernel<NCT, TR>), dim3((rows + 63) / 64, nsplit), dim3(256), 0, st, R, ldr, rows,
-                     K, T, ldt, h, bs, kspan, part);
-}
-
-// split-K factor: about 512 workgroups, at least 256 of K per split, at most cap splits
-static int splits_for(int tiles, int K, int cap) {
-  int s = (512 + tiles - 1) / tiles;
-  const int maxs = (K + 255) / 256;
-  s = s > maxs ? maxs : s;
-  s = s > cap ? cap : s;
-  return s < 1 ? 1 : s;
-}
-
-static void reduce_splits(const double* part, int ns, long long cnt, double* out, hipStream_t st) {
-  const long long nb = (cnt + 255) / 256;
-  hipLaunchKernelGGL(reduce_splits_kernel, dim3((unsigned)(nb < 4096 ? nb : 4096)), dim3(256), 0, st, part, ns, cnt,
-                     out);
-}
-
-// out[c][i] = sum_k R[i][k] h_k T[c][k] for R rows x K (ld ldr), T bs x K (ld ldt), split over K
-template <typename TR>
-static void rw_contract(const TR* R, int ldr, int rows, int K, const int8_t* T, int ldt, const float* h, int bs,
-                        int cap, double* part, double* out, hipStream_t st) {
-  const int ns = splits_for((rows + 63) / 64, K, cap);
-  const int nct = (bs + 15) / 16;
-  if (nct <= 1) launch_rw<1, TR>(R, ldr, rows, K, T, ldt, h, bs, ns, part, st);
-  else if (nct <= 2) launch_rw<2, TR>(R, ldr, rows, K, T, ldt, h, bs, ns, part, st);
-  else if (nct <= 4) launch_rw<4, TR>(R, ldr, rows, K, T, ldt, h, bs, ns, part, st);
-  else if (nct <= 8) launch_rw<8, TR>(R, ldr, rows, K, T, ldt, h, bs, ns, part, st);
-  else launch_rw<16, TR>(R, ldr, rows, K, T, ldt, h, bs, ns, part, st);
-  reduce_splits(part, ns, (long long)bs * rows, out, st);
-}
-
 // K splits of an int8 contraction with `tiles` workgroups per split: about 512 workgroups, at
 // least 256 of K per split, at most 16 splits; kspan is a multiple of the 64-wide k chunk.
 static int i8_splits(int tiles, int K, int* kspan) {
@@ -1239,13 +1162,16 @@ static void zero_fill(double* p, long long count, hipStream_t st) {
 // Y^T (bs x m) = (R diag(h) V^T)^T for V = Vt rows, on int8 MFMA with R in fixed point
 static void rw_product(const BlockLaunch& L, const BlockWs& w, const float* h, int bs, int sblk, double* outT,
                        hipStream_t st) {
-  const int nct = bs <= 16 ? 1 : (bs <= 32 ? 2 : 4);
+  const int nct = bs <= 16 ? 1 : (bs <= 32 ? 2 : (bs <= 64 ? 4 : 8));
   const int gx = (L.m + 63) / 64, gy = (bs + 16 * nct - 1) / (16 * nct);
   int kspan = 0;
   const int gz = i8_splits(gx * gy, L.n, &kspan);
   if (gz > 1) zero_fill(outT, (long long)bs * L.m, st);
   const dim3 grid(gx, gy, gz);
-  if (nct == 1)
+  if (nct == 8)
+    hipLaunchKernelGGL(rv_i8_kernel<8>, grid, dim3(256), 0, st, L.R, L.ldr, L.m, L.n, w.Vt, w.ldv, h, L.EHm, bs,
+                       w.rmax, sblk, kspan, outT);
+  else if (nct == 1)
     hipLaunchKernelGGL(rv_i8_kernel<1>, grid, dim3(256), 0, st, L.R, L.ldr, L.m, L.n, w.Vt, w.ldv, h, L.EHm, bs,
                        w.rmax, sblk, kspan, outT);
   else if (nct == 2)
@@ -1257,25 +1183,28 @@ static void rw_product(const BlockLaunch& L, const BlockWs& w, const float* h, i
 }
 
 // G (bs x bs) = T diag(w) T^T for ternary rows T (bs x len, ld ldt); integer-exact without weights
-static void gram_product(const BlockWs& w, const int8_t* T, int len, int ldt, const float* wt, int bs, double* G,
-                         hipStream_t st) {
+static void gram_product(const BlockWs& w, const int8_t* T, int len, int ldt, const float* wt, int ehm, int bs,
+                         double* G, hipStream_t st) {
+  const int nt = (bs + 15) / 16;
   if (!wt) {
-    const int nt = (bs + 15) / 16;
     hipLaunchKernelGGL(gram_i8_kernel, dim3(nt * (nt + 1) / 2), dim3(1024), 0, st, T, ldt, len, bs, G);
     return;
   }
-  rw_contract<int8_t>(T, ldt, bs, len, T, ldt, wt, bs, kMaxGramSplit, w.gpart, G, st);
+  hipLaunchKernelGGL(gram_w_i8_kernel, dim3(nt * (nt + 1) / 2), dim3(1024), 0, st, T, ldt, len, bs, w.hdig, ehm, G);
 }
 
 // X (bs x n) = U^T R, on int8 MFMA with R in fixed point
 static void utr_product(const BlockLaunch& L, const BlockWs& w, int bs, int sblk, hipStream_t st) {
-  const int nct = bs <= 16 ? 1 : (bs <= 32 ? 2 : 4);
+  const int nct = bs <= 16 ? 1 : (bs <= 32 ? 2 : (bs <= 64 ? 4 : 8));
   const int gx = (L.n + 63) / 64, gy = (bs + 16 * nct - 1) / (16 * nct);
   int kspan = 0;
   const int gz = i8_splits(gx * gy, L.m, &kspan);
   if (gz > 1) zero_fill(w.X, (long long)bs * L.n, st);
   const dim3 grid(gx, gy, gz);
-  if (nct == 1)
+  if (nct == 8)
+    hipLaunchKernelGGL(utr_i8_kernel<8>, grid, dim3(256), 0, st, L.R, L.ldr, L.m, L.n, w.Ut, w.ldu, bs, w.rmax,
+                       sblk, kspan, w.X);
+  else if (nct == 1)
     hipLaunchKernelGGL(utr_i8_kernel<1>, grid, dim3(256), 0, st, L.R, L.ldr, L.m, L.n, w.Ut, w.ldu, bs, w.rmax,
                        sblk, kspan, w.X);
   else if (nct == 2)
@@ -1291,12 +1220,10 @@ static void chol_inverse(const BlockWs& w, const double* G, int bs, hipStream_t 
   if (bs <= kSpdMax) {
     static bool attr_set[64] = {};  // once per device: dynamic LDS above 64 KB
     int dev = 0;
-    hipGetDevice(&dev);
-    if (dev >= 0 && dev < 64 && !attr_set[dev]) {
-      hipFuncSetAttribute((const void*)spd_inv_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                          (int)spd_lds_bytes(kSpdMax));
-      attr_set[dev] = true;
-    }
+    if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64 && !attr_set[dev] &&
+        hipFuncSetAttribute((const void*)spd_inv_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)spd_lds_bytes(kSpdMax)) == hipSuccess)
+      attr_set[dev] = true;  // a failure shows up as a launch error, checked by the caller
     hipLaunchKernelGGL(spd_inv_kernel, dim3(1), dim3(256), spd_lds_bytes(bs), st, G, bs, w.Li);
     return;
   }
@@ -1388,7 +1315,7 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops) {
   // inverse on the side stream, concurrently with the residual contraction queued next on st
   auto gram_inverse = [&](const int8_t* T, int len, int ldt, const float* wt, int bs, double* G) -> hipError_t {
     hipError_t r;
-    gram_product(w, T, len, ldt, wt, bs, G, st);
+    gram_product(w, T, len, ldt, wt, L.EHm, bs, G, st);
     if ((r = hipEventRecord(ss->fork, st)) != hipSuccess) return r;
     if ((r = hipStreamWaitEvent(ss->s, ss->fork, 0)) != hipSuccess) return r;
     chol_inverse(w, G, bs, ss->s);
@@ -1401,6 +1328,8 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops) {
     hipLaunchKernelGGL(rmax_kernel, dim3((unsigned)(nb < 2048 ? nb : 2048)), dim3(256), 0, st, L.R, L.ldr, m, n,
                        w.rmax);
   }
+  if (L.h)
+    hipLaunchKernelGGL(hdig_kernel, dim3((w.ldv + 255) / 256), dim3(256), 0, st, L.h, n, w.ldv, L.EHm, w.hdig);
   const int nblocks = (L.k + L.b - 1) / L.b;
   double fl = 0.0;
   for (int s = 0; s < nblocks; ++s) {
@@ -1431,7 +1360,7 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops) {
       fl += 4.0 * m * n * bs;
     }
     // scales against Q = R H V of the last U-step, then the update and the outputs
-    gram_product(w, w.Ut, m, w.ldu, nullptr, bs, w.GU, st);
+    gram_product(w, w.Ut, m, w.ldu, nullptr, 0, bs, w.GU, st);
     hipLaunchKernelGGL(rowdot_kernel, dim3(bs), dim3(256), 0, st, w.Ut, w.ldu, w.Yt, m, w.Md);
     hipLaunchKernelGGL(scales_kernel, dim3(1), dim3(256), 0, st, w.Md, w.GU, w.GV, bs, k0, L.T, w.d, L.D, L.energy,
                        w.st, w.flags, L.stats);
