@@ -1162,16 +1162,13 @@ static void zero_fill(double* p, long long count, hipStream_t st) {
 // Y^T (bs x m) = (R diag(h) V^T)^T for V = Vt rows, on int8 MFMA with R in fixed point
 static void rw_product(const BlockLaunch& L, const BlockWs& w, const float* h, int bs, int sblk, double* outT,
                        hipStream_t st) {
-  const int nct = bs <= 16 ? 1 : (bs <= 32 ? 2 : (bs <= 64 ? 4 : 8));
+  const int nct = bs <= 16 ? 1 : (bs <= 32 ? 2 : 4);  // 8 tiles: one wave per SIMD, slower
   const int gx = (L.m + 63) / 64, gy = (bs + 16 * nct - 1) / (16 * nct);
   int kspan = 0;
   const int gz = i8_splits(gx * gy, L.n, &kspan);
   if (gz > 1) zero_fill(outT, (long long)bs * L.m, st);
   const dim3 grid(gx, gy, gz);
-  if (nct == 8)
-    hipLaunchKernelGGL(rv_i8_kernel<8>, grid, dim3(256), 0, st, L.R, L.ldr, L.m, L.n, w.Vt, w.ldv, h, L.EHm, bs,
-                       w.rmax, sblk, kspan, outT);
-  else if (nct == 1)
+  if (nct == 1)
     hipLaunchKernelGGL(rv_i8_kernel<1>, grid, dim3(256), 0, st, L.R, L.ldr, L.m, L.n, w.Vt, w.ldv, h, L.EHm, bs,
                        w.rmax, sblk, kspan, outT);
   else if (nct == 2)
@@ -1195,16 +1192,13 @@ static void gram_product(const BlockWs& w, const int8_t* T, int len, int ldt, co
 
 // X (bs x n) = U^T R, on int8 MFMA with R in fixed point
 static void utr_product(const BlockLaunch& L, const BlockWs& w, int bs, int sblk, hipStream_t st) {
-  const int nct = bs <= 16 ? 1 : (bs <= 32 ? 2 : (bs <= 64 ? 4 : 8));
+  const int nct = bs <= 16 ? 1 : (bs <= 32 ? 2 : 4);  // 8 tiles: one wave per SIMD, slower
   const int gx = (L.n + 63) / 64, gy = (bs + 16 * nct - 1) / (16 * nct);
   int kspan = 0;
   const int gz = i8_splits(gx * gy, L.m, &kspan);
   if (gz > 1) zero_fill(w.X, (long long)bs * L.n, st);
   const dim3 grid(gx, gy, gz);
-  if (nct == 8)
-    hipLaunchKernelGGL(utr_i8_kernel<8>, grid, dim3(256), 0, st, L.R, L.ldr, L.m, L.n, w.Ut, w.ldu, bs, w.rmax,
-                       sblk, kspan, w.X);
-  else if (nct == 1)
+  if (nct == 1)
     hipLaunchKernelGGL(utr_i8_kernel<1>, grid, dim3(256), 0, st, L.R, L.ldr, L.m, L.n, w.Ut, w.ldu, bs, w.rmax,
                        sblk, kspan, w.X);
   else if (nct == 2)
