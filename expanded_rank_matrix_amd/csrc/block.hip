@@ -221,9 +221,9 @@ __global__ void __launch_bounds__(256) rv_i8_kernel(const float* R, int ldr, int
   for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[ct][t] = (v4i){0, 0, 0, 0};
-  for (int k0 = kb; k0 < ke; k0 += 64) {
+  // operands of the chunk at k0 + 16 g: 16 values of row i and 16 bytes of each component row
+  auto load = [&](int k0, float (&xv)[16], v4i (&tb)[NCT]) {
     const int k = k0 + 16 * g;
-    float xv[16];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -233,12 +233,24 @@ __global__ void __launch_bounds__(256) rv_i8_kernel(const float* R, int ldr, int
       xv[4 * q + 2] = v.z;
       xv[4 * q + 3] = v.w;
     }
-    v4i tb[NCT];
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
       const int c = c0 + ct * 16 + lr;
       tb[ct] = (c < bs && k < ke) ? load16(T + (size_t)c * ldt + k) : (v4i){0, 0, 0, 0};
     }
+  };
+  float xn[16];
+  v4i tn[NCT];
+  if (kb < ke) load(kb, xn, tn);
+  for (int k0 = kb; k0 < ke; k0 += 64) {  // the next chunk loads while this one is converted
+    const int k = k0 + 16 * g;
+    float xv[16];
+    v4i tb[NCT];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) xv[t] = xn[t];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) tb[ct] = tn[ct];
+    if (k0 + 64 < ke) load(k0 + 64, xn, tn);
     int nv[16];
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
@@ -293,17 +305,27 @@ __global__ void __launch_bounds__(256) utr_i8_kernel(const float* R, int ldr, in
   for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[ct][t] = (v4i){0, 0, 0, 0};
-  for (int k0 = kb; k0 < ke; k0 += 64) {
+  auto load = [&](int k0, float (&xv)[16], v4i (&ua)[NCT]) {
     const int k = k0 + 16 * g;
-    float xv[16];
 #pragma unroll
     for (int t = 0; t < 16; ++t) xv[t] = (jok && k + t < ke) ? R[(size_t)(k + t) * ldr + j] : 0.0f;
-    v4i ua[NCT];
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
       const int c = c0 + ct * 16 + lr;
       ua[ct] = (c < bs && k < ke) ? load16(U + (size_t)c * ldu + k) : (v4i){0, 0, 0, 0};
     }
+  };
+  float xn[16];
+  v4i un[NCT];
+  if (kb < ke) load(kb, xn, un);
+  for (int k0 = kb; k0 < ke; k0 += 64) {  // the next chunk loads while this one is converted
+    float xv[16];
+    v4i ua[NCT];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) xv[t] = xn[t];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) ua[ct] = un[ct];
+    if (k0 + 64 < ke) load(k0 + 64, xn, un);
     int nv[16];
 #pragma unroll
     for (int t = 0; t < 16; ++t) nv[t] = __float2int_rn(xv[t] * fscale);
@@ -655,15 +677,16 @@ __global__ void __launch_bounds__(256) spd_inv_kernel(const double* G, int bs, d
       for (int c = 0; c < 16; ++c) x[c] = 0.0;
 #pragma unroll
       for (int t = 0; t < 16; ++t) {
-        // row t of X = L^-1 is finished: x[c] held -sum_{j<t} L_tj X_jc
+        // row t of X = L^-1 is finished: x[c] held -sum_{j<t} L_tj X_jc (one scale per lane
+        // instead of a select per entry)
+        const double sc = r == t ? rk[t] : 1.0;
 #pragma unroll
-        for (int c = 0; c < t; ++c) x[c] = r == t ? x[c] * rk[t] : x[c];
+        for (int c = 0; c < t; ++c) x[c] *= sc;
         x[t] = r == t ? rk[t] : x[t];
+        // later rows r > t take -L_rt X_tc; the multiplier is zero for rows r <= t
+        const double lrt = r > t ? a[t] : 0.0;
 #pragma unroll
-        for (int c = 0; c <= t; ++c) {
-          const double xtc = readlane_f64(x[c], t);
-          x[c] = r > t ? fma(-a[t], xtc, x[c]) : x[c];
-        }
+        for (int c = 0; c <= t; ++c) x[c] = fma(-lrt, readlane_f64(x[c], t), x[c]);
       }
       if (lane < 16) {
 #pragma unroll
@@ -1024,6 +1047,18 @@ __global__ void __launch_bounds__(256) update_kernel(float* R, int ldr, int m, i
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
   const int bs4 = (bs + 3) & ~3;
+  // this lane's 16 residual entries, loaded first so that their latency overlaps the staging and
+  // the products
+  float rv[4][4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int j = j0 + t * 16 + (lane & 15);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = i0 + wid * 16 + (lane >> 4) + 4 * r;
+      rv[t][r] = (i < m && j < n) ? R[(size_t)i * ldr + j] : 0.0f;
+    }
+  }
   // 16-byte pieces: rows of Ut / Vt are zero-padded to a multiple of 16, and i0, j0 are multiples
   // of 64, so a piece is either inside the padded row or past it
   for (int x = tid; x < bs4 * 4; x += 256) {
@@ -1056,12 +1091,11 @@ __global__ void __launch_bounds__(256) update_kernel(float* R, int ldr, int m, i
     for (int r = 0; r < 4; ++r) {
       const int i = i0 + wid * 16 + (lane >> 4) + 4 * r;
       if (i < m && j < n) {
-        float* p = R + (size_t)i * ldr + j;
         const double s = acc[t][r];
-        float x = *p;
+        float x = rv[t][r];
         if (s != 0.0) {
           x = (float)((double)x - s);
-          *p = x;
+          R[(size_t)i * ldr + j] = x;
         }
         const unsigned b = __float_as_uint(x) & 0x7FFFFFFFu;
         mx = b > mx ? b : mx;
