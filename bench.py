@@ -21,7 +21,6 @@ import time
 import numpy as np
 
 HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E
-FP64_MFMA_PEAK_TFLOPS = 78.6  # MI355X dense fp64 matrix
 
 
 def log(*a):
@@ -147,11 +146,14 @@ def main():
                 "kernel": "seq_kernel (persistent)", "kernel_ms": kms,
                 "bytes_per_launch": stats["bytes_algorithmic"]}
     else:
-        achieved = stats["flops_algorithmic"] / (kms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": achieved, "peak": FP64_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / FP64_MFMA_PEAK_TFLOPS, "traffic": traffic,
-                "kernel": "block-ALS contractions", "kernel_ms": kms,
-                "flops_per_launch": stats["flops_algorithmic"]}
+        # The block path's contractions run on int8 MFMA with R in fixed point; they stream R once
+        # each, so the bound is HBM.  The fp64-equivalent rate of the same work is reported beside.
+        achieved = stats["bytes_algorithmic"] / (kms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+                "kernel": "block-ALS path (all kernels)", "kernel_ms": kms,
+                "bytes_per_launch": stats["bytes_algorithmic"],
+                "fp64_equivalent_tflops": stats["flops_algorithmic"] / (kms * 1e-3) / 1e12}
     res = {
         "metric": "ExTernD components fitted/sec + achieved GB/s at 2560x2560, mu=3",
         "source_digest": source_digest(),
@@ -168,7 +170,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "m": m, "n": n, "mu": c["mu"], "k": k, "tau": c["tau"],
                    "als_iters": c["als_iters"], "block": c["block"],
-                   "residual": "fp32 in HBM, fp64 accumulation",
+                   "residual": ("fp32 in HBM, fp64 accumulation" if c["block"] in (0, 1) else
+                                "fp32 in HBM; contractions exact on its 32-bit fixed-point image (int8 MFMA)"),
                    "energy_final": float(energy[-1]),
                    "passes": stats["passes"], "early_exits": stats["early_exits"]},
         "roofline": roof,

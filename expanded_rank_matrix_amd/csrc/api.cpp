@@ -183,7 +183,7 @@ int externd_decompose(const float* A, int64_t m, int64_t n, float mu, float tau,
       (void)hipEventDestroy(b);
     }
   } evg{e0, e1};
-  double flops = 0.0;
+  double flops = 0.0, blk_bytes = -1.0;
   if (b == 1) {
     float* RT = reinterpret_cast<float*>(base + o_RT);
     HIP_OR_FAIL(stage_transpose(A, mi, ni, RT, ldt, st));
@@ -238,7 +238,7 @@ int externd_decompose(const float* A, int64_t m, int64_t n, float mu, float tau,
     L.stats = dstats;
     L.ws = base + o_blk;
     HIP_OR_FAIL(hipEventRecord(e0, st));
-    HIP_OR_FAIL(block_run(L, st, &flops));
+    HIP_OR_FAIL(block_run(L, st, &flops, &blk_bytes));
     HIP_OR_FAIL(hipEventRecord(e1, st));
   }
   // final explicit energy from the residual
@@ -280,7 +280,7 @@ int externd_decompose(const float* A, int64_t m, int64_t n, float mu, float tau,
     stats->block = b;
     stats->energy_final_explicit = e0s > 0.0 ? 1.0 - er / e0s : 1.0;
     stats->kernel_ms = ms;
-    stats->bytes_algorithmic = hbytes;
+    stats->bytes_algorithmic = blk_bytes >= 0.0 ? blk_bytes : hbytes;
     stats->flops_algorithmic = flops;
     stats->seconds = std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count();
   }

@@ -1332,7 +1332,7 @@ static hipError_t side_stream(SideStream** out) {
   return hipSuccess;
 }
 
-hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops) {
+hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops, double* bytes) {
   if (L.b > 256) return hipErrorInvalidValue;
   const BlockWs w = carve(L.ws, L.m, L.n, L.b);
   const int m = L.m, n = L.n;
@@ -1359,7 +1359,8 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops) {
   if (L.h)
     hipLaunchKernelGGL(hdig_kernel, dim3((w.ldv + 255) / 256), dim3(256), 0, st, L.h, n, w.ldv, L.EHm, w.hdig);
   const int nblocks = (L.k + L.b - 1) / L.b;
-  double fl = 0.0;
+  double fl = 0.0, by = 0.0;  // multiply-adds of R by ternary operands; residual bytes read/written
+  const double rbytes = 4.0 * m * n;
   for (int s = 0; s < nblocks; ++s) {
     const int bs = (L.k - s * L.b) < L.b ? (L.k - s * L.b) : L.b;
     const int k0 = s * L.b;
@@ -1372,6 +1373,7 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops) {
     hipLaunchKernelGGL(fallback_kernel, dim3(1), dim3(512), 0, st, L.R, L.ldr, m, n, bs, w.Ut, w.ldu, w.PHC,
                        w.flags, w.used);
     fl += 2.0 * m * n * bs;
+    by += rbytes;
     for (int t = 0; t < L.T; ++t) {
       // V-step: G = (U^T U + eps I)^-1 U^T R, rows ternarized with weights h
       if ((e = gram_inverse(w.Ut, m, w.ldu, nullptr, bs, w.GU)) != hipSuccess) return e;
@@ -1386,6 +1388,7 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops) {
       solve(w, bs, w.Yt, w.Ft, m, st);
       select_rows(w.Ft, m, w.ldu, bs, L.tau, nullptr, 0, w.Ut, w.PHC, w.flags, 0, st);
       fl += 4.0 * m * n * bs;
+      by += 2.0 * rbytes;
     }
     // scales against Q = R H V of the last U-step, then the update and the outputs
     gram_product(w, w.Ut, m, w.ldu, nullptr, 0, bs, w.GU, st);
@@ -1397,9 +1400,11 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops) {
     hipLaunchKernelGGL(emit_kernel, dim3(256), dim3(256), 0, st, w.Ut, w.ldu, w.Vt, w.ldv, m, n, bs, k0, L.Bp, L.Cp,
                        w.flags);
     fl += 2.0 * m * n * bs;
+    by += 2.0 * rbytes;
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   *flops = fl;
+  *bytes = by;
   return hipGetLastError();
 }
 

@@ -69,6 +69,8 @@ struct BlockLaunch {
   void* ws;            // workspace (block_workspace_bytes)
 };
 size_t block_workspace_bytes(int m, int n, int b);
-hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops);
+// flops: multiply-adds of the residual by ternary operands x 2; bytes: residual bytes that the
+// contractions read and the updates read and write (4 m n per pass)
+hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops, double* bytes);
 
 }  // namespace externd
