@@ -69,6 +69,7 @@ def _load():
                                               ctypes.c_int, vp, vp, vp, vp, i64, vp, vp, vp,
                                               vp, vp, vp]
         lib.externd_oracle_matvec.restype = ctypes.c_int
+        lib.externd_oracle_apply.argtypes = [vp, vp, vp, i64, i64, i64, vp, i64, vp, ctypes.c_int]
         lib.externd_oracle_matvec.argtypes = [vp, i64, i64, vp, vp, ctypes.c_int, vp,
                                               ctypes.c_int]
         _lib = lib
@@ -222,3 +223,21 @@ def matvec(R, t, h=None, transpose: bool = False, threads: int = 0):
     _load().externd_oracle_matvec(_ptr(R), m, n, _ptr(t), _ptr(h), int(transpose), _ptr(out),
                                   threads)
     return out
+
+
+def apply(B, C, D, m: int, n: int, X, threads: int = 0):
+    """Y = (B diag(D) C X^T)^T from packed factors (k x words(m), k x words(n)); X is n or batch x n."""
+    B = np.ascontiguousarray(B, dtype=np.uint32)
+    C = np.ascontiguousarray(C, dtype=np.uint32)
+    D = np.ascontiguousarray(D, dtype=np.float32)
+    X = np.ascontiguousarray(X, dtype=np.float32)
+    single = X.ndim == 1
+    X2 = X.reshape(1, -1) if single else X
+    k = D.shape[0]
+    assert X2.shape[1] == n and B.shape == (k, words(m)) and C.shape == (k, words(n))
+    Y = np.zeros((X2.shape[0], m), dtype=np.float32)
+    rc = _load().externd_oracle_apply(_ptr(B), _ptr(C), _ptr(D), k, m, n, _ptr(X2), X2.shape[0], _ptr(Y),
+                                      threads)
+    if rc != 0:
+        raise ValueError(f"oracle apply failed ({rc})")
+    return Y[0] if single else Y

@@ -875,6 +875,46 @@ int externd_oracle_replay(const float* A, int64_t m, int64_t n, float mu, float 
                          Co, Do, gap_o, energy_replay, opts);
 }
 
+// Inference from the packed factors (ExTernD review, Significance: the factorisation stays free
+// of multiplications at inference, ternary additions and subtractions plus one scale per
+// component; pith.science report, the mask+sign storage assumption of Eq. 5):
+//   y = B diag(D) C x,  t_i = sum_j C_ij x_j,  s_i = D_i t_i,  y_r = sum_i B_ri s_i,
+// for each of `batch` vectors x (rows of X, n values) into the rows of Y (m values).  Sums in fp64
+// in ascending index order, y rounded once to fp32.  B is k x words(m) (row i = column i of B),
+// C is k x words(n).
+int externd_oracle_apply(const uint32_t* B, const uint32_t* C, const float* D, int64_t k, int64_t m,
+                         int64_t n, const float* X, int64_t batch, float* Y, int threads) {
+  if (k < 0 || m < 1 || n < 1 || batch < 0) return -1;
+  const int nt = threads > 0 ? threads : omp_get_max_threads();
+  const int64_t wm = externd_oracle_words(m), wn = externd_oracle_words(n);
+  for (int64_t b = 0; b < batch; ++b) {
+    const float* x = X + b * n;
+    std::vector<double> s(k);
+#pragma omp parallel for num_threads(nt) schedule(static)
+    for (int64_t i = 0; i < k; ++i) {
+      std::vector<int8_t> c(n);
+      unpack(C + i * wn, n, c.data());
+      double t = 0.0;
+      for (int64_t j = 0; j < n; ++j)
+        if (c[j] != 0) t += c[j] > 0 ? (double)x[j] : -(double)x[j];
+      s[i] = (double)D[i] * t;
+    }
+    std::vector<int8_t> bcol(k * m);
+#pragma omp parallel for num_threads(nt) schedule(static)
+    for (int64_t i = 0; i < k; ++i) unpack(B + i * wm, m, bcol.data() + i * m);
+#pragma omp parallel for num_threads(nt) schedule(static)
+    for (int64_t r = 0; r < m; ++r) {
+      double y = 0.0;
+      for (int64_t i = 0; i < k; ++i) {
+        const int8_t c = bcol[i * m + r];
+        if (c != 0) y += c > 0 ? s[i] : -s[i];
+      }
+      Y[b * m + r] = (float)y;
+    }
+  }
+  return 0;
+}
+
 int externd_oracle_matvec(const float* R, int64_t m, int64_t n, const int8_t* t, const float* h,
                           int transpose, double* out, int threads) {
   const int nt = threads > 0 ? threads : omp_get_max_threads();

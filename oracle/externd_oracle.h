@@ -64,6 +64,11 @@ int externd_oracle_replay(const float* A, int64_t m, int64_t n, float mu, float 
                           uint32_t* Bo, uint32_t* Co, float* Do, double* gap_o,
                           double* energy_replay, const externd_oracle_opts* opts);
 
+/* Inference from the packed factors: Y (batch x m) = (B diag(D) C X^T)^T for X (batch x n),
+ * fp64 sums in index order, one fp32 rounding.  B: k x words(m), C: k x words(n). */
+int externd_oracle_apply(const uint32_t* B, const uint32_t* C, const float* D, int64_t k, int64_t m,
+                         int64_t n, const float* X, int64_t batch, float* Y, int threads);
+
 /* Plain matvecs used by kernel-level parity tests: out = R^T u (transpose = 1) or R (h .* v). */
 int externd_oracle_matvec(const float* R, int64_t m, int64_t n, const int8_t* t, const float* h,
                           int transpose, double* out, int threads);
