@@ -65,6 +65,8 @@ def load():
         lib.externd_project.argtypes = [vp, i64, i64, f32, vp, vp, vp, vp]
         lib.externd_matvec.restype = ci
         lib.externd_matvec.argtypes = [vp, i64, i64, vp, vp, ci, vp, vp]
+        lib.externd_apply_factors.restype = ci
+        lib.externd_apply_factors.argtypes = [vp, vp, vp, i64, i64, i64, vp, i64, vp, vp]
         lib.externd_status_string.restype = ctypes.c_char_p
         lib.externd_status_string.argtypes = [ci]
         lib.externd_last_error.restype = ctypes.c_char_p
@@ -178,6 +180,30 @@ def matvec(R, t, h=None, transpose: bool = False, stream=None):
                                _dev_ptr(out), _stream_ptr(stream))
     _check(rc)
     return out
+
+
+def apply_factors(B, C, D, m: int, n: int, X, stream=None, out=None):
+    """Y = (B diag(D) C X^T)^T from packed factors (as returned by decompose) for X (n or batch x n,
+    fp32, device); returns Y (m or batch x m, fp32)."""
+    import torch
+
+    D = _require(D, torch.float32, "D")
+    X = _require(X, torch.float32, "X")
+    for t, name in ((B, "B"), (C, "C")):
+        if not (t.is_cuda and t.dtype in (torch.int32, torch.uint32) and t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous 32-bit CUDA tensor of packed words")
+    k = D.shape[0]
+    if B.shape != (k, packed_words(m)) or C.shape != (k, packed_words(n)):
+        raise ValueError("B, C must be k x packed_words(m), k x packed_words(n)")
+    single = X.dim() == 1
+    X2 = X.reshape(1, -1) if single else X
+    if X2.shape[1] != n:
+        raise ValueError("X must have n columns")
+    Y = out if out is not None else torch.empty((X2.shape[0], m), dtype=torch.float32, device=X.device)
+    rc = load().externd_apply_factors(_dev_ptr(B), _dev_ptr(C), _dev_ptr(D), k, m, n, _dev_ptr(X2),
+                                      X2.shape[0], _dev_ptr(Y), _stream_ptr(stream))
+    _check(rc)
+    return Y[0] if single else Y
 
 
 def unpack(packed, length: int) -> np.ndarray:

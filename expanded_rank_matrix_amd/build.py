@@ -12,7 +12,7 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 OUT = os.path.join(HERE, "libexternd.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
-SOURCES = ["api.cpp", "stage.hip", "seq.hip", "project.hip", "block.hip"]
+SOURCES = ["api.cpp", "stage.hip", "seq.hip", "project.hip", "block.hip", "apply.hip"]
 ARCH = os.environ.get("EXTERND_ARCH", "gfx950")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -323,6 +323,30 @@ int externd_project(const float* X, int64_t count, int64_t L, float tau, const f
   return EXTERND_OK;
 }
 
+int externd_apply_factors(const uint32_t* B_packed, const uint32_t* C_packed, const float* D, int64_t k, int64_t m,
+                          int64_t n, const float* X, int64_t batch, float* Y, void* stream) {
+  g_last_error.clear();
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (!B_packed || !C_packed || !D || !X || !Y) return fail(EXTERND_EINVAL, "null pointer argument");
+  if (k < 1 || k > 2147483647 || m < 1 || n < 1 || m > 2147483647 - 15 || n > 2147483647 - 15)
+    return fail(EXTERND_EINVAL, "need k, m, n >= 1 (and below 2^31)");
+  if (batch < 1 || batch > 65535) return fail(EXTERND_EINVAL, "need 1 <= batch <= 65535");
+  const size_t wsb = infer_workspace_bytes((int)k, (int)m, (int)batch);
+  void* p = nullptr;
+  if (hipMallocAsync(&p, wsb, st) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(EXTERND_ENOMEM, "workspace allocation failed");
+  }
+  struct F {
+    void* p;
+    hipStream_t s;
+    ~F() { (void)hipFreeAsync(p, s); }
+  } fg{p, st};
+  HIP_OR_FAIL(infer_run(B_packed, C_packed, D, (int)k, (int)m, (int)n, X, (int)batch, Y, p, st));
+  HIP_OR_FAIL(hipStreamSynchronize(st));
+  return EXTERND_OK;
+}
+
 int externd_matvec(const float* R, int64_t m, int64_t n, const int8_t* t, const float* h, int transpose, double* out,
                    void* stream) {
   g_last_error.clear();

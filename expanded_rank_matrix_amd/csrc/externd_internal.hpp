@@ -73,4 +73,9 @@ size_t block_workspace_bytes(int m, int n, int b);
 // contractions read and the updates read and write (4 m n per pass)
 hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops, double* bytes);
 
+// Inference from the packed factors (apply.hip)
+size_t infer_workspace_bytes(int k, int m, int batch);
+hipError_t infer_run(const uint32_t* B, const uint32_t* C, const float* D, int k, int m, int n, const float* X,
+                     int batch, float* Y, void* ws, hipStream_t st);
+
 }  // namespace externd

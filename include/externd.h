@@ -101,6 +101,22 @@ int externd_project(const float* X, int64_t count, int64_t L, float tau, const f
 int externd_matvec(const float* R, int64_t m, int64_t n, const int8_t* t, const float* h,
                    int transpose, double* out, void* stream);
 
+/* Inference straight from the packed factors (ExTernD review, Significance: ternary additions
+ * and subtractions plus one scale per component; pith.science report, the mask+sign storage of
+ * Eq. 5):  Y[b] = B diag(D) C X[b] for each of `batch` vectors, i.e.
+ *   s_i = D_i sum_j C_ij X[b][j],   Y[b][r] = sum_i B_ri s_i,
+ * with fp64 sums in a fixed order (deterministic) and one fp32 rounding of each output.
+ *   B_packed k x packed_words(m) uint32 (device): row i = column i of B, as externd_decompose
+ *   C_packed k x packed_words(n) uint32 (device): row i = row i of C
+ *   D        k fp32 (device)
+ *   X        batch x n fp32 row-major (device), read only
+ *   Y        batch x m fp32 row-major (device), written
+ * 1 <= k, m, n < 2^31, 1 <= batch <= 65535.  Inputs are not checked for NaN/Inf.  The call
+ * allocates its workspace (batch k + chunks x batch x m fp64) on `stream` and returns after the
+ * stream's work has completed; EXTERND_EINVAL / ENOMEM / EDEVICE as for externd_decompose. */
+int externd_apply_factors(const uint32_t* B_packed, const uint32_t* C_packed, const float* D, int64_t k,
+                          int64_t m, int64_t n, const float* X, int64_t batch, float* Y, void* stream);
+
 /* Human-readable name of a status code (static string). */
 const char* externd_status_string(int status);
 

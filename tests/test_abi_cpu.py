@@ -59,3 +59,16 @@ def test_invalid_arguments_rejected_before_device_work():
     assert rc == erm.EINVAL and "mu" in erm.last_error()
     rc = lib.externd_project(None, 1, 4, 0.0, None, None, None, None)
     assert rc == erm.EINVAL
+
+
+def test_apply_factors_arguments_rejected_before_device_work():
+    lib = erm.load()
+    fake = ctypes.c_void_p(16)  # never dereferenced: validation fails first
+    rc = lib.externd_apply_factors(None, fake, fake, 4, 4, 4, fake, 1, fake, None)
+    assert rc == erm.EINVAL and "null" in erm.last_error()
+    rc = lib.externd_apply_factors(fake, fake, fake, 0, 4, 4, fake, 1, fake, None)
+    assert rc == erm.EINVAL
+    rc = lib.externd_apply_factors(fake, fake, fake, 4, 4, 4, fake, 0, fake, None)
+    assert rc == erm.EINVAL and "batch" in erm.last_error()
+    rc = lib.externd_apply_factors(fake, fake, fake, 4, 4, 4, fake, 70000, fake, None)
+    assert rc == erm.EINVAL and "batch" in erm.last_error()
