@@ -93,6 +93,50 @@ def cpu_baseline(A, c, seconds_target=15.0):
             "sample": f"first {done} components of the same workload ({dt:.1f} s wall)"}
 
 
+def infer_bench(args, erm, torch, A, h, c, k, m, n, out, stream):
+    """Inference y = B diag(D) C x from the packed factors of one decomposition of the workload
+    (decomposed once, untimed); each step is one externd_apply_factors call on `batch` vectors
+    already in HBM.  The roofline counts the packed factors, D, x and y once per call."""
+    erm.decompose(A, c["mu"], c["tau"], h, c["als_iters"], c["block"], stream=stream, out=out)
+    X = torch.randn((args.batch, n), dtype=torch.float32, device="cuda")
+    Y = torch.empty((args.batch, m), dtype=torch.float32, device="cuda")
+    for _ in range(max(1, args.warmup)):
+        erm.apply_factors(out["B"], out["C"], out["D"], m, n, X, stream=stream, out=Y)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        erm.apply_factors(out["B"], out["C"], out["D"], m, n, X, stream=stream, out=Y)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = e0.elapsed_time(e1) / args.steps
+    nbytes = 4.0 * (out["B"].numel() + out["C"].numel() + k) + 4.0 * args.batch * (m + n)
+    achieved = nbytes / (gpu_ms * 1e-3) / 1e9
+    res = {
+        "metric": f"packed-factor inference vectors/s ({m}x{n}, k={k})",
+        "value": args.batch * args.steps / wall,
+        "unit": "vectors/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"infer_{args.workload}", "m": m, "n": n, "k": k, "batch": args.batch,
+                   "factors": "packed 2-bit B and C of one decomposition of the workload"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
+                     "kernel": "infer_c + infer_b + infer_reduce (one call)", "gpu_ms_per_call": gpu_ms,
+                     "bytes_per_call": nbytes},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -102,6 +146,9 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="run a plain copy of this many MiB first (counter calibration)")
+    ap.add_argument("--infer", action="store_true",
+                    help="time inference from the workload's packed factors instead of the decomposition")
+    ap.add_argument("--batch", type=int, default=1, help="vectors per inference call (--infer)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build runs the "
@@ -126,6 +173,9 @@ def main():
                D=torch.empty(k, dtype=torch.float32, device="cuda"),
                energy=torch.empty(k, dtype=torch.float64, device="cuda"))
     stream = torch.cuda.current_stream()
+    if args.infer:
+        infer_bench(args, erm, torch, A, h, c, k, m, n, out, stream)
+        return
     for _ in range(args.warmup):
         erm.decompose(A, c["mu"], c["tau"], h, c["als_iters"], c["block"], stream=stream, out=out)
     torch.cuda.synchronize()
