@@ -45,6 +45,8 @@ class _Opts(ctypes.Structure):
         ("energy_explicit", ctypes.POINTER(ctypes.c_double)),
         ("residual_fp64", ctypes.c_int),
         ("block_engine", ctypes.c_int),
+        ("energy_target", ctypes.c_double),
+        ("used", ctypes.POINTER(ctypes.c_int64)),
     ]
 
 
@@ -122,7 +124,7 @@ def project(x, tau: float = 0.0, h=None):
 
 
 def _make_opts(threads, safeguard, k_limit, gaps, counters, eexp, residual_fp64,
-               block_engine=False):
+               block_engine=False, energy_target=0.0, used=None):
     o = _Opts()
     o.threads = int(threads)
     o.safeguard = int(bool(safeguard))
@@ -133,15 +135,19 @@ def _make_opts(threads, safeguard, k_limit, gaps, counters, eexp, residual_fp64,
     o.energy_explicit = eexp.ctypes.data_as(dp) if eexp is not None else dp()
     o.residual_fp64 = int(bool(residual_fp64))
     o.block_engine = int(bool(block_engine))
+    o.energy_target = float(energy_target)
+    o.used = used.ctypes.data_as(ip) if used is not None else ip()
     return o
 
 
 def decompose(A, mu: float, tau: float = 0.0, h=None, als_iters: int = 4, block: int = 1,
               threads: int = 0, safeguard: bool = False, k_limit: int = 0,
-              residual_fp64: bool = False, block_engine: bool = False):
+              residual_fp64: bool = False, block_engine: bool = False,
+              energy_target: float = 0.0):
     """Free-running oracle decomposition.  Returns a dict with packed B, C, D, energy, gaps,
     counters (fallbacks, safeguard activations, ALS passes, zero components), the explicit
-    final energy and k."""
+    final energy, k and ``used`` (components fitted before an energy-target stop; all of
+    them without a target)."""
     A = np.ascontiguousarray(A, dtype=np.float32)
     h = _f32(h)
     m, n = A.shape
@@ -155,8 +161,9 @@ def decompose(A, mu: float, tau: float = 0.0, h=None, als_iters: int = 4, block:
     gaps = np.full(k, np.inf)
     counters = np.zeros(4, dtype=np.int64)
     eexp = np.zeros(1, dtype=np.float64)
+    used = np.zeros(1, dtype=np.int64)
     o = _make_opts(threads, safeguard, k_limit, gaps, counters, eexp, residual_fp64,
-                   block_engine)
+                   block_engine, energy_target, used)
     rc = _load().externd_oracle_decompose(_ptr(A), m, n, mu, tau, _ptr(h), als_iters, block,
                                           _ptr(B), _ptr(C), _ptr(D), _ptr(energy),
                                           ctypes.addressof(o))
@@ -167,7 +174,7 @@ def decompose(A, mu: float, tau: float = 0.0, h=None, als_iters: int = 4, block:
         b = resolve_block(block, m, n, k)
         kk = min(k, -(-kk // b) * b)
     return dict(B=B[:kk], C=C[:kk], D=D[:kk], energy=energy[:kk], gaps=gaps[:kk],
-                counters=counters, energy_explicit=float(eexp[0]), k=k)
+                counters=counters, energy_explicit=float(eexp[0]), k=k, used=int(used[0]))
 
 
 def resolve_block(block: int, m: int, n: int, k: int) -> int:

@@ -605,9 +605,13 @@ Block fit_block(State<RT>& st, int64_t s, int64_t bs) {
 }
 
 // Block energy bookkeeping for given factors on the current residual (before the update).
+// With target > 0 the walk ends after the first component whose energy reaches the target; the
+// return value is the number of components walked (bs when the target is not reached) and
+// *reached tells whether it was.
 template <typename RT>
-void block_energy(State<RT>& st, const std::vector<int8_t>& U, const std::vector<int8_t>& V,
-                  const std::vector<float>& d, int64_t bs, double* energy_out) {
+int64_t block_energy(State<RT>& st, const std::vector<int8_t>& U, const std::vector<int8_t>& V,
+                     const std::vector<float>& d, int64_t bs, double* energy_out, double target = 0.0,
+                     bool* reached = nullptr) {
   std::vector<double> Q;
   mul_rhv(st, V, bs, Q);
   std::vector<double> GU = gram(U, st.m, bs, nullptr), GV = gram(V, st.n, bs, st.h);
@@ -620,7 +624,12 @@ void block_energy(State<RT>& st, const std::vector<int8_t>& U, const std::vector
     const double dd = (double)d[c];
     st.E = st.E - (2.0 * dd * p - dd * dd * q);
     energy_out[c] = 1.0 - st.E / st.E0;
+    if (target > 0.0 && energy_out[c] >= target) {
+      if (reached) *reached = true;
+      return c + 1;
+    }
   }
+  return bs;
 }
 
 // R_ij <- fl32(R_ij - sum_c d_c U_ci V_cj), the inner sum in fp64 over c ascending.
@@ -679,12 +688,15 @@ int decompose_t(const float* A, int64_t m, int64_t n, float mu, float tau, const
   double* gaps = opts ? opts->gaps : nullptr;
   std::vector<int8_t> zu(m, 0), zv(n, 0);
   const int64_t b = resolve_block(block, m, n, k);
+  const double target = opts && opts->energy_target > 0.0 ? opts->energy_target : 0.0;
+  int64_t used = klim;  // components fitted before the energy target stopped the walk
   if (st.E0 == 0.0) {
     for (int64_t i = 0; i < klim; ++i) {
       emit(B, C, D, i, m, n, zu.data(), zv.data(), 0.0f);
       energy[i] = 1.0;
       if (gaps) gaps[i] = kInf;
     }
+    if (target > 0.0) used = 1;
   } else if (b == 1 && !(opts && opts->block_engine)) {
     bool dead = false;
     for (int64_t i = 0; i < klim; ++i) {
@@ -697,16 +709,20 @@ int decompose_t(const float* A, int64_t m, int64_t n, float mu, float tau, const
         emit(B, C, D, i, m, n, zu.data(), zv.data(), 0.0f);
         energy[i] = 1.0;
         if (gaps) gaps[i] = kInf;
-        continue;
+      } else {
+        if (c.fallback) st.fallbacks++;
+        if (sg && apply_safeguard(st, c)) st.safeguards++;
+        deflate(st, c.u.data(), c.v.data(), c.d);
+        const double dd = (double)c.d;
+        st.E = st.E - (2.0 * dd * c.p - dd * dd * c.q);
+        energy[i] = 1.0 - st.E / st.E0;
+        emit(B, C, D, i, m, n, c.u.data(), c.v.data(), c.d);
+        if (gaps) gaps[i] = c.gap;
       }
-      if (c.fallback) st.fallbacks++;
-      if (sg && apply_safeguard(st, c)) st.safeguards++;
-      deflate(st, c.u.data(), c.v.data(), c.d);
-      const double dd = (double)c.d;
-      st.E = st.E - (2.0 * dd * c.p - dd * dd * c.q);
-      energy[i] = 1.0 - st.E / st.E0;
-      emit(B, C, D, i, m, n, c.u.data(), c.v.data(), c.d);
-      if (gaps) gaps[i] = c.gap;
+      if (target > 0.0 && energy[i] >= target) {
+        used = i + 1;
+        break;
+      }
     }
   } else {
     const int64_t nblocks = (k + b - 1) / b;
@@ -718,22 +734,44 @@ int decompose_t(const float* A, int64_t m, int64_t n, float mu, float tau, const
       if (dead || bl.zero) {
         dead = true;
         st.E = 0.0;
-        for (int64_t c = 0; c < bs; ++c) {
+        // with a target, the first zero component (energy 1) ends the walk
+        const int64_t nz = target > 0.0 ? 1 : bs;
+        for (int64_t c = 0; c < nz; ++c) {
           emit(B, C, D, s * b + c, m, n, zu.data(), zv.data(), 0.0f);
           energy[s * b + c] = 1.0;
           if (gaps) gaps[s * b + c] = kInf;
           st.zeros++;
         }
+        if (target > 0.0) {
+          used = s * b + 1;
+          break;
+        }
         continue;
       }
-      block_energy(st, bl.U, bl.V, bl.d, bs, energy + s * b);
+      bool reached = false;
+      const int64_t kept = block_energy(st, bl.U, bl.V, bl.d, bs, energy + s * b, target, &reached);
+      for (int64_t c = kept; c < bs; ++c) bl.d[c] = 0.0f;  // dropped: neither applied nor emitted
       block_update(st, bl.U, bl.V, bl.d, bs);
-      for (int64_t c = 0; c < bs; ++c) {
+      for (int64_t c = 0; c < kept; ++c) {
         emit(B, C, D, s * b + c, m, n, bl.U.data() + c * m, bl.V.data() + c * n, bl.d[c]);
         if (gaps) gaps[s * b + c] = bl.gap[c];
       }
+      if (reached) {
+        used = s * b + kept;
+        break;
+      }
     }
   }
+  // components after the stop: zero, energy held
+  if (used < klim) {
+    const double held = energy[used - 1];
+    for (int64_t i = used; i < klim; ++i) {
+      emit(B, C, D, i, m, n, zu.data(), zv.data(), 0.0f);
+      energy[i] = held;
+      if (gaps) gaps[i] = kInf;
+    }
+  }
+  if (opts && opts->used) opts->used[0] = used;
   if (opts && opts->counters) {
     opts->counters[0] = st.fallbacks;
     opts->counters[1] = st.safeguards;

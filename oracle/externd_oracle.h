@@ -34,6 +34,9 @@ typedef struct {
   double* energy_explicit;  /* nullable, 1: 1 - ||R||^2_H / ||A||^2_H recomputed from R at the end */
   int residual_fp64;        /* 1 = keep the residual in fp64 instead of fp32 (precision study only) */
   int block_engine;         /* 1 = run the block engine even when b == 1 (invariant test) */
+  double energy_target;     /* in (0, 1]: stop after the first component whose energy >= target;
+                               later components are zero with the energy held; <= 0: off */
+  int64_t* used;            /* nullable, 1: components fitted before the stop (all when none) */
 } externd_oracle_opts;
 
 int64_t externd_oracle_rank(int64_t m, int64_t n, float mu);
@@ -44,7 +47,14 @@ int externd_oracle_project(const float* x, int64_t L, float tau, const float* h,
                            int8_t* v, double* out, int64_t* jstar, double* gap);
 
 /* Free-running decomposition.  block <= 1: sequential deflation; block >= 2: block-ALS;
- * block == -1: b = min(256, min(m,n)/8) (at least 1). */
+ * block == -1: b = min(256, min(m,n)/8) (at least 1).
+ * Energy target (pith.science free parameters: mu is the accuracy dial, set per matrix to reach
+ * a target energy): the greedy components do not depend on k, so fitting until the energy
+ * first reaches the target gives the per-matrix rank directly.  After the first component i
+ * with energy[i] >= target (a zero component of a vanished residual counts, its energy is 1),
+ * components i+1.. are zero with energy[i] repeated and gap +inf; on the block path the stop
+ * can fall inside a block, whose later components are then dropped (zero scale, not applied).
+ * The safeguard (Prop. 2) applies to the sequential engine only. */
 int externd_oracle_decompose(const float* A, int64_t m, int64_t n, float mu, float tau,
                              const float* h, int als_iters, int block,
                              uint32_t* B, uint32_t* C, float* D, double* energy,
