@@ -39,10 +39,19 @@ class Stats(ctypes.Structure):
         ("kernel_ms", ctypes.c_double),
         ("bytes_algorithmic", ctypes.c_double),
         ("flops_algorithmic", ctypes.c_double),
+        ("components_used", ctypes.c_int64),
+        ("safeguard_activations", ctypes.c_int64),
     ]
 
     def as_dict(self):
         return {name: getattr(self, name) for name, _ in self._fields_}
+
+
+class Options(ctypes.Structure):
+    _fields_ = [
+        ("energy_target", ctypes.c_double),
+        ("safeguard", ctypes.c_int),
+    ]
 
 
 def load():
@@ -61,6 +70,9 @@ def load():
         lib.externd_decompose.restype = ci
         lib.externd_decompose.argtypes = [vp, i64, i64, f32, f32, vp, ci, ci, vp, vp, vp, vp, vp,
                                           ctypes.POINTER(Stats)]
+        lib.externd_decompose_ex.restype = ci
+        lib.externd_decompose_ex.argtypes = [vp, i64, i64, f32, f32, vp, ci, ci, vp, vp, vp, vp,
+                                             ctypes.POINTER(Options), vp, ctypes.POINTER(Stats)]
         lib.externd_project.restype = ci
         lib.externd_project.argtypes = [vp, i64, i64, f32, vp, vp, vp, vp]
         lib.externd_matvec.restype = ci
@@ -118,12 +130,15 @@ def _require(t, dtype, name):
 
 
 def decompose(A, mu: float, tau: float = 0.0, h=None, als_iters: int = 4, block: int = 1,
-              stream=None, out=None):
-    """Run externd_decompose on a device fp32 matrix A (m x n).
+              stream=None, out=None, energy_target: float = 0.0, safeguard: bool = False):
+    """Run externd_decompose (externd_decompose_ex when an option is set) on a device fp32
+    matrix A (m x n).
 
     Returns dict(B, C, D, energy, stats): B (k x words(m)) and C (k x words(n)) packed uint32
     stored in int32 tensors, D fp32 (k), energy fp64 (k), stats dict.  ``out`` may supply
-    preallocated outputs as a dict with the same keys."""
+    preallocated outputs as a dict with the same keys.  ``energy_target`` in (0, 1] stops after
+    the first component whose energy reaches it (stats["components_used"]); ``safeguard`` turns
+    on the best single-entry safeguard (sequential path)."""
     import torch
 
     A = _require(A, torch.float32, "A")
@@ -141,9 +156,17 @@ def decompose(A, mu: float, tau: float = 0.0, h=None, als_iters: int = 4, block:
             energy=torch.empty(k, dtype=torch.float64, device=dev),
         )
     st = Stats()
-    rc = load().externd_decompose(_dev_ptr(A), m, n, mu, tau, _dev_ptr(h), als_iters, block,
-                                  _dev_ptr(out["B"]), _dev_ptr(out["C"]), _dev_ptr(out["D"]),
-                                  _dev_ptr(out["energy"]), _stream_ptr(stream), ctypes.byref(st))
+    if energy_target or safeguard:
+        opt = Options(float(energy_target), int(bool(safeguard)))
+        rc = load().externd_decompose_ex(_dev_ptr(A), m, n, mu, tau, _dev_ptr(h), als_iters, block,
+                                         _dev_ptr(out["B"]), _dev_ptr(out["C"]),
+                                         _dev_ptr(out["D"]), _dev_ptr(out["energy"]),
+                                         ctypes.byref(opt), _stream_ptr(stream), ctypes.byref(st))
+    else:
+        rc = load().externd_decompose(_dev_ptr(A), m, n, mu, tau, _dev_ptr(h), als_iters, block,
+                                      _dev_ptr(out["B"]), _dev_ptr(out["C"]), _dev_ptr(out["D"]),
+                                      _dev_ptr(out["energy"]), _stream_ptr(stream),
+                                      ctypes.byref(st))
     _check(rc)
     res = dict(out)
     res["stats"] = st.as_dict()

@@ -92,8 +92,20 @@ const char* externd_last_error(void) { return g_last_error.c_str(); }
 int externd_decompose(const float* A, int64_t m, int64_t n, float mu, float tau, const float* h, int als_iters,
                       int block, uint32_t* B_packed, uint32_t* C_packed, float* D, double* energy, void* stream,
                       externd_stats* stats) {
+  return externd_decompose_ex(A, m, n, mu, tau, h, als_iters, block, B_packed, C_packed, D, energy, nullptr, stream,
+                              stats);
+}
+
+int externd_decompose_ex(const float* A, int64_t m, int64_t n, float mu, float tau, const float* h, int als_iters,
+                         int block, uint32_t* B_packed, uint32_t* C_packed, float* D, double* energy,
+                         const externd_options* options, void* stream, externd_stats* stats) {
   const auto t0 = std::chrono::steady_clock::now();
   g_last_error.clear();
+  const double target = options ? options->energy_target : 0.0;
+  const int safeguard = options ? options->safeguard : 0;
+  if (!(target == 0.0 || (target > 0.0 && target <= 1.0)))
+    return fail(EXTERND_EINVAL, "energy_target must be 0 (off) or in (0, 1]");
+  if (safeguard != 0 && safeguard != 1) return fail(EXTERND_EINVAL, "safeguard must be 0 or 1");
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (!A || !B_packed || !C_packed || !D || !energy) return fail(EXTERND_EINVAL, "null pointer argument");
   if (m < 1 || n < 1) return fail(EXTERND_EINVAL, "m and n must be >= 1 (got %lld x %lld)", (long long)m, (long long)n);
@@ -106,6 +118,7 @@ int externd_decompose(const float* A, int64_t m, int64_t n, float mu, float tau,
   if (k < 1) return fail(EXTERND_EINVAL, "mu must be finite and > 0 with k = floor(mu min(m,n)) >= 1");
   int64_t b = block == -1 ? std::max<int64_t>(1, std::min<int64_t>(256, std::min(m, n) / 8)) : (block <= 1 ? 1 : block);
   if (b > k) b = k;
+  if (safeguard && b > 1) return fail(EXTERND_EINVAL, "the safeguard applies to the sequential path only (block resolved to %lld)", (long long)b);
   const int mi = (int)m, ni = (int)n, ki = (int)k, bi = (int)b;
   const int ldr = (ni + 3) & ~3, ldt = (mi + 3) & ~3;
 
@@ -136,7 +149,7 @@ int externd_decompose(const float* A, int64_t m, int64_t n, float mu, float tau,
     HIP_OR_FAIL(hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev));
     if (!seq_plan(mi, ni, h != nullptr, ncu, &grid, &rl))
       return fail(EXTERND_EINVAL, "problem too large for the sequential kernel's on-chip state (%d x %d)", mi, ni);
-    o_xf = take((size_t)2 * grid * sizeof(double));
+    o_xf = take((size_t)4 * grid * sizeof(double));
     o_rsg = take((size_t)grid * mi * sizeof(double));
   } else {
     o_blk = take(block_workspace_bytes(mi, ni, bi));
@@ -215,6 +228,8 @@ int externd_decompose(const float* A, int64_t m, int64_t n, float mu, float tau,
     L.grid = grid;
     L.tau = tau;
     L.spin_limit = spin_limit_from_env();
+    L.target = target;
+    L.safeguard = safeguard;
     HIP_OR_FAIL(hipEventRecord(e0, st));
     HIP_OR_FAIL(seq_launch(L, st));
     HIP_OR_FAIL(hipEventRecord(e1, st));
@@ -237,6 +252,7 @@ int externd_decompose(const float* A, int64_t m, int64_t n, float mu, float tau,
     L.energy = energy;
     L.stats = dstats;
     L.ws = base + o_blk;
+    L.target = target;
     HIP_OR_FAIL(hipEventRecord(e0, st));
     HIP_OR_FAIL(block_run(L, st, &flops, &blk_bytes));
     HIP_OR_FAIL(hipEventRecord(e1, st));
@@ -282,6 +298,8 @@ int externd_decompose(const float* A, int64_t m, int64_t n, float mu, float tau,
     stats->kernel_ms = ms;
     stats->bytes_algorithmic = blk_bytes >= 0.0 ? blk_bytes : hbytes;
     stats->flops_algorithmic = flops;
+    stats->components_used = hst[5] > 0 ? (int64_t)hst[5] : k;
+    stats->safeguard_activations = (int64_t)hst[4];
     stats->seconds = std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count();
   }
   return EXTERND_OK;

@@ -44,7 +44,8 @@ struct BlockWs {
   double* PHC;     // b x 3 selection results
   float* d;        // b
   double* st;      // [0] E, [1] E0
-  int* flags;      // [0] dead, [1] empty sketch columns, [2] fallbacks
+  int* flags;      // [0] dead, [1] empty sketch columns, [2] fallbacks, [3] energy target reached,
+                   // [4] components of the block kept (emitted)
   int* used;       // m: rows used by sketch fallbacks within the block
   unsigned* rmax;  // [64 (s & 1) + w]: max |R| (fp32 bits) at the start of block s, spread over 64
                    // words w to keep the atomics of one update uncontended
@@ -972,16 +973,21 @@ __global__ void __launch_bounds__(512) fallback_kernel(const float* R, int ldr, 
 //   p_t = Md_t - sum_{c < t} d_c (u_t . u_c) (v_c^T H v_t),   d_t = fp32(p_t / q_t),
 // the subtractions applied in ascending c (as the textbook loop does); the Gram of U is exactly
 // symmetric (integer entries), so row c is read for column c.
+// With target > 0 the energy walk ends at the first component whose energy reaches the target:
+// the later components of the block get d = 0 (not applied, emitted as zero) and the energy of
+// the last kept one.
 __global__ void __launch_bounds__(256) scales_kernel(const double* Md, const double* GU, const double* GV, int bs,
                                                      int k0, int T, float* dvec, float* D, double* energy,
-                                                     double* st, int* flags, u64* stats) {
+                                                     double* st, int* flags, u64* stats, double target) {
 #pragma clang fp contract(off)
   __shared__ float ds[256];
   __shared__ double ps[256], qs[256];
+  __shared__ int kept_s;
   const int tid = threadIdx.x;
   if (tid == 0) {
     if (flags[0]) {
-      if (st[1] > 0.0) stats[3] += (u64)bs;  // zero components (none counted when A = 0)
+      // zero components (none counted when A = 0); with a target only the first is fitted
+      if (st[1] > 0.0) stats[3] += (u64)(target > 0.0 ? 1 : bs);
     } else {
       stats[0] += (u64)(2 * T);   // ALS half-steps
       stats[2] += (u64)flags[2];  // sketch columns started from the largest entry
@@ -992,6 +998,10 @@ __global__ void __launch_bounds__(256) scales_kernel(const double* Md, const dou
       dvec[tid] = 0.0f;
       D[k0 + tid] = 0.0f;
       energy[k0 + tid] = 1.0;
+    }
+    if (tid == 0 && target > 0.0) {
+      flags[3] = 1;
+      stats[5] = (u64)(k0 + 1);
     }
     return;
   }
@@ -1018,19 +1028,32 @@ __global__ void __launch_bounds__(256) scales_kernel(const double* Md, const dou
     gv = gv2;
   }
   __syncthreads();
-  if (own) {
-    dvec[tid] = ds[tid];
-    D[k0 + tid] = ds[tid];
-  }
   if (tid == 0) {
     double E = st[0];
     const double E0 = st[1];
+    int kept = bs;
     for (int c = 0; c < bs; ++c) {
       const double dd = (double)ds[c];
       E = E - (2.0 * dd * ps[c] - dd * dd * qs[c]);
-      energy[k0 + c] = 1.0 - E / E0;
+      const double e = 1.0 - E / E0;
+      energy[k0 + c] = e;
+      if (target > 0.0 && e >= target) {
+        kept = c + 1;
+        for (int c2 = kept; c2 < bs; ++c2) energy[k0 + c2] = e;
+        flags[3] = 1;
+        stats[5] = (u64)(k0 + kept);
+        break;
+      }
     }
     st[0] = E;
+    flags[4] = kept;
+    kept_s = kept;
+  }
+  __syncthreads();
+  if (own) {
+    const float d = tid < kept_s ? ds[tid] : 0.0f;
+    dvec[tid] = d;
+    D[k0 + tid] = d;
   }
 }
 
@@ -1119,6 +1142,7 @@ __global__ void __launch_bounds__(256) emit_kernel(const int8_t* Ut, int ldu, co
                                                    int bs, int k0, uint32_t* Bp, uint32_t* Cp, const int* flags) {
   const int wm = (m + 15) / 16, wn = (n + 15) / 16;
   const bool dead = flags[0] != 0;
+  const int kept = flags[4];  // components past an energy-target stop are emitted as zero
   const long long totB = (long long)bs * wm, totC = (long long)bs * wn;
   for (long long x = blockIdx.x * 256ll + threadIdx.x; x < totB + totC; x += (long long)gridDim.x * 256) {
     const bool isB = x < totB;
@@ -1127,12 +1151,30 @@ __global__ void __launch_bounds__(256) emit_kernel(const int8_t* Ut, int ldu, co
     const int c = (int)(y / words), w = (int)(y - (long long)c * words);
     const int8_t* src = isB ? Ut + (size_t)c * ldu : Vt + (size_t)c * ldv;
     unsigned word = 0u;
-    if (!dead)
+    if (!dead && c < kept)
       for (int q = 0; q < 16; ++q) {
         const int i = w * 16 + q;
         if (i < len) word |= tcode(src[i]) << (2 * q);
       }
     (isB ? Bp : Cp)[(size_t)(k0 + c) * words + w] = word;
+  }
+}
+
+// components [from, k) after an energy-target stop: zero codes and scale, the energy of
+// component from - 1 held
+__global__ void __launch_bounds__(256) stop_fill_kernel(uint32_t* Bp, uint32_t* Cp, float* D, double* energy, int m,
+                                                        int n, int from, int k) {
+  const long long wm = (m + 15) / 16, wn = (n + 15) / 16;
+  const long long nb = (long long)(k - from) * wm, nc = (long long)(k - from) * wn;
+  const double held = energy[from - 1];
+  for (long long x = blockIdx.x * 256ll + threadIdx.x; x < nb + nc + (k - from); x += (long long)gridDim.x * 256) {
+    if (x < nb) Bp[(size_t)from * wm + x] = 0u;
+    else if (x < nb + nc) Cp[(size_t)from * wn + (x - nb)] = 0u;
+    else {
+      const int c = from + (int)(x - nb - nc);
+      D[c] = 0.0f;
+      energy[c] = held;
+    }
   }
 }
 
@@ -1152,6 +1194,8 @@ __global__ void block_init_kernel(const double* rowE, int m, double* st, int* fl
     flags[0] = E0 > 0.0 ? 0 : 1;
     flags[1] = 0;
     flags[2] = 0;
+    flags[3] = 0;
+    flags[4] = 0;
     for (int x = 0; x < 2 * kMaxWords; ++x) rmax[x] = 0u;
   }
 }
@@ -1394,7 +1438,7 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops, double
     gram_product(w, w.Ut, m, w.ldu, nullptr, 0, bs, w.GU, st);
     hipLaunchKernelGGL(rowdot_kernel, dim3(bs), dim3(256), 0, st, w.Ut, w.ldu, w.Yt, m, w.Md);
     hipLaunchKernelGGL(scales_kernel, dim3(1), dim3(256), 0, st, w.Md, w.GU, w.GV, bs, k0, L.T, w.d, L.D, L.energy,
-                       w.st, w.flags, L.stats);
+                       w.st, w.flags, L.stats, L.target);
     hipLaunchKernelGGL(update_kernel, dim3((n + 63) / 64, (m + 63) / 64), dim3(256), 0, st, L.R, L.ldr, m, n, w.Ut,
                        w.ldu, w.Vt, w.ldv, w.d, bs, w.flags, w.rmax + kMaxWords * ((s + 1) & 1));
     hipLaunchKernelGGL(emit_kernel, dim3(256), dim3(256), 0, st, w.Ut, w.ldu, w.Vt, w.ldv, m, n, bs, k0, L.Bp, L.Cp,
@@ -1402,6 +1446,17 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops, double
     fl += 2.0 * m * n * bs;
     by += 2.0 * rbytes;
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (L.target > 0.0 && k0 + bs < L.k) {
+      // the host learns of a stop before queueing the next block (one 4-byte read per block)
+      int reached = 0;
+      if ((e = hipMemcpyAsync(&reached, w.flags + 3, sizeof(int), hipMemcpyDeviceToHost, st)) != hipSuccess) return e;
+      if ((e = hipStreamSynchronize(st)) != hipSuccess) return e;
+      if (reached) {
+        hipLaunchKernelGGL(stop_fill_kernel, dim3(256), dim3(256), 0, st, L.Bp, L.Cp, L.D, L.energy, m, n, k0 + bs,
+                           L.k);
+        break;
+      }
+    }
   }
   *flops = fl;
   *bytes = by;

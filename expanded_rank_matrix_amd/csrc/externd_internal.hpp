@@ -29,6 +29,8 @@ struct SeqLaunch {
   bool rl;  // R slab resident in LDS
   float tau;
   unsigned spin_limit;
+  double target = 0.0;  // > 0: stop once the energy reaches it
+  int safeguard = 0;    // 1: Prop. 2 best single-entry safeguard
 };
 size_t seq_smem_bytes(int m, int n, bool weighted, int G, bool rl);
 // Grid size (one workgroup per CU at most) and whether the R slab fits in LDS; 0 if the problem
@@ -67,6 +69,7 @@ struct BlockLaunch {
   double* energy;
   u64* stats;
   void* ws;            // workspace (block_workspace_bytes)
+  double target = 0.0; // > 0: stop once the energy reaches it
 };
 size_t block_workspace_bytes(int m, int n, int b);
 // flops: multiply-adds of the residual by ternary operands x 2; bytes: residual bytes that the

@@ -38,7 +38,7 @@ struct SeqArgs {
   const double* rowE;  // m
   double* xz;          // m
   double* xw;          // n
-  double* xf;          // 2 * gridDim.x
+  double* xf;          // 4 * gridDim.x
   double* rsg;         // gridDim.x x m: private row-sum copies
   unsigned* bar;
   uint32_t* Bp;
@@ -46,10 +46,13 @@ struct SeqArgs {
   float* D;
   double* energy;
   u64* stats;          // [0] passes [1] early exits [2] fallbacks [3] zero components
+                       // [4] safeguard activations [5] components fitted before a target stop
   double* bytes;       // algorithmic bytes
   int m, n, ldr, ldt, k, T, wm, wn, EHm;
   float tau;
   unsigned spin_limit;
+  double target;       // > 0: stop once the energy reaches it
+  int safeguard;       // 1: Prop. 2 best single-entry safeguard
 };
 
 __device__ __forceinline__ int code_at(const uint32_t* pk, int i) {
@@ -254,6 +257,45 @@ __device__ __forceinline__ void slab_deflate(float* base, int row_base, int ld, 
   __syncthreads();
 }
 
+// Per-workgroup part of the safeguard's search: the largest h_j R_ij^2 over rows [r0, r1)
+// (smallest row-major index on ties); wave w leaves (value, index, R_ij) in part[3w..3w+2].
+// Kept out of line: it runs only with the safeguard on and would otherwise add to the register
+// pressure of the whole persistent kernel.
+template <int NW>
+__device__ __noinline__ void best_entry_rows(const float* Rb, int Rrow0, int Rld, int r0, int r1, int n,
+                                             const float* hl, double* part) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  double best = 0.0, bidx = -1.0, bval = 0.0;
+  for (int i = r0 + wid; i < r1; i += NW) {
+    const float* row = Rb + (size_t)(i - Rrow0) * Rld;
+    for (int j = lane; j < n; j += 64) {
+      const double r = (double)row[j];
+      const double sv = (hl ? (double)hl[j] * r : r) * r;
+      const double idx = (double)i * (double)n + (double)j;
+      if (sv > best || (sv == best && sv > 0.0 && idx < bidx)) {
+        best = sv;
+        bidx = idx;
+        bval = r;
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const double b2 = __shfl_xor(best, o), i2 = __shfl_xor(bidx, o), v2 = __shfl_xor(bval, o);
+    if (b2 > best || (b2 == best && b2 > 0.0 && i2 < bidx)) {
+      best = b2;
+      bidx = i2;
+      bval = v2;
+    }
+  }
+  if (lane == 0) {
+    part[3 * wid] = best;
+    part[3 * wid + 1] = bidx;
+    part[3 * wid + 2] = bval;
+  }
+  __syncthreads();
+}
+
 template <int NT, bool WV, bool RL>
 __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
   constexpr int NW = NT / 64;
@@ -454,6 +496,56 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
     __syncthreads();
     return sh.ivals[0];
   };
+  // Prop. 2 safeguard: the single entry whose removal lowers the residual most, i.e. the largest
+  // h_j R_ij^2 (fp64, h_j R_ij first), smallest row-major index on ties, over the residual after
+  // the pending deflation.  All workgroups return the same (row, col, value); row -1 if R == 0,
+  // -2 on a barrier failure.
+  auto best_entry = [&](double* sbest, int* col, float* val) -> int {
+    if (have_pending && !r_applied) {
+      slab_deflate<NT>(Rb, Rrow0, Rld, n4 / 4, r0, r1, du, dv, pd);
+      r_applied = true;
+    }
+    best_entry_rows<NW>(Rb, Rrow0, Rld, r0, r1, n, WV ? hl : nullptr, part);
+    if (tid == 0) {
+      double bb = 0.0, bi = -1.0, bv = 0.0;
+      for (int w = 0; w < NW; ++w) {
+        const double v = part[3 * w], ix = part[3 * w + 1];
+        if (v > bb || (v == bb && v > 0.0 && ix < bi)) {
+          bb = v;
+          bi = ix;
+          bv = part[3 * w + 2];
+        }
+      }
+      st_dev(a.xf + 4 * g, bb);
+      st_dev(a.xf + 4 * g + 1, bi);
+      st_dev(a.xf + 4 * g + 2, bv);
+    }
+    ++epoch;
+    if (grid_barrier(a.bar, epoch, a.spin_limit, &bar_flag)) return -2;
+    if (tid == 0) {
+      double bb = 0.0, bi = -1.0, bv = 0.0;
+      for (int q = 0; q < G; ++q) {
+        const double v = ld_dev(a.xf + 4 * q), ix = ld_dev(a.xf + 4 * q + 1);
+        if (v > bb || (v == bb && v > 0.0 && ix < bi)) {
+          bb = v;
+          bi = ix;
+          bv = ld_dev(a.xf + 4 * q + 2);
+        }
+      }
+      const int row = bb > 0.0 ? (int)(bi / (double)n) : -1;
+      sh.ivals[0] = row;
+      sh.ivals[2] = row >= 0 ? (int)(bi - (double)row * (double)n) : 0;
+      part[0] = bb;
+      part[1] = bv;
+    }
+    __syncthreads();
+    *sbest = part[0];
+    *col = sh.ivals[2];
+    *val = (float)part[1];
+    const int row = sh.ivals[0];
+    __syncthreads();  // part is reused by the next pass
+    return row;
+  };
   auto set_unit_u = [&](int r) {
     for (int w = tid; w < wm; w += NT) pu[w] = (w == (r >> 4)) ? (1u << (2 * (r & 15))) : 0u;
     __syncthreads();
@@ -479,9 +571,12 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
     return r;
   };
 
-  for (int comp = 0; comp < a.k; ++comp) {
+  // an energy-target stop leaves the loop by break with comp at the last fitted component
+  int comp = 0;
+  for (; comp < a.k; ++comp) {
     if (dead) {
       emit_zero(comp);
+      if (a.target > 0.0) break;
       continue;
     }
     // ---------------- initial u: ternarized fp32 row sums
@@ -508,6 +603,7 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
       if (r < 0) {
         dead = true;
         emit_zero(comp);
+        if (a.target > 0.0) break;
         continue;
       }
       set_unit_u(r);
@@ -586,11 +682,35 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
     }
     if (dead) {
       emit_zero(comp);
+      if (a.target > 0.0) break;
       continue;
     }
-    // ---------------- scale, energy, outputs
-    const double q = (double)cnt_u * Hv;
-    const float d = (float)(p / q);
+    // ---------------- safeguard, scale, energy, outputs
+    double q = (double)cnt_u * Hv;
+    bool sg_on = false;
+    float d_sg = 0.0f;
+    if (a.safeguard) {
+      // keep whichever removes more energy: the ALS component (p^2 / q) or the best entry
+      double sbest;
+      int col;
+      float rv;
+      const int row = best_entry(&sbest, &col, &rv);
+      if (row == -2) return;
+      if (row >= 0 && sbest > p * p / q) {
+        sg_on = true;
+        set_unit_u(row);
+        for (int w = tid; w < wn; w += NT)
+          pv[w] = (w == (col >> 4)) ? ((rv > 0.0f ? 1u : 3u) << (2 * (col & 15))) : 0u;
+        const double hj = WV ? (double)hl[col] : 1.0;
+        d_sg = fabsf(rv);
+        p = hj * (double)d_sg;
+        q = hj;
+        cnt_u = 1;
+        sumv = rv > 0.0f ? 1 : -1;
+        __syncthreads();
+      }
+    }
+    const float d = sg_on ? d_sg : (float)(p / q);
     const double dd = (double)d;
     E = E - (2.0 * dd * p - dd * dd * q);
     if (g == 0) {
@@ -612,8 +732,10 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
         a.stats[0] += (u64)passes;
         if (early) a.stats[1] += 1ull;
         if (fallback) a.stats[2] += 1ull;
+        if (sg_on) a.stats[4] += 1ull;
         a.bytes[0] += 4.0 * (double)n * (double)un + 4.0 * (double)n * (double)pn +
-                      (double)usteps * 4.0 * (double)m * (double)n + vbytes;
+                      (double)usteps * 4.0 * (double)m * (double)n + vbytes +
+                      (a.safeguard ? 4.0 * (double)m * (double)n : 0.0);
       }
     }
     // row-sum recurrence and pending deflation
@@ -629,7 +751,20 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
     r_applied = false;
     rt_applied = false;
     __syncthreads();
+    if (a.target > 0.0 && 1.0 - E / E0 >= a.target) break;
   }
+  // components after an energy-target stop: zero, the energy held (1 after a zero component)
+  const int used = comp < a.k ? comp + 1 : a.k;
+  if (used < a.k && g == 0) {
+    const double held = dead ? 1.0 : 1.0 - E / E0;
+    for (long long x = tid; x < (long long)(a.k - used) * wm; x += NT) a.Bp[(size_t)used * wm + x] = 0u;
+    for (long long x = tid; x < (long long)(a.k - used) * wn; x += NT) a.Cp[(size_t)used * wn + x] = 0u;
+    for (int c = used + tid; c < a.k; c += NT) {
+      a.D[c] = 0.0f;
+      a.energy[c] = held;
+    }
+  }
+  if (g == 0 && tid == 0) a.stats[5] = (u64)used;
   // apply the last pending deflation to R (the transpose copy is no longer needed)
   if (have_pending && !r_applied) slab_deflate<NT>(Rb, Rrow0, Rld, n4 / 4, r0, r1, du, dv, pd);
   if (RL) {  // the final residual back to HBM
@@ -712,6 +847,8 @@ hipError_t seq_launch(const SeqLaunch& L, hipStream_t st) {
   a.EHm = L.EHm;
   a.tau = L.tau;
   a.spin_limit = L.spin_limit;
+  a.target = L.target;
+  a.safeguard = L.safeguard;
   const size_t smem = seq_smem_bytes(L.m, L.n, L.h != nullptr, L.grid, L.rl);
   if (L.h) return L.rl ? launch_one<true, true>(a, L.grid, smem, st) : launch_one<true, false>(a, L.grid, smem, st);
   return L.rl ? launch_one<false, true>(a, L.grid, smem, st) : launch_one<false, false>(a, L.grid, smem, st);

@@ -51,7 +51,29 @@ typedef struct {
   double kernel_ms;             /* device time of the decomposition kernels (HIP events) */
   double bytes_algorithmic;     /* residual bytes the method must move (sequential path) */
   double flops_algorithmic;     /* contraction flops of the block path */
+  int64_t components_used;      /* components fitted before an energy-target stop (k without one) */
+  int64_t safeguard_activations;/* components replaced by the best single entry (Prop. 2) */
 } externd_stats;
+
+/* (host) optional behaviour of externd_decompose_ex; all-zero = externd_decompose.
+ *   energy_target  0 = off; in (0, 1]: per-matrix rank by energy (pith.science, free parameters:
+ *                  mu is the accuracy dial, chosen per matrix to reach a target energy).  The
+ *                  greedy components do not depend on k, so fitting stops after the first
+ *                  component i with energy[i] >= energy_target (a zero component of a vanished
+ *                  residual counts, its energy is 1); components i+1 .. k-1 are written as zero
+ *                  codes with D = 0 and energy[i] repeated.  On the block path the stop can fall
+ *                  inside a block: the block's later components are dropped (not applied to the
+ *                  residual, written as zero).  stats->components_used = i + 1.
+ *   safeguard      0 or 1: Prop. 2's convergence safeguard (pith.science, major comment 1 on
+ *                  Appendix A): after the ALS of each component, if the largest h_j R_ij^2 over
+ *                  the residual (smallest row-major index on ties) exceeds the ALS component's
+ *                  p^2 / q, the component becomes u = e_i, v = sign(R_ij) e_j, d = |R_ij|.
+ *                  Sequential path only (block >= 2 after resolution is EXTERND_EINVAL).  Costs
+ *                  one extra read of the residual and one grid-wide exchange per component. */
+typedef struct {
+  double energy_target;
+  int safeguard;
+} externd_options;
 
 /* k = floor(mu * min(m, n) + 1e-9); -1 if m < 1, n < 1, mu not finite or > 0, or k < 1. */
 int64_t externd_rank(int64_t m, int64_t n, float mu);
@@ -81,6 +103,14 @@ int externd_decompose(const float* A, int64_t m, int64_t n, float mu, float tau,
                       const float* importance_weights, int als_iters, int block,
                       uint32_t* B_packed, uint32_t* C_packed, float* D, double* energy,
                       void* stream, externd_stats* stats);
+
+/* externd_decompose with options (host pointer, nullable = all off).  energy_target must be 0 or
+ * in (0, 1] and safeguard 0 or 1, else EXTERND_EINVAL.  With a target on the block path the host
+ * reads one flag after each block (a stream synchronisation per block). */
+int externd_decompose_ex(const float* A, int64_t m, int64_t n, float mu, float tau,
+                         const float* importance_weights, int als_iters, int block,
+                         uint32_t* B_packed, uint32_t* C_packed, float* D, double* energy,
+                         const externd_options* options, void* stream, externd_stats* stats);
 
 /* Ternary projection T_tau(x; h) of `count` independent vectors, the operator every V- and
  * U-step applies (reading of the adaptive ternarization operator, review Method; pith.science

@@ -16,14 +16,14 @@ D_RTOL = 1e-5
 E_ATOL = 1e-4
 
 
-def gpu_decompose(A, mu, tau, h, T, block):
+def gpu_decompose(A, mu, tau, h, T, block, **options):
     import torch
 
     import expanded_rank_matrix_amd as erm
 
     At = torch.from_numpy(np.ascontiguousarray(A)).cuda()
     ht = None if h is None else torch.from_numpy(np.ascontiguousarray(h)).cuda()
-    r = erm.decompose(At, mu, tau, ht, T, block)
+    r = erm.decompose(At, mu, tau, ht, T, block, **options)
     torch.cuda.synchronize()
     return dict(B=r["B"].cpu().numpy().view(np.uint32), C=r["C"].cpu().numpy().view(np.uint32),
                 D=r["D"].cpu().numpy(), energy=r["energy"].cpu().numpy(), stats=r["stats"], k=r["k"])

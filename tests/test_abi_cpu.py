@@ -72,3 +72,19 @@ def test_apply_factors_arguments_rejected_before_device_work():
     assert rc == erm.EINVAL and "batch" in erm.last_error()
     rc = lib.externd_apply_factors(fake, fake, fake, 4, 4, 4, fake, 70000, fake, None)
     assert rc == erm.EINVAL and "batch" in erm.last_error()
+
+
+def test_decompose_options_rejected_before_device_work():
+    lib = erm.load()
+    fake = ctypes.c_void_p(16)  # never dereferenced: validation fails first
+
+    def call(opt, block=1):
+        return lib.externd_decompose_ex(fake, 8, 8, 2.0, 0.0, None, 1, block, fake, fake, fake,
+                                        fake, ctypes.byref(opt), None, None)
+
+    for t in (1.5, -0.1, float("nan"), float("inf")):
+        assert call(erm.Options(t, 0)) == erm.EINVAL
+        assert "energy_target" in erm.last_error()
+    assert call(erm.Options(0.5, 2)) == erm.EINVAL and "safeguard" in erm.last_error()
+    # the safeguard is defined for the sequential path; block 4 resolves to b = 4 here
+    assert call(erm.Options(0.0, 1), block=4) == erm.EINVAL and "sequential" in erm.last_error()
