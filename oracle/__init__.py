@@ -47,6 +47,7 @@ class _Opts(ctypes.Structure):
         ("block_engine", ctypes.c_int),
         ("energy_target", ctypes.c_double),
         ("used", ctypes.POINTER(ctypes.c_int64)),
+        ("sweeps", ctypes.c_int),
     ]
 
 
@@ -124,7 +125,7 @@ def project(x, tau: float = 0.0, h=None):
 
 
 def _make_opts(threads, safeguard, k_limit, gaps, counters, eexp, residual_fp64,
-               block_engine=False, energy_target=0.0, used=None):
+               block_engine=False, energy_target=0.0, used=None, sweeps=0):
     o = _Opts()
     o.threads = int(threads)
     o.safeguard = int(bool(safeguard))
@@ -137,13 +138,14 @@ def _make_opts(threads, safeguard, k_limit, gaps, counters, eexp, residual_fp64,
     o.block_engine = int(bool(block_engine))
     o.energy_target = float(energy_target)
     o.used = used.ctypes.data_as(ip) if used is not None else ip()
+    o.sweeps = int(sweeps)
     return o
 
 
 def decompose(A, mu: float, tau: float = 0.0, h=None, als_iters: int = 4, block: int = 1,
               threads: int = 0, safeguard: bool = False, k_limit: int = 0,
               residual_fp64: bool = False, block_engine: bool = False,
-              energy_target: float = 0.0):
+              energy_target: float = 0.0, sweeps: int = 0):
     """Free-running oracle decomposition.  Returns a dict with packed B, C, D, energy, gaps,
     counters (fallbacks, safeguard activations, ALS passes, zero components), the explicit
     final energy, k and ``used`` (components fitted before an energy-target stop; all of
@@ -163,7 +165,7 @@ def decompose(A, mu: float, tau: float = 0.0, h=None, als_iters: int = 4, block:
     eexp = np.zeros(1, dtype=np.float64)
     used = np.zeros(1, dtype=np.int64)
     o = _make_opts(threads, safeguard, k_limit, gaps, counters, eexp, residual_fp64,
-                   block_engine, energy_target, used)
+                   block_engine, energy_target, used, sweeps)
     rc = _load().externd_oracle_decompose(_ptr(A), m, n, mu, tau, _ptr(h), als_iters, block,
                                           _ptr(B), _ptr(C), _ptr(D), _ptr(energy),
                                           ctypes.addressof(o))

@@ -263,17 +263,29 @@ bool set_fallback(const State<RT>& st, std::vector<int8_t>& u) {
   return true;
 }
 
+// One component by ALS against the current residual.  The initial u is the ternarized row sums
+// or, for a refinement sweep, the component's previous u (u_init).
 template <typename RT>
-Comp fit_component(State<RT>& st, bool keep_vectors) {
+Comp fit_component(State<RT>& st, bool keep_vectors, const int8_t* u_init = nullptr) {
   const int64_t m = st.m, n = st.n;
   Comp c;
   c.u.assign(m, 0);
   c.v.assign(n, 0);
   std::vector<float> xs(std::max(m, n));
   std::vector<double> w(n), z(m);
-  for (int64_t i = 0; i < m; ++i) xs[i] = (float)st.rs[i];
-  Proj pr = project(xs.data(), m, st.tau, nullptr, c.u.data());
-  double gap = pr.gap;
+  Proj pr;
+  double gap = kInf;
+  if (u_init) {
+    pr.j = 0;
+    for (int64_t i = 0; i < m; ++i) {
+      c.u[i] = u_init[i];
+      if (u_init[i]) pr.j++;
+    }
+  } else {
+    for (int64_t i = 0; i < m; ++i) xs[i] = (float)st.rs[i];
+    pr = project(xs.data(), m, st.tau, nullptr, c.u.data());
+    gap = pr.gap;
+  }
   if (pr.j == 0) {
     if (!set_fallback(st, c.u)) {
       c.zero = true;
@@ -524,7 +536,12 @@ void mul_utr(const State<RT>& st, const std::vector<int8_t>& U, int64_t bs, std:
 }
 
 template <typename RT>
-Block fit_block(State<RT>& st, int64_t s, int64_t bs) {
+Block als_block(State<RT>& st, Block& b);
+
+// With U_init (a refinement sweep) the ALS starts from the block's previous U instead of the
+// sketch; an all-zero column then stays zero (its Gram row is the regularisation alone).
+template <typename RT>
+Block fit_block(State<RT>& st, int64_t s, int64_t bs, const int8_t* U_init = nullptr) {
   const int64_t m = st.m, n = st.n;
   Block b;
   b.bs = bs;
@@ -533,6 +550,10 @@ Block fit_block(State<RT>& st, int64_t s, int64_t bs) {
   b.d.assign(bs, 0.0f);
   b.gap.assign(bs, kInf);
   std::vector<float> xs(std::max(m, n));
+  if (U_init) {
+    std::copy(U_init, U_init + bs * m, b.U.begin());
+    return als_block(st, b);
+  }
   // Sketch Y = R Omega, U[:,c] = T_tau(fp32 Y[:,c]).
   std::vector<double> Om(bs * n);
   for (int64_t c = 0; c < bs; ++c)
@@ -560,6 +581,14 @@ Block fit_block(State<RT>& st, int64_t s, int64_t bs) {
       b.gap[c] = std::min(b.gap[c], pr.gap);
     }
   }
+  return als_block(st, b);
+}
+
+// Block-ALS iterations from the block's initial U, then the scales.
+template <typename RT>
+Block als_block(State<RT>& st, Block& b) {
+  const int64_t m = st.m, n = st.n, bs = b.bs;
+  std::vector<float> xs(std::max(m, n));
   std::vector<double> X, Q, GV;
   for (int it = 0; it < st.T; ++it) {
     // V-step, Eq. 3: G = (U^T U + eps I)^-1 U^T R, each row ternarized with weights h.
@@ -674,6 +703,83 @@ void emit(uint32_t* B, uint32_t* C, float* D, int64_t i, int64_t m, int64_t n, c
   D[i] = d;
 }
 
+// Refinement sweeps (review, Results: sweeps add energy and lower the rank needed; reading:
+// backfitting).  Each sweep walks the fitted components (blocks) in order: their contribution is
+// added back to the residual, R <- fl32(R + d u v^T) (for a block the fp64 sum over its
+// components, then one rounding), they are refitted by ALS from their previous u (U), and the
+// new fit is deflated.  The energy bookkeeping continues through the sweep:
+//   |R + X|^2_H = |R|^2_H + 2 <R + X, X>_H - |X|^2_H,  X = sum_c d_c u_c v_c^T,
+// with <R + X, X>_H = sum_c d_c u_c^T (R + X) H v_c taken on the residual after the add-back;
+// energy[i] is the value after component i's refit in the last sweep.  Components past an
+// energy-target stop are not refitted.
+template <typename RT>
+void refine(State<RT>& st, uint32_t* B, uint32_t* C, float* D, double* energy, double* gaps, int64_t used,
+            int64_t b, int64_t k, int sweeps, bool sg) {
+  const int64_t m = st.m, n = st.n, wm = words_of(m), wn = words_of(n);
+  for (int sw = 0; sw < sweeps; ++sw) {
+    for (int64_t s0 = 0; s0 < used; s0 += b) {
+      const int64_t bs = std::min(std::min(b, k - s0), used - s0);
+      std::vector<int8_t> U(bs * m), V(bs * n);
+      std::vector<float> d(bs), nd(bs);
+      for (int64_t c = 0; c < bs; ++c) {
+        unpack(B + (s0 + c) * wm, m, U.data() + c * m);
+        unpack(C + (s0 + c) * wn, n, V.data() + c * n);
+        d[c] = D[s0 + c];
+        nd[c] = -d[c];
+      }
+      // add back, then the energy of the residual with the contribution restored
+      double cross = 0.0, xx = 0.0;
+      if (b == 1) {
+        if (d[0] != 0.0f) {
+          deflate(st, U.data(), V.data(), nd[0]);
+          double pp, qq;
+          exact_pq(st, U.data(), V.data(), &pp, &qq);
+          cross = (double)d[0] * pp;
+          xx = (double)d[0] * (double)d[0] * qq;
+        }
+      } else {
+        block_update(st, U, V, nd, bs);
+        std::vector<double> Q;
+        mul_rhv(st, V, bs, Q);
+        std::vector<double> GU = gram(U, m, bs, nullptr), GV = gram(V, n, bs, st.h);
+        for (int64_t c = 0; c < bs; ++c) {
+          double pp = 0.0;
+          for (int64_t i = 0; i < m; ++i)
+            if (U[c * m + i]) pp += (double)U[c * m + i] * Q[i * bs + c];
+          cross += (double)d[c] * pp;
+          for (int64_t c2 = 0; c2 < bs; ++c2) xx += (double)d[c] * (double)d[c2] * GU[c * bs + c2] * GV[c * bs + c2];
+        }
+      }
+      st.E = st.E + 2.0 * cross - xx;
+      if (b == 1) {
+        Comp c = fit_component(st, false, U.data());
+        if (c.zero) {  // the residual with the contribution restored is zero
+          emit(B, C, D, s0, m, n, c.u.data(), c.v.data(), 0.0f);
+          energy[s0] = 1.0 - st.E / st.E0;
+          if (gaps) gaps[s0] = kInf;
+          continue;
+        }
+        if (c.fallback) st.fallbacks++;
+        if (sg && apply_safeguard(st, c)) st.safeguards++;
+        deflate(st, c.u.data(), c.v.data(), c.d);
+        const double dd = (double)c.d;
+        st.E = st.E - (2.0 * dd * c.p - dd * dd * c.q);
+        energy[s0] = 1.0 - st.E / st.E0;
+        emit(B, C, D, s0, m, n, c.u.data(), c.v.data(), c.d);
+        if (gaps) gaps[s0] = c.gap;
+      } else {
+        Block bl = fit_block(st, s0 / b, bs, U.data());
+        block_energy(st, bl.U, bl.V, bl.d, bs, energy + s0);
+        block_update(st, bl.U, bl.V, bl.d, bs);
+        for (int64_t c = 0; c < bs; ++c) {
+          emit(B, C, D, s0 + c, m, n, bl.U.data() + c * m, bl.V.data() + c * n, bl.d[c]);
+          if (gaps) gaps[s0 + c] = bl.gap[c];
+        }
+      }
+    }
+  }
+}
+
 template <typename RT>
 int decompose_t(const float* A, int64_t m, int64_t n, float mu, float tau, const float* h, int T,
                 int block, uint32_t* B, uint32_t* C, float* D, double* energy,
@@ -770,6 +876,11 @@ int decompose_t(const float* A, int64_t m, int64_t n, float mu, float tau, const
       energy[i] = held;
       if (gaps) gaps[i] = kInf;
     }
+  }
+  const int sweeps = opts && opts->sweeps > 0 ? opts->sweeps : 0;
+  if (sweeps > 0 && st.E0 > 0.0) {
+    refine(st, B, C, D, energy, gaps, used, b == 1 && !(opts && opts->block_engine) ? 1 : b, k, sweeps, sg);
+    for (int64_t i = used; i < klim; ++i) energy[i] = energy[used - 1];
   }
   if (opts && opts->used) opts->used[0] = used;
   if (opts && opts->counters) {

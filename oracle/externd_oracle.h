@@ -37,6 +37,7 @@ typedef struct {
   double energy_target;     /* in (0, 1]: stop after the first component whose energy >= target;
                                later components are zero with the energy held; <= 0: off */
   int64_t* used;            /* nullable, 1: components fitted before the stop (all when none) */
+  int sweeps;               /* >= 1: refinement sweeps (backfitting) after the greedy pass */
 } externd_oracle_opts;
 
 int64_t externd_oracle_rank(int64_t m, int64_t n, float mu);
