@@ -51,6 +51,7 @@ class Options(ctypes.Structure):
     _fields_ = [
         ("energy_target", ctypes.c_double),
         ("safeguard", ctypes.c_int),
+        ("sweeps", ctypes.c_int),
     ]
 
 
@@ -130,7 +131,8 @@ def _require(t, dtype, name):
 
 
 def decompose(A, mu: float, tau: float = 0.0, h=None, als_iters: int = 4, block: int = 1,
-              stream=None, out=None, energy_target: float = 0.0, safeguard: bool = False):
+              stream=None, out=None, energy_target: float = 0.0, safeguard: bool = False,
+              sweeps: int = 0):
     """Run externd_decompose (externd_decompose_ex when an option is set) on a device fp32
     matrix A (m x n).
 
@@ -138,7 +140,8 @@ def decompose(A, mu: float, tau: float = 0.0, h=None, als_iters: int = 4, block:
     stored in int32 tensors, D fp32 (k), energy fp64 (k), stats dict.  ``out`` may supply
     preallocated outputs as a dict with the same keys.  ``energy_target`` in (0, 1] stops after
     the first component whose energy reaches it (stats["components_used"]); ``safeguard`` turns
-    on the best single-entry safeguard (sequential path)."""
+    on the best single-entry safeguard (sequential path); ``sweeps`` refinement sweeps refit
+    every component after the greedy pass."""
     import torch
 
     A = _require(A, torch.float32, "A")
@@ -156,8 +159,8 @@ def decompose(A, mu: float, tau: float = 0.0, h=None, als_iters: int = 4, block:
             energy=torch.empty(k, dtype=torch.float64, device=dev),
         )
     st = Stats()
-    if energy_target or safeguard:
-        opt = Options(float(energy_target), int(bool(safeguard)))
+    if energy_target or safeguard or sweeps:
+        opt = Options(float(energy_target), int(bool(safeguard)), int(sweeps))
         rc = load().externd_decompose_ex(_dev_ptr(A), m, n, mu, tau, _dev_ptr(h), als_iters, block,
                                          _dev_ptr(out["B"]), _dev_ptr(out["C"]),
                                          _dev_ptr(out["D"]), _dev_ptr(out["energy"]),

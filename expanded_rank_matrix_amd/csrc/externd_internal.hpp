@@ -31,6 +31,7 @@ struct SeqLaunch {
   unsigned spin_limit;
   double target = 0.0;  // > 0: stop once the energy reaches it
   int safeguard = 0;    // 1: Prop. 2 best single-entry safeguard
+  int sweeps = 0;       // refinement sweeps after the greedy pass
 };
 size_t seq_smem_bytes(int m, int n, bool weighted, int G, bool rl);
 // Grid size (one workgroup per CU at most) and whether the R slab fits in LDS; 0 if the problem

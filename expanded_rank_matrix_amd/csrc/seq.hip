@@ -53,6 +53,7 @@ struct SeqArgs {
   unsigned spin_limit;
   double target;       // > 0: stop once the energy reaches it
   int safeguard;       // 1: Prop. 2 best single-entry safeguard
+  int sweeps;          // refinement sweeps after the greedy pass
 };
 
 __device__ __forceinline__ int code_at(const uint32_t* pk, int i) {
@@ -296,7 +297,86 @@ __device__ __noinline__ void best_entry_rows(const float* Rb, int Rrow0, int Rld
   __syncthreads();
 }
 
-template <int NT, bool WV, bool RL>
+// Start of a refit in a refinement sweep: the pending deflation of the previous fit is applied to
+// this workgroup's rows of both residual copies (where not yet fused), then the component's
+// previous codes are read back (device-coherent) into du/dv (its add-back, the new pending
+// update) and pu (the ALS's initial u).  Workgroup 0 adds the deflation's bytes to *bytes.
+// Out of line: it runs only in sweeps and would otherwise add to the register pressure of the
+// persistent kernel.
+template <int NT>
+__device__ __noinline__ void refit_begin(float* Rb, int Rrow0, int Rld, int len4r, float* RT, int ldt, int len4t,
+                                         int r0, int r1, int c0, int c1, bool apply_r, bool apply_rt, float pd,
+                                         uint32_t* du, uint32_t* dv, uint32_t* pu, const uint32_t* Bk,
+                                         const uint32_t* Ck, int wm, int wn, double* bytes) {
+  __shared__ int cnt[2];
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    cnt[0] = 0;
+    cnt[1] = 0;
+  }
+  __syncthreads();
+  if (apply_r) slab_deflate<NT>(Rb, Rrow0, Rld, len4r, r0, r1, du, dv, pd);
+  if (apply_rt) slab_deflate<NT>(RT, 0, ldt, len4t, c0, c1, dv, du, pd);
+  if (bytes) {
+    int pu_n = 0, pv_n = 0;
+    if (apply_r)
+      for (int w = tid; w < wm; w += NT) pu_n += __popc((du[w] | (du[w] >> 1)) & 0x55555555u);
+    if (apply_rt)
+      for (int w = tid; w < wn; w += NT) pv_n += __popc((dv[w] | (dv[w] >> 1)) & 0x55555555u);
+    if (pu_n) atomicAdd(&cnt[0], pu_n);
+    if (pv_n) atomicAdd(&cnt[1], pv_n);
+  }
+  __syncthreads();
+  if (bytes && tid == 0)  // rows of R and of its transpose read and written
+    bytes[0] += 8.0 * (double)(len4r * 4) * (double)cnt[0] + 8.0 * (double)(len4t * 4) * (double)cnt[1];
+  for (int w = tid; w < wm; w += NT) {
+    const unsigned x = ld_dev(Bk + w);
+    du[w] = x;
+    pu[w] = x;
+  }
+  for (int w = tid; w < wn; w += NT) dv[w] = ld_dev(Ck + w);
+  __syncthreads();
+}
+
+// 2 d v^T H w - d^2 |u|^2 |v|^2_H for the exchanged w (dl) and the packed u, v: the change of
+// the energy when d u v^T is added back to the residual behind w = (R + d u v^T)^T u.  Sums in
+// a fixed order; each thread reads only the dl entries it stored itself.
+template <int NT>
+__device__ __noinline__ double addback_energy(const double* dl, const uint32_t* du, const uint32_t* dv,
+                                              const float* hl, int n, int wm, double d, double* part) {
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  double pv_acc = 0.0, hv_acc = 0.0, un_acc = 0.0;
+  for (int j = tid; j < n; j += NT) {
+    const int c = code_at(dv, j);
+    if (c != 0) {
+      const double hj = hl ? (double)hl[j] : 1.0;
+      pv_acc += (double)c * hj * dl[j];
+      hv_acc += hj;
+    }
+  }
+  for (int w = tid; w < wm; w += NT) un_acc += (double)__popc((du[w] | (du[w] >> 1)) & 0x55555555u);
+  pv_acc = wave_sum_f64(pv_acc);
+  hv_acc = wave_sum_f64(hv_acc);
+  un_acc = wave_sum_f64(un_acc);
+  __syncthreads();
+  if (lane == 0) {
+    part[3 * wid] = pv_acc;
+    part[3 * wid + 1] = hv_acc;
+    part[3 * wid + 2] = un_acc;
+  }
+  __syncthreads();
+  double pp = 0.0, hh = 0.0, uu = 0.0;
+  for (int w = 0; w < NW; ++w) {
+    pp += part[3 * w];
+    hh += part[3 * w + 1];
+    uu += part[3 * w + 2];
+  }
+  __syncthreads();
+  return 2.0 * d * pp - d * d * (uu * hh);
+}
+
+template <int NT, bool WV, bool RL, bool SW>
 __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
   constexpr int NW = NT / 64;
   extern __shared__ __align__(16) char smem[];
@@ -550,14 +630,16 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
     for (int w = tid; w < wm; w += NT) pu[w] = (w == (r >> 4)) ? (1u << (2 * (r & 15))) : 0u;
     __syncthreads();
   };
-  auto emit_zero = [&](int comp) {
+  // Component outputs are stored device-coherently: a refinement sweep reads them back from
+  // every workgroup.  counted = false for a refit that came out zero (energy from E).
+  auto emit_zero = [&](int comp, bool counted, double energy) {
     if (g == 0) {
-      for (int w = tid; w < wm; w += NT) a.Bp[(size_t)comp * wm + w] = 0u;
-      for (int w = tid; w < wn; w += NT) a.Cp[(size_t)comp * wn + w] = 0u;
+      for (int w = tid; w < wm; w += NT) st_dev(a.Bp + (size_t)comp * wm + w, 0u);
+      for (int w = tid; w < wn; w += NT) st_dev(a.Cp + (size_t)comp * wn + w, 0u);
       if (tid == 0) {
-        a.D[comp] = 0.0f;
-        a.energy[comp] = 1.0;
-        a.stats[3] += 1ull;
+        st_dev(reinterpret_cast<unsigned*>(a.D) + comp, 0u);
+        a.energy[comp] = energy;
+        if (counted) a.stats[3] += 1ull;
       }
     }
   };
@@ -571,11 +653,38 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
     return r;
   };
 
-  // an energy-target stop leaves the loop by break with comp at the last fitted component
+  // Pass 0 is the greedy pass over all k components; an energy-target stop leaves it by break
+  // with comp at the last fitted component.  Passes 1..sweeps refit the fitted components in
+  // order (backfitting): the previous fit's deflation is applied to both residual copies, the
+  // component's own contribution becomes the pending update (added back inside the refit's
+  // first passes), and the ALS starts from the component's previous u.
+  int used = a.k;
+  const int nsweeps = SW ? a.sweeps : 0;  // the sweep code exists only in the SW kernels
+  for (int sweep = 0; sweep <= nsweeps; ++sweep) {
+  if (SW && sweep > 0) {
+    if (!(E0 > 0.0)) break;
+    dead = false;
+  }
+  const int ncomp = (!SW || sweep == 0) ? a.k : used;
   int comp = 0;
-  for (; comp < a.k; ++comp) {
+  for (; comp < ncomp; ++comp) {
+    bool fallback = false, refit_plus = false;
+    float d_old = 0.0f;
+    if (SW && sweep > 0) {
+      // ---------------- refit: add-back pending, u from the previous fit
+      refit_begin<NT>(Rb, Rrow0, Rld, n4 / 4, a.RT, a.ldt, m4 / 4, r0, r1, c0, c1, have_pending && !r_applied,
+                      have_pending && !rt_applied, pd, du, dv, pu, a.Bp + (size_t)comp * wm,
+                      a.Cp + (size_t)comp * wn, wm, wn, g == 0 ? a.bytes : nullptr);
+      d_old = __uint_as_float(ld_dev(reinterpret_cast<const unsigned*>(a.D) + comp));
+      pd = -d_old;
+      have_pending = d_old != 0.0f;
+      r_applied = false;
+      rt_applied = false;
+      refit_plus = have_pending;
+      __syncthreads();
+    } else {
     if (dead) {
-      emit_zero(comp);
+      emit_zero(comp, true, 1.0);
       if (a.target > 0.0) break;
       continue;
     }
@@ -596,13 +705,13 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
       select_prepare<NT>(s, kx);
     }
     const SelResult su = ternary_select<NT, false, double, WV, true>(dl, nullptr, m, a.tau, 0, s);
-    bool fallback = false;
     if (su.count == 0u) {
       const int r = fallback_row();
       if (r == -2) return;
       if (r < 0) {
         dead = true;
-        emit_zero(comp);
+        E = 0.0;
+        emit_zero(comp, true, 1.0);
         if (a.target > 0.0) break;
         continue;
       }
@@ -611,6 +720,7 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
     } else {
       pack_sel(dl, m, su, pu, nullptr, false);
     }
+    }  // pass 0
     for (int w = tid; w < wm; w += NT) pu0[w] = pu[w];
     __syncthreads();
 
@@ -630,6 +740,13 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
       ++epoch;
       if (grid_barrier(a.bar, epoch, a.spin_limit, &bar_flag)) return;
       load_exchange(a.xw, n);
+      if (SW && refit_plus) {
+        // energy with the contribution restored, from w = (R + X)^T u_old:
+        //   |R + X|^2_H = E + 2 d v_old^T H w - d^2 |u_old|^2 |v_old|^2_H
+        refit_plus = false;
+        const double dd0 = (double)d_old;
+        E = E + addback_energy<NT>(dl, du, dv, WV ? hl : nullptr, n, wm, dd0, part);
+      }
       const SelResult sv = ternary_select<NT, WV, double, WV, true>(dl, hw, n, a.tau, a.EHm, s);
       if (sv.count == 0u) {
         // R^T u == 0: only possible for the initial u; restart from the largest-entry row
@@ -681,7 +798,13 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
       }
     }
     if (dead) {
-      emit_zero(comp);
+      if (SW && sweep > 0) {  // the residual with the contribution restored is zero
+        emit_zero(comp, false, 1.0 - E / E0);
+        dead = false;
+        continue;
+      }
+      E = 0.0;
+      emit_zero(comp, true, 1.0);
       if (a.target > 0.0) break;
       continue;
     }
@@ -714,8 +837,8 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
     const double dd = (double)d;
     E = E - (2.0 * dd * p - dd * dd * q);
     if (g == 0) {
-      for (int w = tid; w < wm; w += NT) a.Bp[(size_t)comp * wm + w] = pu[w];
-      for (int w = tid; w < wn; w += NT) a.Cp[(size_t)comp * wn + w] = pv[w];
+      for (int w = tid; w < wm; w += NT) st_dev(a.Bp + (size_t)comp * wm + w, pu[w]);
+      for (int w = tid; w < wn; w += NT) st_dev(a.Cp + (size_t)comp * wn + w, pv[w]);
       // |supp u0 U supp u_prev| (fused deflate + first V-step rows) and |supp u_prev| (writes)
       int un = 0, pn = 0;
       for (int w = tid; w < wm; w += NT) {
@@ -727,7 +850,7 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
       un = block_sum_int(un);
       pn = block_sum_int(pn);
       if (tid == 0) {
-        a.D[comp] = d;
+        st_dev(reinterpret_cast<unsigned*>(a.D) + comp, __float_as_uint(d));
         a.energy[comp] = 1.0 - E / E0;
         a.stats[0] += (u64)passes;
         if (early) a.stats[1] += 1ull;
@@ -751,12 +874,14 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
     r_applied = false;
     rt_applied = false;
     __syncthreads();
-    if (a.target > 0.0 && 1.0 - E / E0 >= a.target) break;
+    if ((!SW || sweep == 0) && a.target > 0.0 && 1.0 - E / E0 >= a.target) break;
   }
-  // components after an energy-target stop: zero, the energy held (1 after a zero component)
-  const int used = comp < a.k ? comp + 1 : a.k;
+  if (!SW || sweep == 0) used = comp < a.k ? comp + 1 : a.k;
+  }  // passes
+  // components after an energy-target stop: zero, the final energy held (1 after a zero
+  // component: E was set to 0 there)
   if (used < a.k && g == 0) {
-    const double held = dead ? 1.0 : 1.0 - E / E0;
+    const double held = E0 > 0.0 ? 1.0 - E / E0 : 1.0;
     for (long long x = tid; x < (long long)(a.k - used) * wm; x += NT) a.Bp[(size_t)used * wm + x] = 0u;
     for (long long x = tid; x < (long long)(a.k - used) * wn; x += NT) a.Cp[(size_t)used * wn + x] = 0u;
     for (int c = used + tid; c < a.k; c += NT) {
@@ -781,9 +906,9 @@ size_t seq_smem_bytes(int m, int n, bool weighted, int G, bool rl) {
   return seq_lds_layout(m, n, weighted, G, rl).total;
 }
 
-template <bool WV, bool RL>
+template <bool WV, bool RL, bool SW>
 static hipError_t launch_one(const SeqArgs& a, int G, size_t smem, hipStream_t st) {
-  auto kern = seq_kernel<512, WV, RL>;
+  auto kern = seq_kernel<512, WV, RL, SW>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (e != hipSuccess) return e;
   SeqArgs copy = a;
@@ -793,12 +918,16 @@ static hipError_t launch_one(const SeqArgs& a, int G, size_t smem, hipStream_t s
 
 template <bool WV, bool RL>
 static int coresident_one(size_t smem) {
-  int nb = 0;
-  auto kern = seq_kernel<512, WV, RL>;
+  int nb = 0, nb2 = 0;
+  auto kern = seq_kernel<512, WV, RL, false>;
+  auto kern2 = seq_kernel<512, WV, RL, true>;
   if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem) != hipSuccess)
     return 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, 512, smem) != hipSuccess) return 0;
-  return nb;
+  if (hipFuncSetAttribute((const void*)kern2, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem) != hipSuccess)
+    return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb2, kern2, 512, smem) != hipSuccess) return 0;
+  return nb < nb2 ? nb : nb2;
 }
 
 constexpr size_t kLdsBytes = 160 * 1024;
@@ -849,9 +978,16 @@ hipError_t seq_launch(const SeqLaunch& L, hipStream_t st) {
   a.spin_limit = L.spin_limit;
   a.target = L.target;
   a.safeguard = L.safeguard;
+  a.sweeps = L.sweeps;
   const size_t smem = seq_smem_bytes(L.m, L.n, L.h != nullptr, L.grid, L.rl);
-  if (L.h) return L.rl ? launch_one<true, true>(a, L.grid, smem, st) : launch_one<true, false>(a, L.grid, smem, st);
-  return L.rl ? launch_one<false, true>(a, L.grid, smem, st) : launch_one<false, false>(a, L.grid, smem, st);
+  if (L.sweeps > 0) {
+    if (L.h)
+      return L.rl ? launch_one<true, true, true>(a, L.grid, smem, st) : launch_one<true, false, true>(a, L.grid, smem, st);
+    return L.rl ? launch_one<false, true, true>(a, L.grid, smem, st) : launch_one<false, false, true>(a, L.grid, smem, st);
+  }
+  if (L.h)
+    return L.rl ? launch_one<true, true, false>(a, L.grid, smem, st) : launch_one<true, false, false>(a, L.grid, smem, st);
+  return L.rl ? launch_one<false, true, false>(a, L.grid, smem, st) : launch_one<false, false, false>(a, L.grid, smem, st);
 }
 
 // ---- standalone matvec with the same slab routine (kernel-level parity tests) ----------

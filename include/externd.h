@@ -69,10 +69,20 @@ typedef struct {
  *                  the residual (smallest row-major index on ties) exceeds the ALS component's
  *                  p^2 / q, the component becomes u = e_i, v = sign(R_ij) e_j, d = |R_ij|.
  *                  Sequential path only (block >= 2 after resolution is EXTERND_EINVAL).  Costs
- *                  one extra read of the residual and one grid-wide exchange per component. */
+ *                  one extra read of the residual and one grid-wide exchange per component.
+ *   sweeps         0..64 refinement sweeps after the greedy pass (review, Results: sweeps add
+ *                  energy and lower the rank a target needs; read as backfitting).  Each sweep
+ *                  walks the fitted components in order: the component's contribution is added
+ *                  back to the residual (one fp32 rounding per entry), it is refitted by ALS
+ *                  starting from its previous u, and the new fit is deflated.  The energy
+ *                  bookkeeping continues through the add-backs; energy[i] is then the value
+ *                  right after component i's refit in the last sweep, so energy[k-1] is the
+ *                  final energy.  Components past an energy-target stop are not refitted.
+ *                  Sequential path only for now (block >= 2 with sweeps is EXTERND_EINVAL). */
 typedef struct {
   double energy_target;
   int safeguard;
+  int sweeps;
 } externd_options;
 
 /* k = floor(mu * min(m, n) + 1e-9); -1 if m < 1, n < 1, mu not finite or > 0, or k < 1. */
