@@ -41,6 +41,7 @@ class Stats(ctypes.Structure):
         ("flops_algorithmic", ctypes.c_double),
         ("components_used", ctypes.c_int64),
         ("safeguard_activations", ctypes.c_int64),
+        ("sweep_reverts", ctypes.c_int64),
     ]
 
     def as_dict(self):

@@ -121,8 +121,6 @@ int externd_decompose_ex(const float* A, int64_t m, int64_t n, float mu, float t
   int64_t b = block == -1 ? std::max<int64_t>(1, std::min<int64_t>(256, std::min(m, n) / 8)) : (block <= 1 ? 1 : block);
   if (b > k) b = k;
   if (safeguard && b > 1) return fail(EXTERND_EINVAL, "the safeguard applies to the sequential path only (block resolved to %lld)", (long long)b);
-  if (sweeps > 0 && b > 1)
-    return fail(EXTERND_EINVAL, "refinement sweeps are implemented for the sequential path only (block resolved to %lld)", (long long)b);
   const int mi = (int)m, ni = (int)n, ki = (int)k, bi = (int)b;
   const int ldr = (ni + 3) & ~3, ldt = (mi + 3) & ~3;
 
@@ -258,6 +256,7 @@ int externd_decompose_ex(const float* A, int64_t m, int64_t n, float mu, float t
     L.stats = dstats;
     L.ws = base + o_blk;
     L.target = target;
+    L.sweeps = sweeps;
     HIP_OR_FAIL(hipEventRecord(e0, st));
     HIP_OR_FAIL(block_run(L, st, &flops, &blk_bytes));
     HIP_OR_FAIL(hipEventRecord(e1, st));
@@ -305,6 +304,7 @@ int externd_decompose_ex(const float* A, int64_t m, int64_t n, float mu, float t
     stats->flops_algorithmic = flops;
     stats->components_used = hst[5] > 0 ? (int64_t)hst[5] : k;
     stats->safeguard_activations = (int64_t)hst[4];
+    stats->sweep_reverts = (int64_t)hst[6];
     stats->seconds = std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count();
   }
   return EXTERND_OK;

@@ -43,13 +43,17 @@ struct BlockWs {
   double* Md;      // b: u_c^T Q_c (diagonal of U^T R H V)
   double* PHC;     // b x 3 selection results
   float* d;        // b
-  double* st;      // [0] E, [1] E0
+  double* st;      // [0] E, [1] E0, [2] E before a refit's add-back, [3] E with it restored
   int* flags;      // [0] dead, [1] empty sketch columns, [2] fallbacks, [3] energy target reached,
-                   // [4] components of the block kept (emitted)
+                   // [4] components of the block kept (emitted), [5] refit discarded (sweeps)
   int* used;       // m: rows used by sketch fallbacks within the block
   unsigned* rmax;  // [64 (s & 1) + w]: max |R| (fp32 bits) at the start of block s, spread over 64
                    // words w to keep the atomics of one update uncontended
   uint8_t* hdig;   // kHDig x ldv: 7-bit digits of the fixed-point column weights (weighted only)
+  double* GUo;     // b x b: Gram of the old U (refinement sweeps)
+  double* GVo;     // b x b: weighted Gram of the old V
+  double* ppo;     // b: u_c^T (R + X) H v_c of the old components
+  float* dold;     // b: old scales
 };
 
 constexpr int kMaxWords = 64;      // words per residual-max slot (one per lane of a wave)
@@ -79,6 +83,10 @@ static void ws_layout(int m, int n, int b, F&& take) {
   take((void**)nullptr, (size_t)m * 4);
   take((void**)nullptr, 2 * kMaxWords * 4);
   take((void**)nullptr, (size_t)kHDig * (size_t)((n + 15) & ~15));
+  take((void**)nullptr, bb * bb * 8);
+  take((void**)nullptr, bb * bb * 8);
+  take((void**)nullptr, bb * 8);
+  take((void**)nullptr, bb * 4);
 }
 
 static BlockWs carve(void* base, int m, int n, int b) {
@@ -112,6 +120,10 @@ static BlockWs carve(void* base, int m, int n, int b) {
   w.used = static_cast<int*>(ptrs[q++]);
   w.rmax = static_cast<unsigned*>(ptrs[q++]);
   w.hdig = static_cast<uint8_t*>(ptrs[q++]);
+  w.GUo = static_cast<double*>(ptrs[q++]);
+  w.GVo = static_cast<double*>(ptrs[q++]);
+  w.ppo = static_cast<double*>(ptrs[q++]);
+  w.dold = static_cast<float*>(ptrs[q++]);
   return w;
 }
 
@@ -1178,6 +1190,134 @@ __global__ void __launch_bounds__(256) stop_fill_kernel(uint32_t* Bp, uint32_t* 
   }
 }
 
+// ---- refinement sweeps: refit block [k0, k0 + bs) from its previous factors ----------------
+// Unpack the block's codes into Ut / Vt (zero padded), dvec = -D (its add-back through the update
+// kernel), reset the per-block flags and clear the residual-max slot the add-back writes.
+// (restore = true: the same unpacking, done only when the refit was discarded, flags[5].)
+__global__ void __launch_bounds__(256) refit_load_kernel(const uint32_t* Bp, const uint32_t* Cp, const float* D, int m,
+                                                         int n, int k0, int bs, int8_t* Ut, int ldu, int8_t* Vt,
+                                                         int ldv, float* dvec, float* dold, double* st, int* flags,
+                                                         unsigned* rmax_slot, bool restore) {
+  const int wm = (m + 15) / 16, wn = (n + 15) / 16;
+  if (restore) {
+    if (!flags[5]) return;
+  } else if (blockIdx.x == 0) {
+    if (threadIdx.x < kMaxWords) rmax_slot[threadIdx.x] = 0u;
+    if (threadIdx.x < bs) {
+      dvec[threadIdx.x] = -D[k0 + threadIdx.x];
+      dold[threadIdx.x] = D[k0 + threadIdx.x];
+    }
+    if (threadIdx.x == 0) {
+      flags[0] = 0;
+      flags[1] = 0;
+      flags[2] = 0;
+      flags[5] = 0;
+      st[2] = st[0];  // the energy before the add-back
+    }
+  }
+  const long long tu = (long long)bs * ldu, tv = (long long)bs * ldv;
+  for (long long x = blockIdx.x * 256ll + threadIdx.x; x < tu + tv; x += (long long)gridDim.x * 256) {
+    const bool isU = x < tu;
+    const long long y = isU ? x : x - tu;
+    const int ld = isU ? ldu : ldv, len = isU ? m : n, words = isU ? wm : wn;
+    const int c = (int)(y / ld), i = (int)(y - (long long)c * ld);
+    int8_t t = 0;
+    if (i < len) {
+      const unsigned code = ((isU ? Bp : Cp)[(size_t)(k0 + c) * words + (i >> 4)] >> (2 * (i & 15))) & 3u;
+      t = code == 1u ? (int8_t)1 : (code == 3u ? (int8_t)-1 : (int8_t)0);
+    }
+    (isU ? Ut : Vt)[y] = t;
+  }
+}
+
+// pp[c] = v_c^T H X[c] for the first V-step's X = U^T (R + X_blk) and the block's old V: one
+// workgroup per component, fixed reduction order.
+__global__ void __launch_bounds__(256) addback_dot_kernel(const double* X, int n, const int8_t* Vt, int ldv,
+                                                          const float* h, double* pp) {
+  __shared__ double red[4];
+  const int c = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  double acc = 0.0;
+  for (int j = tid; j < n; j += 256) {
+    const int v = Vt[(size_t)c * ldv + j];
+    if (v) acc += (double)v * (h ? (double)h[j] : 1.0) * X[(size_t)c * n + j];
+  }
+  acc = wave_sum_f64(acc);
+  if (lane == 0) red[wid] = acc;
+  __syncthreads();
+  if (tid == 0) pp[c] = (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+// E <- E + 2 sum_c d_c pp_c - sum_{c,c'} d_c d_c' (u_c . u_c') (v_c^T H v_c'): the energy of the
+// residual with the block's contribution X_blk restored, |R + X|^2 = |R|^2 + 2 <R + X, X> - |X|^2
+// (kept in st[3] too).  GU holds the Gram of the old U (copied to GUo), GV the weighted Gram of
+// the old V.  Also clears the residual-max slot the refit's own update will write.
+__global__ void __launch_bounds__(256) addback_energy_kernel(const double* pp, const double* GU, const double* GV,
+                                                             const float* D, int k0, int bs, double* st,
+                                                             unsigned* rmax_slot, double* GUo) {
+  __shared__ double red[2][4];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  if (tid < kMaxWords) rmax_slot[tid] = 0u;
+  for (int x = tid; x < bs * bs; x += 256) GUo[x] = GU[x];
+  double cr = 0.0, xx = 0.0;
+  if (tid < bs) {
+    const double dc = (double)D[k0 + tid];
+    cr = dc * pp[tid];
+    for (int c2 = 0; c2 < bs; ++c2)
+      xx += dc * (double)D[k0 + c2] * GU[(size_t)tid * bs + c2] * GV[(size_t)tid * bs + c2];
+  }
+  cr = wave_sum_f64(cr);
+  xx = wave_sum_f64(xx);
+  if (lane == 0) {
+    red[0][wid] = cr;
+    red[1][wid] = xx;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const double c = (red[0][0] + red[0][1]) + (red[0][2] + red[0][3]);
+    const double x = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
+    st[0] = st[0] + 2.0 * c - x;
+    st[3] = st[0];
+  }
+}
+
+// After the refit's scales: if the refit leaves the residual larger than before the add-back by
+// more than 1e-9 |A|^2_H, keep the old block instead (flags[5] = 1): its scales go back to D and
+// dvec, and its own sequential energy walk on the restored residual, from st[3], replaces the
+// refit's energies (thread t forms p_t = pp_t - sum_{c < t} d_c (u_t . u_c)(v_c^T H v_t)).
+__global__ void __launch_bounds__(256) refit_choose_kernel(const double* ppo, const double* GUo, const double* GVo,
+                                                           const float* dold, int k0, int bs, float* dvec, float* D,
+                                                           double* energy, double* st, int* flags, u64* stats) {
+#pragma clang fp contract(off)
+  __shared__ double ps[256], qs[256];
+  __shared__ int revert;
+  const int tid = threadIdx.x;
+  if (tid == 0) revert = st[0] > st[2] + 1e-9 * st[1] ? 1 : 0;
+  __syncthreads();
+  if (!revert) return;
+  if (tid < bs) {
+    double p = ppo[tid];
+    for (int c2 = 0; c2 < tid; ++c2)
+      p -= (double)dold[c2] * GUo[(size_t)tid * bs + c2] * GVo[(size_t)c2 * bs + tid];
+    ps[tid] = p;
+    qs[tid] = GUo[(size_t)tid * bs + tid] * GVo[(size_t)tid * bs + tid];
+    dvec[tid] = dold[tid];
+    D[k0 + tid] = dold[tid];
+  }
+  __syncthreads();
+  if (tid == 0) {
+    double E = st[3];
+    const double E0 = st[1];
+    for (int c = 0; c < bs; ++c) {
+      const double dd = (double)dold[c];
+      E = E - (2.0 * dd * ps[c] - dd * dd * qs[c]);
+      energy[k0 + c] = 1.0 - E / E0;
+    }
+    st[0] = E;
+    flags[5] = 1;
+    stats[6] += 1ull;
+  }
+}
+
 // E0 from the per-row energies (fixed order), dead flag for A = 0
 __global__ void block_init_kernel(const double* rowE, int m, double* st, int* flags, unsigned* rmax) {
   __shared__ double red[4];
@@ -1405,6 +1545,53 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops, double
   const int nblocks = (L.k + L.b - 1) / L.b;
   double fl = 0.0, by = 0.0;  // multiply-adds of R by ternary operands; residual bytes read/written
   const double rbytes = 4.0 * m * n;
+  int used = L.k;  // components fitted before an energy-target stop
+  // ALS iterations of one block from its current Ut, then the scales, the update and the outputs.
+  // sblk: residual updates so far (which max slot holds max |R|); addback: the first V-step also
+  // yields the energy of the residual with the block's old contribution restored.
+  auto als_fit = [&](int sblk, int bs, int k0, double target, bool addback) -> hipError_t {
+    hipError_t r;
+    for (int t = 0; t < L.T; ++t) {
+      // V-step: G = (U^T U + eps I)^-1 U^T R, rows ternarized with weights h
+      if ((r = gram_inverse(w.Ut, m, w.ldu, nullptr, bs, w.GU)) != hipSuccess) return r;
+      utr_product(L, w, bs, sblk, st);
+      if ((r = join()) != hipSuccess) return r;
+      if (addback && t == 0) {
+        hipLaunchKernelGGL(addback_dot_kernel, dim3(bs), dim3(256), 0, st, w.X, n, w.Vt, w.ldv, L.h, w.ppo);
+        hipLaunchKernelGGL(addback_energy_kernel, dim3(1), dim3(256), 0, st, w.ppo, w.GU, w.GVo, L.D, k0, bs, w.st,
+                           w.rmax + kMaxWords * ((sblk + 1) & 1), w.GUo);
+      }
+      solve(w, bs, w.X, w.Z, n, st);
+      select_rows(w.Z, n, w.ldv, bs, L.tau, L.h, L.EHm, w.Vt, w.PHC, w.flags, 0, st);
+      // U-step: F^T = (V^T H V + eps I)^-1 (R H V)^T, columns ternarized without weights
+      if ((r = gram_inverse(w.Vt, n, w.ldv, L.h, bs, w.GV)) != hipSuccess) return r;
+      rw_product(L, w, L.h, bs, sblk, w.Yt, st);
+      if ((r = join()) != hipSuccess) return r;
+      solve(w, bs, w.Yt, w.Ft, m, st);
+      select_rows(w.Ft, m, w.ldu, bs, L.tau, nullptr, 0, w.Ut, w.PHC, w.flags, 0, st);
+      fl += 4.0 * m * n * bs;
+      by += 2.0 * rbytes;
+    }
+    // scales against Q = R H V of the last U-step, then the update and the outputs
+    gram_product(w, w.Ut, m, w.ldu, nullptr, 0, bs, w.GU, st);
+    hipLaunchKernelGGL(rowdot_kernel, dim3(bs), dim3(256), 0, st, w.Ut, w.ldu, w.Yt, m, w.Md);
+    hipLaunchKernelGGL(scales_kernel, dim3(1), dim3(256), 0, st, w.Md, w.GU, w.GV, bs, k0, L.T, w.d, L.D, L.energy,
+                       w.st, w.flags, L.stats, target);
+    if (addback) {  // keep the better of the refit and the old block
+      hipLaunchKernelGGL(refit_choose_kernel, dim3(1), dim3(256), 0, st, w.ppo, w.GUo, w.GVo, w.dold, k0, bs, w.d,
+                         L.D, L.energy, w.st, w.flags, L.stats);
+      const long long nb = ((long long)bs * (w.ldu + w.ldv) + 255) / 256;
+      hipLaunchKernelGGL(refit_load_kernel, dim3((unsigned)(nb < 1024 ? nb : 1024)), dim3(256), 0, st, L.Bp, L.Cp,
+                         L.D, m, n, k0, bs, w.Ut, w.ldu, w.Vt, w.ldv, w.d, w.dold, w.st, w.flags, w.rmax, true);
+    }
+    hipLaunchKernelGGL(update_kernel, dim3((n + 63) / 64, (m + 63) / 64), dim3(256), 0, st, L.R, L.ldr, m, n, w.Ut,
+                       w.ldu, w.Vt, w.ldv, w.d, bs, w.flags, w.rmax + kMaxWords * ((sblk + 1) & 1));
+    hipLaunchKernelGGL(emit_kernel, dim3(256), dim3(256), 0, st, w.Ut, w.ldu, w.Vt, w.ldv, m, n, bs, k0, L.Bp, L.Cp,
+                       w.flags);
+    fl += 2.0 * m * n * bs;
+    by += 2.0 * rbytes;
+    return hipGetLastError();
+  };
   for (int s = 0; s < nblocks; ++s) {
     const int bs = (L.k - s * L.b) < L.b ? (L.k - s * L.b) : L.b;
     const int k0 = s * L.b;
@@ -1418,46 +1605,60 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops, double
                        w.flags, w.used);
     fl += 2.0 * m * n * bs;
     by += rbytes;
-    for (int t = 0; t < L.T; ++t) {
-      // V-step: G = (U^T U + eps I)^-1 U^T R, rows ternarized with weights h
-      if ((e = gram_inverse(w.Ut, m, w.ldu, nullptr, bs, w.GU)) != hipSuccess) return e;
-      utr_product(L, w, bs, s, st);
-      if ((e = join()) != hipSuccess) return e;
-      solve(w, bs, w.X, w.Z, n, st);
-      select_rows(w.Z, n, w.ldv, bs, L.tau, L.h, L.EHm, w.Vt, w.PHC, w.flags, 0, st);
-      // U-step: F^T = (V^T H V + eps I)^-1 (R H V)^T, columns ternarized without weights
-      if ((e = gram_inverse(w.Vt, n, w.ldv, L.h, bs, w.GV)) != hipSuccess) return e;
-      rw_product(L, w, L.h, bs, s, w.Yt, st);
-      if ((e = join()) != hipSuccess) return e;
-      solve(w, bs, w.Yt, w.Ft, m, st);
-      select_rows(w.Ft, m, w.ldu, bs, L.tau, nullptr, 0, w.Ut, w.PHC, w.flags, 0, st);
-      fl += 4.0 * m * n * bs;
-      by += 2.0 * rbytes;
-    }
-    // scales against Q = R H V of the last U-step, then the update and the outputs
-    gram_product(w, w.Ut, m, w.ldu, nullptr, 0, bs, w.GU, st);
-    hipLaunchKernelGGL(rowdot_kernel, dim3(bs), dim3(256), 0, st, w.Ut, w.ldu, w.Yt, m, w.Md);
-    hipLaunchKernelGGL(scales_kernel, dim3(1), dim3(256), 0, st, w.Md, w.GU, w.GV, bs, k0, L.T, w.d, L.D, L.energy,
-                       w.st, w.flags, L.stats, L.target);
-    hipLaunchKernelGGL(update_kernel, dim3((n + 63) / 64, (m + 63) / 64), dim3(256), 0, st, L.R, L.ldr, m, n, w.Ut,
-                       w.ldu, w.Vt, w.ldv, w.d, bs, w.flags, w.rmax + kMaxWords * ((s + 1) & 1));
-    hipLaunchKernelGGL(emit_kernel, dim3(256), dim3(256), 0, st, w.Ut, w.ldu, w.Vt, w.ldv, m, n, bs, k0, L.Bp, L.Cp,
-                       w.flags);
-    fl += 2.0 * m * n * bs;
-    by += 2.0 * rbytes;
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = als_fit(s, bs, k0, L.target, false)) != hipSuccess) return e;
     if (L.target > 0.0 && k0 + bs < L.k) {
       // the host learns of a stop before queueing the next block (one 4-byte read per block)
       int reached = 0;
       if ((e = hipMemcpyAsync(&reached, w.flags + 3, sizeof(int), hipMemcpyDeviceToHost, st)) != hipSuccess) return e;
       if ((e = hipStreamSynchronize(st)) != hipSuccess) return e;
       if (reached) {
+        u64 u = 0;
+        if ((e = hipMemcpyAsync(&u, L.stats + 5, sizeof(u64), hipMemcpyDeviceToHost, st)) != hipSuccess) return e;
+        if ((e = hipStreamSynchronize(st)) != hipSuccess) return e;
+        used = (int)u;
         hipLaunchKernelGGL(stop_fill_kernel, dim3(256), dim3(256), 0, st, L.Bp, L.Cp, L.D, L.energy, m, n, k0 + bs,
                            L.k);
         break;
       }
     }
   }
+  // refinement sweeps: refit each block of the first `used` components from its previous
+  // factors (backfitting).  step numbers the residual updates: update number t writes the max
+  // slot (t + 1) & 1 that the contractions after it read; every refit starts with an add-back
+  // update, so the slot history before the sweeps does not matter.
+  int step = nblocks;
+  bool zero_start = false;  // A == 0: nothing to refit
+  if (L.sweeps > 0) {
+    double e0h[2] = {0.0, 0.0};
+    u64 u = 0;  // a stop inside the last block is not seen by the per-block check
+    if ((e = hipMemcpyAsync(e0h, w.st, 2 * sizeof(double), hipMemcpyDeviceToHost, st)) != hipSuccess) return e;
+    if ((e = hipMemcpyAsync(&u, L.stats + 5, sizeof(u64), hipMemcpyDeviceToHost, st)) != hipSuccess) return e;
+    if ((e = hipStreamSynchronize(st)) != hipSuccess) return e;
+    zero_start = !(e0h[1] > 0.0);
+    if (L.target > 0.0 && u > 0) used = (int)u;
+  }
+  for (int sw = 0; sw < L.sweeps && !zero_start; ++sw) {
+    for (int k0 = 0; k0 < used; k0 += L.b) {
+      int bs = L.k - k0 < L.b ? L.k - k0 : L.b;
+      if (used - k0 < bs) bs = used - k0;
+      const long long tot = (long long)bs * (w.ldu + w.ldv);
+      const long long nb = (tot + 255) / 256;
+      hipLaunchKernelGGL(refit_load_kernel, dim3((unsigned)(nb < 1024 ? nb : 1024)), dim3(256), 0, st, L.Bp, L.Cp,
+                         L.D, m, n, k0, bs, w.Ut, w.ldu, w.Vt, w.ldv, w.d, w.dold, w.st, w.flags,
+                         w.rmax + kMaxWords * ((step + 1) & 1), false);
+      // add the block back: R <- fl32(R + U diag(d) V^T), the new residual max into the next slot
+      hipLaunchKernelGGL(update_kernel, dim3((n + 63) / 64, (m + 63) / 64), dim3(256), 0, st, L.R, L.ldr, m, n,
+                         w.Ut, w.ldu, w.Vt, w.ldv, w.d, bs, w.flags, w.rmax + kMaxWords * ((step + 1) & 1));
+      ++step;
+      // the old V's weighted Gram for the add-back energy (the U-step overwrites GV)
+      gram_product(w, w.Vt, n, w.ldv, L.h, L.EHm, bs, w.GVo, st);
+      by += 2.0 * rbytes;
+      if ((e = als_fit(step, bs, k0, 0.0, true)) != hipSuccess) return e;
+      ++step;
+    }
+  }
+  if (L.sweeps > 0 && !zero_start && used < L.k)  // the held energy after the stop is the final one
+    hipLaunchKernelGGL(stop_fill_kernel, dim3(256), dim3(256), 0, st, L.Bp, L.Cp, L.D, L.energy, m, n, used, L.k);
   *flops = fl;
   *bytes = by;
   return hipGetLastError();

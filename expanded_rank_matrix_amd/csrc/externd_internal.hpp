@@ -71,6 +71,7 @@ struct BlockLaunch {
   u64* stats;
   void* ws;            // workspace (block_workspace_bytes)
   double target = 0.0; // > 0: stop once the energy reaches it
+  int sweeps = 0;      // refinement sweeps after the greedy pass
 };
 size_t block_workspace_bytes(int m, int n, int b);
 // flops: multiply-adds of the residual by ternary operands x 2; bytes: residual bytes that the

@@ -47,6 +47,7 @@ struct SeqArgs {
   double* energy;
   u64* stats;          // [0] passes [1] early exits [2] fallbacks [3] zero components
                        // [4] safeguard activations [5] components fitted before a target stop
+                       // [6] refits discarded for the old component
   double* bytes;       // algorithmic bytes
   int m, n, ldr, ldt, k, T, wm, wn, EHm;
   float tau;
@@ -670,6 +671,7 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
   for (; comp < ncomp; ++comp) {
     bool fallback = false, refit_plus = false;
     float d_old = 0.0f;
+    double E_before = 0.0;  // refit: the energy before the add-back
     if (SW && sweep > 0) {
       // ---------------- refit: add-back pending, u from the previous fit
       refit_begin<NT>(Rb, Rrow0, Rld, n4 / 4, a.RT, a.ldt, m4 / 4, r0, r1, c0, c1, have_pending && !r_applied,
@@ -681,6 +683,7 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
       r_applied = false;
       rt_applied = false;
       refit_plus = have_pending;
+      E_before = E;
       __syncthreads();
     } else {
     if (dead) {
@@ -833,9 +836,21 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
         __syncthreads();
       }
     }
-    const float d = sg_on ? d_sg : (float)(p / q);
-    const double dd = (double)d;
+    float d = sg_on ? d_sg : (float)(p / q);
+    double dd = (double)d;
     E = E - (2.0 * dd * p - dd * dd * q);
+    bool reverted = false;
+    if (SW && sweep > 0 && E > E_before + 1e-9 * E0) {
+      // the refit leaves more than the old component did: deflate the old one again (its
+      // codes are the pending add-back's, already applied to both copies)
+      reverted = true;
+      for (int w = tid; w < wm; w += NT) pu[w] = du[w];
+      for (int w = tid; w < wn; w += NT) pv[w] = dv[w];
+      d = d_old;
+      dd = (double)d;
+      E = E_before;
+      __syncthreads();
+    }
     if (g == 0) {
       for (int w = tid; w < wm; w += NT) st_dev(a.Bp + (size_t)comp * wm + w, pu[w]);
       for (int w = tid; w < wn; w += NT) st_dev(a.Cp + (size_t)comp * wn + w, pv[w]);
@@ -856,6 +871,7 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
         if (early) a.stats[1] += 1ull;
         if (fallback) a.stats[2] += 1ull;
         if (sg_on) a.stats[4] += 1ull;
+        if (reverted) a.stats[6] += 1ull;
         a.bytes[0] += 4.0 * (double)n * (double)un + 4.0 * (double)n * (double)pn +
                       (double)usteps * 4.0 * (double)m * (double)n + vbytes +
                       (a.safeguard ? 4.0 * (double)m * (double)n : 0.0);

@@ -53,6 +53,7 @@ typedef struct {
   double flops_algorithmic;     /* contraction flops of the block path */
   int64_t components_used;      /* components fitted before an energy-target stop (k without one) */
   int64_t safeguard_activations;/* components replaced by the best single entry (Prop. 2) */
+  int64_t sweep_reverts;        /* refits discarded for the old component (block), see sweeps */
 } externd_stats;
 
 /* (host) optional behaviour of externd_decompose_ex; all-zero = externd_decompose.
@@ -74,11 +75,17 @@ typedef struct {
  *                  energy and lower the rank a target needs; read as backfitting).  Each sweep
  *                  walks the fitted components in order: the component's contribution is added
  *                  back to the residual (one fp32 rounding per entry), it is refitted by ALS
- *                  starting from its previous u, and the new fit is deflated.  The energy
+ *                  starting from its previous u, and the new fit is deflated unless it leaves
+ *                  the residual larger than before the add-back by more than 1e-9 |A|^2_H, in
+ *                  which case the old component is deflated again (keeping whichever removes
+ *                  more, as Prop. 2 does; block-ALS from a warm start is not monotone).  The energy
  *                  bookkeeping continues through the add-backs; energy[i] is then the value
  *                  right after component i's refit in the last sweep, so energy[k-1] is the
- *                  final energy.  Components past an energy-target stop are not refitted.
- *                  Sequential path only for now (block >= 2 with sweeps is EXTERND_EINVAL). */
+ *                  final energy.  Components past an energy-target stop are not refitted.  On
+ *                  the block path each block is added back (fp64 sum over its components, one
+ *                  rounding) and refitted by block-ALS from its previous U.  With a target on the
+ *                  block path the stop can fall inside a block; that block is then refitted as
+ *                  a smaller block of its kept components. */
 typedef struct {
   double energy_target;
   int safeguard;

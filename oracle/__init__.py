@@ -48,6 +48,7 @@ class _Opts(ctypes.Structure):
         ("energy_target", ctypes.c_double),
         ("used", ctypes.POINTER(ctypes.c_int64)),
         ("sweeps", ctypes.c_int),
+        ("reverts", ctypes.POINTER(ctypes.c_int64)),
     ]
 
 
@@ -125,7 +126,7 @@ def project(x, tau: float = 0.0, h=None):
 
 
 def _make_opts(threads, safeguard, k_limit, gaps, counters, eexp, residual_fp64,
-               block_engine=False, energy_target=0.0, used=None, sweeps=0):
+               block_engine=False, energy_target=0.0, used=None, sweeps=0, reverts=None):
     o = _Opts()
     o.threads = int(threads)
     o.safeguard = int(bool(safeguard))
@@ -139,6 +140,7 @@ def _make_opts(threads, safeguard, k_limit, gaps, counters, eexp, residual_fp64,
     o.energy_target = float(energy_target)
     o.used = used.ctypes.data_as(ip) if used is not None else ip()
     o.sweeps = int(sweeps)
+    o.reverts = reverts.ctypes.data_as(ip) if reverts is not None else ip()
     return o
 
 
@@ -164,8 +166,9 @@ def decompose(A, mu: float, tau: float = 0.0, h=None, als_iters: int = 4, block:
     counters = np.zeros(4, dtype=np.int64)
     eexp = np.zeros(1, dtype=np.float64)
     used = np.zeros(1, dtype=np.int64)
+    reverts = np.zeros(1, dtype=np.int64)
     o = _make_opts(threads, safeguard, k_limit, gaps, counters, eexp, residual_fp64,
-                   block_engine, energy_target, used, sweeps)
+                   block_engine, energy_target, used, sweeps, reverts)
     rc = _load().externd_oracle_decompose(_ptr(A), m, n, mu, tau, _ptr(h), als_iters, block,
                                           _ptr(B), _ptr(C), _ptr(D), _ptr(energy),
                                           ctypes.addressof(o))
@@ -176,7 +179,8 @@ def decompose(A, mu: float, tau: float = 0.0, h=None, als_iters: int = 4, block:
         b = resolve_block(block, m, n, k)
         kk = min(k, -(-kk // b) * b)
     return dict(B=B[:kk], C=C[:kk], D=D[:kk], energy=energy[:kk], gaps=gaps[:kk],
-                counters=counters, energy_explicit=float(eexp[0]), k=k, used=int(used[0]))
+                counters=counters, energy_explicit=float(eexp[0]), k=k, used=int(used[0]),
+                reverts=int(reverts[0]))
 
 
 def resolve_block(block: int, m: int, n: int, k: int) -> int:

@@ -712,9 +712,15 @@ void emit(uint32_t* B, uint32_t* C, float* D, int64_t i, int64_t m, int64_t n, c
 // with <R + X, X>_H = sum_c d_c u_c^T (R + X) H v_c taken on the residual after the add-back;
 // energy[i] is the value after component i's refit in the last sweep.  Components past an
 // energy-target stop are not refitted.
+// A refit is kept unless it leaves the residual larger than before the add-back by more than
+// kKeepTol |A|^2_H; otherwise the old component (block) is deflated again (as Prop. 2 keeps
+// whichever step lowers the residual more).  Block-ALS from a warm start is not monotone, and
+// the margin keeps the choice away from rounding-level differences between implementations.
+constexpr double kKeepTol = 1e-9;
+
 template <typename RT>
 void refine(State<RT>& st, uint32_t* B, uint32_t* C, float* D, double* energy, double* gaps, int64_t used,
-            int64_t b, int64_t k, int sweeps, bool sg) {
+            int64_t b, int64_t k, int sweeps, bool sg, int64_t* reverts) {
   const int64_t m = st.m, n = st.n, wm = words_of(m), wn = words_of(n);
   for (int sw = 0; sw < sweeps; ++sw) {
     for (int64_t s0 = 0; s0 < used; s0 += b) {
@@ -728,11 +734,11 @@ void refine(State<RT>& st, uint32_t* B, uint32_t* C, float* D, double* energy, d
         nd[c] = -d[c];
       }
       // add back, then the energy of the residual with the contribution restored
-      double cross = 0.0, xx = 0.0;
+      const double E_before = st.E;
+      double cross = 0.0, xx = 0.0, pp = 0.0, qq = 0.0;
       if (b == 1) {
         if (d[0] != 0.0f) {
           deflate(st, U.data(), V.data(), nd[0]);
-          double pp, qq;
           exact_pq(st, U.data(), V.data(), &pp, &qq);
           cross = (double)d[0] * pp;
           xx = (double)d[0] * (double)d[0] * qq;
@@ -761,18 +767,39 @@ void refine(State<RT>& st, uint32_t* B, uint32_t* C, float* D, double* energy, d
         }
         if (c.fallback) st.fallbacks++;
         if (sg && apply_safeguard(st, c)) st.safeguards++;
-        deflate(st, c.u.data(), c.v.data(), c.d);
         const double dd = (double)c.d;
-        st.E = st.E - (2.0 * dd * c.p - dd * dd * c.q);
+        const double E_new = st.E - (2.0 * dd * c.p - dd * dd * c.q);
+        if (E_new > E_before + kKeepTol * st.E0) {  // the old component removes more: keep it
+          deflate(st, U.data(), V.data(), d[0]);
+          st.E = E_before;
+          if (reverts) reverts[0]++;
+          emit(B, C, D, s0, m, n, U.data(), V.data(), d[0]);
+        } else {
+          deflate(st, c.u.data(), c.v.data(), c.d);
+          st.E = E_new;
+          emit(B, C, D, s0, m, n, c.u.data(), c.v.data(), c.d);
+        }
         energy[s0] = 1.0 - st.E / st.E0;
-        emit(B, C, D, s0, m, n, c.u.data(), c.v.data(), c.d);
         if (gaps) gaps[s0] = c.gap;
       } else {
         Block bl = fit_block(st, s0 / b, bs, U.data());
-        block_energy(st, bl.U, bl.V, bl.d, bs, energy + s0);
-        block_update(st, bl.U, bl.V, bl.d, bs);
+        const double E_plus = st.E;
+        std::vector<double> en(bs);
+        block_energy(st, bl.U, bl.V, bl.d, bs, en.data());
+        const bool keep_old = st.E > E_before + kKeepTol * st.E0;
+        const std::vector<int8_t>& Uk = keep_old ? U : bl.U;
+        const std::vector<int8_t>& Vk = keep_old ? V : bl.V;
+        const std::vector<float>& dk = keep_old ? d : bl.d;
+        if (keep_old) {  // the old block on the restored residual: its own energy walk
+          st.E = E_plus;
+          block_energy(st, U, V, d, bs, energy + s0);
+          if (reverts) reverts[0]++;
+        } else {
+          std::copy(en.begin(), en.end(), energy + s0);
+        }
+        block_update(st, Uk, Vk, dk, bs);
         for (int64_t c = 0; c < bs; ++c) {
-          emit(B, C, D, s0 + c, m, n, bl.U.data() + c * m, bl.V.data() + c * n, bl.d[c]);
+          emit(B, C, D, s0 + c, m, n, Uk.data() + c * m, Vk.data() + c * n, dk[c]);
           if (gaps) gaps[s0 + c] = bl.gap[c];
         }
       }
@@ -878,8 +905,10 @@ int decompose_t(const float* A, int64_t m, int64_t n, float mu, float tau, const
     }
   }
   const int sweeps = opts && opts->sweeps > 0 ? opts->sweeps : 0;
+  if (opts && opts->reverts) opts->reverts[0] = 0;
   if (sweeps > 0 && st.E0 > 0.0) {
-    refine(st, B, C, D, energy, gaps, used, b == 1 && !(opts && opts->block_engine) ? 1 : b, k, sweeps, sg);
+    refine(st, B, C, D, energy, gaps, used, b == 1 && !(opts && opts->block_engine) ? 1 : b, k, sweeps, sg,
+           opts ? opts->reverts : nullptr);
     for (int64_t i = used; i < klim; ++i) energy[i] = energy[used - 1];
   }
   if (opts && opts->used) opts->used[0] = used;

@@ -38,6 +38,7 @@ typedef struct {
                                later components are zero with the energy held; <= 0: off */
   int64_t* used;            /* nullable, 1: components fitted before the stop (all when none) */
   int sweeps;               /* >= 1: refinement sweeps (backfitting) after the greedy pass */
+  int64_t* reverts;         /* nullable, 1: refits discarded for the old component (block) */
 } externd_oracle_opts;
 
 int64_t externd_oracle_rank(int64_t m, int64_t n, float mu);

@@ -52,6 +52,7 @@ def test_sweeps_free_run(name, m, n, mu, tau, weighted):
             assert g["stats"]["fallback_inits"] == o["counters"][0]
             # executed passes: the GPU leaves an ALS early at an exact fixed point
             assert g["stats"]["passes"] <= o["counters"][2]
+            assert g["stats"]["sweep_reverts"] == o["reverts"]
         # the bookkeeping ends at the energy of the final residual
         assert abs(g["energy"][-1] - g["stats"]["energy_final_explicit"]) < 1e-6
         assert abs(g["stats"]["energy_final_explicit"] - o["energy_explicit"]) <= P.E_ATOL
@@ -92,12 +93,41 @@ def test_sweeps_special_cases():
     P.check_free_run(g, o, "safeguard + sweep")
 
 
-def test_sweeps_rejected_on_the_block_path():
-    import torch
+@pytest.mark.parametrize("block,m,n,mu,tau,weighted", [
+    (8, 64, 48, 1.0, 0.0, False),
+    (16, 130, 97, 1.0, 0.0, True),     # weighted Gram and fixed-point weights
+    (64, 300, 260, 0.5, 0.2, False),   # several tiles, split-K, ragged last block
+    (5, 40, 37, 2.0, 0.0, False),      # block not a multiple of the MFMA tile
+    (8, 64, 48, 2.0, 0.0, False),      # heavy tails: refits get discarded
+])
+def test_block_sweeps_free_run(block, m, n, mu, tau, weighted):
+    A, h = inputs.make_input("down2560x9728" if weighted else "attn2560", m=m, n=n)
+    if not weighted:
+        h = None
+    g0 = P.gpu_decompose(A, mu, tau, h, 3, block)
+    o0 = oracle.decompose(A, mu, tau, h, 3, block)
+    assert P.first_divergence(g0, o0) == g0["k"], "greedy pass diverged: pick another case"
+    g = P.gpu_decompose(A, mu, tau, h, 3, block, sweeps=1)
+    o = oracle.decompose(A, mu, tau, h, 3, block, sweeps=1)
+    f = P.check_free_run(g, o, f"b={block} sweeps=1", block)
+    assert abs(g["energy"][-1] - g["stats"]["energy_final_explicit"]) < 1e-6
+    assert abs(g["stats"]["energy_final_explicit"] - o["energy_explicit"]) <= P.E_ATOL
+    assert g["energy"][-1] > g0["energy"][-1] - 1e-6
+    if f == g["k"]:
+        assert g["stats"]["passes"] == o["counters"][2]
+        assert g["stats"]["sweep_reverts"] == o["reverts"]
 
-    import expanded_rank_matrix_amd as erm
 
-    A = torch.ones((16, 16), dtype=torch.float32, device="cuda")
-    with pytest.raises(erm.ExterndError) as e:
-        erm.decompose(A, 1.0, block=4, sweeps=1)
-    assert e.value.status == erm.EINVAL
+def test_block_sweeps_after_a_target_stop():
+    A, _ = inputs.make_input("tiny64x48")
+    full = oracle.decompose(A, 2.0, 0.0, None, 3, 8)
+    for i in (29, 95):  # inside a block, and inside the last block
+        t = 0.5 * float(full["energy"][i - 1] + full["energy"][i]) if i < 95 else \
+            0.5 * float(full["energy"][i - 2] + full["energy"][i - 1])
+        g = P.gpu_decompose(A, 2.0, 0.0, None, 3, 8, energy_target=t, sweeps=2)
+        o = oracle.decompose(A, 2.0, 0.0, None, 3, 8, energy_target=t, sweeps=2)
+        used = g["stats"]["components_used"]
+        assert used == o["used"]
+        assert np.all(g["D"][used:] == 0) and np.all(g["B"][used:] == 0)
+        assert np.all(g["energy"][used:] == g["energy"][used - 1])
+        assert abs(g["energy"][used - 1] - o["energy"][used - 1]) <= P.E_ATOL
