@@ -149,6 +149,11 @@ def main():
     ap.add_argument("--infer", action="store_true",
                     help="time inference from the workload's packed factors instead of the decomposition")
     ap.add_argument("--batch", type=int, default=1, help="vectors per inference call (--infer)")
+    ap.add_argument("--sweeps", type=int, default=0, help="refinement sweeps after the greedy pass")
+    ap.add_argument("--energy-target", type=float, default=0.0,
+                    help="stop at the first component whose energy reaches this value")
+    ap.add_argument("--safeguard", action="store_true", help="Prop. 2 single-entry safeguard")
+    ap.add_argument("--block", type=int, default=None, help="override the workload's block size")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build runs the "
@@ -162,7 +167,11 @@ def main():
 
     if args.copy_mb > 0:
         copy_probe(args.copy_mb)
-    c = inputs.CONFIGS[args.workload]
+    c = dict(inputs.CONFIGS[args.workload])
+    if args.block is not None:
+        c["block"] = args.block
+    options = dict(energy_target=args.energy_target, safeguard=args.safeguard, sweeps=args.sweeps)
+    variant = any(options.values()) or args.block is not None  # not the workload as defined
     A_np, h_np = inputs.make_input(args.workload)
     m, n = A_np.shape
     A = torch.from_numpy(A_np).cuda()
@@ -177,21 +186,25 @@ def main():
         infer_bench(args, erm, torch, A, h, c, k, m, n, out, stream)
         return
     for _ in range(args.warmup):
-        erm.decompose(A, c["mu"], c["tau"], h, c["als_iters"], c["block"], stream=stream, out=out)
+        erm.decompose(A, c["mu"], c["tau"], h, c["als_iters"], c["block"], stream=stream, out=out, **options)
     torch.cuda.synchronize()
     kernel_ms, stats = [], None
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        r = erm.decompose(A, c["mu"], c["tau"], h, c["als_iters"], c["block"], stream=stream, out=out)
+        r = erm.decompose(A, c["mu"], c["tau"], h, c["als_iters"], c["block"], stream=stream, out=out,
+                          **options)
         stats = r["stats"]
         kernel_ms.append(stats["kernel_ms"])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
-    value = k * args.steps / wall
+    # components fitted: with an energy target only the kept ones, each sweep refits them again
+    fits = stats["components_used"] * (1 + args.sweeps)
+    value = fits * args.steps / wall
     kms = float(np.mean(kernel_ms))
     energy = out["energy"].cpu().numpy()
-    traffic = measured_traffic(args.workload)
+    # the traffic record was taken on the workload as defined; a variant has none
+    traffic = None if variant else measured_traffic(args.workload)
     if c["block"] in (0, 1):
         achieved = stats["bytes_algorithmic"] / (kms * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -229,7 +242,13 @@ def main():
                    "passes": stats["passes"], "early_exits": stats["early_exits"]},
         "roofline": roof,
     }
-    if not args.no_cpu:
+    if variant:
+        res["config"]["options"] = dict(options, block=c["block"])
+        res["config"]["components_used"] = stats["components_used"]
+        res["config"]["fits_per_decomposition"] = fits
+        res["config"]["safeguard_activations"] = stats["safeguard_activations"]
+        res["config"]["sweep_reverts"] = stats["sweep_reverts"]
+    if not args.no_cpu and not variant:
         res["cpu_baseline"] = cpu_baseline(A_np, c)
     print(json.dumps(res), flush=True)
 

@@ -261,29 +261,39 @@ __device__ __forceinline__ void slab_deflate(float* base, int row_base, int ld, 
 
 // Per-workgroup part of the safeguard's search: the largest h_j R_ij^2 over rows [r0, r1)
 // (smallest row-major index on ties); wave w leaves (value, index, R_ij) in part[3w..3w+2].
-// Kept out of line: it runs only with the safeguard on and would otherwise add to the register
-// pressure of the whole persistent kernel.
+// Rows are read as float4 (ld is a multiple of 4); a lane visits its entries in increasing index
+// order, so a strict comparison keeps the smallest index among its equal maxima.
 template <int NW>
-__device__ __noinline__ void best_entry_rows(const float* Rb, int Rrow0, int Rld, int r0, int r1, int n,
-                                             const float* hl, double* part) {
+__device__ __forceinline__ void best_entry_rows(const float* Rb, int Rrow0, int Rld, int r0, int r1, int n,
+                                                const float* hl, double* part) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  double best = 0.0, bidx = -1.0, bval = 0.0;
+  const int q4 = (n + 3) >> 2;
+  double best = 0.0;
+  int bidx = -1;
+  float bval = 0.0f;
   for (int i = r0 + wid; i < r1; i += NW) {
-    const float* row = Rb + (size_t)(i - Rrow0) * Rld;
-    for (int j = lane; j < n; j += 64) {
-      const double r = (double)row[j];
-      const double sv = (hl ? (double)hl[j] * r : r) * r;
-      const double idx = (double)i * (double)n + (double)j;
-      if (sv > best || (sv == best && sv > 0.0 && idx < bidx)) {
-        best = sv;
-        bidx = idx;
-        bval = r;
+    const float4* row = reinterpret_cast<const float4*>(Rb + (size_t)(i - Rrow0) * Rld);
+    for (int q = lane; q < q4; q += 64) {
+      const float4 x4 = row[q];
+      const float xs[4] = {x4.x, x4.y, x4.z, x4.w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int j = 4 * q + c;
+        const double r = (double)xs[c];
+        const double sv = (hl ? (double)hl[j < n ? j : 0] * r : r) * r;
+        if (j < n && sv > best) {
+          best = sv;
+          bidx = i * n + j;
+          bval = xs[c];
+        }
       }
     }
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
-    const double b2 = __shfl_xor(best, o), i2 = __shfl_xor(bidx, o), v2 = __shfl_xor(bval, o);
+    const double b2 = __shfl_xor(best, o);
+    const int i2 = __shfl_xor(bidx, o);
+    const float v2 = __shfl_xor(bval, o);
     if (b2 > best || (b2 == best && b2 > 0.0 && i2 < bidx)) {
       best = b2;
       bidx = i2;
@@ -292,8 +302,8 @@ __device__ __noinline__ void best_entry_rows(const float* Rb, int Rrow0, int Rld
   }
   if (lane == 0) {
     part[3 * wid] = best;
-    part[3 * wid + 1] = bidx;
-    part[3 * wid + 2] = bval;
+    part[3 * wid + 1] = (double)bidx;
+    part[3 * wid + 2] = (double)bval;
   }
   __syncthreads();
 }
@@ -302,10 +312,8 @@ __device__ __noinline__ void best_entry_rows(const float* Rb, int Rrow0, int Rld
 // this workgroup's rows of both residual copies (where not yet fused), then the component's
 // previous codes are read back (device-coherent) into du/dv (its add-back, the new pending
 // update) and pu (the ALS's initial u).  Workgroup 0 adds the deflation's bytes to *bytes.
-// Out of line: it runs only in sweeps and would otherwise add to the register pressure of the
-// persistent kernel.
 template <int NT>
-__device__ __noinline__ void refit_begin(float* Rb, int Rrow0, int Rld, int len4r, float* RT, int ldt, int len4t,
+__device__ __forceinline__ void refit_begin(float* Rb, int Rrow0, int Rld, int len4r, float* RT, int ldt, int len4t,
                                          int r0, int r1, int c0, int c1, bool apply_r, bool apply_rt, float pd,
                                          uint32_t* du, uint32_t* dv, uint32_t* pu, const uint32_t* Bk,
                                          const uint32_t* Ck, int wm, int wn, double* bytes) {
@@ -343,7 +351,7 @@ __device__ __noinline__ void refit_begin(float* Rb, int Rrow0, int Rld, int len4
 // the energy when d u v^T is added back to the residual behind w = (R + d u v^T)^T u.  Sums in
 // a fixed order; each thread reads only the dl entries it stored itself.
 template <int NT>
-__device__ __noinline__ double addback_energy(const double* dl, const uint32_t* du, const uint32_t* dv,
+__device__ __forceinline__ double addback_energy(const double* dl, const uint32_t* du, const uint32_t* dv,
                                               const float* hl, int n, int wm, double d, double* part) {
   constexpr int NW = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -377,7 +385,7 @@ __device__ __noinline__ double addback_energy(const double* dl, const uint32_t* 
   return 2.0 * d * pp - d * d * (uu * hh);
 }
 
-template <int NT, bool WV, bool RL, bool SW>
+template <int NT, bool WV, bool RL, bool EXT>
 __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
   constexpr int NW = NT / 64;
   extern __shared__ __align__(16) char smem[];
@@ -519,6 +527,49 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
   };
   // Largest |R_ij| over the residual (smallest row-major index on ties), after the pending
   // deflation.  Returns the row, -1 if R == 0, -2 on a barrier failure.
+  // Best of the workgroups' candidates (value, index, entry) at xf[4q..4q+2] after a grid
+  // barrier: the largest value > 0, the smallest index on ties.  One load per thread and a tree
+  // of the same comparison (it is a total order, so the result does not depend on the tree).
+  // Leaves (value, index, entry) in part[0..2] for every thread.
+  auto global_best = [&]() {
+    double v = 0.0, ix = -1.0, ev = 0.0;
+    if (tid < G) {
+      v = ld_dev(a.xf + 4 * tid);
+      ix = ld_dev(a.xf + 4 * tid + 1);
+      ev = ld_dev(a.xf + 4 * tid + 2);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const double v2 = __shfl_xor(v, o), i2 = __shfl_xor(ix, o), e2 = __shfl_xor(ev, o);
+      if (v2 > v || (v2 == v && v2 > 0.0 && i2 < ix)) {
+        v = v2;
+        ix = i2;
+        ev = e2;
+      }
+    }
+    __syncthreads();  // part may still be read by the caller's earlier step
+    if (lane == 0) {
+      part[3 * wid] = v;
+      part[3 * wid + 1] = ix;
+      part[3 * wid + 2] = ev;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      double bb = 0.0, bi = -1.0, bv = 0.0;
+      for (int w = 0; w < NW; ++w) {
+        const double v3 = part[3 * w], i3 = part[3 * w + 1];
+        if (v3 > bb || (v3 == bb && v3 > 0.0 && i3 < bi)) {
+          bb = v3;
+          bi = i3;
+          bv = part[3 * w + 2];
+        }
+      }
+      part[0] = bb;
+      part[1] = bi;
+      part[2] = bv;
+    }
+    __syncthreads();
+  };
   auto fallback_row = [&]() -> int {
     if (have_pending && !r_applied) {
       slab_deflate<NT>(Rb, Rrow0, Rld, n4 / 4, r0, r1, du, dv, pd);
@@ -558,24 +609,16 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
           bi = ix;
         }
       }
-      st_dev(a.xf + 2 * g, bb);
-      st_dev(a.xf + 2 * g + 1, bi);
+      st_dev(a.xf + 4 * g, bb);
+      st_dev(a.xf + 4 * g + 1, bi);
+      st_dev(a.xf + 4 * g + 2, 0.0);
     }
     ++epoch;
     if (grid_barrier(a.bar, epoch, a.spin_limit, &bar_flag)) return -2;
-    if (tid == 0) {
-      double bb = 0.0, bi = -1.0;
-      for (int q = 0; q < G; ++q) {
-        const double v = ld_dev(a.xf + 2 * q), ix = ld_dev(a.xf + 2 * q + 1);
-        if (v > bb || (v == bb && v > 0.0 && ix < bi)) {
-          bb = v;
-          bi = ix;
-        }
-      }
-      sh.ivals[0] = bb > 0.0 ? (int)(bi / (double)n) : -1;
-    }
-    __syncthreads();
-    return sh.ivals[0];
+    global_best();
+    const int row = part[0] > 0.0 ? (int)(part[1] / (double)n) : -1;
+    __syncthreads();  // part is reused by the next pass
+    return row;
   };
   // Prop. 2 safeguard: the single entry whose removal lowers the residual most, i.e. the largest
   // h_j R_ij^2 (fp64, h_j R_ij first), smallest row-major index on ties, over the residual after
@@ -603,27 +646,12 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
     }
     ++epoch;
     if (grid_barrier(a.bar, epoch, a.spin_limit, &bar_flag)) return -2;
-    if (tid == 0) {
-      double bb = 0.0, bi = -1.0, bv = 0.0;
-      for (int q = 0; q < G; ++q) {
-        const double v = ld_dev(a.xf + 4 * q), ix = ld_dev(a.xf + 4 * q + 1);
-        if (v > bb || (v == bb && v > 0.0 && ix < bi)) {
-          bb = v;
-          bi = ix;
-          bv = ld_dev(a.xf + 4 * q + 2);
-        }
-      }
-      const int row = bb > 0.0 ? (int)(bi / (double)n) : -1;
-      sh.ivals[0] = row;
-      sh.ivals[2] = row >= 0 ? (int)(bi - (double)row * (double)n) : 0;
-      part[0] = bb;
-      part[1] = bv;
-    }
-    __syncthreads();
-    *sbest = part[0];
-    *col = sh.ivals[2];
-    *val = (float)part[1];
-    const int row = sh.ivals[0];
+    global_best();
+    const double bb = part[0], bi = part[1];
+    const int row = bb > 0.0 ? (int)(bi / (double)n) : -1;
+    *sbest = bb;
+    *col = row >= 0 ? (int)(bi - (double)row * (double)n) : 0;
+    *val = (float)part[2];
     __syncthreads();  // part is reused by the next pass
     return row;
   };
@@ -660,19 +688,19 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
   // component's own contribution becomes the pending update (added back inside the refit's
   // first passes), and the ALS starts from the component's previous u.
   int used = a.k;
-  const int nsweeps = SW ? a.sweeps : 0;  // the sweep code exists only in the SW kernels
+  const int nsweeps = EXT ? a.sweeps : 0;  // sweeps and the safeguard exist only in the EXT kernels
   for (int sweep = 0; sweep <= nsweeps; ++sweep) {
-  if (SW && sweep > 0) {
+  if (EXT && sweep > 0) {
     if (!(E0 > 0.0)) break;
     dead = false;
   }
-  const int ncomp = (!SW || sweep == 0) ? a.k : used;
+  const int ncomp = (!EXT || sweep == 0) ? a.k : used;
   int comp = 0;
   for (; comp < ncomp; ++comp) {
     bool fallback = false, refit_plus = false;
     float d_old = 0.0f;
     double E_before = 0.0;  // refit: the energy before the add-back
-    if (SW && sweep > 0) {
+    if (EXT && sweep > 0) {
       // ---------------- refit: add-back pending, u from the previous fit
       refit_begin<NT>(Rb, Rrow0, Rld, n4 / 4, a.RT, a.ldt, m4 / 4, r0, r1, c0, c1, have_pending && !r_applied,
                       have_pending && !rt_applied, pd, du, dv, pu, a.Bp + (size_t)comp * wm,
@@ -743,7 +771,7 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
       ++epoch;
       if (grid_barrier(a.bar, epoch, a.spin_limit, &bar_flag)) return;
       load_exchange(a.xw, n);
-      if (SW && refit_plus) {
+      if (EXT && refit_plus) {
         // energy with the contribution restored, from w = (R + X)^T u_old:
         //   |R + X|^2_H = E + 2 d v_old^T H w - d^2 |u_old|^2 |v_old|^2_H
         refit_plus = false;
@@ -801,7 +829,7 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
       }
     }
     if (dead) {
-      if (SW && sweep > 0) {  // the residual with the contribution restored is zero
+      if (EXT && sweep > 0) {  // the residual with the contribution restored is zero
         emit_zero(comp, false, 1.0 - E / E0);
         dead = false;
         continue;
@@ -815,7 +843,7 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
     double q = (double)cnt_u * Hv;
     bool sg_on = false;
     float d_sg = 0.0f;
-    if (a.safeguard) {
+    if (EXT && a.safeguard) {
       // keep whichever removes more energy: the ALS component (p^2 / q) or the best entry
       double sbest;
       int col;
@@ -840,7 +868,7 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
     double dd = (double)d;
     E = E - (2.0 * dd * p - dd * dd * q);
     bool reverted = false;
-    if (SW && sweep > 0 && E > E_before + 1e-9 * E0) {
+    if (EXT && sweep > 0 && E > E_before + 1e-9 * E0) {
       // the refit leaves more than the old component did: deflate the old one again (its
       // codes are the pending add-back's, already applied to both copies)
       reverted = true;
@@ -874,7 +902,7 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
         if (reverted) a.stats[6] += 1ull;
         a.bytes[0] += 4.0 * (double)n * (double)un + 4.0 * (double)n * (double)pn +
                       (double)usteps * 4.0 * (double)m * (double)n + vbytes +
-                      (a.safeguard ? 4.0 * (double)m * (double)n : 0.0);
+                      (EXT && a.safeguard ? 4.0 * (double)m * (double)n : 0.0);
       }
     }
     // row-sum recurrence and pending deflation
@@ -890,9 +918,9 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
     r_applied = false;
     rt_applied = false;
     __syncthreads();
-    if ((!SW || sweep == 0) && a.target > 0.0 && 1.0 - E / E0 >= a.target) break;
+    if ((!EXT || sweep == 0) && a.target > 0.0 && 1.0 - E / E0 >= a.target) break;
   }
-  if (!SW || sweep == 0) used = comp < a.k ? comp + 1 : a.k;
+  if (!EXT || sweep == 0) used = comp < a.k ? comp + 1 : a.k;
   }  // passes
   // components after an energy-target stop: zero, the final energy held (1 after a zero
   // component: E was set to 0 there)
@@ -922,9 +950,9 @@ size_t seq_smem_bytes(int m, int n, bool weighted, int G, bool rl) {
   return seq_lds_layout(m, n, weighted, G, rl).total;
 }
 
-template <bool WV, bool RL, bool SW>
+template <bool WV, bool RL, bool EXT>
 static hipError_t launch_one(const SeqArgs& a, int G, size_t smem, hipStream_t st) {
-  auto kern = seq_kernel<512, WV, RL, SW>;
+  auto kern = seq_kernel<512, WV, RL, EXT>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (e != hipSuccess) return e;
   SeqArgs copy = a;
@@ -996,7 +1024,7 @@ hipError_t seq_launch(const SeqLaunch& L, hipStream_t st) {
   a.safeguard = L.safeguard;
   a.sweeps = L.sweeps;
   const size_t smem = seq_smem_bytes(L.m, L.n, L.h != nullptr, L.grid, L.rl);
-  if (L.sweeps > 0) {
+  if (L.sweeps > 0 || L.safeguard) {
     if (L.h)
       return L.rl ? launch_one<true, true, true>(a, L.grid, smem, st) : launch_one<true, false, true>(a, L.grid, smem, st);
     return L.rl ? launch_one<false, true, true>(a, L.grid, smem, st) : launch_one<false, false, true>(a, L.grid, smem, st);
