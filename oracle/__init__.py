@@ -49,6 +49,7 @@ class _Opts(ctypes.Structure):
         ("used", ctypes.POINTER(ctypes.c_int64)),
         ("sweeps", ctypes.c_int),
         ("reverts", ctypes.POINTER(ctypes.c_int64)),
+        ("ablation", ctypes.c_int),
     ]
 
 
@@ -126,7 +127,8 @@ def project(x, tau: float = 0.0, h=None):
 
 
 def _make_opts(threads, safeguard, k_limit, gaps, counters, eexp, residual_fp64,
-               block_engine=False, energy_target=0.0, used=None, sweeps=0, reverts=None):
+               block_engine=False, energy_target=0.0, used=None, sweeps=0, reverts=None,
+               ablation=0):
     o = _Opts()
     o.threads = int(threads)
     o.safeguard = int(bool(safeguard))
@@ -141,13 +143,14 @@ def _make_opts(threads, safeguard, k_limit, gaps, counters, eexp, residual_fp64,
     o.used = used.ctypes.data_as(ip) if used is not None else ip()
     o.sweeps = int(sweeps)
     o.reverts = reverts.ctypes.data_as(ip) if reverts is not None else ip()
+    o.ablation = int(ablation)
     return o
 
 
 def decompose(A, mu: float, tau: float = 0.0, h=None, als_iters: int = 4, block: int = 1,
               threads: int = 0, safeguard: bool = False, k_limit: int = 0,
               residual_fp64: bool = False, block_engine: bool = False,
-              energy_target: float = 0.0, sweeps: int = 0):
+              energy_target: float = 0.0, sweeps: int = 0, ablation: int = 0):
     """Free-running oracle decomposition.  Returns a dict with packed B, C, D, energy, gaps,
     counters (fallbacks, safeguard activations, ALS passes, zero components), the explicit
     final energy, k and ``used`` (components fitted before an energy-target stop; all of
@@ -168,7 +171,7 @@ def decompose(A, mu: float, tau: float = 0.0, h=None, als_iters: int = 4, block:
     used = np.zeros(1, dtype=np.int64)
     reverts = np.zeros(1, dtype=np.int64)
     o = _make_opts(threads, safeguard, k_limit, gaps, counters, eexp, residual_fp64,
-                   block_engine, energy_target, used, sweeps, reverts)
+                   block_engine, energy_target, used, sweeps, reverts, ablation)
     rc = _load().externd_oracle_decompose(_ptr(A), m, n, mu, tau, _ptr(h), als_iters, block,
                                           _ptr(B), _ptr(C), _ptr(D), _ptr(energy),
                                           ctypes.addressof(o))

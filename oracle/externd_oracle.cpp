@@ -176,8 +176,16 @@ struct State {
   float tau = 0.0f;
   int T = 1;
   int nt = 1;
+  int ablation = 0;  // kNaiveTarget | kNaiveWeights (block engine)
   int64_t fallbacks = 0, safeguards = 0, passes = 0, zeros = 0;
 };
+
+// Ablations (the pages' ablation study; review, Validation):
+//   kNaiveTarget   block engine: the batched targets without Eq. 3's decorrelation, G = U^T R and
+//                  F = R H V;
+//   kNaiveWeights  both engines: the V-step projection ignores the weights, v = T_tau(w)
+//                  unweighted (the scales and the energy stay in the H-norm).
+constexpr int kNaiveTarget = 1, kNaiveWeights = 2;
 
 template <typename RT>
 void init_state(State<RT>& st, const float* A, int64_t m, int64_t n, const float* h, float tau, int T, int nt) {
@@ -298,7 +306,7 @@ Comp fit_component(State<RT>& st, bool keep_vectors, const int8_t* u_init = null
   for (int t = 1; t <= st.T; ++t) {
     mv_rt(st.R.data(), m, n, c.u.data(), w.data(), st.nt);
     for (int64_t j = 0; j < n; ++j) xs[j] = (float)w[j];
-    pv = project(xs.data(), n, st.tau, st.h, c.v.data());
+    pv = project(xs.data(), n, st.tau, (st.ablation & kNaiveWeights) ? nullptr : st.h, c.v.data());
     if (pv.j == 0) {
       // R^T u == 0: only possible for the initial u; restart from the largest-entry row.
       if (c.fallback || !set_fallback(st, c.u)) {
@@ -596,10 +604,10 @@ Block als_block(State<RT>& st, Block& b) {
     double tr = 0.0;
     for (int64_t c = 0; c < bs; ++c) tr += GU[c * bs + c];
     mul_utr(st, b.U, bs, X);
-    chol_solve(GU, bs, 1e-6 * tr / (double)bs, X.data(), n);
+    if (!(st.ablation & kNaiveTarget)) chol_solve(GU, bs, 1e-6 * tr / (double)bs, X.data(), n);
     for (int64_t c = 0; c < bs; ++c) {
       for (int64_t j = 0; j < n; ++j) xs[j] = (float)X[c * n + j];
-      Proj pr = project(xs.data(), n, st.tau, st.h, b.V.data() + c * n);
+      Proj pr = project(xs.data(), n, st.tau, (st.ablation & kNaiveWeights) ? nullptr : st.h, b.V.data() + c * n);
       b.gap[c] = std::min(b.gap[c], pr.gap);
     }
     // U-step, the same least-squares target with the roles swapped and the weighted Gram:
@@ -611,7 +619,7 @@ Block als_block(State<RT>& st, Block& b) {
     std::vector<double> Ft(bs * m);  // F^T = (GV + eps I)^-1 Q^T  (GV symmetric)
     for (int64_t i = 0; i < m; ++i)
       for (int64_t c = 0; c < bs; ++c) Ft[c * m + i] = Q[i * bs + c];
-    chol_solve(GV, bs, 1e-6 * trv / (double)bs, Ft.data(), m);
+    if (!(st.ablation & kNaiveTarget)) chol_solve(GV, bs, 1e-6 * trv / (double)bs, Ft.data(), m);
     for (int64_t c = 0; c < bs; ++c) {
       for (int64_t i = 0; i < m; ++i) xs[i] = (float)Ft[c * m + i];
       Proj pr = project(xs.data(), m, st.tau, nullptr, b.U.data() + c * m);
@@ -817,6 +825,7 @@ int decompose_t(const float* A, int64_t m, int64_t n, float mu, float tau, const
   if (opts && opts->k_limit > 0) klim = std::min(k, opts->k_limit);
   State<RT> st;
   init_state(st, A, m, n, h, tau, T, nthreads(opts));
+  st.ablation = opts ? opts->ablation : 0;
   const bool sg = opts && opts->safeguard;
   double* gaps = opts ? opts->gaps : nullptr;
   std::vector<int8_t> zu(m, 0), zv(n, 0);

@@ -39,6 +39,8 @@ typedef struct {
   int64_t* used;            /* nullable, 1: components fitted before the stop (all when none) */
   int sweeps;               /* >= 1: refinement sweeps (backfitting) after the greedy pass */
   int64_t* reverts;         /* nullable, 1: refits discarded for the old component (block) */
+  int ablation;             /* block engine: 1 = targets without Eq. 3's decorrelation,
+                               2 = V-step projection without the weights (both: 3) */
 } externd_oracle_opts;
 
 int64_t externd_oracle_rank(int64_t m, int64_t n, float mu);
