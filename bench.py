@@ -154,6 +154,9 @@ def main():
                     help="stop at the first component whose energy reaches this value")
     ap.add_argument("--safeguard", action="store_true", help="Prop. 2 single-entry safeguard")
     ap.add_argument("--block", type=int, default=None, help="override the workload's block size")
+    ap.add_argument("--mu", type=float, default=None, help="override the workload's mu")
+    ap.add_argument("--ablation", type=int, default=0,
+                    help="1: block targets without decorrelation, 2: unweighted V-step projection")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build runs the "
@@ -170,8 +173,12 @@ def main():
     c = dict(inputs.CONFIGS[args.workload])
     if args.block is not None:
         c["block"] = args.block
-    options = dict(energy_target=args.energy_target, safeguard=args.safeguard, sweeps=args.sweeps)
-    variant = any(options.values()) or args.block is not None  # not the workload as defined
+    if args.mu is not None:
+        c["mu"] = args.mu
+    options = dict(energy_target=args.energy_target, safeguard=args.safeguard, sweeps=args.sweeps,
+                   ablation=args.ablation)
+    # not the workload as defined
+    variant = any(options.values()) or args.block is not None or args.mu is not None
     A_np, h_np = inputs.make_input(args.workload)
     m, n = A_np.shape
     A = torch.from_numpy(A_np).cuda()
@@ -243,7 +250,7 @@ def main():
         "roofline": roof,
     }
     if variant:
-        res["config"]["options"] = dict(options, block=c["block"])
+        res["config"]["options"] = dict(options, block=c["block"], mu=c["mu"])
         res["config"]["components_used"] = stats["components_used"]
         res["config"]["fits_per_decomposition"] = fits
         res["config"]["safeguard_activations"] = stats["safeguard_activations"]

@@ -53,6 +53,7 @@ class Options(ctypes.Structure):
         ("energy_target", ctypes.c_double),
         ("safeguard", ctypes.c_int),
         ("sweeps", ctypes.c_int),
+        ("ablation", ctypes.c_int),
     ]
 
 
@@ -133,7 +134,7 @@ def _require(t, dtype, name):
 
 def decompose(A, mu: float, tau: float = 0.0, h=None, als_iters: int = 4, block: int = 1,
               stream=None, out=None, energy_target: float = 0.0, safeguard: bool = False,
-              sweeps: int = 0):
+              sweeps: int = 0, ablation: int = 0):
     """Run externd_decompose (externd_decompose_ex when an option is set) on a device fp32
     matrix A (m x n).
 
@@ -142,7 +143,8 @@ def decompose(A, mu: float, tau: float = 0.0, h=None, als_iters: int = 4, block:
     preallocated outputs as a dict with the same keys.  ``energy_target`` in (0, 1] stops after
     the first component whose energy reaches it (stats["components_used"]); ``safeguard`` turns
     on the best single-entry safeguard (sequential path); ``sweeps`` refinement sweeps refit
-    every component after the greedy pass."""
+    every component after the greedy pass; ``ablation`` switches parts of the method off for
+    ablation studies (1: block targets without decorrelation, 2: unweighted V-step projection)."""
     import torch
 
     A = _require(A, torch.float32, "A")
@@ -160,8 +162,8 @@ def decompose(A, mu: float, tau: float = 0.0, h=None, als_iters: int = 4, block:
             energy=torch.empty(k, dtype=torch.float64, device=dev),
         )
     st = Stats()
-    if energy_target or safeguard or sweeps:
-        opt = Options(float(energy_target), int(bool(safeguard)), int(sweeps))
+    if energy_target or safeguard or sweeps or ablation:
+        opt = Options(float(energy_target), int(bool(safeguard)), int(sweeps), int(ablation))
         rc = load().externd_decompose_ex(_dev_ptr(A), m, n, mu, tau, _dev_ptr(h), als_iters, block,
                                          _dev_ptr(out["B"]), _dev_ptr(out["C"]),
                                          _dev_ptr(out["D"]), _dev_ptr(out["energy"]),

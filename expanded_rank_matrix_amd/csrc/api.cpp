@@ -104,6 +104,8 @@ int externd_decompose_ex(const float* A, int64_t m, int64_t n, float mu, float t
   const double target = options ? options->energy_target : 0.0;
   const int safeguard = options ? options->safeguard : 0;
   const int sweeps = options ? options->sweeps : 0;
+  const int ablation = options ? options->ablation : 0;
+  if (ablation & ~3) return fail(EXTERND_EINVAL, "ablation must be a combination of 1 and 2");
   if (sweeps < 0 || sweeps > 64) return fail(EXTERND_EINVAL, "sweeps must be in [0, 64]");
   if (!(target == 0.0 || (target > 0.0 && target <= 1.0)))
     return fail(EXTERND_EINVAL, "energy_target must be 0 (off) or in (0, 1]");
@@ -121,6 +123,8 @@ int externd_decompose_ex(const float* A, int64_t m, int64_t n, float mu, float t
   int64_t b = block == -1 ? std::max<int64_t>(1, std::min<int64_t>(256, std::min(m, n) / 8)) : (block <= 1 ? 1 : block);
   if (b > k) b = k;
   if (safeguard && b > 1) return fail(EXTERND_EINVAL, "the safeguard applies to the sequential path only (block resolved to %lld)", (long long)b);
+  if ((ablation & 1) && b == 1)
+    return fail(EXTERND_EINVAL, "ablation 1 (targets without decorrelation) applies to the block path only");
   const int mi = (int)m, ni = (int)n, ki = (int)k, bi = (int)b;
   const int ldr = (ni + 3) & ~3, ldt = (mi + 3) & ~3;
 
@@ -233,6 +237,7 @@ int externd_decompose_ex(const float* A, int64_t m, int64_t n, float mu, float t
     L.target = target;
     L.safeguard = safeguard;
     L.sweeps = sweeps;
+    L.ablation = ablation;
     HIP_OR_FAIL(hipEventRecord(e0, st));
     HIP_OR_FAIL(seq_launch(L, st));
     HIP_OR_FAIL(hipEventRecord(e1, st));
@@ -257,6 +262,7 @@ int externd_decompose_ex(const float* A, int64_t m, int64_t n, float mu, float t
     L.ws = base + o_blk;
     L.target = target;
     L.sweeps = sweeps;
+    L.ablation = ablation;
     HIP_OR_FAIL(hipEventRecord(e0, st));
     HIP_OR_FAIL(block_run(L, st, &flops, &blk_bytes));
     HIP_OR_FAIL(hipEventRecord(e1, st));

@@ -1549,9 +1549,30 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops, double
   // ALS iterations of one block from its current Ut, then the scales, the update and the outputs.
   // sblk: residual updates so far (which max slot holds max |R|); addback: the first V-step also
   // yields the energy of the residual with the block's old contribution restored.
+  // Ablations: naive_t drops Eq. 3's decorrelation (the targets are U^T R and R H V themselves),
+  // hsel = nullptr projects the V-step without the weights.
+  const bool naive_t = (L.ablation & 1) != 0;
+  const float* hsel = (L.ablation & 2) ? nullptr : L.h;
+  const int ehsel = (L.ablation & 2) ? 0 : L.EHm;
   auto als_fit = [&](int sblk, int bs, int k0, double target, bool addback) -> hipError_t {
     hipError_t r;
     for (int t = 0; t < L.T; ++t) {
+      if (naive_t) {
+        if (addback && t == 0) gram_product(w, w.Ut, m, w.ldu, nullptr, 0, bs, w.GU, st);
+        utr_product(L, w, bs, sblk, st);
+        if (addback && t == 0) {
+          hipLaunchKernelGGL(addback_dot_kernel, dim3(bs), dim3(256), 0, st, w.X, n, w.Vt, w.ldv, L.h, w.ppo);
+          hipLaunchKernelGGL(addback_energy_kernel, dim3(1), dim3(256), 0, st, w.ppo, w.GU, w.GVo, L.D, k0, bs,
+                             w.st, w.rmax + kMaxWords * ((sblk + 1) & 1), w.GUo);
+        }
+        select_rows(w.X, n, w.ldv, bs, L.tau, hsel, ehsel, w.Vt, w.PHC, w.flags, 0, st);
+        gram_product(w, w.Vt, n, w.ldv, L.h, L.EHm, bs, w.GV, st);  // for the scales
+        rw_product(L, w, L.h, bs, sblk, w.Yt, st);
+        select_rows(w.Yt, m, w.ldu, bs, L.tau, nullptr, 0, w.Ut, w.PHC, w.flags, 0, st);
+        fl += 4.0 * m * n * bs;
+        by += 2.0 * rbytes;
+        continue;
+      }
       // V-step: G = (U^T U + eps I)^-1 U^T R, rows ternarized with weights h
       if ((r = gram_inverse(w.Ut, m, w.ldu, nullptr, bs, w.GU)) != hipSuccess) return r;
       utr_product(L, w, bs, sblk, st);
@@ -1562,7 +1583,7 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops, double
                            w.rmax + kMaxWords * ((sblk + 1) & 1), w.GUo);
       }
       solve(w, bs, w.X, w.Z, n, st);
-      select_rows(w.Z, n, w.ldv, bs, L.tau, L.h, L.EHm, w.Vt, w.PHC, w.flags, 0, st);
+      select_rows(w.Z, n, w.ldv, bs, L.tau, hsel, ehsel, w.Vt, w.PHC, w.flags, 0, st);
       // U-step: F^T = (V^T H V + eps I)^-1 (R H V)^T, columns ternarized without weights
       if ((r = gram_inverse(w.Vt, n, w.ldv, L.h, bs, w.GV)) != hipSuccess) return r;
       rw_product(L, w, L.h, bs, sblk, w.Yt, st);

@@ -32,6 +32,7 @@ struct SeqLaunch {
   double target = 0.0;  // > 0: stop once the energy reaches it
   int safeguard = 0;    // 1: Prop. 2 best single-entry safeguard
   int sweeps = 0;       // refinement sweeps after the greedy pass
+  int ablation = 0;     // 2: the V-step projection ignores the weights
 };
 size_t seq_smem_bytes(int m, int n, bool weighted, int G, bool rl);
 // Grid size (one workgroup per CU at most) and whether the R slab fits in LDS; 0 if the problem
@@ -72,6 +73,7 @@ struct BlockLaunch {
   void* ws;            // workspace (block_workspace_bytes)
   double target = 0.0; // > 0: stop once the energy reaches it
   int sweeps = 0;      // refinement sweeps after the greedy pass
+  int ablation = 0;    // 1: targets without Eq. 3's decorrelation, 2: V-step projection unweighted
 };
 size_t block_workspace_bytes(int m, int n, int b);
 // flops: multiply-adds of the residual by ternary operands x 2; bytes: residual bytes that the

@@ -55,6 +55,7 @@ struct SeqArgs {
   double target;       // > 0: stop once the energy reaches it
   int safeguard;       // 1: Prop. 2 best single-entry safeguard
   int sweeps;          // refinement sweeps after the greedy pass
+  int ablation;        // 2: the V-step projection ignores the weights
 };
 
 __device__ __forceinline__ int code_at(const uint32_t* pk, int i) {
@@ -778,7 +779,10 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
         const double dd0 = (double)d_old;
         E = E + addback_energy<NT>(dl, du, dv, WV ? hl : nullptr, n, wm, dd0, part);
       }
-      const SelResult sv = ternary_select<NT, WV, double, WV, true>(dl, hw, n, a.tau, a.EHm, s);
+      // (ablation: the projection may ignore the weights; the scale and energy stay weighted)
+      const bool naive_w = EXT && WV && (a.ablation & 2);
+      const SelResult sv = naive_w ? ternary_select<NT, false, double, WV, true>(dl, nullptr, n, a.tau, 0, s)
+                                   : ternary_select<NT, WV, double, WV, true>(dl, hw, n, a.tau, a.EHm, s);
       if (sv.count == 0u) {
         // R^T u == 0: only possible for the initial u; restart from the largest-entry row
         if (fallback) {
@@ -801,6 +805,18 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
       sumv = pvo.sum;
       const int vchanged = pvo.changed;
       Hv = sv.H;
+      if (naive_w) {  // sum of h over supp(v), fixed order
+        double hs = 0.0;
+        for (int j = tid; j < n; j += NT)
+          if (code_at(pv, j) != 0) hs += (double)hl[j];
+        hs = wave_sum_f64(hs);
+        __syncthreads();
+        if (lane == 0) part[wid] = hs;
+        __syncthreads();
+        Hv = 0.0;
+        for (int w = 0; w < NW; ++w) Hv += part[w];
+        __syncthreads();
+      }
       if (t >= 1) vbytes += 4.0 * (double)n * (double)cnt_u;  // rows of the u behind this V-step
       if (t >= 1 && !vchanged) {
         early = true;
@@ -1023,8 +1039,9 @@ hipError_t seq_launch(const SeqLaunch& L, hipStream_t st) {
   a.target = L.target;
   a.safeguard = L.safeguard;
   a.sweeps = L.sweeps;
+  a.ablation = L.ablation;
   const size_t smem = seq_smem_bytes(L.m, L.n, L.h != nullptr, L.grid, L.rl);
-  if (L.sweeps > 0 || L.safeguard) {
+  if (L.sweeps > 0 || L.safeguard || (L.h && (L.ablation & 2))) {
     if (L.h)
       return L.rl ? launch_one<true, true, true>(a, L.grid, smem, st) : launch_one<true, false, true>(a, L.grid, smem, st);
     return L.rl ? launch_one<false, true, true>(a, L.grid, smem, st) : launch_one<false, false, true>(a, L.grid, smem, st);

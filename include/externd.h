@@ -85,11 +85,18 @@ typedef struct {
  *                  the block path each block is added back (fp64 sum over its components, one
  *                  rounding) and refitted by block-ALS from its previous U.  With a target on the
  *                  block path the stop can fall inside a block; that block is then refitted as
- *                  a smaller block of its kept components. */
+ *                  a smaller block of its kept components.
+ *   ablation       0 for the method; bits switching parts of it off for the pages' ablation
+ *                  study (review, Validation): 1 = block path only, the batched targets without
+ *                  Eq. 3's decorrelation (V from U^T R, U from R H V directly); 2 = the V-step
+ *                  projection ignores the importance weights (the scales and the energy stay
+ *                  weighted; inert without weights).  Joint fitting is block = k (b <= 256).
+ *                  Other bits, or bit 1 on the sequential path, are EXTERND_EINVAL. */
 typedef struct {
   double energy_target;
   int safeguard;
   int sweeps;
+  int ablation;
 } externd_options;
 
 /* k = floor(mu * min(m, n) + 1e-9); -1 if m < 1, n < 1, mu not finite or > 0, or k < 1. */

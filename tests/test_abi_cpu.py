@@ -83,10 +83,12 @@ def test_decompose_options_rejected_before_device_work():
                                         fake, ctypes.byref(opt), None, None)
 
     for t in (1.5, -0.1, float("nan"), float("inf")):
-        assert call(erm.Options(t, 0, 0)) == erm.EINVAL
+        assert call(erm.Options(t, 0, 0, 0)) == erm.EINVAL
         assert "energy_target" in erm.last_error()
-    assert call(erm.Options(0.5, 2, 0)) == erm.EINVAL and "safeguard" in erm.last_error()
-    assert call(erm.Options(0.0, 0, -1)) == erm.EINVAL and "sweeps" in erm.last_error()
-    assert call(erm.Options(0.0, 0, 65)) == erm.EINVAL and "sweeps" in erm.last_error()
+    assert call(erm.Options(0.5, 2, 0, 0)) == erm.EINVAL and "safeguard" in erm.last_error()
+    assert call(erm.Options(0.0, 0, -1, 0)) == erm.EINVAL and "sweeps" in erm.last_error()
+    assert call(erm.Options(0.0, 0, 65, 0)) == erm.EINVAL and "sweeps" in erm.last_error()
     # the safeguard is defined for the sequential path; block 4 resolves to b = 4 here
-    assert call(erm.Options(0.0, 1, 0), block=4) == erm.EINVAL and "sequential" in erm.last_error()
+    assert call(erm.Options(0.0, 1, 0, 0), block=4) == erm.EINVAL and "sequential" in erm.last_error()
+    assert call(erm.Options(0.0, 0, 0, 4)) == erm.EINVAL and "ablation" in erm.last_error()
+    assert call(erm.Options(0.0, 0, 0, 1)) == erm.EINVAL and "block path" in erm.last_error()
