@@ -142,7 +142,8 @@ __device__ __forceinline__ u64 splitmix64(u64 key) {
 }
 
 __global__ void __launch_bounds__(256) omega_kernel(int8_t* Vt, int ldv, int bs, int n, long long s, int* flags,
-                                                    unsigned* rmax) {
+                                                    unsigned* rmax, double* Z0, long long zcount) {
+  for (long long x = blockIdx.x * 256ll + threadIdx.x; x < zcount; x += (long long)gridDim.x * 256) Z0[x] = 0.0;
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     flags[1] = 0;  // empty sketch columns of this block
     flags[2] = 0;  // fallback starts of this block
@@ -882,37 +883,39 @@ __global__ void __launch_bounds__(256) apply_strip_kernel(const double* __restri
   }
 }
 
-// ---- Md[c] = sum_i U[c][i] Y[c][i] (one workgroup per component, fixed reduction order)
-__global__ void __launch_bounds__(256) rowdot_kernel(const int8_t* Ut, int ldu, const double* Yt, int m, double* Md) {
-  __shared__ double red[4];
-  const int c = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  double acc = 0.0;
-  for (int i = tid; i < m; i += 256) {
-    const int u = Ut[(size_t)c * ldu + i];
-    if (u) acc += (double)u * Yt[(size_t)c * m + i];
-  }
-  acc = wave_sum_f64(acc);
-  if (lane == 0) red[wid] = acc;
-  __syncthreads();
-  if (tid == 0) Md[c] = (red[0] + red[1]) + (red[2] + red[3]);
-}
-
 // ---- one workgroup per component row: T[c] = T_tau(fp32(X[c]); h) -----------------------------
 template <bool W>
+// Z0 (nullable): row c of the next split-K contraction's output is cleared here (zlen doubles),
+// which saves that contraction a separate clearing launch.  Md (nullable): Md[c] = T[c] . Yd[c]
+// over the L entries (the last U-step's u_c^T Q_c for the scales), fixed reduction order.
 __global__ void __launch_bounds__(512) select_rows_kernel(const double* X, int L, int ldT, float tau,
                                                           const float* h, int EHm, int8_t* T, double* PHC,
-                                                          int* flags, int flag_empty) {
+                                                          int* flags, int flag_empty, double* Z0, int zlen,
+                                                          const double* Yd, double* Md) {
   __shared__ SelScratchT<W> s;
+  __shared__ double red[8];
   const int c = blockIdx.x;
   const double* x = X + (size_t)c * L;
+  if (Z0)
+    for (int j = threadIdx.x; j < zlen; j += 512) Z0[(size_t)c * zlen + j] = 0.0;
   if (flags[0]) {  // residual is zero: nothing to select
     for (int j = threadIdx.x; j < ldT; j += 512) T[(size_t)c * ldT + j] = 0;
     return;
   }
   const SelResult r = ternary_select<512, W>(x, h, L, tau, EHm, s);
+  double dot = 0.0;
   for (int j = threadIdx.x; j < ldT; j += 512) {  // the padding [L, ldT) stays zero
     const float xv = j < L ? (float)x[j] : 0.0f;
-    T[(size_t)c * ldT + j] = selected(xv, r) ? (xv > 0.0f ? (int8_t)1 : (int8_t)-1) : (int8_t)0;
+    const int8_t t = selected(xv, r) ? (xv > 0.0f ? (int8_t)1 : (int8_t)-1) : (int8_t)0;
+    T[(size_t)c * ldT + j] = t;
+    if (Md && t) dot += (double)t * Yd[(size_t)c * L + j];
+  }
+  if (Md) {
+    dot = wave_sum_f64(dot);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = dot;
+    __syncthreads();
+    if (threadIdx.x == 0)
+      Md[c] = ((red[0] + red[1]) + (red[2] + red[3])) + ((red[4] + red[5]) + (red[6] + red[7]));
   }
   if (threadIdx.x == 0) {
     PHC[3 * c + 0] = r.P;
@@ -980,6 +983,13 @@ __global__ void __launch_bounds__(512) fallback_kernel(const float* R, int ldr, 
   }
 }
 
+// Rows of GU and GV staged at a time by scales_kernel: 96 KB of dynamic LDS at most.
+__host__ __device__ inline int scales_window(int bs) {
+  const int w = (96 * 1024) / (16 * bs);
+  return w < bs ? w : bs;
+}
+__host__ inline size_t scales_lds_bytes(int bs) { return (size_t)16 * scales_window(bs) * bs; }
+
 // ---- scales and energy: one workgroup, thread t owns component t.  The sequential scale of each
 // component against the residual left by the earlier ones of the block:
 //   p_t = Md_t - sum_{c < t} d_c (u_t . u_c) (v_c^T H v_t),   d_t = fp32(p_t / q_t),
@@ -1018,26 +1028,54 @@ __global__ void __launch_bounds__(256) scales_kernel(const double* Md, const dou
     return;
   }
   const bool own = tid < bs;
-  double acc = own ? Md[tid] : 0.0;
-  const double q = own ? GU[(size_t)tid * bs + tid] * GV[(size_t)tid * bs + tid] : 0.0;
-  double gu = own ? GU[tid] : 0.0, gv = own ? GV[tid] : 0.0;  // row 0
-  for (int c = 0; c < bs; ++c) {
-    if (tid == c) {
-      const float d = q > 0.0 ? (float)(acc / q) : 0.0f;
-      ds[c] = d;
-      ps[c] = acc;
-      qs[c] = q;
+  // One wave walks the recurrence: lane l owns components l, l + 64, l + 128, l + 192 (slots);
+  // component c's value comes to every lane by readlane, so no workgroup barrier per step.  The
+  // rows of GU and GV it reads are staged in LDS by the whole workgroup, `wr` rows at a time, so
+  // that the walk waits on no global load.
+  extern __shared__ __align__(16) double sg[];  // wr x bs of GU, then wr x bs of GV
+  const int wr = scales_window(bs);
+  double* sgu = sg;
+  double* sgv = sg + (size_t)wr * bs;
+  double acc[4], q[4];
+  if (tid < 64) {
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl) {
+      const int c2 = tid + 64 * sl;
+      const bool o = c2 < bs;
+      acc[sl] = o ? Md[c2] : 0.0;
+      q[sl] = o ? GU[(size_t)c2 * bs + c2] * GV[(size_t)c2 * bs + c2] : 0.0;
     }
-    // prefetch row c + 1 before waiting
-    double gu2 = 0.0, gv2 = 0.0;
-    if (own && c + 1 < bs) {
-      gu2 = GU[(size_t)(c + 1) * bs + tid];
-      gv2 = GV[(size_t)(c + 1) * bs + tid];
+  }
+  for (int w0 = 0; w0 < bs; w0 += wr) {
+    const int rows = bs - w0 < wr ? bs - w0 : wr;
+    __syncthreads();  // the previous window is consumed
+    for (int x = tid; x < rows * bs; x += 256) {
+      sgu[x] = GU[(size_t)w0 * bs + x];
+      sgv[x] = GV[(size_t)w0 * bs + x];
     }
     __syncthreads();
-    if (own && tid > c) acc -= (double)ds[c] * gu * gv;
-    gu = gu2;
-    gv = gv2;
+    if (tid < 64) {
+      const int lane = tid;
+      for (int c = w0; c < w0 + rows; ++c) {
+        const int sc = c >> 6, lc = c & 63;  // uniform
+        const double a_own = sc == 0 ? acc[0] : (sc == 1 ? acc[1] : (sc == 2 ? acc[2] : acc[3]));
+        const double q_own = sc == 0 ? q[0] : (sc == 1 ? q[1] : (sc == 2 ? q[2] : q[3]));
+        const double ac = readlane_f64(a_own, lc), qc = readlane_f64(q_own, lc);
+        const float d = qc > 0.0 ? (float)(ac / qc) : 0.0f;
+        if (lane == 0) {
+          ds[c] = d;
+          ps[c] = ac;
+          qs[c] = qc;
+        }
+        const double* gur = sgu + (size_t)(c - w0) * bs;
+        const double* gvr = sgv + (size_t)(c - w0) * bs;
+#pragma unroll
+        for (int sl = 0; sl < 4; ++sl) {
+          const int c2 = lane + 64 * sl;
+          if (c2 < bs && c2 > c) acc[sl] -= (double)d * gur[c2] * gvr[c2];
+        }
+      }
+    }
   }
   __syncthreads();
   if (tid == 0) {
@@ -1071,19 +1109,20 @@ __global__ void __launch_bounds__(256) scales_kernel(const double* Md, const dou
 
 // ---- update: R <- fl32(R - U diag(d) V^T), fp64 MFMA with K = bs ----------------------------
 // Tile 64 x 64 of R; wave w owns rows 16w..16w+15 and four 16-column strips.
-// A[i][k] = d_k U[k][i], B[k][j] = V[k][j].
-__global__ void __launch_bounds__(256) update_kernel(float* R, int ldr, int m, int n, const int8_t* Ut, int ldu,
+// A[i][k] = d_k U[k][i], B[k][j] = V[k][j].  The operands are staged 64 components at a time
+// (10 KB of LDS), so that many workgroups share a CU: the kernel streams R once each way and
+// needs many loads in flight.  Each lane's 16 entries of R are loaded before anything else
+// (the dead-residual flag included), in the MFMA output layout: lane l of wave w holds rows
+// 16 w + l / 16 + 4 r, column 16 t + l % 16 of strip t.  Entries whose product is zero are not
+// written back.
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) update_kernel(float* R, int ldr, int m, int n, const int8_t* Ut, int ldu,
                                                      const int8_t* Vt, int ldv, const float* dvec, int bs,
                                                      const int* flags, unsigned* rmax_next) {
-  if (flags[0]) return;
-  __shared__ __align__(16) int8_t Us[256][64 + 16];
-  __shared__ __align__(16) int8_t Vs[256][64 + 16];
-  __shared__ float ds[256];
+  __shared__ __align__(16) int8_t Us[64][64 + 16];
+  __shared__ __align__(16) int8_t Vs[64][64 + 16];
+  __shared__ float ds[64];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
-  const int bs4 = (bs + 3) & ~3;
-  // this lane's 16 residual entries, loaded first so that their latency overlaps the staging and
-  // the products
   float rv[4][4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
@@ -1094,28 +1133,36 @@ __global__ void __launch_bounds__(256) update_kernel(float* R, int ldr, int m, i
       rv[t][r] = (i < m && j < n) ? R[(size_t)i * ldr + j] : 0.0f;
     }
   }
-  // 16-byte pieces: rows of Ut / Vt are zero-padded to a multiple of 16, and i0, j0 are multiples
-  // of 64, so a piece is either inside the padded row or past it
-  for (int x = tid; x < bs4 * 4; x += 256) {
-    const int c = x >> 2, q = (x & 3) * 16;
-    const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-    *reinterpret_cast<uint4*>(&Us[c][q]) =
-        (c < bs && i0 + q < ldu) ? *reinterpret_cast<const uint4*>(Ut + (size_t)c * ldu + i0 + q) : z;
-    *reinterpret_cast<uint4*>(&Vs[c][q]) =
-        (c < bs && j0 + q < ldv) ? *reinterpret_cast<const uint4*>(Vt + (size_t)c * ldv + j0 + q) : z;
-  }
-  for (int c = tid; c < bs4; c += 256) ds[c] = c < bs ? dvec[c] : 0.0f;
-  __syncthreads();
+  if (flags[0]) return;
+  const int bs4 = (bs + 3) & ~3;
   dbl4 acc[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) acc[t] = (dbl4){0.0, 0.0, 0.0, 0.0};
-  for (int k0 = 0; k0 < bs4; k0 += 4) {
-    const int k = k0 + (lane >> 4);
-    const double a = (double)ds[k] * (double)Us[k][wid * 16 + (lane & 15)];
+  for (int kc = 0; kc < bs4; kc += 64) {
+    const int kn = bs4 - kc < 64 ? bs4 - kc : 64;
+    if (kc > 0) __syncthreads();  // the previous chunk's operands are consumed
+    // 16-byte pieces: rows of Ut / Vt are zero-padded to a multiple of 16, and i0, j0 are
+    // multiples of 64, so a piece is either inside the padded row or past it
+    {
+      const int x = tid, c = x >> 2, q = (x & 3) * 16, cg = kc + c;
+      const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+      if (c < kn) {
+        *reinterpret_cast<uint4*>(&Us[c][q]) =
+            (cg < bs && i0 + q < ldu) ? *reinterpret_cast<const uint4*>(Ut + (size_t)cg * ldu + i0 + q) : z;
+        *reinterpret_cast<uint4*>(&Vs[c][q]) =
+            (cg < bs && j0 + q < ldv) ? *reinterpret_cast<const uint4*>(Vt + (size_t)cg * ldv + j0 + q) : z;
+      }
+    }
+    if (tid < kn) ds[tid] = kc + tid < bs ? dvec[kc + tid] : 0.0f;
+    __syncthreads();
+    for (int k0 = 0; k0 < kn; k0 += 4) {
+      const int k = k0 + (lane >> 4);
+      const double a = (double)ds[k] * (double)Us[k][wid * 16 + (lane & 15)];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const double bv = (double)Vs[k][t * 16 + (lane & 15)];
-      acc[t] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, bv, acc[t], 0, 0, 0);
+      for (int t = 0; t < 4; ++t) {
+        const double bv = (double)Vs[k][t * 16 + (lane & 15)];
+        acc[t] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, bv, acc[t], 0, 0, 0);
+      }
     }
   }
   unsigned mx = 0u;  // largest |R| of the tile after the update (fp32 bits)
@@ -1126,10 +1173,10 @@ __global__ void __launch_bounds__(256) update_kernel(float* R, int ldr, int m, i
     for (int r = 0; r < 4; ++r) {
       const int i = i0 + wid * 16 + (lane >> 4) + 4 * r;
       if (i < m && j < n) {
-        const double s = acc[t][r];
+        const double sv = acc[t][r];
         float x = rv[t][r];
-        if (s != 0.0) {
-          x = (float)((double)x - s);
+        if (sv != 0.0) {
+          x = (float)((double)x - sv);
           R[(size_t)i * ldr + j] = x;
         }
         const unsigned b = __float_as_uint(x) & 0x7FFFFFFFu;
@@ -1197,11 +1244,15 @@ __global__ void __launch_bounds__(256) stop_fill_kernel(uint32_t* Bp, uint32_t* 
 __global__ void __launch_bounds__(256) refit_load_kernel(const uint32_t* Bp, const uint32_t* Cp, const float* D, int m,
                                                          int n, int k0, int bs, int8_t* Ut, int ldu, int8_t* Vt,
                                                          int ldv, float* dvec, float* dold, double* st, int* flags,
-                                                         unsigned* rmax_slot, bool restore) {
+                                                         unsigned* rmax_slot, bool restore, double* Z0,
+                                                         long long zcount) {
   const int wm = (m + 15) / 16, wn = (n + 15) / 16;
   if (restore) {
     if (!flags[5]) return;
-  } else if (blockIdx.x == 0) {
+  } else {
+    for (long long x = blockIdx.x * 256ll + threadIdx.x; x < zcount; x += (long long)gridDim.x * 256) Z0[x] = 0.0;
+  }
+  if (!restore && blockIdx.x == 0) {
     if (threadIdx.x < kMaxWords) rmax_slot[threadIdx.x] = 0u;
     if (threadIdx.x < bs) {
       dvec[threadIdx.x] = -D[k0 + threadIdx.x];
@@ -1378,13 +1429,26 @@ static void zero_fill(double* p, long long count, hipStream_t st) {
 }
 
 // Y^T (bs x m) = (R diag(h) V^T)^T for V = Vt rows, on int8 MFMA with R in fixed point
+// Whether the contraction of R (rows or columns) with bs ternary vectors splits K, so that its
+// output must be cleared first.
+static bool rw_splits(const BlockLaunch& L, int bs) {
+  const int nct = bs <= 16 ? 1 : (bs <= 32 ? 2 : 4);
+  int kspan = 0;
+  return i8_splits(((L.m + 63) / 64) * ((bs + 16 * nct - 1) / (16 * nct)), L.n, &kspan) > 1;
+}
+static bool utr_splits(const BlockLaunch& L, int bs) {
+  const int nct = bs <= 16 ? 1 : (bs <= 32 ? 2 : 4);
+  int kspan = 0;
+  return i8_splits(((L.n + 63) / 64) * ((bs + 16 * nct - 1) / (16 * nct)), L.m, &kspan) > 1;
+}
+
 static void rw_product(const BlockLaunch& L, const BlockWs& w, const float* h, int bs, int sblk, double* outT,
-                       hipStream_t st) {
+                       hipStream_t st, bool prezeroed = false) {
   const int nct = bs <= 16 ? 1 : (bs <= 32 ? 2 : 4);  // 8 tiles: one wave per SIMD, slower
   const int gx = (L.m + 63) / 64, gy = (bs + 16 * nct - 1) / (16 * nct);
   int kspan = 0;
   const int gz = i8_splits(gx * gy, L.n, &kspan);
-  if (gz > 1) zero_fill(outT, (long long)bs * L.m, st);
+  if (gz > 1 && !prezeroed) zero_fill(outT, (long long)bs * L.m, st);
   const dim3 grid(gx, gy, gz);
   if (nct == 1)
     hipLaunchKernelGGL(rv_i8_kernel<1>, grid, dim3(256), 0, st, L.R, L.ldr, L.m, L.n, w.Vt, w.ldv, h, L.EHm, bs,
@@ -1409,12 +1473,13 @@ static void gram_product(const BlockWs& w, const int8_t* T, int len, int ldt, co
 }
 
 // X (bs x n) = U^T R, on int8 MFMA with R in fixed point
-static void utr_product(const BlockLaunch& L, const BlockWs& w, int bs, int sblk, hipStream_t st) {
+static void utr_product(const BlockLaunch& L, const BlockWs& w, int bs, int sblk, hipStream_t st,
+                        bool prezeroed = false) {
   const int nct = bs <= 16 ? 1 : (bs <= 32 ? 2 : 4);  // 8 tiles: one wave per SIMD, slower
   const int gx = (L.n + 63) / 64, gy = (bs + 16 * nct - 1) / (16 * nct);
   int kspan = 0;
   const int gz = i8_splits(gx * gy, L.m, &kspan);
-  if (gz > 1) zero_fill(w.X, (long long)bs * L.n, st);
+  if (gz > 1 && !prezeroed) zero_fill(w.X, (long long)bs * L.n, st);
   const dim3 grid(gx, gy, gz);
   if (nct == 1)
     hipLaunchKernelGGL(utr_i8_kernel<1>, grid, dim3(256), 0, st, L.R, L.ldr, L.m, L.n, w.Ut, w.ldu, bs, w.rmax,
@@ -1483,13 +1548,14 @@ static void solve(const BlockWs& w, int bs, const double* in, double* out, int n
 }
 
 static void select_rows(const double* X, int L, int ldT, int bs, float tau, const float* h, int EHm, int8_t* T,
-                        double* PHC, int* flags, int flag_empty, hipStream_t st) {
+                        double* PHC, int* flags, int flag_empty, hipStream_t st, double* Z0 = nullptr,
+                        int zlen = 0, const double* Yd = nullptr, double* Md = nullptr) {
   if (h)
     hipLaunchKernelGGL(select_rows_kernel<true>, dim3(bs), dim3(512), 0, st, X, L, ldT, tau, h, EHm, T, PHC, flags,
-                       flag_empty);
+                       flag_empty, Z0, zlen, Yd, Md);
   else
     hipLaunchKernelGGL(select_rows_kernel<false>, dim3(bs), dim3(512), 0, st, X, L, ldT, tau, h, EHm, T, PHC, flags,
-                       flag_empty);
+                       flag_empty, Z0, zlen, Yd, Md);
 }
 
 // Side stream for the Gram and inverse-factor work, which overlaps the residual contraction of
@@ -1518,6 +1584,19 @@ static hipError_t side_stream(SideStream** out) {
 
 hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops, double* bytes) {
   if (L.b > 256) return hipErrorInvalidValue;
+  {
+    static bool scales_attr[64] = {};  // once per device: dynamic LDS above 64 KB
+    int dev = 0;
+    hipError_t ea = hipGetDevice(&dev);
+    if (ea != hipSuccess) return ea;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    if (!scales_attr[dev]) {
+      ea = hipFuncSetAttribute((const void*)scales_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)(96 * 1024));
+      if (ea != hipSuccess) return ea;
+      scales_attr[dev] = true;
+    }
+  }
   const BlockWs w = carve(L.ws, L.m, L.n, L.b);
   const int m = L.m, n = L.n;
   SideStream* ss = nullptr;
@@ -1554,28 +1633,34 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops, double
   const bool naive_t = (L.ablation & 1) != 0;
   const float* hsel = (L.ablation & 2) ? nullptr : L.h;
   const int ehsel = (L.ablation & 2) ? 0 : L.EHm;
+  // Split-K outputs are cleared by the kernel before their contraction: X by the selection of U
+  // (or the sketch's, or the refit's load), Yt by the selection of V (or the sketch's Omega).
   auto als_fit = [&](int sblk, int bs, int k0, double target, bool addback) -> hipError_t {
     hipError_t r;
+    const bool xz = utr_splits(L, bs), yz = rw_splits(L, bs);
     for (int t = 0; t < L.T; ++t) {
+      double* x0 = (xz && t + 1 < L.T) ? w.X : nullptr;  // for the next V-step
+      double* y0 = yz ? w.Yt : nullptr;                  // for this U-step
       if (naive_t) {
         if (addback && t == 0) gram_product(w, w.Ut, m, w.ldu, nullptr, 0, bs, w.GU, st);
-        utr_product(L, w, bs, sblk, st);
+        utr_product(L, w, bs, sblk, st, true);
         if (addback && t == 0) {
           hipLaunchKernelGGL(addback_dot_kernel, dim3(bs), dim3(256), 0, st, w.X, n, w.Vt, w.ldv, L.h, w.ppo);
           hipLaunchKernelGGL(addback_energy_kernel, dim3(1), dim3(256), 0, st, w.ppo, w.GU, w.GVo, L.D, k0, bs,
                              w.st, w.rmax + kMaxWords * ((sblk + 1) & 1), w.GUo);
         }
-        select_rows(w.X, n, w.ldv, bs, L.tau, hsel, ehsel, w.Vt, w.PHC, w.flags, 0, st);
+        select_rows(w.X, n, w.ldv, bs, L.tau, hsel, ehsel, w.Vt, w.PHC, w.flags, 0, st, y0, m);
         gram_product(w, w.Vt, n, w.ldv, L.h, L.EHm, bs, w.GV, st);  // for the scales
-        rw_product(L, w, L.h, bs, sblk, w.Yt, st);
-        select_rows(w.Yt, m, w.ldu, bs, L.tau, nullptr, 0, w.Ut, w.PHC, w.flags, 0, st);
+        rw_product(L, w, L.h, bs, sblk, w.Yt, st, true);
+        select_rows(w.Yt, m, w.ldu, bs, L.tau, nullptr, 0, w.Ut, w.PHC, w.flags, 0, st, x0, n,
+                    t + 1 == L.T ? w.Yt : nullptr, t + 1 == L.T ? w.Md : nullptr);
         fl += 4.0 * m * n * bs;
         by += 2.0 * rbytes;
         continue;
       }
       // V-step: G = (U^T U + eps I)^-1 U^T R, rows ternarized with weights h
       if ((r = gram_inverse(w.Ut, m, w.ldu, nullptr, bs, w.GU)) != hipSuccess) return r;
-      utr_product(L, w, bs, sblk, st);
+      utr_product(L, w, bs, sblk, st, true);
       if ((r = join()) != hipSuccess) return r;
       if (addback && t == 0) {
         hipLaunchKernelGGL(addback_dot_kernel, dim3(bs), dim3(256), 0, st, w.X, n, w.Vt, w.ldv, L.h, w.ppo);
@@ -1583,27 +1668,28 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops, double
                            w.rmax + kMaxWords * ((sblk + 1) & 1), w.GUo);
       }
       solve(w, bs, w.X, w.Z, n, st);
-      select_rows(w.Z, n, w.ldv, bs, L.tau, hsel, ehsel, w.Vt, w.PHC, w.flags, 0, st);
+      select_rows(w.Z, n, w.ldv, bs, L.tau, hsel, ehsel, w.Vt, w.PHC, w.flags, 0, st, y0, m);
       // U-step: F^T = (V^T H V + eps I)^-1 (R H V)^T, columns ternarized without weights
       if ((r = gram_inverse(w.Vt, n, w.ldv, L.h, bs, w.GV)) != hipSuccess) return r;
-      rw_product(L, w, L.h, bs, sblk, w.Yt, st);
+      rw_product(L, w, L.h, bs, sblk, w.Yt, st, true);
       if ((r = join()) != hipSuccess) return r;
       solve(w, bs, w.Yt, w.Ft, m, st);
-      select_rows(w.Ft, m, w.ldu, bs, L.tau, nullptr, 0, w.Ut, w.PHC, w.flags, 0, st);
+      select_rows(w.Ft, m, w.ldu, bs, L.tau, nullptr, 0, w.Ut, w.PHC, w.flags, 0, st, x0, n,
+                  t + 1 == L.T ? w.Yt : nullptr, t + 1 == L.T ? w.Md : nullptr);
       fl += 4.0 * m * n * bs;
       by += 2.0 * rbytes;
     }
     // scales against Q = R H V of the last U-step, then the update and the outputs
-    gram_product(w, w.Ut, m, w.ldu, nullptr, 0, bs, w.GU, st);
-    hipLaunchKernelGGL(rowdot_kernel, dim3(bs), dim3(256), 0, st, w.Ut, w.ldu, w.Yt, m, w.Md);
-    hipLaunchKernelGGL(scales_kernel, dim3(1), dim3(256), 0, st, w.Md, w.GU, w.GV, bs, k0, L.T, w.d, L.D, L.energy,
-                       w.st, w.flags, L.stats, target);
+    gram_product(w, w.Ut, m, w.ldu, nullptr, 0, bs, w.GU, st);  // Md came with the last selection
+    hipLaunchKernelGGL(scales_kernel, dim3(1), dim3(256), scales_lds_bytes(bs), st, w.Md, w.GU, w.GV, bs, k0, L.T,
+                       w.d, L.D, L.energy, w.st, w.flags, L.stats, target);
     if (addback) {  // keep the better of the refit and the old block
       hipLaunchKernelGGL(refit_choose_kernel, dim3(1), dim3(256), 0, st, w.ppo, w.GUo, w.GVo, w.dold, k0, bs, w.d,
                          L.D, L.energy, w.st, w.flags, L.stats);
       const long long nb = ((long long)bs * (w.ldu + w.ldv) + 255) / 256;
       hipLaunchKernelGGL(refit_load_kernel, dim3((unsigned)(nb < 1024 ? nb : 1024)), dim3(256), 0, st, L.Bp, L.Cp,
-                         L.D, m, n, k0, bs, w.Ut, w.ldu, w.Vt, w.ldv, w.d, w.dold, w.st, w.flags, w.rmax, true);
+                         L.D, m, n, k0, bs, w.Ut, w.ldu, w.Vt, w.ldv, w.d, w.dold, w.st, w.flags, w.rmax, true,
+                         nullptr, 0ll);
     }
     hipLaunchKernelGGL(update_kernel, dim3((n + 63) / 64, (m + 63) / 64), dim3(256), 0, st, L.R, L.ldr, m, n, w.Ut,
                        w.ldu, w.Vt, w.ldv, w.d, bs, w.flags, w.rmax + kMaxWords * ((sblk + 1) & 1));
@@ -1618,9 +1704,10 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops, double
     const int k0 = s * L.b;
     // sketch
     hipLaunchKernelGGL(omega_kernel, dim3(256), dim3(256), 0, st, w.Vt, w.ldv, bs, n, (long long)s, w.flags,
-                       w.rmax);
-    rw_product(L, w, nullptr, bs, s, w.Yt, st);
-    select_rows(w.Yt, m, w.ldu, bs, L.tau, nullptr, 0, w.Ut, w.PHC, w.flags, 1, st);
+                       w.rmax, w.Yt, rw_splits(L, bs) ? (long long)bs * m : 0ll);
+    rw_product(L, w, nullptr, bs, s, w.Yt, st, true);
+    select_rows(w.Yt, m, w.ldu, bs, L.tau, nullptr, 0, w.Ut, w.PHC, w.flags, 1, st,
+                utr_splits(L, bs) ? w.X : nullptr, n);
     hipLaunchKernelGGL(zero_check_kernel, dim3(1), dim3(256), 0, st, L.R, L.ldr, m, n, w.flags, w.st);
     hipLaunchKernelGGL(fallback_kernel, dim3(1), dim3(512), 0, st, L.R, L.ldr, m, n, bs, w.Ut, w.ldu, w.PHC,
                        w.flags, w.used);
@@ -1666,7 +1753,8 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops, double
       const long long nb = (tot + 255) / 256;
       hipLaunchKernelGGL(refit_load_kernel, dim3((unsigned)(nb < 1024 ? nb : 1024)), dim3(256), 0, st, L.Bp, L.Cp,
                          L.D, m, n, k0, bs, w.Ut, w.ldu, w.Vt, w.ldv, w.d, w.dold, w.st, w.flags,
-                         w.rmax + kMaxWords * ((step + 1) & 1), false);
+                         w.rmax + kMaxWords * ((step + 1) & 1), false, w.X,
+                         utr_splits(L, bs) ? (long long)bs * n : 0ll);
       // add the block back: R <- fl32(R + U diag(d) V^T), the new residual max into the next slot
       hipLaunchKernelGGL(update_kernel, dim3((n + 63) / 64, (m + 63) / 64), dim3(256), 0, st, L.R, L.ldr, m, n,
                          w.Ut, w.ldu, w.Vt, w.ldv, w.d, bs, w.flags, w.rmax + kMaxWords * ((step + 1) & 1));
