@@ -213,64 +213,84 @@ __device__ __forceinline__ void fx_operands(const int (&nv)[16], v4i (&op)[4]) {
 
 __device__ __forceinline__ v4i load16(const int8_t* p) { return *reinterpret_cast<const v4i*>(p); }
 
+// The residual tile of each 64-wide k chunk is loaded by the whole workgroup as float4 rows
+// (256 contiguous bytes per tile row: full cache lines), converted to its fixed-point image
+// once, and staged in LDS; each lane then reads its 16 values of the MFMA layout from there.  The
+// next chunk's loads are issued before the current chunk is consumed.
+constexpr int kTileP = 68;  // int32 pitch of a [64 rows][64 k] tile (rows 16 B aligned)
+constexpr int kTileQ = 65;  // int32 pitch of a [64 k][64 cols] tile (column reads conflict-free)
+
 // out[c][i] (+)= sum_{k in this split} x_ik T[c][k], x_ik = R[i][k] (h_k): rows of R x components.
 // Workgroup: 64 rows (16 per wave) x 16 NCT components (blockIdx.y), K range blockIdx.z.
 template <int NCT>
 __global__ void __launch_bounds__(256) rv_i8_kernel(const float* R, int ldr, int rows, int K, const int8_t* T,
                                                     int ldt, const float* h, int ehm, int bs, const unsigned* rmax,
                                                     int sblk, int kspan, double* out) {
+  __shared__ __align__(16) int tile[64 * kTileP];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int lr = lane & 15, g = lane >> 4;
-  const int i = blockIdx.x * 64 + wid * 16 + lr;  // row supplied by this lane
   const int c0 = blockIdx.y * 16 * NCT;
   const int kb = blockIdx.z * kspan, ke = kb + kspan < K ? kb + kspan : K;
   const int E = fx_exponent(rmax, sblk, h ? ehm : 0);
   const int sc = 30 - E < 126 ? (30 - E > -126 ? 30 - E : -126) : 126;  // scale 2^sc, a normal float
   const float fscale = ldexpf(1.0f, sc);
   const double dscale = ldexp(1.0, sc);
-  const bool rok = i < rows;
-  const float* rp = R + (size_t)(rok ? i : 0) * ldr;
+  // staging role: thread t loads tile rows t / 16 + 16 q, k columns 4 (t % 16) .. + 3
+  const int srow = tid >> 4, scol = 4 * (tid & 15);
   v4i acc[NCT][4];
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[ct][t] = (v4i){0, 0, 0, 0};
-  // operands of the chunk at k0 + 16 g: 16 values of row i and 16 bytes of each component row
-  auto load = [&](int k0, float (&xv)[16], v4i (&tb)[NCT]) {
-    const int k = k0 + 16 * g;
+  float4 pre[4];
+  float4 hpre = make_float4(0.f, 0.f, 0.f, 0.f);
+  auto fetch = [&](int k0) {
+    const int k = k0 + scol;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (rok && k + 4 * q < ke) v = *reinterpret_cast<const float4*>(rp + k + 4 * q);
-      xv[4 * q] = v.x;
-      xv[4 * q + 1] = v.y;
-      xv[4 * q + 2] = v.z;
-      xv[4 * q + 3] = v.w;
+      const int i = blockIdx.x * 64 + srow + 16 * q;
+      pre[q] = (i < rows && k < ke) ? *reinterpret_cast<const float4*>(R + (size_t)i * ldr + k)
+                                    : make_float4(0.f, 0.f, 0.f, 0.f);
     }
+    if (h && k < ke)  // the caller's weights: scalar loads, each inside [0, K)
+      hpre = make_float4(h[k], k + 1 < K ? h[k + 1] : 0.f, k + 2 < K ? h[k + 2] : 0.f, k + 3 < K ? h[k + 3] : 0.f);
+  };
+  if (kb < ke) fetch(kb);
+  for (int k0 = kb; k0 < ke; k0 += 64) {
+    __syncthreads();  // the previous chunk's tile is consumed
+    {
+      const int k = k0 + scol;
+      const float hv[4] = {hpre.x, hpre.y, hpre.z, hpre.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float xv[4] = {pre[q].x, pre[q].y, pre[q].z, pre[q].w};
+        int nv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool in = k + e < ke;
+          if (h) nv[e] = in ? __double2int_rn((double)xv[e] * (double)hv[e] * dscale) : 0;
+          else nv[e] = in ? __float2int_rn(xv[e] * fscale) : 0;
+        }
+        *reinterpret_cast<int4*>(&tile[(srow + 16 * q) * kTileP + scol]) = make_int4(nv[0], nv[1], nv[2], nv[3]);
+      }
+    }
+    __syncthreads();
+    if (k0 + 64 < ke) fetch(k0 + 64);
+    const int k = k0 + 16 * g;
+    v4i tb[NCT];
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
       const int c = c0 + ct * 16 + lr;
       tb[ct] = (c < bs && k < ke) ? load16(T + (size_t)c * ldt + k) : (v4i){0, 0, 0, 0};
     }
-  };
-  float xn[16];
-  v4i tn[NCT];
-  if (kb < ke) load(kb, xn, tn);
-  for (int k0 = kb; k0 < ke; k0 += 64) {  // the next chunk loads while this one is converted
-    const int k = k0 + 16 * g;
-    float xv[16];
-    v4i tb[NCT];
-#pragma unroll
-    for (int t = 0; t < 16; ++t) xv[t] = xn[t];
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) tb[ct] = tn[ct];
-    if (k0 + 64 < ke) load(k0 + 64, xn, tn);
     int nv[16];
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const bool in = k + t < ke;
-      if (h) nv[t] = in ? __double2int_rn((double)xv[t] * (double)h[k + t] * dscale) : 0;
-      else nv[t] = in ? __float2int_rn(xv[t] * fscale) : 0;
+    for (int p = 0; p < 4; ++p) {
+      const int4 v = *reinterpret_cast<const int4*>(&tile[(wid * 16 + lr) * kTileP + 16 * g + 4 * p]);
+      nv[4 * p] = v.x;
+      nv[4 * p + 1] = v.y;
+      nv[4 * p + 2] = v.z;
+      nv[4 * p + 3] = v.w;
     }
     v4i da[4];
     fx_operands(nv, da);
@@ -305,6 +325,7 @@ __global__ void __launch_bounds__(256) rv_i8_kernel(const float* R, int ldr, int
 template <int NCT>
 __global__ void __launch_bounds__(256) utr_i8_kernel(const float* R, int ldr, int m, int n, const int8_t* U, int ldu,
                                                      int bs, const unsigned* rmax, int sblk, int kspan, double* out) {
+  __shared__ int tile[64 * kTileQ];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int lr = lane & 15, g = lane >> 4;
   const int j = blockIdx.x * 64 + wid * 16 + lr;  // column supplied by this lane
@@ -314,35 +335,45 @@ __global__ void __launch_bounds__(256) utr_i8_kernel(const float* R, int ldr, in
   const int sc = 30 - E < 126 ? (30 - E > -126 ? 30 - E : -126) : 126;  // scale 2^sc, a normal float
   const float fscale = ldexpf(1.0f, sc);
   const bool jok = j < n;
+  // staging role: thread t loads tile rows (k) t / 16 + 16 q, columns 4 (t % 16) .. + 3
+  const int srow = tid >> 4, scol = 4 * (tid & 15), sj = blockIdx.x * 64 + scol;
   v4i acc[NCT][4];
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[ct][t] = (v4i){0, 0, 0, 0};
-  auto load = [&](int k0, float (&xv)[16], v4i (&ua)[NCT]) {
-    const int k = k0 + 16 * g;
+  float4 pre[4];
+  auto fetch = [&](int k0) {
 #pragma unroll
-    for (int t = 0; t < 16; ++t) xv[t] = (jok && k + t < ke) ? R[(size_t)(k + t) * ldr + j] : 0.0f;
+    for (int q = 0; q < 4; ++q) {
+      const int i = k0 + srow + 16 * q;
+      pre[q] = (i < ke && sj < ldr) ? *reinterpret_cast<const float4*>(R + (size_t)i * ldr + sj)
+                                    : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  if (kb < ke) fetch(kb);
+  for (int k0 = kb; k0 < ke; k0 += 64) {
+    __syncthreads();  // the previous chunk's tile is consumed
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {  // columns past n hold R's zero padding (or nothing: zero)
+      int* trow = &tile[(srow + 16 * q) * kTileQ + scol];
+      trow[0] = __float2int_rn(pre[q].x * fscale);
+      trow[1] = __float2int_rn(pre[q].y * fscale);
+      trow[2] = __float2int_rn(pre[q].z * fscale);
+      trow[3] = __float2int_rn(pre[q].w * fscale);
+    }
+    __syncthreads();
+    if (k0 + 64 < ke) fetch(k0 + 64);
+    const int k = k0 + 16 * g;
+    v4i ua[NCT];
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
       const int c = c0 + ct * 16 + lr;
       ua[ct] = (c < bs && k < ke) ? load16(U + (size_t)c * ldu + k) : (v4i){0, 0, 0, 0};
     }
-  };
-  float xn[16];
-  v4i un[NCT];
-  if (kb < ke) load(kb, xn, un);
-  for (int k0 = kb; k0 < ke; k0 += 64) {  // the next chunk loads while this one is converted
-    float xv[16];
-    v4i ua[NCT];
-#pragma unroll
-    for (int t = 0; t < 16; ++t) xv[t] = xn[t];
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) ua[ct] = un[ct];
-    if (k0 + 64 < ke) load(k0 + 64, xn, un);
     int nv[16];
 #pragma unroll
-    for (int t = 0; t < 16; ++t) nv[t] = __float2int_rn(xv[t] * fscale);
+    for (int t = 0; t < 16; ++t) nv[t] = tile[(16 * g + t) * kTileQ + wid * 16 + lr];
     v4i db[4];
     fx_operands(nv, db);
 #pragma unroll
@@ -629,14 +660,18 @@ __global__ void __launch_bounds__(NT) chol_inv_kernel(const double* G, int bs, d
 // 16 x 16 diagonal blocks are factored and inverted by one wave with a row per lane.  Pivots that
 // are not positive give zero rows, as in a plain Cholesky solve.  The matrix is padded to a
 // multiple of 16 with an identity block, which keeps it block diagonal and leaves the real part of
-// the inverse unchanged.  One workgroup of 256 threads; about 4 (nb - 1) + 2 barriers for nb tiles
-// per side.
+// the inverse unchanged.  One workgroup; about 4 (nb - 1) + 2 barriers for nb tiles per side.
 constexpr int kSpdMax = 128;
 __host__ __device__ inline size_t spd_lds_bytes(int bs) {
   const int bp = (bs + 15) & ~15, ld = bp + 1;
   return 8 * ((size_t)bp * ld + (size_t)(bp / 16) * 256 + 16);
 }
-__global__ void __launch_bounds__(256) spd_inv_kernel(const double* G, int bs, double* Gi) {
+// NT threads share the tile products (256 for b <= 64, where four waves cover the few tiles and a
+// small workgroup finds a CU sooner beside the concurrent contraction; 1024 above); wave 0
+// factors the diagonal blocks.
+template <int NT>
+__global__ void __launch_bounds__(NT) spd_inv_kernel(const double* G, int bs, double* Gi) {
+  constexpr int NWV = NT / 64;
   extern __shared__ __align__(16) char smem[];
   const int bp = (bs + 15) & ~15, nb = bp / 16, ld = bp + 1;
   double* A = reinterpret_cast<double*>(smem);  // bp x ld
@@ -652,7 +687,7 @@ __global__ void __launch_bounds__(256) spd_inv_kernel(const double* G, int bs, d
   }
   __syncthreads();
   const double eps = misc[0];
-  for (int x = tid; x < bp * bp; x += 256) {
+  for (int x = tid; x < bp * bp; x += NT) {
     const int i = x / bp, j = x - i * bp;
     double v;
     if (i < bs && j < bs) v = G[(size_t)i * bs + j] + (i == j ? eps : 0.0);
@@ -712,7 +747,7 @@ __global__ void __launch_bounds__(256) spd_inv_kernel(const double* G, int bs, d
     }
     __syncthreads();
     // panel below: L_ip = A_ip D_p^T (in place)
-    for (int i = p + 1 + wid; i < nb; i += 4) {
+    for (int i = p + 1 + wid; i < nb; i += NWV) {
       double* T = at(i, p);
       dbl4 acc = (dbl4){0.0, 0.0, 0.0, 0.0};
 #pragma unroll
@@ -724,7 +759,7 @@ __global__ void __launch_bounds__(256) spd_inv_kernel(const double* G, int bs, d
     __syncthreads();
     // trailing update: A_ij -= L_ip L_jp^T for p < j <= i (tiles numbered row by row)
     const int rem = nb - 1 - p;
-    for (int t = wid; t < rem * (rem + 1) / 2; t += 4) {
+    for (int t = wid; t < rem * (rem + 1) / 2; t += NWV) {
       int ii = 0;
       while ((ii + 1) * (ii + 2) / 2 <= t) ++ii;
       const int jj = t - ii * (ii + 1) / 2;
@@ -746,7 +781,7 @@ __global__ void __launch_bounds__(256) spd_inv_kernel(const double* G, int bs, d
   // ---------------- X = L^-1 by block rows: X_ii = D_i, X_ij = -D_i sum_{k=j}^{i-1} L_ik X_kj.
   // X_ij (i > j) is stored transposed in the free upper block (j, i) of A.
   for (int i = 1; i < nb; ++i) {
-    for (int j = wid; j < i; j += 4) {
+    for (int j = wid; j < i; j += NWV) {
       dbl4 sacc = (dbl4){0.0, 0.0, 0.0, 0.0};
       for (int k = j; k < i; ++k) {
         const double* P = at(i, k);
@@ -768,7 +803,7 @@ __global__ void __launch_bounds__(256) spd_inv_kernel(const double* G, int bs, d
     __syncthreads();
   }
   // ---------------- Gi = X^T X: tile (i, j), i >= j, is sum_{k >= i} X_ki^T X_kj
-  for (int t = wid; t < nb * (nb + 1) / 2; t += 4) {
+  for (int t = wid; t < nb * (nb + 1) / 2; t += NWV) {
     int i = 0;
     while ((i + 1) * (i + 2) / 2 <= t) ++i;
     const int j = t - i * (i + 1) / 2;
@@ -1498,10 +1533,15 @@ static void chol_inverse(const BlockWs& w, const double* G, int bs, hipStream_t 
     static bool attr_set[64] = {};  // once per device: dynamic LDS above 64 KB
     int dev = 0;
     if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < 64 && !attr_set[dev] &&
-        hipFuncSetAttribute((const void*)spd_inv_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+        hipFuncSetAttribute((const void*)spd_inv_kernel<256>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)spd_lds_bytes(kSpdMax)) == hipSuccess &&
+        hipFuncSetAttribute((const void*)spd_inv_kernel<1024>, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)spd_lds_bytes(kSpdMax)) == hipSuccess)
       attr_set[dev] = true;  // a failure shows up as a launch error, checked by the caller
-    hipLaunchKernelGGL(spd_inv_kernel, dim3(1), dim3(256), spd_lds_bytes(bs), st, G, bs, w.Li);
+    if (bs <= 64)
+      hipLaunchKernelGGL(spd_inv_kernel<256>, dim3(1), dim3(256), spd_lds_bytes(bs), st, G, bs, w.Li);
+    else
+      hipLaunchKernelGGL(spd_inv_kernel<1024>, dim3(1), dim3(1024), spd_lds_bytes(bs), st, G, bs, w.Li);
     return;
   }
   const int ne = bs * (bs + 1) / 2;
