@@ -700,52 +700,72 @@ __global__ void __launch_bounds__(NT) spd_inv_kernel(const double* G, int bs, do
   auto opr = [&](const double* t, int tld, int sl) -> double { return t[(size_t)lr * tld + 4 * sl + lk]; };
   // operand "row 4 s + lk, column lr" (B of P Q with Q row-major)
   auto opc = [&](const double* t, int tld, int sl) -> double { return t[(size_t)(4 * sl + lk) * tld + lr]; };
-  // ---------------- Cholesky, one 16-column panel at a time
-  for (int p = 0; p < nb; ++p) {
-    if (wid == 0) {
-      // factor and invert the diagonal block: lane r (mod 16) holds row r
-      const int r = lr;
-      double* T = at(p, p);
-      double a[16], x[16], rk[16];
+  // ---------------- Cholesky, one 16-column panel at a time.  Look-ahead: after the panel of p,
+  // wave 0 updates diagonal block p + 1 first and factors it while the other waves finish the
+  // trailing update, so the serial 16 x 16 factorisation leaves the critical path.
+  // 16 x 16 diagonal block: Cholesky factor and its inverse by wave 0, lane r (mod 16) holding row r
+  auto factor_diag = [&](int p) {  // wave 0
+    const int r = lr;
+    double* T = at(p, p);
+    double a[16], x[16], rk[16];
 #pragma unroll
-      for (int c = 0; c < 16; ++c) a[c] = T[(size_t)r * ld + c];
+    for (int c = 0; c < 16; ++c) a[c] = T[(size_t)r * ld + c];
 #pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const double piv = readlane_f64(a[k], k);
-        const double lkk = piv > 0.0 ? sqrt(piv) : 0.0;
-        const double rr = lkk > 0.0 ? 1.0 / lkk : 0.0;
-        rk[k] = rr;
-        a[k] = r > k ? a[k] * rr : (r == k ? lkk : a[k]);
+    for (int k = 0; k < 16; ++k) {
+      const double piv = readlane_f64(a[k], k);
+      const double lkk = piv > 0.0 ? sqrt(piv) : 0.0;
+      const double rr = lkk > 0.0 ? 1.0 / lkk : 0.0;
+      rk[k] = rr;
+      a[k] = r > k ? a[k] * rr : (r == k ? lkk : a[k]);
 #pragma unroll
-        for (int j = k + 1; j < 16; ++j) {
-          const double ljk = readlane_f64(a[k], j);
-          a[j] = fma(-a[k], ljk, a[j]);  // meaningful for rows r >= j
-        }
-      }
-#pragma unroll
-      for (int c = 0; c < 16; ++c) x[c] = 0.0;
-#pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        // row t of X = L^-1 is finished: x[c] held -sum_{j<t} L_tj X_jc (one scale per lane
-        // instead of a select per entry)
-        const double sc = r == t ? rk[t] : 1.0;
-#pragma unroll
-        for (int c = 0; c < t; ++c) x[c] *= sc;
-        x[t] = r == t ? rk[t] : x[t];
-        // later rows r > t take -L_rt X_tc; the multiplier is zero for rows r <= t
-        const double lrt = r > t ? a[t] : 0.0;
-#pragma unroll
-        for (int c = 0; c <= t; ++c) x[c] = fma(-lrt, readlane_f64(x[c], t), x[c]);
-      }
-      if (lane < 16) {
-#pragma unroll
-        for (int c = 0; c < 16; ++c) {
-          T[(size_t)r * ld + c] = c <= r ? a[c] : 0.0;
-          Dg[p * 256 + r * 16 + c] = c <= r ? x[c] : 0.0;
-        }
+      for (int j = k + 1; j < 16; ++j) {
+        const double ljk = readlane_f64(a[k], j);
+        a[j] = fma(-a[k], ljk, a[j]);  // meaningful for rows r >= j
       }
     }
-    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < 16; ++c) x[c] = 0.0;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      // row t of X = L^-1 is finished: x[c] held -sum_{j<t} L_tj X_jc (one scale per lane
+      // instead of a select per entry)
+      const double sc = r == t ? rk[t] : 1.0;
+#pragma unroll
+      for (int c = 0; c < t; ++c) x[c] *= sc;
+      x[t] = r == t ? rk[t] : x[t];
+      // later rows r > t take -L_rt X_tc; the multiplier is zero for rows r <= t
+      const double lrt = r > t ? a[t] : 0.0;
+#pragma unroll
+      for (int c = 0; c <= t; ++c) x[c] = fma(-lrt, readlane_f64(x[c], t), x[c]);
+    }
+    if (lane < 16) {
+#pragma unroll
+      for (int c = 0; c < 16; ++c) {
+        T[(size_t)r * ld + c] = c <= r ? a[c] : 0.0;
+        Dg[p * 256 + r * 16 + c] = c <= r ? x[c] : 0.0;
+      }
+    }
+  };
+  auto trailing_tile = [&](int p, int t) {  // A_ij -= L_ip L_jp^T, tile t of the p-th update
+    int ii = 0;
+    while ((ii + 1) * (ii + 2) / 2 <= t) ++ii;
+    const int jj = t - ii * (ii + 1) / 2;
+    const int i = p + 1 + ii, j = p + 1 + jj;
+    double* T = at(i, j);
+    const double* Li_ = at(i, p);
+    const double* Lj_ = at(j, p);
+    dbl4 acc;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[q] = T[(size_t)(4 * q + lk) * ld + lr];
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl)
+      acc = __builtin_amdgcn_mfma_f64_16x16x4f64(-opr(Li_, ld, sl), opr(Lj_, ld, sl), acc, 0, 0, 0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) T[(size_t)(4 * q + lk) * ld + lr] = acc[q];
+  };
+  if (wid == 0) factor_diag(0);
+  __syncthreads();
+  for (int p = 0; p < nb; ++p) {
     // panel below: L_ip = A_ip D_p^T (in place)
     for (int i = p + 1 + wid; i < nb; i += NWV) {
       double* T = at(i, p);
@@ -757,24 +777,14 @@ __global__ void __launch_bounds__(NT) spd_inv_kernel(const double* G, int bs, do
       for (int q = 0; q < 4; ++q) T[(size_t)(4 * q + lk) * ld + lr] = acc[q];
     }
     __syncthreads();
-    // trailing update: A_ij -= L_ip L_jp^T for p < j <= i (tiles numbered row by row)
-    const int rem = nb - 1 - p;
-    for (int t = wid; t < rem * (rem + 1) / 2; t += NWV) {
-      int ii = 0;
-      while ((ii + 1) * (ii + 2) / 2 <= t) ++ii;
-      const int jj = t - ii * (ii + 1) / 2;
-      const int i = p + 1 + ii, j = p + 1 + jj;
-      double* T = at(i, j);
-      const double* Li_ = at(i, p);
-      const double* Lj_ = at(j, p);
-      dbl4 acc;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) acc[q] = T[(size_t)(4 * q + lk) * ld + lr];
-#pragma unroll
-      for (int sl = 0; sl < 4; ++sl)
-        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(-opr(Li_, ld, sl), opr(Lj_, ld, sl), acc, 0, 0, 0);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) T[(size_t)(4 * q + lk) * ld + lr] = acc[q];
+    if (p + 1 == nb) break;
+    // trailing update; tile 0 is diagonal block p + 1
+    const int rem = nb - 1 - p, ntile = rem * (rem + 1) / 2;
+    if (wid == 0) {
+      trailing_tile(p, 0);
+      factor_diag(p + 1);
+    } else {
+      for (int t = wid; t < ntile; t += NWV - 1) trailing_tile(p, t);
     }
     __syncthreads();
   }
