@@ -929,27 +929,27 @@ __global__ void __launch_bounds__(256) apply_strip_kernel(const double* __restri
 }
 
 // ---- one workgroup per component row: T[c] = T_tau(fp32(X[c]); h) -----------------------------
-template <bool W>
+template <bool W, int NT>
 // Z0 (nullable): row c of the next split-K contraction's output is cleared here (zlen doubles),
 // which saves that contraction a separate clearing launch.  Md (nullable): Md[c] = T[c] . Yd[c]
 // over the L entries (the last U-step's u_c^T Q_c for the scales), fixed reduction order.
-__global__ void __launch_bounds__(512) select_rows_kernel(const double* X, int L, int ldT, float tau,
+__global__ void __launch_bounds__(NT) select_rows_kernel(const double* X, int L, int ldT, float tau,
                                                           const float* h, int EHm, int8_t* T, double* PHC,
                                                           int* flags, int flag_empty, double* Z0, int zlen,
                                                           const double* Yd, double* Md) {
   __shared__ SelScratchT<W> s;
-  __shared__ double red[8];
+  __shared__ double red[NT / 64];
   const int c = blockIdx.x;
   const double* x = X + (size_t)c * L;
   if (Z0)
-    for (int j = threadIdx.x; j < zlen; j += 512) Z0[(size_t)c * zlen + j] = 0.0;
+    for (int j = threadIdx.x; j < zlen; j += NT) Z0[(size_t)c * zlen + j] = 0.0;
   if (flags[0]) {  // residual is zero: nothing to select
-    for (int j = threadIdx.x; j < ldT; j += 512) T[(size_t)c * ldT + j] = 0;
+    for (int j = threadIdx.x; j < ldT; j += NT) T[(size_t)c * ldT + j] = 0;
     return;
   }
-  const SelResult r = ternary_select<512, W>(x, h, L, tau, EHm, s);
+  const SelResult r = ternary_select<NT, W>(x, h, L, tau, EHm, s);
   double dot = 0.0;
-  for (int j = threadIdx.x; j < ldT; j += 512) {  // the padding [L, ldT) stays zero
+  for (int j = threadIdx.x; j < ldT; j += NT) {  // the padding [L, ldT) stays zero
     const float xv = j < L ? (float)x[j] : 0.0f;
     const int8_t t = selected(xv, r) ? (xv > 0.0f ? (int8_t)1 : (int8_t)-1) : (int8_t)0;
     T[(size_t)c * ldT + j] = t;
@@ -959,8 +959,11 @@ __global__ void __launch_bounds__(512) select_rows_kernel(const double* X, int L
     dot = wave_sum_f64(dot);
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = dot;
     __syncthreads();
-    if (threadIdx.x == 0)
-      Md[c] = ((red[0] + red[1]) + (red[2] + red[3])) + ((red[4] + red[5]) + (red[6] + red[7]));
+    if (threadIdx.x == 0) {
+      double t = 0.0;
+      for (int w = 0; w < NT / 64; ++w) t += red[w];
+      Md[c] = t;
+    }
   }
   if (threadIdx.x == 0) {
     PHC[3 * c + 0] = r.P;
@@ -1600,12 +1603,22 @@ static void solve(const BlockWs& w, int bs, const double* in, double* out, int n
 static void select_rows(const double* X, int L, int ldT, int bs, float tau, const float* h, int EHm, int8_t* T,
                         double* PHC, int* flags, int flag_empty, hipStream_t st, double* Z0 = nullptr,
                         int zlen = 0, const double* Yd = nullptr, double* Md = nullptr) {
+  // long rows take 1024 threads (only bs workgroups run, so the CUs have room)
+  if (L > 4096) {
+    if (h)
+      hipLaunchKernelGGL((select_rows_kernel<true, 1024>), dim3(bs), dim3(1024), 0, st, X, L, ldT, tau, h, EHm, T,
+                         PHC, flags, flag_empty, Z0, zlen, Yd, Md);
+    else
+      hipLaunchKernelGGL((select_rows_kernel<false, 1024>), dim3(bs), dim3(1024), 0, st, X, L, ldT, tau, h, EHm, T,
+                         PHC, flags, flag_empty, Z0, zlen, Yd, Md);
+    return;
+  }
   if (h)
-    hipLaunchKernelGGL(select_rows_kernel<true>, dim3(bs), dim3(512), 0, st, X, L, ldT, tau, h, EHm, T, PHC, flags,
-                       flag_empty, Z0, zlen, Yd, Md);
+    hipLaunchKernelGGL((select_rows_kernel<true, 512>), dim3(bs), dim3(512), 0, st, X, L, ldT, tau, h, EHm, T, PHC,
+                       flags, flag_empty, Z0, zlen, Yd, Md);
   else
-    hipLaunchKernelGGL(select_rows_kernel<false>, dim3(bs), dim3(512), 0, st, X, L, ldT, tau, h, EHm, T, PHC, flags,
-                       flag_empty, Z0, zlen, Yd, Md);
+    hipLaunchKernelGGL((select_rows_kernel<false, 512>), dim3(bs), dim3(512), 0, st, X, L, ldT, tau, h, EHm, T, PHC,
+                       flags, flag_empty, Z0, zlen, Yd, Md);
 }
 
 // Side stream for the Gram and inverse-factor work, which overlaps the residual contraction of
