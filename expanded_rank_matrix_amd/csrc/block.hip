@@ -1038,21 +1038,20 @@ __host__ __device__ inline int scales_window(int bs) {
 }
 __host__ inline size_t scales_lds_bytes(int bs) { return (size_t)16 * scales_window(bs) * bs; }
 
-// ---- scales and energy: one workgroup, thread t owns component t.  The sequential scale of each
-// component against the residual left by the earlier ones of the block:
+// ---- scales and energy: one workgroup; one wave walks, lane l owning components l + 64 s for
+// the NS = ceil(bs / 64) slots s.  The sequential scale of each component against the residual
+// left by the earlier ones of the block:
 //   p_t = Md_t - sum_{c < t} d_c (u_t . u_c) (v_c^T H v_t),   d_t = fp32(p_t / q_t),
 // the subtractions applied in ascending c (as the textbook loop does); the Gram of U is exactly
 // symmetric (integer entries), so row c is read for column c.
 // With target > 0 the energy walk ends at the first component whose energy reaches the target:
 // the later components of the block get d = 0 (not applied, emitted as zero) and the energy of
 // the last kept one.
+template <int NS>
 __global__ void __launch_bounds__(256) scales_kernel(const double* Md, const double* GU, const double* GV, int bs,
                                                      int k0, int T, float* dvec, float* D, double* energy,
                                                      double* st, int* flags, u64* stats, double target) {
 #pragma clang fp contract(off)
-  __shared__ float ds[256];
-  __shared__ double ps[256], qs[256];
-  __shared__ int kept_s;
   const int tid = threadIdx.x;
   if (tid == 0) {
     if (flags[0]) {
@@ -1075,20 +1074,19 @@ __global__ void __launch_bounds__(256) scales_kernel(const double* Md, const dou
     }
     return;
   }
-  const bool own = tid < bs;
-  // One wave walks the recurrence: lane l owns components l, l + 64, l + 128, l + 192 (slots);
-  // component c's value comes to every lane by readlane, so no workgroup barrier per step.  The
-  // rows of GU and GV it reads are staged in LDS by the whole workgroup, `wr` rows at a time, so
-  // that the walk waits on no global load.
+  // Component c's running value comes to every lane by readlane, so no workgroup barrier per
+  // step.  The rows of GU and GV the walk reads are staged in LDS by the whole workgroup, `wr`
+  // rows at a time, so that it waits on no global load.
   extern __shared__ __align__(16) double sg[];  // wr x bs of GU, then wr x bs of GV
   const int wr = scales_window(bs);
   double* sgu = sg;
   double* sgv = sg + (size_t)wr * bs;
-  double acc[4], q[4];
+  const int lane = tid & 63;
+  double acc[NS], q[NS];
   if (tid < 64) {
 #pragma unroll
-    for (int sl = 0; sl < 4; ++sl) {
-      const int c2 = tid + 64 * sl;
+    for (int sl = 0; sl < NS; ++sl) {
+      const int c2 = lane + 64 * sl;
       const bool o = c2 < bs;
       acc[sl] = o ? Md[c2] : 0.0;
       q[sl] = o ? GU[(size_t)c2 * bs + c2] * GV[(size_t)c2 * bs + c2] : 0.0;
@@ -1103,55 +1101,92 @@ __global__ void __launch_bounds__(256) scales_kernel(const double* Md, const dou
     }
     __syncthreads();
     if (tid < 64) {
-      const int lane = tid;
-      for (int c = w0; c < w0 + rows; ++c) {
-        const int sc = c >> 6, lc = c & 63;  // uniform
-        const double a_own = sc == 0 ? acc[0] : (sc == 1 ? acc[1] : (sc == 2 ? acc[2] : acc[3]));
-        const double q_own = sc == 0 ? q[0] : (sc == 1 ? q[1] : (sc == 2 ? q[2] : q[3]));
-        const double ac = readlane_f64(a_own, lc), qc = readlane_f64(q_own, lc);
-        const float d = qc > 0.0 ? (float)(ac / qc) : 0.0f;
-        if (lane == 0) {
-          ds[c] = d;
-          ps[c] = ac;
-          qs[c] = qc;
-        }
-        const double* gur = sgu + (size_t)(c - w0) * bs;
-        const double* gvr = sgv + (size_t)(c - w0) * bs;
 #pragma unroll
-        for (int sl = 0; sl < 4; ++sl) {
-          const int c2 = lane + 64 * sl;
-          if (c2 < bs && c2 > c) acc[sl] -= (double)d * gur[c2] * gvr[c2];
+      for (int sc = 0; sc < NS; ++sc) {  // the slot of the current component, static
+        const int cb = w0 > 64 * sc ? w0 : 64 * sc;
+        const int ce = w0 + rows < 64 * sc + 64 ? w0 + rows : 64 * sc + 64;
+        for (int c = cb; c < ce; ++c) {
+          const double* gur = sgu + (size_t)(c - w0) * bs;
+          const double* gvr = sgv + (size_t)(c - w0) * bs;
+          double gu[NS], gv[NS];
+#pragma unroll
+          for (int sl = sc; sl < NS; ++sl) {  // read before the scale: the reads overlap the division
+            const int c2 = lane + 64 * sl;
+            const int ci = c2 < bs ? c2 : bs - 1;
+            gu[sl] = gur[ci];
+            gv[sl] = gvr[ci];
+          }
+          const double ac = readlane_f64(acc[sc], c & 63), qc = readlane_f64(q[sc], c & 63);
+          const double dd = (double)(qc > 0.0 ? (float)(ac / qc) : 0.0f);
+#pragma unroll
+          for (int sl = sc; sl < NS; ++sl) {
+            const int c2 = lane + 64 * sl;
+            const double t = dd * gu[sl] * gv[sl];
+            acc[sl] = (c2 > c && c2 < bs) ? acc[sl] - t : acc[sl];
+          }
         }
       }
     }
   }
-  __syncthreads();
-  if (tid == 0) {
-    double E = st[0];
-    const double E0 = st[1];
-    int kept = bs;
-    for (int c = 0; c < bs; ++c) {
-      const double dd = (double)ds[c];
-      E = E - (2.0 * dd * ps[c] - dd * dd * qs[c]);
-      const double e = 1.0 - E / E0;
-      energy[k0 + c] = e;
-      if (target > 0.0 && e >= target) {
-        kept = c + 1;
-        for (int c2 = kept; c2 < bs; ++c2) energy[k0 + c2] = e;
-        flags[3] = 1;
-        stats[5] = (u64)(k0 + kept);
-        break;
-      }
-    }
-    st[0] = E;
-    flags[4] = kept;
-    kept_s = kept;
+  if (tid >= 64) return;
+  // acc now holds each component's final p (no later step touches it), so the owner lane forms
+  // its scale again (the same operands, the same value) and the term 2 d p - d^2 q it removes
+  // from the residual energy.  The energy chain E_c = E_{c-1} - term_c runs in ascending c.
+  float dl[NS];
+  double tl[NS], el[NS];
+#pragma unroll
+  for (int sl = 0; sl < NS; ++sl) {
+    dl[sl] = q[sl] > 0.0 ? (float)(acc[sl] / q[sl]) : 0.0f;
+    const double dd = (double)dl[sl];
+    tl[sl] = 2.0 * dd * acc[sl] - dd * dd * q[sl];
+    el[sl] = 0.0;
   }
-  __syncthreads();
-  if (own) {
-    const float d = tid < kept_s ? ds[tid] : 0.0f;
-    dvec[tid] = d;
-    D[k0 + tid] = d;
+  double E = st[0];
+  const double E0 = st[1];
+  // (a lane past bs holds the term +0, which leaves E as it is, so every slot runs 64 steps)
+#pragma unroll
+  for (int sl = 0; sl < NS; ++sl) {
+#pragma unroll 16
+    for (int lc = 0; lc < 64; ++lc) {
+      E = E - readlane_f64(tl[sl], lc);
+      el[sl] = lane == lc ? E : el[sl];
+    }
+  }
+  // energies and the first component that reaches the target
+  int first = bs;
+  double en[NS];
+#pragma unroll
+  for (int sl = NS - 1; sl >= 0; --sl) {
+    en[sl] = 1.0 - el[sl] / E0;
+    const u64 hit = __ballot(target > 0.0 && lane + 64 * sl < bs && en[sl] >= target);
+    if (hit) first = 64 * sl + __ffsll((unsigned long long)hit) - 1;
+  }
+  const int kept = first < bs ? first + 1 : bs;
+  const int ks = (kept - 1) >> 6, kl = (kept - 1) & 63;
+  double e_last = 0.0, E_last = 0.0;
+#pragma unroll
+  for (int sl = 0; sl < NS; ++sl)
+    if (sl == ks) {
+      e_last = readlane_f64(en[sl], kl);
+      E_last = readlane_f64(el[sl], kl);
+    }
+#pragma unroll
+  for (int sl = 0; sl < NS; ++sl) {
+    const int c = lane + 64 * sl;
+    if (c < bs) {
+      energy[k0 + c] = c < kept ? en[sl] : e_last;
+      const float d = c < kept ? dl[sl] : 0.0f;
+      dvec[c] = d;
+      D[k0 + c] = d;
+    }
+  }
+  if (lane == 0) {
+    if (first < bs) {
+      flags[3] = 1;
+      stats[5] = (u64)(k0 + kept);
+    }
+    st[0] = E_last;
+    flags[4] = kept;
   }
 }
 
@@ -1654,9 +1689,12 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops, double
     if (ea != hipSuccess) return ea;
     if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
     if (!scales_attr[dev]) {
-      ea = hipFuncSetAttribute((const void*)scales_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                               (int)(96 * 1024));
-      if (ea != hipSuccess) return ea;
+      const void* kernels[4] = {(const void*)scales_kernel<1>, (const void*)scales_kernel<2>,
+                                (const void*)scales_kernel<3>, (const void*)scales_kernel<4>};
+      for (const void* kf : kernels) {
+        ea = hipFuncSetAttribute(kf, hipFuncAttributeMaxDynamicSharedMemorySize, (int)(96 * 1024));
+        if (ea != hipSuccess) return ea;
+      }
       scales_attr[dev] = true;
     }
   }
@@ -1744,8 +1782,11 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops, double
     }
     // scales against Q = R H V of the last U-step, then the update and the outputs
     gram_product(w, w.Ut, m, w.ldu, nullptr, 0, bs, w.GU, st);  // Md came with the last selection
-    hipLaunchKernelGGL(scales_kernel, dim3(1), dim3(256), scales_lds_bytes(bs), st, w.Md, w.GU, w.GV, bs, k0, L.T,
-                       w.d, L.D, L.energy, w.st, w.flags, L.stats, target);
+    {
+      auto kern = bs <= 64 ? scales_kernel<1> : bs <= 128 ? scales_kernel<2> : bs <= 192 ? scales_kernel<3> : scales_kernel<4>;
+      hipLaunchKernelGGL(kern, dim3(1), dim3(256), scales_lds_bytes(bs), st, w.Md, w.GU, w.GV, bs, k0, L.T, w.d, L.D,
+                         L.energy, w.st, w.flags, L.stats, target);
+    }
     if (addback) {  // keep the better of the refit and the old block
       hipLaunchKernelGGL(refit_choose_kernel, dim3(1), dim3(256), 0, st, w.ppo, w.GUo, w.GVo, w.dold, k0, bs, w.d,
                          L.D, L.energy, w.st, w.flags, L.stats);
