@@ -213,6 +213,11 @@ __device__ __forceinline__ void fx_operands(const int (&nv)[16], v4i (&op)[4]) {
 
 __device__ __forceinline__ v4i load16(const int8_t* p) { return *reinterpret_cast<const v4i*>(p); }
 
+// (G + eps I)^-1 by one workgroup of NT threads over `smem` (spd_lds_bytes(bs) bytes); below.
+template <int NT>
+__device__ __forceinline__ void spd_inv_body(const double* G, int bs, double* Gi, char* smem);
+__host__ __device__ inline size_t spd_lds_bytes(int bs);
+
 // The residual tile of each 64-wide k chunk is loaded by the whole workgroup as float4 rows
 // (256 contiguous bytes per tile row: full cache lines), converted to its fixed-point image
 // once, and staged in LDS; each lane then reads its 16 values of the MFMA layout from there.  The
@@ -223,10 +228,16 @@ constexpr int kTileQ = 65;  // int32 pitch of a [64 k][64 cols] tile (column rea
 // out[c][i] (+)= sum_{k in this split} x_ik T[c][k], x_ik = R[i][k] (h_k): rows of R x components.
 // Workgroup: 64 rows (16 per wave) x 16 NCT components (blockIdx.y), K range blockIdx.z.
 template <int NCT>
-__global__ void __launch_bounds__(256) rv_i8_kernel(const float* R, int ldr, int rows, int K, const int8_t* T,
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) rv_i8_kernel(const float* R, int ldr, int rows, int K, const int8_t* T,
                                                     int ldt, const float* h, int ehm, int bs, const unsigned* rmax,
-                                                    int sblk, int kspan, double* out) {
-  __shared__ __align__(16) int tile[64 * kTileP];
+                                                    int sblk, int kspan, double* out, const double* spdG,
+                                                    double* spdGi) {
+  extern __shared__ __align__(16) char dsm[];
+  if (spdG && blockIdx.x == gridDim.x - 1) {  // the extra column of workgroups: one inverts spdG
+    if (blockIdx.y == 0 && blockIdx.z == 0) spd_inv_body<256>(spdG, bs, spdGi, dsm);
+    return;
+  }
+  int* tile = reinterpret_cast<int*>(dsm);  // 64 x kTileP
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int lr = lane & 15, g = lane >> 4;
   const int c0 = blockIdx.y * 16 * NCT;
@@ -323,9 +334,15 @@ __global__ void __launch_bounds__(256) rv_i8_kernel(const float* R, int ldr, int
 // out[c][j] (+)= sum_{i in this split} U[c][i] R[i][j]: components x columns of R.
 // Workgroup: 64 columns (16 per wave) x 16 NCT components (blockIdx.y), K = m range blockIdx.z.
 template <int NCT>
-__global__ void __launch_bounds__(256) utr_i8_kernel(const float* R, int ldr, int m, int n, const int8_t* U, int ldu,
-                                                     int bs, const unsigned* rmax, int sblk, int kspan, double* out) {
-  __shared__ int tile[64 * kTileQ];
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) utr_i8_kernel(const float* R, int ldr, int m, int n, const int8_t* U, int ldu,
+                                                     int bs, const unsigned* rmax, int sblk, int kspan, double* out,
+                                                     const double* spdG, double* spdGi) {
+  extern __shared__ __align__(16) char dsm[];
+  if (spdG && blockIdx.x == gridDim.x - 1) {  // the extra column of workgroups: one inverts spdG
+    if (blockIdx.y == 0 && blockIdx.z == 0) spd_inv_body<256>(spdG, bs, spdGi, dsm);
+    return;
+  }
+  int* tile = reinterpret_cast<int*>(dsm);  // 64 x kTileQ
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int lr = lane & 15, g = lane >> 4;
   const int j = blockIdx.x * 64 + wid * 16 + lr;  // column supplied by this lane
@@ -662,6 +679,7 @@ __global__ void __launch_bounds__(NT) chol_inv_kernel(const double* G, int bs, d
 // multiple of 16 with an identity block, which keeps it block diagonal and leaves the real part of
 // the inverse unchanged.  One workgroup; about 4 (nb - 1) + 2 barriers for nb tiles per side.
 constexpr int kSpdMax = 128;
+constexpr int kSpdFused = 64;  // largest b whose inverse runs inside the contraction launch
 __host__ __device__ inline size_t spd_lds_bytes(int bs) {
   const int bp = (bs + 15) & ~15, ld = bp + 1;
   return 8 * ((size_t)bp * ld + (size_t)(bp / 16) * 256 + 16);
@@ -669,10 +687,11 @@ __host__ __device__ inline size_t spd_lds_bytes(int bs) {
 // NT threads share the tile products (256 for b <= 64, where four waves cover the few tiles and a
 // small workgroup finds a CU sooner beside the concurrent contraction; 1024 above); wave 0
 // factors the diagonal blocks.
+// The body runs in its own launch (spd_inv_kernel) or as one extra workgroup of a residual
+// contraction (rv_i8_kernel, utr_i8_kernel), which overlaps the two without a second stream.
 template <int NT>
-__global__ void __launch_bounds__(NT) spd_inv_kernel(const double* G, int bs, double* Gi) {
+__device__ __forceinline__ void spd_inv_body(const double* G, int bs, double* Gi, char* smem) {
   constexpr int NWV = NT / 64;
-  extern __shared__ __align__(16) char smem[];
   const int bp = (bs + 15) & ~15, nb = bp / 16, ld = bp + 1;
   double* A = reinterpret_cast<double*>(smem);  // bp x ld
   double* Dg = A + (size_t)bp * ld;             // nb diagonal-block inverses, 16 x 16 row-major
@@ -836,6 +855,12 @@ __global__ void __launch_bounds__(NT) spd_inv_kernel(const double* G, int bs, do
       }
     }
   }
+}
+
+template <int NT>
+__global__ void __launch_bounds__(NT) spd_inv_kernel(const double* G, int bs, double* Gi) {
+  extern __shared__ __align__(16) char smem[];
+  spd_inv_body<NT>(G, bs, Gi, smem);
 }
 
 // ---- out (bs x ncols) = op(A) B with A bs x bs (op: A or A^T), B bs x ncols, fp64 MFMA, K = bs.
@@ -1526,22 +1551,26 @@ static bool utr_splits(const BlockLaunch& L, int bs) {
 }
 
 static void rw_product(const BlockLaunch& L, const BlockWs& w, const float* h, int bs, int sblk, double* outT,
-                       hipStream_t st, bool prezeroed = false) {
+                       hipStream_t st, bool prezeroed = false, const double* spdG = nullptr,
+                       double* spdGi = nullptr) {
   const int nct = bs <= 16 ? 1 : (bs <= 32 ? 2 : 4);  // 8 tiles: one wave per SIMD, slower
   const int gx = (L.m + 63) / 64, gy = (bs + 16 * nct - 1) / (16 * nct);
   int kspan = 0;
   const int gz = i8_splits(gx * gy, L.n, &kspan);
   if (gz > 1 && !prezeroed) zero_fill(outT, (long long)bs * L.m, st);
-  const dim3 grid(gx, gy, gz);
+  // with spdG, one more column of workgroups, one of which inverts spdG
+  const dim3 grid(gx + (spdG ? 1 : 0), gy, gz);
+  size_t lds = (size_t)4 * 64 * kTileP;
+  if (spdG && spd_lds_bytes(bs) > lds) lds = spd_lds_bytes(bs);
   if (nct == 1)
-    hipLaunchKernelGGL(rv_i8_kernel<1>, grid, dim3(256), 0, st, L.R, L.ldr, L.m, L.n, w.Vt, w.ldv, h, L.EHm, bs,
-                       w.rmax, sblk, kspan, outT);
+    hipLaunchKernelGGL(rv_i8_kernel<1>, grid, dim3(256), lds, st, L.R, L.ldr, L.m, L.n, w.Vt, w.ldv, h, L.EHm, bs,
+                       w.rmax, sblk, kspan, outT, spdG, spdGi);
   else if (nct == 2)
-    hipLaunchKernelGGL(rv_i8_kernel<2>, grid, dim3(256), 0, st, L.R, L.ldr, L.m, L.n, w.Vt, w.ldv, h, L.EHm, bs,
-                       w.rmax, sblk, kspan, outT);
+    hipLaunchKernelGGL(rv_i8_kernel<2>, grid, dim3(256), lds, st, L.R, L.ldr, L.m, L.n, w.Vt, w.ldv, h, L.EHm, bs,
+                       w.rmax, sblk, kspan, outT, spdG, spdGi);
   else
-    hipLaunchKernelGGL(rv_i8_kernel<4>, grid, dim3(256), 0, st, L.R, L.ldr, L.m, L.n, w.Vt, w.ldv, h, L.EHm, bs,
-                       w.rmax, sblk, kspan, outT);
+    hipLaunchKernelGGL(rv_i8_kernel<4>, grid, dim3(256), lds, st, L.R, L.ldr, L.m, L.n, w.Vt, w.ldv, h, L.EHm, bs,
+                       w.rmax, sblk, kspan, outT, spdG, spdGi);
 }
 
 // G (bs x bs) = T diag(w) T^T for ternary rows T (bs x len, ld ldt); integer-exact without weights
@@ -1557,22 +1586,25 @@ static void gram_product(const BlockWs& w, const int8_t* T, int len, int ldt, co
 
 // X (bs x n) = U^T R, on int8 MFMA with R in fixed point
 static void utr_product(const BlockLaunch& L, const BlockWs& w, int bs, int sblk, hipStream_t st,
-                        bool prezeroed = false) {
+                        bool prezeroed = false, const double* spdG = nullptr, double* spdGi = nullptr) {
   const int nct = bs <= 16 ? 1 : (bs <= 32 ? 2 : 4);  // 8 tiles: one wave per SIMD, slower
   const int gx = (L.n + 63) / 64, gy = (bs + 16 * nct - 1) / (16 * nct);
   int kspan = 0;
   const int gz = i8_splits(gx * gy, L.m, &kspan);
   if (gz > 1 && !prezeroed) zero_fill(w.X, (long long)bs * L.n, st);
-  const dim3 grid(gx, gy, gz);
+  // with spdG, one more column of workgroups, one of which inverts spdG
+  const dim3 grid(gx + (spdG ? 1 : 0), gy, gz);
+  size_t lds = (size_t)4 * 64 * kTileQ;
+  if (spdG && spd_lds_bytes(bs) > lds) lds = spd_lds_bytes(bs);
   if (nct == 1)
-    hipLaunchKernelGGL(utr_i8_kernel<1>, grid, dim3(256), 0, st, L.R, L.ldr, L.m, L.n, w.Ut, w.ldu, bs, w.rmax,
-                       sblk, kspan, w.X);
+    hipLaunchKernelGGL(utr_i8_kernel<1>, grid, dim3(256), lds, st, L.R, L.ldr, L.m, L.n, w.Ut, w.ldu, bs, w.rmax,
+                       sblk, kspan, w.X, spdG, spdGi);
   else if (nct == 2)
-    hipLaunchKernelGGL(utr_i8_kernel<2>, grid, dim3(256), 0, st, L.R, L.ldr, L.m, L.n, w.Ut, w.ldu, bs, w.rmax,
-                       sblk, kspan, w.X);
+    hipLaunchKernelGGL(utr_i8_kernel<2>, grid, dim3(256), lds, st, L.R, L.ldr, L.m, L.n, w.Ut, w.ldu, bs, w.rmax,
+                       sblk, kspan, w.X, spdG, spdGi);
   else
-    hipLaunchKernelGGL(utr_i8_kernel<4>, grid, dim3(256), 0, st, L.R, L.ldr, L.m, L.n, w.Ut, w.ldu, bs, w.rmax,
-                       sblk, kspan, w.X);
+    hipLaunchKernelGGL(utr_i8_kernel<4>, grid, dim3(256), lds, st, L.R, L.ldr, L.m, L.n, w.Ut, w.ldu, bs, w.rmax,
+                       sblk, kspan, w.X, spdG, spdGi);
 }
 
 // Li = (G + eps I)^-1 for bs <= kSpdMax, else Li = L^-1 for L L^T = G + eps I
@@ -1739,6 +1771,7 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops, double
   auto als_fit = [&](int sblk, int bs, int k0, double target, bool addback) -> hipError_t {
     hipError_t r;
     const bool xz = utr_splits(L, bs), yz = rw_splits(L, bs);
+    const bool fused = bs <= kSpdFused;
     for (int t = 0; t < L.T; ++t) {
       double* x0 = (xz && t + 1 < L.T) ? w.X : nullptr;  // for the next V-step
       double* y0 = yz ? w.Yt : nullptr;                  // for this U-step
@@ -1759,10 +1792,16 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops, double
         by += 2.0 * rbytes;
         continue;
       }
-      // V-step: G = (U^T U + eps I)^-1 U^T R, rows ternarized with weights h
-      if ((r = gram_inverse(w.Ut, m, w.ldu, nullptr, bs, w.GU)) != hipSuccess) return r;
-      utr_product(L, w, bs, sblk, st, true);
-      if ((r = join()) != hipSuccess) return r;
+      // V-step: G = (U^T U + eps I)^-1 U^T R, rows ternarized with weights h.  For b <= 64 the
+      // inverse runs inside the contraction's launch; above, on the side stream beside it.
+      if (fused) {
+        gram_product(w, w.Ut, m, w.ldu, nullptr, 0, bs, w.GU, st);
+        utr_product(L, w, bs, sblk, st, true, w.GU, w.Li);
+      } else {
+        if ((r = gram_inverse(w.Ut, m, w.ldu, nullptr, bs, w.GU)) != hipSuccess) return r;
+        utr_product(L, w, bs, sblk, st, true);
+        if ((r = join()) != hipSuccess) return r;
+      }
       if (addback && t == 0) {
         hipLaunchKernelGGL(addback_dot_kernel, dim3(bs), dim3(256), 0, st, w.X, n, w.Vt, w.ldv, L.h, w.ppo);
         hipLaunchKernelGGL(addback_energy_kernel, dim3(1), dim3(256), 0, st, w.ppo, w.GU, w.GVo, L.D, k0, bs, w.st,
@@ -1771,9 +1810,14 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops, double
       solve(w, bs, w.X, w.Z, n, st);
       select_rows(w.Z, n, w.ldv, bs, L.tau, hsel, ehsel, w.Vt, w.PHC, w.flags, 0, st, y0, m);
       // U-step: F^T = (V^T H V + eps I)^-1 (R H V)^T, columns ternarized without weights
-      if ((r = gram_inverse(w.Vt, n, w.ldv, L.h, bs, w.GV)) != hipSuccess) return r;
-      rw_product(L, w, L.h, bs, sblk, w.Yt, st, true);
-      if ((r = join()) != hipSuccess) return r;
+      if (fused) {
+        gram_product(w, w.Vt, n, w.ldv, L.h, L.EHm, bs, w.GV, st);
+        rw_product(L, w, L.h, bs, sblk, w.Yt, st, true, w.GV, w.Li);
+      } else {
+        if ((r = gram_inverse(w.Vt, n, w.ldv, L.h, bs, w.GV)) != hipSuccess) return r;
+        rw_product(L, w, L.h, bs, sblk, w.Yt, st, true);
+        if ((r = join()) != hipSuccess) return r;
+      }
       solve(w, bs, w.Yt, w.Ft, m, st);
       select_rows(w.Ft, m, w.ldu, bs, L.tau, nullptr, 0, w.Ut, w.PHC, w.flags, 0, st, x0, n,
                   t + 1 == L.T ? w.Yt : nullptr, t + 1 == L.T ? w.Md : nullptr);
