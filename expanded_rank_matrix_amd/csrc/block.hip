@@ -1688,30 +1688,6 @@ static void select_rows(const double* X, int L, int ldT, int bs, float tau, cons
                        flags, flag_empty, Z0, zlen, Yd, Md);
 }
 
-// Side stream for the Gram and inverse-factor work, which overlaps the residual contraction of
-// the same half-step (both depend only on the ternary factor just selected).  Created once per
-// device at the default priority.
-struct SideStream {
-  hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-};
-
-static hipError_t side_stream(SideStream** out) {
-  static SideStream per_dev[64];
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  SideStream& ss = per_dev[dev];
-  if (!ss.s) {
-    if ((e = hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking)) != hipSuccess) return e;
-    if ((e = hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming)) != hipSuccess) return e;
-    if ((e = hipEventCreateWithFlags(&ss.join, hipEventDisableTiming)) != hipSuccess) return e;
-  }
-  *out = &ss;
-  return hipSuccess;
-}
-
 hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops, double* bytes) {
   if (L.b > 256) return hipErrorInvalidValue;
   {
@@ -1732,20 +1708,7 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops, double
   }
   const BlockWs w = carve(L.ws, L.m, L.n, L.b);
   const int m = L.m, n = L.n;
-  SideStream* ss = nullptr;
-  hipError_t e = side_stream(&ss);
-  if (e != hipSuccess) return e;
-  // G (on st: a short kernel that would otherwise wait for CUs behind the contraction), then its
-  // inverse on the side stream, concurrently with the residual contraction queued next on st
-  auto gram_inverse = [&](const int8_t* T, int len, int ldt, const float* wt, int bs, double* G) -> hipError_t {
-    hipError_t r;
-    gram_product(w, T, len, ldt, wt, L.EHm, bs, G, st);
-    if ((r = hipEventRecord(ss->fork, st)) != hipSuccess) return r;
-    if ((r = hipStreamWaitEvent(ss->s, ss->fork, 0)) != hipSuccess) return r;
-    chol_inverse(w, G, bs, ss->s);
-    return hipEventRecord(ss->join, ss->s);
-  };
-  auto join = [&]() -> hipError_t { return hipStreamWaitEvent(st, ss->join, 0); };
+  hipError_t e = hipSuccess;
   hipLaunchKernelGGL(block_init_kernel, dim3(1), dim3(256), 0, st, L.rowE, m, w.st, w.flags, w.rmax);
   {
     const long long nb = ((long long)m * n + 255) / 256;
@@ -1769,7 +1732,6 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops, double
   // Split-K outputs are cleared by the kernel before their contraction: X by the selection of U
   // (or the sketch's, or the refit's load), Yt by the selection of V (or the sketch's Omega).
   auto als_fit = [&](int sblk, int bs, int k0, double target, bool addback) -> hipError_t {
-    hipError_t r;
     const bool xz = utr_splits(L, bs), yz = rw_splits(L, bs);
     const bool fused = bs <= kSpdFused;
     for (int t = 0; t < L.T; ++t) {
@@ -1793,14 +1755,15 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops, double
         continue;
       }
       // V-step: G = (U^T U + eps I)^-1 U^T R, rows ternarized with weights h.  For b <= 64 the
-      // inverse runs inside the contraction's launch; above, on the side stream beside it.
+      // inverse runs inside the contraction's launch; above, before it on the same stream (beside
+      // a contraction on a second stream it ran ~1.6x slower, and the events cost more again).
       if (fused) {
         gram_product(w, w.Ut, m, w.ldu, nullptr, 0, bs, w.GU, st);
         utr_product(L, w, bs, sblk, st, true, w.GU, w.Li);
       } else {
-        if ((r = gram_inverse(w.Ut, m, w.ldu, nullptr, bs, w.GU)) != hipSuccess) return r;
+        gram_product(w, w.Ut, m, w.ldu, nullptr, 0, bs, w.GU, st);
+        chol_inverse(w, w.GU, bs, st);
         utr_product(L, w, bs, sblk, st, true);
-        if ((r = join()) != hipSuccess) return r;
       }
       if (addback && t == 0) {
         hipLaunchKernelGGL(addback_dot_kernel, dim3(bs), dim3(256), 0, st, w.X, n, w.Vt, w.ldv, L.h, w.ppo);
@@ -1814,9 +1777,9 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops, double
         gram_product(w, w.Vt, n, w.ldv, L.h, L.EHm, bs, w.GV, st);
         rw_product(L, w, L.h, bs, sblk, w.Yt, st, true, w.GV, w.Li);
       } else {
-        if ((r = gram_inverse(w.Vt, n, w.ldv, L.h, bs, w.GV)) != hipSuccess) return r;
+        gram_product(w, w.Vt, n, w.ldv, L.h, L.EHm, bs, w.GV, st);
+        chol_inverse(w, w.GV, bs, st);
         rw_product(L, w, L.h, bs, sblk, w.Yt, st, true);
-        if ((r = join()) != hipSuccess) return r;
       }
       solve(w, bs, w.Yt, w.Ft, m, st);
       select_rows(w.Ft, m, w.ldu, bs, L.tau, nullptr, 0, w.Ut, w.PHC, w.flags, 0, st, x0, n,
