@@ -706,12 +706,19 @@ __device__ __forceinline__ void spd_inv_body(const double* G, int bs, double* Gi
   }
   __syncthreads();
   const double eps = misc[0];
-  for (int x = tid; x < bp * bp; x += NT) {
-    const int i = x / bp, j = x - i * bp;
-    double v;
-    if (i < bs && j < bs) v = G[(size_t)i * bs + j] + (i == j ? eps : 0.0);
-    else v = i == j ? 1.0 : 0.0;
-    A[(size_t)i * ld + j] = v;
+  for (int x0 = 0; x0 < bp * bp; x0 += 8 * NT) {  // 8 loads in flight per thread, then the stores
+    double v8[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int x = x0 + tid + NT * q, i = x / bp, j = x - i * bp;
+      if (x < bp * bp && i < bs && j < bs) v8[q] = G[(size_t)i * bs + j] + (i == j ? eps : 0.0);
+      else v8[q] = i == j ? 1.0 : 0.0;
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int x = x0 + tid + NT * q, i = x / bp, j = x - i * bp;
+      if (x < bp * bp) A[(size_t)i * ld + j] = v8[q];
+    }
   }
   __syncthreads();
   auto at = [&](int bi, int bj) -> double* { return A + (size_t)(16 * bi) * ld + 16 * bj; };
@@ -898,46 +905,51 @@ __global__ void __launch_bounds__(256) apply_kernel(const double* __restrict__ A
 
 // ---- out (bs x ncols) = A B for bs <= kSpdMax (A bs x bs, B bs x ncols), fp64 MFMA, K = bs.
 // Workgroup: one 16-column strip of B (staged in LDS) x all bs rows; wave w takes the row tiles
-// w, w + 4, ...  Loads of A run 8 k-steps ahead of the MFMAs.
-template <int NRW>
+// w, w + 4, ...  Every A operand of the whole K range (NKS k-steps of 4) is loaded into registers
+// before the strip is staged, so the workgroup waits for one round of loads, then runs its MFMAs
+// back to back.
+template <int NRW, int NKS>
 __global__ void __launch_bounds__(256) apply_strip_kernel(const double* __restrict__ A, int bs, const double* Bm,
                                                           double* out, int ncols) {
   __shared__ double Bs[kSpdMax][16];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int lr = lane & 15, lk = lane >> 4;
   const int col0 = blockIdx.x * 16;
-  for (int x = tid; x < bs * 16; x += 256) {
-    const int k = x >> 4, c = x & 15;
-    Bs[k][c] = col0 + c < ncols ? Bm[(size_t)k * ncols + col0 + c] : 0.0;
-  }
-  __syncthreads();
   const int ntiles = (bs + 15) / 16;
   dbl4 acc[NRW];
-  const double* ap[NRW];
-  bool rok[NRW];
+  double av[NKS][NRW];
 #pragma unroll
   for (int u = 0; u < NRW; ++u) {
     acc[u] = (dbl4){0.0, 0.0, 0.0, 0.0};
     const int r = (wid + 4 * u) * 16 + lr;
-    rok[u] = wid + 4 * u < ntiles && r < bs;
-    ap[u] = A + (size_t)(rok[u] ? r : 0) * bs;
+    const bool rok = wid + 4 * u < ntiles && r < bs;
+    const double* ap = A + (size_t)(rok ? r : 0) * bs;
+#pragma unroll
+    for (int st = 0; st < NKS; ++st) {
+      const int k = 4 * st + lk;
+      av[st][u] = (rok && k < bs) ? ap[k] : 0.0;
+    }
   }
-  constexpr int kAhead = 8;  // k-steps of 4 whose A operands are loaded together
-  for (int k0 = 0; k0 < bs; k0 += 4 * kAhead) {
-    double av[kAhead][NRW];
+  // the strip: (4 NKS) x 16 values, NKS / 4 per thread, all loads issued before the first store
+  constexpr int NB = NKS / 4;
+  double bl[NB];
 #pragma unroll
-    for (int st = 0; st < kAhead; ++st) {
-      const int k = k0 + 4 * st + lk;
+  for (int i = 0; i < NB; ++i) {
+    const int x = tid + 256 * i, k = x >> 4, c = x & 15;
+    bl[i] = (k < bs && col0 + c < ncols) ? Bm[(size_t)k * ncols + col0 + c] : 0.0;
+  }
 #pragma unroll
-      for (int u = 0; u < NRW; ++u) av[st][u] = (rok[u] && k < bs) ? ap[u][k] : 0.0;
-    }
+  for (int i = 0; i < NB; ++i) {
+    const int x = tid + 256 * i;
+    Bs[x >> 4][x & 15] = bl[i];
+  }
+  __syncthreads();
 #pragma unroll
-    for (int st = 0; st < kAhead; ++st) {
-      const int k = k0 + 4 * st + lk;
-      const double bv = k < bs ? Bs[k][lr] : 0.0;
+  for (int st = 0; st < NKS; ++st) {
+    const int k = 4 * st + lk;
+    const double bv = k < bs ? Bs[k][lr] : 0.0;
 #pragma unroll
-      for (int u = 0; u < NRW; ++u) acc[u] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[st][u], bv, acc[u], 0, 0, 0);
-    }
+    for (int u = 0; u < NRW; ++u) acc[u] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[st][u], bv, acc[u], 0, 0, 0);
   }
   const int col = col0 + lr;
   if (col < ncols) {
@@ -1120,9 +1132,23 @@ __global__ void __launch_bounds__(256) scales_kernel(const double* Md, const dou
   for (int w0 = 0; w0 < bs; w0 += wr) {
     const int rows = bs - w0 < wr ? bs - w0 : wr;
     __syncthreads();  // the previous window is consumed
-    for (int x = tid; x < rows * bs; x += 256) {
-      sgu[x] = GU[(size_t)w0 * bs + x];
-      sgv[x] = GV[(size_t)w0 * bs + x];
+    const int tot = rows * bs;
+    for (int x0 = 0; x0 < tot; x0 += 8 * 256) {  // 16 loads in flight per thread, then the stores
+      double u8[8], v8[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int x = x0 + tid + 256 * q;
+        u8[q] = x < tot ? GU[(size_t)w0 * bs + x] : 0.0;
+        v8[q] = x < tot ? GV[(size_t)w0 * bs + x] : 0.0;
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int x = x0 + tid + 256 * q;
+        if (x < tot) {
+          sgu[x] = u8[q];
+          sgv[x] = v8[q];
+        }
+      }
     }
     __syncthreads();
     if (tid < 64) {
@@ -1658,9 +1684,9 @@ static void solve(const BlockWs& w, int bs, const double* in, double* out, int n
   if (bs <= kSpdMax) {
     const dim3 grid((ncols + 15) / 16);
     if (bs <= 64)
-      hipLaunchKernelGGL(apply_strip_kernel<1>, grid, dim3(256), 0, st, w.Li, bs, in, out, ncols);
+      hipLaunchKernelGGL((apply_strip_kernel<1, 16>), grid, dim3(256), 0, st, w.Li, bs, in, out, ncols);
     else
-      hipLaunchKernelGGL(apply_strip_kernel<2>, grid, dim3(256), 0, st, w.Li, bs, in, out, ncols);
+      hipLaunchKernelGGL((apply_strip_kernel<2, 32>), grid, dim3(256), 0, st, w.Li, bs, in, out, ncols);
     return;
   }
   apply<false>(w.Li, bs, in, w.Tmp, ncols, st);
