@@ -904,23 +904,24 @@ __global__ void __launch_bounds__(256) apply_kernel(const double* __restrict__ A
 }
 
 // ---- out (bs x ncols) = A B for bs <= kSpdMax (A bs x bs, B bs x ncols), fp64 MFMA, K = bs.
-// Workgroup: one 16-column strip of B (staged in LDS) x all bs rows; wave w takes the row tiles
+// Workgroup: NCT 16-column strips of B (staged in LDS) x all bs rows; wave w takes the row tiles
 // w, w + 4, ...  Every A operand of the whole K range (NKS k-steps of 4) is loaded into registers
-// before the strip is staged, so the workgroup waits for one round of loads, then runs its MFMAs
-// back to back.
-template <int NRW, int NKS>
+// before the strips are staged, so the workgroup waits for one round of loads, then runs its MFMAs
+// back to back, each A operand serving the NCT strips.
+template <int NRW, int NKS, int NCT>
 __global__ void __launch_bounds__(256) apply_strip_kernel(const double* __restrict__ A, int bs, const double* Bm,
                                                           double* out, int ncols) {
-  __shared__ double Bs[kSpdMax][16];
+  __shared__ double Bs[kSpdMax][16 * NCT];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int lr = lane & 15, lk = lane >> 4;
-  const int col0 = blockIdx.x * 16;
+  const int col0 = blockIdx.x * 16 * NCT;
   const int ntiles = (bs + 15) / 16;
-  dbl4 acc[NRW];
+  dbl4 acc[NRW][NCT];
   double av[NKS][NRW];
 #pragma unroll
   for (int u = 0; u < NRW; ++u) {
-    acc[u] = (dbl4){0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) acc[u][ct] = (dbl4){0.0, 0.0, 0.0, 0.0};
     const int r = (wid + 4 * u) * 16 + lr;
     const bool rok = wid + 4 * u < ntiles && r < bs;
     const double* ap = A + (size_t)(rok ? r : 0) * bs;
@@ -930,36 +931,43 @@ __global__ void __launch_bounds__(256) apply_strip_kernel(const double* __restri
       av[st][u] = (rok && k < bs) ? ap[k] : 0.0;
     }
   }
-  // the strip: (4 NKS) x 16 values, NKS / 4 per thread, all loads issued before the first store
-  constexpr int NB = NKS / 4;
+  // the strips: (4 NKS) x 16 NCT values, NKS NCT / 4 per thread, all loads issued before the
+  // first store
+  constexpr int NB = NKS * NCT / 4, W = 16 * NCT;
   double bl[NB];
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
-    const int x = tid + 256 * i, k = x >> 4, c = x & 15;
+    const int x = tid + 256 * i, k = x / W, c = x % W;
     bl[i] = (k < bs && col0 + c < ncols) ? Bm[(size_t)k * ncols + col0 + c] : 0.0;
   }
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
     const int x = tid + 256 * i;
-    Bs[x >> 4][x & 15] = bl[i];
+    Bs[x / W][x % W] = bl[i];
   }
   __syncthreads();
 #pragma unroll
   for (int st = 0; st < NKS; ++st) {
     const int k = 4 * st + lk;
-    const double bv = k < bs ? Bs[k][lr] : 0.0;
 #pragma unroll
-    for (int u = 0; u < NRW; ++u) acc[u] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[st][u], bv, acc[u], 0, 0, 0);
+    for (int ct = 0; ct < NCT; ++ct) {
+      const double bv = k < bs ? Bs[k][16 * ct + lr] : 0.0;
+#pragma unroll
+      for (int u = 0; u < NRW; ++u)
+        acc[u][ct] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[st][u], bv, acc[u][ct], 0, 0, 0);
+    }
   }
-  const int col = col0 + lr;
-  if (col < ncols) {
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    const int col = col0 + 16 * ct + lr;
+    if (col >= ncols) continue;
 #pragma unroll
     for (int u = 0; u < NRW; ++u) {
       if (wid + 4 * u >= ntiles) continue;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int r = (wid + 4 * u) * 16 + lk + 4 * q;
-        if (r < bs) out[(size_t)r * ncols + col] = acc[u][q];
+        if (r < bs) out[(size_t)r * ncols + col] = acc[u][ct][q];
       }
     }
   }
@@ -1682,11 +1690,16 @@ static void apply(const double* A, int bs, const double* Bm, double* out, int nc
 // bs > kSpdMax; in and out may not alias
 static void solve(const BlockWs& w, int bs, const double* in, double* out, int ncols, hipStream_t st) {
   if (bs <= kSpdMax) {
-    const dim3 grid((ncols + 15) / 16);
-    if (bs <= 64)
-      hipLaunchKernelGGL((apply_strip_kernel<1, 16>), grid, dim3(256), 0, st, w.Li, bs, in, out, ncols);
-    else
-      hipLaunchKernelGGL((apply_strip_kernel<2, 32>), grid, dim3(256), 0, st, w.Li, bs, in, out, ncols);
+    // two strips per workgroup once that still leaves a workgroup per CU or more
+    const bool two = ncols >= 2 * 16 * 256;
+    const dim3 grid(two ? (ncols + 31) / 32 : (ncols + 15) / 16);
+    if (bs <= 64) {
+      if (two) hipLaunchKernelGGL((apply_strip_kernel<1, 16, 2>), grid, dim3(256), 0, st, w.Li, bs, in, out, ncols);
+      else hipLaunchKernelGGL((apply_strip_kernel<1, 16, 1>), grid, dim3(256), 0, st, w.Li, bs, in, out, ncols);
+    } else {
+      if (two) hipLaunchKernelGGL((apply_strip_kernel<2, 32, 2>), grid, dim3(256), 0, st, w.Li, bs, in, out, ncols);
+      else hipLaunchKernelGGL((apply_strip_kernel<2, 32, 1>), grid, dim3(256), 0, st, w.Li, bs, in, out, ncols);
+    }
     return;
   }
   apply<false>(w.Li, bs, in, w.Tmp, ncols, st);
