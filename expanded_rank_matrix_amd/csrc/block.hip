@@ -429,17 +429,18 @@ __global__ void __launch_bounds__(1024) gram_i8_kernel(const int8_t* T, int ldt,
   const int ra = ti * 16 + lr, rb = tj * 16 + lr;
   const int nch = (K + 63) / 64;
   v4i acc = (v4i){0, 0, 0, 0};
-  for (int c0 = wid; c0 < nch; c0 += 4 * 16) {
-    v4i a[4], b[4];
+  constexpr int CH = 8;  // chunks per wave and round, all their loads issued before the products
+  for (int c0 = wid; c0 < nch; c0 += CH * 16) {
+    v4i a[CH], b[CH];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < CH; ++u) {
       const int k = (c0 + 16 * u) * 64 + 16 * g;
       const bool ok = c0 + 16 * u < nch && k < ldt;
       a[u] = (ok && ra < bs) ? load16(T + (size_t)ra * ldt + k) : (v4i){0, 0, 0, 0};
       b[u] = (ok && rb < bs) ? load16(T + (size_t)rb * ldt + k) : (v4i){0, 0, 0, 0};
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[u], b[u], acc, 0, 0, 0);
+    for (int u = 0; u < CH; ++u) acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[u], b[u], acc, 0, 0, 0);
   }
 #pragma unroll
   for (int q = 0; q < 4; ++q) red[wid][q * 64 + lane] = acc[q];
@@ -494,18 +495,28 @@ __global__ void __launch_bounds__(1024) gram_w_i8_kernel(const int8_t* T, int ld
   v4i acc[kHDig];
 #pragma unroll
   for (int t = 0; t < kHDig; ++t) acc[t] = (v4i){0, 0, 0, 0};
-  for (int ch = wid; ch < nch; ch += 16) {
-    const int k = ch * 64 + 16 * g;
-    const bool ok = k < ldt;
-    const v4i a = (ok && ra < bs) ? load16(T + (size_t)ra * ldt + k) : (v4i){0, 0, 0, 0};
-    const v4i b = (ok && rb < bs) ? load16(T + (size_t)rb * ldt + k) : (v4i){0, 0, 0, 0};
+  constexpr int CH = 3;  // chunks per wave and round, all their loads issued before the products
+  for (int c0 = wid; c0 < nch; c0 += CH * 16) {
+    v4i a[CH], b[CH], d[CH][kHDig];
 #pragma unroll
-    for (int t = 0; t < kHDig; ++t) {
-      const v4i d = ok ? load16(reinterpret_cast<const int8_t*>(hdig) + (size_t)t * ldt + k) : (v4i){0, 0, 0, 0};
-      v4i bd;
+    for (int u = 0; u < CH; ++u) {
+      const int k = (c0 + 16 * u) * 64 + 16 * g;
+      const bool ok = c0 + 16 * u < nch && k < ldt;
+      a[u] = (ok && ra < bs) ? load16(T + (size_t)ra * ldt + k) : (v4i){0, 0, 0, 0};
+      b[u] = (ok && rb < bs) ? load16(T + (size_t)rb * ldt + k) : (v4i){0, 0, 0, 0};
 #pragma unroll
-      for (int q = 0; q < 4; ++q) bd[q] = (int)tmul_bytes((unsigned)b[q], (unsigned)d[q]);
-      acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bd, acc[t], 0, 0, 0);
+      for (int t = 0; t < kHDig; ++t)
+        d[u][t] = ok ? load16(reinterpret_cast<const int8_t*>(hdig) + (size_t)t * ldt + k) : (v4i){0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+#pragma unroll
+      for (int t = 0; t < kHDig; ++t) {
+        v4i bd;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) bd[q] = (int)tmul_bytes((unsigned)b[u][q], (unsigned)d[u][t][q]);
+        acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[u], bd, acc[t], 0, 0, 0);
+      }
     }
   }
 #pragma unroll
