@@ -28,6 +28,9 @@ namespace externd {
 
 typedef double dbl4 __attribute__((ext_vector_type(4)));
 
+constexpr int kGramSplit = 8;    // most K splits of the weighted Gram
+constexpr int kGramTiles = 136;  // lower 16 x 16 tiles of a Gram with b <= 256
+
 struct BlockWs {
   int ldu, ldv;    // row lengths of Ut / Vt: m and n rounded up to 16 (zero padding)
   int8_t* Ut;      // b x ldu, component-major
@@ -50,6 +53,8 @@ struct BlockWs {
   unsigned* rmax;  // [64 (s & 1) + w]: max |R| (fp32 bits) at the start of block s, spread over 64
                    // words w to keep the atomics of one update uncontended
   uint8_t* hdig;   // kHDig x ldv: 7-bit digits of the fixed-point column weights (weighted only)
+  double* gpart;   // kGramSplit x kGramTiles x 256: split-K partial tiles of the weighted Gram
+  unsigned* gcnt;  // kGramTiles: workgroups of each tile done (zero between launches)
   double* GUo;     // b x b: Gram of the old U (refinement sweeps)
   double* GVo;     // b x b: weighted Gram of the old V
   double* ppo;     // b: u_c^T (R + X) H v_c of the old components
@@ -87,6 +92,8 @@ static void ws_layout(int m, int n, int b, F&& take) {
   take((void**)nullptr, bb * bb * 8);
   take((void**)nullptr, bb * 8);
   take((void**)nullptr, bb * 4);
+  take((void**)nullptr, (size_t)kGramSplit * kGramTiles * 256 * 8);  // split-K Gram partial tiles
+  take((void**)nullptr, (size_t)kGramTiles * 4);                     // their arrival counters
 }
 
 static BlockWs carve(void* base, int m, int n, int b) {
@@ -124,6 +131,8 @@ static BlockWs carve(void* base, int m, int n, int b) {
   w.GVo = static_cast<double*>(ptrs[q++]);
   w.ppo = static_cast<double*>(ptrs[q++]);
   w.dold = static_cast<float*>(ptrs[q++]);
+  w.gpart = static_cast<double*>(ptrs[q++]);
+  w.gcnt = static_cast<unsigned*>(ptrs[q++]);
   return w;
 }
 
@@ -480,28 +489,33 @@ __device__ __forceinline__ unsigned tmul_bytes(unsigned t, unsigned d) {
 
 // G = T diag(h) T^T for ternary rows T with h in fixed point (hdig): sum_t 2^(7 t) T (T o dig_t)^T,
 // each digit product exact in int32, recombined exactly in fp64, times 2^-(35 - EHm).  The only
-// difference from the fp64 sum is the rounding of each h_j to the grid.  One workgroup of 16
-// waves per lower 16 x 16 tile; the waves split K and add in LDS in wave order.
+// difference from the fp64 sum is the rounding of each h_j to the grid.  Workgroup: 16 waves on
+// one lower 16 x 16 tile (blockIdx.x) and one of gridDim.y ranges of K; the waves add in LDS in
+// wave order.  With several ranges each workgroup stores its partial tile, and the last one of the
+// tile to arrive adds them in range order; every partial is an integer below 2^53 (in units of
+// the grid), so the sums are exact and the result does not depend on the split.
 __global__ void __launch_bounds__(1024) gram_w_i8_kernel(const int8_t* T, int ldt, int K, int bs, const uint8_t* hdig,
-                                                         int ehm, double* G) {
+                                                         int ehm, double* G, double* gpart, unsigned* gcnt) {
   __shared__ double red[16][256];
+  __shared__ unsigned last_s;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int lr = lane & 15, g = lane >> 4;
   int ti = 0;
   while ((ti + 1) * (ti + 2) / 2 <= (int)blockIdx.x) ++ti;
   const int tj = (int)blockIdx.x - ti * (ti + 1) / 2;
   const int ra = ti * 16 + lr, rb = tj * 16 + lr;
-  const int nch = (K + 63) / 64;
+  const int nch = (K + 63) / 64, S = (int)gridDim.y, y = (int)blockIdx.y;
+  const int cb = (int)((long long)nch * y / S), ce = (int)((long long)nch * (y + 1) / S);
   v4i acc[kHDig];
 #pragma unroll
   for (int t = 0; t < kHDig; ++t) acc[t] = (v4i){0, 0, 0, 0};
   constexpr int CH = 3;  // chunks per wave and round, all their loads issued before the products
-  for (int c0 = wid; c0 < nch; c0 += CH * 16) {
+  for (int c0 = cb + wid; c0 < ce; c0 += CH * 16) {
     v4i a[CH], b[CH], d[CH][kHDig];
 #pragma unroll
     for (int u = 0; u < CH; ++u) {
       const int k = (c0 + 16 * u) * 64 + 16 * g;
-      const bool ok = c0 + 16 * u < nch && k < ldt;
+      const bool ok = c0 + 16 * u < ce && k < ldt;
       a[u] = (ok && ra < bs) ? load16(T + (size_t)ra * ldt + k) : (v4i){0, 0, 0, 0};
       b[u] = (ok && rb < bs) ? load16(T + (size_t)rb * ldt + k) : (v4i){0, 0, 0, 0};
 #pragma unroll
@@ -527,18 +541,44 @@ __global__ void __launch_bounds__(1024) gram_w_i8_kernel(const int8_t* T, int ld
     red[wid][q * 64 + lane] = v;
   }
   __syncthreads();
+  double v[4] = {0.0, 0.0, 0.0, 0.0};
+  if (wid == 0) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int w2 = 0; w2 < 16; ++w2) v[q] += red[w2][q * 64 + lane];
+  }
+  if (S > 1) {
+    const int ntile = (int)gridDim.x;
+    if (wid == 0) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) st_dev(gpart + ((size_t)y * ntile + blockIdx.x) * 256 + q * 64 + lane, v[q]);
+    }
+    // the partials go through agent-coherent stores and loads (no L2 writeback or invalidate);
+    // each store has completed before the arrival is counted
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) last_s = add_dev(&gcnt[blockIdx.x], 1u) == (unsigned)(S - 1) ? 1u : 0u;
+    __syncthreads();
+    if (!last_s) return;
+    if (wid == 0) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[q] = 0.0;
+        for (int y2 = 0; y2 < S; ++y2) v[q] += ld_dev(gpart + ((size_t)y2 * ntile + blockIdx.x) * 256 + q * 64 + lane);
+      }
+    }
+    if (tid == 0) st_dev(&gcnt[blockIdx.x], 0u);  // ready for the next launch
+  }
   if (wid == 0) {
     const double unit = ldexp(1.0, ehm - kHDig * 7);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      double v = 0.0;
-#pragma unroll
-      for (int w2 = 0; w2 < 16; ++w2) v += red[w2][q * 64 + lane];
-      v *= unit;
+      const double x = v[q] * unit;
       const int r = ti * 16 + 4 * g + q, c = tj * 16 + lr;
       if (r < bs && c < bs) {
-        G[(size_t)r * bs + c] = v;
-        G[(size_t)c * bs + r] = v;
+        G[(size_t)r * bs + c] = x;
+        G[(size_t)c * bs + r] = x;
       }
     }
   }
@@ -1523,9 +1563,11 @@ __global__ void __launch_bounds__(256) refit_choose_kernel(const double* ppo, co
 }
 
 // E0 from the per-row energies (fixed order), dead flag for A = 0
-__global__ void block_init_kernel(const double* rowE, int m, double* st, int* flags, unsigned* rmax) {
+__global__ void block_init_kernel(const double* rowE, int m, double* st, int* flags, unsigned* rmax,
+                                  unsigned* gcnt) {
   __shared__ double red[4];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  if (tid < kGramTiles) gcnt[tid] = 0u;
   double e = 0.0;
   for (int i = tid; i < m; i += 256) e += rowE[i];
   e = wave_sum_f64(e);
@@ -1626,7 +1668,12 @@ static void gram_product(const BlockWs& w, const int8_t* T, int len, int ldt, co
     hipLaunchKernelGGL(gram_i8_kernel, dim3(nt * (nt + 1) / 2), dim3(1024), 0, st, T, ldt, len, bs, G);
     return;
   }
-  hipLaunchKernelGGL(gram_w_i8_kernel, dim3(nt * (nt + 1) / 2), dim3(1024), 0, st, T, ldt, len, bs, w.hdig, ehm, G);
+  // K split so that each wave takes about one round of chunks (16 waves x 3 chunks per range)
+  const int nch = (len + 63) / 64;
+  int split = (nch + 47) / 48;
+  split = split < 1 ? 1 : (split > kGramSplit ? kGramSplit : split);
+  hipLaunchKernelGGL(gram_w_i8_kernel, dim3(nt * (nt + 1) / 2, split), dim3(1024), 0, st, T, ldt, len, bs, w.hdig,
+                     ehm, G, w.gpart, w.gcnt);
 }
 
 // X (bs x n) = U^T R, on int8 MFMA with R in fixed point
@@ -1759,7 +1806,7 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops, double
   const BlockWs w = carve(L.ws, L.m, L.n, L.b);
   const int m = L.m, n = L.n;
   hipError_t e = hipSuccess;
-  hipLaunchKernelGGL(block_init_kernel, dim3(1), dim3(256), 0, st, L.rowE, m, w.st, w.flags, w.rmax);
+  hipLaunchKernelGGL(block_init_kernel, dim3(1), dim3(256), 0, st, L.rowE, m, w.st, w.flags, w.rmax, w.gcnt);
   {
     const long long nb = ((long long)m * n + 255) / 256;
     hipLaunchKernelGGL(rmax_kernel, dim3((unsigned)(nb < 2048 ? nb : 2048)), dim3(256), 0, st, L.R, L.ldr, m, n,
