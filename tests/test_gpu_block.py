@@ -102,6 +102,23 @@ def test_block_determinism():
         assert np.array_equal(g1[key], g2[key]), key
 
 
+@pytest.mark.parametrize("m,n,block", [(160, 6200, 32), (200, 6200, 128)])
+def test_split_gram_long_rows(m, n, block):
+    """Weighted Gram over rows longer than 3072 (split over K, partials added by the last
+    workgroup of each tile) and the inverse inside the contraction launch: two runs agree bit for
+    bit, and the run agrees with the oracle over the first blocks and on a replayed block."""
+    A, h = inputs.make_input("down2560x9728", m=m, n=n)
+    g1 = P.gpu_decompose(A, 0.5, 0.2, h, 2, block)
+    g2 = P.gpu_decompose(A, 0.5, 0.2, h, 2, block)
+    for key in ("B", "C", "D", "energy"):
+        assert np.array_equal(g1[key], g2[key]), key
+    o = oracle.decompose(A, 0.5, 0.2, h, 2, block, k_limit=2 * block)
+    label = f"split gram {m}x{n} b={block}"
+    P.check_free_run(g1, o, label, block)
+    nb = -(-g1["k"] // block)
+    P.check_replay(A, 0.5, 0.2, h, 2, block, g1, [0, nb - 1], label)
+
+
 def test_block_integer_inputs_exact():
     """Small integer matrices: every fp64 sum is exact in any order, so the GPU must reproduce
     the oracle bit for bit, ties included."""
