@@ -735,9 +735,8 @@ __host__ __device__ inline size_t spd_lds_bytes(int bs) {
   const int bp = (bs + 15) & ~15, ld = bp + 1;
   return 8 * ((size_t)bp * ld + (size_t)(bp / 16) * 256 + 16);
 }
-// NT threads share the tile products (256 for b <= 64, where four waves cover the few tiles and a
-// small workgroup finds a CU sooner beside the concurrent contraction; 1024 above); wave 0
-// factors the diagonal blocks.
+// NT threads share the tile products (256 for b <= 64, where four waves cover the few tiles and
+// the body fits a contraction's workgroup; 1024 above); wave 0 factors the diagonal blocks.
 // The body runs in its own launch (spd_inv_kernel) or as one extra workgroup of a residual
 // contraction (rv_i8_kernel, utr_i8_kernel), which overlaps the two without a second stream.
 template <int NT>
