@@ -49,6 +49,7 @@ def test_tiny_blocks_every_component(block):
     ("lowrank1024", 300, 260, 1.0, -1),      # default block size min(256, min(m, n) / 8)
     ("attn2560", 300, 280, 1.0, 256),        # largest block
     ("attn2560", 333, 257, 1.0, 100),        # block not a multiple of the MFMA tile
+    ("attn2560", 400, 360, 1.0, 160),        # three components per lane in the scale walk
     ("attn2560", 1, 37, 2.0, 2),
     ("attn2560", 41, 1, 2.0, 2),
     ("attn2560", 17, 1100, 1.0, 8),
