@@ -70,6 +70,7 @@ def test_sequential_target_stop(name, m, n, mu, tau, weighted):
     (8, 64, 48, 2.0, False),
     (16, 130, 97, 2.0, True),
     (64, 300, 260, 1.0, False),
+    (128, 400, 300, 1.0, False),   # stops in the second 64-component slot of the scale walk
 ])
 def test_block_target_stop_inside_a_block(block, m, n, mu, weighted):
     A, h = inputs.make_input("down2560x9728" if weighted else "attn2560", m=m, n=n)
@@ -77,7 +78,7 @@ def test_block_target_stop_inside_a_block(block, m, n, mu, weighted):
         h = None
     full = oracle.decompose(A, mu, 0.0, h, 3, block)
     k = full["k"]
-    picks = [block + block // 2, 2 * block - 1, 3 * block, k - 2]
+    picks = [p for p in (block + block // 2, 2 * block - 1, 3 * block, k - 2) if 1 <= p < k]
     for i, t in safe_targets(full["energy"], picks, sep=2e-4):
         g = P.gpu_decompose(A, mu, 0.0, h, 3, block, energy_target=t)
         o = oracle.decompose(A, mu, 0.0, h, 3, block, energy_target=t)
