@@ -72,11 +72,14 @@ def _load():
         lib.externd_oracle_replay.restype = ctypes.c_int
         lib.externd_oracle_replay.argtypes = [vp, i64, i64, f32, f32, vp, ctypes.c_int,
                                               ctypes.c_int, vp, vp, vp, vp, i64, vp, vp, vp,
-                                              vp, vp, vp]
+                                              vp, vp, vp, vp]
         lib.externd_oracle_matvec.restype = ctypes.c_int
         lib.externd_oracle_apply.argtypes = [vp, vp, vp, i64, i64, i64, vp, i64, vp, ctypes.c_int]
         lib.externd_oracle_matvec.argtypes = [vp, i64, i64, vp, vp, ctypes.c_int, vp,
                                               ctypes.c_int]
+        lib.externd_oracle_explicit_energy.restype = ctypes.c_int
+        lib.externd_oracle_explicit_energy.argtypes = [vp, i64, i64, vp, vp, vp, vp, i64, vp, i64,
+                                                       vp, ctypes.c_int]
         _lib = lib
     return _lib
 
@@ -199,8 +202,10 @@ def replay(A, mu: float, tau: float, h, als_iters: int, block: int, B, C, D, sam
     """Replay given factors; fit the sampled components (sequential) or blocks afresh.
 
     ``upto`` > 0 stops the walk after that many components (energy_replay is NaN beyond).
-    Returns dict(Bo, Co, Do, gap_o, energy_replay).  For the block path each sample slot holds
-    b components (rows sample_index*b .. +b of the factor arrays)."""
+    Returns dict(Bo, Co, Do, gap_o, dec_o, energy_replay): the oracle's refit of each sample, its
+    selection gaps and its energy decreases (units of |A|^2_H), and the energy curve of the given
+    factors on the replayed residual.  For the block path each sample slot holds b components
+    (rows sample_index*b .. +b of the factor arrays)."""
     A = np.ascontiguousarray(A, dtype=np.float32)
     h = _f32(h)
     m, n = A.shape
@@ -217,15 +222,16 @@ def replay(A, mu: float, tau: float, h, als_iters: int, block: int, B, C, D, sam
     Co = np.zeros((max(slots, 1), words(n)), dtype=np.uint32)
     Do = np.zeros(max(slots, 1), dtype=np.float32)
     go = np.full(max(slots, 1), np.inf)
+    dec = np.zeros(max(slots, 1), dtype=np.float64)
     er = np.full(k, np.nan)
     o = _make_opts(threads, False, upto, None, None, None, False)
     rc = _load().externd_oracle_replay(_ptr(A), m, n, mu, tau, _ptr(h), als_iters, block,
                                        _ptr(B), _ptr(C), _ptr(D), _ptr(sample), ns, _ptr(Bo),
-                                       _ptr(Co), _ptr(Do), _ptr(go), _ptr(er),
+                                       _ptr(Co), _ptr(Do), _ptr(go), _ptr(dec), _ptr(er),
                                        ctypes.addressof(o))
     if rc != 0:
         raise ValueError(f"oracle replay failed ({rc})")
-    return dict(Bo=Bo[:slots], Co=Co[:slots], Do=Do[:slots], gap_o=go[:slots],
+    return dict(Bo=Bo[:slots], Co=Co[:slots], Do=Do[:slots], gap_o=go[:slots], dec_o=dec[:slots],
                 energy_replay=er, b=b, sample=sample)
 
 
@@ -239,6 +245,26 @@ def matvec(R, t, h=None, transpose: bool = False, threads: int = 0):
     _load().externd_oracle_matvec(_ptr(R), m, n, _ptr(t), _ptr(h), int(transpose), _ptr(out),
                                   threads)
     return out
+
+
+def explicit_energy(A, h, B, C, D, at, threads: int = 0):
+    """1 - |A - sum_{c<=i} D_c b_c c_c^T|^2_h / |A|^2_h after each component i in ``at``,
+    recomputed in fp64 from the packed factors (the definition of the energy preserved)."""
+    A = np.ascontiguousarray(A, dtype=np.float32)
+    h = _f32(h)
+    m, n = A.shape
+    B = np.ascontiguousarray(B, dtype=np.uint32)
+    C = np.ascontiguousarray(C, dtype=np.uint32)
+    D = np.ascontiguousarray(D, dtype=np.float32)
+    k = D.shape[0]
+    assert B.shape == (k, words(m)) and C.shape == (k, words(n))
+    at = np.ascontiguousarray(np.asarray(at, dtype=np.int64))
+    out = np.zeros(max(1, at.shape[0]), dtype=np.float64)
+    rc = _load().externd_oracle_explicit_energy(_ptr(A), m, n, _ptr(h), _ptr(B), _ptr(C), _ptr(D), k,
+                                                _ptr(at), at.shape[0], _ptr(out), threads)
+    if rc != 0:
+        raise ValueError("oracle explicit_energy: bad arguments")
+    return out[:at.shape[0]]
 
 
 def apply(B, C, D, m: int, n: int, X, threads: int = 0):

@@ -936,7 +936,7 @@ template <typename RT>
 int replay_t(const float* A, int64_t m, int64_t n, float mu, float tau, const float* h, int T,
              int block, const uint32_t* B, const uint32_t* C, const float* D,
              const int64_t* sample, int64_t nsample, uint32_t* Bo, uint32_t* Co, float* Do,
-             double* gap_o, double* energy_replay, const externd_oracle_opts* opts) {
+             double* gap_o, double* dec_o, double* energy_replay, const externd_oracle_opts* opts) {
   const int64_t k = externd_oracle_rank(m, n, mu);
   if (k < 1) return -1;
   State<RT> st;
@@ -958,6 +958,9 @@ int replay_t(const float* A, int64_t m, int64_t n, float mu, float tau, const fl
           pack(c.v.data(), n, Co + si * wn);
           Do[si] = c.zero ? 0.0f : c.d;
           gap_o[si] = c.zero ? kInf : c.gap;
+          // the refit's energy decrease 2 d p - d^2 q, in units of |A|^2_H
+          const double dd = (double)c.d;
+          dec_o[si] = c.zero ? 0.0 : (2.0 * dd * c.p - dd * dd * c.q) / st.E0;
         }
         ++si;
       }
@@ -986,11 +989,19 @@ int replay_t(const float* A, int64_t m, int64_t n, float mu, float tau, const fl
       if (si < nsample && sample[si] == s) {
         if (st.E0 > 0.0) {
           Block bl = fit_block(st, s, bs);
+          // the refit's energy walk on this residual (per-component decreases), E restored after
+          std::vector<double> ew(bs, 0.0);
+          const double E_keep = st.E;
+          if (!bl.zero) block_energy(st, bl.U, bl.V, bl.d, bs, ew.data());
+          st.E = E_keep;
+          double prev = 1.0 - E_keep / st.E0;
           for (int64_t c = 0; c < bs; ++c) {
             pack(bl.U.data() + c * m, m, Bo + (si * b + c) * wm);
             pack(bl.V.data() + c * n, n, Co + (si * b + c) * wn);
             Do[si * b + c] = bl.zero ? 0.0f : bl.d[c];
             gap_o[si * b + c] = bl.zero ? kInf : bl.gap[c];
+            dec_o[si * b + c] = bl.zero ? 0.0 : ew[c] - prev;
+            if (!bl.zero) prev = ew[c];
           }
         }
         ++si;
@@ -1056,10 +1067,10 @@ int externd_oracle_replay(const float* A, int64_t m, int64_t n, float mu, float 
                           const float* h, int als_iters, int block, const uint32_t* B,
                           const uint32_t* C, const float* D, const int64_t* sample,
                           int64_t nsample, uint32_t* Bo, uint32_t* Co, float* Do, double* gap_o,
-                          double* energy_replay, const externd_oracle_opts* opts) {
+                          double* dec_o, double* energy_replay, const externd_oracle_opts* opts) {
   if (als_iters < 1 || block < -1 || tau < 0.0f || tau > 1.0f) return -1;
   return replay_t<float>(A, m, n, mu, tau, h, als_iters, block, B, C, D, sample, nsample, Bo,
-                         Co, Do, gap_o, energy_replay, opts);
+                         Co, Do, gap_o, dec_o, energy_replay, opts);
 }
 
 // Inference from the packed factors (ExTernD review, Significance: the factorisation stays free
@@ -1098,6 +1109,52 @@ int externd_oracle_apply(const uint32_t* B, const uint32_t* C, const float* D, i
       }
       Y[b * m + r] = (float)y;
     }
+  }
+  return 0;
+}
+
+// Energy preserved by given factors, recomputed from the definition E = 1 - |A - Ahat|^2 / |A|^2
+// (pith.science, "Load-bearing premise"; in the column-weighted norm when h is given): the
+// residual A - sum_{c <= i} D_c u_c v_c^T in fp64, one component at a time, its squared norm taken
+// after each component listed in `at`.  Independent of the engines' fp32 residual and their
+// bookkeeping E <- E - (2 d p - d^2 q), so it checks both.
+int externd_oracle_explicit_energy(const float* A, int64_t m, int64_t n, const float* h, const uint32_t* B,
+                                   const uint32_t* C, const float* D, int64_t k, const int64_t* at, int64_t nat,
+                                   double* out, int threads) {
+  if (m < 1 || n < 1 || k < 0 || nat < 0) return -1;
+  for (int64_t t = 0; t < nat; ++t)
+    if (at[t] < 0 || at[t] >= k || (t > 0 && at[t] <= at[t - 1])) return -1;
+  const int nt = threads > 0 ? threads : omp_get_max_threads();
+  const int64_t wm = words_of(m), wn = words_of(n);
+  std::vector<double> R(A, A + m * n);
+  auto norm = [&]() {
+    std::vector<double> rowE(m, 0.0);
+#pragma omp parallel for num_threads(nt) schedule(static)
+    for (int64_t i = 0; i < m; ++i) {
+      double e = 0.0;
+      for (int64_t j = 0; j < n; ++j) e += (h ? (double)h[j] : 1.0) * R[i * n + j] * R[i * n + j];
+      rowE[i] = e;
+    }
+    double E = 0.0;
+    for (int64_t i = 0; i < m; ++i) E += rowE[i];
+    return E;
+  };
+  const double E0 = norm();
+  std::vector<int8_t> u(m), v(n);
+  int64_t t = 0;
+  for (int64_t c = 0; c < k && t < nat; ++c) {
+    unpack(B + c * wm, m, u.data());
+    unpack(C + c * wn, n, v.data());
+    const double d = (double)D[c];
+    std::vector<int64_t> cols;
+    for (int64_t j = 0; j < n; ++j)
+      if (v[j]) cols.push_back(j);
+#pragma omp parallel for num_threads(nt) schedule(static)
+    for (int64_t i = 0; i < m; ++i) {
+      if (!u[i]) continue;
+      for (int64_t j : cols) R[i * n + j] -= d * (double)(u[i] * v[j]);
+    }
+    if (c == at[t]) out[t++] = E0 > 0.0 ? 1.0 - norm() / E0 : 1.0;
   }
   return 0;
 }

@@ -67,7 +67,10 @@ int externd_oracle_decompose(const float* A, int64_t m, int64_t n, float mu, flo
 /* Replay: walk the components (or blocks) of a finished decomposition (B, C, D given), applying
  * each with the oracle's deflation rule.  Before applying component (block) s listed in
  * `sample` (ascending), fit it afresh from the replayed residual and write the oracle's own
- * result to Bo/Co/Do/gap_o (one slot per sample; a block slot holds b components).
+ * result to Bo/Co/Do/gap_o (one slot per sample; a block slot holds b components), and to
+ * dec_o the refit's energy decrease in units of |A|^2_H (2 d p - d^2 q per component; for a block
+ * the steps of its own energy walk on the replayed residual), so that a given component (block)
+ * that differs from the refit can be compared by what it removes.
  * energy_replay[i] = energy after applying the given component i, from the oracle's own exact
  * p, q of that component on the replayed residual.  With opts->k_limit > 0 the walk stops
  * after that many components (entries beyond it are left untouched). */
@@ -76,12 +79,20 @@ int externd_oracle_replay(const float* A, int64_t m, int64_t n, float mu, float 
                           const uint32_t* B, const uint32_t* C, const float* D,
                           const int64_t* sample, int64_t nsample,
                           uint32_t* Bo, uint32_t* Co, float* Do, double* gap_o,
-                          double* energy_replay, const externd_oracle_opts* opts);
+                          double* dec_o, double* energy_replay, const externd_oracle_opts* opts);
 
 /* Inference from the packed factors: Y (batch x m) = (B diag(D) C X^T)^T for X (batch x n),
  * fp64 sums in index order, one fp32 rounding.  B: k x words(m), C: k x words(n). */
 int externd_oracle_apply(const uint32_t* B, const uint32_t* C, const float* D, int64_t k, int64_t m,
                          int64_t n, const float* X, int64_t batch, float* Y, int threads);
+
+/* Energy preserved by given factors, recomputed from its definition: the residual
+ * A - sum_{c <= i} D_c b_c c_c^T is formed in fp64 one component at a time and, after each
+ * component i listed in `at` (ascending, < k), out[t] = 1 - |residual|^2_h / |A|^2_h
+ * (column weights h, NULL = uniform).  B: k x words(m), C: k x words(n). */
+int externd_oracle_explicit_energy(const float* A, int64_t m, int64_t n, const float* h,
+                                   const uint32_t* B, const uint32_t* C, const float* D, int64_t k,
+                                   const int64_t* at, int64_t nat, double* out, int threads);
 
 /* Plain matvecs used by kernel-level parity tests: out = R^T u (transpose = 1) or R (h .* v). */
 int externd_oracle_matvec(const float* R, int64_t m, int64_t n, const int8_t* t, const float* h,

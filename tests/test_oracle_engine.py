@@ -277,3 +277,24 @@ def test_low_rank_share_of_generator():
     s = np.linalg.svd(A.astype(np.float64), compute_uv=False)
     share = np.sum(s[:16] ** 2) / np.sum(s ** 2)
     assert 0.3 <= share <= 0.6
+
+
+def test_explicit_energy_from_factors():
+    """The explicit recomputation E = 1 - |A - B diag(D) C|^2_h / |A|^2_h (pith.science,
+    Load-bearing premise) of given factors: the hand-worked 2 x 2 energies exactly, and the
+    engines' fp64 bookkeeping within the fp32 residual's rounding (1e-7) on both engines,
+    weighted and with tau > 0."""
+    ex = json.load(open(GOLDEN))["decomposition_2x2"]
+    A = np.array(ex["A"], np.float32)
+    o = oracle.decompose(A, ex["mu"], ex["tau"], None, ex["als_iters"], 1)
+    e = oracle.explicit_energy(A, None, o["B"], o["C"], o["D"], [0, 1, 2])
+    assert np.allclose(e, ex["energy"], rtol=0, atol=1e-15)
+    A, h = inputs.make_input("down2560x9728", m=60, n=90)
+    for block in (1, 8):
+        o = oracle.decompose(A, 1.0, 0.2, h, 3, block)
+        at = np.arange(0, o["k"], 7)
+        e = oracle.explicit_energy(A, h, o["B"], o["C"], o["D"], at)
+        assert np.max(np.abs(e - o["energy"][at])) < 1e-7
+    # a wrong sign of D shows: the first component's energy becomes negative
+    bad = oracle.explicit_energy(A, h, o["B"], o["C"], -o["D"], [0])
+    assert bad[0] < 0

@@ -169,3 +169,37 @@ def test_corrected_v_step_never_worse_than_naive():
         vu, *_ = oracle.project(x, 0.0, None)                       # naive: ignore h
         naive2 = (vu.astype(np.float64) @ (h * xd)) ** 2 / (np.abs(vu).astype(np.float64) @ h)
         assert S >= max(naive1, naive2) * (1 - 1e-12)
+
+
+def test_gap_hand_worked():
+    """The selection gap that decides which GPU/oracle differences count as near-ties, against
+    hand-worked values (tests/golden/worked_examples.json, "gap"): a relative score gap g1 to the
+    best other prefix length, the boundary-membership gap g2, and with tau > 0 the eligibility
+    margins on both sides of theta.  A dropped normalisation, a shifted index or a missing
+    threshold side changes one of them by far more than the fp32 rounding of tau and h
+    (rel 1e-6)."""
+    cases = json.load(open(GOLDEN))["gap"]["cases"]
+    for c in cases:
+        x = np.asarray(c["x"], np.float32)
+        h = None if c["h"] is None else np.asarray(c["h"], np.float32)
+        gap = oracle.project(x, c["tau"], h)[5]
+        assert gap == pytest.approx(c["gap"], rel=1e-6), c
+    # the ineligible side matters: without it the tau = 0.8 case would give 0.2
+    c = cases[2]
+    assert c["gap"] < c["g3_eligible"]
+
+
+def test_gap_scales_and_exact_tie():
+    """The gap is a ratio: invariant under scaling x; a prefix tie in S gives gap 0."""
+    rng = np.random.default_rng(7)
+    for _ in range(20):
+        x = rng.standard_normal(12).astype(np.float32)
+        g = oracle.project(x, 0.0)[5]
+        g2 = oracle.project(x * np.float32(4.0), 0.0)[5]
+        assert g == pytest.approx(g2, rel=1e-12)
+    # x = (3, 1, 1), h = (1, 1.5, 1.5): S = 9, 4.5^2 / 2.5 = 8.1, 6^2 / 4 = 9 -- an exact tie
+    # between j = 1 and j = 3; the smallest j wins and the gap is zero
+    x = np.array([3, 1, 1], np.float32)
+    h = np.array([1, 1.5, 1.5], np.float32)
+    v, P, H, S, j, gap = oracle.project(x, 0.0, h)
+    assert S == 9.0 and j == 1 and gap == 0.0 and v.tolist() == [1, 0, 0]
