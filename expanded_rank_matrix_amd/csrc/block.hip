@@ -1,4 +1,4 @@
-// Block-ALS path: b components per block with dense contractions on fp64 MFMA (gfx950).
+// Block-ALS path: b components per block with dense contractions on int8 and fp64 MFMA (gfx950).
 //
 // Method (ExTernD review, Method: "a batched block-ALS GPU algorithm with a decorrelated
 // least-squares target"; pith.science minor comment 1, Eq. 3: V <- T_tau((U^T U + eps I)^-1
@@ -13,14 +13,19 @@
 //   R <- fl32(R - U diag(d) V^T).
 // eps = 1e-6 trace(Gram) / b.
 //
-// MI355X mapping.  The three residual contractions per half-step (R Omega / R H V with K = n,
-// U^T R with K = m, and the rank-b update with K = b) run on v_mfma_f64_16x16x4f64: R is
-// converted fp32 -> fp64 exactly, the ternary operand is exact, accumulation is fp64, so the
-// contractions agree with the fp64 sums of a plain implementation to rounding order.  Split-K
-// partial results are summed in a fixed order (deterministic).  The small b x b work (Grams,
-// Cholesky, triangular solves, scales) runs in dedicated kernels with the same operation order as
-// a textbook implementation.  Selections use the same exact projection as the sequential path,
-// one workgroup per component.
+// MI355X mapping.  The residual contractions (R Omega and R H V with K = n, U^T R with K = m) run
+// on v_mfma_i32_16x16x64_i8: the ternary operand is exact int8, and R (times h_j, formed in fp64,
+// in the weighted U-step) enters as its 48-bit fixed-point image split into six signed 8-bit
+// digits, one power-of-two grid per block chosen from max |R| (and max h).  Digit products sum
+// exactly in int32 and recombine exactly in int64; split-K partials add with 64-bit integer
+// atomics, so each contraction is the exact contraction of the image, independent of launch shape
+// and atomic order, within 2^-47 of max |R| per entry of the fp64 sums of a plain implementation.
+// The contraction outputs stay integers (with their grid unit) until the kernels that read them.
+// Grams are the same int8 MFMA on the ternary rows (integer-exact; the weighted Gram takes h in
+// 35-bit fixed point).  The b x b solves use (G + eps I)^-1 from a blocked Cholesky (fp64 MFMA
+// tiles) and one fp64 MFMA product per solve; the rank-b update runs on v_mfma_f64_16x16x4f64 with
+// K = b and one fp32 rounding per entry.  Selections use the same exact projection as the
+// sequential path, one workgroup per component row.
 #include "externd_internal.hpp"
 #include "select.hpp"
 
@@ -35,9 +40,9 @@ struct BlockWs {
   int ldu, ldv;    // row lengths of Ut / Vt: m and n rounded up to 16 (zero padding)
   int8_t* Ut;      // b x ldu, component-major
   int8_t* Vt;      // b x ldv (also holds Omega for the sketch)
-  double* Yt;      // b x m: sketch / (R H V)^T
+  double* Yt;      // b x m: sketch / (R H V)^T, int64 in units of unit[1] (see Yi)
   double* Ft;      // b x m: F^T
-  double* X;       // b x n: U^T R
+  double* X;       // b x n: U^T R, int64 in units of unit[0] (see Xi)
   double* Z;       // b x max(m, n): G (V-step target)
   double* Tmp;     // b x max(m, n): L^-1 times the right-hand sides
   double* GU;      // b x b
@@ -59,6 +64,9 @@ struct BlockWs {
   double* GVo;     // b x b: weighted Gram of the old V
   double* ppo;     // b: u_c^T (R + X) H v_c of the old components
   float* dold;     // b: old scales
+  double* unit;    // [0] unit of X, [1] unit of Yt: the fixed-point grid of the last contraction
+  long long* Xi;   // X and Yt as the contractions write them (exact integers)
+  long long* Yi;
 };
 
 constexpr int kMaxWords = 64;      // words per residual-max slot (one per lane of a wave)
@@ -94,6 +102,7 @@ static void ws_layout(int m, int n, int b, F&& take) {
   take((void**)nullptr, bb * 4);
   take((void**)nullptr, (size_t)kGramSplit * kGramTiles * 256 * 8);  // split-K Gram partial tiles
   take((void**)nullptr, (size_t)kGramTiles * 4);                     // their arrival counters
+  take((void**)nullptr, 64);                                         // contraction units
 }
 
 static BlockWs carve(void* base, int m, int n, int b) {
@@ -133,6 +142,9 @@ static BlockWs carve(void* base, int m, int n, int b) {
   w.dold = static_cast<float*>(ptrs[q++]);
   w.gpart = static_cast<double*>(ptrs[q++]);
   w.gcnt = static_cast<unsigned*>(ptrs[q++]);
+  w.unit = static_cast<double*>(ptrs[q++]);
+  w.Xi = reinterpret_cast<long long*>(w.X);
+  w.Yi = reinterpret_cast<long long*>(w.Yt);
   return w;
 }
 
@@ -175,15 +187,21 @@ __global__ void __launch_bounds__(256) omega_kernel(int8_t* Vt, int ldv, int bs,
 // of column l % 16 of B, paired on the same k; D(i, j) lands in lane j + 16 (i / 4), register i % 4.
 // Lane group g = l / 16 takes k = k0 + 16 g .. k0 + 16 g + 15 of each 64-wide k chunk.
 //
-// R enters as N = rint(x 2^f), x = R_ij (times h_j where weighted), with one power-of-two scale per
-// block chosen from max |R| so that |N| <= 2^30, split into four signed 8-bit digits
-// N = sum_s 2^(8 s) d_s.  The ternary operand is exact in int8, each digit product sums exactly
-// in int32 (|sum| <= 2^7 K), the digits recombine exactly in fp64 and splits of K add exactly
-// (every partial is an integer times 2^-f below 2^53).  The result is therefore the exact
-// contraction of the fixed-point image of R, whatever the launch shape or the order of the
-// atomic adds: its only error is the rounding of each x to the grid 2^-f, at most 2^-31 of the
-// largest |x|.
+// R enters as N = rint(x 2^f), x = R_ij (times h_j where weighted, formed in fp64), with one
+// power-of-two scale per block chosen from max |R| (and max h) so that |N| <= 2^46, split into six
+// signed 8-bit digits N = sum_s 2^(8 s) d_s.  The ternary operand is exact in int8, each digit
+// product sums exactly in int32 (|sum| <= 2^7 K), the digits recombine exactly in int64
+// (|sum| <= 2^46 K < 2^61 for K <= 16384) and splits of K add exactly with 64-bit integer
+// atomics.  The result is the exact contraction of the fixed-point image of R, whatever the launch
+// shape or the order of the atomic adds; its only error is the rounding of each x to the grid
+// 2^-f, at most 2^-47 of the largest |x| (a 32-bit image, 2^-31, left the weighted targets of the
+// 2560 x 9728 down projection within ~1e-7 of their fp64 values, one or two fp32 ulps, enough to
+// flip near-tied selections).  The outputs are these integers (int64, in units of 2^-f); each
+// launch also stores the unit 2^-f, and every kernel that reads an output scales it by that unit.
 typedef int v4i __attribute__((ext_vector_type(4)));
+
+constexpr int kFxBits = 46;  // |N| <= 2^kFxBits
+constexpr int kDig = 6;      // signed 8-bit digits of N
 
 // exponent E of the fixed-point range: |x| < 2^E for every x entering a contraction (each wave
 // reduces the 64 words of block s's slot itself)
@@ -193,31 +211,58 @@ __device__ __forceinline__ int fx_exponent(const unsigned* rmax, int s, int ehm)
   return exp_bound(__uint_as_float(bits)) + ehm;
 }
 
+// scale exponent f with |x 2^f| <= 2^kFxBits, inside fp64's normal range
+__device__ __forceinline__ int fx_scale(const unsigned* rmax, int s, int ehm) {
+  const int f = kFxBits - fx_exponent(rmax, s, ehm);
+  return f < 1000 ? (f > -1000 ? f : -1000) : 1000;
+}
+
+// rint of an fp64 value of magnitude <= 2^46 (exact conversion of the integral result)
+__device__ __forceinline__ long long fx_round(double v) { return (long long)rint(v); }
+
 // Digits of four fixed-point values: word t holds digit t of n[0..3] in bytes 0..3.  With
-// B = n + 0x808080, digits 0..2 are B's bytes minus 128 (byte ^ 0x80) and digit 3 is B >> 24.
-__device__ __forceinline__ void fx_digits4(int n0, int n1, int n2, int n3, unsigned (&w)[4]) {
-  const unsigned b0 = (unsigned)(n0 + 0x808080), b1 = (unsigned)(n1 + 0x808080);
-  const unsigned b2 = (unsigned)(n2 + 0x808080), b3 = (unsigned)(n3 + 0x808080);
+// B = n + 0x8080808080 (128 in bytes 0..4), digits 0..4 are B's bytes minus 128 (byte ^ 0x80) and
+// digit 5 is B >> 40, in [-64, 64] for |n| <= 2^46 (B's byte 5 read as a signed byte).
+__device__ __forceinline__ void fx_digits6(long long n0, long long n1, long long n2, long long n3,
+                                           unsigned (&w)[kDig]) {
+  const long long bias = 0x8080808080ll;
+  const unsigned long long b0 = (unsigned long long)(n0 + bias), b1 = (unsigned long long)(n1 + bias);
+  const unsigned long long b2 = (unsigned long long)(n2 + bias), b3 = (unsigned long long)(n3 + bias);
+  const unsigned l0 = (unsigned)b0, l1 = (unsigned)b1, l2 = (unsigned)b2, l3 = (unsigned)b3;
+  const unsigned h0 = (unsigned)(b0 >> 32), h1 = (unsigned)(b1 >> 32), h2 = (unsigned)(b2 >> 32),
+                 h3 = (unsigned)(b3 >> 32);
   // v_perm_b32: selector bytes 0..3 pick bytes of the second source, 4..7 of the first
-  const unsigned x01lo = __builtin_amdgcn_perm(b1, b0, 0x05010400u);  // b0.0 b1.0 b0.1 b1.1
-  const unsigned x01hi = __builtin_amdgcn_perm(b1, b0, 0x07030602u);  // b0.2 b1.2 b0.3 b1.3
-  const unsigned x23lo = __builtin_amdgcn_perm(b3, b2, 0x05010400u);
-  const unsigned x23hi = __builtin_amdgcn_perm(b3, b2, 0x07030602u);
+  const unsigned x01lo = __builtin_amdgcn_perm(l1, l0, 0x05010400u);  // b0.0 b1.0 b0.1 b1.1
+  const unsigned x01hi = __builtin_amdgcn_perm(l1, l0, 0x07030602u);  // b0.2 b1.2 b0.3 b1.3
+  const unsigned x23lo = __builtin_amdgcn_perm(l3, l2, 0x05010400u);
+  const unsigned x23hi = __builtin_amdgcn_perm(l3, l2, 0x07030602u);
+  const unsigned y01 = __builtin_amdgcn_perm(h1, h0, 0x05010400u);    // b0.4 b1.4 b0.5 b1.5
+  const unsigned y23 = __builtin_amdgcn_perm(h3, h2, 0x05010400u);
   w[0] = __builtin_amdgcn_perm(x23lo, x01lo, 0x05040100u) ^ 0x80808080u;
   w[1] = __builtin_amdgcn_perm(x23lo, x01lo, 0x07060302u) ^ 0x80808080u;
   w[2] = __builtin_amdgcn_perm(x23hi, x01hi, 0x05040100u) ^ 0x80808080u;
-  w[3] = __builtin_amdgcn_perm(x23hi, x01hi, 0x07060302u);
+  w[3] = __builtin_amdgcn_perm(x23hi, x01hi, 0x07060302u) ^ 0x80808080u;
+  w[4] = __builtin_amdgcn_perm(y23, y01, 0x05040100u) ^ 0x80808080u;
+  w[5] = __builtin_amdgcn_perm(y23, y01, 0x07060302u);
 }
 
-// 16 fixed-point values -> the four digit operands (operand t = digit t of values 0..15)
-__device__ __forceinline__ void fx_operands(const int (&nv)[16], v4i (&op)[4]) {
+// 16 fixed-point values -> the six digit operands (operand t = digit t of values 0..15)
+__device__ __forceinline__ void fx_operands(const long long (&nv)[16], v4i (&op)[kDig]) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    unsigned w[4];
-    fx_digits4(nv[4 * q], nv[4 * q + 1], nv[4 * q + 2], nv[4 * q + 3], w);
+    unsigned w[kDig];
+    fx_digits6(nv[4 * q], nv[4 * q + 1], nv[4 * q + 2], nv[4 * q + 3], w);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) op[t][q] = (int)w[t];
+    for (int t = 0; t < kDig; ++t) op[t][q] = (int)w[t];
   }
+}
+
+// the digit sums of one output recombined: sum_t 256^t acc_t, exact in int64
+__device__ __forceinline__ long long fx_combine(const v4i (&acc)[kDig], int q) {
+  long long v = 0;
+#pragma unroll
+  for (int t = kDig - 1; t >= 0; --t) v = v * 256ll + (long long)acc[t][q];
+  return v;
 }
 
 __device__ __forceinline__ v4i load16(const int8_t* p) { return *reinterpret_cast<const v4i*>(p); }
@@ -231,37 +276,39 @@ __host__ __device__ inline size_t spd_lds_bytes(int bs);
 // (256 contiguous bytes per tile row: full cache lines), converted to its fixed-point image
 // once, and staged in LDS; each lane then reads its 16 values of the MFMA layout from there.  The
 // next chunk's loads are issued before the current chunk is consumed.
-constexpr int kTileP = 68;  // int32 pitch of a [64 rows][64 k] tile (rows 16 B aligned)
-constexpr int kTileQ = 65;  // int32 pitch of a [64 k][64 cols] tile (column reads conflict-free)
+constexpr int kTileP = 66;  // int64 pitch of a [64 rows][64 k] tile (rows 16 B aligned)
+constexpr int kTileQ = 65;  // int64 pitch of a [64 k][64 cols] tile
+constexpr size_t kTileBytesP = sizeof(long long) * 64 * kTileP;
+constexpr size_t kTileBytesQ = sizeof(long long) * 64 * kTileQ;
 
-// out[c][i] (+)= sum_{k in this split} x_ik T[c][k], x_ik = R[i][k] (h_k): rows of R x components.
-// Workgroup: 64 rows (16 per wave) x 16 NCT components (blockIdx.y), K range blockIdx.z.
+// out[c][i] (+)= sum_{k in this split} N(x_ik) T[c][k], x_ik = R[i][k] (h_k): rows of R x
+// components, in units *unit = 2^-f.  Workgroup: 64 rows (16 per wave) x 16 NCT components
+// (blockIdx.y), K range blockIdx.z.
 template <int NCT>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) rv_i8_kernel(const float* R, int ldr, int rows, int K, const int8_t* T,
                                                     int ldt, const float* h, int ehm, int bs, const unsigned* rmax,
-                                                    int sblk, int kspan, double* out, const double* spdG,
-                                                    double* spdGi) {
+                                                    int sblk, int kspan, long long* out, double* unit,
+                                                    const double* spdG, double* spdGi) {
   extern __shared__ __align__(16) char dsm[];
   if (spdG && blockIdx.x == gridDim.x - 1) {  // the extra column of workgroups: one inverts spdG
     if (blockIdx.y == 0 && blockIdx.z == 0) spd_inv_body<256>(spdG, bs, spdGi, dsm);
     return;
   }
-  int* tile = reinterpret_cast<int*>(dsm);  // 64 x kTileP
+  long long* tile = reinterpret_cast<long long*>(dsm);  // 64 x kTileP
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int lr = lane & 15, g = lane >> 4;
   const int c0 = blockIdx.y * 16 * NCT;
   const int kb = blockIdx.z * kspan, ke = kb + kspan < K ? kb + kspan : K;
-  const int E = fx_exponent(rmax, sblk, h ? ehm : 0);
-  const int sc = 30 - E < 126 ? (30 - E > -126 ? 30 - E : -126) : 126;  // scale 2^sc, a normal float
-  const float fscale = ldexpf(1.0f, sc);
+  const int sc = fx_scale(rmax, sblk, h ? ehm : 0);
   const double dscale = ldexp(1.0, sc);
+  if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && tid == 0) *unit = ldexp(1.0, -sc);
   // staging role: thread t loads tile rows t / 16 + 16 q, k columns 4 (t % 16) .. + 3
   const int srow = tid >> 4, scol = 4 * (tid & 15);
-  v4i acc[NCT][4];
+  v4i acc[NCT][kDig];
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) acc[ct][t] = (v4i){0, 0, 0, 0};
+    for (int t = 0; t < kDig; ++t) acc[ct][t] = (v4i){0, 0, 0, 0};
   float4 pre[4];
   float4 hpre = make_float4(0.f, 0.f, 0.f, 0.f);
   auto fetch = [&](int k0) {
@@ -284,14 +331,16 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) r
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const float xv[4] = {pre[q].x, pre[q].y, pre[q].z, pre[q].w};
-        int nv[4];
+        long long nv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const bool in = k + e < ke;
-          if (h) nv[e] = in ? __double2int_rn((double)xv[e] * (double)hv[e] * dscale) : 0;
-          else nv[e] = in ? __float2int_rn(xv[e] * fscale) : 0;
+          const double x = h ? (double)xv[e] * (double)hv[e] : (double)xv[e];
+          nv[e] = in ? fx_round(x * dscale) : 0ll;
         }
-        *reinterpret_cast<int4*>(&tile[(srow + 16 * q) * kTileP + scol]) = make_int4(nv[0], nv[1], nv[2], nv[3]);
+        long long* trow = &tile[(srow + 16 * q) * kTileP + scol];
+        *reinterpret_cast<longlong2*>(trow) = make_longlong2(nv[0], nv[1]);
+        *reinterpret_cast<longlong2*>(trow + 2) = make_longlong2(nv[2], nv[3]);
       }
     }
     __syncthreads();
@@ -303,25 +352,23 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) r
       const int c = c0 + ct * 16 + lr;
       tb[ct] = (c < bs && k < ke) ? load16(T + (size_t)c * ldt + k) : (v4i){0, 0, 0, 0};
     }
-    int nv[16];
+    long long nv[16];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int4 v = *reinterpret_cast<const int4*>(&tile[(wid * 16 + lr) * kTileP + 16 * g + 4 * p]);
-      nv[4 * p] = v.x;
-      nv[4 * p + 1] = v.y;
-      nv[4 * p + 2] = v.z;
-      nv[4 * p + 3] = v.w;
+    for (int p = 0; p < 8; ++p) {
+      const longlong2 v = *reinterpret_cast<const longlong2*>(&tile[(wid * 16 + lr) * kTileP + 16 * g + 2 * p]);
+      nv[2 * p] = v.x;
+      nv[2 * p + 1] = v.y;
     }
-    v4i da[4];
+    v4i da[kDig];
     fx_operands(nv, da);
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-      for (int t = 0; t < 4; ++t) acc[ct][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(tb[ct], da[t], acc[ct][t], 0, 0, 0);
+      for (int t = 0; t < kDig; ++t)
+        acc[ct][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(tb[ct], da[t], acc[ct][t], 0, 0, 0);
   }
   // D = T x^T: lane l, register q holds component 4 g + q of the tile for row lr, so each store
   // instruction covers four components x 16 consecutive rows
-  const double unit = ldexp(1.0, -sc);
   const bool split = gridDim.z > 1;
   const int r = blockIdx.x * 64 + wid * 16 + lr;
 #pragma unroll
@@ -330,44 +377,44 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) r
     for (int q = 0; q < 4; ++q) {
       const int c = c0 + ct * 16 + 4 * g + q;
       if (c < bs && r < rows) {
-        const double v = ((double)acc[ct][0][q] + 256.0 * (double)acc[ct][1][q] + 65536.0 * (double)acc[ct][2][q] +
-                          16777216.0 * (double)acc[ct][3][q]) * unit;
-        double* o = out + (size_t)c * rows + r;
-        if (split) atomicAdd(o, v);
+        const long long v = fx_combine(acc[ct], q);
+        long long* o = out + (size_t)c * rows + r;
+        if (split) atomicAdd(reinterpret_cast<unsigned long long*>(o), (unsigned long long)v);
         else *o = v;
       }
     }
   }
 }
 
-// out[c][j] (+)= sum_{i in this split} U[c][i] R[i][j]: components x columns of R.
-// Workgroup: 64 columns (16 per wave) x 16 NCT components (blockIdx.y), K = m range blockIdx.z.
+// out[c][j] (+)= sum_{i in this split} U[c][i] N(R[i][j]): components x columns of R, in units
+// *unit = 2^-f.  Workgroup: 64 columns (16 per wave) x 16 NCT components (blockIdx.y), K = m range
+// blockIdx.z.
 template <int NCT>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) utr_i8_kernel(const float* R, int ldr, int m, int n, const int8_t* U, int ldu,
-                                                     int bs, const unsigned* rmax, int sblk, int kspan, double* out,
-                                                     const double* spdG, double* spdGi) {
+                                                     int bs, const unsigned* rmax, int sblk, int kspan, long long* out,
+                                                     double* unit, const double* spdG, double* spdGi) {
   extern __shared__ __align__(16) char dsm[];
   if (spdG && blockIdx.x == gridDim.x - 1) {  // the extra column of workgroups: one inverts spdG
     if (blockIdx.y == 0 && blockIdx.z == 0) spd_inv_body<256>(spdG, bs, spdGi, dsm);
     return;
   }
-  int* tile = reinterpret_cast<int*>(dsm);  // 64 x kTileQ
+  long long* tile = reinterpret_cast<long long*>(dsm);  // 64 x kTileQ
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int lr = lane & 15, g = lane >> 4;
   const int j = blockIdx.x * 64 + wid * 16 + lr;  // column supplied by this lane
   const int c0 = blockIdx.y * 16 * NCT;
   const int kb = blockIdx.z * kspan, ke = kb + kspan < m ? kb + kspan : m;
-  const int E = fx_exponent(rmax, sblk, 0);
-  const int sc = 30 - E < 126 ? (30 - E > -126 ? 30 - E : -126) : 126;  // scale 2^sc, a normal float
-  const float fscale = ldexpf(1.0f, sc);
+  const int sc = fx_scale(rmax, sblk, 0);
+  const double dscale = ldexp(1.0, sc);
+  if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && tid == 0) *unit = ldexp(1.0, -sc);
   const bool jok = j < n;
   // staging role: thread t loads tile rows (k) t / 16 + 16 q, columns 4 (t % 16) .. + 3
   const int srow = tid >> 4, scol = 4 * (tid & 15), sj = blockIdx.x * 64 + scol;
-  v4i acc[NCT][4];
+  v4i acc[NCT][kDig];
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-    for (int t = 0; t < 4; ++t) acc[ct][t] = (v4i){0, 0, 0, 0};
+    for (int t = 0; t < kDig; ++t) acc[ct][t] = (v4i){0, 0, 0, 0};
   float4 pre[4];
   auto fetch = [&](int k0) {
 #pragma unroll
@@ -382,11 +429,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) u
     __syncthreads();  // the previous chunk's tile is consumed
 #pragma unroll
     for (int q = 0; q < 4; ++q) {  // columns past n hold R's zero padding (or nothing: zero)
-      int* trow = &tile[(srow + 16 * q) * kTileQ + scol];
-      trow[0] = __float2int_rn(pre[q].x * fscale);
-      trow[1] = __float2int_rn(pre[q].y * fscale);
-      trow[2] = __float2int_rn(pre[q].z * fscale);
-      trow[3] = __float2int_rn(pre[q].w * fscale);
+      long long* trow = &tile[(srow + 16 * q) * kTileQ + scol];
+      trow[0] = fx_round((double)pre[q].x * dscale);
+      trow[1] = fx_round((double)pre[q].y * dscale);
+      trow[2] = fx_round((double)pre[q].z * dscale);
+      trow[3] = fx_round((double)pre[q].w * dscale);
     }
     __syncthreads();
     if (k0 + 64 < ke) fetch(k0 + 64);
@@ -397,17 +444,17 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) u
       const int c = c0 + ct * 16 + lr;
       ua[ct] = (c < bs && k < ke) ? load16(U + (size_t)c * ldu + k) : (v4i){0, 0, 0, 0};
     }
-    int nv[16];
+    long long nv[16];
 #pragma unroll
     for (int t = 0; t < 16; ++t) nv[t] = tile[(16 * g + t) * kTileQ + wid * 16 + lr];
-    v4i db[4];
+    v4i db[kDig];
     fx_operands(nv, db);
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-      for (int t = 0; t < 4; ++t) acc[ct][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ua[ct], db[t], acc[ct][t], 0, 0, 0);
+      for (int t = 0; t < kDig; ++t)
+        acc[ct][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ua[ct], db[t], acc[ct][t], 0, 0, 0);
   }
-  const double unit = ldexp(1.0, -sc);
   const bool split = gridDim.z > 1;
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) {
@@ -415,10 +462,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) u
     for (int q = 0; q < 4; ++q) {
       const int c = c0 + ct * 16 + 4 * g + q;
       if (c < bs && jok) {
-        const double v = ((double)acc[ct][0][q] + 256.0 * (double)acc[ct][1][q] + 65536.0 * (double)acc[ct][2][q] +
-                          16777216.0 * (double)acc[ct][3][q]) * unit;
-        double* o = out + (size_t)c * n + j;
-        if (split) atomicAdd(o, v);
+        const long long v = fx_combine(acc[ct], q);
+        long long* o = out + (size_t)c * n + j;
+        if (split) atomicAdd(reinterpret_cast<unsigned long long*>(o), (unsigned long long)v);
         else *o = v;
       }
     }
@@ -922,10 +968,13 @@ __global__ void __launch_bounds__(NT) spd_inv_kernel(const double* G, int bs, do
 
 // ---- out (bs x ncols) = op(A) B with A bs x bs (op: A or A^T), B bs x ncols, fp64 MFMA, K = bs.
 // Workgroup: 64 columns; wave w: columns 16 w .. 16 w + 15, all bs rows (NRT tiles of 16).
+// bunit (nullable): Bm holds a contraction's int64 output in units of *bunit.
 template <int NRT, bool TA>
 __global__ void __launch_bounds__(256) apply_kernel(const double* __restrict__ A, int bs, const double* Bm,
-                                                    double* out, int ncols) {
+                                                    const double* bunit, double* out, int ncols) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const double bu = bunit ? *bunit : 1.0;
+  const long long* Bi = reinterpret_cast<const long long*>(Bm);
   const int col = blockIdx.x * 64 + wid * 16 + (lane & 15);
   const bool okc = col < ncols;
   dbl4 acc[NRT];
@@ -933,7 +982,8 @@ __global__ void __launch_bounds__(256) apply_kernel(const double* __restrict__ A
   for (int t = 0; t < NRT; ++t) acc[t] = (dbl4){0.0, 0.0, 0.0, 0.0};
   for (int k0 = 0; k0 < bs; k0 += 4) {
     const int k = k0 + (lane >> 4);
-    const double bv = (k < bs && okc) ? Bm[(size_t)k * ncols + col] : 0.0;
+    const double bv = (k < bs && okc) ? (bunit ? (double)Bi[(size_t)k * ncols + col] * bu : Bm[(size_t)k * ncols + col])
+                                      : 0.0;
 #pragma unroll
     for (int t = 0; t < NRT; ++t) {
       const int r = t * 16 + (lane & 15);
@@ -958,9 +1008,10 @@ __global__ void __launch_bounds__(256) apply_kernel(const double* __restrict__ A
 // w, w + 4, ...  Every A operand of the whole K range (NKS k-steps of 4) is loaded into registers
 // before the strips are staged, so the workgroup waits for one round of loads, then runs its MFMAs
 // back to back, each A operand serving the NCT strips.
+// Bm holds a contraction's int64 output in units of *bunit.
 template <int NRW, int NKS, int NCT>
-__global__ void __launch_bounds__(256) apply_strip_kernel(const double* __restrict__ A, int bs, const double* Bm,
-                                                          double* out, int ncols) {
+__global__ void __launch_bounds__(256) apply_strip_kernel(const double* __restrict__ A, int bs, const long long* Bm,
+                                                          const double* bunit, double* out, int ncols) {
   __shared__ double Bs[kSpdMax][16 * NCT];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int lr = lane & 15, lk = lane >> 4;
@@ -988,12 +1039,13 @@ __global__ void __launch_bounds__(256) apply_strip_kernel(const double* __restri
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
     const int x = tid + 256 * i, k = x / W, c = x % W;
-    bl[i] = (k < bs && col0 + c < ncols) ? Bm[(size_t)k * ncols + col0 + c] : 0.0;
+    bl[i] = (k < bs && col0 + c < ncols) ? (double)Bm[(size_t)k * ncols + col0 + c] : 0.0;
   }
+  const double bu = *bunit;
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
     const int x = tid + 256 * i;
-    Bs[x / W][x % W] = bl[i];
+    Bs[x / W][x % W] = bl[i] * bu;
   }
   __syncthreads();
 #pragma unroll
@@ -1024,16 +1076,20 @@ __global__ void __launch_bounds__(256) apply_strip_kernel(const double* __restri
 }
 
 // ---- one workgroup per component row: T[c] = T_tau(fp32(X[c]); h) -----------------------------
+// X holds fp64 rows, or (xunit set) a contraction's int64 rows in units of *xunit, whose fp32
+// roundings are formed in LDS first.  Z0 (nullable): row c of the next split-K contraction's
+// output is cleared here (zlen values), which saves that contraction a separate clearing launch.
+// Md (nullable): Md[c] = T[c] . Yd[c] over the L entries (the last U-step's u_c^T Q_c for the
+// scales); Yd is a contraction's int64 output in units of *ydunit, so the sum is exact in int64 and
+// scaled once.
 template <bool W, int NT>
-// Z0 (nullable): row c of the next split-K contraction's output is cleared here (zlen doubles),
-// which saves that contraction a separate clearing launch.  Md (nullable): Md[c] = T[c] . Yd[c]
-// over the L entries (the last U-step's u_c^T Q_c for the scales), fixed reduction order.
-__global__ void __launch_bounds__(NT) select_rows_kernel(const double* X, int L, int ldT, float tau,
-                                                          const float* h, int EHm, int8_t* T, double* PHC,
+__global__ void __launch_bounds__(NT) select_rows_kernel(const double* X, const double* xunit, int L, int ldT,
+                                                          float tau, const float* h, int EHm, int8_t* T, double* PHC,
                                                           int* flags, int flag_empty, double* Z0, int zlen,
-                                                          const double* Yd, double* Md) {
+                                                          const long long* Yd, const double* ydunit, double* Md) {
   __shared__ SelScratchT<W> s;
-  __shared__ double red[NT / 64];
+  __shared__ u64 red[NT / 64];
+  extern __shared__ float xs[];  // L values when xunit is set
   const int c = blockIdx.x;
   const double* x = X + (size_t)c * L;
   if (Z0)
@@ -1042,22 +1098,31 @@ __global__ void __launch_bounds__(NT) select_rows_kernel(const double* X, int L,
     for (int j = threadIdx.x; j < ldT; j += NT) T[(size_t)c * ldT + j] = 0;
     return;
   }
-  const SelResult r = ternary_select<NT, W>(x, h, L, tau, EHm, s);
-  double dot = 0.0;
+  SelResult r;
+  if (xunit) {
+    const long long* xi = reinterpret_cast<const long long*>(x);
+    const double u = *xunit;
+    for (int j = threadIdx.x; j < L; j += NT) xs[j] = (float)((double)xi[j] * u);
+    __syncthreads();
+    r = ternary_select<NT, W>(xs, h, L, tau, EHm, s);
+  } else {
+    r = ternary_select<NT, W>(x, h, L, tau, EHm, s);
+  }
+  long long dot = 0;
   for (int j = threadIdx.x; j < ldT; j += NT) {  // the padding [L, ldT) stays zero
-    const float xv = j < L ? (float)x[j] : 0.0f;
+    const float xv = j < L ? (xunit ? xs[j] : (float)x[j]) : 0.0f;
     const int8_t t = selected(xv, r) ? (xv > 0.0f ? (int8_t)1 : (int8_t)-1) : (int8_t)0;
     T[(size_t)c * ldT + j] = t;
-    if (Md && t) dot += (double)t * Yd[(size_t)c * L + j];
+    if (Md && t) dot += t > 0 ? Yd[(size_t)c * L + j] : -Yd[(size_t)c * L + j];
   }
   if (Md) {
-    dot = wave_sum_f64(dot);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = dot;
+    const u64 wsum = wave_sum_u64((u64)dot);  // two's complement: exact in any order
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = wsum;
     __syncthreads();
     if (threadIdx.x == 0) {
-      double t = 0.0;
+      u64 t = 0;
       for (int w = 0; w < NT / 64; ++w) t += red[w];
-      Md[c] = t;
+      Md[c] = (double)(long long)t * *ydunit;
     }
   }
   if (threadIdx.x == 0) {
@@ -1473,16 +1538,17 @@ __global__ void __launch_bounds__(256) refit_load_kernel(const uint32_t* Bp, con
   }
 }
 
-// pp[c] = v_c^T H X[c] for the first V-step's X = U^T (R + X_blk) and the block's old V: one
-// workgroup per component, fixed reduction order.
-__global__ void __launch_bounds__(256) addback_dot_kernel(const double* X, int n, const int8_t* Vt, int ldv,
-                                                          const float* h, double* pp) {
+// pp[c] = v_c^T H X[c] for the first V-step's X = U^T (R + X_blk) (int64 in units of *xunit) and
+// the block's old V: one workgroup per component, fixed reduction order.
+__global__ void __launch_bounds__(256) addback_dot_kernel(const long long* X, const double* xunit, int n,
+                                                          const int8_t* Vt, int ldv, const float* h, double* pp) {
   __shared__ double red[4];
   const int c = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const double u = *xunit;
   double acc = 0.0;
   for (int j = tid; j < n; j += 256) {
     const int v = Vt[(size_t)c * ldv + j];
-    if (v) acc += (double)v * (h ? (double)h[j] : 1.0) * X[(size_t)c * n + j];
+    if (v) acc += (double)v * (h ? (double)h[j] : 1.0) * ((double)X[(size_t)c * n + j] * u);
   }
   acc = wave_sum_f64(acc);
   if (lane == 0) red[wid] = acc;
@@ -1625,38 +1691,39 @@ static void zero_fill(double* p, long long count, hipStream_t st) {
 // Y^T (bs x m) = (R diag(h) V^T)^T for V = Vt rows, on int8 MFMA with R in fixed point
 // Whether the contraction of R (rows or columns) with bs ternary vectors splits K, so that its
 // output must be cleared first.
+// 16-component tiles per contraction workgroup: six digit accumulators per tile, so four tiles
+// would exceed the register budget of three workgroups per CU (and spill)
+static int contract_nct(int bs) { return bs <= 16 ? 1 : 2; }
+
 static bool rw_splits(const BlockLaunch& L, int bs) {
-  const int nct = bs <= 16 ? 1 : (bs <= 32 ? 2 : 4);
+  const int nct = contract_nct(bs);
   int kspan = 0;
   return i8_splits(((L.m + 63) / 64) * ((bs + 16 * nct - 1) / (16 * nct)), L.n, &kspan) > 1;
 }
 static bool utr_splits(const BlockLaunch& L, int bs) {
-  const int nct = bs <= 16 ? 1 : (bs <= 32 ? 2 : 4);
+  const int nct = contract_nct(bs);
   int kspan = 0;
   return i8_splits(((L.n + 63) / 64) * ((bs + 16 * nct - 1) / (16 * nct)), L.m, &kspan) > 1;
 }
 
-static void rw_product(const BlockLaunch& L, const BlockWs& w, const float* h, int bs, int sblk, double* outT,
+static void rw_product(const BlockLaunch& L, const BlockWs& w, const float* h, int bs, int sblk, long long* outT,
                        hipStream_t st, bool prezeroed = false, const double* spdG = nullptr,
                        double* spdGi = nullptr) {
-  const int nct = bs <= 16 ? 1 : (bs <= 32 ? 2 : 4);  // 8 tiles: one wave per SIMD, slower
+  const int nct = contract_nct(bs);
   const int gx = (L.m + 63) / 64, gy = (bs + 16 * nct - 1) / (16 * nct);
   int kspan = 0;
   const int gz = i8_splits(gx * gy, L.n, &kspan);
-  if (gz > 1 && !prezeroed) zero_fill(outT, (long long)bs * L.m, st);
+  if (gz > 1 && !prezeroed) zero_fill(reinterpret_cast<double*>(outT), (long long)bs * L.m, st);
   // with spdG, one more column of workgroups, one of which inverts spdG
   const dim3 grid(gx + (spdG ? 1 : 0), gy, gz);
-  size_t lds = (size_t)4 * 64 * kTileP;
+  size_t lds = kTileBytesP;
   if (spdG && spd_lds_bytes(bs) > lds) lds = spd_lds_bytes(bs);
   if (nct == 1)
     hipLaunchKernelGGL(rv_i8_kernel<1>, grid, dim3(256), lds, st, L.R, L.ldr, L.m, L.n, w.Vt, w.ldv, h, L.EHm, bs,
-                       w.rmax, sblk, kspan, outT, spdG, spdGi);
-  else if (nct == 2)
-    hipLaunchKernelGGL(rv_i8_kernel<2>, grid, dim3(256), lds, st, L.R, L.ldr, L.m, L.n, w.Vt, w.ldv, h, L.EHm, bs,
-                       w.rmax, sblk, kspan, outT, spdG, spdGi);
+                       w.rmax, sblk, kspan, outT, w.unit + 1, spdG, spdGi);
   else
-    hipLaunchKernelGGL(rv_i8_kernel<4>, grid, dim3(256), lds, st, L.R, L.ldr, L.m, L.n, w.Vt, w.ldv, h, L.EHm, bs,
-                       w.rmax, sblk, kspan, outT, spdG, spdGi);
+    hipLaunchKernelGGL(rv_i8_kernel<2>, grid, dim3(256), lds, st, L.R, L.ldr, L.m, L.n, w.Vt, w.ldv, h, L.EHm, bs,
+                       w.rmax, sblk, kspan, outT, w.unit + 1, spdG, spdGi);
 }
 
 // G (bs x bs) = T diag(w) T^T for ternary rows T (bs x len, ld ldt); integer-exact without weights
@@ -1678,24 +1745,21 @@ static void gram_product(const BlockWs& w, const int8_t* T, int len, int ldt, co
 // X (bs x n) = U^T R, on int8 MFMA with R in fixed point
 static void utr_product(const BlockLaunch& L, const BlockWs& w, int bs, int sblk, hipStream_t st,
                         bool prezeroed = false, const double* spdG = nullptr, double* spdGi = nullptr) {
-  const int nct = bs <= 16 ? 1 : (bs <= 32 ? 2 : 4);  // 8 tiles: one wave per SIMD, slower
+  const int nct = contract_nct(bs);
   const int gx = (L.n + 63) / 64, gy = (bs + 16 * nct - 1) / (16 * nct);
   int kspan = 0;
   const int gz = i8_splits(gx * gy, L.m, &kspan);
   if (gz > 1 && !prezeroed) zero_fill(w.X, (long long)bs * L.n, st);
   // with spdG, one more column of workgroups, one of which inverts spdG
   const dim3 grid(gx + (spdG ? 1 : 0), gy, gz);
-  size_t lds = (size_t)4 * 64 * kTileQ;
+  size_t lds = kTileBytesQ;
   if (spdG && spd_lds_bytes(bs) > lds) lds = spd_lds_bytes(bs);
   if (nct == 1)
     hipLaunchKernelGGL(utr_i8_kernel<1>, grid, dim3(256), lds, st, L.R, L.ldr, L.m, L.n, w.Ut, w.ldu, bs, w.rmax,
-                       sblk, kspan, w.X, spdG, spdGi);
-  else if (nct == 2)
-    hipLaunchKernelGGL(utr_i8_kernel<2>, grid, dim3(256), lds, st, L.R, L.ldr, L.m, L.n, w.Ut, w.ldu, bs, w.rmax,
-                       sblk, kspan, w.X, spdG, spdGi);
+                       sblk, kspan, w.Xi, w.unit, spdG, spdGi);
   else
-    hipLaunchKernelGGL(utr_i8_kernel<4>, grid, dim3(256), lds, st, L.R, L.ldr, L.m, L.n, w.Ut, w.ldu, bs, w.rmax,
-                       sblk, kspan, w.X, spdG, spdGi);
+    hipLaunchKernelGGL(utr_i8_kernel<2>, grid, dim3(256), lds, st, L.R, L.ldr, L.m, L.n, w.Ut, w.ldu, bs, w.rmax,
+                       sblk, kspan, w.Xi, w.unit, spdG, spdGi);
 }
 
 // Li = (G + eps I)^-1 for bs <= kSpdMax, else Li = L^-1 for L L^T = G + eps I
@@ -1732,56 +1796,63 @@ static void chol_inverse(const BlockWs& w, const double* G, int bs, hipStream_t 
     hipLaunchKernelGGL((chol_inv_kernel<1024, 33>), dim3(1), dim3(1024), 0, st, G, bs, w.Li);
 }
 
+// bunit (nullable): Bm is a contraction's int64 output in units of *bunit
 template <bool TA>
-static void apply(const double* A, int bs, const double* Bm, double* out, int ncols, hipStream_t st) {
+static void apply(const double* A, int bs, const double* Bm, const double* bunit, double* out, int ncols,
+                  hipStream_t st) {
   const dim3 grid((ncols + 63) / 64);
   const int nrt = (bs + 15) / 16;
-  if (nrt <= 1) hipLaunchKernelGGL((apply_kernel<1, TA>), grid, dim3(256), 0, st, A, bs, Bm, out, ncols);
-  else if (nrt <= 2) hipLaunchKernelGGL((apply_kernel<2, TA>), grid, dim3(256), 0, st, A, bs, Bm, out, ncols);
-  else if (nrt <= 4) hipLaunchKernelGGL((apply_kernel<4, TA>), grid, dim3(256), 0, st, A, bs, Bm, out, ncols);
-  else if (nrt <= 8) hipLaunchKernelGGL((apply_kernel<8, TA>), grid, dim3(256), 0, st, A, bs, Bm, out, ncols);
-  else hipLaunchKernelGGL((apply_kernel<16, TA>), grid, dim3(256), 0, st, A, bs, Bm, out, ncols);
+  if (nrt <= 1) hipLaunchKernelGGL((apply_kernel<1, TA>), grid, dim3(256), 0, st, A, bs, Bm, bunit, out, ncols);
+  else if (nrt <= 2) hipLaunchKernelGGL((apply_kernel<2, TA>), grid, dim3(256), 0, st, A, bs, Bm, bunit, out, ncols);
+  else if (nrt <= 4) hipLaunchKernelGGL((apply_kernel<4, TA>), grid, dim3(256), 0, st, A, bs, Bm, bunit, out, ncols);
+  else if (nrt <= 8) hipLaunchKernelGGL((apply_kernel<8, TA>), grid, dim3(256), 0, st, A, bs, Bm, bunit, out, ncols);
+  else hipLaunchKernelGGL((apply_kernel<16, TA>), grid, dim3(256), 0, st, A, bs, Bm, bunit, out, ncols);
 }
 
 // out (bs x ncols) = (G + eps I)^-1 in: one product with the inverse, or L^-T (L^-1 in) for
-// bs > kSpdMax; in and out may not alias
-static void solve(const BlockWs& w, int bs, const double* in, double* out, int ncols, hipStream_t st) {
+// bs > kSpdMax; in is a contraction's int64 output in units of *in_unit; in and out may not alias
+static void solve(const BlockWs& w, int bs, const long long* in, const double* in_unit, double* out, int ncols,
+                  hipStream_t st) {
   if (bs <= kSpdMax) {
     // two strips per workgroup once that still leaves a workgroup per CU or more
     const bool two = ncols >= 2 * 16 * 256;
     const dim3 grid(two ? (ncols + 31) / 32 : (ncols + 15) / 16);
     if (bs <= 64) {
-      if (two) hipLaunchKernelGGL((apply_strip_kernel<1, 16, 2>), grid, dim3(256), 0, st, w.Li, bs, in, out, ncols);
-      else hipLaunchKernelGGL((apply_strip_kernel<1, 16, 1>), grid, dim3(256), 0, st, w.Li, bs, in, out, ncols);
+      if (two) hipLaunchKernelGGL((apply_strip_kernel<1, 16, 2>), grid, dim3(256), 0, st, w.Li, bs, in, in_unit, out, ncols);
+      else hipLaunchKernelGGL((apply_strip_kernel<1, 16, 1>), grid, dim3(256), 0, st, w.Li, bs, in, in_unit, out, ncols);
     } else {
-      if (two) hipLaunchKernelGGL((apply_strip_kernel<2, 32, 2>), grid, dim3(256), 0, st, w.Li, bs, in, out, ncols);
-      else hipLaunchKernelGGL((apply_strip_kernel<2, 32, 1>), grid, dim3(256), 0, st, w.Li, bs, in, out, ncols);
+      if (two) hipLaunchKernelGGL((apply_strip_kernel<2, 32, 2>), grid, dim3(256), 0, st, w.Li, bs, in, in_unit, out, ncols);
+      else hipLaunchKernelGGL((apply_strip_kernel<2, 32, 1>), grid, dim3(256), 0, st, w.Li, bs, in, in_unit, out, ncols);
     }
     return;
   }
-  apply<false>(w.Li, bs, in, w.Tmp, ncols, st);
-  apply<true>(w.Li, bs, w.Tmp, out, ncols, st);
+  apply<false>(w.Li, bs, reinterpret_cast<const double*>(in), in_unit, w.Tmp, ncols, st);
+  apply<true>(w.Li, bs, w.Tmp, nullptr, out, ncols, st);
 }
 
-static void select_rows(const double* X, int L, int ldT, int bs, float tau, const float* h, int EHm, int8_t* T,
-                        double* PHC, int* flags, int flag_empty, hipStream_t st, double* Z0 = nullptr,
-                        int zlen = 0, const double* Yd = nullptr, double* Md = nullptr) {
+// X: fp64 rows, or with xunit a contraction's int64 rows; Yd/ydunit: the int64 output whose row
+// products with the selection give Md (see select_rows_kernel)
+static void select_rows(const double* X, const double* xunit, int L, int ldT, int bs, float tau, const float* h,
+                        int EHm, int8_t* T, double* PHC, int* flags, int flag_empty, hipStream_t st,
+                        double* Z0 = nullptr, int zlen = 0, const long long* Yd = nullptr,
+                        const double* ydunit = nullptr, double* Md = nullptr) {
+  const size_t dyn = xunit ? sizeof(float) * (size_t)L : 0;
   // long rows take 1024 threads (only bs workgroups run, so the CUs have room)
   if (L > 4096) {
     if (h)
-      hipLaunchKernelGGL((select_rows_kernel<true, 1024>), dim3(bs), dim3(1024), 0, st, X, L, ldT, tau, h, EHm, T,
-                         PHC, flags, flag_empty, Z0, zlen, Yd, Md);
+      hipLaunchKernelGGL((select_rows_kernel<true, 1024>), dim3(bs), dim3(1024), dyn, st, X, xunit, L, ldT, tau, h,
+                         EHm, T, PHC, flags, flag_empty, Z0, zlen, Yd, ydunit, Md);
     else
-      hipLaunchKernelGGL((select_rows_kernel<false, 1024>), dim3(bs), dim3(1024), 0, st, X, L, ldT, tau, h, EHm, T,
-                         PHC, flags, flag_empty, Z0, zlen, Yd, Md);
+      hipLaunchKernelGGL((select_rows_kernel<false, 1024>), dim3(bs), dim3(1024), dyn, st, X, xunit, L, ldT, tau, h,
+                         EHm, T, PHC, flags, flag_empty, Z0, zlen, Yd, ydunit, Md);
     return;
   }
   if (h)
-    hipLaunchKernelGGL((select_rows_kernel<true, 512>), dim3(bs), dim3(512), 0, st, X, L, ldT, tau, h, EHm, T, PHC,
-                       flags, flag_empty, Z0, zlen, Yd, Md);
+    hipLaunchKernelGGL((select_rows_kernel<true, 512>), dim3(bs), dim3(512), dyn, st, X, xunit, L, ldT, tau, h, EHm,
+                       T, PHC, flags, flag_empty, Z0, zlen, Yd, ydunit, Md);
   else
-    hipLaunchKernelGGL((select_rows_kernel<false, 512>), dim3(bs), dim3(512), 0, st, X, L, ldT, tau, h, EHm, T, PHC,
-                       flags, flag_empty, Z0, zlen, Yd, Md);
+    hipLaunchKernelGGL((select_rows_kernel<false, 512>), dim3(bs), dim3(512), dyn, st, X, xunit, L, ldT, tau, h, EHm,
+                       T, PHC, flags, flag_empty, Z0, zlen, Yd, ydunit, Md);
 }
 
 hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops, double* bytes) {
@@ -1797,6 +1868,13 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops, double
                                 (const void*)scales_kernel<3>, (const void*)scales_kernel<4>};
       for (const void* kf : kernels) {
         ea = hipFuncSetAttribute(kf, hipFuncAttributeMaxDynamicSharedMemorySize, (int)(96 * 1024));
+        if (ea != hipSuccess) return ea;
+      }
+      // the fp32 copy of an int64 row (up to 16384 values) beside the selection scratch
+      const void* sel[4] = {(const void*)select_rows_kernel<true, 1024>, (const void*)select_rows_kernel<false, 1024>,
+                            (const void*)select_rows_kernel<true, 512>, (const void*)select_rows_kernel<false, 512>};
+      for (const void* kf : sel) {
+        ea = hipFuncSetAttribute(kf, hipFuncAttributeMaxDynamicSharedMemorySize, (int)(64 * 1024));
         if (ea != hipSuccess) return ea;
       }
       scales_attr[dev] = true;
@@ -1837,15 +1915,18 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops, double
         if (addback && t == 0) gram_product(w, w.Ut, m, w.ldu, nullptr, 0, bs, w.GU, st);
         utr_product(L, w, bs, sblk, st, true);
         if (addback && t == 0) {
-          hipLaunchKernelGGL(addback_dot_kernel, dim3(bs), dim3(256), 0, st, w.X, n, w.Vt, w.ldv, L.h, w.ppo);
+          hipLaunchKernelGGL(addback_dot_kernel, dim3(bs), dim3(256), 0, st, w.Xi, w.unit, n, w.Vt, w.ldv, L.h,
+                             w.ppo);
           hipLaunchKernelGGL(addback_energy_kernel, dim3(1), dim3(256), 0, st, w.ppo, w.GU, w.GVo, L.D, k0, bs,
                              w.st, w.rmax + kMaxWords * ((sblk + 1) & 1), w.GUo);
         }
-        select_rows(w.X, n, w.ldv, bs, L.tau, hsel, ehsel, w.Vt, w.PHC, w.flags, 0, st, y0, m);
+        select_rows(w.X, w.unit, n, w.ldv, bs, L.tau, hsel, ehsel, w.Vt, w.PHC, w.flags, 0, st, y0, m);
         gram_product(w, w.Vt, n, w.ldv, L.h, L.EHm, bs, w.GV, st);  // for the scales
-        rw_product(L, w, L.h, bs, sblk, w.Yt, st, true);
-        select_rows(w.Yt, m, w.ldu, bs, L.tau, nullptr, 0, w.Ut, w.PHC, w.flags, 0, st, x0, n,
-                    t + 1 == L.T ? w.Yt : nullptr, t + 1 == L.T ? w.Md : nullptr);
+        rw_product(L, w, L.h, bs, sblk, w.Yi, st, true);
+        // the selection reads Yt while the last one also forms Md from it: Md reads the integers
+        // (the selection converts its own copy in LDS)
+        select_rows(w.Yt, w.unit + 1, m, w.ldu, bs, L.tau, nullptr, 0, w.Ut, w.PHC, w.flags, 0, st, x0, n,
+                    t + 1 == L.T ? w.Yi : nullptr, w.unit + 1, t + 1 == L.T ? w.Md : nullptr);
         fl += 4.0 * m * n * bs;
         by += 2.0 * rbytes;
         continue;
@@ -1862,24 +1943,25 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops, double
         utr_product(L, w, bs, sblk, st, true);
       }
       if (addback && t == 0) {
-        hipLaunchKernelGGL(addback_dot_kernel, dim3(bs), dim3(256), 0, st, w.X, n, w.Vt, w.ldv, L.h, w.ppo);
+        hipLaunchKernelGGL(addback_dot_kernel, dim3(bs), dim3(256), 0, st, w.Xi, w.unit, n, w.Vt, w.ldv, L.h,
+                           w.ppo);
         hipLaunchKernelGGL(addback_energy_kernel, dim3(1), dim3(256), 0, st, w.ppo, w.GU, w.GVo, L.D, k0, bs, w.st,
                            w.rmax + kMaxWords * ((sblk + 1) & 1), w.GUo);
       }
-      solve(w, bs, w.X, w.Z, n, st);
-      select_rows(w.Z, n, w.ldv, bs, L.tau, hsel, ehsel, w.Vt, w.PHC, w.flags, 0, st, y0, m);
+      solve(w, bs, w.Xi, w.unit, w.Z, n, st);
+      select_rows(w.Z, nullptr, n, w.ldv, bs, L.tau, hsel, ehsel, w.Vt, w.PHC, w.flags, 0, st, y0, m);
       // U-step: F^T = (V^T H V + eps I)^-1 (R H V)^T, columns ternarized without weights
       if (fused) {
         gram_product(w, w.Vt, n, w.ldv, L.h, L.EHm, bs, w.GV, st);
-        rw_product(L, w, L.h, bs, sblk, w.Yt, st, true, w.GV, w.Li);
+        rw_product(L, w, L.h, bs, sblk, w.Yi, st, true, w.GV, w.Li);
       } else {
         gram_product(w, w.Vt, n, w.ldv, L.h, L.EHm, bs, w.GV, st);
         chol_inverse(w, w.GV, bs, st);
-        rw_product(L, w, L.h, bs, sblk, w.Yt, st, true);
+        rw_product(L, w, L.h, bs, sblk, w.Yi, st, true);
       }
-      solve(w, bs, w.Yt, w.Ft, m, st);
-      select_rows(w.Ft, m, w.ldu, bs, L.tau, nullptr, 0, w.Ut, w.PHC, w.flags, 0, st, x0, n,
-                  t + 1 == L.T ? w.Yt : nullptr, t + 1 == L.T ? w.Md : nullptr);
+      solve(w, bs, w.Yi, w.unit + 1, w.Ft, m, st);
+      select_rows(w.Ft, nullptr, m, w.ldu, bs, L.tau, nullptr, 0, w.Ut, w.PHC, w.flags, 0, st, x0, n,
+                  t + 1 == L.T ? w.Yi : nullptr, w.unit + 1, t + 1 == L.T ? w.Md : nullptr);
       fl += 4.0 * m * n * bs;
       by += 2.0 * rbytes;
     }
@@ -1912,8 +1994,8 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops, double
     // sketch
     hipLaunchKernelGGL(omega_kernel, dim3(256), dim3(256), 0, st, w.Vt, w.ldv, bs, n, (long long)s, w.flags,
                        w.rmax, w.Yt, rw_splits(L, bs) ? (long long)bs * m : 0ll);
-    rw_product(L, w, nullptr, bs, s, w.Yt, st, true);
-    select_rows(w.Yt, m, w.ldu, bs, L.tau, nullptr, 0, w.Ut, w.PHC, w.flags, 1, st,
+    rw_product(L, w, nullptr, bs, s, w.Yi, st, true);
+    select_rows(w.Yt, w.unit + 1, m, w.ldu, bs, L.tau, nullptr, 0, w.Ut, w.PHC, w.flags, 1, st,
                 utr_splits(L, bs) ? w.X : nullptr, n);
     hipLaunchKernelGGL(zero_check_kernel, dim3(1), dim3(256), 0, st, L.R, L.ldr, m, n, w.flags, w.st);
     hipLaunchKernelGGL(fallback_kernel, dim3(1), dim3(512), 0, st, L.R, L.ldr, m, n, bs, w.Ut, w.ldu, w.PHC,
