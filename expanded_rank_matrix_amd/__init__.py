@@ -82,6 +82,8 @@ def load():
         lib.externd_matvec.argtypes = [vp, i64, i64, vp, vp, ci, vp, vp]
         lib.externd_apply_factors.restype = ci
         lib.externd_apply_factors.argtypes = [vp, vp, vp, i64, i64, i64, vp, i64, vp, vp]
+        lib.externd_apply_factors_static.restype = ci
+        lib.externd_apply_factors_static.argtypes = [vp, vp, vp, i64, i64, i64, vp, i64, vp, vp]
         lib.externd_status_string.restype = ctypes.c_char_p
         lib.externd_status_string.argtypes = [ci]
         lib.externd_last_error.restype = ctypes.c_char_p
@@ -231,6 +233,32 @@ def apply_factors(B, C, D, m: int, n: int, X, stream=None, out=None):
     Y = out if out is not None else torch.empty((X2.shape[0], m), dtype=torch.float32, device=X.device)
     rc = load().externd_apply_factors(_dev_ptr(B), _dev_ptr(C), _dev_ptr(D), k, m, n, _dev_ptr(X2),
                                       X2.shape[0], _dev_ptr(Y), _stream_ptr(stream))
+    _check(rc)
+    return Y[0] if single else Y
+
+
+def apply_factors_static(B, C, D, m: int, n: int, X, stream=None, out=None):
+    """externd_apply_factors_static: as apply_factors, with the library's fixed per-GPU workspace
+    (no device allocation) and without waiting for the stream; synchronise before reading Y."""
+    import torch
+
+    D = _require(D, torch.float32, "D")
+    X = _require(X, torch.float32, "X")
+    for t, name in ((B, "B"), (C, "C")):
+        if not (t.is_cuda and t.dtype in (torch.int32, torch.uint32) and t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous 32-bit CUDA tensor of packed words")
+    k = D.shape[0]
+    if B.shape != (k, packed_words(m)) or C.shape != (k, packed_words(n)):
+        raise ValueError("B, C must be k x packed_words(m), k x packed_words(n)")
+    single = X.dim() == 1
+    X2 = X.reshape(1, -1) if single else X
+    if X2.shape[1] != n:
+        raise ValueError("X must have n columns")
+    Y = out if out is not None else torch.empty((X2.shape[0], m), dtype=torch.float32, device=X.device)
+    if Y.dtype != torch.float32 or not Y.is_contiguous() or Y.numel() != X2.shape[0] * m:
+        raise ValueError("out must be a contiguous fp32 tensor of batch x m values")
+    rc = load().externd_apply_factors_static(_dev_ptr(B), _dev_ptr(C), _dev_ptr(D), k, m, n, _dev_ptr(X2),
+                                             X2.shape[0], _dev_ptr(Y), _stream_ptr(stream))
     _check(rc)
     return Y[0] if single else Y
 

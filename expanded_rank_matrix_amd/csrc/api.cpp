@@ -376,6 +376,25 @@ int externd_apply_factors(const uint32_t* B_packed, const uint32_t* C_packed, co
   return EXTERND_OK;
 }
 
+int externd_apply_factors_static(const uint32_t* B_packed, const uint32_t* C_packed, const float* D, int64_t k,
+                                 int64_t m, int64_t n, const float* X, int64_t batch, float* Y, void* stream) {
+  g_last_error.clear();
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (!B_packed || !C_packed || !D || !X || !Y) return fail(EXTERND_EINVAL, "null pointer argument");
+  if (k < 1 || k > 2147483647 || m < 1 || n < 1 || m > 2147483647 - 15 || n > 2147483647 - 15)
+    return fail(EXTERND_EINVAL, "need k, m, n >= 1 (and below 2^31)");
+  if (batch < 1 || batch > 65535) return fail(EXTERND_EINVAL, "need 1 <= batch <= 65535");
+  const size_t need = infer_workspace_bytes((int)k, (int)m, (int)batch);
+  if (need > kInferStaticBytes)
+    return fail(EXTERND_EINVAL,
+                "batch x (k + m) too large for the fixed workspace: needs %zu bytes, the limit is %zu "
+                "(8 batch (k + m) bytes + 8 KiB)", need, kInferStaticBytes);
+  void* ws = nullptr;
+  HIP_OR_FAIL(infer_static_scratch(&ws));
+  HIP_OR_FAIL(infer_run(B_packed, C_packed, D, (int)k, (int)m, (int)n, X, (int)batch, Y, ws, st));
+  return EXTERND_OK;
+}
+
 int externd_matvec(const float* R, int64_t m, int64_t n, const int8_t* t, const float* h, int transpose, double* out,
                    void* stream) {
   g_last_error.clear();

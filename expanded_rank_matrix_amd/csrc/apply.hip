@@ -10,6 +10,8 @@
 // t_i is an fp64 sum in a fixed order; y is exact for the fixed-point s (one unit is
 // 2^(E + ceil(log2(k + 1)) - 62) for max |s| < 2^E, below 2^-46 of it) and rounded once to fp32.
 // Both are deterministic.
+#include <mutex>
+
 #include "common.hpp"
 #include "externd_internal.hpp"
 
@@ -190,6 +192,31 @@ hipError_t infer_run(const uint32_t* B, const uint32_t* C, const float* D, int k
   hipLaunchKernelGGL(infer_fin_kernel, dim3((unsigned)(nb < 4096 ? nb : 4096)), dim3(256), 0, st, Yacc, nY, k, smax,
                      Y);
   return hipGetLastError();
+}
+
+// ---- allocation-free inference: the workspace in a file-scope device array -------------------
+// One array per GPU, held until the process ends.  Host code never passes `scratch` itself to a
+// kernel (in host code the name is a host-side stand-in); it passes the device address that
+// hipGetSymbolAddress returns, fetched once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[kInferStaticBytes];
+
+hipError_t infer_static_scratch(void** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 }  // namespace externd

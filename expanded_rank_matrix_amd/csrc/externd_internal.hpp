@@ -82,6 +82,10 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops, double
 
 // Inference from the packed factors (apply.hip)
 size_t infer_workspace_bytes(int k, int m, int batch);
+// size of the file-scope inference workspace of each GPU (allocation-free entry point)
+constexpr size_t kInferStaticBytes = (size_t)16 << 20;
+// device address of this GPU's file-scope inference workspace (kInferStaticBytes bytes)
+hipError_t infer_static_scratch(void** ptr);
 hipError_t infer_run(const uint32_t* B, const uint32_t* C, const float* D, int k, int m, int n, const float* X,
                      int batch, float* Y, void* ws, hipStream_t st);
 

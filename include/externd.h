@@ -171,6 +171,20 @@ int externd_matvec(const float* R, int64_t m, int64_t n, const int8_t* t, const 
 int externd_apply_factors(const uint32_t* B_packed, const uint32_t* C_packed, const float* D, int64_t k,
                           int64_t m, int64_t n, const float* X, int64_t batch, float* Y, void* stream);
 
+/* externd_apply_factors for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same arguments, arithmetic and
+ * results (bit for bit) as externd_apply_factors, but the workspace is a fixed 16 MiB device
+ * array inside the library, one per GPU, held until the process ends; the call allocates and frees
+ * nothing.  Limit: 8 * batch * (k + m) bytes (rounded up to 256 twice) + 8 KiB must fit in the
+ * 16 MiB, else EXTERND_EINVAL (batch 1: k + m up to about 2 million; k = 7680, m = 2560: batch up
+ * to 204).  The call only enqueues its kernels on `stream` and returns without waiting; the caller
+ * synchronises the stream before reading Y.  Every call on one GPU uses that GPU's array (the
+ * kernels clear what must start at zero), so calls that may overlap on one GPU (different streams,
+ * threads) race: serialise them on one stream.  EXTERND_EINVAL for bad sizes or null pointers,
+ * EXTERND_EDEVICE for HIP errors. */
+int externd_apply_factors_static(const uint32_t* B_packed, const uint32_t* C_packed, const float* D, int64_t k,
+                                 int64_t m, int64_t n, const float* X, int64_t batch, float* Y, void* stream);
+
 /* Human-readable name of a status code (static string). */
 const char* externd_status_string(int status);
 
