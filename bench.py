@@ -6,6 +6,8 @@ already resident in HBM.  Default workload: the attention-projection case, A 256
 iterations, sequential deflation.  Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+    python bench.py --probe            # sustained read / copy bandwidth at 26 MB, 100 MB, 1 GB
+    python bench.py --oracle-timings   # the oracle on one and on all host cores (small workloads)
 """
 
 from __future__ import annotations
@@ -70,27 +72,116 @@ def copy_probe(megabytes):
     log(f"copy probe: {megabytes} MiB read + {megabytes} MiB written")
 
 
-def cpu_baseline(A, c, seconds_target=15.0):
-    """The oracle as it stands on the host cores, over a bounded prefix of the same workload."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def oracle_rate(A, h, c, threads, seconds_target):
+    """Components/s of the oracle on `threads` host threads over a prefix of the workload sized for
+    about seconds_target (calibrated on a short prefix)."""
     import oracle
 
-    threads = min(len(os.sched_getaffinity(0)), 16)
     block = c["block"]
-    # calibrate on a short prefix, then run a prefix sized for ~seconds_target
     k_cal = 8 if block in (0, 1) else c["block"]
     t0 = time.perf_counter()
-    oracle.decompose(A, c["mu"], c["tau"], None, c["als_iters"], block, threads=threads, k_limit=k_cal)
-    dt = time.perf_counter() - t0
-    per = dt / k_cal
+    oracle.decompose(A, c["mu"], c["tau"], h, c["als_iters"], block, threads=threads, k_limit=k_cal)
+    per = (time.perf_counter() - t0) / k_cal
     k_s = int(max(k_cal, min(4096, seconds_target / max(per, 1e-9))))
     if block not in (0, 1):
         k_s = max(block, (k_s // block) * block)
     t0 = time.perf_counter()
-    r = oracle.decompose(A, c["mu"], c["tau"], None, c["als_iters"], block, threads=threads, k_limit=k_s)
+    r = oracle.decompose(A, c["mu"], c["tau"], h, c["als_iters"], block, threads=threads, k_limit=k_s)
     dt = time.perf_counter() - t0
     done = len(r["D"])
-    return {"value": done / dt, "unit": "components/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {done} components of the same workload ({dt:.1f} s wall)"}
+    return done / dt, done, dt
+
+
+def cpu_baseline(A, h, c, seconds_target=15.0):
+    """The oracle as it stands on the host cores, over a bounded prefix of the same workload (the
+    same weights as the GPU run)."""
+    threads = min(len(os.sched_getaffinity(0)), 16)
+    v, done, dt = oracle_rate(A, h, c, threads, seconds_target)
+    return {"value": v, "unit": "components/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {done} components of the same workload ({dt:.1f} s wall)",
+            "cpu_model": cpu_model()}
+
+
+def oracle_timings():
+    """The plain oracle single-threaded and on all host cores (up to 16) on the small workloads and
+    on a prefix of the 2560 x 2560 one; one JSON line."""
+    from expanded_rank_matrix_amd import inputs
+
+    cores = min(len(os.sched_getaffinity(0)), 16)
+    rows = []
+    for name, budget in (("tiny64x48", 5.0), ("lowrank1024", 20.0), ("attn2560", 20.0)):
+        c = inputs.CONFIGS[name]
+        A, h = inputs.make_input(name)
+        for threads in (1, cores):
+            v, done, dt = oracle_rate(A, h, c, threads, budget)
+            rows.append({"workload": name, "threads": threads, "components_per_s": v, "components": done,
+                         "seconds": dt})
+            log(f"oracle {name} threads={threads}: {v:.1f} components/s over {done} components ({dt:.1f} s)")
+    print(json.dumps({"oracle_timings": rows, "cpu_model": cpu_model(), "cores": cores}), flush=True)
+
+
+def bandwidth_probe():
+    """Sustained read and copy bandwidth of buffers inside and beyond the 256 MB Infinity Cache
+    (26 MB is the 2560 x 2560 residual, 100 MB the 9728 x 2560 one): a sum reads the buffer once, a
+    copy reads and writes it.  Repeated back to back, a buffer that fits stays in the cache."""
+    import torch
+
+    out = []
+    for mb in (26, 100, 1024):
+        n = mb * (1 << 20) // 4
+        x = torch.randn(n, dtype=torch.float32, device="cuda")
+        y = torch.empty_like(x)
+        reps = max(20, int(4096 / mb))
+        for _ in range(3):
+            x.sum()
+            y.copy_(x)
+        torch.cuda.synchronize()
+        res = {"MB": mb}
+        for kind in ("read", "copy"):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                if kind == "read":
+                    x.sum()
+                else:
+                    y.copy_(x)
+            e1.record()
+            torch.cuda.synchronize()
+            sec = e0.elapsed_time(e1) * 1e-3 / reps
+            nbytes = 4.0 * n * (1 if kind == "read" else 2)
+            res[kind + "_GBps"] = nbytes / sec / 1e9
+        log(f"probe {mb} MB: read {res['read_GBps']:.0f} GB/s, copy {res['copy_GBps']:.0f} GB/s")
+        out.append(res)
+        del x, y
+    print(json.dumps({"bandwidth_probe": out, "note": "torch sum (read once) and copy_ (read + write), "
+                      "buffers repeated back to back; 26 and 100 MB fit the 256 MB Infinity Cache"}), flush=True)
+
+
+def factor_sparsity(out, m, n):
+    """Zero fractions of B and C and the effective bits per weight of the mask+sign storage,
+    (m k (2 - s_B) + k n (2 - s_C)) / (m n), D absorbed (pith.science free parameters, Eq. 5);
+    counted on the host from the emitted packed factors."""
+    def zeros(packed, length):
+        # a 2-bit code is nonzero iff either of its bits is set; tail codes are zero by the format
+        w = packed.cpu().numpy().view(np.uint32)
+        nonzero = int(np.bitwise_count((w | (w >> np.uint32(1))) & np.uint32(0x55555555)).sum())
+        return w.shape[0] * length - nonzero
+    k = out["D"].shape[0]
+    sB = zeros(out["B"], m) / (m * k)
+    sC = zeros(out["C"], n) / (k * n)
+    bpw = (m * k * (2.0 - sB) + k * n * (2.0 - sC)) / (m * n)
+    return {"zero_fraction_B": sB, "zero_fraction_C": sC, "bpw": bpw, "bpw_with_D": bpw + 32.0 * k / (m * n)}
 
 
 def infer_bench(args, erm, torch, A, h, c, k, m, n, out, stream):
@@ -157,7 +248,14 @@ def main():
     ap.add_argument("--mu", type=float, default=None, help="override the workload's mu")
     ap.add_argument("--ablation", type=int, default=0,
                     help="1: block targets without decorrelation, 2: unweighted V-step projection")
+    ap.add_argument("--residual-hbm", action="store_true",
+                    help="sequential path: keep the residual in HBM even where it fits in LDS")
+    ap.add_argument("--probe", action="store_true", help="bandwidth probe only")
+    ap.add_argument("--oracle-timings", action="store_true", help="oracle timings only (host)")
     args = ap.parse_args()
+    if args.oracle_timings:
+        oracle_timings()
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this build runs the "
               "decomposition on a single MI355X", file=sys.stderr)
@@ -168,6 +266,9 @@ def main():
     import expanded_rank_matrix_amd as erm
     from expanded_rank_matrix_amd import inputs
 
+    if args.probe:
+        bandwidth_probe()
+        return
     if args.copy_mb > 0:
         copy_probe(args.copy_mb)
     c = dict(inputs.CONFIGS[args.workload])
@@ -176,7 +277,7 @@ def main():
     if args.mu is not None:
         c["mu"] = args.mu
     options = dict(energy_target=args.energy_target, safeguard=args.safeguard, sweeps=args.sweeps,
-                   ablation=args.ablation)
+                   ablation=args.ablation, residual_hbm=args.residual_hbm)
     # not the workload as defined
     variant = any(options.values()) or args.block is not None or args.mu is not None
     A_np, h_np = inputs.make_input(args.workload)
@@ -214,10 +315,17 @@ def main():
     traffic = None if variant else measured_traffic(args.workload)
     if c["block"] in (0, 1):
         achieved = stats["bytes_algorithmic"] / (kms * 1e-3) / 1e9
+        lds = bool(stats["residual_lds"])
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
                 "kernel": "seq_kernel (persistent)", "kernel_ms": kms,
-                "bytes_per_launch": stats["bytes_algorithmic"]}
+                "bytes_per_launch": stats["bytes_algorithmic"],
+                "achieved_is": "algorithmic residual bytes / kernel time (the effective rate)",
+                "residual_served_by": ("R rows from each workgroup's LDS, R^T from L2/HBM" if lds
+                                       else "R and R^T from L2/HBM"),
+                "limiter": "latency: 2T + 1 dependent grid-wide exchanges and exact selections per component"}
+        if traffic is not None:
+            roof["counter_GBps"] = traffic / (kms * 1e-3) / 1e9
     else:
         # The block path's contractions run on int8 MFMA with R in fixed point; they stream R once
         # each, so the bound is HBM.  The fp64-equivalent rate of the same work is reported beside.
@@ -243,8 +351,10 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "m": m, "n": n, "mu": c["mu"], "k": k, "tau": c["tau"],
                    "als_iters": c["als_iters"], "block": c["block"],
-                   "residual": ("fp32 in HBM, fp64 accumulation" if c["block"] in (0, 1) else
-                                "fp32 in HBM; contractions exact on its 32-bit fixed-point image (int8 MFMA)"),
+                   "residual": (("fp32, rows resident in each workgroup's LDS, transpose in HBM; fp64 sums"
+                                 if stats["residual_lds"] else "fp32 in HBM (both copies); fp64 sums")
+                                if c["block"] in (0, 1) else
+                                "fp32 in HBM; contractions exact on its 48-bit fixed-point image (int8 MFMA)"),
                    "energy_final": float(energy[-1]),
                    "passes": stats["passes"], "early_exits": stats["early_exits"]},
         "roofline": roof,
@@ -255,8 +365,12 @@ def main():
         res["config"]["fits_per_decomposition"] = fits
         res["config"]["safeguard_activations"] = stats["safeguard_activations"]
         res["config"]["sweep_reverts"] = stats["sweep_reverts"]
+    if c["block"] not in (0, 1):
+        res["config"].update(factor_sparsity(out, m, n))
+    if c["block"] in (0, 1) and k >= 256:
+        res["config"]["energy_every_256"] = [float(energy[i]) for i in range(255, k, 256)]
     if not args.no_cpu and not variant:
-        res["cpu_baseline"] = cpu_baseline(A_np, c)
+        res["cpu_baseline"] = cpu_baseline(A_np, h_np, c)
     print(json.dumps(res), flush=True)
 
 

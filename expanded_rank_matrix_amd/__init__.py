@@ -42,6 +42,7 @@ class Stats(ctypes.Structure):
         ("components_used", ctypes.c_int64),
         ("safeguard_activations", ctypes.c_int64),
         ("sweep_reverts", ctypes.c_int64),
+        ("residual_lds", ctypes.c_int64),
     ]
 
     def as_dict(self):
@@ -54,6 +55,7 @@ class Options(ctypes.Structure):
         ("safeguard", ctypes.c_int),
         ("sweeps", ctypes.c_int),
         ("ablation", ctypes.c_int),
+        ("residual_hbm", ctypes.c_int),
     ]
 
 
@@ -124,19 +126,25 @@ def _stream_ptr(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _require(t, dtype, name):
-    import torch
-
+def _require(t, dtype, name, shape=None, device=None):
+    """t as the C ABI will read or write it: a contiguous CUDA tensor of ``dtype`` (any of them
+    when a tuple), on ``device`` and of exactly ``shape`` when given.  The library gets raw
+    pointers and sizes, so a short or mistyped buffer would be read or written out of bounds."""
     if t is None:
         return None
-    if not (t.is_cuda and t.dtype == dtype and t.is_contiguous()):
-        raise ValueError(f"{name} must be a contiguous {dtype} CUDA tensor")
+    dtypes = dtype if isinstance(dtype, tuple) else (dtype,)
+    if not (t.is_cuda and t.dtype in dtypes and t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous CUDA tensor of {' or '.join(map(str, dtypes))}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     return t
 
 
 def decompose(A, mu: float, tau: float = 0.0, h=None, als_iters: int = 4, block: int = 1,
               stream=None, out=None, energy_target: float = 0.0, safeguard: bool = False,
-              sweeps: int = 0, ablation: int = 0):
+              sweeps: int = 0, ablation: int = 0, residual_hbm: bool = False):
     """Run externd_decompose (externd_decompose_ex when an option is set) on a device fp32
     matrix A (m x n).
 
@@ -146,16 +154,19 @@ def decompose(A, mu: float, tau: float = 0.0, h=None, als_iters: int = 4, block:
     the first component whose energy reaches it (stats["components_used"]); ``safeguard`` turns
     on the best single-entry safeguard (sequential path); ``sweeps`` refinement sweeps refit
     every component after the greedy pass; ``ablation`` switches parts of the method off for
-    ablation studies (1: block targets without decorrelation, 2: unweighted V-step projection)."""
+    ablation studies (1: block targets without decorrelation, 2: unweighted V-step projection);
+    ``residual_hbm`` keeps the sequential path's residual in HBM even where it fits in LDS."""
     import torch
 
     A = _require(A, torch.float32, "A")
-    h = _require(h, torch.float32, "h")
+    if A.dim() != 2:
+        raise ValueError("A must be a 2-d matrix")
     m, n = A.shape
+    dev = A.device
+    h = _require(h, torch.float32, "h", shape=(n,), device=dev)
     k = rank(m, n, mu)
     if k < 1:
         raise ExterndError(EINVAL, "mu gives k < 1")
-    dev = A.device
     if out is None:
         out = dict(
             B=torch.empty((k, packed_words(m)), dtype=torch.int32, device=dev),
@@ -163,9 +174,15 @@ def decompose(A, mu: float, tau: float = 0.0, h=None, als_iters: int = 4, block:
             D=torch.empty(k, dtype=torch.float32, device=dev),
             energy=torch.empty(k, dtype=torch.float64, device=dev),
         )
+    words32 = (torch.int32, torch.uint32)
+    _require(out["B"], words32, "out['B']", shape=(k, packed_words(m)), device=dev)
+    _require(out["C"], words32, "out['C']", shape=(k, packed_words(n)), device=dev)
+    _require(out["D"], torch.float32, "out['D']", shape=(k,), device=dev)
+    _require(out["energy"], torch.float64, "out['energy']", shape=(k,), device=dev)
     st = Stats()
-    if energy_target or safeguard or sweeps or ablation:
-        opt = Options(float(energy_target), int(bool(safeguard)), int(sweeps), int(ablation))
+    if energy_target or safeguard or sweeps or ablation or residual_hbm:
+        opt = Options(float(energy_target), int(bool(safeguard)), int(sweeps), int(ablation),
+                      int(bool(residual_hbm)))
         rc = load().externd_decompose_ex(_dev_ptr(A), m, n, mu, tau, _dev_ptr(h), als_iters, block,
                                          _dev_ptr(out["B"]), _dev_ptr(out["C"]),
                                          _dev_ptr(out["D"]), _dev_ptr(out["energy"]),
@@ -188,8 +205,10 @@ def project(X, tau: float = 0.0, h=None, stream=None):
     import torch
 
     X = _require(X, torch.float32, "X")
-    h = _require(h, torch.float32, "h")
+    if X.dim() != 2:
+        raise ValueError("X must be count x L")
     count, L = X.shape
+    h = _require(h, torch.float32, "h", shape=(L,), device=X.device)
     V = torch.empty((count, L), dtype=torch.int8, device=X.device)
     PHC = torch.empty((count, 3), dtype=torch.float64, device=X.device)
     rc = load().externd_project(_dev_ptr(X), count, L, tau, _dev_ptr(h), _dev_ptr(V), _dev_ptr(PHC),
@@ -203,9 +222,13 @@ def matvec(R, t, h=None, transpose: bool = False, stream=None):
     import torch
 
     R = _require(R, torch.float32, "R")
-    t = _require(t, torch.int8, "t")
-    h = _require(h, torch.float32, "h")
+    if R.dim() != 2:
+        raise ValueError("R must be a 2-d matrix")
     m, n = R.shape
+    t = _require(t, torch.int8, "t", shape=(m if transpose else n,), device=R.device)
+    if h is not None and transpose:
+        raise ValueError("h weights the U-step product R (h .* t) only")
+    h = _require(h, torch.float32, "h", shape=(n,), device=R.device)
     out = torch.empty(n if transpose else m, dtype=torch.float64, device=R.device)
     rc = load().externd_matvec(_dev_ptr(R), m, n, _dev_ptr(t), _dev_ptr(h), int(transpose),
                                _dev_ptr(out), _stream_ptr(stream))
@@ -213,54 +236,48 @@ def matvec(R, t, h=None, transpose: bool = False, stream=None):
     return out
 
 
-def apply_factors(B, C, D, m: int, n: int, X, stream=None, out=None):
-    """Y = (B diag(D) C X^T)^T from packed factors (as returned by decompose) for X (n or batch x n,
-    fp32, device); returns Y (m or batch x m, fp32)."""
+def _apply_args(B, C, D, m, n, X, out):
+    """Validated (B, C, D, k, X2, Y, single) for the inference entry points."""
     import torch
 
     D = _require(D, torch.float32, "D")
-    X = _require(X, torch.float32, "X")
-    for t, name in ((B, "B"), (C, "C")):
-        if not (t.is_cuda and t.dtype in (torch.int32, torch.uint32) and t.is_contiguous()):
-            raise ValueError(f"{name} must be a contiguous 32-bit CUDA tensor of packed words")
+    if D.dim() != 1:
+        raise ValueError("D must be a vector of k scales")
     k = D.shape[0]
-    if B.shape != (k, packed_words(m)) or C.shape != (k, packed_words(n)):
-        raise ValueError("B, C must be k x packed_words(m), k x packed_words(n)")
+    dev = D.device
+    words32 = (torch.int32, torch.uint32)
+    _require(B, words32, "B", shape=(k, packed_words(m)), device=dev)
+    _require(C, words32, "C", shape=(k, packed_words(n)), device=dev)
+    X = _require(X, torch.float32, "X", device=dev)
     single = X.dim() == 1
     X2 = X.reshape(1, -1) if single else X
-    if X2.shape[1] != n:
-        raise ValueError("X must have n columns")
-    Y = out if out is not None else torch.empty((X2.shape[0], m), dtype=torch.float32, device=X.device)
+    if X2.dim() != 2 or X2.shape[1] != n:
+        raise ValueError("X must be n or batch x n")
+    Y = out if out is not None else torch.empty((X2.shape[0], m), dtype=torch.float32, device=dev)
+    _require(Y, torch.float32, "out", device=dev)
+    if Y.numel() != X2.shape[0] * m:
+        raise ValueError("out must hold batch x m values")
+    return B, C, D, k, X2, Y, single
+
+
+def apply_factors(B, C, D, m: int, n: int, X, stream=None, out=None):
+    """Y = (B diag(D) C X^T)^T from packed factors (as returned by decompose) for X (n or batch x n,
+    fp32, device); returns Y (m or batch x m, fp32)."""
+    B, C, D, k, X2, Y, single = _apply_args(B, C, D, m, n, X, out)
     rc = load().externd_apply_factors(_dev_ptr(B), _dev_ptr(C), _dev_ptr(D), k, m, n, _dev_ptr(X2),
                                       X2.shape[0], _dev_ptr(Y), _stream_ptr(stream))
     _check(rc)
-    return Y[0] if single else Y
+    return Y[0] if single else Y.reshape(X2.shape[0], m)
 
 
 def apply_factors_static(B, C, D, m: int, n: int, X, stream=None, out=None):
     """externd_apply_factors_static: as apply_factors, with the library's fixed per-GPU workspace
     (no device allocation) and without waiting for the stream; synchronise before reading Y."""
-    import torch
-
-    D = _require(D, torch.float32, "D")
-    X = _require(X, torch.float32, "X")
-    for t, name in ((B, "B"), (C, "C")):
-        if not (t.is_cuda and t.dtype in (torch.int32, torch.uint32) and t.is_contiguous()):
-            raise ValueError(f"{name} must be a contiguous 32-bit CUDA tensor of packed words")
-    k = D.shape[0]
-    if B.shape != (k, packed_words(m)) or C.shape != (k, packed_words(n)):
-        raise ValueError("B, C must be k x packed_words(m), k x packed_words(n)")
-    single = X.dim() == 1
-    X2 = X.reshape(1, -1) if single else X
-    if X2.shape[1] != n:
-        raise ValueError("X must have n columns")
-    Y = out if out is not None else torch.empty((X2.shape[0], m), dtype=torch.float32, device=X.device)
-    if Y.dtype != torch.float32 or not Y.is_contiguous() or Y.numel() != X2.shape[0] * m:
-        raise ValueError("out must be a contiguous fp32 tensor of batch x m values")
+    B, C, D, k, X2, Y, single = _apply_args(B, C, D, m, n, X, out)
     rc = load().externd_apply_factors_static(_dev_ptr(B), _dev_ptr(C), _dev_ptr(D), k, m, n, _dev_ptr(X2),
                                              X2.shape[0], _dev_ptr(Y), _stream_ptr(stream))
     _check(rc)
-    return Y[0] if single else Y
+    return Y[0] if single else Y.reshape(X2.shape[0], m)
 
 
 def unpack(packed, length: int) -> np.ndarray:
@@ -276,16 +293,3 @@ def unpack(packed, length: int) -> np.ndarray:
     out[codes == 1] = 1
     out[codes == 3] = -1
     return out
-
-
-def sparsity_and_bpw(B_packed, C_packed, m: int, n: int):
-    """Zero fractions of B and C and the effective bits per weight of the mask+sign storage
-    model, (m k (2 - s_B) + k n (2 - s_C)) / (m n), the pages' Eq. 5 accounting with D absorbed
-    (pith.science free parameters, Eq. 5)."""
-    U = unpack(B_packed, m)
-    V = unpack(C_packed, n)
-    k = U.shape[0]
-    sB = 1.0 - np.count_nonzero(U) / (m * k)
-    sC = 1.0 - np.count_nonzero(V) / (k * n)
-    bpw = (m * k * (2.0 - sB) + k * n * (2.0 - sC)) / (m * n)
-    return sB, sC, bpw

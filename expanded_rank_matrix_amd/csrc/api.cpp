@@ -105,7 +105,9 @@ int externd_decompose_ex(const float* A, int64_t m, int64_t n, float mu, float t
   const int safeguard = options ? options->safeguard : 0;
   const int sweeps = options ? options->sweeps : 0;
   const int ablation = options ? options->ablation : 0;
+  const int residual_hbm = options ? options->residual_hbm : 0;
   if (ablation & ~3) return fail(EXTERND_EINVAL, "ablation must be a combination of 1 and 2");
+  if (residual_hbm != 0 && residual_hbm != 1) return fail(EXTERND_EINVAL, "residual_hbm must be 0 or 1");
   if (sweeps < 0 || sweeps > 64) return fail(EXTERND_EINVAL, "sweeps must be in [0, 64]");
   if (!(target == 0.0 || (target > 0.0 && target <= 1.0)))
     return fail(EXTERND_EINVAL, "energy_target must be 0 (off) or in (0, 1]");
@@ -153,7 +155,7 @@ int externd_decompose_ex(const float* A, int64_t m, int64_t n, float mu, float t
     HIP_OR_FAIL(hipGetDevice(&dev));
     int ncu = 0;
     HIP_OR_FAIL(hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev));
-    if (!seq_plan(mi, ni, h != nullptr, ncu, &grid, &rl))
+    if (!seq_plan(mi, ni, h != nullptr, ncu, residual_hbm == 0, &grid, &rl))
       return fail(EXTERND_EINVAL, "problem too large for the sequential kernel's on-chip state (%d x %d)", mi, ni);
     o_xf = take((size_t)4 * grid * sizeof(double));
     o_rsg = take((size_t)grid * mi * sizeof(double));
@@ -311,6 +313,7 @@ int externd_decompose_ex(const float* A, int64_t m, int64_t n, float mu, float t
     stats->components_used = hst[5] > 0 ? (int64_t)hst[5] : k;
     stats->safeguard_activations = (int64_t)hst[4];
     stats->sweep_reverts = (int64_t)hst[6];
+    stats->residual_lds = rl ? 1 : 0;
     stats->seconds = std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count();
   }
   return EXTERND_OK;

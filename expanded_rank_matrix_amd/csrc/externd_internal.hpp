@@ -35,9 +35,9 @@ struct SeqLaunch {
   int ablation = 0;     // 2: the V-step projection ignores the weights
 };
 size_t seq_smem_bytes(int m, int n, bool weighted, int G, bool rl);
-// Grid size (one workgroup per CU at most) and whether the R slab fits in LDS; 0 if the problem
-// does not fit the kernel's on-chip state.
-int seq_plan(int m, int n, bool weighted, int ncu, int* grid, bool* rl);
+// Grid size (one workgroup per CU at most) and whether the R slab is held in LDS (only where it
+// fits and allow_rl); 0 if the problem does not fit the kernel's on-chip state.
+int seq_plan(int m, int n, bool weighted, int ncu, bool allow_rl, int* grid, bool* rl);
 hipError_t seq_launch(const SeqLaunch& L, hipStream_t st);
 // out[r] = R_r . (t .* h) for rows of a padded row-major matrix; t (and h, nullable) padded to
 // len4 * 4 entries.  Same slab routine as the sequential kernel.

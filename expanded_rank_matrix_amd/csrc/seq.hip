@@ -992,10 +992,10 @@ static int coresident_one(size_t smem) {
 
 constexpr size_t kLdsBytes = 160 * 1024;
 
-int seq_plan(int m, int n, bool weighted, int ncu, int* grid, bool* rl) {
+int seq_plan(int m, int n, bool weighted, int ncu, bool allow_rl, int* grid, bool* rl) {
   const int want = (int)std::max<long long>(1, std::min<long long>(ncu, ((long long)std::max(m, n) + 7) / 8));
-  // the R slab in LDS when it fits (one workgroup per CU)
-  const bool try_rl = !weighted && seq_smem_bytes(m, n, weighted, want, true) <= kLdsBytes;
+  // the R slab in LDS when it fits (one workgroup per CU) and the caller allows it
+  const bool try_rl = allow_rl && !weighted && seq_smem_bytes(m, n, weighted, want, true) <= kLdsBytes;
   const size_t smem = seq_smem_bytes(m, n, weighted, want, try_rl);
   if (smem > kLdsBytes) return 0;
   int per = 0;

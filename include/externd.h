@@ -54,6 +54,7 @@ typedef struct {
   int64_t components_used;      /* components fitted before an energy-target stop (k without one) */
   int64_t safeguard_activations;/* components replaced by the best single entry (Prop. 2) */
   int64_t sweep_reverts;        /* refits discarded for the old component (block), see sweeps */
+  int64_t residual_lds;         /* sequential path: 1 if each workgroup kept its rows of R in LDS */
 } externd_stats;
 
 /* (host) optional behaviour of externd_decompose_ex; all-zero = externd_decompose.
@@ -91,12 +92,17 @@ typedef struct {
  *                  Eq. 3's decorrelation (V from U^T R, U from R H V directly); 2 = the V-step
  *                  projection ignores the importance weights (the scales and the energy stay
  *                  weighted; inert without weights).  Joint fitting is block = k (b <= 256).
- *                  Other bits, or bit 1 on the sequential path, are EXTERND_EINVAL. */
+ *                  Other bits, or bit 1 on the sequential path, are EXTERND_EINVAL.
+ *   residual_hbm   0 or 1: the sequential path keeps both residual copies in HBM even where each
+ *                  workgroup's rows of R would fit in its LDS (the default then holds them there
+ *                  for the whole decomposition); results are identical, only the time differs.
+ *                  Inert on the block path. */
 typedef struct {
   double energy_target;
   int safeguard;
   int sweeps;
   int ablation;
+  int residual_hbm;
 } externd_options;
 
 /* k = floor(mu * min(m, n) + 1e-9); -1 if m < 1, n < 1, mu not finite or > 0, or k < 1. */

@@ -92,3 +92,25 @@ def test_decompose_options_rejected_before_device_work():
     assert call(erm.Options(0.0, 1, 0, 0), block=4) == erm.EINVAL and "sequential" in erm.last_error()
     assert call(erm.Options(0.0, 0, 0, 4)) == erm.EINVAL and "ablation" in erm.last_error()
     assert call(erm.Options(0.0, 0, 0, 1)) == erm.EINVAL and "block path" in erm.last_error()
+    assert call(erm.Options(0.0, 0, 0, 0, 2)) == erm.EINVAL and "residual_hbm" in erm.last_error()
+
+
+def test_static_apply_arguments_rejected_before_device_work():
+    lib = erm.load()
+    fake = ctypes.c_void_p(16)  # never dereferenced: validation fails first
+    rc = lib.externd_apply_factors_static(None, fake, fake, 4, 4, 4, fake, 1, fake, None)
+    assert rc == erm.EINVAL and "null" in erm.last_error()
+    rc = lib.externd_apply_factors_static(fake, fake, fake, 4, 4, 4, fake, 0, fake, None)
+    assert rc == erm.EINVAL and "batch" in erm.last_error()
+    # 8 batch (k + m) bytes beyond the fixed 16 MiB workspace
+    rc = lib.externd_apply_factors_static(fake, fake, fake, 7680, 2560, 2560, fake, 300, fake, None)
+    assert rc == erm.EINVAL and "workspace" in erm.last_error()
+
+
+def test_binding_rejects_host_tensors():
+    torch = pytest.importorskip("torch")
+    A = torch.zeros((4, 4), dtype=torch.float32)
+    with pytest.raises(ValueError):
+        erm.decompose(A, 1.0)
+    with pytest.raises(ValueError):
+        erm.project(A)

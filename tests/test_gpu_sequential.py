@@ -74,6 +74,23 @@ def test_weighted_sequential():
     print(f"weighted: identical prefix {f} of {g['k']}, replay mismatches {mism}")
 
 
+@pytest.mark.parametrize("name,m,n,mu", [("attn2560", 300, 260, 1.0), ("lowrank1024", 1024, 1024, 0.25)])
+def test_residual_in_hbm(name, m, n, mu):
+    """The unweighted kernel with both residual copies in HBM (residual_hbm): the same factors as
+    the oracle and bit-equal to the default LDS-resident run."""
+    c = inputs.CONFIGS[name]
+    A, h = inputs.make_input(name, m=m, n=n)
+    g = P.gpu_decompose(A, mu, c["tau"], h, c["als_iters"], 1, residual_hbm=True)
+    assert g["stats"]["residual_lds"] == 0
+    o = oracle.decompose(A, mu, c["tau"], h, c["als_iters"], 1)
+    f = P.check_free_run(g, o, f"{name} {m}x{n} in HBM", alt=(A, mu, c["tau"], h, c["als_iters"], 1))
+    assert f == g["k"], f
+    g2 = P.gpu_decompose(A, mu, c["tau"], h, c["als_iters"], 1)
+    assert g2["stats"]["residual_lds"] == 1
+    for key in ("B", "C", "D", "energy"):
+        assert np.array_equal(g[key], g2[key]), key
+
+
 def test_determinism():
     A, _ = inputs.make_input("lowrank1024", m=512, n=384)
     g1 = P.gpu_decompose(A, 1.5, 0.1, None, 4, 1)
