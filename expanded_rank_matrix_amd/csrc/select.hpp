@@ -43,8 +43,8 @@ struct SelScratchT {
   unsigned cnt[kSelBins];
   u64 psum[kSelBins];
   u64 hsum[HW ? kSelBins : 1];
-  unsigned w_key[kWinMax];
-  u64 w_p[kWinMax];
+  alignas(16) unsigned w_key[kWinMax];
+  alignas(16) u64 w_p[kWinMax];
   u64 w_h[HW ? kWinMax : 1];
   u64 a_p[16], a_h[16];  // per-wave sums (above a refined range; the distinct-key walk)
   unsigned a_c[16];
@@ -60,6 +60,9 @@ struct SelScratchT {
   unsigned red_u[16];
   double bn, bd;  // best boundary score so far, as a fraction
   unsigned slot;
+  // window of the key-array selection: keys [win_klo, win_khi], sums above it, element count
+  unsigned win_klo, win_khi, win_ac, win_nw;
+  u64 win_ap;
 };
 
 struct SelResult {
@@ -625,6 +628,279 @@ __device__ __forceinline__ SelResult ternary_select(const T* vals, const float* 
   out.P = ldexp((double)s.f_p[bw], -sP);
   out.H = W ? ldexp((double)s.f_h[bw], -sH) : (double)out.count;
   __syncthreads();
+  return out;
+}
+
+// ---- the same selection for unweighted vectors held as fp32 bit patterns in LDS ---------------
+// keys[0..L): the fp32 roundings of the vector (sign bit included), km: the largest |key|, the
+// histogram cleared beforehand (select_prepare).  The result equals ternary_select<NT, false>'s on
+// the same values: the same candidate rule and the same exact scoring, with less work per element
+// and fewer workgroup barriers, which is what bounds a selection of a few thousand values:
+//  * bins are aligned to the fp32 exponent (64 per octave, bin b holds the keys with
+//    key >> 17 == (km >> 17) - b, the last bin the rest), so every element of a bin but the last has
+//    the same exponent and the bin's sum of P is an integer sum of 24-bit mantissas, shifted into
+//    the fixed-point scale once per bin instead of once per element;
+//  * thread t owns bins 2t and 2t + 1 (a wave: 128 contiguous bins), so the prefix sums, the best
+//    boundary and the candidate window take one wave scan and one eight-value exchange each, and
+//    every thread learns the window without a further round;
+//  * the window's elements are scored by one wave, reading them four at a time.
+// The window holds at most kWinMax elements; `ok` comes back false (result unset, every thread
+// alike) when it would hold more, and the caller runs ternary_select instead after clearing the
+// histogram again.
+template <int NT, bool HW>
+__device__ __forceinline__ SelResult ternary_select_keys(const unsigned* keys, int L, float tau, unsigned km,
+                                                         SelScratchT<HW>& s, bool* ok) {
+  static_assert(NT == 512, "two bins per thread");
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  constexpr int kLast = kSelBins - 1;
+  SelResult out;
+  out.tkey = 0xFFFFFFFFu;
+  out.ekey = 0xFFFFFFFFu;
+  out.P = 0.0;
+  out.H = 0.0;
+  out.count = 0u;
+  *ok = true;
+  if (km == 0u) return out;
+  const float M = __uint_as_float(km);
+  const double theta = (double)tau * (double)M;
+  unsigned ekey;
+  {
+    unsigned t = __float_as_uint((float)theta);
+    if ((double)__uint_as_float(t) < theta) ++t;
+    while (t > 1u && (double)__uint_as_float(t - 1u) >= theta) --t;
+    ekey = t == 0u ? 1u : t;
+  }
+  out.ekey = ekey;
+  const int LB = 32 - __clz((unsigned)L);
+  const int sP = 62 - exp_bound(M) - LB;
+  const unsigned top = km >> 17;
+  // ---- histogram
+  constexpr int kGrp = 8;
+  for (int i0 = tid; i0 < L; i0 += kGrp * NT) {
+    unsigned kk[kGrp];
+#pragma unroll
+    for (int u = 0; u < kGrp; ++u) kk[u] = i0 + u * NT < L ? keys[i0 + u * NT] & 0x7FFFFFFFu : 0u;
+#pragma unroll
+    for (int u = 0; u < kGrp; ++u) {
+      const unsigned k = kk[u];
+      if (k == 0u || k < ekey) continue;
+      const unsigned d = top - (k >> 17);
+      if (d < (unsigned)kLast) {
+        atomicAdd(&s.cnt[d], 1u);
+        atomicAdd(&s.psum[d], (u64)((k & 0x7FFFFFu) | ((k >> 23) != 0u ? 0x800000u : 0u)));
+      } else {
+        atomicAdd(&s.cnt[kLast], 1u);
+        atomicAdd(&s.psum[kLast], fixkey(k, sP));
+      }
+    }
+  }
+  __syncthreads();
+  // ---- A1: own two bins, wave scan, wave totals
+  const int b0 = 2 * tid;
+  auto conv = [&](int b, u64 v, unsigned cb) -> u64 {
+    if (b == kLast || cb == 0u) return v;
+    const int ex = (int)((top - (unsigned)b) >> 6);
+    const int sh = (ex > 0 ? ex : 1) - 150 + sP;
+    return sh >= 0 ? (v << (sh & 63)) : (sh > -64 ? (v >> ((-sh) & 63)) : 0ull);
+  };
+  const uint2 cc = *reinterpret_cast<const uint2*>(&s.cnt[b0]);
+  const ulonglong2 pp2 = *reinterpret_cast<const ulonglong2*>(&s.psum[b0]);
+  const unsigned c0 = cc.x, c1 = cc.y;
+  const u64 p0 = conv(b0, pp2.x, c0), p1 = conv(b0 + 1, pp2.y, c1);
+  const u64 tp = p0 + p1;
+  const unsigned tc = c0 + c1;
+  const u64 ip = wave_scan_u64(tp);
+  const unsigned ic = wave_scan_u32(tc);
+  if (lane == 63) {
+    s.w_sp[wid] = ip;
+    s.w_sc[wid] = ic;
+  }
+  __syncthreads();
+  // ---- A2: prefix at the own bins, boundary scores, wave best
+  u64 P0 = ip - tp;
+  unsigned C0 = ic - tc;
+#pragma unroll
+  for (int w = 0; w < NW - 1; ++w) {
+    const u64 pw = s.w_sp[w];
+    const unsigned cw = s.w_sc[w];
+    P0 += w < wid ? pw : 0ull;
+    C0 += w < wid ? cw : 0u;
+  }
+  const u64 P1 = P0 + p0, P2 = P1 + p1;  // prefix through bin b0, b0 + 1
+  const unsigned C1 = C0 + c0, C2 = C1 + c1;
+  double bn = 0.0, bd = 1.0;
+  {
+    const double d1 = (double)P1, d2 = (double)P2;
+    if (c0 != 0u) {
+      bn = d1 * d1;
+      bd = (double)C1;
+    }
+    if (c1 != 0u && d2 * d2 * bd > bn * (double)C2) {
+      bn = d2 * d2;
+      bd = (double)C2;
+    }
+  }
+#define EXTERND_STEP(C, R)                                     \
+  {                                                            \
+    const double n2 = dppf64<C, R>(bn), d2 = dppf64<C, R>(bd); \
+    if (n2 * bd > bn * d2) {                                   \
+      bn = n2;                                                 \
+      bd = d2;                                                 \
+    }                                                          \
+  }
+  EXTERND_WAVE_STEPS(EXTERND_STEP)
+#undef EXTERND_STEP
+  if (lane == 63) {
+    s.w_bn[wid] = bn;
+    s.w_bd[wid] = bd;
+  }
+  __syncthreads();
+  // ---- A3: global best, candidate bins, per-wave window
+  bn = s.w_bn[0];
+  bd = s.w_bd[0];
+#pragma unroll
+  for (int w = 1; w < NW; ++w) {
+    const double n2 = s.w_bn[w], d2 = s.w_bd[w];
+    if (n2 * bd > bn * d2) {
+      bn = n2;
+      bd = d2;
+    }
+  }
+  const double cutn = bn * (1.0 - 1e-9);
+  const double tconv = ldexp(1.0, sP);
+  auto cand_of = [&](int b, unsigned cb, u64 Pa, u64 Pb, unsigned Ca, unsigned Cb) -> bool {
+    if (cb == 0u) return false;
+    const double pbd = (double)Pb, pad = (double)Pa;
+    bool cand = pbd * pbd * bd >= cutn * (double)Cb;
+    if (!cand && cb >= 2u) {
+      unsigned tk = b < kLast ? (((top - (unsigned)b) << 17) | 0x1FFFFu) : (((top - (unsigned)(kLast - 1)) << 17) - 1u);
+      tk = tk < km ? tk : km;
+      const double t1 = pad + (double)__uint_as_float(tk) * tconv * (double)cb;
+      cand = t1 * t1 * bd >= cutn * (double)Cb || (Ca > 0u && pad * pad * bd >= cutn * (double)Ca);
+    }
+    return cand;
+  };
+  const bool k0 = cand_of(b0, c0, P0, P1, C0, C1);
+  const bool k1 = cand_of(b0 + 1, c1, P1, P2, C1, C2);
+  // this thread's lowest / highest candidate bin with the sums above it / the count through it
+  const int tlo = k0 ? b0 : (k1 ? b0 + 1 : kSelBins);
+  const int thi = k1 ? b0 + 1 : (k0 ? b0 : -1);
+  const u64 tap = k0 ? P0 : P1;
+  const unsigned tac = k0 ? C0 : C1, tch = k1 ? C2 : C1;
+  const int wlo = kSelBins - (int)wave_max_u32((unsigned)(kSelBins - tlo));
+  const int whi = (int)wave_max_u32((unsigned)(thi + 1)) - 1;
+  if (lane == 0) {
+    s.w_lo[wid] = wlo;
+    s.w_hi[wid] = whi;
+  }
+  {
+    const int llo = wlo < kSelBins ? (wlo >> 1) - wid * 64 : 0;
+    const int lhi = whi >= 0 ? (whi >> 1) - wid * 64 : 0;
+    const u64 ap_lo = readlane64(tap, llo);
+    const unsigned ac_lo = readlane32(tac, llo), ac_hi = readlane32(tch, lhi);
+    if (lane == 0) {
+      s.w_plo[wid] = ap_lo;
+      s.w_clo[wid] = ac_lo;
+      s.w_chi[wid] = ac_hi;
+    }
+  }
+  __syncthreads();
+  // ---- A4: the window (every thread), then the gather
+  int lo = kSelBins, hi = -1, wl = 0, wh = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int l = s.w_lo[w], h = s.w_hi[w];
+    wl = l < lo ? w : wl;
+    lo = l < lo ? l : lo;
+    wh = h > hi ? w : wh;
+    hi = h > hi ? h : hi;
+  }
+  const u64 AP = s.w_plo[wl];
+  const unsigned AC = s.w_clo[wl];
+  const unsigned nw = hi >= lo ? s.w_chi[wh] - AC : 0u;
+  if (nw == 0u || nw > (unsigned)kWinMax) {
+    *ok = false;
+    __syncthreads();
+    return out;
+  }
+  const unsigned khi = lo == 0 ? km : ((((top - (unsigned)lo) << 17) | 0x1FFFFu) < km ? (((top - (unsigned)lo) << 17) | 0x1FFFFu) : km);
+  unsigned klo = hi < kLast ? ((top - (unsigned)hi) << 17) : ekey;
+  klo = klo > ekey ? klo : ekey;
+  for (int i0 = tid; i0 < L; i0 += kGrp * NT) {
+    unsigned kk[kGrp];
+#pragma unroll
+    for (int u = 0; u < kGrp; ++u) kk[u] = i0 + u * NT < L ? keys[i0 + u * NT] & 0x7FFFFFFFu : 0u;
+#pragma unroll
+    for (int u = 0; u < kGrp; ++u) {
+      const unsigned k = kk[u];
+      if (k != 0u && k >= klo && k <= khi) {
+        const unsigned slot = atomicAdd(&s.slot, 1u);
+        s.w_key[slot] = k;
+        s.w_p[slot] = fixkey(k, sP);
+      }
+    }
+  }
+  __syncthreads();
+  // ---- scoring by wave 0: lane e holds window elements e, e + 64, ...; P(t) = AP + sum of the
+  // window values with key >= t, read four at a time
+  const int ns = (int)nw;
+  if (wid == 0) {
+    double myS = -1.0;
+    unsigned myK = 0u, myC = 0u;
+    u64 myP = 0ull;
+    for (int e = lane; e < ((ns + 63) & ~63); e += 64) {
+      const unsigned ke = e < ns ? s.w_key[e] : 0xFFFFFFFFu;
+      u64 P = AP;
+      unsigned C = AC;
+      for (int j = 0; j < ns; j += 4) {
+        const uint4 kq = *reinterpret_cast<const uint4*>(&s.w_key[j]);
+        const ulonglong2 pa = *reinterpret_cast<const ulonglong2*>(&s.w_p[j]);
+        const ulonglong2 pb = *reinterpret_cast<const ulonglong2*>(&s.w_p[j + 2]);
+        const bool i0 = kq.x >= ke, i1 = j + 1 < ns && kq.y >= ke, i2 = j + 2 < ns && kq.z >= ke,
+                   i3 = j + 3 < ns && kq.w >= ke;
+        P += (i0 ? pa.x : 0ull) + (i1 ? pa.y : 0ull) + (i2 ? pb.x : 0ull) + (i3 ? pb.y : 0ull);
+        C += (unsigned)i0 + (unsigned)i1 + (unsigned)i2 + (unsigned)i3;
+      }
+      if (e < ns) {
+        const double Pd = (double)P;
+        const double S = Pd * Pd / (double)C;
+        if (better(S, ke, myS, myK)) {
+          myS = S;
+          myK = ke;
+          myP = P;
+          myC = C;
+        }
+      }
+    }
+    int src = lane;
+#define EXTERND_STEP(C, R)                                                 \
+  {                                                                        \
+    const double S2 = dppf64<C, R>(myS);                                   \
+    const unsigned k2 = dpp32<C, R>(myK), s2 = dpp32<C, R>((unsigned)src); \
+    if (better(S2, k2, myS, myK)) {                                        \
+      myS = S2;                                                            \
+      myK = k2;                                                            \
+      src = (int)s2;                                                       \
+    }                                                                      \
+  }
+    EXTERND_WAVE_STEPS(EXTERND_STEP)
+#undef EXTERND_STEP
+    myK = readlane32(myK, 63);
+    src = (int)readlane32((unsigned)src, 63);
+    const u64 pp = readlane64(myP, src);
+    const unsigned cc2 = readlane32(myC, src);
+    if (lane == 0) {
+      s.f_k[0] = myK;
+      s.f_c[0] = cc2;
+      s.f_p[0] = pp;
+    }
+  }
+  __syncthreads();
+  out.tkey = s.f_k[0];
+  out.count = s.f_c[0];
+  out.P = ldexp((double)s.f_p[0], -sP);
+  out.H = (double)out.count;
   return out;
 }
 

@@ -65,7 +65,7 @@ __device__ __forceinline__ int code_at(const uint32_t* pk, int i) {
 
 // Dynamic LDS of the sequential kernel; every region starts on a 16-byte boundary.
 struct SeqLds {
-  size_t dl, hl, pk, part, slab, total;
+  size_t dl, kl, hl, pk, part, slab, total;
 };
 __host__ __device__ inline size_t al16(size_t x) { return (x + 15) & ~(size_t)15; }
 __host__ __device__ inline SeqLds seq_lds_layout(int m, int n, bool weighted, int G, bool rl) {
@@ -75,7 +75,8 @@ __host__ __device__ inline SeqLds seq_lds_layout(int m, int n, bool weighted, in
   const size_t parts = 8 * 16;  // matvec segment sums (at least kMvPart)
   SeqLds s;
   s.dl = al16(weighted ? sizeof(SelScratchT<true>) : sizeof(SelScratchT<false>));
-  s.hl = al16(s.dl + 8 * L);
+  s.kl = al16(s.dl + 8 * L);
+  s.hl = al16(s.kl + 4 * L);
   s.pk = al16(s.hl + (weighted ? 4 * n4 : 0));
   s.part = al16(s.pk + 4 * (4 * wm + 3 * wn + 4));
   s.slab = al16(s.part + 8 * parts);
@@ -395,6 +396,7 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
   const int m4 = (m + 3) & ~3, n4 = (n + 3) & ~3;
   const SeqLds lay = seq_lds_layout(m, n, WV, (int)gridDim.x, RL);
   double* dl = reinterpret_cast<double*>(smem + lay.dl);    // exchanged vector (z or w)
+  unsigned* kl = reinterpret_cast<unsigned*>(smem + lay.kl);  // its fp32 roundings (bit patterns)
   float* hl = reinterpret_cast<float*>(smem + lay.hl);      // n4 column weights (weighted)
   uint32_t* pk = reinterpret_cast<uint32_t*>(smem + lay.pk);
   double* part = reinterpret_cast<double*>(smem + lay.part);
@@ -456,30 +458,46 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
       for (int u = 0; u < kXg; ++u) v[u] = j0 + u * NT < len ? ld_dev(src + j0 + u * NT) : 0.0;
 #pragma unroll
       for (int u = 0; u < kXg; ++u) {
-        if (j0 + u * NT < len) dl[j0 + u * NT] = v[u];
-        const unsigned k = __float_as_uint((float)v[u]) & 0x7FFFFFFFu;
+        const unsigned kb = __float_as_uint((float)v[u]);
+        if (j0 + u * NT < len) {
+          dl[j0 + u * NT] = v[u];
+          kl[j0 + u * NT] = kb;
+        }
+        const unsigned k = kb & 0x7FFFFFFFu;
         kx = k > kx ? k : kx;
       }
     }
     select_prepare<NT>(s, kx);
   };
+  // Unweighted projection of the vector in dl / kl (select_prepare done): the key-array selection,
+  // or, when its candidate window is too wide, the general one (same result either way).
+  auto select_unweighted = [&](int len) -> SelResult {
+    unsigned km = 0u;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) km = s.red_u[w] > km ? s.red_u[w] : km;
+    bool ok = true;
+    const SelResult r = ternary_select_keys<NT>(kl, len, a.tau, km, s, &ok);
+    if (ok) return r;
+    select_prepare<NT>(s, km);
+    return ternary_select<NT, false, double, WV, true>(dl, nullptr, len, a.tau, 0, s);
+  };
   // Pack the selection r of vals[0..len) into dst (2-bit codes) with wave ballots: wave w takes
   // the 64-element chunks w, w + NW, ...; lanes 0..3 write the chunk's four words.  prev, when
   // given, receives the old words.  Block totals are combined in wave order (deterministic).
-  auto pack_sel = [&](const double* vals, int len, const SelResult& r, uint32_t* dst, uint32_t* prev,
-                      bool want_p) -> PackOut {
+  auto pack_sel = [&](const double* vals, const unsigned* kv, int len, const SelResult& r, uint32_t* dst,
+                      uint32_t* prev, bool want_p) -> PackOut {
     const int words = (len + 15) >> 4;
     const int nch = (len + 63) >> 6;
     int changed = 0, sum = 0;
     double pacc = 0.0;
     constexpr int kPg = 8;  // chunks per wave whose loads are issued together
     for (int c0 = wid; c0 < nch; c0 += kPg * NW) {
-      double xs[kPg];
+      unsigned ks[kPg];
       unsigned olds[kPg];
 #pragma unroll
       for (int u = 0; u < kPg; ++u) {
         const int c = c0 + u * NW, i = c * 64 + lane, w = c * 4 + lane;
-        xs[u] = (c < nch && i < len) ? vals[i] : 0.0;
+        ks[u] = (c < nch && i < len) ? kv[i] : 0u;
         olds[u] = (c < nch && lane < 4 && w < words) ? dst[w] : 0u;
       }
 #pragma unroll
@@ -487,12 +505,11 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
         const int c = c0 + u * NW;
         if (c >= nch) break;  // uniform within the wave
         const int i = c * 64 + lane;
-        const double xv = xs[u];
-        const float x = (float)xv;
-        const bool sel = i < len && selected(x, r);
-        const bool neg = sel && x < 0.0f;
+        const unsigned kb = ks[u];
+        const bool sel = i < len && selected(__uint_as_float(kb), r);
+        const bool neg = sel && (kb >> 31) != 0u;
         const u64 mnz = __ballot(sel), mneg = __ballot(neg);
-        if (want_p && sel) pacc += fabs(xv);
+        if (want_p && sel) pacc += fabs(vals[i]);
         sum += (int)__popcll(mnz) - 2 * (int)__popcll(mneg);
         const int w = c * 4 + lane;
         if (lane < 4 && w < words) {
@@ -729,14 +746,18 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
         for (int u = 0; u < kXg; ++u) v[u] = i0 + u * NT < m ? rs[i0 + u * NT] : 0.0;
 #pragma unroll
         for (int u = 0; u < kXg; ++u) {
-          if (i0 + u * NT < m) dl[i0 + u * NT] = v[u];
-          const unsigned k = __float_as_uint((float)v[u]) & 0x7FFFFFFFu;
+          const unsigned kb = __float_as_uint((float)v[u]);
+          if (i0 + u * NT < m) {
+            dl[i0 + u * NT] = v[u];
+            kl[i0 + u * NT] = kb;
+          }
+          const unsigned k = kb & 0x7FFFFFFFu;
           kx = k > kx ? k : kx;
         }
       }
       select_prepare<NT>(s, kx);
     }
-    const SelResult su = ternary_select<NT, false, double, WV, true>(dl, nullptr, m, a.tau, 0, s);
+    const SelResult su = select_unweighted(m);
     if (su.count == 0u) {
       const int r = fallback_row();
       if (r == -2) return;
@@ -750,7 +771,7 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
       set_unit_u(r);
       fallback = true;
     } else {
-      pack_sel(dl, m, su, pu, nullptr, false);
+      pack_sel(dl, kl, m, su, pu, nullptr, false);
     }
     }  // pass 0
     for (int w = tid; w < wm; w += NT) pu0[w] = pu[w];
@@ -781,8 +802,8 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
       }
       // (ablation: the projection may ignore the weights; the scale and energy stay weighted)
       const bool naive_w = EXT && WV && (a.ablation & 2);
-      const SelResult sv = naive_w ? ternary_select<NT, false, double, WV, true>(dl, nullptr, n, a.tau, 0, s)
-                                   : ternary_select<NT, WV, double, WV, true>(dl, hw, n, a.tau, a.EHm, s);
+      const SelResult sv = (naive_w || !WV) ? select_unweighted(n)
+                                            : ternary_select<NT, WV, double, WV, true>(dl, hw, n, a.tau, a.EHm, s);
       if (sv.count == 0u) {
         // R^T u == 0: only possible for the initial u; restart from the largest-entry row
         if (fallback) {
@@ -801,7 +822,7 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
         __syncthreads();
         continue;
       }
-      const PackOut pvo = pack_sel(dl, n, sv, pv, nullptr, false);
+      const PackOut pvo = pack_sel(dl, kl, n, sv, pv, nullptr, false);
       sumv = pvo.sum;
       const int vchanged = pvo.changed;
       Hv = sv.H;
@@ -831,10 +852,10 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
       ++epoch;
       if (grid_barrier(a.bar, epoch, a.spin_limit, &bar_flag)) return;
       load_exchange(a.xz, m);
-      const SelResult s2 = ternary_select<NT, false, double, WV, true>(dl, nullptr, m, a.tau, 0, s);
+      const SelResult s2 = select_unweighted(m);
       // new u, the previous one kept in pu_prev, and p = sum over supp(u) of u_i z_i with the
       // fp64 z (fixed reduction order)
-      const PackOut puo = pack_sel(dl, m, s2, pu, pu_prev, true);
+      const PackOut puo = pack_sel(dl, kl, m, s2, pu, pu_prev, true);
       p = puo.p;
       cnt_u = s2.count;
       const int uchanged = puo.changed;
