@@ -160,7 +160,7 @@ int externd_decompose_ex(const float* A, int64_t m, int64_t n, float mu, float t
     o_xf = take((size_t)4 * grid * sizeof(double));
     o_rsg = take((size_t)grid * mi * sizeof(double));
   } else {
-    o_blk = take(block_workspace_bytes(mi, ni, bi));
+    o_blk = take(block_workspace_bytes(mi, ni, bi, h != nullptr));
   }
   Workspace ws(st);
   if (hipMallocAsync(&ws.p, off, st) != hipSuccess) {

@@ -64,9 +64,15 @@ struct BlockWs {
   double* GVo;     // b x b: weighted Gram of the old V
   double* ppo;     // b: u_c^T (R + X) H v_c of the old components
   float* dold;     // b: old scales
-  double* unit;    // [0] unit of X, [1] unit of Yt: the fixed-point grid of the last contraction
+  double* unit;    // [0] unit of X, [1] unit of Yt: the fixed-point grid of the last contraction;
+                   // [2] unit of R's images, [3] of the image of R H
   long long* Xi;   // X and Yt as the contractions write them (exact integers)
   long long* Yi;
+  int mp, np;      // m and n padded to 64: image row lengths (per digit) and row counts
+  int8_t* imr;     // mp x 6 np: image of R's rows
+  int8_t* imrw;    // mp x 6 np: image of the rows of R H (imr when unweighted)
+  int8_t* imc;     // np x 6 mp: image of R's columns
+  int8_t* Ts;      // the ternary operand of a contraction, swizzled (b rounded up to 64 x max(mp, np))
 };
 
 constexpr int kMaxWords = 64;      // words per residual-max slot (one per lane of a wave)
@@ -76,7 +82,7 @@ static size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // One layout for both sizing and carving.
 template <typename F>
-static void ws_layout(int m, int n, int b, F&& take) {
+static void ws_layout(int m, int n, int b, bool weighted, F&& take) {
   const size_t mx = (size_t)(m > n ? m : n), bb = (size_t)b;
   take((void**)nullptr, bb * (size_t)((m + 15) & ~15));  // Ut
   take((void**)nullptr, bb * (size_t)((n + 15) & ~15));  // Vt
@@ -103,14 +109,19 @@ static void ws_layout(int m, int n, int b, F&& take) {
   take((void**)nullptr, (size_t)kGramSplit * kGramTiles * 256 * 8);  // split-K Gram partial tiles
   take((void**)nullptr, (size_t)kGramTiles * 4);                     // their arrival counters
   take((void**)nullptr, 64);                                         // contraction units
+  const size_t img = (size_t)((m + 63) & ~63) * (size_t)((n + 63) & ~63) * 6;
+  take((void**)nullptr, img);                                        // images of R
+  take((void**)nullptr, img);
+  take((void**)nullptr, weighted ? img : 0);                         // image of R H
+  take((void**)nullptr, (size_t)((b + 63) & ~63) * ((mx + 63) & ~(size_t)63));  // swizzled T
 }
 
-static BlockWs carve(void* base, int m, int n, int b) {
+static BlockWs carve(void* base, int m, int n, int b, bool weighted) {
   char* p = static_cast<char*>(base);
   size_t o = 0;
   void* ptrs[32];
   int np = 0;
-  ws_layout(m, n, b, [&](void**, size_t bytes) {
+  ws_layout(m, n, b, weighted, [&](void**, size_t bytes) {
     ptrs[np++] = p + o;
     o = al(o + bytes);
   });
@@ -143,14 +154,21 @@ static BlockWs carve(void* base, int m, int n, int b) {
   w.gpart = static_cast<double*>(ptrs[q++]);
   w.gcnt = static_cast<unsigned*>(ptrs[q++]);
   w.unit = static_cast<double*>(ptrs[q++]);
+  w.imr = static_cast<int8_t*>(ptrs[q++]);
+  w.imc = static_cast<int8_t*>(ptrs[q++]);
+  w.imrw = weighted ? static_cast<int8_t*>(ptrs[q++]) : w.imr;
+  if (!weighted) ++q;  // the empty slot of the image of R H
+  w.Ts = static_cast<int8_t*>(ptrs[q++]);
+  w.mp = (m + 63) & ~63;
+  w.np = (n + 63) & ~63;
   w.Xi = reinterpret_cast<long long*>(w.X);
   w.Yi = reinterpret_cast<long long*>(w.Yt);
   return w;
 }
 
-size_t block_workspace_bytes(int m, int n, int b) {
+size_t block_workspace_bytes(int m, int n, int b, bool weighted) {
   size_t o = 0;
-  ws_layout(m, n, b, [&](void**, size_t bytes) { o = al(o + bytes); });
+  ws_layout(m, n, b, weighted, [&](void**, size_t bytes) { o = al(o + bytes); });
   return o;
 }
 
@@ -272,105 +290,194 @@ template <int NT>
 __device__ __forceinline__ void spd_inv_body(const double* G, int bs, double* Gi, char* smem);
 __host__ __device__ inline size_t spd_lds_bytes(int bs);
 
-// The residual tile of each 64-wide k chunk is loaded by the whole workgroup as float4 rows
-// (256 contiguous bytes per tile row: full cache lines), converted to its fixed-point image
-// once, and staged in LDS; each lane then reads its 16 values of the MFMA layout from there.  The
-// next chunk's loads are issued before the current chunk is consumed.
-constexpr int kTileP = 66;  // int64 pitch of a [64 rows][64 k] tile (rows 16 B aligned)
-constexpr int kTileQ = 65;  // int64 pitch of a [64 k][64 cols] tile
-constexpr size_t kTileBytesP = sizeof(long long) * 64 * kTileP;
-constexpr size_t kTileBytesQ = sizeof(long long) * 64 * kTileQ;
+// A contraction workgroup of 512 threads runs two tiles, one per half.  The registers of a tile's
+// waves allow eight waves per CU, so this is the occupancy of two 256-thread workgroups, while a
+// single workgroup per CU can also hold the LDS of a fused inverse.  Tiles that read the same image
+// rows (row tile x, K range z; component groups y = 0 .. gy - 1) are run by workgroups on one XCD
+// (the dispatcher deals workgroup ids round-robin over the eight XCDs), in consecutive halves, so
+// the rows are fetched into that XCD's L2 once instead of gy times.  Halves past the last tile
+// return at once.
+__device__ __forceinline__ bool tile_decode(int w, int half, int gx, int gy, int gz, int* bx, int* by, int* bz) {
+  const int x = w & 7, i = 2 * (w >> 3) + half;
+  const int uu = i / gy, y = i - uu * gy;
+  const int u = 8 * uu + x;
+  if (u >= gx * gz) return false;
+  *bx = u % gx;
+  *bz = u / gx;
+  *by = y;
+  return true;
+}
+static int tile_grid(int gx, int gy, int gz) { return 8 * ((((gx * gz + 7) / 8) * gy + 1) / 2); }
 
-// out[c][i] (+)= sum_{k in this split} N(x_ik) T[c][k], x_ik = R[i][k] (h_k): rows of R x
-// components, in units *unit = 2^-f.  Workgroup: 64 rows (16 per wave) x 16 NCT components
-// (blockIdx.y), K range blockIdx.z.
-template <int NCT>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) rv_i8_kernel(const float* R, int ldr, int rows, int K, const int8_t* T,
-                                                    int ldt, const float* h, int ehm, int bs, const unsigned* rmax,
-                                                    int sblk, int kspan, long long* out, double* unit,
-                                                    const double* spdG, double* spdGi) {
-  extern __shared__ __align__(16) char dsm[];
-  if (spdG && blockIdx.x == gridDim.x - 1) {  // the extra column of workgroups: one inverts spdG
-    if (blockIdx.y == 0 && blockIdx.z == 0) spd_inv_body<256>(spdG, bs, spdGi, dsm);
-    return;
-  }
-  long long* tile = reinterpret_cast<long long*>(dsm);  // 64 x kTileP
+// ---- the residual's fixed-point image.  After every change of R (staging, each block's update,
+// a refit's add-back) one pass writes the digits of N(x) for every entry in the layouts the
+// contractions read, so that the block's seven contractions of one R stream int8 digits straight
+// into the MFMA; converting R inside each contraction cost fp64 arithmetic for every entry and
+// component group, several times the time of the products themselves.
+// Image of an a x K matrix X (rows padded to a multiple of 64, K to Kp, a multiple of 64, with
+// zeros), stored in the order the contraction's waves consume it: one 6 KB block per 16 rows and
+// 64-wide k chunk, holding for each digit t (1 KB) the MFMA operand of every lane l = 16 g + rr
+// (16 B: digit t of N(X_r,k) for r = 16 p + rr and k = 64 c + 16 g .. + 15, block (p, c)).  Each
+// load instruction of a wave then reads 1 KB contiguous, and a wave walks one contiguous 16-row
+// strip.  Three images: of R's rows (R Omega), of the rows of R H (R H V; the same buffer when
+// unweighted) and of R's columns (U^T R), this last one with rows j and k = i.
+constexpr int kImgBlock = 6144;  // bytes of one 16-row x 64-k block
+__host__ __device__ inline int pad64(int x) { return (x + 63) & ~63; }
+
+// One 64 x 64 tile of R per workgroup: row images from the tile as loaded (float4 rows), the
+// column image from its unweighted fixed-point values transposed through LDS.
+__global__ void __launch_bounds__(256) digitize_kernel(const float* R, int ldr, int m, int n, const float* h,
+                                                       int ehm, const unsigned* rmax, int sblk, int mp, int np,
+                                                       int8_t* imr, int8_t* imrw, int8_t* imc, double* units) {
+  __shared__ long long tile[64][65];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int j0 = blockIdx.x * 64, i0 = blockIdx.y * 64;
+  const int scu = fx_scale(rmax, sblk, 0);
+  const int scw = h ? fx_scale(rmax, sblk, ehm) : scu;
+  const double du = ldexp(1.0, scu), dw = ldexp(1.0, scw);
+  if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) {
+    units[0] = ldexp(1.0, -scu);  // R's images
+    units[1] = ldexp(1.0, -scw);  // the image of R H
+  }
+  const int srow = tid >> 4, scol = 4 * (tid & 15), k = j0 + scol;
+  const int nch = np / 64;  // k chunks per row image
+  float hv[4] = {0.f, 0.f, 0.f, 0.f};
+  if (h) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) hv[e] = k + e < n ? h[k + e] : 0.f;
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int i = i0 + srow + 16 * q;
+    // R rows are padded to a multiple of 4 floats, so the float4 at k < n is inside the row
+    const float4 x4 = (i < m && k < n) ? *reinterpret_cast<const float4*>(R + (size_t)i * ldr + k)
+                                       : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float xv[4] = {x4.x, x4.y, x4.z, x4.w};
+    long long nu[4], nw[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool in = i < m && k + e < n;
+      nu[e] = in ? fx_round((double)xv[e] * du) : 0ll;
+      nw[e] = in ? fx_round(((double)xv[e] * (double)hv[e]) * dw) : 0ll;
+    }
+    unsigned wd[kDig];
+    fx_digits6(nu[0], nu[1], nu[2], nu[3], wd);
+    // block (i / 16, k / 64), lane 16 ((k % 64) / 16) + i % 16, bytes k % 16 .. + 3
+    const size_t go = ((size_t)(i >> 4) * nch + (k >> 6)) * kImgBlock + ((((k & 63) >> 4) << 4) + (i & 15)) * 16 +
+                      (k & 15);
+    int8_t* pr = imr + go;
+#pragma unroll
+    for (int t = 0; t < kDig; ++t) *reinterpret_cast<unsigned*>(pr + 1024 * t) = wd[t];
+    if (h) {
+      fx_digits6(nw[0], nw[1], nw[2], nw[3], wd);
+      pr = imrw + go;
+#pragma unroll
+      for (int t = 0; t < kDig; ++t) *reinterpret_cast<unsigned*>(pr + 1024 * t) = wd[t];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) tile[srow + 16 * q][scol + e] = nu[e];
+  }
+  __syncthreads();
+  // column image: wave w takes tile columns 16 w .. 16 w + 15; lane 4 jj + g writes the operands
+  // of column 16 w + jj for rows 16 g .. 16 g + 15 (so each digit's stores fill 1 KB)
+  const int jj = lane >> 2, g = lane & 3, cl = 16 * wid + jj;
+  long long nv[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) nv[r] = tile[16 * g + r][cl];
+  v4i op[kDig];
+  fx_operands(nv, op);
+  const int j = j0 + cl;
+  int8_t* pc = imc + ((size_t)(j >> 4) * (mp / 64) + (i0 >> 6)) * kImgBlock + (16 * g + (j & 15)) * 16;
+#pragma unroll
+  for (int t = 0; t < kDig; ++t) *reinterpret_cast<v4i*>(pc + 1024 * t) = op[t];
+}
+
+// The ternary operand in the same order: one 1 KB block per 16 components and 64-wide k chunk,
+// lane l = 16 g + cc holding T[16 p + cc][64 c + 16 g .. + 15] (block (p, c)); components past
+// bs and k past ldt are zero.  Written from the row-major T before each contraction, so that
+// every operand load of a wave reads 1 KB contiguous instead of 64 bytes of 16 rows.
+__global__ void __launch_bounds__(256) swizzle_t_kernel(const int8_t* T, int ldt, int bs, int nct, int nchunk,
+                                                        int8_t* Ts) {
+  const int blk = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (blk >= nct * nchunk) return;
+  const int p = blk / nchunk, ch = blk - p * nchunk;
+  const int c = 16 * p + (lane & 15), k = 64 * ch + 16 * (lane >> 4);
+  const v4i v = (c < bs && k < ldt) ? load16(T + (size_t)c * ldt + k) : (v4i){0, 0, 0, 0};
+  *reinterpret_cast<v4i*>(Ts + (size_t)blk * 1024 + 16 * lane) = v;
+}
+
+// out[c][r] (+)= sum_{k in this split} N(X_rk) T[c][k] from an image of X (a rows, Kp bytes per
+// digit) and the swizzled T, in units *img_unit, copied to *unit.  Workgroup: 64 rows (16 per
+// wave) x 16 NCT components; per 64-wide k chunk each lane loads 96 bytes of digits and 16 NCT
+// bytes of T, the next chunk's loads in flight while the current one is multiplied.
+template <int NCT>
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+img_contract_kernel(const int8_t* img, int Kp, int rows, const int8_t* Ts, int bs, int kspan, int gx, int gy, int gz,
+                    const double* img_unit, long long* out, double* unit, const double* spdG, double* spdGi) {
+  extern __shared__ __align__(16) char dsm[];
+  int w = (int)blockIdx.x;
+  if (spdG) {  // workgroup 0, dispatched first, inverts spdG beside the contraction
+    if (w == 0) {
+      spd_inv_body<512>(spdG, bs, spdGi, dsm);
+      return;
+    }
+    --w;
+  }
+  int bx, by, bz;
+  if (!tile_decode(w, (int)threadIdx.x >> 8, gx, gy, gz, &bx, &by, &bz)) return;  // no barriers below
+  const int tid = threadIdx.x & 255, lane = tid & 63, wid = tid >> 6;
   const int lr = lane & 15, g = lane >> 4;
-  const int c0 = blockIdx.y * 16 * NCT;
-  const int kb = blockIdx.z * kspan, ke = kb + kspan < K ? kb + kspan : K;
-  const int sc = fx_scale(rmax, sblk, h ? ehm : 0);
-  const double dscale = ldexp(1.0, sc);
-  if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && tid == 0) *unit = ldexp(1.0, -sc);
-  // staging role: thread t loads tile rows t / 16 + 16 q, k columns 4 (t % 16) .. + 3
-  const int srow = tid >> 4, scol = 4 * (tid & 15);
+  const int c0 = by * 16 * NCT;
+  const int kb = bz * kspan, ke = kb + kspan < Kp ? kb + kspan : Kp;
+  if (bx == 0 && by == 0 && bz == 0 && tid == 0) *unit = *img_unit;
+  const int r = bx * 64 + wid * 16 + lr;  // image rows are padded to 64: always inside
+  const int8_t* src = img + (size_t)(r >> 4) * (Kp / 64) * kImgBlock + 16 * lane;  // chunk k0: + 96 k0
+  const int8_t* tsrc = Ts + (size_t)(c0 / 16) * (Kp / 64) * 1024 + 16 * lane;     // tile ct: + ct Kp 16
   v4i acc[NCT][kDig];
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
     for (int t = 0; t < kDig; ++t) acc[ct][t] = (v4i){0, 0, 0, 0};
-  float4 pre[4];
-  float4 hpre = make_float4(0.f, 0.f, 0.f, 0.f);
-  auto fetch = [&](int k0) {
-    const int k = k0 + scol;
+  // No load is masked or branched around, so the products wait only for the older chunk's loads
+  auto load = [&](int k0, v4i(&d)[kDig], v4i(&tt)[NCT]) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int i = blockIdx.x * 64 + srow + 16 * q;
-      pre[q] = (i < rows && k < ke) ? *reinterpret_cast<const float4*>(R + (size_t)i * ldr + k)
-                                    : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    if (h && k < ke)  // the caller's weights: scalar loads, each inside [0, K)
-      hpre = make_float4(h[k], k + 1 < K ? h[k + 1] : 0.f, k + 2 < K ? h[k + 2] : 0.f, k + 3 < K ? h[k + 3] : 0.f);
+    for (int t = 0; t < kDig; ++t) d[t] = load16(src + (size_t)96 * k0 + 1024 * t);
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) tt[ct] = load16(tsrc + (size_t)16 * k0 + (size_t)ct * Kp * 16);
   };
-  if (kb < ke) fetch(kb);
-  for (int k0 = kb; k0 < ke; k0 += 64) {
-    __syncthreads();  // the previous chunk's tile is consumed
-    {
-      const int k = k0 + scol;
-      const float hv[4] = {hpre.x, hpre.y, hpre.z, hpre.w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float xv[4] = {pre[q].x, pre[q].y, pre[q].z, pre[q].w};
-        long long nv[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bool in = k + e < ke;
-          const double x = h ? (double)xv[e] * (double)hv[e] : (double)xv[e];
-          nv[e] = in ? fx_round(x * dscale) : 0ll;
-        }
-        long long* trow = &tile[(srow + 16 * q) * kTileP + scol];
-        *reinterpret_cast<longlong2*>(trow) = make_longlong2(nv[0], nv[1]);
-        *reinterpret_cast<longlong2*>(trow + 2) = make_longlong2(nv[2], nv[3]);
-      }
-    }
-    __syncthreads();
-    if (k0 + 64 < ke) fetch(k0 + 64);
-    const int k = k0 + 16 * g;
-    v4i tb[NCT];
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      const int c = c0 + ct * 16 + lr;
-      tb[ct] = (c < bs && k < ke) ? load16(T + (size_t)c * ldt + k) : (v4i){0, 0, 0, 0};
-    }
-    long long nv[16];
-#pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      const longlong2 v = *reinterpret_cast<const longlong2*>(&tile[(wid * 16 + lr) * kTileP + 16 * g + 2 * p]);
-      nv[2 * p] = v.x;
-      nv[2 * p + 1] = v.y;
-    }
-    v4i da[kDig];
-    fx_operands(nv, da);
+  auto products = [&](const v4i(&d)[kDig], const v4i(&tt)[NCT]) {
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
       for (int t = 0; t < kDig; ++t)
-        acc[ct][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(tb[ct], da[t], acc[ct][t], 0, 0, 0);
+        acc[ct][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(tt[ct], d[t], acc[ct][t], 0, 0, 0);
+  };
+  // kb < ke: the split index is below gz = ceil(Kp / kspan), and both are multiples of 64.
+  // Two register sets in turn (no copies between them): the loads of one chunk are in flight
+  // while the other is multiplied.
+  const int nk = (ke - kb) / 64;
+  v4i da[kDig], ta[NCT], db[kDig], tb[NCT];
+  load(kb, da, ta);
+  int it = 1;
+  for (; it + 1 < nk; it += 2) {
+    load(kb + 64 * it, db, tb);
+    __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the products
+    products(da, ta);
+    load(kb + 64 * (it + 1), da, ta);
+    __builtin_amdgcn_sched_barrier(0);
+    products(db, tb);
+  }
+  if (it < nk) {
+    load(kb + 64 * it, db, tb);
+    __builtin_amdgcn_sched_barrier(0);
+    products(da, ta);
+    products(db, tb);
+  } else {
+    products(da, ta);
   }
   // D = T x^T: lane l, register q holds component 4 g + q of the tile for row lr, so each store
   // instruction covers four components x 16 consecutive rows
-  const bool split = gridDim.z > 1;
-  const int r = blockIdx.x * 64 + wid * 16 + lr;
+  const bool split = gz > 1;
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) {
 #pragma unroll
@@ -379,91 +486,6 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) r
       if (c < bs && r < rows) {
         const long long v = fx_combine(acc[ct], q);
         long long* o = out + (size_t)c * rows + r;
-        if (split) atomicAdd(reinterpret_cast<unsigned long long*>(o), (unsigned long long)v);
-        else *o = v;
-      }
-    }
-  }
-}
-
-// out[c][j] (+)= sum_{i in this split} U[c][i] N(R[i][j]): components x columns of R, in units
-// *unit = 2^-f.  Workgroup: 64 columns (16 per wave) x 16 NCT components (blockIdx.y), K = m range
-// blockIdx.z.
-template <int NCT>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) utr_i8_kernel(const float* R, int ldr, int m, int n, const int8_t* U, int ldu,
-                                                     int bs, const unsigned* rmax, int sblk, int kspan, long long* out,
-                                                     double* unit, const double* spdG, double* spdGi) {
-  extern __shared__ __align__(16) char dsm[];
-  if (spdG && blockIdx.x == gridDim.x - 1) {  // the extra column of workgroups: one inverts spdG
-    if (blockIdx.y == 0 && blockIdx.z == 0) spd_inv_body<256>(spdG, bs, spdGi, dsm);
-    return;
-  }
-  long long* tile = reinterpret_cast<long long*>(dsm);  // 64 x kTileQ
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int lr = lane & 15, g = lane >> 4;
-  const int j = blockIdx.x * 64 + wid * 16 + lr;  // column supplied by this lane
-  const int c0 = blockIdx.y * 16 * NCT;
-  const int kb = blockIdx.z * kspan, ke = kb + kspan < m ? kb + kspan : m;
-  const int sc = fx_scale(rmax, sblk, 0);
-  const double dscale = ldexp(1.0, sc);
-  if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && tid == 0) *unit = ldexp(1.0, -sc);
-  const bool jok = j < n;
-  // staging role: thread t loads tile rows (k) t / 16 + 16 q, columns 4 (t % 16) .. + 3
-  const int srow = tid >> 4, scol = 4 * (tid & 15), sj = blockIdx.x * 64 + scol;
-  v4i acc[NCT][kDig];
-#pragma unroll
-  for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-    for (int t = 0; t < kDig; ++t) acc[ct][t] = (v4i){0, 0, 0, 0};
-  float4 pre[4];
-  auto fetch = [&](int k0) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int i = k0 + srow + 16 * q;
-      pre[q] = (i < ke && sj < ldr) ? *reinterpret_cast<const float4*>(R + (size_t)i * ldr + sj)
-                                    : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-  };
-  if (kb < ke) fetch(kb);
-  for (int k0 = kb; k0 < ke; k0 += 64) {
-    __syncthreads();  // the previous chunk's tile is consumed
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {  // columns past n hold R's zero padding (or nothing: zero)
-      long long* trow = &tile[(srow + 16 * q) * kTileQ + scol];
-      trow[0] = fx_round((double)pre[q].x * dscale);
-      trow[1] = fx_round((double)pre[q].y * dscale);
-      trow[2] = fx_round((double)pre[q].z * dscale);
-      trow[3] = fx_round((double)pre[q].w * dscale);
-    }
-    __syncthreads();
-    if (k0 + 64 < ke) fetch(k0 + 64);
-    const int k = k0 + 16 * g;
-    v4i ua[NCT];
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      const int c = c0 + ct * 16 + lr;
-      ua[ct] = (c < bs && k < ke) ? load16(U + (size_t)c * ldu + k) : (v4i){0, 0, 0, 0};
-    }
-    long long nv[16];
-#pragma unroll
-    for (int t = 0; t < 16; ++t) nv[t] = tile[(16 * g + t) * kTileQ + wid * 16 + lr];
-    v4i db[kDig];
-    fx_operands(nv, db);
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-      for (int t = 0; t < kDig; ++t)
-        acc[ct][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(ua[ct], db[t], acc[ct][t], 0, 0, 0);
-  }
-  const bool split = gridDim.z > 1;
-#pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int c = c0 + ct * 16 + 4 * g + q;
-      if (c < bs && jok) {
-        const long long v = fx_combine(acc[ct], q);
-        long long* o = out + (size_t)c * n + j;
         if (split) atomicAdd(reinterpret_cast<unsigned long long*>(o), (unsigned long long)v);
         else *o = v;
       }
@@ -776,45 +798,43 @@ __global__ void __launch_bounds__(NT) chol_inv_kernel(const double* G, int bs, d
 // multiple of 16 with an identity block, which keeps it block diagonal and leaves the real part of
 // the inverse unchanged.  One workgroup; about 4 (nb - 1) + 2 barriers for nb tiles per side.
 constexpr int kSpdMax = 128;
-constexpr int kSpdFused = 64;  // largest b whose inverse runs inside the contraction launch
+constexpr int kSpdFused = kSpdMax;  // largest b whose inverse runs inside the contraction launch
 __host__ __device__ inline size_t spd_lds_bytes(int bs) {
   const int bp = (bs + 15) & ~15, ld = bp + 1;
-  return 8 * ((size_t)bp * ld + (size_t)(bp / 16) * 256 + 16);
+  return 8 * ((size_t)bp * ld + (size_t)(bp / 16) * 256);
 }
-// NT threads share the tile products (256 for b <= 64, where four waves cover the few tiles and
-// the body fits a contraction's workgroup; 1024 above); wave 0 factors the diagonal blocks.
-// The body runs in its own launch (spd_inv_kernel) or as one extra workgroup of a residual
-// contraction (rv_i8_kernel, utr_i8_kernel), which overlaps the two without a second stream.
+// NT threads share the tile products; wave 0 factors the diagonal blocks.  The body runs as
+// workgroup 0 (512 threads) of the residual contraction of the same half-step, which overlaps the
+// two without a second stream, or in its own launch (spd_inv_kernel).
 template <int NT>
 __device__ __forceinline__ void spd_inv_body(const double* G, int bs, double* Gi, char* smem) {
   constexpr int NWV = NT / 64;
   const int bp = (bs + 15) & ~15, nb = bp / 16, ld = bp + 1;
   double* A = reinterpret_cast<double*>(smem);  // bp x ld
   double* Dg = A + (size_t)bp * ld;             // nb diagonal-block inverses, 16 x 16 row-major
-  double* misc = Dg + (size_t)nb * 256;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int lr = lane & 15, lk = lane >> 4;  // MFMA operand coordinates: row / column lr, k 4 s + lk
-  if (wid == 0) {
-    double tr = 0.0;
-    for (int c = lane; c < bs; c += 64) tr += G[(size_t)c * bs + c];
-    tr = wave_sum_f64(tr);
-    if (lane == 0) misc[0] = 1e-6 * tr / (double)bs;
+  for (int x0 = 0; x0 < bp * bp; x0 += 16 * NT) {  // 16 loads in flight per thread, then the stores
+    double v16[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int x = x0 + tid + NT * q, i = x / bp, j = x - i * bp;
+      if (x < bp * bp && i < bs && j < bs) v16[q] = G[(size_t)i * bs + j];
+      else v16[q] = i == j ? 1.0 : 0.0;
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int x = x0 + tid + NT * q, i = x / bp, j = x - i * bp;
+      if (x < bp * bp) A[(size_t)i * ld + j] = v16[q];
+    }
   }
   __syncthreads();
-  const double eps = misc[0];
-  for (int x0 = 0; x0 < bp * bp; x0 += 8 * NT) {  // 8 loads in flight per thread, then the stores
-    double v8[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int x = x0 + tid + NT * q, i = x / bp, j = x - i * bp;
-      if (x < bp * bp && i < bs && j < bs) v8[q] = G[(size_t)i * bs + j] + (i == j ? eps : 0.0);
-      else v8[q] = i == j ? 1.0 : 0.0;
-    }
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int x = x0 + tid + NT * q, i = x / bp, j = x - i * bp;
-      if (x < bp * bp) A[(size_t)i * ld + j] = v8[q];
-    }
+  if (wid == 0) {  // eps from the trace (summed per lane in c order, then across the wave)
+    double tr = 0.0;
+    for (int c = lane; c < bs; c += 64) tr += A[(size_t)c * ld + c];
+    tr = wave_sum_f64(tr);
+    const double eps = 1e-6 * tr / (double)bs;
+    for (int c = lane; c < bs; c += 64) A[(size_t)c * ld + c] += eps;
   }
   __syncthreads();
   auto at = [&](int bi, int bj) -> double* { return A + (size_t)(16 * bi) * ld + 16 * bj; };
@@ -835,8 +855,16 @@ __device__ __forceinline__ void spd_inv_body(const double* G, int bs, double* Gi
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       const double piv = readlane_f64(a[k], k);
-      const double lkk = piv > 0.0 ? sqrt(piv) : 0.0;
-      const double rr = lkk > 0.0 ? 1.0 / lkk : 0.0;
+      // 1 / sqrt(piv): the hardware estimate and two Newton steps (each squares the relative
+      // error), then sqrt(piv) = piv / sqrt(piv); far shorter than a rounded sqrt and divide
+      double rr = 0.0;
+      if (piv > 0.0) {
+        double y = __builtin_amdgcn_rsq(piv);
+        y = y * fma(-0.5 * piv * y, y, 1.5);
+        y = y * fma(-0.5 * piv * y, y, 1.5);
+        rr = y;
+      }
+      const double lkk = piv * rr;
       rk[k] = rr;
       a[k] = r > k ? a[k] * rr : (r == k ? lkk : a[k]);
 #pragma unroll
@@ -1688,42 +1716,63 @@ static void zero_fill(double* p, long long count, hipStream_t st) {
   hipLaunchKernelGGL(zero_kernel, dim3((unsigned)(nb < 2048 ? nb : 2048)), dim3(256), 0, st, p, count);
 }
 
-// Y^T (bs x m) = (R diag(h) V^T)^T for V = Vt rows, on int8 MFMA with R in fixed point
-// Whether the contraction of R (rows or columns) with bs ternary vectors splits K, so that its
-// output must be cleared first.
-// 16-component tiles per contraction workgroup: six digit accumulators per tile, so four tiles
-// would exceed the register budget of three workgroups per CU (and spill)
-static int contract_nct(int bs) { return bs <= 16 ? 1 : 2; }
+// 16-component tiles per contraction workgroup (six digit accumulators each)
+static int contract_nct(int bs) { return bs <= 16 ? 1 : bs <= 32 ? 2 : 4; }
 
-static bool rw_splits(const BlockLaunch& L, int bs) {
+// launch shape of a contraction of `rows` image rows (K padded to Kp) with bs ternary vectors;
+// returns the number of K splits (> 1: the output must be cleared first)
+static int contract_shape(int rows, int Kp, int bs, int* gx, int* gy, int* kspan) {
   const int nct = contract_nct(bs);
-  int kspan = 0;
-  return i8_splits(((L.m + 63) / 64) * ((bs + 16 * nct - 1) / (16 * nct)), L.n, &kspan) > 1;
+  *gx = (rows + 63) / 64;
+  *gy = (bs + 16 * nct - 1) / (16 * nct);
+  return i8_splits(*gx * *gy, Kp, kspan);
+}
+static bool rw_splits(const BlockLaunch& L, int bs) {
+  int gx, gy, kspan;
+  return contract_shape(L.m, pad64(L.n), bs, &gx, &gy, &kspan) > 1;
 }
 static bool utr_splits(const BlockLaunch& L, int bs) {
-  const int nct = contract_nct(bs);
-  int kspan = 0;
-  return i8_splits(((L.n + 63) / 64) * ((bs + 16 * nct - 1) / (16 * nct)), L.m, &kspan) > 1;
+  int gx, gy, kspan;
+  return contract_shape(L.n, pad64(L.m), bs, &gx, &gy, &kspan) > 1;
 }
 
-static void rw_product(const BlockLaunch& L, const BlockWs& w, const float* h, int bs, int sblk, long long* outT,
+// out (bs x rows, int64) = T N(X)^T from an image of X; with spdG one more workgroup inverts spdG
+static void contract(const BlockWs& w, const int8_t* img, int Kp, int rows, const int8_t* T, int ldt, int bs,
+                     const double* img_unit, long long* out, double* unit, hipStream_t st, bool prezeroed,
+                     const double* spdG, double* spdGi) {
+  const int nct = contract_nct(bs);
+  int gx, gy, kspan;
+  const int gz = contract_shape(rows, Kp, bs, &gx, &gy, &kspan);
+  if (gz > 1 && !prezeroed) zero_fill(reinterpret_cast<double*>(out), (long long)bs * rows, st);
+  {
+    const int nblk = gy * nct * (Kp / 64);  // every component tile the launch reads
+    hipLaunchKernelGGL(swizzle_t_kernel, dim3((nblk + 3) / 4), dim3(256), 0, st, T, ldt, bs, gy * nct, Kp / 64, w.Ts);
+  }
+  const dim3 grid(tile_grid(gx, gy, gz) + (spdG ? 1 : 0));
+  const size_t lds = spdG ? spd_lds_bytes(bs) : 0;
+  if (nct == 1)
+    hipLaunchKernelGGL(img_contract_kernel<1>, grid, dim3(512), lds, st, img, Kp, rows, w.Ts, bs, kspan, gx, gy, gz,
+                       img_unit, out, unit, spdG, spdGi);
+  else if (nct == 2)
+    hipLaunchKernelGGL(img_contract_kernel<2>, grid, dim3(512), lds, st, img, Kp, rows, w.Ts, bs, kspan, gx, gy, gz,
+                       img_unit, out, unit, spdG, spdGi);
+  else
+    hipLaunchKernelGGL(img_contract_kernel<4>, grid, dim3(512), lds, st, img, Kp, rows, w.Ts, bs, kspan, gx, gy, gz,
+                       img_unit, out, unit, spdG, spdGi);
+}
+
+// the images of the current R, with the scales of residual-max slot sblk
+static void digitize(const BlockLaunch& L, const BlockWs& w, int sblk, hipStream_t st) {
+  hipLaunchKernelGGL(digitize_kernel, dim3(w.np / 64, w.mp / 64), dim3(256), 0, st, L.R, L.ldr, L.m, L.n, L.h,
+                     L.EHm, w.rmax, sblk, w.mp, w.np, w.imr, w.imrw, w.imc, w.unit + 2);
+}
+
+// Y^T (bs x m) = (R diag(h) V^T)^T for V = Vt rows (h may be null: R V^T)
+static void rw_product(const BlockLaunch& L, const BlockWs& w, const float* h, int bs, long long* outT,
                        hipStream_t st, bool prezeroed = false, const double* spdG = nullptr,
                        double* spdGi = nullptr) {
-  const int nct = contract_nct(bs);
-  const int gx = (L.m + 63) / 64, gy = (bs + 16 * nct - 1) / (16 * nct);
-  int kspan = 0;
-  const int gz = i8_splits(gx * gy, L.n, &kspan);
-  if (gz > 1 && !prezeroed) zero_fill(reinterpret_cast<double*>(outT), (long long)bs * L.m, st);
-  // with spdG, one more column of workgroups, one of which inverts spdG
-  const dim3 grid(gx + (spdG ? 1 : 0), gy, gz);
-  size_t lds = kTileBytesP;
-  if (spdG && spd_lds_bytes(bs) > lds) lds = spd_lds_bytes(bs);
-  if (nct == 1)
-    hipLaunchKernelGGL(rv_i8_kernel<1>, grid, dim3(256), lds, st, L.R, L.ldr, L.m, L.n, w.Vt, w.ldv, h, L.EHm, bs,
-                       w.rmax, sblk, kspan, outT, w.unit + 1, spdG, spdGi);
-  else
-    hipLaunchKernelGGL(rv_i8_kernel<2>, grid, dim3(256), lds, st, L.R, L.ldr, L.m, L.n, w.Vt, w.ldv, h, L.EHm, bs,
-                       w.rmax, sblk, kspan, outT, w.unit + 1, spdG, spdGi);
+  contract(w, h ? w.imrw : w.imr, w.np, L.m, w.Vt, w.ldv, bs, w.unit + (h ? 3 : 2), outT, w.unit + 1, st, prezeroed,
+           spdG, spdGi);
 }
 
 // G (bs x bs) = T diag(w) T^T for ternary rows T (bs x len, ld ldt); integer-exact without weights
@@ -1742,24 +1791,10 @@ static void gram_product(const BlockWs& w, const int8_t* T, int len, int ldt, co
                      ehm, G, w.gpart, w.gcnt);
 }
 
-// X (bs x n) = U^T R, on int8 MFMA with R in fixed point
-static void utr_product(const BlockLaunch& L, const BlockWs& w, int bs, int sblk, hipStream_t st,
-                        bool prezeroed = false, const double* spdG = nullptr, double* spdGi = nullptr) {
-  const int nct = contract_nct(bs);
-  const int gx = (L.n + 63) / 64, gy = (bs + 16 * nct - 1) / (16 * nct);
-  int kspan = 0;
-  const int gz = i8_splits(gx * gy, L.m, &kspan);
-  if (gz > 1 && !prezeroed) zero_fill(w.X, (long long)bs * L.n, st);
-  // with spdG, one more column of workgroups, one of which inverts spdG
-  const dim3 grid(gx + (spdG ? 1 : 0), gy, gz);
-  size_t lds = kTileBytesQ;
-  if (spdG && spd_lds_bytes(bs) > lds) lds = spd_lds_bytes(bs);
-  if (nct == 1)
-    hipLaunchKernelGGL(utr_i8_kernel<1>, grid, dim3(256), lds, st, L.R, L.ldr, L.m, L.n, w.Ut, w.ldu, bs, w.rmax,
-                       sblk, kspan, w.Xi, w.unit, spdG, spdGi);
-  else
-    hipLaunchKernelGGL(utr_i8_kernel<2>, grid, dim3(256), lds, st, L.R, L.ldr, L.m, L.n, w.Ut, w.ldu, bs, w.rmax,
-                       sblk, kspan, w.Xi, w.unit, spdG, spdGi);
+// X (bs x n) = U^T R
+static void utr_product(const BlockLaunch& L, const BlockWs& w, int bs, hipStream_t st, bool prezeroed = false,
+                        const double* spdG = nullptr, double* spdGi = nullptr) {
+  contract(w, w.imc, w.mp, L.n, w.Ut, w.ldu, bs, w.unit + 2, w.Xi, w.unit, st, prezeroed, spdG, spdGi);
 }
 
 // Li = (G + eps I)^-1 for bs <= kSpdMax, else Li = L^-1 for L L^T = G + eps I
@@ -1877,10 +1912,17 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops, double
         ea = hipFuncSetAttribute(kf, hipFuncAttributeMaxDynamicSharedMemorySize, (int)(64 * 1024));
         if (ea != hipSuccess) return ea;
       }
+      // a contraction launch may carry the inverse of a b <= kSpdMax Gram (its LDS for all groups)
+      const void* con[3] = {(const void*)img_contract_kernel<1>, (const void*)img_contract_kernel<2>,
+                            (const void*)img_contract_kernel<4>};
+      for (const void* kf : con) {
+        ea = hipFuncSetAttribute(kf, hipFuncAttributeMaxDynamicSharedMemorySize, (int)spd_lds_bytes(kSpdMax));
+        if (ea != hipSuccess) return ea;
+      }
       scales_attr[dev] = true;
     }
   }
-  const BlockWs w = carve(L.ws, L.m, L.n, L.b);
+  const BlockWs w = carve(L.ws, L.m, L.n, L.b, L.h != nullptr);
   const int m = L.m, n = L.n;
   hipError_t e = hipSuccess;
   hipLaunchKernelGGL(block_init_kernel, dim3(1), dim3(256), 0, st, L.rowE, m, w.st, w.flags, w.rmax, w.gcnt);
@@ -1913,7 +1955,7 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops, double
       double* y0 = yz ? w.Yt : nullptr;                  // for this U-step
       if (naive_t) {
         if (addback && t == 0) gram_product(w, w.Ut, m, w.ldu, nullptr, 0, bs, w.GU, st);
-        utr_product(L, w, bs, sblk, st, true);
+        utr_product(L, w, bs, st, true);
         if (addback && t == 0) {
           hipLaunchKernelGGL(addback_dot_kernel, dim3(bs), dim3(256), 0, st, w.Xi, w.unit, n, w.Vt, w.ldv, L.h,
                              w.ppo);
@@ -1922,7 +1964,7 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops, double
         }
         select_rows(w.X, w.unit, n, w.ldv, bs, L.tau, hsel, ehsel, w.Vt, w.PHC, w.flags, 0, st, y0, m);
         gram_product(w, w.Vt, n, w.ldv, L.h, L.EHm, bs, w.GV, st);  // for the scales
-        rw_product(L, w, L.h, bs, sblk, w.Yi, st, true);
+        rw_product(L, w, L.h, bs, w.Yi, st, true);
         // the selection reads Yt while the last one also forms Md from it: Md reads the integers
         // (the selection converts its own copy in LDS)
         select_rows(w.Yt, w.unit + 1, m, w.ldu, bs, L.tau, nullptr, 0, w.Ut, w.PHC, w.flags, 0, st, x0, n,
@@ -1931,16 +1973,15 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops, double
         by += 2.0 * rbytes;
         continue;
       }
-      // V-step: G = (U^T U + eps I)^-1 U^T R, rows ternarized with weights h.  For b <= 64 the
-      // inverse runs inside the contraction's launch; above, before it on the same stream (beside
-      // a contraction on a second stream it ran ~1.6x slower, and the events cost more again).
+      // V-step: G = (U^T U + eps I)^-1 U^T R, rows ternarized with weights h.  For b <= kSpdMax the
+      // inverse runs inside the contraction's launch, beside it; above, before it on the stream.
       if (fused) {
         gram_product(w, w.Ut, m, w.ldu, nullptr, 0, bs, w.GU, st);
-        utr_product(L, w, bs, sblk, st, true, w.GU, w.Li);
+        utr_product(L, w, bs, st, true, w.GU, w.Li);
       } else {
         gram_product(w, w.Ut, m, w.ldu, nullptr, 0, bs, w.GU, st);
         chol_inverse(w, w.GU, bs, st);
-        utr_product(L, w, bs, sblk, st, true);
+        utr_product(L, w, bs, st, true);
       }
       if (addback && t == 0) {
         hipLaunchKernelGGL(addback_dot_kernel, dim3(bs), dim3(256), 0, st, w.Xi, w.unit, n, w.Vt, w.ldv, L.h,
@@ -1953,11 +1994,11 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops, double
       // U-step: F^T = (V^T H V + eps I)^-1 (R H V)^T, columns ternarized without weights
       if (fused) {
         gram_product(w, w.Vt, n, w.ldv, L.h, L.EHm, bs, w.GV, st);
-        rw_product(L, w, L.h, bs, sblk, w.Yi, st, true, w.GV, w.Li);
+        rw_product(L, w, L.h, bs, w.Yi, st, true, w.GV, w.Li);
       } else {
         gram_product(w, w.Vt, n, w.ldv, L.h, L.EHm, bs, w.GV, st);
         chol_inverse(w, w.GV, bs, st);
-        rw_product(L, w, L.h, bs, sblk, w.Yi, st, true);
+        rw_product(L, w, L.h, bs, w.Yi, st, true);
       }
       solve(w, bs, w.Yi, w.unit + 1, w.Ft, m, st);
       select_rows(w.Ft, nullptr, m, w.ldu, bs, L.tau, nullptr, 0, w.Ut, w.PHC, w.flags, 0, st, x0, n,
@@ -1991,10 +2032,11 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops, double
   for (int s = 0; s < nblocks; ++s) {
     const int bs = (L.k - s * L.b) < L.b ? (L.k - s * L.b) : L.b;
     const int k0 = s * L.b;
+    digitize(L, w, s, st);  // R as the previous update (or the staging) left it
     // sketch
     hipLaunchKernelGGL(omega_kernel, dim3(256), dim3(256), 0, st, w.Vt, w.ldv, bs, n, (long long)s, w.flags,
                        w.rmax, w.Yt, rw_splits(L, bs) ? (long long)bs * m : 0ll);
-    rw_product(L, w, nullptr, bs, s, w.Yi, st, true);
+    rw_product(L, w, nullptr, bs, w.Yi, st, true);
     select_rows(w.Yt, w.unit + 1, m, w.ldu, bs, L.tau, nullptr, 0, w.Ut, w.PHC, w.flags, 1, st,
                 utr_splits(L, bs) ? w.X : nullptr, n);
     hipLaunchKernelGGL(zero_check_kernel, dim3(1), dim3(256), 0, st, L.R, L.ldr, m, n, w.flags, w.st);
@@ -2048,6 +2090,7 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops, double
       hipLaunchKernelGGL(update_kernel, dim3((n + 63) / 64, (m + 63) / 64), dim3(256), 0, st, L.R, L.ldr, m, n,
                          w.Ut, w.ldu, w.Vt, w.ldv, w.d, bs, w.flags, w.rmax + kMaxWords * ((step + 1) & 1));
       ++step;
+      digitize(L, w, step, st);
       // the old V's weighted Gram for the add-back energy (the U-step overwrites GV)
       gram_product(w, w.Vt, n, w.ldv, L.h, L.EHm, bs, w.GVo, st);
       by += 2.0 * rbytes;

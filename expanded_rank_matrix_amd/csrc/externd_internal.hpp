@@ -75,7 +75,7 @@ struct BlockLaunch {
   int sweeps = 0;      // refinement sweeps after the greedy pass
   int ablation = 0;    // 1: targets without Eq. 3's decorrelation, 2: V-step projection unweighted
 };
-size_t block_workspace_bytes(int m, int n, int b);
+size_t block_workspace_bytes(int m, int n, int b, bool weighted);
 // flops: multiply-adds of the residual by ternary operands x 2; bytes: residual bytes that the
 // contractions read and the updates read and write (4 m n per pass)
 hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops, double* bytes);
