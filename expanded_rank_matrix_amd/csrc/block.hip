@@ -1035,7 +1035,9 @@ __global__ void __launch_bounds__(256) apply_kernel(const double* __restrict__ A
 // Workgroup: NCT 16-column strips of B (staged in LDS) x all bs rows; wave w takes the row tiles
 // w, w + 4, ...  Every A operand of the whole K range (NKS k-steps of 4) is loaded into registers
 // before the strips are staged, so the workgroup waits for one round of loads, then runs its MFMAs
-// back to back, each A operand serving the NCT strips.
+// back to back, each A operand serving the NCT strips.  K is walked in the order k = NKS lk + st
+// (step st, lane group lk): any order gives the same products, and in this one a lane's A
+// operands are NKS consecutive entries of its row, loaded 16 bytes at a time.
 // Bm holds a contraction's int64 output in units of *bunit.
 template <int NRW, int NKS, int NCT>
 __global__ void __launch_bounds__(256) apply_strip_kernel(const double* __restrict__ A, int bs, const long long* Bm,
@@ -1053,11 +1055,17 @@ __global__ void __launch_bounds__(256) apply_strip_kernel(const double* __restri
     for (int ct = 0; ct < NCT; ++ct) acc[u][ct] = (dbl4){0.0, 0.0, 0.0, 0.0};
     const int r = (wid + 4 * u) * 16 + lr;
     const bool rok = wid + 4 * u < ntiles && r < bs;
-    const double* ap = A + (size_t)(rok ? r : 0) * bs;
+    const double* ap = A + (size_t)(rok ? r : 0) * bs + NKS * lk;
+    if ((bs & 1) == 0 && rok && NKS * lk + NKS <= bs) {  // 16-byte aligned and inside the row
 #pragma unroll
-    for (int st = 0; st < NKS; ++st) {
-      const int k = 4 * st + lk;
-      av[st][u] = (rok && k < bs) ? ap[k] : 0.0;
+      for (int st = 0; st < NKS; st += 2) {
+        const double2 v = *reinterpret_cast<const double2*>(ap + st);
+        av[st][u] = v.x;
+        av[st + 1][u] = v.y;
+      }
+    } else {
+#pragma unroll
+      for (int st = 0; st < NKS; ++st) av[st][u] = (rok && NKS * lk + st < bs) ? ap[st] : 0.0;
     }
   }
   // the strips: (4 NKS) x 16 NCT values, NKS NCT / 4 per thread, all loads issued before the
@@ -1078,7 +1086,7 @@ __global__ void __launch_bounds__(256) apply_strip_kernel(const double* __restri
   __syncthreads();
 #pragma unroll
   for (int st = 0; st < NKS; ++st) {
-    const int k = 4 * st + lk;
+    const int k = NKS * lk + st;
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
       const double bv = k < bs ? Bs[k][16 * ct + lr] : 0.0;
@@ -1392,63 +1400,222 @@ __global__ void __launch_bounds__(256) scales_kernel(const double* Md, const dou
   }
 }
 
-// ---- update: R <- fl32(R - U diag(d) V^T), fp64 MFMA with K = bs ----------------------------
-// Tile 64 x 64 of R; wave w owns rows 16w..16w+15 and four 16-column strips.
-// A[i][k] = d_k U[k][i], B[k][j] = V[k][j].  The operands are staged 64 components at a time
-// (10 KB of LDS), so that many workgroups share a CU: the kernel streams R once each way and
-// needs many loads in flight.  Each lane's 16 entries of R are loaded before anything else
-// (the dead-residual flag included), in the MFMA output layout: lane l of wave w holds rows
-// 16 w + l / 16 + 4 r, column 16 t + l % 16 of strip t.  Entries whose product is zero are not
-// written back.
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) update_kernel(float* R, int ldr, int m, int n, const int8_t* Ut, int ldu,
+// ---- update: R <- fl32(R - U diag(d) V^T) -----------------------------------------------------
+// The inner sum s_ij = sum_c d_c u_ic v_jc is exact whenever every d_c is an integer multiple of
+// 2^(E - 45) with max |d_c| < 2^E: its partial sums, in any order, are then multiples of that
+// unit below 2^(E + 7) for b <= 128 components (2^(E + 8) for 256), within fp64's 53 bits.  In
+// that case (always, unless the block's scales span more than 2^22 or so) the kernel forms
+// D_c = d_c 2^(45 - E) in int64 and takes the sum on int8 MFMA: six signed 8-bit digits of D_c
+// (of -D_c where u_ic = -1) times the ternary operands, recombined exactly in int64; otherwise it
+// sums on fp64 MFMA.  Both give the exact s_ij, the same value as a sum in fp64 in any order.
+// Tile 64 x 64 of R; wave w owns rows 16w..16w+15 and four 16-column strips.  The ternary
+// operands are staged 64 components at a time, transposed (component index fastest) for the int8
+// products.  Each lane's 16 entries of R are loaded before anything else (the dead-residual flag
+// included), in the MFMA output layout: lane l of wave w holds rows 16 w + 4 (l / 16) + r, column
+// 16 t + l % 16 of strip t.  Entries whose sum is zero are not written back.
+constexpr int kUpdPitch = 80;    // bytes per staged row of the fp64 path (64 components + padding)
+constexpr int kUpdPitch2 = 144;  // bytes per staged row of the int8 path (128 components + padding)
+
+// signed 8-bit digits of n (|n| < 2^45): n = sum_t 256^t d_t
+__device__ __forceinline__ void fx_digits_one(long long n, int8_t (&d)[kDig]) {
+  const unsigned long long bv = (unsigned long long)(n + 0x8080808080ll);
+#pragma unroll
+  for (int t = 0; t < kDig - 1; ++t) d[t] = (int8_t)((unsigned)((bv >> (8 * t)) & 0xFFu) ^ 0x80u);
+  d[kDig - 1] = (int8_t)(unsigned)((bv >> 40) & 0xFFu);
+}
+
+// 4 x 4 byte transpose: out[q] byte e = in[e] byte q
+__device__ __forceinline__ void transpose4x4(const unsigned (&w)[4], unsigned (&o)[4]) {
+  const unsigned a = __builtin_amdgcn_perm(w[1], w[0], 0x05010400u), b = __builtin_amdgcn_perm(w[1], w[0], 0x07030602u);
+  const unsigned c = __builtin_amdgcn_perm(w[3], w[2], 0x05010400u), d = __builtin_amdgcn_perm(w[3], w[2], 0x07030602u);
+  o[0] = __builtin_amdgcn_perm(c, a, 0x05040100u);
+  o[1] = __builtin_amdgcn_perm(c, a, 0x07060302u);
+  o[2] = __builtin_amdgcn_perm(d, b, 0x05040100u);
+  o[3] = __builtin_amdgcn_perm(d, b, 0x07060302u);
+}
+
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) update_kernel(float* R, int ldr, int m, int n, const int8_t* Ut, int ldu,
                                                      const int8_t* Vt, int ldv, const float* dvec, int bs,
                                                      const int* flags, unsigned* rmax_next) {
-  __shared__ __align__(16) int8_t Us[64][64 + 16];
-  __shared__ __align__(16) int8_t Vs[64][64 + 16];
+  // int8 path: [i][c] for 128 components; fp64 path: [c][i] for 64
+  __shared__ __align__(16) int8_t Us[64 * kUpdPitch2];
+  __shared__ __align__(16) int8_t Vs[64 * kUpdPitch2];
+  __shared__ __align__(16) int8_t dg[2][kDig][256];  // digits of D_c and of -D_c
   __shared__ float ds[64];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
+  // every global load the int8 path needs for its first 128 components is issued here, before
+  // anything waits: R, the scales, and the ternary pieces (thread (cq, pq): components
+  // 4 cq .. + 3 of each 64-chunk, positions 4 pq .. + 3 of the tile; rows of Ut / Vt are
+  // zero-padded to a multiple of 16, so a 4-byte piece is inside them or past them)
   float rv[4][4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int j = j0 + t * 16 + (lane & 15);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int i = i0 + wid * 16 + (lane >> 4) + 4 * r;
+      const int i = i0 + wid * 16 + (lane >> 4) * 4 + r;
       rv[t][r] = (i < m && j < n) ? R[(size_t)i * ldr + j] : 0.0f;
     }
   }
+  float dl[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) dl[q] = lane + 64 * q < bs ? dvec[lane + 64 * q] : 0.0f;
+  const int cq = tid >> 4, pq = tid & 15;
+  unsigned wu[2][4], wv[2][4];
+  auto stage_loads = [&](int kc) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int c = kc + 64 * h + 4 * cq + e;
+        const bool oku = c < bs && i0 + 4 * pq < ldu, okv = c < bs && j0 + 4 * pq < ldv;
+        const unsigned a = *reinterpret_cast<const unsigned*>(oku ? Ut + (size_t)c * ldu + i0 + 4 * pq : Ut);
+        const unsigned b = *reinterpret_cast<const unsigned*>(okv ? Vt + (size_t)c * ldv + j0 + 4 * pq : Vt);
+        wu[h][e] = oku ? a : 0u;
+        wv[h][e] = okv ? b : 0u;
+      }
+  };
+  stage_loads(0);
   if (flags[0]) return;
+  // the scales' exponent and whether they are exact on the grid 2^(E - 45) (every wave alike)
+  unsigned mb = 0u;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const unsigned b = __float_as_uint(dl[q]) & 0x7FFFFFFFu;
+    mb = b > mb ? b : mb;
+  }
+  mb = wave_max_u32(mb);
+  int E = 0;
+  if (mb != 0u) frexp((double)__uint_as_float(mb), &E);  // max |d| < 2^E
+  const int f = 45 - E;
+  unsigned inexact = 0u;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const double x = ldexp((double)dl[q], f);
+    inexact |= x != rint(x) ? 1u : 0u;
+  }
+  const bool use_i8 = mb != 0u && wave_sum_u32(inexact) == 0u;
   const int bs4 = (bs + 3) & ~3;
-  dbl4 acc[4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) acc[t] = (dbl4){0.0, 0.0, 0.0, 0.0};
-  for (int kc = 0; kc < bs4; kc += 64) {
-    const int kn = bs4 - kc < 64 ? bs4 - kc : 64;
-    if (kc > 0) __syncthreads();  // the previous chunk's operands are consumed
-    // 16-byte pieces: rows of Ut / Vt are zero-padded to a multiple of 16, and i0, j0 are
-    // multiples of 64, so a piece is either inside the padded row or past it
+  double sv[4][4];
+  if (use_i8) {
+    // digit tables: dg[0][t][c] of D_c, dg[1][t][c] of -D_c (zero past bs); wave w fills
+    // components 64 w .. 64 w + 63 from its lanes' scales (dl[w] of lane c - 64 w)
     {
-      const int x = tid, c = x >> 2, q = (x & 3) * 16, cg = kc + c;
-      const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-      if (c < kn) {
-        *reinterpret_cast<uint4*>(&Us[c][q]) =
-            (cg < bs && i0 + q < ldu) ? *reinterpret_cast<const uint4*>(Ut + (size_t)cg * ldu + i0 + q) : z;
-        *reinterpret_cast<uint4*>(&Vs[c][q]) =
-            (cg < bs && j0 + q < ldv) ? *reinterpret_cast<const uint4*>(Vt + (size_t)cg * ldv + j0 + q) : z;
-      }
-    }
-    if (tid < kn) ds[tid] = kc + tid < bs ? dvec[kc + tid] : 0.0f;
-    __syncthreads();
-    for (int k0 = 0; k0 < kn; k0 += 4) {
-      const int k = k0 + (lane >> 4);
-      const double a = (double)ds[k] * (double)Us[k][wid * 16 + (lane & 15)];
+      int8_t dp[kDig], dn[kDig];
+      float dw = dl[0];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const double bv = (double)Vs[k][t * 16 + (lane & 15)];
-        acc[t] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, bv, acc[t], 0, 0, 0);
+      for (int q = 1; q < 4; ++q) dw = wid == q ? dl[q] : dw;
+      const long long D = (long long)ldexp((double)dw, f);
+      fx_digits_one(D, dp);
+      fx_digits_one(-D, dn);
+#pragma unroll
+      for (int t = 0; t < kDig; ++t) {
+        dg[0][t][tid] = dp[t];
+        dg[1][t][tid] = dn[t];
       }
     }
+    v4i acc[4][kDig];
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2)
+#pragma unroll
+      for (int t = 0; t < kDig; ++t) acc[s2][t] = (v4i){0, 0, 0, 0};
+    const int lr = lane & 15, g = lane >> 4;
+    for (int kc = 0; kc < bs; kc += 128) {
+      if (kc > 0) {
+        __syncthreads();  // the previous 128 components' operands are consumed
+        stage_loads(kc);
+      }
+      // transposed into [position][component] (128 components per row)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        unsigned ou[4], ov[4];
+        transpose4x4(wu[h], ou);
+        transpose4x4(wv[h], ov);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          *reinterpret_cast<unsigned*>(&Us[(4 * pq + q) * kUpdPitch2 + 64 * h + 4 * cq]) = ou[q];
+          *reinterpret_cast<unsigned*>(&Vs[(4 * pq + q) * kUpdPitch2 + 64 * h + 4 * cq]) = ov[q];
+        }
+      }
+      __syncthreads();
+      const int nsub = bs - kc < 128 ? (bs - kc + 63) / 64 : 2;
+      for (int h = 0; h < nsub; ++h) {
+        // A_t[i][c] = digit t of u_ic D_c (row i = 16 w + lr, c = kc + 64 h + 16 g ..): the bytes
+        // of u (1, -1 = 0xFF, 0) as masks over the digit bytes of D_c and -D_c
+        const v4i u4 = *reinterpret_cast<const v4i*>(&Us[(wid * 16 + lr) * kUpdPitch2 + 64 * h + 16 * g]);
+        unsigned pm[4], nm[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const unsigned u = (unsigned)u4[q];
+          const unsigned nb = (u >> 1) & 0x01010101u, pb = (u & 0x01010101u) ^ nb;
+          nm[q] = (nb << 8) - nb;  // 0xFF in the bytes where u = -1
+          pm[q] = (pb << 8) - pb;  // 0xFF where u = 1
+        }
+        v4i bv[4];
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2)
+          bv[s2] = *reinterpret_cast<const v4i*>(&Vs[(s2 * 16 + lr) * kUpdPitch2 + 64 * h + 16 * g]);
+        const int cb = kc + 64 * h + 16 * g;
+#pragma unroll
+        for (int t = 0; t < kDig; ++t) {
+          const v4i dp = *reinterpret_cast<const v4i*>(&dg[0][t][cb]);
+          const v4i dn = *reinterpret_cast<const v4i*>(&dg[1][t][cb]);
+          v4i at;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) at[q] = (int)(((unsigned)dp[q] & pm[q]) | ((unsigned)dn[q] & nm[q]));
+#pragma unroll
+          for (int s2 = 0; s2 < 4; ++s2)
+            acc[s2][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(at, bv[s2], acc[s2][t], 0, 0, 0);
+        }
+      }
+    }
+    // D(i, j) = sum_c A[i][c] V[j][c]: lane l, register r holds row 4 (l / 16) + r, column l % 16
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sv[s2][r] = ldexp((double)fx_combine(acc[s2], r), -f);
+  } else {
+    dbl4 acc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[t] = (dbl4){0.0, 0.0, 0.0, 0.0};
+    for (int kc = 0; kc < bs4; kc += 64) {
+      const int kn = bs4 - kc < 64 ? bs4 - kc : 64;
+      __syncthreads();  // the previous chunk's operands are consumed
+      // 16-byte pieces: rows of Ut / Vt are zero-padded to a multiple of 16, and i0, j0 are
+      // multiples of 64, so a piece is either inside the padded row or past it
+      {
+        const int x = tid, c = x >> 2, q = (x & 3) * 16, cg = kc + c;
+        if (c < kn) {
+          // an out-of-range piece reads row 0's first bytes and is replaced by zeros
+          const bool oku = cg < bs && i0 + q < ldu, okv = cg < bs && j0 + q < ldv;
+          uint4 a = *reinterpret_cast<const uint4*>(oku ? Ut + (size_t)cg * ldu + i0 + q : Ut);
+          uint4 b = *reinterpret_cast<const uint4*>(okv ? Vt + (size_t)cg * ldv + j0 + q : Vt);
+          if (!oku) a = make_uint4(0u, 0u, 0u, 0u);
+          if (!okv) b = make_uint4(0u, 0u, 0u, 0u);
+          *reinterpret_cast<uint4*>(&Us[c * kUpdPitch + q]) = a;
+          *reinterpret_cast<uint4*>(&Vs[c * kUpdPitch + q]) = b;
+        }
+      }
+      if (tid < kn) ds[tid] = kc + tid < bs ? dvec[kc + tid] : 0.0f;
+      __syncthreads();
+      // A[i][k] = d_k U[k][i], B[k][j] = V[k][j].  This MFMA leaves row a + 4 r of its output in
+      // lane 16 a + j, register r; A's rows are supplied permuted (sigma(x) = 4 (x % 4) + x / 4)
+      // so that lane l, register r holds row 4 (l / 16) + r, the layout of R's values above
+      for (int k0 = 0; k0 < kn; k0 += 4) {
+        const int k = k0 + (lane >> 4), x = lane & 15;
+        const double a = (double)ds[k] * (double)Us[k * kUpdPitch + wid * 16 + 4 * (x & 3) + (x >> 2)];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const double bvv = (double)Vs[k * kUpdPitch + t * 16 + (lane & 15)];
+          acc[t] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, bvv, acc[t], 0, 0, 0);
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sv[t][r] = acc[t][r];
   }
   unsigned mx = 0u;  // largest |R| of the tile after the update (fp32 bits)
 #pragma unroll
@@ -1456,12 +1623,11 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(6))) u
     const int j = j0 + t * 16 + (lane & 15);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int i = i0 + wid * 16 + (lane >> 4) + 4 * r;
+      const int i = i0 + wid * 16 + (lane >> 4) * 4 + r;
       if (i < m && j < n) {
-        const double sv = acc[t][r];
         float x = rv[t][r];
-        if (sv != 0.0) {
-          x = (float)((double)x - sv);
+        if (sv[t][r] != 0.0) {
+          x = (float)((double)x - sv[t][r]);
           R[(size_t)i * ldr + j] = x;
         }
         const unsigned b = __float_as_uint(x) & 0x7FFFFFFFu;

@@ -68,6 +68,29 @@ def test_scaled_blocks_free_run_and_replay(name, m, n, mu, block):
     assert P.monotone(g["energy"]), label
 
 
+def test_update_wide_scale_range():
+    """Two entries ~3e6 times the noise: the first block's scales span more than 2^26, so some
+    are not multiples of 2^(E - 45) (max |d| < 2^E) and the residual update cannot take its int8
+    path; it sums in fp64 instead.  The next blocks, which see that update, still match the
+    oracle.  (Noise far smaller still would fall below the contractions' fixed-point grid, which
+    is relative to max |R|, and cost the small scales their last digits.)"""
+    rng = np.random.default_rng(7)
+    m, n, b = 96, 80, 8
+    A = (rng.standard_normal((m, n)) * 1e-2).astype(np.float32)
+    A[3, 5] = 3.0e4
+    A[10, 40] = -2.0e4
+    g, o = run_both(A, 0.5, 0.3, None, 2, b)
+    d0 = np.abs(g["D"][:b].astype(np.float64))
+    d0 = d0[d0 > 0]
+    e = np.frexp(d0.max())[1]
+    off_grid = int(np.sum(np.ldexp(d0, 45 - e) != np.rint(np.ldexp(d0, 45 - e))))
+    assert off_grid > 0, "the block's scales must defeat the fixed-point grid of the update"
+    f = P.check_free_run(g, o, "wide-range", b, alt=(A, 0.5, 0.3, None, 2, b))
+    print(f"wide-range: identical prefix {f} of {g['k']}, d span {d0.max() / d0.min():.3e}, "
+          f"{off_grid} scales off the grid")
+    assert f >= 2 * b
+
+
 def test_block_determinism():
     A, h = inputs.make_input("down2560x9728", m=512, n=700)
     g1 = P.gpu_decompose(A, 1.0, 0.2, h, 3, 32)
