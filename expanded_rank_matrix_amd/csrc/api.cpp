@@ -160,6 +160,7 @@ int externd_decompose_ex(const float* A, int64_t m, int64_t n, float mu, float t
     o_xf = take((size_t)4 * grid * sizeof(double));
     o_rsg = take((size_t)grid * mi * sizeof(double));
   } else {
+    o_RT = take((size_t)ni * ldt * sizeof(float));
     o_blk = take(block_workspace_bytes(mi, ni, bi, h != nullptr));
   }
   Workspace ws(st);
@@ -244,11 +245,15 @@ int externd_decompose_ex(const float* A, int64_t m, int64_t n, float mu, float t
     HIP_OR_FAIL(seq_launch(L, st));
     HIP_OR_FAIL(hipEventRecord(e1, st));
   } else {
+    float* RT = reinterpret_cast<float*>(base + o_RT);
+    HIP_OR_FAIL(stage_transpose(A, mi, ni, RT, ldt, st));
     BlockLaunch L;
     L.R = R;
+    L.RT = RT;
     L.m = mi;
     L.n = ni;
     L.ldr = ldr;
+    L.ldt = ldt;
     L.k = ki;
     L.b = bi;
     L.T = als_iters;

@@ -27,6 +27,7 @@
 // K = b and one fp32 rounding per entry.  Selections use the same exact projection as the
 // sequential path, one workgroup per component row.
 #include "externd_internal.hpp"
+#include <type_traits>
 #include "select.hpp"
 
 namespace externd {
@@ -64,15 +65,12 @@ struct BlockWs {
   double* GVo;     // b x b: weighted Gram of the old V
   double* ppo;     // b: u_c^T (R + X) H v_c of the old components
   float* dold;     // b: old scales
-  double* unit;    // [0] unit of X, [1] unit of Yt: the fixed-point grid of the last contraction;
-                   // [2] unit of R's images, [3] of the image of R H
+  double* unit;    // [0] unit of X, [1] unit of Yt: the fixed-point grid of the last contraction
   long long* Xi;   // X and Yt as the contractions write them (exact integers)
   long long* Yi;
-  int mp, np;      // m and n padded to 64: image row lengths (per digit) and row counts
-  int8_t* imr;     // mp x 6 np: image of R's rows
-  int8_t* imrw;    // mp x 6 np: image of the rows of R H (imr when unweighted)
-  int8_t* imc;     // np x 6 mp: image of R's columns
-  int8_t* Ts;      // the ternary operand of a contraction, swizzled (b rounded up to 64 x max(mp, np))
+  float* hpad;     // the column weights, zero-padded to a multiple of 64 (weighted only)
+  int8_t* Ts;      // the ternary operand of a contraction, swizzled (b rounded up to 64 x max(m, n)
+                   // rounded up to 64)
 };
 
 constexpr int kMaxWords = 64;      // words per residual-max slot (one per lane of a wave)
@@ -109,10 +107,7 @@ static void ws_layout(int m, int n, int b, bool weighted, F&& take) {
   take((void**)nullptr, (size_t)kGramSplit * kGramTiles * 256 * 8);  // split-K Gram partial tiles
   take((void**)nullptr, (size_t)kGramTiles * 4);                     // their arrival counters
   take((void**)nullptr, 64);                                         // contraction units
-  const size_t img = (size_t)((m + 63) & ~63) * (size_t)((n + 63) & ~63) * 6;
-  take((void**)nullptr, img);                                        // images of R
-  take((void**)nullptr, img);
-  take((void**)nullptr, weighted ? img : 0);                         // image of R H
+  take((void**)nullptr, weighted ? (size_t)((n + 63) & ~63) * 4 : 0);            // padded weights
   take((void**)nullptr, (size_t)((b + 63) & ~63) * ((mx + 63) & ~(size_t)63));  // swizzled T
 }
 
@@ -154,13 +149,9 @@ static BlockWs carve(void* base, int m, int n, int b, bool weighted) {
   w.gpart = static_cast<double*>(ptrs[q++]);
   w.gcnt = static_cast<unsigned*>(ptrs[q++]);
   w.unit = static_cast<double*>(ptrs[q++]);
-  w.imr = static_cast<int8_t*>(ptrs[q++]);
-  w.imc = static_cast<int8_t*>(ptrs[q++]);
-  w.imrw = weighted ? static_cast<int8_t*>(ptrs[q++]) : w.imr;
-  if (!weighted) ++q;  // the empty slot of the image of R H
+  w.hpad = weighted ? static_cast<float*>(ptrs[q]) : nullptr;
+  ++q;
   w.Ts = static_cast<int8_t*>(ptrs[q++]);
-  w.mp = (m + 63) & ~63;
-  w.np = (n + 63) & ~63;
   w.Xi = reinterpret_cast<long long*>(w.X);
   w.Yi = reinterpret_cast<long long*>(w.Yt);
   return w;
@@ -309,111 +300,70 @@ __device__ __forceinline__ bool tile_decode(int w, int half, int gx, int gy, int
 }
 static int tile_grid(int gx, int gy, int gz) { return 8 * ((((gx * gz + 7) / 8) * gy + 1) / 2); }
 
-// ---- the residual's fixed-point image.  After every change of R (staging, each block's update,
-// a refit's add-back) one pass writes the digits of N(x) for every entry in the layouts the
-// contractions read, so that the block's seven contractions of one R stream int8 digits straight
-// into the MFMA; converting R inside each contraction cost fp64 arithmetic for every entry and
-// component group, several times the time of the products themselves.
-// Image of an a x K matrix X (rows padded to a multiple of 64, K to Kp, a multiple of 64, with
-// zeros), stored in the order the contraction's waves consume it: one 6 KB block per 16 rows and
-// 64-wide k chunk, holding for each digit t (1 KB) the MFMA operand of every lane l = 16 g + rr
-// (16 B: digit t of N(X_r,k) for r = 16 p + rr and k = 64 c + 16 g .. + 15, block (p, c)).  Each
-// load instruction of a wave then reads 1 KB contiguous, and a wave walks one contiguous 16-row
-// strip.  Three images: of R's rows (R Omega), of the rows of R H (R H V; the same buffer when
-// unweighted) and of R's columns (U^T R), this last one with rows j and k = i.
-constexpr int kImgBlock = 6144;  // bytes of one 16-row x 64-k block
 __host__ __device__ inline int pad64(int x) { return (x + 63) & ~63; }
 
-// One 64 x 64 tile of R per workgroup: row images from the tile as loaded (float4 rows), the
-// column image from its unweighted fixed-point values transposed through LDS.
-__global__ void __launch_bounds__(256) digitize_kernel(const float* R, int ldr, int m, int n, const float* h,
-                                                       int ehm, const unsigned* rmax, int sblk, int mp, int np,
-                                                       int8_t* imr, int8_t* imrw, int8_t* imc, double* units) {
-  __shared__ long long tile[64][65];
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int j0 = blockIdx.x * 64, i0 = blockIdx.y * 64;
-  const int scu = fx_scale(rmax, sblk, 0);
-  const int scw = h ? fx_scale(rmax, sblk, ehm) : scu;
-  const double du = ldexp(1.0, scu), dw = ldexp(1.0, scw);
-  if (blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) {
-    units[0] = ldexp(1.0, -scu);  // R's images
-    units[1] = ldexp(1.0, -scw);  // the image of R H
-  }
-  const int srow = tid >> 4, scol = 4 * (tid & 15), k = j0 + scol;
-  const int nch = np / 64;  // k chunks per row image
-  float hv[4] = {0.f, 0.f, 0.f, 0.f};
-  if (h) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) hv[e] = k + e < n ? h[k + e] : 0.f;
-  }
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int i = i0 + srow + 16 * q;
-    // R rows are padded to a multiple of 4 floats, so the float4 at k < n is inside the row
-    const float4 x4 = (i < m && k < n) ? *reinterpret_cast<const float4*>(R + (size_t)i * ldr + k)
-                                       : make_float4(0.f, 0.f, 0.f, 0.f);
-    const float xv[4] = {x4.x, x4.y, x4.z, x4.w};
-    long long nu[4], nw[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const bool in = i < m && k + e < n;
-      nu[e] = in ? fx_round((double)xv[e] * du) : 0ll;
-      nw[e] = in ? fx_round(((double)xv[e] * (double)hv[e]) * dw) : 0ll;
-    }
-    unsigned wd[kDig];
-    fx_digits6(nu[0], nu[1], nu[2], nu[3], wd);
-    // block (i / 16, k / 64), lane 16 ((k % 64) / 16) + i % 16, bytes k % 16 .. + 3
-    const size_t go = ((size_t)(i >> 4) * nch + (k >> 6)) * kImgBlock + ((((k & 63) >> 4) << 4) + (i & 15)) * 16 +
-                      (k & 15);
-    int8_t* pr = imr + go;
-#pragma unroll
-    for (int t = 0; t < kDig; ++t) *reinterpret_cast<unsigned*>(pr + 1024 * t) = wd[t];
-    if (h) {
-      fx_digits6(nw[0], nw[1], nw[2], nw[3], wd);
-      pr = imrw + go;
-#pragma unroll
-      for (int t = 0; t < kDig; ++t) *reinterpret_cast<unsigned*>(pr + 1024 * t) = wd[t];
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) tile[srow + 16 * q][scol + e] = nu[e];
-  }
-  __syncthreads();
-  // column image: wave w takes tile columns 16 w .. 16 w + 15; lane 4 jj + g writes the operands
-  // of column 16 w + jj for rows 16 g .. 16 g + 15 (so each digit's stores fill 1 KB)
-  const int jj = lane >> 2, g = lane & 3, cl = 16 * wid + jj;
-  long long nv[16];
-#pragma unroll
-  for (int r = 0; r < 16; ++r) nv[r] = tile[16 * g + r][cl];
-  v4i op[kDig];
-  fx_operands(nv, op);
-  const int j = j0 + cl;
-  int8_t* pc = imc + ((size_t)(j >> 4) * (mp / 64) + (i0 >> 6)) * kImgBlock + (16 * g + (j & 15)) * 16;
-#pragma unroll
-  for (int t = 0; t < kDig; ++t) *reinterpret_cast<v4i*>(pc + 1024 * t) = op[t];
-}
-
-// The ternary operand in the same order: one 1 KB block per 16 components and 64-wide k chunk,
-// lane l = 16 g + cc holding T[16 p + cc][64 c + 16 g .. + 15] (block (p, c)); components past
-// bs and k past ldt are zero.  Written from the row-major T before each contraction, so that
-// every operand load of a wave reads 1 KB contiguous instead of 64 bytes of 16 rows.
+// ---- contraction operands.  The k order inside each 64-wide chunk is free (the products are
+// summed over it), so it is chosen for the loads: lane group g of a wave takes, for each of the
+// four 16-wide quarters q of the chunk, the 4 consecutive k = 16 q + 4 g .. + 3; byte 4 q + e of
+// the lane's 16-byte MFMA operand is then k = 16 q + 4 g + e.  A wave's float4 loads of R read 64
+// contiguous bytes of each of its 16 rows per instruction.
+//
+// The ternary operand in that order, swizzled so that each operand load of a wave reads 1 KB
+// contiguous: one 1 KB block per 16 components and chunk, lane l = 16 g + cc holding the operand
+// of component 16 p + cc (block (p, c)); components past bs and k past ldt are zero.
 __global__ void __launch_bounds__(256) swizzle_t_kernel(const int8_t* T, int ldt, int bs, int nct, int nchunk,
                                                         int8_t* Ts) {
   const int blk = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (blk >= nct * nchunk) return;
   const int p = blk / nchunk, ch = blk - p * nchunk;
-  const int c = 16 * p + (lane & 15), k = 64 * ch + 16 * (lane >> 4);
-  const v4i v = (c < bs && k < ldt) ? load16(T + (size_t)c * ldt + k) : (v4i){0, 0, 0, 0};
+  const int c = 16 * p + (lane & 15), g = lane >> 4;
+  v4i v;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int k = 64 * ch + 16 * q + 4 * g;  // ldt is a multiple of 16: the word is inside or past
+    v[q] = (c < bs && k < ldt) ? *reinterpret_cast<const int*>(T + (size_t)c * ldt + k) : 0;
+  }
   *reinterpret_cast<v4i*>(Ts + (size_t)blk * 1024 + 16 * lane) = v;
 }
 
-// out[c][r] (+)= sum_{k in this split} N(X_rk) T[c][k] from an image of X (a rows, Kp bytes per
-// digit) and the swizzled T, in units *img_unit, copied to *unit.  Workgroup: 64 rows (16 per
-// wave) x 16 NCT components; per 64-wide k chunk each lane loads 96 bytes of digits and 16 NCT
-// bytes of T, the next chunk's loads in flight while the current one is multiplied.
-template <int NCT>
+// The six digit words of four fp32 values x (times weights w, all in fp64): fma(x, w 2^f, 1.5 2^52)
+// rounds x w 2^f to the nearest integer N (ties to even, as rint) in the low bits of the mantissa,
+// exactly for |N| < 2^51; the bit pattern minus the constant's is N, and adding the digit bias of
+// fx_digits6 gives its biased form directly.
+__device__ __forceinline__ void fx_digits_of(const float (&x)[4], const double (&ws)[4], unsigned (&w)[kDig]) {
+  constexpr double kMagic = 6755399441055744.0;                        // 1.5 2^52
+  constexpr unsigned long long kOff = 0x4338000000000000ull - 0x8080808080ull;  // its bits, less the bias
+  unsigned long long bv[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) bv[e] = (unsigned long long)__double_as_longlong(fma((double)x[e], ws[e], kMagic)) - kOff;
+  const unsigned l0 = (unsigned)bv[0], l1 = (unsigned)bv[1], l2 = (unsigned)bv[2], l3 = (unsigned)bv[3];
+  const unsigned h0 = (unsigned)(bv[0] >> 32), h1 = (unsigned)(bv[1] >> 32), h2 = (unsigned)(bv[2] >> 32),
+                 h3 = (unsigned)(bv[3] >> 32);
+  const unsigned x01lo = __builtin_amdgcn_perm(l1, l0, 0x05010400u);
+  const unsigned x01hi = __builtin_amdgcn_perm(l1, l0, 0x07030602u);
+  const unsigned x23lo = __builtin_amdgcn_perm(l3, l2, 0x05010400u);
+  const unsigned x23hi = __builtin_amdgcn_perm(l3, l2, 0x07030602u);
+  const unsigned y01 = __builtin_amdgcn_perm(h1, h0, 0x05010400u);
+  const unsigned y23 = __builtin_amdgcn_perm(h3, h2, 0x05010400u);
+  w[0] = __builtin_amdgcn_perm(x23lo, x01lo, 0x05040100u) ^ 0x80808080u;
+  w[1] = __builtin_amdgcn_perm(x23lo, x01lo, 0x07060302u) ^ 0x80808080u;
+  w[2] = __builtin_amdgcn_perm(x23hi, x01hi, 0x05040100u) ^ 0x80808080u;
+  w[3] = __builtin_amdgcn_perm(x23hi, x01hi, 0x07060302u) ^ 0x80808080u;
+  w[4] = __builtin_amdgcn_perm(y23, y01, 0x05040100u) ^ 0x80808080u;
+  w[5] = __builtin_amdgcn_perm(y23, y01, 0x07060302u);
+}
+
+// out[c][r] (+)= sum_{k in this split} N(x_rk) T[c][k] for the rows r of X (R, or R^T), with
+// x_rk = X_rk (times h_k when HW) and N the fixed-point image at the scale of residual-max slot
+// sblk, in units *unit = 2^-f.  Workgroup: two tiles of 64 rows (16 per wave) x 16 NCT components;
+// per 64-wide k chunk a lane loads 64 bytes of its row (and of the weights) and 16 NCT bytes of
+// the swizzled T, the next chunk's loads in flight while the current one is converted and
+// multiplied.  Columns past ldx read as zero (the rows' padding up to ldx is zero).
+template <int NCT, bool HW>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
-img_contract_kernel(const int8_t* img, int Kp, int rows, const int8_t* Ts, int bs, int kspan, int gx, int gy, int gz,
-                    const double* img_unit, long long* out, double* unit, const double* spdG, double* spdGi) {
+fx_contract_kernel(const float* X, int ldx, int rows, int Kp, const float* hp, int ehm, const unsigned* rmax,
+                   int sblk, const int8_t* Ts, int bs, int kspan, int gx, int gy, int gz, long long* out,
+                   double* unit, const double* spdG, double* spdGi) {
   extern __shared__ __align__(16) char dsm[];
   int w = (int)blockIdx.x;
   if (spdG) {  // workgroup 0, dispatched first, inverts spdG beside the contraction
@@ -429,51 +379,76 @@ img_contract_kernel(const int8_t* img, int Kp, int rows, const int8_t* Ts, int b
   const int lr = lane & 15, g = lane >> 4;
   const int c0 = by * 16 * NCT;
   const int kb = bz * kspan, ke = kb + kspan < Kp ? kb + kspan : Kp;
-  if (bx == 0 && by == 0 && bz == 0 && tid == 0) *unit = *img_unit;
-  const int r = bx * 64 + wid * 16 + lr;  // image rows are padded to 64: always inside
-  const int8_t* src = img + (size_t)(r >> 4) * (Kp / 64) * kImgBlock + 16 * lane;  // chunk k0: + 96 k0
-  const int8_t* tsrc = Ts + (size_t)(c0 / 16) * (Kp / 64) * 1024 + 16 * lane;     // tile ct: + ct Kp 16
+  const int sc = fx_scale(rmax, sblk, HW ? ehm : 0);
+  const double dsc = ldexp(1.0, sc);
+  if (bx == 0 && by == 0 && bz == 0 && tid == 0) *unit = ldexp(1.0, -sc);
+  const int r = bx * 64 + wid * 16 + lr;
+  // rows past `rows` only reach outputs that are not stored: they read row 0
+  const float* xrow = X + (size_t)(r < rows ? r : 0) * ldx + 4 * g;
+  const int8_t* tsrc = Ts + (size_t)(c0 / 16) * (Kp / 64) * 1024 + 16 * lane;  // tile ct: + ct Kp 16
   v4i acc[NCT][kDig];
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
     for (int t = 0; t < kDig; ++t) acc[ct][t] = (v4i){0, 0, 0, 0};
-  // No load is masked or branched around, so the products wait only for the older chunk's loads
-  auto load = [&](int k0, v4i(&d)[kDig], v4i(&tt)[NCT]) {
+  // Every lane issues every load (past ldx it reads its row's start and the value is dropped at
+  // use), so the loop has no branches and the products wait only for the older chunk's loads.
+  auto load = [&](int k0, float4(&xv)[4], float4(&hv)[4], v4i(&tt)[NCT]) {
 #pragma unroll
-    for (int t = 0; t < kDig; ++t) d[t] = load16(src + (size_t)96 * k0 + 1024 * t);
+    for (int q = 0; q < 4; ++q) {
+      const int k = k0 + 16 * q + 4 * g;
+      xv[q] = *reinterpret_cast<const float4*>(xrow + (k < ldx ? k0 + 16 * q : -4 * g));
+      if (HW) hv[q] = *reinterpret_cast<const float4*>(hp + k);  // hp is padded to Kp
+    }
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) tt[ct] = load16(tsrc + (size_t)16 * k0 + (size_t)ct * Kp * 16);
   };
-  auto products = [&](const v4i(&d)[kDig], const v4i(&tt)[NCT]) {
+  auto products = [&](int k0, const float4(&xv)[4], const float4(&hv)[4], const v4i(&tt)[NCT]) {
+    v4i da[kDig];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const bool in = k0 + 16 * q + 4 * g < ldx;
+      const float x[4] = {in ? xv[q].x : 0.f, in ? xv[q].y : 0.f, in ? xv[q].z : 0.f, in ? xv[q].w : 0.f};
+      double ws[4] = {dsc, dsc, dsc, dsc};
+      if (HW) {
+        ws[0] = (double)hv[q].x * dsc;
+        ws[1] = (double)hv[q].y * dsc;
+        ws[2] = (double)hv[q].z * dsc;
+        ws[3] = (double)hv[q].w * dsc;
+      }
+      unsigned wd[kDig];
+      fx_digits_of(x, ws, wd);
+#pragma unroll
+      for (int t = 0; t < kDig; ++t) da[t][q] = (int)wd[t];
+    }
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
       for (int t = 0; t < kDig; ++t)
-        acc[ct][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(tt[ct], d[t], acc[ct][t], 0, 0, 0);
+        acc[ct][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(tt[ct], da[t], acc[ct][t], 0, 0, 0);
   };
   // kb < ke: the split index is below gz = ceil(Kp / kspan), and both are multiples of 64.
-  // Two register sets in turn (no copies between them): the loads of one chunk are in flight
-  // while the other is multiplied.
+  // Two register sets in turn (no copies between them).
   const int nk = (ke - kb) / 64;
-  v4i da[kDig], ta[NCT], db[kDig], tb[NCT];
-  load(kb, da, ta);
+  float4 xa[4], ha[4], xb[4], hb[4];
+  v4i ta[NCT], tb[NCT];
+  load(kb, xa, ha, ta);
   int it = 1;
   for (; it + 1 < nk; it += 2) {
-    load(kb + 64 * it, db, tb);
+    load(kb + 64 * it, xb, hb, tb);
     __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the products
-    products(da, ta);
-    load(kb + 64 * (it + 1), da, ta);
+    products(kb + 64 * (it - 1), xa, ha, ta);
+    load(kb + 64 * (it + 1), xa, ha, ta);
     __builtin_amdgcn_sched_barrier(0);
-    products(db, tb);
+    products(kb + 64 * it, xb, hb, tb);
   }
   if (it < nk) {
-    load(kb + 64 * it, db, tb);
+    load(kb + 64 * it, xb, hb, tb);
     __builtin_amdgcn_sched_barrier(0);
-    products(da, ta);
-    products(db, tb);
+    products(kb + 64 * (it - 1), xa, ha, ta);
+    products(kb + 64 * it, xb, hb, tb);
   } else {
-    products(da, ta);
+    products(kb + 64 * (it - 1), xa, ha, ta);
   }
   // D = T x^T: lane l, register q holds component 4 g + q of the tile for row lr, so each store
   // instruction covers four components x 16 consecutive rows
@@ -545,6 +520,12 @@ __global__ void __launch_bounds__(256) hdig_kernel(const float* h, int n, int ld
 #pragma unroll
     for (int t = 0; t < kHDig; ++t) hdig[(size_t)t * ldv + j] = (uint8_t)((H >> (7 * t)) & 0x7Fu);
   }
+}
+
+// hp[j] = h_j for j < n, 0 up to np
+__global__ void __launch_bounds__(256) hpad_kernel(const float* h, int n, int np, float* hp) {
+  const int j = blockIdx.x * 256 + threadIdx.x;
+  if (j < np) hp[j] = j < n ? h[j] : 0.0f;
 }
 
 // bytes of t (each 0, 1 or -1) times bytes of d (each 0..127), as signed bytes
@@ -790,6 +771,25 @@ __global__ void __launch_bounds__(NT) chol_inv_kernel(const double* G, int bs, d
     }
 }
 
+// compile-time loop: f(integral_constant<int, I>) for I = B .. E - 1
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// lane N's value of each 16-lane row, in every lane of that row (DPP row_newbcast: a VALU move,
+// where a readlane would go through a scalar register)
+template <int N>
+__device__ __forceinline__ double bcast16(double v) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(unsigned)b, 0x150 + N, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(unsigned)(b >> 32), 0x150 + N, 0xF, 0xF, false);
+  return __longlong_as_double((long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo));
+}
+
 // ---- Gi = (G + eps I)^-1 for bs <= 128, eps = 1e-6 trace(G) / bs (the regularised Gram of the
 // pages' Eq. 3), by a blocked Cholesky factorisation on 16 x 16 tiles, the block inverse of the
 // factor and the product X^T X (X = L^-1), all in LDS.  The tile products run on fp64 MFMA; the
@@ -846,15 +846,15 @@ __device__ __forceinline__ void spd_inv_body(const double* G, int bs, double* Gi
   // wave 0 updates diagonal block p + 1 first and factors it while the other waves finish the
   // trailing update, so the serial 16 x 16 factorisation leaves the critical path.
   // 16 x 16 diagonal block: Cholesky factor and its inverse by wave 0, lane r (mod 16) holding row r
-  auto factor_diag = [&](int p) {  // wave 0
+  auto factor_diag = [&](int p) {  // wave 0; each 16-lane row of the wave holds the block
     const int r = lr;
     double* T = at(p, p);
     double a[16], x[16], rk[16];
 #pragma unroll
     for (int c = 0; c < 16; ++c) a[c] = T[(size_t)r * ld + c];
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const double piv = readlane_f64(a[k], k);
+    static_for<0, 16>([&](auto kc) {
+      constexpr int k = decltype(kc)::value;
+      const double piv = bcast16<k>(a[k]);
       // 1 / sqrt(piv): the hardware estimate and two Newton steps (each squares the relative
       // error), then sqrt(piv) = piv / sqrt(piv); far shorter than a rounded sqrt and divide
       double rr = 0.0;
@@ -867,16 +867,15 @@ __device__ __forceinline__ void spd_inv_body(const double* G, int bs, double* Gi
       const double lkk = piv * rr;
       rk[k] = rr;
       a[k] = r > k ? a[k] * rr : (r == k ? lkk : a[k]);
-#pragma unroll
-      for (int j = k + 1; j < 16; ++j) {
-        const double ljk = readlane_f64(a[k], j);
-        a[j] = fma(-a[k], ljk, a[j]);  // meaningful for rows r >= j
-      }
-    }
+      static_for<k + 1, 16>([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        a[j] = fma(-a[k], bcast16<j>(a[k]), a[j]);  // meaningful for rows r >= j
+      });
+    });
 #pragma unroll
     for (int c = 0; c < 16; ++c) x[c] = 0.0;
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
+    static_for<0, 16>([&](auto tc) {
+      constexpr int t = decltype(tc)::value;
       // row t of X = L^-1 is finished: x[c] held -sum_{j<t} L_tj X_jc (one scale per lane
       // instead of a select per entry)
       const double sc = r == t ? rk[t] : 1.0;
@@ -885,9 +884,11 @@ __device__ __forceinline__ void spd_inv_body(const double* G, int bs, double* Gi
       x[t] = r == t ? rk[t] : x[t];
       // later rows r > t take -L_rt X_tc; the multiplier is zero for rows r <= t
       const double lrt = r > t ? a[t] : 0.0;
-#pragma unroll
-      for (int c = 0; c <= t; ++c) x[c] = fma(-lrt, readlane_f64(x[c], t), x[c]);
-    }
+      static_for<0, t + 1>([&](auto cc) {
+        constexpr int c = decltype(cc)::value;
+        x[c] = fma(-lrt, bcast16<t>(x[c]), x[c]);
+      });
+    });
     if (lane < 16) {
 #pragma unroll
       for (int c = 0; c < 16; ++c) {
@@ -1434,9 +1435,10 @@ __device__ __forceinline__ void transpose4x4(const unsigned (&w)[4], unsigned (&
   o[3] = __builtin_amdgcn_perm(d, b, 0x07060302u);
 }
 
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) update_kernel(float* R, int ldr, int m, int n, const int8_t* Ut, int ldu,
-                                                     const int8_t* Vt, int ldv, const float* dvec, int bs,
-                                                     const int* flags, unsigned* rmax_next) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) update_kernel(float* R, int ldr, float* RT, int ldt, int m, int n,
+                                                     const int8_t* Ut, int ldu, const int8_t* Vt, int ldv,
+                                                     const float* dvec, int bs, const int* flags,
+                                                     unsigned* rmax_next) {
   // int8 path: [i][c] for 128 components; fp64 path: [c][i] for 64
   __shared__ __align__(16) int8_t Us[64 * kUpdPitch2];
   __shared__ __align__(16) int8_t Vs[64 * kUpdPitch2];
@@ -1617,15 +1619,16 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) u
 #pragma unroll
       for (int r = 0; r < 4; ++r) sv[t][r] = acc[t][r];
   }
-  unsigned mx = 0u;  // largest |R| of the tile after the update (fp32 bits)
+  __shared__ float tt[64][65];  // the updated tile, transposed, for R^T
+  unsigned mx = 0u;              // largest |R| of the tile after the update (fp32 bits)
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int j = j0 + t * 16 + (lane & 15);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int i = i0 + wid * 16 + (lane >> 4) * 4 + r;
+      const int il = wid * 16 + (lane >> 4) * 4 + r, i = i0 + il;
+      float x = rv[t][r];  // zero outside the matrix
       if (i < m && j < n) {
-        float x = rv[t][r];
         if (sv[t][r] != 0.0) {
           x = (float)((double)x - sv[t][r]);
           R[(size_t)i * ldr + j] = x;
@@ -1633,12 +1636,21 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) u
         const unsigned b = __float_as_uint(x) & 0x7FFFFFFFu;
         mx = b > mx ? b : mx;
       }
+      tt[t * 16 + (lane & 15)][il] = x;
     }
   }
   __shared__ unsigned wm[4];
   mx = wave_max_u32(mx);
   if (lane == 0) wm[wid] = mx;
   __syncthreads();
+  // R^T rows j0 .. j0 + 63, entries i0 .. i0 + 63 (past m: zeros, R^T's padding up to ldt)
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int x = tid + 256 * q, jl = x >> 4, iq = 4 * (x & 15);
+    if (j0 + jl < n && i0 + iq < ldt)
+      *reinterpret_cast<float4*>(RT + (size_t)(j0 + jl) * ldt + i0 + iq) =
+          make_float4(tt[jl][iq], tt[jl][iq + 1], tt[jl][iq + 2], tt[jl][iq + 3]);
+  }
   if (tid == 0) {
     mx = wm[0] > wm[1] ? wm[0] : wm[1];
     mx = wm[2] > mx ? wm[2] : mx;
@@ -1902,11 +1914,13 @@ static bool utr_splits(const BlockLaunch& L, int bs) {
   return contract_shape(L.n, pad64(L.m), bs, &gx, &gy, &kspan) > 1;
 }
 
-// out (bs x rows, int64) = T N(X)^T from an image of X; with spdG one more workgroup inverts spdG
-static void contract(const BlockWs& w, const int8_t* img, int Kp, int rows, const int8_t* T, int ldt, int bs,
-                     const double* img_unit, long long* out, double* unit, hipStream_t st, bool prezeroed,
-                     const double* spdG, double* spdGi) {
-  const int nct = contract_nct(bs);
+// out (bs x rows, int64) = T N(X)^T for the rows of X (ld ldx, K columns; hp: the padded weights
+// or null), at the fixed-point scale of residual-max slot sblk; with spdG one more workgroup
+// inverts spdG
+static void contract(const BlockLaunch& L, const BlockWs& w, const float* X, int ldx, int rows, int K,
+                     const float* hp, int sblk, const int8_t* T, int ldt, int bs, long long* out, double* unit,
+                     hipStream_t st, bool prezeroed, const double* spdG, double* spdGi) {
+  const int nct = contract_nct(bs), Kp = pad64(K);
   int gx, gy, kspan;
   const int gz = contract_shape(rows, Kp, bs, &gx, &gy, &kspan);
   if (gz > 1 && !prezeroed) zero_fill(reinterpret_cast<double*>(out), (long long)bs * rows, st);
@@ -1916,28 +1930,26 @@ static void contract(const BlockWs& w, const int8_t* img, int Kp, int rows, cons
   }
   const dim3 grid(tile_grid(gx, gy, gz) + (spdG ? 1 : 0));
   const size_t lds = spdG ? spd_lds_bytes(bs) : 0;
-  if (nct == 1)
-    hipLaunchKernelGGL(img_contract_kernel<1>, grid, dim3(512), lds, st, img, Kp, rows, w.Ts, bs, kspan, gx, gy, gz,
-                       img_unit, out, unit, spdG, spdGi);
-  else if (nct == 2)
-    hipLaunchKernelGGL(img_contract_kernel<2>, grid, dim3(512), lds, st, img, Kp, rows, w.Ts, bs, kspan, gx, gy, gz,
-                       img_unit, out, unit, spdG, spdGi);
-  else
-    hipLaunchKernelGGL(img_contract_kernel<4>, grid, dim3(512), lds, st, img, Kp, rows, w.Ts, bs, kspan, gx, gy, gz,
-                       img_unit, out, unit, spdG, spdGi);
-}
-
-// the images of the current R, with the scales of residual-max slot sblk
-static void digitize(const BlockLaunch& L, const BlockWs& w, int sblk, hipStream_t st) {
-  hipLaunchKernelGGL(digitize_kernel, dim3(w.np / 64, w.mp / 64), dim3(256), 0, st, L.R, L.ldr, L.m, L.n, L.h,
-                     L.EHm, w.rmax, sblk, w.mp, w.np, w.imr, w.imrw, w.imc, w.unit + 2);
+#define EXTERND_CONTRACT(NCT, HW)                                                                             \
+  hipLaunchKernelGGL((fx_contract_kernel<NCT, HW>), grid, dim3(512), lds, st, X, ldx, rows, Kp, hp, L.EHm, w.rmax, \
+                     sblk, w.Ts, bs, kspan, gx, gy, gz, out, unit, spdG, spdGi)
+  if (hp) {
+    if (nct == 1) EXTERND_CONTRACT(1, true);
+    else if (nct == 2) EXTERND_CONTRACT(2, true);
+    else EXTERND_CONTRACT(4, true);
+  } else {
+    if (nct == 1) EXTERND_CONTRACT(1, false);
+    else if (nct == 2) EXTERND_CONTRACT(2, false);
+    else EXTERND_CONTRACT(4, false);
+  }
+#undef EXTERND_CONTRACT
 }
 
 // Y^T (bs x m) = (R diag(h) V^T)^T for V = Vt rows (h may be null: R V^T)
-static void rw_product(const BlockLaunch& L, const BlockWs& w, const float* h, int bs, long long* outT,
+static void rw_product(const BlockLaunch& L, const BlockWs& w, const float* h, int bs, int sblk, long long* outT,
                        hipStream_t st, bool prezeroed = false, const double* spdG = nullptr,
                        double* spdGi = nullptr) {
-  contract(w, h ? w.imrw : w.imr, w.np, L.m, w.Vt, w.ldv, bs, w.unit + (h ? 3 : 2), outT, w.unit + 1, st, prezeroed,
+  contract(L, w, L.R, L.ldr, L.m, L.n, h ? w.hpad : nullptr, sblk, w.Vt, w.ldv, bs, outT, w.unit + 1, st, prezeroed,
            spdG, spdGi);
 }
 
@@ -1957,10 +1969,10 @@ static void gram_product(const BlockWs& w, const int8_t* T, int len, int ldt, co
                      ehm, G, w.gpart, w.gcnt);
 }
 
-// X (bs x n) = U^T R
-static void utr_product(const BlockLaunch& L, const BlockWs& w, int bs, hipStream_t st, bool prezeroed = false,
-                        const double* spdG = nullptr, double* spdGi = nullptr) {
-  contract(w, w.imc, w.mp, L.n, w.Ut, w.ldu, bs, w.unit + 2, w.Xi, w.unit, st, prezeroed, spdG, spdGi);
+// X (bs x n) = U^T R, from the rows of R^T
+static void utr_product(const BlockLaunch& L, const BlockWs& w, int bs, int sblk, hipStream_t st,
+                        bool prezeroed = false, const double* spdG = nullptr, double* spdGi = nullptr) {
+  contract(L, w, L.RT, L.ldt, L.n, L.m, nullptr, sblk, w.Ut, w.ldu, bs, w.Xi, w.unit, st, prezeroed, spdG, spdGi);
 }
 
 // Li = (G + eps I)^-1 for bs <= kSpdMax, else Li = L^-1 for L L^T = G + eps I
@@ -2079,8 +2091,9 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops, double
         if (ea != hipSuccess) return ea;
       }
       // a contraction launch may carry the inverse of a b <= kSpdMax Gram (its LDS for all groups)
-      const void* con[3] = {(const void*)img_contract_kernel<1>, (const void*)img_contract_kernel<2>,
-                            (const void*)img_contract_kernel<4>};
+      const void* con[6] = {(const void*)fx_contract_kernel<1, false>, (const void*)fx_contract_kernel<2, false>,
+                            (const void*)fx_contract_kernel<4, false>, (const void*)fx_contract_kernel<1, true>,
+                            (const void*)fx_contract_kernel<2, true>, (const void*)fx_contract_kernel<4, true>};
       for (const void* kf : con) {
         ea = hipFuncSetAttribute(kf, hipFuncAttributeMaxDynamicSharedMemorySize, (int)spd_lds_bytes(kSpdMax));
         if (ea != hipSuccess) return ea;
@@ -2097,8 +2110,10 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops, double
     hipLaunchKernelGGL(rmax_kernel, dim3((unsigned)(nb < 2048 ? nb : 2048)), dim3(256), 0, st, L.R, L.ldr, m, n,
                        w.rmax);
   }
-  if (L.h)
+  if (L.h) {
     hipLaunchKernelGGL(hdig_kernel, dim3((w.ldv + 255) / 256), dim3(256), 0, st, L.h, n, w.ldv, L.EHm, w.hdig);
+    hipLaunchKernelGGL(hpad_kernel, dim3((pad64(n) + 255) / 256), dim3(256), 0, st, L.h, n, pad64(n), w.hpad);
+  }
   const int nblocks = (L.k + L.b - 1) / L.b;
   double fl = 0.0, by = 0.0;  // multiply-adds of R by ternary operands; residual bytes read/written
   const double rbytes = 4.0 * m * n;
@@ -2121,7 +2136,7 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops, double
       double* y0 = yz ? w.Yt : nullptr;                  // for this U-step
       if (naive_t) {
         if (addback && t == 0) gram_product(w, w.Ut, m, w.ldu, nullptr, 0, bs, w.GU, st);
-        utr_product(L, w, bs, st, true);
+        utr_product(L, w, bs, sblk, st, true);
         if (addback && t == 0) {
           hipLaunchKernelGGL(addback_dot_kernel, dim3(bs), dim3(256), 0, st, w.Xi, w.unit, n, w.Vt, w.ldv, L.h,
                              w.ppo);
@@ -2130,7 +2145,7 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops, double
         }
         select_rows(w.X, w.unit, n, w.ldv, bs, L.tau, hsel, ehsel, w.Vt, w.PHC, w.flags, 0, st, y0, m);
         gram_product(w, w.Vt, n, w.ldv, L.h, L.EHm, bs, w.GV, st);  // for the scales
-        rw_product(L, w, L.h, bs, w.Yi, st, true);
+        rw_product(L, w, L.h, bs, sblk, w.Yi, st, true);
         // the selection reads Yt while the last one also forms Md from it: Md reads the integers
         // (the selection converts its own copy in LDS)
         select_rows(w.Yt, w.unit + 1, m, w.ldu, bs, L.tau, nullptr, 0, w.Ut, w.PHC, w.flags, 0, st, x0, n,
@@ -2143,11 +2158,11 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops, double
       // inverse runs inside the contraction's launch, beside it; above, before it on the stream.
       if (fused) {
         gram_product(w, w.Ut, m, w.ldu, nullptr, 0, bs, w.GU, st);
-        utr_product(L, w, bs, st, true, w.GU, w.Li);
+        utr_product(L, w, bs, sblk, st, true, w.GU, w.Li);
       } else {
         gram_product(w, w.Ut, m, w.ldu, nullptr, 0, bs, w.GU, st);
         chol_inverse(w, w.GU, bs, st);
-        utr_product(L, w, bs, st, true);
+        utr_product(L, w, bs, sblk, st, true);
       }
       if (addback && t == 0) {
         hipLaunchKernelGGL(addback_dot_kernel, dim3(bs), dim3(256), 0, st, w.Xi, w.unit, n, w.Vt, w.ldv, L.h,
@@ -2160,11 +2175,11 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops, double
       // U-step: F^T = (V^T H V + eps I)^-1 (R H V)^T, columns ternarized without weights
       if (fused) {
         gram_product(w, w.Vt, n, w.ldv, L.h, L.EHm, bs, w.GV, st);
-        rw_product(L, w, L.h, bs, w.Yi, st, true, w.GV, w.Li);
+        rw_product(L, w, L.h, bs, sblk, w.Yi, st, true, w.GV, w.Li);
       } else {
         gram_product(w, w.Vt, n, w.ldv, L.h, L.EHm, bs, w.GV, st);
         chol_inverse(w, w.GV, bs, st);
-        rw_product(L, w, L.h, bs, w.Yi, st, true);
+        rw_product(L, w, L.h, bs, sblk, w.Yi, st, true);
       }
       solve(w, bs, w.Yi, w.unit + 1, w.Ft, m, st);
       select_rows(w.Ft, nullptr, m, w.ldu, bs, L.tau, nullptr, 0, w.Ut, w.PHC, w.flags, 0, st, x0, n,
@@ -2187,7 +2202,7 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops, double
                          L.D, m, n, k0, bs, w.Ut, w.ldu, w.Vt, w.ldv, w.d, w.dold, w.st, w.flags, w.rmax, true,
                          nullptr, 0ll);
     }
-    hipLaunchKernelGGL(update_kernel, dim3((n + 63) / 64, (m + 63) / 64), dim3(256), 0, st, L.R, L.ldr, m, n, w.Ut,
+    hipLaunchKernelGGL(update_kernel, dim3((n + 63) / 64, (m + 63) / 64), dim3(256), 0, st, L.R, L.ldr, L.RT, L.ldt, m, n, w.Ut,
                        w.ldu, w.Vt, w.ldv, w.d, bs, w.flags, w.rmax + kMaxWords * ((sblk + 1) & 1));
     hipLaunchKernelGGL(emit_kernel, dim3(256), dim3(256), 0, st, w.Ut, w.ldu, w.Vt, w.ldv, m, n, bs, k0, L.Bp, L.Cp,
                        w.flags);
@@ -2198,11 +2213,10 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops, double
   for (int s = 0; s < nblocks; ++s) {
     const int bs = (L.k - s * L.b) < L.b ? (L.k - s * L.b) : L.b;
     const int k0 = s * L.b;
-    digitize(L, w, s, st);  // R as the previous update (or the staging) left it
     // sketch
     hipLaunchKernelGGL(omega_kernel, dim3(256), dim3(256), 0, st, w.Vt, w.ldv, bs, n, (long long)s, w.flags,
                        w.rmax, w.Yt, rw_splits(L, bs) ? (long long)bs * m : 0ll);
-    rw_product(L, w, nullptr, bs, w.Yi, st, true);
+    rw_product(L, w, nullptr, bs, s, w.Yi, st, true);
     select_rows(w.Yt, w.unit + 1, m, w.ldu, bs, L.tau, nullptr, 0, w.Ut, w.PHC, w.flags, 1, st,
                 utr_splits(L, bs) ? w.X : nullptr, n);
     hipLaunchKernelGGL(zero_check_kernel, dim3(1), dim3(256), 0, st, L.R, L.ldr, m, n, w.flags, w.st);
@@ -2253,10 +2267,9 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops, double
                          w.rmax + kMaxWords * ((step + 1) & 1), false, w.X,
                          utr_splits(L, bs) ? (long long)bs * n : 0ll);
       // add the block back: R <- fl32(R + U diag(d) V^T), the new residual max into the next slot
-      hipLaunchKernelGGL(update_kernel, dim3((n + 63) / 64, (m + 63) / 64), dim3(256), 0, st, L.R, L.ldr, m, n,
+      hipLaunchKernelGGL(update_kernel, dim3((n + 63) / 64, (m + 63) / 64), dim3(256), 0, st, L.R, L.ldr, L.RT, L.ldt, m, n,
                          w.Ut, w.ldu, w.Vt, w.ldv, w.d, bs, w.flags, w.rmax + kMaxWords * ((step + 1) & 1));
       ++step;
-      digitize(L, w, step, st);
       // the old V's weighted Gram for the add-back energy (the U-step overwrites GV)
       gram_product(w, w.Vt, n, w.ldv, L.h, L.EHm, bs, w.GVo, st);
       by += 2.0 * rbytes;

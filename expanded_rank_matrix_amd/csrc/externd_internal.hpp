@@ -61,7 +61,8 @@ hipError_t project_rows(const float* X, int count, int L, float tau, const float
 // ---- block-ALS (block.hip)
 struct BlockLaunch {
   float* R;            // m x ldr residual
-  int m, n, ldr, k, b, T, EHm;
+  float* RT;           // n x ldt: its transpose, kept alongside
+  int m, n, ldr, ldt, k, b, T, EHm;
   float tau;
   const float* h;
   const double* rowE;  // m
