@@ -69,6 +69,7 @@ struct BlockWs {
   long long* Xi;   // X and Yt as the contractions write them (exact integers)
   long long* Yi;
   float* hpad;     // the column weights, zero-padded to a multiple of 64 (weighted only)
+  int ncu;         // compute units of the device (contraction workgroups per launch)
   int8_t* Ts;      // the ternary operand of a contraction, swizzled (b rounded up to 64 x max(m, n)
                    // rounded up to 64)
 };
@@ -91,7 +92,7 @@ static void ws_layout(int m, int n, int b, bool weighted, F&& take) {
   take((void**)nullptr, bb * mx * 8);
   take((void**)nullptr, bb * bb * 8);
   take((void**)nullptr, bb * bb * 8);
-  take((void**)nullptr, bb * bb * 8);
+  take((void**)nullptr, ((bb + 15) & ~(size_t)15) * ((bb + 15) & ~(size_t)15) * 8);  // Li
   take((void**)nullptr, bb * 8);
   take((void**)nullptr, bb * 3 * 8);
   take((void**)nullptr, bb * 4);
@@ -281,24 +282,7 @@ template <int NT>
 __device__ __forceinline__ void spd_inv_body(const double* G, int bs, double* Gi, char* smem);
 __host__ __device__ inline size_t spd_lds_bytes(int bs);
 
-// A contraction workgroup of 512 threads runs two tiles, one per half.  The registers of a tile's
-// waves allow eight waves per CU, so this is the occupancy of two 256-thread workgroups, while a
-// single workgroup per CU can also hold the LDS of a fused inverse.  Tiles that read the same image
-// rows (row tile x, K range z; component groups y = 0 .. gy - 1) are run by workgroups on one XCD
-// (the dispatcher deals workgroup ids round-robin over the eight XCDs), in consecutive halves, so
-// the rows are fetched into that XCD's L2 once instead of gy times.  Halves past the last tile
-// return at once.
-__device__ __forceinline__ bool tile_decode(int w, int half, int gx, int gy, int gz, int* bx, int* by, int* bz) {
-  const int x = w & 7, i = 2 * (w >> 3) + half;
-  const int uu = i / gy, y = i - uu * gy;
-  const int u = 8 * uu + x;
-  if (u >= gx * gz) return false;
-  *bx = u % gx;
-  *bz = u / gx;
-  *by = y;
-  return true;
-}
-static int tile_grid(int gx, int gy, int gz) { return 8 * ((((gx * gz + 7) / 8) * gy + 1) / 2); }
+
 
 __host__ __device__ inline int pad64(int x) { return (x + 63) & ~63; }
 
@@ -353,17 +337,25 @@ __device__ __forceinline__ void fx_digits_of(const float (&x)[4], const double (
   w[5] = __builtin_amdgcn_perm(y23, y01, 0x07060302u);
 }
 
-// out[c][r] (+)= sum_{k in this split} N(x_rk) T[c][k] for the rows r of X (R, or R^T), with
-// x_rk = X_rk (times h_k when HW) and N the fixed-point image at the scale of residual-max slot
-// sblk, in units *unit = 2^-f.  Workgroup: two tiles of 64 rows (16 per wave) x 16 NCT components;
-// per 64-wide k chunk a lane loads 64 bytes of its row (and of the weights) and 16 NCT bytes of
-// the swizzled T, the next chunk's loads in flight while the current one is converted and
-// multiplied.  Columns past ldx read as zero (the rows' padding up to ldx is zero).
-template <int NCT, bool HW>
+// out[c][r] += sum_k N(x_rk) T[c][k] for the rows r of X (R, or R^T), with x_rk = X_rk (times
+// h_k when HW) and N the fixed-point image at the scale of residual-max slot sblk, in units
+// *unit = 2^-f; out starts at zero.  Work is split evenly ("stream-K"): the units (row tile of 64,
+// component group of 16 NCT, 64-wide k chunk) are dealt to nwg workgroups in contiguous runs of
+// chunks, so that one launch round fills the CUs whatever the shape, and each run's partial sums
+// are added into out with 64-bit integer atomics (exact, in any order).  With gy >= 2 component
+// groups, the two halves of a workgroup (four waves each, 16 rows per wave) take the groups 2 j and
+// 2 j + 1 of the same rows and chunks, so the rows are read once into the CU's caches; with a
+// single group the halves take separate runs.  Per chunk a lane loads 64 bytes of its row (and of
+// the weights) and 16 NCT bytes of the swizzled T, the next chunk's rows in flight while the
+// current one is converted and multiplied.  Columns past ldx read as zero (the rows' padding up to
+// ldx is zero).
+// HW: 0 unweighted, 1 weights staged in LDS (Kp floats, the launch's dynamic LDS), 2 weights read
+// from global memory (Kp too large for LDS).
+template <int NCT, int HW>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
 fx_contract_kernel(const float* X, int ldx, int rows, int Kp, const float* hp, int ehm, const unsigned* rmax,
-                   int sblk, const int8_t* Ts, int bs, int kspan, int gx, int gy, int gz, long long* out,
-                   double* unit, const double* spdG, double* spdGi) {
+                   int sblk, const int8_t* Ts, int bs, int gx, int gy, int nwg, long long* out, double* unit,
+                   const double* spdG, double* spdGi) {
   extern __shared__ __align__(16) char dsm[];
   int w = (int)blockIdx.x;
   if (spdG) {  // workgroup 0, dispatched first, inverts spdG beside the contraction
@@ -373,96 +365,118 @@ fx_contract_kernel(const float* X, int ldx, int rows, int Kp, const float* hp, i
     }
     --w;
   }
-  int bx, by, bz;
-  if (!tile_decode(w, (int)threadIdx.x >> 8, gx, gy, gz, &bx, &by, &bz)) return;  // no barriers below
+  const int half = (int)threadIdx.x >> 8;
   const int tid = threadIdx.x & 255, lane = tid & 63, wid = tid >> 6;
   const int lr = lane & 15, g = lane >> 4;
-  const int c0 = by * 16 * NCT;
-  const int kb = bz * kspan, ke = kb + kspan < Kp ? kb + kspan : Kp;
+  const float* hsrc = hp;
+  if (HW == 1) {  // every workgroup stages the weights once (all its threads, before any run)
+    float* hs = reinterpret_cast<float*>(dsm);
+    for (int k = 4 * (int)threadIdx.x; k < Kp; k += 4 * 512)
+      *reinterpret_cast<float4*>(hs + k) = *reinterpret_cast<const float4*>(hp + k);
+    __syncthreads();
+    hsrc = hs;
+  }
   const int sc = fx_scale(rmax, sblk, HW ? ehm : 0);
   const double dsc = ldexp(1.0, sc);
-  if (bx == 0 && by == 0 && bz == 0 && tid == 0) *unit = ldexp(1.0, -sc);
-  const int r = bx * 64 + wid * 16 + lr;
-  // rows past `rows` only reach outputs that are not stored: they read row 0
-  const float* xrow = X + (size_t)(r < rows ? r : 0) * ldx + 4 * g;
-  const int8_t* tsrc = Ts + (size_t)(c0 / 16) * (Kp / 64) * 1024 + 16 * lane;  // tile ct: + ct Kp 16
+  if (w == 0 && threadIdx.x == 0) *unit = ldexp(1.0, -sc);
+  const int nch = Kp / 64;
+  const int per = gy == 1 ? 2 : 1;  // workers per workgroup
+  const long long span = (long long)(gy == 1 ? 1 : (gy + 1) / 2) * gx * nch;
+  const long long nwk = (long long)nwg * per, wk = (long long)w * per + (per == 2 ? half : 0);
+  long long u = wk * span / nwk;
+  const long long uend = (wk + 1) * span / nwk;
   v4i acc[NCT][kDig];
-#pragma unroll
-  for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-    for (int t = 0; t < kDig; ++t) acc[ct][t] = (v4i){0, 0, 0, 0};
-  // Every lane issues every load (past ldx it reads its row's start and the value is dropped at
-  // use), so the loop has no branches and the products wait only for the older chunk's loads.
-  auto load = [&](int k0, float4(&xv)[4], float4(&hv)[4], v4i(&tt)[NCT]) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int k = k0 + 16 * q + 4 * g;
-      xv[q] = *reinterpret_cast<const float4*>(xrow + (k < ldx ? k0 + 16 * q : -4 * g));
-      if (HW) hv[q] = *reinterpret_cast<const float4*>(hp + k);  // hp is padded to Kp
-    }
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) tt[ct] = load16(tsrc + (size_t)16 * k0 + (size_t)ct * Kp * 16);
-  };
-  auto products = [&](int k0, const float4(&xv)[4], const float4(&hv)[4], const v4i(&tt)[NCT]) {
-    v4i da[kDig];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const bool in = k0 + 16 * q + 4 * g < ldx;
-      const float x[4] = {in ? xv[q].x : 0.f, in ? xv[q].y : 0.f, in ? xv[q].z : 0.f, in ? xv[q].w : 0.f};
-      double ws[4] = {dsc, dsc, dsc, dsc};
-      if (HW) {
-        ws[0] = (double)hv[q].x * dsc;
-        ws[1] = (double)hv[q].y * dsc;
-        ws[2] = (double)hv[q].z * dsc;
-        ws[3] = (double)hv[q].w * dsc;
-      }
-      unsigned wd[kDig];
-      fx_digits_of(x, ws, wd);
-#pragma unroll
-      for (int t = 0; t < kDig; ++t) da[t][q] = (int)wd[t];
-    }
+  while (u < uend) {  // one run: consecutive chunks of one (row tile, component group)
+    const long long tile = u / nch;
+    const int cs = (int)(u - tile * nch);
+    const int ce = (long long)(nch - cs) < uend - u ? nch : cs + (int)(uend - u);
+    u += ce - cs;
+    const int jg = (int)(tile / gx), bx = (int)(tile - (long long)jg * gx);
+    const int by = gy == 1 ? 0 : 2 * jg + half;
+    if (by >= gy) continue;  // the idle half of an odd count of groups
+    const int c0 = by * 16 * NCT;
+    const int r = bx * 64 + wid * 16 + lr;
+    // rows past `rows` only reach outputs that are not stored: they read row 0
+    const float* xrow = X + (size_t)(r < rows ? r : 0) * ldx + 4 * g;
+    const int8_t* tsrc = Ts + (size_t)(c0 / 16) * (Kp / 64) * 1024 + 16 * lane;  // tile ct: + ct Kp 16
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-      for (int t = 0; t < kDig; ++t)
-        acc[ct][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(tt[ct], da[t], acc[ct][t], 0, 0, 0);
-  };
-  // kb < ke: the split index is below gz = ceil(Kp / kspan), and both are multiples of 64.
-  // Two register sets in turn (no copies between them).
-  const int nk = (ke - kb) / 64;
-  float4 xa[4], ha[4], xb[4], hb[4];
-  v4i ta[NCT], tb[NCT];
-  load(kb, xa, ha, ta);
-  int it = 1;
-  for (; it + 1 < nk; it += 2) {
-    load(kb + 64 * it, xb, hb, tb);
-    __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the products
-    products(kb + 64 * (it - 1), xa, ha, ta);
-    load(kb + 64 * (it + 1), xa, ha, ta);
-    __builtin_amdgcn_sched_barrier(0);
-    products(kb + 64 * it, xb, hb, tb);
-  }
-  if (it < nk) {
-    load(kb + 64 * it, xb, hb, tb);
-    __builtin_amdgcn_sched_barrier(0);
-    products(kb + 64 * (it - 1), xa, ha, ta);
-    products(kb + 64 * it, xb, hb, tb);
-  } else {
-    products(kb + 64 * (it - 1), xa, ha, ta);
-  }
-  // D = T x^T: lane l, register q holds component 4 g + q of the tile for row lr, so each store
-  // instruction covers four components x 16 consecutive rows
-  const bool split = gz > 1;
+      for (int t = 0; t < kDig; ++t) acc[ct][t] = (v4i){0, 0, 0, 0};
+    // Every lane issues every load (past ldx it reads its row's start and the value is dropped
+    // at use), so the chunk loop has no branches and the products wait only for the older
+    // chunk's loads.  The T operands (L2-resident) are loaded as a chunk's conversion starts,
+    // which covers their latency and keeps one register set.
+    auto load = [&](int k0, float4(&xv)[4]) {
 #pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) {
+      for (int q = 0; q < 4; ++q) {
+        const int k = k0 + 16 * q + 4 * g;
+        xv[q] = *reinterpret_cast<const float4*>(xrow + (k < ldx ? k0 + 16 * q : -4 * g));
+      }
+    };
+    auto products = [&](int k0, const float4(&xv)[4]) {
+      v4i tt[NCT];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int c = c0 + ct * 16 + 4 * g + q;
-      if (c < bs && r < rows) {
-        const long long v = fx_combine(acc[ct], q);
-        long long* o = out + (size_t)c * rows + r;
-        if (split) atomicAdd(reinterpret_cast<unsigned long long*>(o), (unsigned long long)v);
-        else *o = v;
+      for (int ct = 0; ct < NCT; ++ct) tt[ct] = load16(tsrc + (size_t)16 * k0 + (size_t)ct * Kp * 16);
+      float4 hv[4];  // the weights (padded to Kp with zeros), from LDS or global memory
+      if (HW) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) hv[q] = *reinterpret_cast<const float4*>(hsrc + k0 + 16 * q + 4 * g);
+      }
+      v4i da[kDig];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const bool in = k0 + 16 * q + 4 * g < ldx;
+        const float x[4] = {in ? xv[q].x : 0.f, in ? xv[q].y : 0.f, in ? xv[q].z : 0.f, in ? xv[q].w : 0.f};
+        double ws[4] = {dsc, dsc, dsc, dsc};
+        if (HW) {
+          ws[0] = (double)hv[q].x * dsc;
+          ws[1] = (double)hv[q].y * dsc;
+          ws[2] = (double)hv[q].z * dsc;
+          ws[3] = (double)hv[q].w * dsc;
+        }
+        unsigned wd[kDig];
+        fx_digits_of(x, ws, wd);
+#pragma unroll
+        for (int t = 0; t < kDig; ++t) da[t][q] = (int)wd[t];
+      }
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int t = 0; t < kDig; ++t)
+          acc[ct][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(tt[ct], da[t], acc[ct][t], 0, 0, 0);
+    };
+    // Two register sets of rows in turn (no copies between them)
+    const int kb = 64 * cs, nk = ce - cs;
+    float4 xa[4], xb[4];
+    load(kb, xa);
+    int it = 1;
+    for (; it + 1 < nk; it += 2) {
+      load(kb + 64 * it, xb);
+      __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the products
+      products(kb + 64 * (it - 1), xa);
+      load(kb + 64 * (it + 1), xa);
+      __builtin_amdgcn_sched_barrier(0);
+      products(kb + 64 * it, xb);
+    }
+    if (it < nk) {
+      load(kb + 64 * it, xb);
+      __builtin_amdgcn_sched_barrier(0);
+      products(kb + 64 * (it - 1), xa);
+      products(kb + 64 * it, xb);
+    } else {
+      products(kb + 64 * (it - 1), xa);
+    }
+    // D = T x^T: lane l, register q holds component 4 g + q of the tile for row lr, so each
+    // atomic instruction covers four components x 16 consecutive rows
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c = c0 + ct * 16 + 4 * g + q;
+        if (c < bs && r < rows)
+          atomicAdd(reinterpret_cast<unsigned long long*>(out + (size_t)c * rows + r),
+                    (unsigned long long)fx_combine(acc[ct], q));
       }
     }
   }
@@ -796,9 +810,10 @@ __device__ __forceinline__ double bcast16(double v) {
 // 16 x 16 diagonal blocks are factored and inverted by one wave with a row per lane.  Pivots that
 // are not positive give zero rows, as in a plain Cholesky solve.  The matrix is padded to a
 // multiple of 16 with an identity block, which keeps it block diagonal and leaves the real part of
-// the inverse unchanged.  One workgroup; about 4 (nb - 1) + 2 barriers for nb tiles per side.
+// the inverse unchanged.  One workgroup; 2 nb + 1 barriers for nb tiles per side.
 constexpr int kSpdMax = 128;
 constexpr int kSpdFused = kSpdMax;  // largest b whose inverse runs inside the contraction launch
+constexpr size_t kContractLds = 160 * 1024;  // dynamic LDS limit of the contraction launches
 __host__ __device__ inline size_t spd_lds_bytes(int bs) {
   const int bp = (bs + 15) & ~15, ld = bp + 1;
   return 8 * ((size_t)bp * ld + (size_t)(bp / 16) * 256);
@@ -939,51 +954,56 @@ __device__ __forceinline__ void spd_inv_body(const double* G, int bs, double* Gi
     }
     __syncthreads();
   }
-  // ---------------- X = L^-1 by block rows: X_ii = D_i, X_ij = -D_i sum_{k=j}^{i-1} L_ik X_kj.
-  // X_ij (i > j) is stored transposed in the free upper block (j, i) of A.
-  for (int i = 1; i < nb; ++i) {
-    for (int j = wid; j < i; j += NWV) {
-      dbl4 sacc = (dbl4){0.0, 0.0, 0.0, 0.0};
+  // ---------------- X = L^-1, one column block per wave and no barrier: a wave reads only L's
+  // tiles, the D_i and the blocks of its own column written before.  X_jj = D_j and
+  // X_ij = -D_i sum_{k=j}^{i-1} L_ik X_kj for i > j, the sum over k split into two accumulator
+  // chains; X_ij is stored transposed in the free upper block (j, i) of A.
+  for (int j = wid; j < nb - 1; j += NWV) {
+    for (int i = j + 1; i < nb; ++i) {
+      dbl4 s0 = (dbl4){0.0, 0.0, 0.0, 0.0}, s1 = s0;
       for (int k = j; k < i; ++k) {
         const double* P = at(i, k);
 #pragma unroll
         for (int sl = 0; sl < 4; ++sl) {
           // X_kj[4 s + lk][lr]: D_j for k == j, else transposed storage in block (j, k)
           const double bq = k == j ? opc(Dg + j * 256, 16, sl) : opr(at(j, k), ld, sl);
-          sacc = __builtin_amdgcn_mfma_f64_16x16x4f64(opr(P, ld, sl), bq, sacc, 0, 0, 0);
+          if ((k - j) & 1) s1 = __builtin_amdgcn_mfma_f64_16x16x4f64(opr(P, ld, sl), bq, s1, 0, 0, 0);
+          else s0 = __builtin_amdgcn_mfma_f64_16x16x4f64(opr(P, ld, sl), bq, s0, 0, 0, 0);
         }
       }
       dbl4 xacc = (dbl4){0.0, 0.0, 0.0, 0.0};
 #pragma unroll
       for (int sl = 0; sl < 4; ++sl)  // an MFMA result in lane l, register s is operand B[4 s + lk][lr]
-        xacc = __builtin_amdgcn_mfma_f64_16x16x4f64(-opr(Dg + i * 256, 16, sl), sacc[sl], xacc, 0, 0, 0);
+        xacc = __builtin_amdgcn_mfma_f64_16x16x4f64(-opr(Dg + i * 256, 16, sl), s0[sl] + s1[sl], xacc, 0, 0, 0);
       double* T = at(j, i);
 #pragma unroll
       for (int q = 0; q < 4; ++q) T[(size_t)lr * ld + 4 * q + lk] = xacc[q];
     }
-    __syncthreads();
   }
-  // ---------------- Gi = X^T X: tile (i, j), i >= j, is sum_{k >= i} X_ki^T X_kj
+  __syncthreads();
+  // ---------------- Gi = X^T X: tile (i, j), i >= j, is sum_{k >= i} X_ki^T X_kj (two chains)
   for (int t = wid; t < nb * (nb + 1) / 2; t += NWV) {
     int i = 0;
     while ((i + 1) * (i + 2) / 2 <= t) ++i;
     const int j = t - i * (i + 1) / 2;
-    dbl4 acc = (dbl4){0.0, 0.0, 0.0, 0.0};
+    dbl4 a0 = (dbl4){0.0, 0.0, 0.0, 0.0}, a1 = a0;
     for (int k = i; k < nb; ++k) {
 #pragma unroll
       for (int sl = 0; sl < 4; ++sl) {
         // X_ki[4 s + lk][lr] and X_kj[4 s + lk][lr]
         const double av = k == i ? opc(Dg + i * 256, 16, sl) : opr(at(i, k), ld, sl);
         const double bv = k == j ? opc(Dg + j * 256, 16, sl) : opr(at(j, k), ld, sl);
-        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc, 0, 0, 0);
+        if ((k - i) & 1) a1 = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, a1, 0, 0, 0);
+        else a0 = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, a0, 0, 0, 0);
       }
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int r = 16 * i + 4 * q + lk, c = 16 * j + lr;
       if (r < bs && c < bs) {
-        Gi[(size_t)r * bs + c] = acc[q];
-        if (i != j) Gi[(size_t)c * bs + r] = acc[q];
+        const double v = a0[q] + a1[q];
+        Gi[(size_t)r * bs + c] = v;
+        if (i != j) Gi[(size_t)c * bs + r] = v;
       }
     }
   }
@@ -1877,18 +1897,6 @@ __global__ void __launch_bounds__(256) zero_check_kernel(const float* R, int ldr
   }
 }
 
-// K splits of an int8 contraction with `tiles` workgroups per split: about 512 workgroups, at
-// least 256 of K per split, at most 16 splits; kspan is a multiple of the 64-wide k chunk.
-static int i8_splits(int tiles, int K, int* kspan) {
-  int z = (512 + tiles - 1) / tiles;
-  const int maxz = (K + 255) / 256;
-  z = z > maxz ? maxz : z;
-  z = z > 16 ? 16 : z;
-  z = z < 1 ? 1 : z;
-  *kspan = ((K + z - 1) / z + 63) / 64 * 64;
-  return (K + *kspan - 1) / *kspan;
-}
-
 static void zero_fill(double* p, long long count, hipStream_t st) {
   const long long nb = (count + 255) / 256;
   hipLaunchKernelGGL(zero_kernel, dim3((unsigned)(nb < 2048 ? nb : 2048)), dim3(256), 0, st, p, count);
@@ -1897,22 +1905,10 @@ static void zero_fill(double* p, long long count, hipStream_t st) {
 // 16-component tiles per contraction workgroup (six digit accumulators each)
 static int contract_nct(int bs) { return bs <= 16 ? 1 : bs <= 32 ? 2 : 4; }
 
-// launch shape of a contraction of `rows` image rows (K padded to Kp) with bs ternary vectors;
-// returns the number of K splits (> 1: the output must be cleared first)
-static int contract_shape(int rows, int Kp, int bs, int* gx, int* gy, int* kspan) {
-  const int nct = contract_nct(bs);
-  *gx = (rows + 63) / 64;
-  *gy = (bs + 16 * nct - 1) / (16 * nct);
-  return i8_splits(*gx * *gy, Kp, kspan);
-}
-static bool rw_splits(const BlockLaunch& L, int bs) {
-  int gx, gy, kspan;
-  return contract_shape(L.m, pad64(L.n), bs, &gx, &gy, &kspan) > 1;
-}
-static bool utr_splits(const BlockLaunch& L, int bs) {
-  int gx, gy, kspan;
-  return contract_shape(L.n, pad64(L.m), bs, &gx, &gy, &kspan) > 1;
-}
+// The contractions add their partial sums into outputs that start at zero (the selection before
+// each clears the next one's output, or zero_fill does)
+static bool rw_splits(const BlockLaunch&, int) { return true; }
+static bool utr_splits(const BlockLaunch&, int) { return true; }
 
 // out (bs x rows, int64) = T N(X)^T for the rows of X (ld ldx, K columns; hp: the padded weights
 // or null), at the fixed-point scale of residual-max slot sblk; with spdG one more workgroup
@@ -1921,26 +1917,34 @@ static void contract(const BlockLaunch& L, const BlockWs& w, const float* X, int
                      const float* hp, int sblk, const int8_t* T, int ldt, int bs, long long* out, double* unit,
                      hipStream_t st, bool prezeroed, const double* spdG, double* spdGi) {
   const int nct = contract_nct(bs), Kp = pad64(K);
-  int gx, gy, kspan;
-  const int gz = contract_shape(rows, Kp, bs, &gx, &gy, &kspan);
-  if (gz > 1 && !prezeroed) zero_fill(reinterpret_cast<double*>(out), (long long)bs * rows, st);
+  const int gx = (rows + 63) / 64, gy = (bs + 16 * nct - 1) / (16 * nct);
+  if (!prezeroed) zero_fill(reinterpret_cast<double*>(out), (long long)bs * rows, st);
   {
     const int nblk = gy * nct * (Kp / 64);  // every component tile the launch reads
     hipLaunchKernelGGL(swizzle_t_kernel, dim3((nblk + 3) / 4), dim3(256), 0, st, T, ldt, bs, gy * nct, Kp / 64, w.Ts);
   }
-  const dim3 grid(tile_grid(gx, gy, gz) + (spdG ? 1 : 0));
-  const size_t lds = spdG ? spd_lds_bytes(bs) : 0;
+  // one workgroup per CU (their registers allow no more), one CU left to a fused inverse
+  const int nwg = w.ncu - (spdG ? 1 : 0);
+  const dim3 grid(nwg + (spdG ? 1 : 0));
+  // weights in LDS when they fit beside nothing else (the inverse's LDS is its workgroup's own)
+  const bool hlds = hp && (size_t)Kp * 4 <= kContractLds;
+  size_t lds = spdG ? spd_lds_bytes(bs) : 0;
+  if (hlds && (size_t)Kp * 4 > lds) lds = (size_t)Kp * 4;
 #define EXTERND_CONTRACT(NCT, HW)                                                                             \
   hipLaunchKernelGGL((fx_contract_kernel<NCT, HW>), grid, dim3(512), lds, st, X, ldx, rows, Kp, hp, L.EHm, w.rmax, \
-                     sblk, w.Ts, bs, kspan, gx, gy, gz, out, unit, spdG, spdGi)
-  if (hp) {
-    if (nct == 1) EXTERND_CONTRACT(1, true);
-    else if (nct == 2) EXTERND_CONTRACT(2, true);
-    else EXTERND_CONTRACT(4, true);
+                     sblk, w.Ts, bs, gx, gy, nwg, out, unit, spdG, spdGi)
+  if (hlds) {
+    if (nct == 1) EXTERND_CONTRACT(1, 1);
+    else if (nct == 2) EXTERND_CONTRACT(2, 1);
+    else EXTERND_CONTRACT(4, 1);
+  } else if (hp) {
+    if (nct == 1) EXTERND_CONTRACT(1, 2);
+    else if (nct == 2) EXTERND_CONTRACT(2, 2);
+    else EXTERND_CONTRACT(4, 2);
   } else {
-    if (nct == 1) EXTERND_CONTRACT(1, false);
-    else if (nct == 2) EXTERND_CONTRACT(2, false);
-    else EXTERND_CONTRACT(4, false);
+    if (nct == 1) EXTERND_CONTRACT(1, 0);
+    else if (nct == 2) EXTERND_CONTRACT(2, 0);
+    else EXTERND_CONTRACT(4, 0);
   }
 #undef EXTERND_CONTRACT
 }
@@ -2070,13 +2074,17 @@ static void select_rows(const double* X, const double* xunit, int L, int ldT, in
 
 hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops, double* bytes) {
   if (L.b > 256) return hipErrorInvalidValue;
+  static int ncu_of[64] = {};  // compute units of each device
+  int dev = 0;
   {
     static bool scales_attr[64] = {};  // once per device: dynamic LDS above 64 KB
-    int dev = 0;
     hipError_t ea = hipGetDevice(&dev);
     if (ea != hipSuccess) return ea;
     if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
     if (!scales_attr[dev]) {
+      ea = hipDeviceGetAttribute(&ncu_of[dev], hipDeviceAttributeMultiprocessorCount, dev);
+      if (ea != hipSuccess) return ea;
+      if (ncu_of[dev] < 2) return hipErrorInvalidDevice;
       const void* kernels[4] = {(const void*)scales_kernel<1>, (const void*)scales_kernel<2>,
                                 (const void*)scales_kernel<3>, (const void*)scales_kernel<4>};
       for (const void* kf : kernels) {
@@ -2091,17 +2099,21 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops, double
         if (ea != hipSuccess) return ea;
       }
       // a contraction launch may carry the inverse of a b <= kSpdMax Gram (its LDS for all groups)
-      const void* con[6] = {(const void*)fx_contract_kernel<1, false>, (const void*)fx_contract_kernel<2, false>,
-                            (const void*)fx_contract_kernel<4, false>, (const void*)fx_contract_kernel<1, true>,
-                            (const void*)fx_contract_kernel<2, true>, (const void*)fx_contract_kernel<4, true>};
+      const void* con[9] = {(const void*)fx_contract_kernel<1, 0>, (const void*)fx_contract_kernel<2, 0>,
+                            (const void*)fx_contract_kernel<4, 0>, (const void*)fx_contract_kernel<1, 1>,
+                            (const void*)fx_contract_kernel<2, 1>, (const void*)fx_contract_kernel<4, 1>,
+                            (const void*)fx_contract_kernel<1, 2>, (const void*)fx_contract_kernel<2, 2>,
+                            (const void*)fx_contract_kernel<4, 2>};
       for (const void* kf : con) {
-        ea = hipFuncSetAttribute(kf, hipFuncAttributeMaxDynamicSharedMemorySize, (int)spd_lds_bytes(kSpdMax));
+        ea = hipFuncSetAttribute(kf, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kContractLds);
         if (ea != hipSuccess) return ea;
       }
+
       scales_attr[dev] = true;
     }
   }
-  const BlockWs w = carve(L.ws, L.m, L.n, L.b, L.h != nullptr);
+  BlockWs w = carve(L.ws, L.m, L.n, L.b, L.h != nullptr);
+  w.ncu = ncu_of[dev];
   const int m = L.m, n = L.n;
   hipError_t e = hipSuccess;
   hipLaunchKernelGGL(block_init_kernel, dim3(1), dim3(256), 0, st, L.rowE, m, w.st, w.flags, w.rmax, w.gcnt);
