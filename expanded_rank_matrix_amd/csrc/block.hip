@@ -1143,7 +1143,8 @@ template <bool W, int NT>
 __global__ void __launch_bounds__(NT) select_rows_kernel(const double* X, const double* xunit, int L, int ldT,
                                                           float tau, const float* h, int EHm, int8_t* T, double* PHC,
                                                           int* flags, int flag_empty, double* Z0, int zlen,
-                                                          const long long* Yd, const double* ydunit, double* Md) {
+                                                          const long long* Yd, const double* ydunit, double* Md,
+                                                          int8_t* Ts) {
   __shared__ SelScratchT<W> s;
   __shared__ u64 red[NT / 64];
   extern __shared__ float xs[];  // L values when xunit is set
@@ -1166,11 +1167,24 @@ __global__ void __launch_bounds__(NT) select_rows_kernel(const double* X, const 
     r = ternary_select<NT, W>(x, h, L, tau, EHm, s);
   }
   long long dot = 0;
-  for (int j = threadIdx.x; j < ldT; j += NT) {  // the padding [L, ldT) stays zero
-    const float xv = j < L ? (xunit ? xs[j] : (float)x[j]) : 0.0f;
-    const int8_t t = selected(xv, r) ? (xv > 0.0f ? (int8_t)1 : (int8_t)-1) : (int8_t)0;
-    T[(size_t)c * ldT + j] = t;
-    if (Md && t) dot += t > 0 ? Yd[(size_t)c * L + j] : -Yd[(size_t)c * L + j];
+  // four entries per thread and store; ldT is a multiple of 16 and the padding [L, ldT) stays
+  // zero.  Ts (nullable): the same words in the swizzled operand order of the next contraction
+  // (K = L), written here so that it needs no swizzle launch; its words past L are not needed.
+  const int nch = (L + 63) >> 6;
+  for (int j4 = 4 * (int)threadIdx.x; j4 < ldT; j4 += 4 * NT) {
+    unsigned word = 0u;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int j = j4 + e;
+      const float xv = j < L ? (xunit ? xs[j] : (float)x[j]) : 0.0f;
+      const int t = selected(xv, r) ? (xv > 0.0f ? 1 : -1) : 0;
+      word |= (unsigned)(t & 0xFF) << (8 * e);
+      if (Md && t) dot += t > 0 ? Yd[(size_t)c * L + j] : -Yd[(size_t)c * L + j];
+    }
+    *reinterpret_cast<unsigned*>(T + (size_t)c * ldT + j4) = word;
+    if (Ts && j4 < L)  // block (c / 16, j / 64), lane 16 g + c % 16, word q: j % 64 = 16 q + 4 g
+      *reinterpret_cast<unsigned*>(Ts + ((size_t)(c >> 4) * nch + (j4 >> 6)) * 1024 +
+                                   (16 * ((j4 >> 2) & 3) + (c & 15)) * 16 + 4 * ((j4 >> 4) & 3)) = word;
   }
   if (Md) {
     const u64 wsum = wave_sum_u64((u64)dot);  // two's complement: exact in any order
@@ -1915,11 +1929,11 @@ static bool utr_splits(const BlockLaunch&, int) { return true; }
 // inverts spdG
 static void contract(const BlockLaunch& L, const BlockWs& w, const float* X, int ldx, int rows, int K,
                      const float* hp, int sblk, const int8_t* T, int ldt, int bs, long long* out, double* unit,
-                     hipStream_t st, bool prezeroed, const double* spdG, double* spdGi) {
+                     hipStream_t st, bool prezeroed, const double* spdG, double* spdGi, bool ts_ready) {
   const int nct = contract_nct(bs), Kp = pad64(K);
   const int gx = (rows + 63) / 64, gy = (bs + 16 * nct - 1) / (16 * nct);
   if (!prezeroed) zero_fill(reinterpret_cast<double*>(out), (long long)bs * rows, st);
-  {
+  if (!ts_ready) {  // else the selection that produced T wrote its swizzled copy
     const int nblk = gy * nct * (Kp / 64);  // every component tile the launch reads
     hipLaunchKernelGGL(swizzle_t_kernel, dim3((nblk + 3) / 4), dim3(256), 0, st, T, ldt, bs, gy * nct, Kp / 64, w.Ts);
   }
@@ -1951,10 +1965,9 @@ static void contract(const BlockLaunch& L, const BlockWs& w, const float* X, int
 
 // Y^T (bs x m) = (R diag(h) V^T)^T for V = Vt rows (h may be null: R V^T)
 static void rw_product(const BlockLaunch& L, const BlockWs& w, const float* h, int bs, int sblk, long long* outT,
-                       hipStream_t st, bool prezeroed = false, const double* spdG = nullptr,
-                       double* spdGi = nullptr) {
+                       hipStream_t st, bool prezeroed, const double* spdG, double* spdGi, bool ts_ready) {
   contract(L, w, L.R, L.ldr, L.m, L.n, h ? w.hpad : nullptr, sblk, w.Vt, w.ldv, bs, outT, w.unit + 1, st, prezeroed,
-           spdG, spdGi);
+           spdG, spdGi, ts_ready);
 }
 
 // G (bs x bs) = T diag(w) T^T for ternary rows T (bs x len, ld ldt); integer-exact without weights
@@ -1974,9 +1987,10 @@ static void gram_product(const BlockWs& w, const int8_t* T, int len, int ldt, co
 }
 
 // X (bs x n) = U^T R, from the rows of R^T
-static void utr_product(const BlockLaunch& L, const BlockWs& w, int bs, int sblk, hipStream_t st,
-                        bool prezeroed = false, const double* spdG = nullptr, double* spdGi = nullptr) {
-  contract(L, w, L.RT, L.ldt, L.n, L.m, nullptr, sblk, w.Ut, w.ldu, bs, w.Xi, w.unit, st, prezeroed, spdG, spdGi);
+static void utr_product(const BlockLaunch& L, const BlockWs& w, int bs, int sblk, hipStream_t st, bool prezeroed,
+                        const double* spdG, double* spdGi, bool ts_ready) {
+  contract(L, w, L.RT, L.ldt, L.n, L.m, nullptr, sblk, w.Ut, w.ldu, bs, w.Xi, w.unit, st, prezeroed, spdG, spdGi,
+           ts_ready);
 }
 
 // Li = (G + eps I)^-1 for bs <= kSpdMax, else Li = L^-1 for L L^T = G + eps I
@@ -2052,24 +2066,24 @@ static void solve(const BlockWs& w, int bs, const long long* in, const double* i
 static void select_rows(const double* X, const double* xunit, int L, int ldT, int bs, float tau, const float* h,
                         int EHm, int8_t* T, double* PHC, int* flags, int flag_empty, hipStream_t st,
                         double* Z0 = nullptr, int zlen = 0, const long long* Yd = nullptr,
-                        const double* ydunit = nullptr, double* Md = nullptr) {
+                        const double* ydunit = nullptr, double* Md = nullptr, int8_t* Ts = nullptr) {
   const size_t dyn = xunit ? sizeof(float) * (size_t)L : 0;
   // long rows take 1024 threads (only bs workgroups run, so the CUs have room)
   if (L > 4096) {
     if (h)
       hipLaunchKernelGGL((select_rows_kernel<true, 1024>), dim3(bs), dim3(1024), dyn, st, X, xunit, L, ldT, tau, h,
-                         EHm, T, PHC, flags, flag_empty, Z0, zlen, Yd, ydunit, Md);
+                         EHm, T, PHC, flags, flag_empty, Z0, zlen, Yd, ydunit, Md, Ts);
     else
       hipLaunchKernelGGL((select_rows_kernel<false, 1024>), dim3(bs), dim3(1024), dyn, st, X, xunit, L, ldT, tau, h,
-                         EHm, T, PHC, flags, flag_empty, Z0, zlen, Yd, ydunit, Md);
+                         EHm, T, PHC, flags, flag_empty, Z0, zlen, Yd, ydunit, Md, Ts);
     return;
   }
   if (h)
     hipLaunchKernelGGL((select_rows_kernel<true, 512>), dim3(bs), dim3(512), dyn, st, X, xunit, L, ldT, tau, h, EHm,
-                       T, PHC, flags, flag_empty, Z0, zlen, Yd, ydunit, Md);
+                       T, PHC, flags, flag_empty, Z0, zlen, Yd, ydunit, Md, Ts);
   else
     hipLaunchKernelGGL((select_rows_kernel<false, 512>), dim3(bs), dim3(512), dyn, st, X, xunit, L, ldT, tau, h, EHm,
-                       T, PHC, flags, flag_empty, Z0, zlen, Yd, ydunit, Md);
+                       T, PHC, flags, flag_empty, Z0, zlen, Yd, ydunit, Md, Ts);
 }
 
 hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops, double* bytes) {
@@ -2148,20 +2162,21 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops, double
       double* y0 = yz ? w.Yt : nullptr;                  // for this U-step
       if (naive_t) {
         if (addback && t == 0) gram_product(w, w.Ut, m, w.ldu, nullptr, 0, bs, w.GU, st);
-        utr_product(L, w, bs, sblk, st, true);
+        utr_product(L, w, bs, sblk, st, true, nullptr, nullptr, t > 0);
         if (addback && t == 0) {
           hipLaunchKernelGGL(addback_dot_kernel, dim3(bs), dim3(256), 0, st, w.Xi, w.unit, n, w.Vt, w.ldv, L.h,
                              w.ppo);
           hipLaunchKernelGGL(addback_energy_kernel, dim3(1), dim3(256), 0, st, w.ppo, w.GU, w.GVo, L.D, k0, bs,
                              w.st, w.rmax + kMaxWords * ((sblk + 1) & 1), w.GUo);
         }
-        select_rows(w.X, w.unit, n, w.ldv, bs, L.tau, hsel, ehsel, w.Vt, w.PHC, w.flags, 0, st, y0, m);
+        select_rows(w.X, w.unit, n, w.ldv, bs, L.tau, hsel, ehsel, w.Vt, w.PHC, w.flags, 0, st, y0, m, nullptr,
+                    nullptr, nullptr, w.Ts);
         gram_product(w, w.Vt, n, w.ldv, L.h, L.EHm, bs, w.GV, st);  // for the scales
-        rw_product(L, w, L.h, bs, sblk, w.Yi, st, true);
+        rw_product(L, w, L.h, bs, sblk, w.Yi, st, true, nullptr, nullptr, true);
         // the selection reads Yt while the last one also forms Md from it: Md reads the integers
         // (the selection converts its own copy in LDS)
         select_rows(w.Yt, w.unit + 1, m, w.ldu, bs, L.tau, nullptr, 0, w.Ut, w.PHC, w.flags, 0, st, x0, n,
-                    t + 1 == L.T ? w.Yi : nullptr, w.unit + 1, t + 1 == L.T ? w.Md : nullptr);
+                    t + 1 == L.T ? w.Yi : nullptr, w.unit + 1, t + 1 == L.T ? w.Md : nullptr, w.Ts);
         fl += 4.0 * m * n * bs;
         by += 2.0 * rbytes;
         continue;
@@ -2170,11 +2185,11 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops, double
       // inverse runs inside the contraction's launch, beside it; above, before it on the stream.
       if (fused) {
         gram_product(w, w.Ut, m, w.ldu, nullptr, 0, bs, w.GU, st);
-        utr_product(L, w, bs, sblk, st, true, w.GU, w.Li);
+        utr_product(L, w, bs, sblk, st, true, w.GU, w.Li, t > 0);
       } else {
         gram_product(w, w.Ut, m, w.ldu, nullptr, 0, bs, w.GU, st);
         chol_inverse(w, w.GU, bs, st);
-        utr_product(L, w, bs, sblk, st, true);
+        utr_product(L, w, bs, sblk, st, true, nullptr, nullptr, t > 0);
       }
       if (addback && t == 0) {
         hipLaunchKernelGGL(addback_dot_kernel, dim3(bs), dim3(256), 0, st, w.Xi, w.unit, n, w.Vt, w.ldv, L.h,
@@ -2183,19 +2198,20 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops, double
                            w.rmax + kMaxWords * ((sblk + 1) & 1), w.GUo);
       }
       solve(w, bs, w.Xi, w.unit, w.Z, n, st);
-      select_rows(w.Z, nullptr, n, w.ldv, bs, L.tau, hsel, ehsel, w.Vt, w.PHC, w.flags, 0, st, y0, m);
+      select_rows(w.Z, nullptr, n, w.ldv, bs, L.tau, hsel, ehsel, w.Vt, w.PHC, w.flags, 0, st, y0, m, nullptr,
+                  nullptr, nullptr, w.Ts);
       // U-step: F^T = (V^T H V + eps I)^-1 (R H V)^T, columns ternarized without weights
       if (fused) {
         gram_product(w, w.Vt, n, w.ldv, L.h, L.EHm, bs, w.GV, st);
-        rw_product(L, w, L.h, bs, sblk, w.Yi, st, true, w.GV, w.Li);
+        rw_product(L, w, L.h, bs, sblk, w.Yi, st, true, w.GV, w.Li, true);
       } else {
         gram_product(w, w.Vt, n, w.ldv, L.h, L.EHm, bs, w.GV, st);
         chol_inverse(w, w.GV, bs, st);
-        rw_product(L, w, L.h, bs, sblk, w.Yi, st, true);
+        rw_product(L, w, L.h, bs, sblk, w.Yi, st, true, nullptr, nullptr, true);
       }
       solve(w, bs, w.Yi, w.unit + 1, w.Ft, m, st);
       select_rows(w.Ft, nullptr, m, w.ldu, bs, L.tau, nullptr, 0, w.Ut, w.PHC, w.flags, 0, st, x0, n,
-                  t + 1 == L.T ? w.Yi : nullptr, w.unit + 1, t + 1 == L.T ? w.Md : nullptr);
+                  t + 1 == L.T ? w.Yi : nullptr, w.unit + 1, t + 1 == L.T ? w.Md : nullptr, w.Ts);
       fl += 4.0 * m * n * bs;
       by += 2.0 * rbytes;
     }
@@ -2228,7 +2244,7 @@ hipError_t block_run(const BlockLaunch& L, hipStream_t st, double* flops, double
     // sketch
     hipLaunchKernelGGL(omega_kernel, dim3(256), dim3(256), 0, st, w.Vt, w.ldv, bs, n, (long long)s, w.flags,
                        w.rmax, w.Yt, rw_splits(L, bs) ? (long long)bs * m : 0ll);
-    rw_product(L, w, nullptr, bs, s, w.Yi, st, true);
+    rw_product(L, w, nullptr, bs, s, w.Yi, st, true, nullptr, nullptr, false);
     select_rows(w.Yt, w.unit + 1, m, w.ldu, bs, L.tau, nullptr, 0, w.Ut, w.PHC, w.flags, 1, st,
                 utr_splits(L, bs) ? w.X : nullptr, n);
     hipLaunchKernelGGL(zero_check_kernel, dim3(1), dim3(256), 0, st, L.R, L.ldr, m, n, w.flags, w.st);
