@@ -191,14 +191,16 @@ def infer_bench(args, erm, torch, A, h, c, k, m, n, out, stream):
     erm.decompose(A, c["mu"], c["tau"], h, c["als_iters"], c["block"], stream=stream, out=out)
     X = torch.randn((args.batch, n), dtype=torch.float32, device="cuda")
     Y = torch.empty((args.batch, m), dtype=torch.float32, device="cuda")
+    # --static: the allocation-free entry point (its kernels only, on the file-scope workspace)
+    call = erm.apply_factors_static if args.static else erm.apply_factors
     for _ in range(max(1, args.warmup)):
-        erm.apply_factors(out["B"], out["C"], out["D"], m, n, X, stream=stream, out=Y)
+        call(out["B"], out["C"], out["D"], m, n, X, stream=stream, out=Y)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     e0.record(stream)
     for _ in range(args.steps):
-        erm.apply_factors(out["B"], out["C"], out["D"], m, n, X, stream=stream, out=Y)
+        call(out["B"], out["C"], out["D"], m, n, X, stream=stream, out=Y)
     e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -219,7 +221,8 @@ def infer_bench(args, erm, torch, A, h, c, k, m, n, out, stream):
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": f"infer_{args.workload}", "m": m, "n": n, "k": k, "batch": args.batch,
-                   "factors": "packed 2-bit B and C of one decomposition of the workload"},
+                   "factors": "packed 2-bit B and C of one decomposition of the workload",
+                   "entry": "externd_apply_factors_static" if args.static else "externd_apply_factors"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": None,
                      "kernel": "infer_c + infer_b + infer_reduce (one call)", "gpu_ms_per_call": gpu_ms,
@@ -240,6 +243,8 @@ def main():
     ap.add_argument("--infer", action="store_true",
                     help="time inference from the workload's packed factors instead of the decomposition")
     ap.add_argument("--batch", type=int, default=1, help="vectors per inference call (--infer)")
+    ap.add_argument("--static", action="store_true",
+                    help="--infer through the allocation-free entry point (no per-call workspace)")
     ap.add_argument("--sweeps", type=int, default=0, help="refinement sweeps after the greedy pass")
     ap.add_argument("--energy-target", type=float, default=0.0,
                     help="stop at the first component whose energy reaches this value")
