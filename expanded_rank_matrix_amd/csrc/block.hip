@@ -21,11 +21,15 @@
 // atomics, so each contraction is the exact contraction of the image, independent of launch shape
 // and atomic order, within 2^-47 of max |R| per entry of the fp64 sums of a plain implementation.
 // The contraction outputs stay integers (with their grid unit) until the kernels that read them.
-// Grams are the same int8 MFMA on the ternary rows (integer-exact; the weighted Gram takes h in
-// 35-bit fixed point).  The b x b solves use (G + eps I)^-1 from a blocked Cholesky (fp64 MFMA
-// tiles) and one fp64 MFMA product per solve; the rank-b update runs on v_mfma_f64_16x16x4f64 with
-// K = b and one fp32 rounding per entry.  Selections use the same exact projection as the
-// sequential path, one workgroup per component row.
+// The contractions split their work evenly over one workgroup per CU (stream-K); the residual is
+// kept twice, R and R^T, so that both read rows.  Grams are the same int8 MFMA on the ternary
+// rows (integer-exact; the weighted Gram takes h in 35-bit fixed point).  The b x b solves use
+// (G + eps I)^-1 from a blocked Cholesky (fp64 MFMA tiles; for b <= 128 one workgroup of the
+// contraction launch computes it) and one fp64 MFMA product per solve.  The rank-b update forms
+// the exact fp64 value of sum_c d_c u_ic v_jc on int8 MFMA from a fixed-point image of the scales
+// (fp64 MFMA when the scales do not fit one grid), rounds once to fp32 and writes R and R^T.
+// Selections use the same exact projection as the sequential path, one workgroup per component
+// row, and write the ternary operand of the next contraction in its load order.
 #include "externd_internal.hpp"
 #include <type_traits>
 #include "select.hpp"

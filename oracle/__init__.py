@@ -64,6 +64,12 @@ def _load():
         lib.externd_oracle_rank.argtypes = [i64, i64, f32]
         lib.externd_oracle_words.restype = i64
         lib.externd_oracle_words.argtypes = [i64]
+        lib.externd_oracle_splitmix64.restype = ctypes.c_uint64
+        lib.externd_oracle_splitmix64.argtypes = [ctypes.c_uint64]
+        lib.externd_oracle_sketch_sign.restype = ctypes.c_double
+        lib.externd_oracle_sketch_sign.argtypes = [i64, i64, i64]
+        lib.externd_oracle_block_targets.restype = ctypes.c_int
+        lib.externd_oracle_block_targets.argtypes = [vp, i64, i64, vp, vp, vp, i64, ctypes.c_int, vp, vp]
         lib.externd_oracle_project.restype = ctypes.c_int
         lib.externd_oracle_project.argtypes = [vp, i64, f32, vp, vp, vp, vp, vp]
         lib.externd_oracle_decompose.restype = ctypes.c_int
@@ -95,6 +101,35 @@ def _f32(a):
 def rank(m: int, n: int, mu: float) -> int:
     """k = floor(mu * min(m, n) + 1e-9), or -1 if invalid."""
     return int(_load().externd_oracle_rank(m, n, mu))
+
+
+def splitmix64(key: int) -> int:
+    """First output of splitmix64 started from state `key` (the sketch's generator)."""
+    return int(_load().externd_oracle_splitmix64(key & 0xFFFFFFFFFFFFFFFF))
+
+
+def sketch_sign(s: int, c: int, j: int) -> float:
+    """Entry (j, c) of block s's sign sketch: 1 for c = 0, else +-1 from splitmix64."""
+    return float(_load().externd_oracle_sketch_sign(s, c, j))
+
+
+def block_targets(A, U, V, h=None, naive: bool = False):
+    """The block engine's targets for ternary U (bs x m) and V (bs x n): (X, Ft) with
+    X = (U^T U + eps I)^-1 U^T A and Ft = (V^T H V + eps I)^-1 (A H V)^T."""
+    A = np.ascontiguousarray(A, dtype=np.float32)
+    m, n = A.shape
+    U = np.ascontiguousarray(U, dtype=np.int8)
+    V = np.ascontiguousarray(V, dtype=np.int8)
+    bs = U.shape[0]
+    assert U.shape == (bs, m) and V.shape == (bs, n)
+    hh = _f32(h)
+    X = np.zeros((bs, n), dtype=np.float64)
+    Ft = np.zeros((bs, m), dtype=np.float64)
+    rc = _load().externd_oracle_block_targets(_ptr(A), m, n, _ptr(hh), _ptr(U), _ptr(V), bs, int(naive),
+                                              _ptr(X), _ptr(Ft))
+    if rc != 0:
+        raise ValueError("oracle block_targets failed")
+    return X, Ft
 
 
 def words(length: int) -> int:

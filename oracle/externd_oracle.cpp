@@ -543,6 +543,34 @@ void mul_utr(const State<RT>& st, const std::vector<int8_t>& U, int64_t bs, std:
   }
 }
 
+// V-step target, Eq. 3: X = (U^T U + eps I)^-1 U^T R (bs x n), eps = 1e-6 trace(U^T U) / bs;
+// without the decorrelation (ablation) X = U^T R.
+template <typename RT>
+void v_target(const State<RT>& st, const std::vector<int8_t>& U, int64_t bs, std::vector<double>& X) {
+  std::vector<double> GU = gram(U, st.m, bs, nullptr);
+  double tr = 0.0;
+  for (int64_t c = 0; c < bs; ++c) tr += GU[c * bs + c];
+  mul_utr(st, U, bs, X);
+  if (!(st.ablation & kNaiveTarget)) chol_solve(GU, bs, 1e-6 * tr / (double)bs, X.data(), st.n);
+}
+
+// U-step target, the same least-squares target with the roles swapped and the weighted Gram:
+// F = R H V (V^T H V + eps I)^-1, returned transposed (Ft, bs x m), with Q = R H V (m x bs) and
+// GV = V^T H V.
+template <typename RT>
+void u_target(const State<RT>& st, const std::vector<int8_t>& V, int64_t bs, std::vector<double>& Q,
+              std::vector<double>& GV, std::vector<double>& Ft) {
+  const int64_t m = st.m, n = st.n;
+  GV = gram(V, n, bs, st.h);
+  double trv = 0.0;
+  for (int64_t c = 0; c < bs; ++c) trv += GV[c * bs + c];
+  mul_rhv(st, V, bs, Q);
+  Ft.assign(bs * m, 0.0);  // F^T = (GV + eps I)^-1 Q^T  (GV symmetric)
+  for (int64_t i = 0; i < m; ++i)
+    for (int64_t c = 0; c < bs; ++c) Ft[c * m + i] = Q[i * bs + c];
+  if (!(st.ablation & kNaiveTarget)) chol_solve(GV, bs, 1e-6 * trv / (double)bs, Ft.data(), m);
+}
+
 template <typename RT>
 Block als_block(State<RT>& st, Block& b);
 
@@ -600,11 +628,7 @@ Block als_block(State<RT>& st, Block& b) {
   std::vector<double> X, Q, GV;
   for (int it = 0; it < st.T; ++it) {
     // V-step, Eq. 3: G = (U^T U + eps I)^-1 U^T R, each row ternarized with weights h.
-    std::vector<double> GU = gram(b.U, m, bs, nullptr);
-    double tr = 0.0;
-    for (int64_t c = 0; c < bs; ++c) tr += GU[c * bs + c];
-    mul_utr(st, b.U, bs, X);
-    if (!(st.ablation & kNaiveTarget)) chol_solve(GU, bs, 1e-6 * tr / (double)bs, X.data(), n);
+    v_target(st, b.U, bs, X);
     for (int64_t c = 0; c < bs; ++c) {
       for (int64_t j = 0; j < n; ++j) xs[j] = (float)X[c * n + j];
       Proj pr = project(xs.data(), n, st.tau, (st.ablation & kNaiveWeights) ? nullptr : st.h, b.V.data() + c * n);
@@ -612,14 +636,8 @@ Block als_block(State<RT>& st, Block& b) {
     }
     // U-step, the same least-squares target with the roles swapped and the weighted Gram:
     // F = R H V (V^T H V + eps I)^-1, each column ternarized without weights.
-    GV = gram(b.V, n, bs, st.h);
-    double trv = 0.0;
-    for (int64_t c = 0; c < bs; ++c) trv += GV[c * bs + c];
-    mul_rhv(st, b.V, bs, Q);
-    std::vector<double> Ft(bs * m);  // F^T = (GV + eps I)^-1 Q^T  (GV symmetric)
-    for (int64_t i = 0; i < m; ++i)
-      for (int64_t c = 0; c < bs; ++c) Ft[c * m + i] = Q[i * bs + c];
-    if (!(st.ablation & kNaiveTarget)) chol_solve(GV, bs, 1e-6 * trv / (double)bs, Ft.data(), m);
+    std::vector<double> Ft;
+    u_target(st, b.V, bs, Q, GV, Ft);
     for (int64_t c = 0; c < bs; ++c) {
       for (int64_t i = 0; i < m; ++i) xs[i] = (float)Ft[c * m + i];
       Proj pr = project(xs.data(), m, st.tau, nullptr, b.U.data() + c * m);
@@ -1042,6 +1060,25 @@ int64_t externd_oracle_rank(int64_t m, int64_t n, float mu) {
 }
 
 int64_t externd_oracle_words(int64_t len) { return words_of(len); }
+
+uint64_t externd_oracle_splitmix64(uint64_t key) { return splitmix64(key); }
+
+double externd_oracle_sketch_sign(int64_t s, int64_t c, int64_t j) { return omega(s, c, j); }
+
+int externd_oracle_block_targets(const float* A, int64_t m, int64_t n, const float* h, const int8_t* U,
+                                 const int8_t* V, int64_t bs, int naive, double* X, double* Ft) {
+  if (m < 1 || n < 1 || bs < 1) return -1;
+  State<float> st;
+  init_state(st, A, m, n, h, 0.0f, 1, 1);
+  st.ablation = naive ? kNaiveTarget : 0;
+  std::vector<int8_t> Uv(U, U + bs * m), Vv(V, V + bs * n);
+  std::vector<double> Xv, Q, GV, Fv;
+  v_target(st, Uv, bs, Xv);
+  u_target(st, Vv, bs, Q, GV, Fv);
+  std::copy(Xv.begin(), Xv.end(), X);
+  std::copy(Fv.begin(), Fv.end(), Ft);
+  return 0;
+}
 
 int externd_oracle_project(const float* x, int64_t L, float tau, const float* h, int8_t* v,
                            double* out, int64_t* jstar, double* gap) {

@@ -45,6 +45,19 @@ typedef struct {
 
 int64_t externd_oracle_rank(int64_t m, int64_t n, float mu);
 int64_t externd_oracle_words(int64_t len);
+// splitmix64 (S. Vigna): the first output of the generator started from state `key`; and the
+// block sketch's entry Omega[j][c] of block s (reading of the review's block-ALS initialisation:
+// column 0 all ones, the rest Rademacher signs from the top bit of splitmix64 at key
+// ((s 2^16 + c) 2^32 + j)).  Exposed so that tests can pin the generator to its published outputs.
+uint64_t externd_oracle_splitmix64(uint64_t key);
+double externd_oracle_sketch_sign(int64_t s, int64_t c, int64_t j);
+// The block engine's least-squares targets for given ternary U (bs x m) and V (bs x n),
+// component-major (pith.science minor comment 1, Eq. 3, and its mirror for U): X = (U^T U +
+// eps I)^-1 U^T A (bs x n) and Ft = (V^T H V + eps I)^-1 (A H V)^T (bs x m), eps = 1e-6 trace of
+// the Gram / bs; naive != 0 drops the inverse (the ablation).  The same routines the decomposition
+// uses; exposed so that tests can pin them to a library solve.
+int externd_oracle_block_targets(const float* A, int64_t m, int64_t n, const float* h, const int8_t* U,
+                                 const int8_t* V, int64_t bs, int naive, double* X, double* Ft);
 
 /* T_tau(x; h): v (int8, L), out[0..2] = P, H, S, *jstar = support size, *gap = selection gap. */
 int externd_oracle_project(const float* x, int64_t L, float tau, const float* h,

@@ -10,6 +10,8 @@ Each check follows from the mathematics of the pages, not from the oracle's own 
   sequential energy (review, Results: within about 0.2 points);
 * the closed-form optimal scale: perturbing d never lowers the residual;
 * determinism across thread counts, fp32-vs-fp64 residual storage, packed format.
+* the sketch generator against splitmix64's published first output; the block engine's Eq. 3
+  targets against a library (LAPACK LU) solve of the same regularised normal equations.
 """
 
 import json
@@ -298,3 +300,52 @@ def test_explicit_energy_from_factors():
     # a wrong sign of D shows: the first component's energy becomes negative
     bad = oracle.explicit_energy(A, h, o["B"], o["C"], -o["D"], [0])
     assert bad[0] < 0
+
+
+def test_splitmix64_published_output():
+    """The sketch's generator against S. Vigna's published splitmix64: started from state 0, its
+    first output is 0xE220A8397B1DCDAF.  Column 0 of the sketch is all ones (reading of the
+    review's block-ALS initialisation: b = 1 then starts from the row sums), the other columns are
+    balanced signs."""
+    assert oracle.splitmix64(0) == 0xE220A8397B1DCDAF
+    assert all(oracle.sketch_sign(s, 0, j) == 1.0 for s in (0, 3) for j in (0, 1, 977))
+    signs = np.array([oracle.sketch_sign(2, c, j) for c in range(1, 9) for j in range(500)])
+    assert set(np.unique(signs)) == {-1.0, 1.0}
+    assert abs(signs.mean()) < 0.05  # 4000 fair signs: |mean| < 0.05 at ~3.2 sigma
+    # different blocks and columns draw different signs
+    a = np.array([oracle.sketch_sign(0, 1, j) for j in range(256)])
+    b = np.array([oracle.sketch_sign(1, 1, j) for j in range(256)])
+    c = np.array([oracle.sketch_sign(0, 2, j) for j in range(256)])
+    assert np.mean(a == b) < 0.7 and np.mean(a == c) < 0.7
+
+
+@pytest.mark.parametrize("weighted", [False, True])
+def test_block_targets_match_library_solve(weighted):
+    """Eq. 3 of the pith.science report (minor comment 1) and its mirror for U: the oracle's
+    targets, formed by its Gram, contraction and textbook Cholesky solve, against numpy's LU solve
+    (LAPACK) of the same regularised normal equations.  U has a repeated and an all-zero
+    component, so the Gram is singular and only the eps = 1e-6 trace / b term keeps it invertible;
+    a transposed operand, a wrong eps or a dropped weight changes the result far beyond 1e-10."""
+    rng = np.random.default_rng(11)
+    m, n, bs = 53, 41, 7
+    A = rng.standard_normal((m, n)).astype(np.float32)
+    h = rng.lognormal(0.0, 1.0, size=n).astype(np.float32) if weighted else None
+    U = rng.integers(-1, 2, size=(bs, m)).astype(np.int8)
+    U[3] = U[1]
+    U[5] = 0
+    V = rng.integers(-1, 2, size=(bs, n)).astype(np.int8)
+    X, Ft = oracle.block_targets(A, U, V, h)
+    Ud, Vd, Ad = U.astype(np.float64), V.astype(np.float64), A.astype(np.float64)
+    hh = np.ones(n) if h is None else h.astype(np.float64)
+    G = Ud @ Ud.T
+    Xr = np.linalg.solve(G + 1e-6 * np.trace(G) / bs * np.eye(bs), Ud @ Ad)
+    GV = (Vd * hh) @ Vd.T
+    Fr = np.linalg.solve(GV + 1e-6 * np.trace(GV) / bs * np.eye(bs), (Ad @ (hh[:, None] * Vd.T)).T)
+    # the repeated component makes the system ill-conditioned (condition ~ 1e6 / eps scale)
+    assert np.max(np.abs(X - Xr)) <= 1e-9 * np.max(np.abs(Xr))
+    assert np.max(np.abs(Ft - Fr)) <= 1e-12 * np.max(np.abs(Fr))
+    assert np.all(X[5] == 0.0)
+    # without the decorrelation the targets are the plain products
+    Xn, Fn = oracle.block_targets(A, U, V, h, naive=True)
+    np.testing.assert_allclose(Xn, Ud @ Ad, rtol=1e-13, atol=1e-12)
+    np.testing.assert_allclose(Fn, (Ad @ (hh[:, None] * Vd.T)).T, rtol=1e-13, atol=1e-12)
