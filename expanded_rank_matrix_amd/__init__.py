@@ -262,7 +262,8 @@ def _apply_args(B, C, D, m, n, X, out):
 
 def apply_factors(B, C, D, m: int, n: int, X, stream=None, out=None):
     """Y = (B diag(D) C X^T)^T from packed factors (as returned by decompose) for X (n or batch x n,
-    fp32, device); returns Y (m or batch x m, fp32)."""
+    fp32, device); returns Y (m or batch x m, fp32).  Enqueued on the stream without waiting (the
+    library keeps a workspace per device and stream)."""
     B, C, D, k, X2, Y, single = _apply_args(B, C, D, m, n, X, out)
     rc = load().externd_apply_factors(_dev_ptr(B), _dev_ptr(C), _dev_ptr(D), k, m, n, _dev_ptr(X2),
                                       X2.shape[0], _dev_ptr(Y), _stream_ptr(stream))

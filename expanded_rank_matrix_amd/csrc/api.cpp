@@ -7,7 +7,11 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <map>
+#include <memory>
+#include <mutex>
 #include <string>
+#include <utility>
 
 #include "externd.h"
 #include "externd_internal.hpp"
@@ -360,6 +364,25 @@ int externd_project(const float* X, int64_t count, int64_t L, float tau, const f
   return EXTERND_OK;
 }
 
+// Workspace of externd_apply_factors: one buffer per (device, stream), grown on demand and held
+// until the process ends, so that a call after the first is its kernels alone.  Calls on one
+// stream use its buffer in stream order; the lock keeps two threads from enqueueing on one stream
+// at once.
+struct InferBuffer {
+  std::mutex mu;
+  void* p = nullptr;
+  size_t bytes = 0;
+};
+
+static InferBuffer& infer_buffer(int dev, hipStream_t st) {
+  static std::mutex mu;
+  static std::map<std::pair<int, hipStream_t>, std::unique_ptr<InferBuffer>> buffers;
+  std::lock_guard<std::mutex> g(mu);
+  std::unique_ptr<InferBuffer>& b = buffers[std::make_pair(dev, st)];
+  if (!b) b.reset(new InferBuffer);
+  return *b;
+}
+
 int externd_apply_factors(const uint32_t* B_packed, const uint32_t* C_packed, const float* D, int64_t k, int64_t m,
                           int64_t n, const float* X, int64_t batch, float* Y, void* stream) {
   g_last_error.clear();
@@ -369,18 +392,25 @@ int externd_apply_factors(const uint32_t* B_packed, const uint32_t* C_packed, co
     return fail(EXTERND_EINVAL, "need k, m, n >= 1 (and below 2^31)");
   if (batch < 1 || batch > 65535) return fail(EXTERND_EINVAL, "need 1 <= batch <= 65535");
   const size_t wsb = infer_workspace_bytes((int)k, (int)m, (int)batch);
-  void* p = nullptr;
-  if (hipMallocAsync(&p, wsb, st) != hipSuccess) {
-    (void)hipGetLastError();
-    return fail(EXTERND_ENOMEM, "workspace allocation failed");
+  int dev = 0;
+  HIP_OR_FAIL(hipGetDevice(&dev));
+  InferBuffer& buf = infer_buffer(dev, st);
+  std::lock_guard<std::mutex> lock(buf.mu);
+  if (buf.bytes < wsb) {
+    if (buf.p) {  // earlier calls on this stream may still use the buffer
+      HIP_OR_FAIL(hipStreamSynchronize(st));
+      (void)hipFree(buf.p);
+      buf.p = nullptr;
+      buf.bytes = 0;
+    }
+    if (hipMalloc(&buf.p, wsb) != hipSuccess) {
+      (void)hipGetLastError();
+      buf.p = nullptr;
+      return fail(EXTERND_ENOMEM, "workspace allocation failed");
+    }
+    buf.bytes = wsb;
   }
-  struct F {
-    void* p;
-    hipStream_t s;
-    ~F() { (void)hipFreeAsync(p, s); }
-  } fg{p, st};
-  HIP_OR_FAIL(infer_run(B_packed, C_packed, D, (int)k, (int)m, (int)n, X, (int)batch, Y, p, st));
-  HIP_OR_FAIL(hipStreamSynchronize(st));
+  HIP_OR_FAIL(infer_run(B_packed, C_packed, D, (int)k, (int)m, (int)n, X, (int)batch, Y, buf.p, st));
   return EXTERND_OK;
 }
 
@@ -396,7 +426,9 @@ int externd_apply_factors_static(const uint32_t* B_packed, const uint32_t* C_pac
   if (need > kInferStaticBytes)
     return fail(EXTERND_EINVAL,
                 "batch x (k + m) too large for the fixed workspace: needs %zu bytes, the limit is %zu "
-                "(8 batch (k + m) bytes + 8 KiB)", need, kInferStaticBytes);
+                "(8 batch (k + m) + 4 batch ceil(k / 32) + 4 ceil(batch / 2) ceil(m / 256) bytes, each part "
+                "rounded up to 256)", need,
+                kInferStaticBytes);
   void* ws = nullptr;
   HIP_OR_FAIL(infer_static_scratch(&ws));
   HIP_OR_FAIL(infer_run(B_packed, C_packed, D, (int)k, (int)m, (int)n, X, (int)batch, Y, ws, st));

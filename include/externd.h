@@ -164,16 +164,25 @@ int externd_matvec(const float* R, int64_t m, int64_t n, const int8_t* t, const 
 /* Inference straight from the packed factors (ExTernD review, Significance: ternary additions
  * and subtractions plus one scale per component; pith.science report, the mask+sign storage of
  * Eq. 5):  Y[b] = B diag(D) C X[b] for each of `batch` vectors, i.e.
- *   s_i = D_i sum_j C_ij X[b][j],   Y[b][r] = sum_i B_ri s_i,
- * with fp64 sums in a fixed order (deterministic) and one fp32 rounding of each output.
+ *   t_i = sum_j C_ij X[b][j],   s_i = D_i t_i,   Y[b][r] = sum_i B_ri s_i.
+ * Both sums are exact integer sums over fixed-point images: X[b] scaled by a power of two per
+ * vector and rounded to integers of at most 50 bits (and n |image| <= 2^62), likewise s (k |image|
+ * <= 2^62); each image is within 2^-50 of the vector's max |x| (max |s|) per element.  The result
+ * is deterministic and independent of the launch shape; each output is rounded once to fp32.
  *   B_packed k x packed_words(m) uint32 (device): row i = column i of B, as externd_decompose
  *   C_packed k x packed_words(n) uint32 (device): row i = row i of C
  *   D        k fp32 (device)
  *   X        batch x n fp32 row-major (device), read only
  *   Y        batch x m fp32 row-major (device), written
- * 1 <= k, m, n < 2^31, 1 <= batch <= 65535.  Inputs are not checked for NaN/Inf.  The call
- * allocates its workspace (batch k + chunks x batch x m fp64) on `stream` and returns after the
- * stream's work has completed; EXTERND_EINVAL / ENOMEM / EDEVICE as for externd_decompose. */
+ * 1 <= k, m, n < 2^31, 1 <= batch <= 65535.  Inputs are not checked for NaN/Inf (a non-finite x
+ * gives meaningless outputs for its vector).  The workspace (8 batch (k + m) bytes plus
+ * 4 batch ceil(k / 32) and 4 ceil(batch / 2) ceil(m / 256)) is a library buffer per (device, stream), allocated on the first call and
+ * grown when a call needs more (after waiting for the stream), held until the process ends; a
+ * call that fits it allocates nothing.  Calls on one stream use its buffer in stream order (calls
+ * from several threads on one stream are serialised); calls on different streams use different
+ * buffers.  The call only enqueues its kernels on `stream` and returns without waiting; the caller
+ * synchronises the stream before reading Y.  EXTERND_EINVAL / ENOMEM / EDEVICE as for
+ * externd_decompose. */
 int externd_apply_factors(const uint32_t* B_packed, const uint32_t* C_packed, const float* D, int64_t k,
                           int64_t m, int64_t n, const float* X, int64_t batch, float* Y, void* stream);
 
@@ -181,12 +190,13 @@ int externd_apply_factors(const uint32_t* B_packed, const uint32_t* C_packed, co
  * capture, tight serving loops, harnesses that forbid hipMalloc.  Same arguments, arithmetic and
  * results (bit for bit) as externd_apply_factors, but the workspace is a fixed 16 MiB device
  * array inside the library, one per GPU, held until the process ends; the call allocates and frees
- * nothing.  Limit: 8 * batch * (k + m) bytes (rounded up to 256 twice) + 8 KiB must fit in the
- * 16 MiB, else EXTERND_EINVAL (batch 1: k + m up to about 2 million; k = 7680, m = 2560: batch up
- * to 204).  The call only enqueues its kernels on `stream` and returns without waiting; the caller
- * synchronises the stream before reading Y.  Every call on one GPU uses that GPU's array (the
- * kernels clear what must start at zero), so calls that may overlap on one GPU (different streams,
- * threads) race: serialise them on one stream.  EXTERND_EINVAL for bad sizes or null pointers,
+ * nothing.  Limit: 8 batch (k + m) + 4 batch ceil(k / 32) + 4 ceil(batch / 2) ceil(m / 256) bytes
+ * (each part rounded up to 256) must fit in the 16 MiB, else EXTERND_EINVAL (batch 1: k + m up to
+ * about 2 million; k = 7680, m = 2560: batch up to 202).  The call only enqueues its kernels on
+ * `stream` and returns without waiting; the caller synchronises the stream before reading Y.
+ * Every call on one GPU uses that GPU's array (the kernels clear what must start at zero), so
+ * calls that may overlap on one GPU (different streams, threads) race: serialise them on one
+ * stream.  EXTERND_EINVAL for bad sizes or null pointers,
  * EXTERND_EDEVICE for HIP errors. */
 int externd_apply_factors_static(const uint32_t* B_packed, const uint32_t* C_packed, const float* D, int64_t k,
                                  int64_t m, int64_t n, const float* X, int64_t batch, float* Y, void* stream);

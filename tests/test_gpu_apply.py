@@ -1,7 +1,11 @@
 """GPU parity of inference from the packed factors (externd_apply_factors, through the C ABI)
-against the oracle: y = B diag(D) C x, fp64 sums in a fixed order on both sides (different
-orders), one fp32 rounding of each output.  The bar: within two fp32 ulps of the oracle's output
-plus 1e-12 of the sum of the magnitudes of the terms (the fp64 reordering)."""
+against the oracle: y = B diag(D) C x, one fp32 rounding of each output.  The oracle sums in fp64
+in index order; the GPU forms both sums exactly over fixed-point images of x (per vector, at most
+50 bits and n |image| <= 2^62) and of s = D (C x) (at most 50 bits and k |image| <= 2^62).  The
+bar, derived from that arithmetic: the two may differ by the images' rounding,
+  sum_i |B_ri D_i| nnz(C_i) 2^(E_x - P_x - 1) + nnz(B_r) 2^(E_s - P_s - 1)
+(2^E bounds the vector's max |x| or |s|, P is the image's bit count), plus two fp32 ulps of the
+output and 1e-12 of the sum of the magnitudes of the terms (the fp64 roundings on both sides)."""
 
 import numpy as np
 import pytest
@@ -31,16 +35,28 @@ def check(Bt, Ct, D, X, label):
     Bp, Cp = pack(Bt), pack(Ct)
     Yg = gpu_apply(Bp, Cp, D, m, n, X)
     Yo = oracle.apply(Bp, Cp, D, m, n, X)
-    S = np.abs((Ct.astype(np.float64) @ X.T.astype(np.float64)) * D.astype(np.float64)[:, None])
-    mag = (np.abs(Bt.T.astype(np.float64)) @ S).T
-    bound = 2 * np.spacing(np.abs(Yo)).astype(np.float64) + 1e-12 * mag
+    k = Bt.shape[0]
+    Bd, Cd, Dd = Bt.astype(np.float64), Ct.astype(np.float64), D.astype(np.float64)
+    Sv = (Cd @ X.T.astype(np.float64)) * Dd[:, None]  # k x batch
+    mag = (np.abs(Bd.T) @ np.abs(Sv)).T
+    bits = lambda length: min(50, 62 - int(length).bit_length())
+    ex = np.array([np.frexp(np.max(np.abs(x)))[1] if np.any(x) else 0 for x in X.astype(np.float64)])
+    es = np.array([np.frexp(np.max(np.abs(sv)))[1] + 1 if np.any(sv) else 0 for sv in Sv.T])
+    ux = np.ldexp(1.0, ex - bits(n) - 1)  # half a unit of x's image, per vector
+    us = np.ldexp(1.0, es - bits(k) - 1)  # half a unit of s's image (one binade of slack)
+    img = (np.abs(Bd.T) @ (np.abs(Dd) * np.count_nonzero(Ct, axis=1)))[None, :] * ux[:, None] \
+        + np.count_nonzero(Bt, axis=0)[None, :] * us[:, None]
+    bound = 2 * np.spacing(np.abs(Yo)).astype(np.float64) + 1e-12 * mag + img
     bad = np.abs(Yg.astype(np.float64) - Yo.astype(np.float64)) > bound
     assert not bad.any(), f"{label}: {bad.sum()} outputs differ, worst {np.max(np.abs(Yg - Yo)):.3g}"
     return Yg, Yo
 
 
 @pytest.mark.parametrize("k,m,n,batch", [(1, 1, 1, 1), (5, 7, 9, 1), (64, 17, 33, 3), (300, 389, 103, 2),
-                                         (1000, 16, 2000, 1), (37, 1100, 17, 5)])
+                                         (1000, 16, 2000, 1), (37, 1100, 17, 5),
+                                         # x in several LDS chunks of digit operands, rows of C and B
+                                         # not a multiple of four words, several component chunks
+                                         (600, 5000, 7000, 3), (513, 4100, 6400, 2), (2000, 300, 260, 33)])
 def test_random_factors(k, m, n, batch):
     rng = np.random.default_rng(100 + k + m + n)
     Bt, Ct, D = random_factors(rng, k, m, n)
