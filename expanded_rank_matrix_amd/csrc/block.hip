@@ -799,12 +799,13 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 // lane N's value of each 16-lane row, in every lane of that row (DPP row_newbcast: a VALU move,
-// where a readlane would go through a scalar register)
+// where a readlane would go through a scalar register; every lane is written, so no old value is
+// needed and the move is not preceded by a copy)
 template <int N>
 __device__ __forceinline__ double bcast16(double v) {
   const long long b = __double_as_longlong(v);
-  const int lo = __builtin_amdgcn_update_dpp(0, (int)(unsigned)b, 0x150 + N, 0xF, 0xF, false);
-  const int hi = __builtin_amdgcn_update_dpp(0, (int)(unsigned)(b >> 32), 0x150 + N, 0xF, 0xF, false);
+  const int lo = __builtin_amdgcn_mov_dpp((int)(unsigned)b, 0x150 + N, 0xF, 0xF, true);
+  const int hi = __builtin_amdgcn_mov_dpp((int)(unsigned)(b >> 32), 0x150 + N, 0xF, 0xF, true);
   return __longlong_as_double((long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo));
 }
 
@@ -864,25 +865,27 @@ __device__ __forceinline__ void spd_inv_body(const double* G, int bs, double* Gi
   // ---------------- Cholesky, one 16-column panel at a time.  Look-ahead: after the panel of p,
   // wave 0 updates diagonal block p + 1 first and factors it while the other waves finish the
   // trailing update, so the serial 16 x 16 factorisation leaves the critical path.
-  // 16 x 16 diagonal block: Cholesky factor and its inverse by wave 0, lane r (mod 16) holding row r
-  auto factor_diag = [&](int p) {  // wave 0; each 16-lane row of the wave holds the block
+  // 16 x 16 diagonal block: Cholesky factor and its inverse by wave 0.  Every 16-lane row of the
+  // wave factors the block (lane r holding row r); the inverse X = L^-1 is split by columns, lane
+  // group g computing columns g, g + 4, g + 8 and g + 12 of every row.
+  auto factor_diag = [&](int p) {  // wave 0
     const int r = lr;
     double* T = at(p, p);
-    double a[16], x[16], rk[16];
+    double a[16], rk[16], x[4];
 #pragma unroll
     for (int c = 0; c < 16; ++c) a[c] = T[(size_t)r * ld + c];
     static_for<0, 16>([&](auto kc) {
       constexpr int k = decltype(kc)::value;
       const double piv = bcast16<k>(a[k]);
       // 1 / sqrt(piv): the hardware estimate and two Newton steps (each squares the relative
-      // error), then sqrt(piv) = piv / sqrt(piv); far shorter than a rounded sqrt and divide
-      double rr = 0.0;
-      if (piv > 0.0) {
-        double y = __builtin_amdgcn_rsq(piv);
-        y = y * fma(-0.5 * piv * y, y, 1.5);
-        y = y * fma(-0.5 * piv * y, y, 1.5);
-        rr = y;
-      }
+      // error), then sqrt(piv) = piv / sqrt(piv); far shorter than a rounded sqrt and divide.  A
+      // pivot that is not positive gives a zero row (computed on 1 and then dropped: no branch).
+      const bool pos = piv > 0.0;
+      const double pv = pos ? piv : 1.0;
+      double y = __builtin_amdgcn_rsq(pv);
+      y = y * fma(-0.5 * pv * y, y, 1.5);
+      y = y * fma(-0.5 * pv * y, y, 1.5);
+      const double rr = pos ? y : 0.0;
       const double lkk = piv * rr;
       rk[k] = rr;
       a[k] = r > k ? a[k] * rr : (r == k ? lkk : a[k]);
@@ -891,29 +894,27 @@ __device__ __forceinline__ void spd_inv_body(const double* G, int bs, double* Gi
         a[j] = fma(-a[k], bcast16<j>(a[k]), a[j]);  // meaningful for rows r >= j
       });
     });
+    // X = L^-1 row by row with the scales deferred: u_t = row t of L_tt X, so that a later row r
+    // takes u_r[c] -= (L_rt / L_tt) u_t[c], and X_rc = u_r[c] / L_rr at the end.  Column c = g + 4 q
+    // sits in x[q]; u_r starts as the unit row e_r.
 #pragma unroll
-    for (int c = 0; c < 16; ++c) x[c] = 0.0;
+    for (int q = 0; q < 4; ++q) x[q] = (lk + 4 * q == r) ? 1.0 : 0.0;
+    double myrk = 0.0;
     static_for<0, 16>([&](auto tc) {
       constexpr int t = decltype(tc)::value;
-      // row t of X = L^-1 is finished: x[c] held -sum_{j<t} L_tj X_jc (one scale per lane
-      // instead of a select per entry)
-      const double sc = r == t ? rk[t] : 1.0;
+      myrk = r == t ? rk[t] : myrk;
+      const double mrt = r > t ? a[t] * rk[t] : 0.0;  // zero for the rows r <= t
 #pragma unroll
-      for (int c = 0; c < t; ++c) x[c] *= sc;
-      x[t] = r == t ? rk[t] : x[t];
-      // later rows r > t take -L_rt X_tc; the multiplier is zero for rows r <= t
-      const double lrt = r > t ? a[t] : 0.0;
-      static_for<0, t + 1>([&](auto cc) {
-        constexpr int c = decltype(cc)::value;
-        x[c] = fma(-lrt, bcast16<t>(x[c]), x[c]);
-      });
+      for (int q = 0; q < 4; ++q) x[q] = fma(-mrt, bcast16<t>(x[q]), x[q]);  // u_t[c] = 0 for c > t
     });
     if (lane < 16) {
 #pragma unroll
-      for (int c = 0; c < 16; ++c) {
-        T[(size_t)r * ld + c] = c <= r ? a[c] : 0.0;
-        Dg[p * 256 + r * 16 + c] = c <= r ? x[c] : 0.0;
-      }
+      for (int c = 0; c < 16; ++c) T[(size_t)r * ld + c] = c <= r ? a[c] : 0.0;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int c = lk + 4 * q;
+      Dg[p * 256 + r * 16 + c] = c <= r ? x[q] * myrk : 0.0;
     }
   };
   auto trailing_tile = [&](int p, int t) {  // A_ij -= L_ip L_jp^T, tile t of the p-th update
@@ -924,14 +925,15 @@ __device__ __forceinline__ void spd_inv_body(const double* G, int bs, double* Gi
     double* T = at(i, j);
     const double* Li_ = at(i, p);
     const double* Lj_ = at(j, p);
-    dbl4 acc;
+    dbl4 acc, c[4];  // the four k-steps in independent chains
 #pragma unroll
     for (int q = 0; q < 4; ++q) acc[q] = T[(size_t)(4 * q + lk) * ld + lr];
 #pragma unroll
     for (int sl = 0; sl < 4; ++sl)
-      acc = __builtin_amdgcn_mfma_f64_16x16x4f64(-opr(Li_, ld, sl), opr(Lj_, ld, sl), acc, 0, 0, 0);
+      c[sl] = __builtin_amdgcn_mfma_f64_16x16x4f64(-opr(Li_, ld, sl), opr(Lj_, ld, sl), (dbl4){0.0, 0.0, 0.0, 0.0},
+                                                   0, 0, 0);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) T[(size_t)(4 * q + lk) * ld + lr] = acc[q];
+    for (int q = 0; q < 4; ++q) T[(size_t)(4 * q + lk) * ld + lr] = acc[q] + ((c[0][q] + c[1][q]) + (c[2][q] + c[3][q]));
   };
   if (wid == 0) factor_diag(0);
   __syncthreads();
@@ -939,12 +941,13 @@ __device__ __forceinline__ void spd_inv_body(const double* G, int bs, double* Gi
     // panel below: L_ip = A_ip D_p^T (in place)
     for (int i = p + 1 + wid; i < nb; i += NWV) {
       double* T = at(i, p);
-      dbl4 acc = (dbl4){0.0, 0.0, 0.0, 0.0};
+      dbl4 c[4];  // the four k-steps in independent chains
 #pragma unroll
       for (int sl = 0; sl < 4; ++sl)
-        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(opr(T, ld, sl), opr(Dg + p * 256, 16, sl), acc, 0, 0, 0);
+        c[sl] = __builtin_amdgcn_mfma_f64_16x16x4f64(opr(T, ld, sl), opr(Dg + p * 256, 16, sl),
+                                                     (dbl4){0.0, 0.0, 0.0, 0.0}, 0, 0, 0);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) T[(size_t)(4 * q + lk) * ld + lr] = acc[q];
+      for (int q = 0; q < 4; ++q) T[(size_t)(4 * q + lk) * ld + lr] = (c[0][q] + c[1][q]) + (c[2][q] + c[3][q]);
     }
     __syncthreads();
     if (p + 1 == nb) break;
@@ -960,52 +963,63 @@ __device__ __forceinline__ void spd_inv_body(const double* G, int bs, double* Gi
   }
   // ---------------- X = L^-1, one column block per wave and no barrier: a wave reads only L's
   // tiles, the D_i and the blocks of its own column written before.  X_jj = D_j and
-  // X_ij = -D_i sum_{k=j}^{i-1} L_ik X_kj for i > j, the sum over k split into two accumulator
-  // chains; X_ij is stored transposed in the free upper block (j, i) of A.
+  // X_ij = -D_i sum_{k=j}^{i-1} L_ik X_kj for i > j, the four k-steps of each tile product in
+  // independent accumulator chains; X_ij is stored transposed in the free upper block (j, i) of A.
   for (int j = wid; j < nb - 1; j += NWV) {
     for (int i = j + 1; i < nb; ++i) {
-      dbl4 s0 = (dbl4){0.0, 0.0, 0.0, 0.0}, s1 = s0;
+      dbl4 sc[4];
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl) sc[sl] = (dbl4){0.0, 0.0, 0.0, 0.0};
       for (int k = j; k < i; ++k) {
         const double* P = at(i, k);
+        double pa[4], pb[4];
 #pragma unroll
         for (int sl = 0; sl < 4; ++sl) {
           // X_kj[4 s + lk][lr]: D_j for k == j, else transposed storage in block (j, k)
-          const double bq = k == j ? opc(Dg + j * 256, 16, sl) : opr(at(j, k), ld, sl);
-          if ((k - j) & 1) s1 = __builtin_amdgcn_mfma_f64_16x16x4f64(opr(P, ld, sl), bq, s1, 0, 0, 0);
-          else s0 = __builtin_amdgcn_mfma_f64_16x16x4f64(opr(P, ld, sl), bq, s0, 0, 0, 0);
+          pa[sl] = opr(P, ld, sl);
+          pb[sl] = k == j ? opc(Dg + j * 256, 16, sl) : opr(at(j, k), ld, sl);
         }
+#pragma unroll
+        for (int sl = 0; sl < 4; ++sl) sc[sl] = __builtin_amdgcn_mfma_f64_16x16x4f64(pa[sl], pb[sl], sc[sl], 0, 0, 0);
       }
-      dbl4 xacc = (dbl4){0.0, 0.0, 0.0, 0.0};
+      const dbl4 sum = (sc[0] + sc[1]) + (sc[2] + sc[3]);
+      dbl4 xc[4];
 #pragma unroll
       for (int sl = 0; sl < 4; ++sl)  // an MFMA result in lane l, register s is operand B[4 s + lk][lr]
-        xacc = __builtin_amdgcn_mfma_f64_16x16x4f64(-opr(Dg + i * 256, 16, sl), s0[sl] + s1[sl], xacc, 0, 0, 0);
+        xc[sl] = __builtin_amdgcn_mfma_f64_16x16x4f64(-opr(Dg + i * 256, 16, sl), sum[sl], (dbl4){0.0, 0.0, 0.0, 0.0},
+                                                      0, 0, 0);
+      const dbl4 xacc = (xc[0] + xc[1]) + (xc[2] + xc[3]);
       double* T = at(j, i);
 #pragma unroll
       for (int q = 0; q < 4; ++q) T[(size_t)lr * ld + 4 * q + lk] = xacc[q];
     }
   }
   __syncthreads();
-  // ---------------- Gi = X^T X: tile (i, j), i >= j, is sum_{k >= i} X_ki^T X_kj (two chains)
+  // ---------------- Gi = X^T X: tile (i, j), i >= j, is sum_{k >= i} X_ki^T X_kj (four chains)
   for (int t = wid; t < nb * (nb + 1) / 2; t += NWV) {
     int i = 0;
     while ((i + 1) * (i + 2) / 2 <= t) ++i;
     const int j = t - i * (i + 1) / 2;
-    dbl4 a0 = (dbl4){0.0, 0.0, 0.0, 0.0}, a1 = a0;
+    dbl4 ac[4];
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl) ac[sl] = (dbl4){0.0, 0.0, 0.0, 0.0};
     for (int k = i; k < nb; ++k) {
+      double av[4], bv[4];
 #pragma unroll
       for (int sl = 0; sl < 4; ++sl) {
         // X_ki[4 s + lk][lr] and X_kj[4 s + lk][lr]
-        const double av = k == i ? opc(Dg + i * 256, 16, sl) : opr(at(i, k), ld, sl);
-        const double bv = k == j ? opc(Dg + j * 256, 16, sl) : opr(at(j, k), ld, sl);
-        if ((k - i) & 1) a1 = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, a1, 0, 0, 0);
-        else a0 = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, a0, 0, 0, 0);
+        av[sl] = k == i ? opc(Dg + i * 256, 16, sl) : opr(at(i, k), ld, sl);
+        bv[sl] = k == j ? opc(Dg + j * 256, 16, sl) : opr(at(j, k), ld, sl);
       }
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl) ac[sl] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[sl], bv[sl], ac[sl], 0, 0, 0);
     }
+    const dbl4 acc = (ac[0] + ac[1]) + (ac[2] + ac[3]);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int r = 16 * i + 4 * q + lk, c = 16 * j + lr;
       if (r < bs && c < bs) {
-        const double v = a0[q] + a1[q];
+        const double v = acc[q];
         Gi[(size_t)r * bs + c] = v;
         if (i != j) Gi[(size_t)c * bs + r] = v;
       }
