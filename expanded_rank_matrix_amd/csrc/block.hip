@@ -81,6 +81,19 @@ struct BlockWs {
 constexpr int kMaxWords = 64;      // words per residual-max slot (one per lane of a wave)
 constexpr int kHDig = 5;           // 7-bit digits of the fixed-point weights (35 bits)
 
+// (G + eps I)^-1 for bs <= 128 is stored in the order the solves read it (apply_strip_kernel): the
+// operand "row r, k" of a lane (lane group lk, lane lr of row tile t = r / 16, k = 4 st + lk)
+// sits at ((((t NKS / 2 + st / 2) 4 + lk) 16 + lr) 2 + st % 2, so that a wave's 16-byte loads of
+// a k-step pair read 1 KB contiguous.  NKS = 32 k-steps for bs > 64, else 16.
+__host__ __device__ inline int spd_nks(int bs) { return bs > 64 ? 32 : 16; }
+__host__ __device__ inline size_t spd_sw(int r, int k, int nks) {
+  const int t = r >> 4, lr = r & 15, lk = k & 3, st = k >> 2;
+  (void)nks;
+  return ((((size_t)t * (nks / 2) + (st >> 1)) * 4 + lk) * 16 + lr) * 2 + (st & 1);
+}
+// doubles of that storage: the row tiles times the 4 NKS k-steps
+__host__ __device__ inline size_t spd_sw_size(int bs) { return (size_t)((bs + 15) & ~15) * 4 * spd_nks(bs); }
+
 static size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // One layout for both sizing and carving.
@@ -96,7 +109,8 @@ static void ws_layout(int m, int n, int b, bool weighted, F&& take) {
   take((void**)nullptr, bb * mx * 8);
   take((void**)nullptr, bb * bb * 8);
   take((void**)nullptr, bb * bb * 8);
-  take((void**)nullptr, ((bb + 15) & ~(size_t)15) * ((bb + 15) & ~(size_t)15) * 8);  // Li
+  // Li: (G + eps I)^-1 in the solves' order for b <= 128, else L^-1 (b x b)
+  take((void**)nullptr, (b <= 128 ? spd_sw_size(b) : ((bb + 15) & ~(size_t)15) * ((bb + 15) & ~(size_t)15)) * 8);
   take((void**)nullptr, bb * 8);
   take((void**)nullptr, bb * 3 * 8);
   take((void**)nullptr, bb * 4);
@@ -285,6 +299,7 @@ __device__ __forceinline__ v4i load16(const int8_t* p) { return *reinterpret_cas
 template <int NT>
 __device__ __forceinline__ void spd_inv_body(const double* G, int bs, double* Gi, char* smem);
 __host__ __device__ inline size_t spd_lds_bytes(int bs);
+
 
 
 
@@ -1020,8 +1035,9 @@ __device__ __forceinline__ void spd_inv_body(const double* G, int bs, double* Gi
       const int r = 16 * i + 4 * q + lk, c = 16 * j + lr;
       if (r < bs && c < bs) {
         const double v = acc[q];
-        Gi[(size_t)r * bs + c] = v;
-        if (i != j) Gi[(size_t)c * bs + r] = v;
+        const int nks = spd_nks(bs);
+        Gi[spd_sw(r, c, nks)] = v;
+        if (i != j) Gi[spd_sw(c, r, nks)] = v;
       }
     }
   }
@@ -1074,14 +1090,17 @@ __global__ void __launch_bounds__(256) apply_kernel(const double* __restrict__ A
 // Workgroup: NCT 16-column strips of B (staged in LDS) x all bs rows; wave w takes the row tiles
 // w, w + 4, ...  Every A operand of the whole K range (NKS k-steps of 4) is loaded into registers
 // before the strips are staged, so the workgroup waits for one round of loads, then runs its MFMAs
-// back to back, each A operand serving the NCT strips.  K is walked in the order k = NKS lk + st
-// (step st, lane group lk): any order gives the same products, and in this one a lane's A
-// operands are NKS consecutive entries of its row, loaded 16 bytes at a time.
+// back to back, each A operand serving the NCT strips.  K is walked in the order k = 4 st + lk
+// (step st, lane group lk): the four lane groups read adjacent rows of the staged strips (distinct
+// LDS banks as far as the wave's 512 bytes allow).  A is (G + eps I)^-1 as the SPD
+// inverse stores it (spd_sw): each 16-byte load of a wave reads 1 KB contiguous.
 // Bm holds a contraction's int64 output in units of *bunit.
 template <int NRW, int NKS, int NCT>
 __global__ void __launch_bounds__(256) apply_strip_kernel(const double* __restrict__ A, int bs, const long long* Bm,
                                                           const double* bunit, double* out, int ncols) {
-  __shared__ double Bs[kSpdMax][16 * NCT];
+  // rows 4 st .. 4 st + 3 feed the four lane groups: a row pitch of 32 mod 64 words (NCT odd) keeps
+  // them on two bank halves
+  __shared__ double Bs[kSpdMax][16 * NCT + (NCT % 2 == 0 ? 16 : 0)];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int lr = lane & 15, lk = lane >> 4;
   const int col0 = blockIdx.x * 16 * NCT;
@@ -1092,19 +1111,16 @@ __global__ void __launch_bounds__(256) apply_strip_kernel(const double* __restri
   for (int u = 0; u < NRW; ++u) {
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) acc[u][ct] = (dbl4){0.0, 0.0, 0.0, 0.0};
-    const int r = (wid + 4 * u) * 16 + lr;
-    const bool rok = wid + 4 * u < ntiles && r < bs;
-    const double* ap = A + (size_t)(rok ? r : 0) * bs + NKS * lk;
-    if ((bs & 1) == 0 && rok && NKS * lk + NKS <= bs) {  // 16-byte aligned and inside the row
+    const int t = wid + 4 * u, r = t * 16 + lr;
+    const bool rok = t < ntiles && r < bs;
+    // the stored order (spd_sw): each 16-byte load of the wave reads 1 KB contiguous
+    const double* ap = A + spd_sw(rok ? r : 0, lk, NKS);
 #pragma unroll
-      for (int st = 0; st < NKS; st += 2) {
-        const double2 v = *reinterpret_cast<const double2*>(ap + st);
-        av[st][u] = v.x;
-        av[st + 1][u] = v.y;
-      }
-    } else {
-#pragma unroll
-      for (int st = 0; st < NKS; ++st) av[st][u] = (rok && NKS * lk + st < bs) ? ap[st] : 0.0;
+    for (int st = 0; st < NKS; st += 2) {
+      const double2 v = *reinterpret_cast<const double2*>(ap + (size_t)st * 64);
+      const int k = 4 * st + lk;
+      av[st][u] = (rok && k < bs) ? v.x : 0.0;
+      av[st + 1][u] = (rok && k + 4 < bs) ? v.y : 0.0;
     }
   }
   // the strips: (4 NKS) x 16 NCT values, NKS NCT / 4 per thread, all loads issued before the
@@ -1125,7 +1141,7 @@ __global__ void __launch_bounds__(256) apply_strip_kernel(const double* __restri
   __syncthreads();
 #pragma unroll
   for (int st = 0; st < NKS; ++st) {
-    const int k = NKS * lk + st;
+    const int k = 4 * st + lk;
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
       const double bv = k < bs ? Bs[k][16 * ct + lr] : 0.0;
@@ -2063,16 +2079,13 @@ static void apply(const double* A, int bs, const double* Bm, const double* bunit
 static void solve(const BlockWs& w, int bs, const long long* in, const double* in_unit, double* out, int ncols,
                   hipStream_t st) {
   if (bs <= kSpdMax) {
-    // two strips per workgroup once that still leaves a workgroup per CU or more
-    const bool two = ncols >= 2 * 16 * 256;
-    const dim3 grid(two ? (ncols + 31) / 32 : (ncols + 15) / 16);
-    if (bs <= 64) {
-      if (two) hipLaunchKernelGGL((apply_strip_kernel<1, 16, 2>), grid, dim3(256), 0, st, w.Li, bs, in, in_unit, out, ncols);
-      else hipLaunchKernelGGL((apply_strip_kernel<1, 16, 1>), grid, dim3(256), 0, st, w.Li, bs, in, in_unit, out, ncols);
-    } else {
-      if (two) hipLaunchKernelGGL((apply_strip_kernel<2, 32, 2>), grid, dim3(256), 0, st, w.Li, bs, in, in_unit, out, ncols);
-      else hipLaunchKernelGGL((apply_strip_kernel<2, 32, 1>), grid, dim3(256), 0, st, w.Li, bs, in, in_unit, out, ncols);
-    }
+    // one 16-column strip per workgroup: with several workgroups per CU one's loads overlap
+    // another's products (measured faster than two or three strips per workgroup at every size)
+    const dim3 grid((ncols + 15) / 16);
+    if (bs <= 64)
+      hipLaunchKernelGGL((apply_strip_kernel<1, 16, 1>), grid, dim3(256), 0, st, w.Li, bs, in, in_unit, out, ncols);
+    else
+      hipLaunchKernelGGL((apply_strip_kernel<2, 32, 1>), grid, dim3(256), 0, st, w.Li, bs, in, in_unit, out, ncols);
     return;
   }
   apply<false>(w.Li, bs, reinterpret_cast<const double*>(in), in_unit, w.Tmp, ncols, st);
