@@ -150,7 +150,7 @@ int externd_decompose_ex(const float* A, int64_t m, int64_t n, float mu, float t
   const size_t o_rowE = take((size_t)mi * sizeof(double));
   size_t o_RT = 0, o_xz = 0, o_xw = 0, o_xf = 0, o_rsg = 0, o_blk = 0;
   int grid = 0;
-  bool rl = false;
+  bool rl = false, keys = true;
   if (b == 1) {
     o_RT = take((size_t)ni * ldt * sizeof(float));
     o_xz = take((size_t)mi * sizeof(double));
@@ -159,7 +159,7 @@ int externd_decompose_ex(const float* A, int64_t m, int64_t n, float mu, float t
     HIP_OR_FAIL(hipGetDevice(&dev));
     int ncu = 0;
     HIP_OR_FAIL(hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev));
-    if (!seq_plan(mi, ni, h != nullptr, ncu, residual_hbm == 0, &grid, &rl))
+    if (!seq_plan(mi, ni, h != nullptr, ncu, residual_hbm == 0, &grid, &rl, &keys))
       return fail(EXTERND_EINVAL, "problem too large for the sequential kernel's on-chip state (%d x %d)", mi, ni);
     o_xf = take((size_t)4 * grid * sizeof(double));
     o_rsg = take((size_t)grid * mi * sizeof(double));
@@ -224,6 +224,7 @@ int externd_decompose_ex(const float* A, int64_t m, int64_t n, float mu, float t
     L.xf = reinterpret_cast<double*>(base + o_xf);
     L.rsg = reinterpret_cast<double*>(base + o_rsg);
     L.rl = rl;
+    L.keys = keys;
     L.bar = bar;
     L.Bp = B_packed;
     L.Cp = C_packed;

@@ -27,6 +27,7 @@ struct SeqLaunch {
   double* bytes;
   int m, n, ldr, ldt, k, T, EHm, grid;
   bool rl;  // R slab resident in LDS
+  bool keys = true;  // LDS key array of the unweighted selections (seq_plan)
   float tau;
   unsigned spin_limit;
   double target = 0.0;  // > 0: stop once the energy reaches it
@@ -34,10 +35,11 @@ struct SeqLaunch {
   int sweeps = 0;       // refinement sweeps after the greedy pass
   int ablation = 0;     // 2: the V-step projection ignores the weights
 };
-size_t seq_smem_bytes(int m, int n, bool weighted, int G, bool rl);
-// Grid size (one workgroup per CU at most) and whether the R slab is held in LDS (only where it
-// fits and allow_rl); 0 if the problem does not fit the kernel's on-chip state.
-int seq_plan(int m, int n, bool weighted, int ncu, bool allow_rl, int* grid, bool* rl);
+size_t seq_smem_bytes(int m, int n, bool weighted, int G, bool rl, bool keys);
+// Grid size (one workgroup per CU at most), whether the R slab is held in LDS (only where it fits
+// and allow_rl) and whether the LDS key array of the unweighted selections fits beside the rest
+// (else they take the general selection); 0 if the problem does not fit the kernel's on-chip state.
+int seq_plan(int m, int n, bool weighted, int ncu, bool allow_rl, int* grid, bool* rl, bool* keys);
 hipError_t seq_launch(const SeqLaunch& L, hipStream_t st);
 // out[r] = R_r . (t .* h) for rows of a padded row-major matrix; t (and h, nullable) padded to
 // len4 * 4 entries.  Same slab routine as the sequential kernel.

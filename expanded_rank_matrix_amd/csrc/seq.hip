@@ -68,7 +68,10 @@ struct SeqLds {
   size_t dl, kl, hl, pk, part, slab, total;
 };
 __host__ __device__ inline size_t al16(size_t x) { return (x + 15) & ~(size_t)15; }
-__host__ __device__ inline SeqLds seq_lds_layout(int m, int n, bool weighted, int G, bool rl) {
+// keys: the LDS array of the exchanged vector's fp32 bit patterns, which the unweighted
+// selections and the packing read (without it they take the general selection and round the
+// fp64 values themselves).
+__host__ __device__ inline SeqLds seq_lds_layout(int m, int n, bool weighted, int G, bool rl, bool keys) {
   const size_t L = (size_t)(m > n ? m : n);
   const size_t n4 = (size_t)((n + 3) & ~3), m4 = (size_t)((m + 3) & ~3);
   const size_t wm = (size_t)((m + 15) / 16), wn = (size_t)((n + 15) / 16);
@@ -76,7 +79,7 @@ __host__ __device__ inline SeqLds seq_lds_layout(int m, int n, bool weighted, in
   SeqLds s;
   s.dl = al16(weighted ? sizeof(SelScratchT<true>) : sizeof(SelScratchT<false>));
   s.kl = al16(s.dl + 8 * L);
-  s.hl = al16(s.kl + 4 * L);
+  s.hl = al16(s.kl + (keys ? 4 * L : 0));
   s.pk = al16(s.hl + (weighted ? 4 * n4 : 0));
   s.part = al16(s.pk + 4 * (4 * wm + 3 * wn + 4));
   s.slab = al16(s.part + 8 * parts);
@@ -387,14 +390,14 @@ __device__ __forceinline__ double addback_energy(const double* dl, const uint32_
   return 2.0 * d * pp - d * d * (uu * hh);
 }
 
-template <int NT, bool WV, bool RL, bool EXT>
+template <int NT, bool WV, bool RL, bool EXT, bool KEYS>
 __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
   constexpr int NW = NT / 64;
   extern __shared__ __align__(16) char smem[];
   SelScratchT<WV>& s = *reinterpret_cast<SelScratchT<WV>*>(smem);
   const int m = a.m, n = a.n;
   const int m4 = (m + 3) & ~3, n4 = (n + 3) & ~3;
-  const SeqLds lay = seq_lds_layout(m, n, WV, (int)gridDim.x, RL);
+  const SeqLds lay = seq_lds_layout(m, n, WV, (int)gridDim.x, RL, KEYS);
   double* dl = reinterpret_cast<double*>(smem + lay.dl);    // exchanged vector (z or w)
   unsigned* kl = reinterpret_cast<unsigned*>(smem + lay.kl);  // its fp32 roundings (bit patterns)
   float* hl = reinterpret_cast<float*>(smem + lay.hl);      // n4 column weights (weighted)
@@ -461,7 +464,7 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
         const unsigned kb = __float_as_uint((float)v[u]);
         if (j0 + u * NT < len) {
           dl[j0 + u * NT] = v[u];
-          kl[j0 + u * NT] = kb;
+          if (KEYS) kl[j0 + u * NT] = kb;
         }
         const unsigned k = kb & 0x7FFFFFFFu;
         kx = k > kx ? k : kx;
@@ -470,8 +473,10 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
     select_prepare<NT>(s, kx);
   };
   // Unweighted projection of the vector in dl / kl (select_prepare done): the key-array selection,
-  // or, when its candidate window is too wide, the general one (same result either way).
+  // or, when its candidate window is too wide or there is no key array, the general one (same
+  // result either way).
   auto select_unweighted = [&](int len) -> SelResult {
+    if (!KEYS) return ternary_select<NT, false, double, WV, true>(dl, nullptr, len, a.tau, 0, s);
     unsigned km = 0u;
 #pragma unroll
     for (int w = 0; w < NW; ++w) km = s.red_u[w] > km ? s.red_u[w] : km;
@@ -497,7 +502,7 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
 #pragma unroll
       for (int u = 0; u < kPg; ++u) {
         const int c = c0 + u * NW, i = c * 64 + lane, w = c * 4 + lane;
-        ks[u] = (c < nch && i < len) ? kv[i] : 0u;
+        ks[u] = (c < nch && i < len) ? (KEYS ? kv[i] : __float_as_uint((float)vals[i])) : 0u;
         olds[u] = (c < nch && lane < 4 && w < words) ? dst[w] : 0u;
       }
 #pragma unroll
@@ -749,7 +754,7 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
           const unsigned kb = __float_as_uint((float)v[u]);
           if (i0 + u * NT < m) {
             dl[i0 + u * NT] = v[u];
-            kl[i0 + u * NT] = kb;
+            if (KEYS) kl[i0 + u * NT] = kb;
           }
           const unsigned k = kb & 0x7FFFFFFFu;
           kx = k > kx ? k : kx;
@@ -983,13 +988,13 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
   }
 }
 
-size_t seq_smem_bytes(int m, int n, bool weighted, int G, bool rl) {
-  return seq_lds_layout(m, n, weighted, G, rl).total;
+size_t seq_smem_bytes(int m, int n, bool weighted, int G, bool rl, bool keys) {
+  return seq_lds_layout(m, n, weighted, G, rl, keys).total;
 }
 
-template <bool WV, bool RL, bool EXT>
+template <bool WV, bool RL, bool EXT, bool KEYS>
 static hipError_t launch_one(const SeqArgs& a, int G, size_t smem, hipStream_t st) {
-  auto kern = seq_kernel<512, WV, RL, EXT>;
+  auto kern = seq_kernel<512, WV, RL, EXT, KEYS>;
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
   if (e != hipSuccess) return e;
   SeqArgs copy = a;
@@ -997,11 +1002,11 @@ static hipError_t launch_one(const SeqArgs& a, int G, size_t smem, hipStream_t s
   return hipLaunchCooperativeKernel((const void*)kern, dim3(G), dim3(512), args, (unsigned)smem, st);
 }
 
-template <bool WV, bool RL>
+template <bool WV, bool RL, bool KEYS>
 static int coresident_one(size_t smem) {
   int nb = 0, nb2 = 0;
-  auto kern = seq_kernel<512, WV, RL, false>;
-  auto kern2 = seq_kernel<512, WV, RL, true>;
+  auto kern = seq_kernel<512, WV, RL, false, KEYS>;
+  auto kern2 = seq_kernel<512, WV, RL, true, KEYS>;
   if (hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem) != hipSuccess)
     return 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, 512, smem) != hipSuccess) return 0;
@@ -1013,19 +1018,26 @@ static int coresident_one(size_t smem) {
 
 constexpr size_t kLdsBytes = 160 * 1024;
 
-int seq_plan(int m, int n, bool weighted, int ncu, bool allow_rl, int* grid, bool* rl) {
+int seq_plan(int m, int n, bool weighted, int ncu, bool allow_rl, int* grid, bool* rl, bool* keys) {
   const int want = (int)std::max<long long>(1, std::min<long long>(ncu, ((long long)std::max(m, n) + 7) / 8));
-  // the R slab in LDS when it fits (one workgroup per CU) and the caller allows it
-  const bool try_rl = allow_rl && !weighted && seq_smem_bytes(m, n, weighted, want, true) <= kLdsBytes;
-  const size_t smem = seq_smem_bytes(m, n, weighted, want, try_rl);
-  if (smem > kLdsBytes) return 0;
-  int per = 0;
-  if (weighted) per = try_rl ? coresident_one<true, true>(smem) : coresident_one<true, false>(smem);
-  else per = try_rl ? coresident_one<false, true>(smem) : coresident_one<false, false>(smem);
-  if (per < 1 || want > ncu * per) return 0;
-  *grid = want;
-  *rl = try_rl;
-  return 1;
+  // in order of preference: the R slab in LDS (one workgroup per CU, where the caller allows it)
+  // with, then without the key array; then R in HBM with, then without it
+  for (int c = 0; c < 4; ++c) {
+    const bool try_rl = c < 2, kc = (c & 1) == 0;
+    if (try_rl && (!allow_rl || weighted)) continue;
+    const size_t smem = seq_smem_bytes(m, n, weighted, want, try_rl, kc);
+    if (smem > kLdsBytes) continue;
+    int per = 0;
+    if (weighted) per = kc ? coresident_one<true, false, true>(smem) : coresident_one<true, false, false>(smem);
+    else if (try_rl) per = kc ? coresident_one<false, true, true>(smem) : coresident_one<false, true, false>(smem);
+    else per = kc ? coresident_one<false, false, true>(smem) : coresident_one<false, false, false>(smem);
+    if (per < 1 || want > ncu * per) continue;
+    *grid = want;
+    *rl = try_rl;
+    *keys = kc;
+    return 1;
+  }
+  return 0;
 }
 
 hipError_t seq_launch(const SeqLaunch& L, hipStream_t st) {
@@ -1061,15 +1073,16 @@ hipError_t seq_launch(const SeqLaunch& L, hipStream_t st) {
   a.safeguard = L.safeguard;
   a.sweeps = L.sweeps;
   a.ablation = L.ablation;
-  const size_t smem = seq_smem_bytes(L.m, L.n, L.h != nullptr, L.grid, L.rl);
-  if (L.sweeps > 0 || L.safeguard || (L.h && (L.ablation & 2))) {
-    if (L.h)
-      return L.rl ? launch_one<true, true, true>(a, L.grid, smem, st) : launch_one<true, false, true>(a, L.grid, smem, st);
-    return L.rl ? launch_one<false, true, true>(a, L.grid, smem, st) : launch_one<false, false, true>(a, L.grid, smem, st);
-  }
-  if (L.h)
-    return L.rl ? launch_one<true, true, false>(a, L.grid, smem, st) : launch_one<true, false, false>(a, L.grid, smem, st);
-  return L.rl ? launch_one<false, true, false>(a, L.grid, smem, st) : launch_one<false, false, false>(a, L.grid, smem, st);
+  const size_t smem = seq_smem_bytes(L.m, L.n, L.h != nullptr, L.grid, L.rl, L.keys);
+  // the weighted kernels never hold the slab in LDS (seq_plan), so they exist only without RL
+  const bool ext = L.sweeps > 0 || L.safeguard || (L.h && (L.ablation & 2));
+#define EXTERND_SEQ(EXT, KEYS)                                                                         \
+  (L.h ? launch_one<true, false, EXT, KEYS>(a, L.grid, smem, st)                                       \
+       : (L.rl ? launch_one<false, true, EXT, KEYS>(a, L.grid, smem, st)                               \
+               : launch_one<false, false, EXT, KEYS>(a, L.grid, smem, st)))
+  if (ext) return L.keys ? EXTERND_SEQ(true, true) : EXTERND_SEQ(true, false);
+  return L.keys ? EXTERND_SEQ(false, true) : EXTERND_SEQ(false, false);
+#undef EXTERND_SEQ
 }
 
 // ---- standalone matvec with the same slab routine (kernel-level parity tests) ----------

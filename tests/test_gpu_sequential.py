@@ -91,6 +91,20 @@ def test_residual_in_hbm(name, m, n, mu):
         assert np.array_equal(g[key], g2[key]), key
 
 
+@pytest.mark.parametrize("name,m,n,mu", [("down2560x9728", 120, 9728, 0.5), ("attn2560", 40, 16384, 1.0)])
+def test_wide_rows_beyond_the_key_array(name, m, n, mu):
+    """Rows so long that the LDS array of fp32 keys no longer fits beside the exchanged vector (and
+    the weights): the kernel sizes the key array for the unweighted U-steps only (weighted, 9728
+    columns) or drops it (16384 columns) and takes the general selection there.  Same factors as
+    the oracle."""
+    c = inputs.CONFIGS[name]
+    A, h = inputs.make_input(name, m=m, n=n)
+    g = P.gpu_decompose(A, mu, c["tau"], h, c["als_iters"], 1)
+    o = oracle.decompose(A, mu, c["tau"], h, c["als_iters"], 1)
+    f = P.check_free_run(g, o, f"{name} {m}x{n}", alt=(A, mu, c["tau"], h, c["als_iters"], 1))
+    assert f == g["k"], f
+
+
 def test_determinism():
     A, _ = inputs.make_input("lowrank1024", m=512, n=384)
     g1 = P.gpu_decompose(A, 1.5, 0.1, None, 4, 1)
