@@ -35,6 +35,7 @@ namespace externd {
 constexpr int kSelBins = 1024;      // bins per histogram level
 constexpr int kSelShift0 = 23 - 6;  // first level: fp32 mantissa bits dropped per bin (64/octave)
 constexpr int kWinMax = 256;        // window elements scored in one pass (4 waves x 64)
+static_assert(kWinMax % 16 == 0, "the key selection pads its window to a multiple of 16");
 constexpr int kSelLevels = 4;       // histogram levels before the distinct-key walk
 
 // LDS scratch of one selection; the weight sums exist only where weighted selections run.
@@ -217,7 +218,11 @@ __device__ __forceinline__ SelResult ternary_select(const T* vals, const float* 
     for (int i0 = tid; i0 < L; i0 += kGrp * NT) {
       unsigned kk[kGrp];
 #pragma unroll
-      for (int u = 0; u < kGrp; ++u) kk[u] = i0 + u * NT < L ? keyof(i0 + u * NT) : 0u;
+      for (int u = 0; u < kGrp; ++u) {  // clamped index: every load is issued before any is used
+        const int i = i0 + u * NT;
+        const unsigned k = keyof(i < L ? i : L - 1);
+        kk[u] = i < L ? k : 0u;
+      }
 #pragma unroll
       for (int u = 0; u < kGrp; ++u) {
         const unsigned k = kk[u];
@@ -452,7 +457,11 @@ __device__ __forceinline__ SelResult ternary_select(const T* vals, const float* 
     for (int i0 = tid; i0 < L; i0 += kGrp * NT) {
       unsigned kk[kGrp];
 #pragma unroll
-      for (int u = 0; u < kGrp; ++u) kk[u] = i0 + u * NT < L ? keyof(i0 + u * NT) : 0u;
+      for (int u = 0; u < kGrp; ++u) {  // clamped index: every load is issued before any is used
+        const int i = i0 + u * NT;
+        const unsigned k = keyof(i < L ? i : L - 1);
+        kk[u] = i < L ? k : 0u;
+      }
 #pragma unroll
       for (int u = 0; u < kGrp; ++u) {
         const unsigned k = kk[u];
@@ -680,15 +689,17 @@ __device__ __forceinline__ SelResult ternary_select_keys(const unsigned* keys, i
   for (int i0 = tid; i0 < L; i0 += kGrp * NT) {
     unsigned kk[kGrp];
 #pragma unroll
-    for (int u = 0; u < kGrp; ++u) kk[u] = i0 + u * NT < L ? keys[i0 + u * NT] & 0x7FFFFFFFu : 0u;
+    for (int u = 0; u < kGrp; ++u) {  // clamped index: every load is issued before any is used
+      const int i = i0 + u * NT;
+      kk[u] = keys[i < L ? i : L - 1] & (i < L ? 0x7FFFFFFFu : 0u);
+    }
 #pragma unroll
     for (int u = 0; u < kGrp; ++u) {
       const unsigned k = kk[u];
       if (k == 0u || k < ekey) continue;
       const unsigned d = top - (k >> 17);
-      if (d < (unsigned)kLast) {
-        atomicAdd(&s.cnt[d], 1u);
-        atomicAdd(&s.psum[d], (u64)((k & 0x7FFFFFu) | ((k >> 23) != 0u ? 0x800000u : 0u)));
+      if (d < (unsigned)kLast) {  // one atomic: the count in bits 40.., the mantissa sum below
+        atomicAdd(&s.psum[d], (1ull << 40) | (u64)((k & 0x7FFFFFu) | ((k >> 23) != 0u ? 0x800000u : 0u)));
       } else {
         atomicAdd(&s.cnt[kLast], 1u);
         atomicAdd(&s.psum[kLast], fixkey(k, sP));
@@ -704,10 +715,13 @@ __device__ __forceinline__ SelResult ternary_select_keys(const unsigned* keys, i
     const int sh = (ex > 0 ? ex : 1) - 150 + sP;
     return sh >= 0 ? (v << (sh & 63)) : (sh > -64 ? (v >> ((-sh) & 63)) : 0ull);
   };
-  const uint2 cc = *reinterpret_cast<const uint2*>(&s.cnt[b0]);
+  // bins below the last hold count << 40 | mantissa sum (at most 2^24 L < 2^40); the last bin's
+  // count is in cnt
   const ulonglong2 pp2 = *reinterpret_cast<const ulonglong2*>(&s.psum[b0]);
-  const unsigned c0 = cc.x, c1 = cc.y;
-  const u64 p0 = conv(b0, pp2.x, c0), p1 = conv(b0 + 1, pp2.y, c1);
+  constexpr u64 kM40 = (1ull << 40) - 1ull;
+  const unsigned c0 = (unsigned)(pp2.x >> 40);
+  const unsigned c1 = b0 + 1 == kLast ? s.cnt[kLast] : (unsigned)(pp2.y >> 40);
+  const u64 p0 = conv(b0, pp2.x & kM40, c0), p1 = conv(b0 + 1, b0 + 1 == kLast ? pp2.y : (pp2.y & kM40), c1);
   const u64 tp = p0 + p1;
   const unsigned tc = c0 + c1;
   const u64 ip = wave_scan_u64(tp);
@@ -830,7 +844,10 @@ __device__ __forceinline__ SelResult ternary_select_keys(const unsigned* keys, i
   for (int i0 = tid; i0 < L; i0 += kGrp * NT) {
     unsigned kk[kGrp];
 #pragma unroll
-    for (int u = 0; u < kGrp; ++u) kk[u] = i0 + u * NT < L ? keys[i0 + u * NT] & 0x7FFFFFFFu : 0u;
+    for (int u = 0; u < kGrp; ++u) {  // clamped index: every load is issued before any is used
+      const int i = i0 + u * NT;
+      kk[u] = keys[i < L ? i : L - 1] & (i < L ? 0x7FFFFFFFu : 0u);
+    }
 #pragma unroll
     for (int u = 0; u < kGrp; ++u) {
       const unsigned k = kk[u];
@@ -849,18 +866,31 @@ __device__ __forceinline__ SelResult ternary_select_keys(const unsigned* keys, i
     double myS = -1.0;
     unsigned myK = 0u, myC = 0u;
     u64 myP = 0ull;
+    // pad the window to a multiple of 16 with key 0, which no element's threshold admits
+    // (kWinMax is a multiple of 16)
+    const int ns16 = (ns + 15) & ~15;
+    for (int e = ns + lane; e < ns16; e += 64) {
+      s.w_key[e] = 0u;
+      s.w_p[e] = 0ull;
+    }
     for (int e = lane; e < ((ns + 63) & ~63); e += 64) {
-      const unsigned ke = e < ns ? s.w_key[e] : 0xFFFFFFFFu;
+      const unsigned ke = s.w_key[e < ns ? e : 0] | (e < ns ? 0u : 0xFFFFFFFFu);
       u64 P = AP;
       unsigned C = AC;
-      for (int j = 0; j < ns; j += 4) {
-        const uint4 kq = *reinterpret_cast<const uint4*>(&s.w_key[j]);
-        const ulonglong2 pa = *reinterpret_cast<const ulonglong2*>(&s.w_p[j]);
-        const ulonglong2 pb = *reinterpret_cast<const ulonglong2*>(&s.w_p[j + 2]);
-        const bool i0 = kq.x >= ke, i1 = j + 1 < ns && kq.y >= ke, i2 = j + 2 < ns && kq.z >= ke,
-                   i3 = j + 3 < ns && kq.w >= ke;
-        P += (i0 ? pa.x : 0ull) + (i1 ? pa.y : 0ull) + (i2 ? pb.x : 0ull) + (i3 ? pb.y : 0ull);
-        C += (unsigned)i0 + (unsigned)i1 + (unsigned)i2 + (unsigned)i3;
+      for (int j = 0; j < ns16; j += 16) {  // sixteen elements: twelve loads in flight
+        uint4 kq[4];
+        ulonglong2 pq[8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) kq[q] = *reinterpret_cast<const uint4*>(&s.w_key[j + 4 * q]);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) pq[q] = *reinterpret_cast<const ulonglong2*>(&s.w_p[j + 2 * q]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const bool i0 = kq[q].x >= ke, i1 = kq[q].y >= ke, i2 = kq[q].z >= ke, i3 = kq[q].w >= ke;
+          P += (i0 ? pq[2 * q].x : 0ull) + (i1 ? pq[2 * q].y : 0ull) + (i2 ? pq[2 * q + 1].x : 0ull) +
+               (i3 ? pq[2 * q + 1].y : 0ull);
+          C += (unsigned)i0 + (unsigned)i1 + (unsigned)i2 + (unsigned)i3;
+        }
       }
       if (e < ns) {
         const double Pd = (double)P;

@@ -499,11 +499,19 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
     for (int c0 = wid; c0 < nch; c0 += kPg * NW) {
       unsigned ks[kPg];
       unsigned olds[kPg];
+      double ab[kPg];  // |vals| (when want_p)
 #pragma unroll
       for (int u = 0; u < kPg; ++u) {
         const int c = c0 + u * NW, i = c * 64 + lane, w = c * 4 + lane;
-        ks[u] = (c < nch && i < len) ? (KEYS ? kv[i] : __float_as_uint((float)vals[i])) : 0u;
-        olds[u] = (c < nch && lane < 4 && w < words) ? dst[w] : 0u;
+        // clamped indexes and masks rather than conditional loads, so that every load is issued
+        // before any result is waited for
+        const int ic = i < len ? i : len - 1;
+        const unsigned in_m = (c < nch && i < len) ? 0xFFFFFFFFu : 0u;
+        ks[u] = (KEYS ? kv[ic] : __float_as_uint((float)vals[ic])) & in_m;
+        if (want_p)
+          ab[u] = __longlong_as_double(__double_as_longlong(fabs(vals[ic])) & (long long)(int)in_m);
+        const bool own = c < nch && lane < 4 && w < words;
+        olds[u] = dst[own ? w : 0] & (own ? 0xFFFFFFFFu : 0u);
       }
 #pragma unroll
       for (int u = 0; u < kPg; ++u) {
@@ -514,7 +522,7 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
         const bool sel = i < len && selected(__uint_as_float(kb), r);
         const bool neg = sel && (kb >> 31) != 0u;
         const u64 mnz = __ballot(sel), mneg = __ballot(neg);
-        if (want_p && sel) pacc += fabs(vals[i]);
+        if (want_p) pacc += sel ? ab[u] : 0.0;  // + 0.0 leaves the (nonnegative) sum unchanged
         sum += (int)__popcll(mnz) - 2 * (int)__popcll(mneg);
         const int w = c * 4 + lane;
         if (lane < 4 && w < words) {
