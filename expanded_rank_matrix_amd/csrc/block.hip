@@ -1130,7 +1130,9 @@ __global__ void __launch_bounds__(256) apply_strip_kernel(const double* __restri
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
     const int x = tid + 256 * i, k = x / W, c = x % W;
-    bl[i] = (k < bs && col0 + c < ncols) ? (double)Bm[(size_t)k * ncols + col0 + c] : 0.0;
+    const bool ok = k < bs && col0 + c < ncols;
+    const double bv = (double)Bm[ok ? (size_t)k * ncols + col0 + c : 0];  // issued unconditionally
+    bl[i] = ok ? bv : 0.0;
   }
   const double bu = *bunit;
 #pragma unroll
@@ -1210,10 +1212,15 @@ __global__ void __launch_bounds__(NT) select_rows_kernel(const double* X, const 
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int j = j4 + e;
-      const float xv = j < L ? (xunit ? xs[j] : (float)x[j]) : 0.0f;
+      const int jc = j < L ? j : L - 1;  // clamped: the loads do not wait for the bounds test
+      const float xr = xunit ? xs[jc] : (float)x[jc];
+      const float xv = j < L ? xr : 0.0f;
       const int t = selected(xv, r) ? (xv > 0.0f ? 1 : -1) : 0;
       word |= (unsigned)(t & 0xFF) << (8 * e);
-      if (Md && t) dot += t > 0 ? Yd[(size_t)c * L + j] : -Yd[(size_t)c * L + j];
+      if (Md) {
+        const long long yv = Yd[(size_t)c * L + jc];
+        dot += t > 0 ? yv : (t < 0 ? -yv : 0ll);
+      }
     }
     *reinterpret_cast<unsigned*>(T + (size_t)c * ldT + j4) = word;
     if (Ts && j4 < L)  // block (c / 16, j / 64), lane 16 g + c % 16, word q: j % 64 = 16 q + 4 g

@@ -501,11 +501,13 @@ __device__ __forceinline__ SelResult ternary_select(const T* vals, const float* 
       u64 P = 0ull, H = 0ull;
       unsigned C = 0u;
 #pragma unroll 4
-      for (int j = j0; j < j1; ++j) {
-        const bool in = s.w_key[j] >= ke;
-        P += in ? s.w_p[j] : 0ull;
-        if (W) H += in ? s.w_h[j] : 0ull;
-        C += in ? 1u : 0u;
+      for (int j = j0; j < j1; ++j) {  // unconditional loads, masked sums
+        const unsigned kj = s.w_key[j];
+        const u64 pj = s.w_p[j], hj = W ? s.w_h[j] : 0ull;
+        const u64 msk = kj >= ke ? ~0ull : 0ull;
+        P += pj & msk;
+        if (W) H += hj & msk;
+        C += kj >= ke ? 1u : 0u;
       }
       const int slot = part * (nch * 64) + e;
       s.psum[slot] = P;
