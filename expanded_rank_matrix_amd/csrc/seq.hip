@@ -133,7 +133,8 @@ __device__ __forceinline__ void slab_matvec(float* base, int row_base, int ld, i
                                             double* part, double* out) {
   constexpr int NW = NT / 64;
   static_assert(kMvPart >= 3 * NW, "segment sums need 3 x waves doubles");
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  // the wave index as a scalar, so that the item loops below branch per wave instead of masking
+  const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int R = r1 - r0;
   if (R <= 0) return;
   int S = 1;
@@ -142,6 +143,7 @@ __device__ __forceinline__ void slab_matvec(float* base, int row_base, int ld, i
   const int segq = (len4 + S - 1) / S;
   const int qb = seg * segq, qe = min(len4, qb + segq);
   const int mine = R > rw0 ? (R - rw0 + rstep - 1) / rstep : 0;  // rows r0 + rw0 + rstep * j
+  const float4* h4 = reinterpret_cast<const float4*>(hl);
   for (int j0 = 0; j0 < mine; j0 += kRW) {
     const int nr = min(kRW, mine - j0);
     int oc[kRW];
@@ -151,16 +153,32 @@ __device__ __forceinline__ void slab_matvec(float* base, int row_base, int ld, i
 #pragma unroll
     for (int k = 0; k < kRW; ++k) acc[k] = 0.0;
     for (int q0 = qb; q0 < qe; q0 += 64 * kQL) {
+      // Every load of the chunk (the rows, their weights, the deflation codes) is issued before
+      // any is used: indexes past the segment are clamped to its last column and their weights
+      // and codes masked to zero, so they add 0 * x and are never written back.
+      float4 xr[kRW][kQL];
+#pragma unroll
+      for (int k = 0; k < kRW; ++k) {
+        if (k < nr) {  // uniform within the wave
+          const float4* r4 = reinterpret_cast<const float4*>(base + (size_t)(r0 + rw0 + rstep * (j0 + k) - row_base) * ld);
+#pragma unroll
+          for (int qi = 0; qi < kQL; ++qi) {
+            const int q = q0 + lane + 64 * qi;
+            xr[k][qi] = r4[q < qe ? q : qe - 1];
+          }
+        }
+      }
       double w[kQL][4];
       float od[kQL][4];
 #pragma unroll
       for (int qi = 0; qi < kQL; ++qi) {
         const int q = q0 + lane + 64 * qi;
-        const bool ok = q < qe;
-        const unsigned word = ok ? pk_w[q >> 2] : 0u;
+        const int qc = q < qe ? q : qe - 1;
+        const unsigned okm = q < qe ? 0xFFFFFFFFu : 0u;
+        const unsigned word = pk_w[qc >> 2] & okm;
         const int off = (q & 3) * 8;
         float4 h = make_float4(1.f, 1.f, 1.f, 1.f);
-        if (hl && ok) h = reinterpret_cast<const float4*>(hl)[q];
+        if (hl) h = h4[qc];
         const float hh[4] = {h.x, h.y, h.z, h.w};
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
@@ -168,35 +186,20 @@ __device__ __forceinline__ void slab_matvec(float* base, int row_base, int ld, i
           w[qi][t] = hl ? c * (double)hh[t] : c;
         }
         if (apply) {
-          const unsigned ow = ok ? pk_other[q >> 2] : 0u;
+          const unsigned ow = pk_other[qc >> 2] & okm;
 #pragma unroll
           for (int t = 0; t < 4; ++t) od[qi][t] = d * (float)code2(ow, off + 2 * t);
         }
       }
-      // the next row's columns are loaded while the current one is summed
-      float4 xn[kQL];
-      auto load_row = [&](int k) {
-        const float4* r4 = reinterpret_cast<const float4*>(base + (size_t)(r0 + rw0 + rstep * (j0 + k) - row_base) * ld);
-#pragma unroll
-        for (int qi = 0; qi < kQL; ++qi) {
-          const int q = q0 + lane + 64 * qi;
-          xn[qi] = q < qe ? r4[q] : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-      };
-      load_row(0);
 #pragma unroll
       for (int k = 0; k < kRW; ++k) {
         if (k >= nr) break;  // uniform within the wave
         const int row = r0 + rw0 + rstep * (j0 + k);
         float4* r4 = reinterpret_cast<float4*>(base + (size_t)(row - row_base) * ld);
-        float4 x[kQL];
-#pragma unroll
-        for (int qi = 0; qi < kQL; ++qi) x[qi] = xn[qi];
-        if (k + 1 < nr) load_row(k + 1);
         double a0 = 0.0, a1 = 0.0;
 #pragma unroll
         for (int qi = 0; qi < kQL; ++qi) {
-          float v[4] = {x[qi].x, x[qi].y, x[qi].z, x[qi].w};
+          float v[4] = {xr[k][qi].x, xr[k][qi].y, xr[k][qi].z, xr[k][qi].w};
           if (oc[k] != 0) {  // uniform within the wave
             const float sg = oc[k] > 0 ? -1.0f : 1.0f;
             bool any = false;
@@ -495,8 +498,10 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
     const int nch = (len + 63) >> 6;
     int changed = 0, sum = 0;
     double pacc = 0.0;
+    // the support is |key| >= kthr; kthr >= 1, so zero entries and the masked tail never enter
+    const unsigned kthr = r.count > 0u ? max(max(r.ekey, r.tkey), 1u) : 0xFFFFFFFFu;
     constexpr int kPg = 8;  // chunks per wave whose loads are issued together
-    for (int c0 = wid; c0 < nch; c0 += kPg * NW) {
+    for (int c0 = __builtin_amdgcn_readfirstlane(wid); c0 < nch; c0 += kPg * NW) {
       unsigned ks[kPg];
       unsigned olds[kPg];
       double ab[kPg];  // |vals| (when want_p)
@@ -517,10 +522,9 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
       for (int u = 0; u < kPg; ++u) {
         const int c = c0 + u * NW;
         if (c >= nch) break;  // uniform within the wave
-        const int i = c * 64 + lane;
         const unsigned kb = ks[u];
-        const bool sel = i < len && selected(__uint_as_float(kb), r);
-        const bool neg = sel && (kb >> 31) != 0u;
+        const bool sel = (kb & 0x7FFFFFFFu) >= kthr;
+        const bool neg = sel & ((kb >> 31) != 0u);
         const u64 mnz = __ballot(sel), mneg = __ballot(neg);
         if (want_p) pacc += sel ? ab[u] : 0.0;  // + 0.0 leaves the (nonnegative) sum unchanged
         sum += (int)__popcll(mnz) - 2 * (int)__popcll(mneg);
