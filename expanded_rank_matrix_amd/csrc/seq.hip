@@ -94,15 +94,6 @@ struct SeqShared {
   double pk_p[16];
 };
 
-// 16 bits spread to the even bit positions of a 32-bit word.
-__device__ __forceinline__ unsigned spread16(unsigned x) {
-  x = (x | (x << 8)) & 0x00FF00FFu;
-  x = (x | (x << 4)) & 0x0F0F0F0Fu;
-  x = (x | (x << 2)) & 0x33333333u;
-  x = (x | (x << 1)) & 0x55555555u;
-  return x;
-}
-
 struct PackOut {
   int changed;  // some word differs from the previous contents
   int sum;      // signed sum of the codes
@@ -489,57 +480,79 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
     select_prepare<NT>(s, km);
     return ternary_select<NT, false, double, WV, true>(dl, nullptr, len, a.tau, 0, s);
   };
-  // Pack the selection r of vals[0..len) into dst (2-bit codes) with wave ballots: wave w takes
-  // the 64-element chunks w, w + NW, ...; lanes 0..3 write the chunk's four words.  prev, when
-  // given, receives the old words.  Block totals are combined in wave order (deterministic).
+  // Pack the selection r of vals[0..len) into dst (2-bit codes).  Wave w takes the 256-element
+  // groups w, w + NW, ...; lane l reads elements 4l..4l+3 of a group with one 16-byte load,
+  // forms their 8 code bits at bit 8 (l % 4) of its word, and an OR over lanes l - 3..l (two DPP
+  // row shifts) leaves word l / 4 of the group in lane l when l % 4 == 3, which writes it.  prev,
+  // when given, receives the old words.  Block totals are combined in wave order (deterministic).
   auto pack_sel = [&](const double* vals, const unsigned* kv, int len, const SelResult& r, uint32_t* dst,
                       uint32_t* prev, bool want_p) -> PackOut {
     const int words = (len + 15) >> 4;
-    const int nch = (len + 63) >> 6;
+    const int ng = (len + 255) >> 8;
     int changed = 0, sum = 0;
     double pacc = 0.0;
     // the support is |key| >= kthr; kthr >= 1, so zero entries and the masked tail never enter
     const unsigned kthr = r.count > 0u ? max(max(r.ekey, r.tkey), 1u) : 0xFFFFFFFFu;
-    constexpr int kPg = 8;  // chunks per wave whose loads are issued together
-    for (int c0 = __builtin_amdgcn_readfirstlane(wid); c0 < nch; c0 += kPg * NW) {
-      unsigned ks[kPg];
+    const bool holder = (lane & 3) == 3;
+    const int sh8 = 8 * (lane & 3);
+    constexpr int kPg = 2;  // groups per wave whose loads are issued together
+    for (int g0 = __builtin_amdgcn_readfirstlane(wid); g0 < ng; g0 += kPg * NW) {
+      unsigned kq[kPg][4];
+      double av[kPg][4];  // |vals| (when want_p)
       unsigned olds[kPg];
-      double ab[kPg];  // |vals| (when want_p)
 #pragma unroll
       for (int u = 0; u < kPg; ++u) {
-        const int c = c0 + u * NW, i = c * 64 + lane, w = c * 4 + lane;
-        // clamped indexes and masks rather than conditional loads, so that every load is issued
-        // before any result is waited for
-        const int ic = i < len ? i : len - 1;
-        const unsigned in_m = (c < nch && i < len) ? 0xFFFFFFFFu : 0u;
-        ks[u] = (KEYS ? kv[ic] : __float_as_uint((float)vals[ic])) & in_m;
-        if (want_p)
-          ab[u] = __longlong_as_double(__double_as_longlong(fabs(vals[ic])) & (long long)(int)in_m);
-        const bool own = c < nch && lane < 4 && w < words;
-        olds[u] = dst[own ? w : 0] & (own ? 0xFFFFFFFFu : 0u);
+        const int g = g0 + u * NW, i = g * 256 + 4 * lane, w = g * 16 + (lane >> 2);
+        // 16-byte loads at a clamped index (the regions are padded to 16 bytes, so a group's last
+        // load stays inside them); elements past len are masked below
+        const int ic = (g < ng && i < len) ? i : 0;
+        if (KEYS) {
+          const uint4 k4 = *reinterpret_cast<const uint4*>(kv + ic);
+          kq[u][0] = k4.x;
+          kq[u][1] = k4.y;
+          kq[u][2] = k4.z;
+          kq[u][3] = k4.w;
+        }
+        if (!KEYS || want_p) {
+          const double2 v01 = *reinterpret_cast<const double2*>(vals + ic);
+          const double2 v23 = *reinterpret_cast<const double2*>(vals + ic + 2);
+          const double vv[4] = {v01.x, v01.y, v23.x, v23.y};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (!KEYS) kq[u][e] = __float_as_uint((float)vv[e]);
+            av[u][e] = fabs(vv[e]);
+          }
+        }
+        olds[u] = dst[(g < ng && w < words) ? w : 0];
       }
 #pragma unroll
       for (int u = 0; u < kPg; ++u) {
-        const int c = c0 + u * NW;
-        if (c >= nch) break;  // uniform within the wave
-        const unsigned kb = ks[u];
-        const bool sel = (kb & 0x7FFFFFFFu) >= kthr;
-        const bool neg = sel & ((kb >> 31) != 0u);
-        const u64 mnz = __ballot(sel), mneg = __ballot(neg);
-        if (want_p) pacc += sel ? ab[u] : 0.0;  // + 0.0 leaves the (nonnegative) sum unchanged
-        sum += (int)__popcll(mnz) - 2 * (int)__popcll(mneg);
-        const int w = c * 4 + lane;
-        if (lane < 4 && w < words) {
-          const unsigned bnz = (unsigned)(mnz >> (16 * lane)) & 0xFFFFu;
-          const unsigned bng = (unsigned)(mneg >> (16 * lane)) & 0xFFFFu;
-          const unsigned word = spread16(bnz) | (spread16(bng) << 1);
+        const int g = g0 + u * NW;
+        if (g >= ng) break;  // uniform within the wave
+        const int rem = len - (g * 256 + 4 * lane);  // elements of this lane that exist
+        unsigned byte = 0u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const unsigned kb = e < rem ? kq[u][e] : 0u;
+          const bool sel = (kb & 0x7FFFFFFFu) >= kthr;
+          const unsigned neg = sel ? kb >> 31 : 0u;
+          byte |= ((sel ? 1u : 0u) | (neg << 1)) << (2 * e);
+          sum += (sel ? 1 : 0) - 2 * (int)neg;
+          if (want_p) pacc += sel ? av[u][e] : 0.0;  // + 0.0 leaves the (nonnegative) sum unchanged
+        }
+        unsigned x = byte << sh8;
+        x |= dpp32<0x111, 0xF>(x);
+        x |= dpp32<0x112, 0xF>(x);
+        const int w = g * 16 + (lane >> 2);
+        if (holder && w < words) {
           const unsigned old = olds[u];
           if (prev) prev[w] = old;
-          changed |= word != old ? 1 : 0;
-          dst[w] = word;
+          changed |= x != old ? 1 : 0;
+          dst[w] = x;
         }
       }
     }
+    sum = (int)wave_sum_u32((unsigned)sum);
     const int wch = __ballot(changed != 0) != 0ull ? 1 : 0;
     if (want_p) pacc = wave_sum_f64(pacc);
     if (lane == 0) {
