@@ -406,6 +406,10 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
   uint32_t* pu0 = dv + wn;      // u0 of this component (for the byte count)
   __shared__ SeqShared sh;
   __shared__ int bar_flag;
+  // workgroup 0's per-component statistics, accumulated here and added to stats / bytes once at
+  // the end (no global read-modify-write on the way to the next component)
+  __shared__ u64 st_acc[5];  // passes, early exits, fallbacks, safeguard activations, reverts
+  __shared__ double bytes_acc;
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int G = gridDim.x, g = blockIdx.x;
@@ -418,6 +422,8 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
   float* Rb = RL ? reinterpret_cast<float*>(smem + lay.slab) : a.R;
   const int Rld = RL ? n4 : a.ldr, Rrow0 = RL ? r0 : 0;
 
+  if (tid < 5) st_acc[tid] = 0ull;
+  if (tid == 0) bytes_acc = 0.0;
   for (int i = tid; i < m; i += NT) rs[i] = a.rs0[i];
   if (RL) {
     const int q4 = n4 / 4;
@@ -720,15 +726,7 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
       }
     }
   };
-  auto block_sum_int = [&](int v) -> int {
-    if (tid == 0) sh.ivals[1] = 0;
-    __syncthreads();
-    if (v != 0) atomicAdd(&sh.ivals[1], v);
-    __syncthreads();
-    const int r = sh.ivals[1];
-    __syncthreads();
-    return r;
-  };
+
 
   // Pass 0 is the greedy pass over all k components; an energy-target stop leaves it by break
   // with comp at the last fitted component.  Passes 1..sweeps refit the fitted components in
@@ -949,28 +947,32 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
     if (g == 0) {
       for (int w = tid; w < wm; w += NT) st_dev(a.Bp + (size_t)comp * wm + w, pu[w]);
       for (int w = tid; w < wn; w += NT) st_dev(a.Cp + (size_t)comp * wn + w, pv[w]);
-      // |supp u0 U supp u_prev| (fused deflate + first V-step rows) and |supp u_prev| (writes)
-      int un = 0, pn = 0;
-      for (int w = tid; w < wm; w += NT) {
-        const unsigned dw = have_pending ? du[w] : 0u;
-        const unsigned x = pu0[w] | dw;
-        un += __popc((x | (x >> 1)) & 0x55555555u);
-        pn += __popc((dw | (dw >> 1)) & 0x55555555u);
+      // |supp u0 U supp u_prev| (fused deflate + first V-step rows) and |supp u_prev| (writes),
+      // counted by wave 0 alone; one barrier keeps du unchanged until it has been read
+      if (tid < 64) {
+        int un = 0, pn = 0;
+        for (int w = tid; w < wm; w += 64) {
+          const unsigned dw = have_pending ? du[w] : 0u;
+          const unsigned x = pu0[w] | dw;
+          un += __popc((x | (x >> 1)) & 0x55555555u);
+          pn += __popc((dw | (dw >> 1)) & 0x55555555u);
+        }
+        un = (int)wave_sum_u32((unsigned)un);
+        pn = (int)wave_sum_u32((unsigned)pn);
+        if (tid == 0) {
+          st_dev(reinterpret_cast<unsigned*>(a.D) + comp, __float_as_uint(d));
+          a.energy[comp] = 1.0 - E / E0;
+          st_acc[0] += (u64)passes;
+          if (early) st_acc[1] += 1ull;
+          if (fallback) st_acc[2] += 1ull;
+          if (sg_on) st_acc[3] += 1ull;
+          if (reverted) st_acc[4] += 1ull;
+          bytes_acc += 4.0 * (double)n * (double)un + 4.0 * (double)n * (double)pn +
+                       (double)usteps * 4.0 * (double)m * (double)n + vbytes +
+                       (EXT && a.safeguard ? 4.0 * (double)m * (double)n : 0.0);
+        }
       }
-      un = block_sum_int(un);
-      pn = block_sum_int(pn);
-      if (tid == 0) {
-        st_dev(reinterpret_cast<unsigned*>(a.D) + comp, __float_as_uint(d));
-        a.energy[comp] = 1.0 - E / E0;
-        a.stats[0] += (u64)passes;
-        if (early) a.stats[1] += 1ull;
-        if (fallback) a.stats[2] += 1ull;
-        if (sg_on) a.stats[4] += 1ull;
-        if (reverted) a.stats[6] += 1ull;
-        a.bytes[0] += 4.0 * (double)n * (double)un + 4.0 * (double)n * (double)pn +
-                      (double)usteps * 4.0 * (double)m * (double)n + vbytes +
-                      (EXT && a.safeguard ? 4.0 * (double)m * (double)n : 0.0);
-      }
+      __syncthreads();
     }
     // row-sum recurrence and pending deflation
     const double dsv = dd * (double)sumv;
@@ -1000,7 +1002,15 @@ __global__ void __launch_bounds__(NT) seq_kernel(SeqArgs a) {
       a.energy[c] = held;
     }
   }
-  if (g == 0 && tid == 0) a.stats[5] = (u64)used;
+  if (g == 0 && tid == 0) {
+    a.stats[5] = (u64)used;
+    a.stats[0] += st_acc[0];
+    a.stats[1] += st_acc[1];
+    a.stats[2] += st_acc[2];
+    a.stats[4] += st_acc[3];
+    a.stats[6] += st_acc[4];
+    a.bytes[0] += bytes_acc;
+  }
   // apply the last pending deflation to R (the transpose copy is no longer needed)
   if (have_pending && !r_applied) slab_deflate<NT>(Rb, Rrow0, Rld, n4 / 4, r0, r1, du, dv, pd);
   if (RL) {  // the final residual back to HBM
