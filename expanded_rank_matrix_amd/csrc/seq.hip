@@ -135,81 +135,80 @@ __device__ __forceinline__ void slab_matvec(float* base, int row_base, int ld, i
   const int qb = seg * segq, qe = min(len4, qb + segq);
   const int mine = R > rw0 ? (R - rw0 + rstep - 1) / rstep : 0;  // rows r0 + rw0 + rstep * j
   const float4* h4 = reinterpret_cast<const float4*>(hl);
-  for (int j0 = 0; j0 < mine; j0 += kRW) {
-    const int nr = min(kRW, mine - j0);
-    int oc[kRW];
+  // Every load of a chunk (the rows, their weights, the deflation codes) is issued before any is
+  // used: indexes past the segment are clamped to its last column and their weights and codes
+  // masked to zero, so they add 0 * x and are never written back.
+  auto load_rows = [&](int j0, int nr, int q0, float4 (&xr)[kRW][kQL]) {
 #pragma unroll
-    for (int k = 0; k < kRW; ++k) oc[k] = (apply && k < nr) ? code_at(pk_own, r0 + rw0 + rstep * (j0 + k)) : 0;
-    double acc[kRW];
-#pragma unroll
-    for (int k = 0; k < kRW; ++k) acc[k] = 0.0;
-    for (int q0 = qb; q0 < qe; q0 += 64 * kQL) {
-      // Every load of the chunk (the rows, their weights, the deflation codes) is issued before
-      // any is used: indexes past the segment are clamped to its last column and their weights
-      // and codes masked to zero, so they add 0 * x and are never written back.
-      float4 xr[kRW][kQL];
-#pragma unroll
-      for (int k = 0; k < kRW; ++k) {
-        if (k < nr) {  // uniform within the wave
-          const float4* r4 = reinterpret_cast<const float4*>(base + (size_t)(r0 + rw0 + rstep * (j0 + k) - row_base) * ld);
-#pragma unroll
-          for (int qi = 0; qi < kQL; ++qi) {
-            const int q = q0 + lane + 64 * qi;
-            xr[k][qi] = r4[q < qe ? q : qe - 1];
-          }
-        }
-      }
-      double w[kQL][4];
-      float od[kQL][4];
-#pragma unroll
-      for (int qi = 0; qi < kQL; ++qi) {
-        const int q = q0 + lane + 64 * qi;
-        const int qc = q < qe ? q : qe - 1;
-        const unsigned okm = q < qe ? 0xFFFFFFFFu : 0u;
-        const unsigned word = pk_w[qc >> 2] & okm;
-        const int off = (q & 3) * 8;
-        float4 h = make_float4(1.f, 1.f, 1.f, 1.f);
-        if (hl) h = h4[qc];
-        const float hh[4] = {h.x, h.y, h.z, h.w};
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const double c = (double)code2(word, off + 2 * t);
-          w[qi][t] = hl ? c * (double)hh[t] : c;
-        }
-        if (apply) {
-          const unsigned ow = pk_other[qc >> 2] & okm;
-#pragma unroll
-          for (int t = 0; t < 4; ++t) od[qi][t] = d * (float)code2(ow, off + 2 * t);
-        }
-      }
-#pragma unroll
-      for (int k = 0; k < kRW; ++k) {
-        if (k >= nr) break;  // uniform within the wave
-        const int row = r0 + rw0 + rstep * (j0 + k);
-        float4* r4 = reinterpret_cast<float4*>(base + (size_t)(row - row_base) * ld);
-        double a0 = 0.0, a1 = 0.0;
+    for (int k = 0; k < kRW; ++k) {
+      if (k < nr) {  // uniform within the wave
+        const float4* r4 = reinterpret_cast<const float4*>(base + (size_t)(r0 + rw0 + rstep * (j0 + k) - row_base) * ld);
 #pragma unroll
         for (int qi = 0; qi < kQL; ++qi) {
-          float v[4] = {xr[k][qi].x, xr[k][qi].y, xr[k][qi].z, xr[k][qi].w};
-          if (oc[k] != 0) {  // uniform within the wave
-            const float sg = oc[k] > 0 ? -1.0f : 1.0f;
-            bool any = false;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              v[t] = fmaf(sg, od[qi][t], v[t]);
-              any = any || od[qi][t] != 0.0f;
-            }
-            const int q = q0 + lane + 64 * qi;
-            if (q < qe && any) r4[q] = make_float4(v[0], v[1], v[2], v[3]);
-          }
-          a0 = fma((double)v[0], w[qi][0], a0);
-          a1 = fma((double)v[1], w[qi][1], a1);
-          a0 = fma((double)v[2], w[qi][2], a0);
-          a1 = fma((double)v[3], w[qi][3], a1);
+          const int q = q0 + lane + 64 * qi;
+          xr[k][qi] = r4[q < qe ? q : qe - 1];
         }
-        acc[k] += a0 + a1;
       }
     }
+  };
+  auto decode = [&](int q0, double (&w)[kQL][4], float (&od)[kQL][4]) {
+#pragma unroll
+    for (int qi = 0; qi < kQL; ++qi) {
+      const int q = q0 + lane + 64 * qi;
+      const int qc = q < qe ? q : qe - 1;
+      const unsigned okm = q < qe ? 0xFFFFFFFFu : 0u;
+      const unsigned word = pk_w[qc >> 2] & okm;
+      const int off = (q & 3) * 8;
+      float4 h = make_float4(1.f, 1.f, 1.f, 1.f);
+      if (hl) h = h4[qc];
+      const float hh[4] = {h.x, h.y, h.z, h.w};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const double c = (double)code2(word, off + 2 * t);
+        w[qi][t] = hl ? c * (double)hh[t] : c;
+      }
+      if (apply) {
+        const unsigned ow = pk_other[qc >> 2] & okm;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) od[qi][t] = d * (float)code2(ow, off + 2 * t);
+      }
+    }
+  };
+  auto own_codes = [&](int j0, int nr, int (&oc)[kRW]) {
+#pragma unroll
+    for (int k = 0; k < kRW; ++k) oc[k] = (apply && k < nr) ? code_at(pk_own, r0 + rw0 + rstep * (j0 + k)) : 0;
+  };
+  auto compute = [&](int j0, int nr, int q0, const float4 (&xr)[kRW][kQL], const double (&w)[kQL][4],
+                     const float (&od)[kQL][4], const int (&oc)[kRW], double (&acc)[kRW]) {
+#pragma unroll
+    for (int k = 0; k < kRW; ++k) {
+      if (k >= nr) break;  // uniform within the wave
+      const int row = r0 + rw0 + rstep * (j0 + k);
+      float4* r4 = reinterpret_cast<float4*>(base + (size_t)(row - row_base) * ld);
+      double a0 = 0.0, a1 = 0.0;
+#pragma unroll
+      for (int qi = 0; qi < kQL; ++qi) {
+        float v[4] = {xr[k][qi].x, xr[k][qi].y, xr[k][qi].z, xr[k][qi].w};
+        if (oc[k] != 0) {  // uniform within the wave
+          const float sg = oc[k] > 0 ? -1.0f : 1.0f;
+          bool any = false;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            v[t] = fmaf(sg, od[qi][t], v[t]);
+            any = any || od[qi][t] != 0.0f;
+          }
+          const int q = q0 + lane + 64 * qi;
+          if (q < qe && any) r4[q] = make_float4(v[0], v[1], v[2], v[3]);
+        }
+        a0 = fma((double)v[0], w[qi][0], a0);
+        a1 = fma((double)v[1], w[qi][1], a1);
+        a0 = fma((double)v[2], w[qi][2], a0);
+        a1 = fma((double)v[3], w[qi][3], a1);
+      }
+      acc[k] += a0 + a1;
+    }
+  };
+  auto finish = [&](int j0, int nr, const double (&acc)[kRW]) {
 #pragma unroll
     for (int k = 0; k < kRW; ++k) {
       if (k >= nr) break;
@@ -219,6 +218,42 @@ __device__ __forceinline__ void slab_matvec(float* base, int row_base, int ld, i
         if (S == 1) st_dev(out + r0 + rl, v);
         else part[rl * S + seg] = v;
       }
+    }
+  };
+  if (qe - qb <= 64 * kQL) {
+    // the segment is one chunk: its weights are decoded once for all of the wave's rows
+    double w[kQL][4];
+    float od[kQL][4];
+    for (int j0 = 0; j0 < mine; j0 += kRW) {
+      const int nr = min(kRW, mine - j0);
+      float4 xr[kRW][kQL];
+      load_rows(j0, nr, qb, xr);
+      if (j0 == 0) decode(qb, w, od);  // overlaps the first rows' loads
+      int oc[kRW];
+      own_codes(j0, nr, oc);
+      double acc[kRW];
+#pragma unroll
+      for (int k = 0; k < kRW; ++k) acc[k] = 0.0;
+      compute(j0, nr, qb, xr, w, od, oc, acc);
+      finish(j0, nr, acc);
+    }
+  } else {
+    for (int j0 = 0; j0 < mine; j0 += kRW) {
+      const int nr = min(kRW, mine - j0);
+      int oc[kRW];
+      own_codes(j0, nr, oc);
+      double acc[kRW];
+#pragma unroll
+      for (int k = 0; k < kRW; ++k) acc[k] = 0.0;
+      for (int q0 = qb; q0 < qe; q0 += 64 * kQL) {
+        float4 xr[kRW][kQL];
+        load_rows(j0, nr, q0, xr);
+        double w[kQL][4];
+        float od[kQL][4];
+        decode(q0, w, od);
+        compute(j0, nr, q0, xr, w, od, oc, acc);
+      }
+      finish(j0, nr, acc);
     }
   }
   if (S > 1) {
