@@ -105,8 +105,9 @@ struct PackOut {
 // out[row] (exchange buffer, device-coherent stores).  Each row is split into S column segments
 // (S a power of two, chosen so that the R x S (row, segment) items spread evenly over the waves);
 // wave w owns segment w % S of rows w / S, w / S + waves / S, ...  A lane covers float4 columns
-// lane, lane + 64, ... of its segment, decodes their weights once per chunk of kQL columns and
-// reuses them for up to kRW rows.  A row's sum is fixed-order: lane partials, a DPP wave sum,
+// lane, lane + 64, ... of its segment in chunks of kQL, kRW rows at a time; it decodes the weights
+// of a chunk once for all of its rows when the segment is one chunk, else once per group of rows.
+// A row's sum is fixed-order: lane partials, a DPP wave sum,
 // then the segments in order: deterministic, with one barrier only when S > 1.  Pending deflation
 // of rows whose own code in pk_own is nonzero is fused in: x <- fl32(x - own * other * d) where
 // pk_other is nonzero, written back by the wave that owns the (row, segment).
