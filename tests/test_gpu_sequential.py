@@ -89,6 +89,10 @@ def test_residual_in_hbm(name, m, n, mu):
     assert g2["stats"]["residual_lds"] == 1
     for key in ("B", "C", "D", "energy"):
         assert np.array_equal(g[key], g2[key]), key
+    # the kernel's bookkeeping (workgroup 0 keeps it in LDS and adds it once at the end) is the
+    # same whichever copy of the residual the kernel holds
+    for key in ("passes", "early_exits", "fallback_inits", "zero_components", "bytes_algorithmic"):
+        assert g["stats"][key] == g2["stats"][key], key
 
 
 @pytest.mark.parametrize("name,m,n,mu", [("down2560x9728", 120, 9728, 0.5), ("attn2560", 40, 16384, 1.0)])
